@@ -1,0 +1,299 @@
+"""CPU oracle for the sigmoid top-K routed MoE layer with Exact Quantile Balancing.
+
+TEST INFRASTRUCTURE.  This module is the plain, slow, obviously correct
+statement of what the layer computes.  Only the test suite, the smoke check
+and the CPU-baseline leg of the benchmark may import it; the library's
+product path never does, and this module imports nothing from the library.
+
+Sources (cited by page title and section):
+  [KPT]  "Kolibri Pre-Training from Scratch: UniBPE, Hybrid Attention and
+         Exact Quantile Balancing" (blog post).
+  [K1D]  "Kolibri 1 im Detail: hybride RNoPE-Attention, Sparse MoE und
+         FP8-Serving" (German architecture guide).
+
+Every step is the definition written out with NumPy (fp64 wherever the pages
+leave the precision open), in the pages' notation: T tokens (N), E routed
+experts, top-K, logits Z, correction bias beta, biased scores B, selections
+I_t, mixture weights S, token bias alpha, quantile Q_m, fair share r.
+
+Readings where the pages are silent (each one is listed with its reason in the
+design notes of the repository):
+  * bf16 values are decoded by placing the 16 bits above 16 zero bits.
+  * Selection order: B descending, ties to the lower expert id; -0 equals +0
+    and is returned as +0.
+  * alpha_t = -(the (K+1)-th largest B_t), margin_t = B_(K) - B_(K+1).
+  * Quantile keys: v = fp32(Z + alpha) rounded to bf16 (round to nearest
+    even) in 16-bit mode, v itself in 32-bit mode; r = floor(T*K/E).
+  * Centring: the fp64 sum of beta_raw taken sequentially in expert order,
+    divided by E, subtracted in fp64, rounded once to fp32.
+  * Mixture weights: sigmoid evaluated in fp64, rounded once to fp32.
+  * Grouping: a stable sort of the (t, k) pairs by expert; within an expert
+    tokens ascend.
+  * Expert MLPs in fp64 with no intermediate rounding.
+
+Parity pins: every function here is checked in ``tests/test_oracle_*.py``
+against the pages' worked example, closed forms, brute force on tiny inputs
+or library routines.  The router GEMM and the SwiGLU layer have no printed
+values on the pages; they are pinned by brute-force loops on tiny inputs and
+by special cases (see the tests).
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+F32 = np.float32
+F64 = np.float64
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 helpers
+# ---------------------------------------------------------------------------
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bits (uint16) -> float32: the 16 bits become the upper half."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(F32)
+
+
+def f32_to_bf16_rne(v: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bits with round-to-nearest, ties to even.
+
+    Finite inputs only.  The low 16 bits are dropped after adding half an
+    ulp of the kept part, minus one when the kept part is already even, so
+    exact halves land on the even neighbour.
+    """
+    v = np.ascontiguousarray(v, dtype=F32)
+    if not np.all(np.isfinite(v)):
+        raise ValueError("bf16 rounding: non-finite input")
+    u = v.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def _canon(a: np.ndarray) -> np.ndarray:
+    """Map -0.0 to +0.0 (in IEEE round-to-nearest, -0 + +0 = +0)."""
+    return (np.asarray(a, dtype=F32) + F32(0.0)).astype(F32)
+
+
+# ---------------------------------------------------------------------------
+# [KPT] §1 "Mathematical Setup": quantiles
+# ---------------------------------------------------------------------------
+def quantile(values, m: int):
+    """Q_m(list): the (m+1)-th largest entry (entries with repeats count
+    separately).  [KPT] §1, definition of Q_m."""
+    a = np.sort(np.asarray(values).ravel())[::-1]
+    if not 0 <= m < a.size:
+        raise ValueError(f"Q_{m} of a list with {a.size} entries")
+    return a[m]
+
+
+# ---------------------------------------------------------------------------
+# [KPT] §6.1 and [K1D] "Routing": router logits, selection, mixture weights
+# ---------------------------------------------------------------------------
+def router_logits(x: np.ndarray, w_router: np.ndarray,
+                  logit_offset: Optional[np.ndarray] = None) -> np.ndarray:
+    """Z = x W_r^T in fp64, rounded once to fp32 ([K1D] "Routing": the router
+    emits FP32 logits of shape [N, 384]).  An optional per-expert offset (a
+    workload knob, not part of the method) is then added in fp32."""
+    z = (np.asarray(x, F64) @ np.asarray(w_router, F64).T).astype(F32)
+    if logit_offset is not None:
+        z = (z + np.asarray(logit_offset, F32)[None, :]).astype(F32)
+    return z
+
+
+def route(Z: np.ndarray, beta: Optional[np.ndarray], K: int):
+    """Selection with the correction bias ([KPT] §6.1; [K1D] "Routing" step 1).
+
+    B = Z + 1_T beta^T in fp32.  I_t = the K largest entries of row t of B,
+    ordered by (B descending, expert id ascending).  Also returns the token
+    bias alpha_t = -Q_K(B_t) ([KPT] §7.1: -(the (K+1)-th largest)) and the
+    selection margin B_(K) - B_(K+1).
+    Returns (ids [T,K] int32, alpha [T] fp32, margin [T] fp32).
+    """
+    Z = np.asarray(Z, F32)
+    T, E = Z.shape
+    if not 1 <= K < E:
+        raise ValueError("need 1 <= K < E")
+    b = np.zeros(E, F32) if beta is None else np.asarray(beta, F32)
+    B = _canon(Z + b[None, :])
+    # A stable sort of -B keeps equal values in ascending expert order.
+    order = np.argsort(-B, axis=1, kind="stable")
+    ids = order[:, :K].astype(np.int32)
+    kth = np.take_along_axis(B, order[:, K - 1:K], axis=1)[:, 0]
+    k1th = np.take_along_axis(B, order[:, K:K + 1], axis=1)[:, 0]
+    alpha = (-k1th).astype(F32)
+    margin = (kth - k1th).astype(F32)
+    return ids, alpha, margin
+
+
+def mixture_weights(Z: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """S_{t,k} = sigma(Z_{t, I_tk}) from the unbiased logits, not renormalised
+    ([KPT] §6.1 "Two details matter"; [K1D] "Routing" step 2).  Evaluated in
+    fp64 and rounded once to fp32."""
+    z = np.take_along_axis(np.asarray(Z, F32), np.asarray(ids, np.int64), axis=1)
+    z64 = z.astype(F64)
+    return (1.0 / (1.0 + np.exp(-z64))).astype(F32)
+
+
+# ---------------------------------------------------------------------------
+# [KPT] §7.1-§7.3: Exact Quantile Balancing
+# ---------------------------------------------------------------------------
+def eqb_keys_values(v: np.ndarray, key_bits: int) -> np.ndarray:
+    """Values whose quantile EQB takes.  16-bit mode: v rounded to bfloat16
+    ([KPT] §7.3: every bfloat16 value gets a 16-bit key); 32-bit mode: v."""
+    v = _canon(v)
+    if key_bits == 16:
+        return _canon(bf16_to_f32(f32_to_bf16_rne(v)))
+    if key_bits == 32:
+        return v
+    raise ValueError("key_bits must be 16 or 32")
+
+
+def eqb_expert_bias(Z: np.ndarray, alpha: np.ndarray, K: int, key_bits: int = 16):
+    """One expert-bias update of Quantile Balancing, taken exactly ([KPT] §7.1,
+    §7.3): beta_e = -Q_r(Z_{:,e} + alpha), r = T*K/E, then centred.
+
+    Returns (beta_new [E] fp32, Q [E] fp32, beta_raw [E] fp32).
+    """
+    Z = np.asarray(Z, F32)
+    T, E = Z.shape
+    r = (T * K) // E
+    v = (Z + np.asarray(alpha, F32)[:, None]).astype(F32)
+    u = eqb_keys_values(v, key_bits)
+    Q = np.array([quantile(u[:, e], r) for e in range(E)], dtype=F32)
+    beta_raw = (-Q).astype(F32)
+    # Centre: the mean of the expert biases is subtracted ([KPT] §7.1, §7.2).
+    acc = 0.0
+    for e in range(E):
+        acc += float(beta_raw[e])
+    mean = acc / E
+    beta_new = np.array([float(b) - mean for b in beta_raw], dtype=F64).astype(F32)
+    return beta_new, Q, beta_raw
+
+
+# ---------------------------------------------------------------------------
+# Grouping by expert (dispatch) and the expert MLPs
+# ---------------------------------------------------------------------------
+def group_by_expert(ids: np.ndarray, E: int):
+    """Stable counting sort of the (t, k) pairs by expert.
+
+    Returns counts c_e [E], offsets [E+1] (exclusive sums), sorted_src [T*K]
+    (flat pair index t*K+k in expert order, tokens ascending within an
+    expert) and src_pos [T,K] (the inverse: where pair (t,k) landed).
+    """
+    ids = np.asarray(ids, np.int64)
+    T, K = ids.shape
+    flat = ids.ravel()
+    counts = np.bincount(flat, minlength=E).astype(np.int32)
+    offsets = np.zeros(E + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    sorted_src = np.argsort(flat, kind="stable").astype(np.int32)
+    src_pos = np.empty(T * K, np.int32)
+    src_pos[sorted_src] = np.arange(T * K, dtype=np.int32)
+    return counts, offsets, sorted_src, src_pos.reshape(T, K)
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    return g / (1.0 + np.exp(-g))
+
+
+def swiglu(X: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
+           w_down: np.ndarray) -> np.ndarray:
+    """One SwiGLU expert with no biases ([K1D] "Routing", expert paragraph):
+    two d -> h projections, SiLU(gate) * up, then h -> d.  fp64 throughout.
+    X [n,d], w_gate/w_up [h,d], w_down [d,h] -> [n,d]."""
+    X = np.asarray(X, F64)
+    G = X @ np.asarray(w_gate, F64).T
+    U = X @ np.asarray(w_up, F64).T
+    H = silu(G) * U
+    return H @ np.asarray(w_down, F64).T
+
+
+def moe_combine(x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+                ids, S, token_subset=None) -> np.ndarray:
+    """y_t = f_shared(x_t) + sum_{e in I_t} S_{t,e} f_e(x_t) ([KPT] §6.1).
+
+    Weights are float arrays of shape [E,h,d]/[E,h,d]/[E,d,h] (routed) and
+    [n_shared,hs,d]/[n_shared,hs,d]/[n_shared,d,hs] (shared; n_shared may be
+    0).  ``token_subset`` restricts the output to those tokens (rows of the
+    result follow the subset).  Returns fp64 [T', d].
+    """
+    x = np.asarray(x, F64)
+    toks = np.arange(x.shape[0]) if token_subset is None else np.asarray(token_subset)
+    xs = x[toks]
+    ids_s = np.asarray(ids)[toks]
+    S_s = np.asarray(S, F64)[toks]
+    y = np.zeros_like(xs)
+    for s in range(ws_gate.shape[0]):
+        y += swiglu(xs, ws_gate[s], ws_up[s], ws_down[s])
+    E = w_gate.shape[0]
+    for e in range(E):
+        rows, slots = np.nonzero(ids_s == e)
+        if rows.size == 0:
+            continue
+        f = swiglu(xs[rows], w_gate[e], w_up[e], w_down[e])
+        y[rows] += S_s[rows, slots][:, None] * f
+    return y
+
+
+# ---------------------------------------------------------------------------
+# Diagnostics: [KPT] §6.2 MaxVio, §9 intervention rate
+# ---------------------------------------------------------------------------
+def max_vio(counts: np.ndarray, T: int, K: int, E: int) -> float:
+    """MaxVio = max_e [c_e / (K T / E) - 1]  ([KPT] §6.2)."""
+    target = K * T / E
+    return float(np.max(np.asarray(counts, F64) / target - 1.0))
+
+
+def intervention_rate(ids_router: np.ndarray, ids_routed: np.ndarray) -> float:
+    """I = mean_t (1 - |I^u_t ∩ I_t| / K) ([KPT] §9)."""
+    a = np.asarray(ids_router)
+    b = np.asarray(ids_routed)
+    K = a.shape[1]
+    overlap = np.array([len(set(a[t].tolist()) & set(b[t].tolist()))
+                        for t in range(a.shape[0])], dtype=F64)
+    return float(np.mean(1.0 - overlap / K))
+
+
+# ---------------------------------------------------------------------------
+# The whole layer
+# ---------------------------------------------------------------------------
+def moe_layer(x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+              beta_in, K: int, recompute_bias: bool = False, key_bits: int = 16,
+              logit_offset=None, logits_in=None, token_subset=None,
+              compute_output: bool = True) -> dict:
+    """Forward pass of one MoE layer as [KPT] §6.1 and §7.1 state it.
+
+    x [T,d] and all weights are float arrays (decode bf16 bits with
+    ``bf16_to_f32`` first).  With ``recompute_bias`` the batch is routed with
+    beta_in, one EQB update computes beta_new over the batch (token bias from
+    that routing, expert quantile, centring) and the batch is routed again
+    with beta_new ([KPT] §7.2 repairs the toy collapse this way).  The
+    ``logits_in`` argument replaces the router product by given logits.
+    """
+    Z = router_logits(x, w_router, logit_offset) if logits_in is None \
+        else np.asarray(logits_in, F32)
+    T, E = Z.shape
+    out = {"logits": Z}
+    ids0, alpha0, margin0 = route(Z, beta_in, K)
+    out["counts_before"] = np.bincount(ids0.ravel(), minlength=E).astype(np.int32)
+    beta = np.zeros(E, F32) if beta_in is None else np.asarray(beta_in, F32)
+    if recompute_bias:
+        beta_new, Q, beta_raw = eqb_expert_bias(Z, alpha0, K, key_bits)
+        out.update(alpha=alpha0, beta_out=beta_new, quantile=Q, beta_raw=beta_raw)
+        beta = beta_new
+        ids, alpha, margin = route(Z, beta, K)
+    else:
+        ids, alpha, margin = ids0, alpha0, margin0
+        out.update(alpha=alpha0)
+    S = mixture_weights(Z, ids)
+    counts, offsets, sorted_src, src_pos = group_by_expert(ids, E)
+    out.update(topk_ids=ids, topk_weights=S, margin=margin, counts=counts,
+               offsets=offsets, sorted_src=sorted_src, src_pos=src_pos,
+               route_alpha=alpha)
+    if compute_output:
+        out["y"] = moe_combine(x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+                               ids, S, token_subset)
+    return out
