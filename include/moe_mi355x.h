@@ -1,0 +1,187 @@
+/*
+ * moe_mi355x.h - C ABI of the sigmoid top-K routed MoE layer for MI355X (gfx950).
+ *
+ * The layer follows "Kolibri Pre-Training from Scratch: UniBPE, Hybrid
+ * Attention and Exact Quantile Balancing" (blog post; cited below as [KPT])
+ * and "Kolibri 1 im Detail: hybride RNoPE-Attention, Sparse MoE und
+ * FP8-Serving" (German architecture guide; cited as [K1D]).
+ *
+ * Notation: N tokens (T on the pages), d model width, E routed experts,
+ * K experts per token, h routed hidden width, hs shared hidden width.
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument is device memory owned by the caller (normally a
+ *    contiguous row-major torch tensor).  The library never allocates or
+ *    frees memory and keeps no pointer after the call returns.
+ *  - bfloat16 data is passed as raw 16-bit patterns (uint16_t).
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and the call returns without waiting.  There is no device-to-host copy
+ *    inside any call.
+ *  - Arguments are checked before anything is enqueued; a rejected call
+ *    returns a non-zero status and touches no memory.
+ *    moe_last_error_message() then describes the problem (thread-local).
+ *  - Outputs are fully overwritten and must not alias inputs.  Workspace
+ *    contents are undefined on entry and on exit; concurrent calls need
+ *    distinct workspaces.
+ *  - Results are deterministic run to run (no floating-point atomics).
+ *  - Non-finite logits or inputs are outside the contract.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,   /* null/misaligned pointer, bad flag, aliasing */
+  MOE_ERR_UNSUPPORTED_SHAPE = 2,  /* a size outside the limits stated below */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4                 /* a HIP launch error; see the message */
+} moe_status_t;
+
+/* Size limits of every entry point: 1 <= N <= 2^24, 1 <= K <= 8,
+ * K < E <= 384, and for the layer also d % 64 == 0 (64 <= d <= 8192),
+ * h % 32 == 0 (32 <= h <= 4096), hs % 32 == 0, n_shared in {0, 1}. */
+#define MOE_MAX_E 384
+#define MOE_MAX_K 8
+
+/* Flags of moe_problem_t.flags */
+#define MOE_RECOMPUTE_BIAS 0x1u  /* route with beta_in, one exact quantile update, re-route */
+#define MOE_KEY32 0x2u           /* quantile over fp32 keys instead of bf16 keys */
+
+/*
+ * moe_route - bias-corrected top-K selection and sigmoid mixture weights over
+ * given logits.  [KPT] §6.1 routing equations: B = Z + 1 beta^T is used for
+ * selection only; S = sigmoid(Z) of the unbiased logits, not renormalised
+ * ([K1D] "Routing", steps 1 and 2).  Also emits the token bias of [KPT] §7.1,
+ * alpha_t = -(the (K+1)-th largest entry of B_t).
+ *
+ *  logits       [N,E] fp32, row-major (Z).
+ *  beta         [E] fp32 correction bias, or NULL for zero.
+ *  topk_ids     [N,K] int32 out: per token, B descending, ties -> lower id.
+ *  topk_weights [N,K] fp32 out: sigmoid(Z[t, id]) (evaluated in fp64).
+ *  alpha        [N] fp32 out or NULL: -(B_(K+1)), with -0 read as +0.
+ *  margin       [N] fp32 out or NULL: B_(K) - B_(K+1) (near-tie indicator).
+ * Pointers 4-byte aligned.  Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, HIP.
+ */
+moe_status_t moe_route(const float* logits, const float* beta, int64_t N,
+                       int32_t E, int32_t K, int32_t* topk_ids,
+                       float* topk_weights, float* alpha, float* margin,
+                       void* stream);
+
+/*
+ * moe_eqb_bias - one exact expert-bias update of Quantile Balancing.
+ * [KPT] §7.1: beta_e = -Q_r(Z[:,e] + alpha), r = floor(N*K/E), then centred
+ * (mean subtracted); Q_m is the (m+1)-th largest entry ([KPT] §1).  The
+ * quantile is found exactly by radix selection over order-preserving integer
+ * keys with 256-bin per-expert histograms ([KPT] §7.3): two passes over
+ * 16-bit keys of the bf16-rounded values v = bf16(fp32(Z + alpha))
+ * (key_bits = 16, the pages' form) or four passes over fp32 keys
+ * (key_bits = 32).  Centring: fp64 sum in expert order / E, subtracted in
+ * fp64, rounded to fp32.
+ *
+ *  logits       [N,E] fp32.
+ *  beta_in      [E] fp32 or NULL: only used when alpha is NULL, to compute
+ *               alpha = -(B_(K+1)) with B = Z + beta_in (as moe_route).
+ *  alpha        [N] fp32 token bias or NULL.
+ *  beta_out     [E] fp32 out: centred bias.
+ *  quantile_out [E] fp32 out or NULL: the raw quantiles Q_r (beta_raw = -Q).
+ *  workspace    device scratch of at least moe_eqb_workspace_bytes(...),
+ *               256-byte aligned.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, WORKSPACE_TOO_SMALL, HIP.
+ */
+size_t moe_eqb_workspace_bytes(int64_t N, int32_t E, int32_t K, int32_t key_bits);
+moe_status_t moe_eqb_bias(const float* logits, const float* beta_in,
+                          const float* alpha, int64_t N, int32_t E, int32_t K,
+                          int32_t key_bits, float* beta_out, float* quantile_out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Problem description of moe_forward. */
+typedef struct {
+  int64_t N;          /* tokens */
+  int32_t d;          /* model width */
+  int32_t E;          /* routed experts */
+  int32_t K;          /* experts per token */
+  int32_t h;          /* routed expert hidden width */
+  int32_t n_shared;   /* 0 or 1 always-on shared expert */
+  int32_t h_shared;   /* shared expert hidden width */
+  uint32_t flags;     /* MOE_RECOMPUTE_BIAS | MOE_KEY32 */
+  const float* logit_offset; /* [E] fp32 or NULL: added to Z before the bias
+                                (an input-side knob, not part of the method) */
+  const float* logits_in;    /* [N,E] fp32 or NULL: use these logits instead
+                                of computing x W_r^T */
+} moe_problem_t;
+
+/* Weights, all bfloat16 bits, row-major, 16-byte aligned.  Shapes follow
+ * [K1D] "Routing" (SwiGLU expert: two d->h projections, SiLU(gate)*up, then
+ * h->d, no biases). */
+typedef struct {
+  const uint16_t* w_router;  /* [E,d]  (may be NULL when logits_in is set) */
+  const uint16_t* w_gate;    /* [E,h,d] */
+  const uint16_t* w_up;      /* [E,h,d] */
+  const uint16_t* w_down;    /* [E,d,h] */
+  const uint16_t* ws_gate;   /* [n_shared,hs,d] */
+  const uint16_t* ws_up;     /* [n_shared,hs,d] */
+  const uint16_t* ws_down;   /* [n_shared,d,hs] */
+} moe_weights_t;
+
+/* Optional outputs of moe_forward; every field may be NULL. */
+typedef struct {
+  float* logits;          /* [N,E] Z (after logit_offset) */
+  int32_t* topk_ids;      /* [N,K] final selection */
+  float* topk_weights;    /* [N,K] */
+  float* alpha;           /* [N] token bias of the first routing (beta_in) */
+  float* margin;          /* [N] selection margin of the final routing */
+  float* beta_out;        /* [E] centred bias (MOE_RECOMPUTE_BIAS only) */
+  float* quantile_out;    /* [E] raw quantiles (MOE_RECOMPUTE_BIAS only) */
+  int32_t* counts_before; /* [E] loads of the beta_in routing */
+  int32_t* counts;        /* [E] loads of the final routing */
+  int32_t* offsets;       /* [E+1] exclusive sums of counts */
+  int32_t* sorted_src;    /* [N*K] pair index t*K+k, grouped by expert, t ascending */
+  int32_t* src_pos;       /* [N,K] inverse of sorted_src */
+} moe_aux_t;
+
+/*
+ * moe_forward - the MoE layer forward pass, [KPT] §6.1:
+ *   y_t = f_shared(x_t) + sum_{e in I_t} S_{t,e} f_e(x_t)
+ * with Z = x W_r^T (+ logit_offset) in fp32, I_t the top-K of Z + beta,
+ * S = sigmoid(Z).  With MOE_RECOMPUTE_BIAS the batch is first routed with
+ * beta_in, one exact quantile update computes the new bias over the batch
+ * ([KPT] §7.1-§7.3) and the batch is routed again with it (the update the
+ * running example of [KPT] §7.2 performs).  Tokens are grouped by expert with
+ * a stable counting sort; the expert MLPs run as grouped bf16 MFMA GEMMs
+ * with fp32 accumulation; the hidden activations and the per-pair expert
+ * outputs are held in bf16; the combine accumulates in fp32.
+ *
+ *  p        problem (sizes, flags, optional logits_in / logit_offset).
+ *  w        weights (see moe_weights_t).
+ *  x        [N,d] bf16 bits.
+ *  beta_in  [E] fp32 or NULL (zero).
+ *  y        [N,d] bf16 bits out.
+ *  aux      optional outputs, or NULL.
+ *  workspace/workspace_bytes: scratch of at least
+ *           moe_forward_workspace_bytes(p), 256-byte aligned.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, WORKSPACE_TOO_SMALL, HIP.
+ */
+size_t moe_forward_workspace_bytes(const moe_problem_t* p);
+moe_status_t moe_forward(const moe_problem_t* p, const moe_weights_t* w,
+                         const uint16_t* x, const float* beta_in, uint16_t* y,
+                         moe_aux_t* aux, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Status name, e.g. "MOE_ERR_INVALID_ARGUMENT". */
+const char* moe_status_string(moe_status_t s);
+/* Detail of the last failed call on this thread ("" if none). */
+const char* moe_last_error_message(void);
+/* Version of this ABI (incremented on any incompatible change). */
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,183 @@
+"""MI355X (gfx950) sigmoid top-K routed MoE layer with Exact Quantile Balancing.
+
+Thin binding over the C ABI of libmoe_mi355x.so (include/moe_mi355x.h):
+``route``, ``eqb_bias`` and ``forward`` marshal torch tensors (device memory
+and the current stream) into the library calls; every step of the layer runs
+in the library's HIP kernels.  There is no CPU fallback: a missing library or
+a non-GPU tensor raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+from typing import Optional
+
+from . import _lib
+from ._lib import MOE_KEY32, MOE_RECOMPUTE_BIAS, MoeAux, MoeError, MoeProblem, MoeWeights
+
+__all__ = ["route", "eqb_bias", "eqb_workspace_bytes", "forward", "forward_workspace_bytes",
+           "ExpertWeights", "MoeError", "load_library"]
+
+AUX_FIELDS = [f for f, _ in MoeAux._fields_]
+
+
+def load_library():
+    return _lib.load()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t, name, dtype=None, shape=None):
+    torch = _torch()
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU torch tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _bf16():
+    torch = _torch()
+    return (torch.bfloat16, torch.uint16, torch.int16)
+
+
+def route(logits, K: int, beta=None, stream=None):
+    """Top-K selection on logits + beta, sigmoid weights of the unbiased
+    logits.  Returns (ids int32 [N,K], weights fp32 [N,K], alpha fp32 [N],
+    margin fp32 [N])."""
+    torch = _torch()
+    lib = _lib.load()
+    logits = _dev(logits, "logits", torch.float32)
+    N, E = logits.shape
+    beta = _dev(beta, "beta", torch.float32, (E,))
+    dev = logits.device
+    ids = torch.empty((N, K), dtype=torch.int32, device=dev)
+    w = torch.empty((N, K), dtype=torch.float32, device=dev)
+    alpha = torch.empty((N,), dtype=torch.float32, device=dev)
+    margin = torch.empty((N,), dtype=torch.float32, device=dev)
+    _lib.check(lib.moe_route(_ptr(logits), _ptr(beta), N, E, K, _ptr(ids), _ptr(w),
+                             _ptr(alpha), _ptr(margin), _stream(stream)))
+    return ids, w, alpha, margin
+
+
+def eqb_workspace_bytes(N: int, E: int, K: int, key_bits: int = 16) -> int:
+    return int(_lib.load().moe_eqb_workspace_bytes(N, E, K, key_bits))
+
+
+def eqb_bias(logits, K: int, beta_in=None, alpha=None, key_bits: int = 16,
+             workspace=None, stream=None):
+    """One exact Quantile Balancing update.  Returns (beta_out [E],
+    quantile [E]) in fp32."""
+    torch = _torch()
+    lib = _lib.load()
+    logits = _dev(logits, "logits", torch.float32)
+    N, E = logits.shape
+    beta_in = _dev(beta_in, "beta_in", torch.float32, (E,))
+    alpha = _dev(alpha, "alpha", torch.float32, (N,))
+    need = int(lib.moe_eqb_workspace_bytes(N, E, K, key_bits))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=logits.device)
+    beta_out = torch.empty((E,), dtype=torch.float32, device=logits.device)
+    q = torch.empty((E,), dtype=torch.float32, device=logits.device)
+    _lib.check(lib.moe_eqb_bias(_ptr(logits), _ptr(beta_in), _ptr(alpha), N, E, K, key_bits,
+                                _ptr(beta_out), _ptr(q), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
+    return beta_out, q
+
+
+@dataclass
+class ExpertWeights:
+    """bf16 weights of one MoE layer (torch tensors on the GPU)."""
+    w_router: object        # [E, d]
+    w_gate: object          # [E, h, d]
+    w_up: object            # [E, h, d]
+    w_down: object          # [E, d, h]
+    ws_gate: object = None  # [S, hs, d]
+    ws_up: object = None    # [S, hs, d]
+    ws_down: object = None  # [S, d, hs]
+
+
+def _problem(N, d, E, K, h, n_shared, h_shared, flags, logit_offset, logits_in):
+    return MoeProblem(N, d, E, K, h, n_shared, h_shared, flags,
+                      _ptr(logit_offset), _ptr(logits_in))
+
+
+def forward_workspace_bytes(N, d, E, K, h, n_shared=1, h_shared=None,
+                            recompute_bias=False, key_bits=16) -> int:
+    flags = (MOE_RECOMPUTE_BIAS if recompute_bias else 0) | (MOE_KEY32 if key_bits == 32 else 0)
+    p = _problem(N, d, E, K, h, n_shared, h_shared or h, flags, None, None)
+    return int(_lib.load().moe_forward_workspace_bytes(C.byref(p)))
+
+
+def forward(x, weights: ExpertWeights, K: int, beta_in=None, recompute_bias: bool = False,
+            key_bits: int = 16, logit_offset=None, logits_in=None, aux=(),
+            workspace=None, out=None, stream=None):
+    """MoE layer forward.  x: [N, d] bf16.  Returns y [N, d] bf16, or
+    (y, dict) when ``aux`` names optional outputs (see moe_aux_t)."""
+    torch = _torch()
+    lib = _lib.load()
+    x = _dev(x, "x", _bf16())
+    N, d = x.shape
+    wg = _dev(weights.w_gate, "w_gate", _bf16())
+    E, h, _ = wg.shape
+    _dev(weights.w_up, "w_up", _bf16(), (E, h, d))
+    _dev(weights.w_down, "w_down", _bf16(), (E, d, h))
+    if weights.w_router is not None:
+        _dev(weights.w_router, "w_router", _bf16(), (E, d))
+    n_shared = 0 if weights.ws_gate is None else int(weights.ws_gate.shape[0])
+    h_shared = h if n_shared == 0 else int(weights.ws_gate.shape[1])
+    if n_shared:
+        _dev(weights.ws_gate, "ws_gate", _bf16(), (n_shared, h_shared, d))
+        _dev(weights.ws_up, "ws_up", _bf16(), (n_shared, h_shared, d))
+        _dev(weights.ws_down, "ws_down", _bf16(), (n_shared, d, h_shared))
+    beta_in = _dev(beta_in, "beta_in", torch.float32, (E,))
+    logit_offset = _dev(logit_offset, "logit_offset", torch.float32, (E,))
+    logits_in = _dev(logits_in, "logits_in", torch.float32, (N, E))
+    flags = (MOE_RECOMPUTE_BIAS if recompute_bias else 0) | (MOE_KEY32 if key_bits == 32 else 0)
+    p = _problem(N, d, E, K, h, n_shared, h_shared, flags, logit_offset, logits_in)
+    need = int(lib.moe_forward_workspace_bytes(C.byref(p)))
+    if need == 0:
+        _lib.check(lib.moe_forward(C.byref(p), None, None, None, None, None, None, 0, None))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    y = out if out is not None else torch.empty((N, d), dtype=torch.bfloat16, device=x.device)
+    _dev(y, "out", _bf16(), (N, d))
+    w = MoeWeights(_ptr(weights.w_router), _ptr(wg), _ptr(weights.w_up),
+                   _ptr(weights.w_down), _ptr(weights.ws_gate), _ptr(weights.ws_up),
+                   _ptr(weights.ws_down))
+    aux_t = {}
+    shapes = {"logits": ((N, E), torch.float32), "topk_ids": ((N, K), torch.int32),
+              "topk_weights": ((N, K), torch.float32), "alpha": ((N,), torch.float32),
+              "margin": ((N,), torch.float32), "beta_out": ((E,), torch.float32),
+              "quantile_out": ((E,), torch.float32), "counts_before": ((E,), torch.int32),
+              "counts": ((E,), torch.int32), "offsets": ((E + 1,), torch.int32),
+              "sorted_src": ((N * K,), torch.int32), "src_pos": ((N, K), torch.int32)}
+    for name in aux:
+        if name not in shapes:
+            raise ValueError(f"unknown aux output {name!r}")
+        shp, dt = shapes[name]
+        aux_t[name] = torch.empty(shp, dtype=dt, device=x.device)
+    a = MoeAux(*[_ptr(aux_t.get(f)) for f in AUX_FIELDS]) if aux_t else None
+    _lib.check(lib.moe_forward(C.byref(p), C.byref(w), _ptr(x), _ptr(beta_in), _ptr(y),
+                               C.byref(a) if a is not None else None, _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream)))
+    return (y, aux_t) if aux else y

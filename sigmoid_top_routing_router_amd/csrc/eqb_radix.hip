@@ -1,0 +1,161 @@
+// Exact Quantile Balancing: the expert bias from an exact per-expert batch
+// quantile, found by radix selection.
+//
+// "Kolibri Pre-Training from Scratch" §7.1: beta_e = -Q_r(Z[:,e] + alpha),
+// r = T*K/E, then centred.  §7.3: every bfloat16 value is mapped to an
+// order-preserving 16-bit key; a 256-bin histogram of the high byte shows
+// which bin holds the wanted rank, and a second histogram of the low byte of
+// the keys inside that bin gives the exact key.  Q_m is the (m+1)-th largest
+// entry (§1).  The 32-bit variant runs the same selection over four bytes of
+// order-preserving fp32 keys.
+//
+// Per pass:
+//  * eqb_hist_kernel: a block owns 64 expert columns and a slab of rows; each
+//    lane of a wave takes one column of one row (coalesced 256-byte row
+//    segments), builds the key of fp32(Z + alpha) and counts the current byte
+//    into a padded per-column LDS histogram (stride 257 words so that the 64
+//    columns fall into different banks); the non-zero bins are then added to
+//    the global [E][256] histogram with integer atomics (order-independent,
+//    so the result is deterministic).
+//  * eqb_scan_kernel: one wave per expert scans its 256 bins from the top,
+//    finds the bin that holds the wanted rank and narrows the key prefix.
+// After the last pass eqb_centre_kernel subtracts the mean of the raw biases:
+// one thread sums them in expert order in fp64, every thread then writes
+// fp32(fp64(beta_raw) - mean).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kEqbCols = 64;
+constexpr int kEqbPad = 257;
+
+size_t eqb_hist_bytes(int E, int key_bits) {
+  return (size_t)(key_bits / 8) * (size_t)E * 256u * sizeof(uint32_t);
+}
+size_t eqb_state_bytes(int E) { return (size_t)(2 * E + 4) * sizeof(uint32_t); }
+
+template <int KB>
+__global__ __launch_bounds__(256) void eqb_hist_kernel(
+    const float* __restrict__ Z, const float* __restrict__ alpha, int64_t N, int E,
+    int pass, int64_t rows_per_block, const uint32_t* __restrict__ prefix,
+    uint32_t* __restrict__ hist) {
+  __shared__ uint32_t lh[kEqbCols * kEqbPad];
+  const int cl = threadIdx.x & (kEqbCols - 1);
+  const int rs = threadIdx.x >> 6;
+  const int e = blockIdx.x * kEqbCols + cl;
+  for (int i = threadIdx.x; i < kEqbCols * kEqbPad; i += 256) lh[i] = 0u;
+  __syncthreads();
+
+  const int shift = KB - 8 * (pass + 1);
+  const bool col_ok = e < E;
+  const uint32_t want = (pass > 0 && col_ok) ? prefix[e] : 0u;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
+  const int64_t r1 = min(N, r0 + rows_per_block);
+  if (col_ok) {
+    uint32_t* my = lh + cl * kEqbPad;
+    for (int64_t t = r0 + rs; t < r1; t += 4) {
+      const float v = Z[t * E + e] + alpha[t];
+      const uint32_t key = (KB == 16) ? bf16_order_key(f32_to_bf16_rne_bits(v))
+                                      : f32_order_key(v);
+      if (pass == 0 || (key >> (shift + 8)) == want)
+        atomicAdd(my + ((key >> shift) & 0xFFu), 1u);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kEqbCols * 256; i += 256) {
+    const int c = i >> 8, b = i & 255;
+    const int ee = blockIdx.x * kEqbCols + c;
+    const uint32_t cnt = lh[c * kEqbPad + b];
+    if (cnt != 0u && ee < E) atomicAdd(hist + (size_t)ee * 256 + b, cnt);
+  }
+}
+
+// One wave per expert.  rank0 is the wanted 1-based rank for pass 0 (r+1).
+__global__ __launch_bounds__(256) void eqb_scan_kernel(
+    const uint32_t* __restrict__ hist, uint32_t* __restrict__ prefix,
+    uint32_t* __restrict__ rank, int E, int pass, int last, int key_bits,
+    uint32_t rank0, float* __restrict__ qraw, float* __restrict__ quantile_out) {
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  const int lane = lane_id();
+  const uint4 v = reinterpret_cast<const uint4*>(hist + (size_t)e * 256)[lane];
+  const uint32_t s = v.x + v.y + v.z + v.w;
+  const uint32_t incl = wave_inclusive_sum_u32(s);
+  const uint32_t total = readlane_u32(incl, 63);
+  const uint32_t want = (pass == 0) ? rank0 : rank[e];
+  // Bins of this lane from the top: 4l+3, 4l+2, 4l+1, 4l.
+  uint32_t c = total - incl;  // entries in the bins above this lane's four
+  int found = -1;
+  uint32_t nr = 0;
+  const uint32_t bins[4] = {v.w, v.z, v.y, v.x};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (found < 0 && c < want && want <= c + bins[i]) { found = 4 * lane + 3 - i; nr = want - c; }
+    c += bins[i];
+  }
+  const uint64_t hit = ballot(found >= 0);
+  const int src = hit ? (__ffsll((unsigned long long)hit) - 1) : 0;
+  const uint32_t bin = readlane_u32((uint32_t)found, src);
+  const uint32_t new_rank = readlane_u32(nr, src);
+  if (lane == 0) {
+    const uint32_t p = ((pass == 0) ? 0u : (prefix[e] << 8)) | (bin & 0xFFu);
+    prefix[e] = p;
+    rank[e] = new_rank;
+    if (last) {
+      const float q = (key_bits == 16) ? bf16_bits_to_f32(bf16_from_order_key(p))
+                                       : f32_from_order_key(p);
+      qraw[e] = q;
+      if (quantile_out) quantile_out[e] = q;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void eqb_centre_kernel(const float* __restrict__ qraw,
+                                                         int E, float* __restrict__ beta_out) {
+  __shared__ double mean_s;
+  if (threadIdx.x == 0) {
+    double acc = 0.0;
+    for (int e = 0; e < E; ++e) acc += (double)(-qraw[e]);
+    mean_s = acc / (double)E;
+  }
+  __syncthreads();
+  const double mean = mean_s;
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    beta_out[e] = (float)((double)(-qraw[e]) - mean);
+}
+
+hipError_t launch_eqb(const float* Z, const float* alpha, int64_t N, int E, int K,
+                      int key_bits, float* beta_out, float* quantile_out,
+                      const EqbWork& w, hipStream_t stream) {
+  const int passes = key_bits / 8;
+  const int64_t r = (N * (int64_t)K) / E;
+  hipError_t err = launch_fill_u32(w.hist, 0u, eqb_hist_bytes(E, key_bits) / 4, stream);
+  if (err != hipSuccess) return err;
+  uint32_t* prefix = w.state;
+  uint32_t* rank = w.state + E;
+  const int col_groups = (E + kEqbCols - 1) / kEqbCols;
+  int64_t chunks = (1536 + col_groups - 1) / col_groups;
+  int64_t rows_per_block = (N + chunks - 1) / chunks;
+  if (rows_per_block < 256) rows_per_block = 256;
+  rows_per_block = (rows_per_block + 3) / 4 * 4;
+  chunks = (N + rows_per_block - 1) / rows_per_block;
+  const dim3 hgrid((unsigned)col_groups, (unsigned)chunks), block(256);
+  const dim3 sgrid((unsigned)((E + 3) / 4));
+  for (int p = 0; p < passes; ++p) {
+    uint32_t* hp = w.hist + (size_t)p * E * 256;
+    if (key_bits == 16)
+      hipLaunchKernelGGL(eqb_hist_kernel<16>, hgrid, block, 0, stream, Z, alpha, N, E, p,
+                         rows_per_block, prefix, hp);
+    else
+      hipLaunchKernelGGL(eqb_hist_kernel<32>, hgrid, block, 0, stream, Z, alpha, N, E, p,
+                         rows_per_block, prefix, hp);
+    hipLaunchKernelGGL(eqb_scan_kernel, sgrid, block, 0, stream, hp, prefix, rank, E, p,
+                       p == passes - 1 ? 1 : 0, key_bits, (uint32_t)(r + 1), w.qraw,
+                       quantile_out);
+  }
+  hipLaunchKernelGGL(eqb_centre_kernel, dim3(1), block, 0, stream, w.qraw, E, beta_out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

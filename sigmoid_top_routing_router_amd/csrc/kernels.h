@@ -1,0 +1,84 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+// Every launcher enqueues on `stream`, performs no allocation and no
+// host/device synchronisation, and returns the launch status.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define MOE_KMAX_INTERNAL 8
+
+namespace moe {
+
+// ---------------------------------------------------------------- routing
+hipError_t launch_route(const float* Z, const float* beta, int64_t N, int E, int K,
+                        int32_t* ids, float* S, float* alpha, float* margin,
+                        hipStream_t stream);
+
+// ---------------------------------------------------------------- EQB
+// Workspace carved by the caller (all 256-byte aligned):
+//   hist  [passes][E][256] uint32 (passes = key_bits / 8)
+//   state [2*E + 4] uint32 (per-expert key prefix and remaining rank, counter)
+//   qraw  [E] fp32 (raw quantiles)
+struct EqbWork {
+  uint32_t* hist;
+  uint32_t* state;
+  float* qraw;
+};
+size_t eqb_hist_bytes(int E, int key_bits);
+size_t eqb_state_bytes(int E);
+hipError_t launch_eqb(const float* Z, const float* alpha, int64_t N, int E, int K,
+                      int key_bits, float* beta_out, float* quantile_out,
+                      const EqbWork& w, hipStream_t stream);
+
+// ---------------------------------------------------------------- grouping
+// Stable counting sort of the (t,k) pairs by expert, plus the m-tile table of
+// the grouped GEMMs (tiles of `bm` rows per expert).
+struct PermWork {
+  uint32_t* chunk_counts;  // [n_chunks][E]
+  int32_t* counts;         // [E]
+  int32_t* offsets;        // [E+1]
+  int32_t* sorted_src;     // [N*K]
+  int32_t* src_pos;        // [N*K]
+  int32_t* tiles;          // [max_tiles][4]: expert, first row, rows, pad
+  int32_t* n_tiles;        // [1]
+};
+int perm_chunk_pairs();
+int64_t perm_num_chunks(int64_t pairs);
+int64_t perm_max_tiles(int64_t pairs, int E, int bm);
+hipError_t launch_permute(const int32_t* ids, int64_t N, int E, int K, int bm,
+                          const PermWork& w, hipStream_t stream);
+// Expert loads only (no permutation): counts[E] must be a device buffer.
+hipError_t launch_count(const int32_t* ids, int64_t pairs, int E, int32_t* counts,
+                        hipStream_t stream);
+
+// ---------------------------------------------------------------- GEMMs
+// Router logits Z[N,E] = x[N,d] W_r[E,d]^T (+ offset[E]) in fp32.
+hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w_router,
+                              const float* offset, int64_t N, int d, int E, float* Z,
+                              hipStream_t stream);
+// Grouped SwiGLU gate/up: for every m-tile of the table, H rows =
+// silu(X W_g^T) * (X W_u^T) (bf16).  When `tiles` is NULL the rows are the
+// tokens 0..N-1 of one expert (shared expert), otherwise A rows are gathered
+// through sorted_src / K.
+hipError_t launch_gateup(const uint16_t* x, const int32_t* sorted_src, int K,
+                         const int32_t* tiles, const int32_t* n_tiles, int64_t max_tiles,
+                         int64_t rows_dense, const uint16_t* w_gate,
+                         const uint16_t* w_up, int d, int h, uint16_t* H,
+                         hipStream_t stream);
+// Grouped down projection: Y rows = H rows W_d^T (bf16 out).
+hipError_t launch_down(const uint16_t* H, const int32_t* tiles, const int32_t* n_tiles,
+                       int64_t max_tiles, int64_t rows_dense, const uint16_t* w_down,
+                       int d, int h, uint16_t* Y, hipStream_t stream);
+int gemm_bm();
+
+// ---------------------------------------------------------------- combine
+// y[t] = sh[t] + sum_k S[t,k] * Y[src_pos[t,k]]  (sh may be NULL)
+hipError_t launch_combine(const uint16_t* sh, const uint16_t* Y, const float* S,
+                          const int32_t* src_pos, int64_t N, int K, int d,
+                          uint16_t* y, hipStream_t stream);
+
+// ---------------------------------------------------------------- misc
+hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,346 @@
+// C ABI of the MoE layer library: argument checks, workspace carving and the
+// launch sequence on the caller's stream.  No allocation, no host/device
+// synchronisation, no device-to-host copies.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/moe_mi355x.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status_t fail(moe_status_t s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+moe_status_t ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+moe_status_t hip_fail(hipError_t e, const char* where) {
+  return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int64_t kMaxN = int64_t(1) << 24;
+constexpr size_t kAlign = 256;
+
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Sequential carve of one workspace; sizes rounded up to 256 bytes.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <class T>
+  T* take(size_t count) {
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += up(count * sizeof(T));
+    return p;
+  }
+};
+
+moe_status_t check_route_shape(int64_t N, int32_t E, int32_t K) {
+  if (N < 1 || N > kMaxN) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "N=%lld outside [1, 2^24]", (long long)N);
+  if (K < 1 || K > MOE_MAX_K) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "K=%d outside [1, %d]", K, MOE_MAX_K);
+  if (E <= K || E > MOE_MAX_E) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "E=%d must satisfy K < E <= %d", E, MOE_MAX_E);
+  return MOE_OK;
+}
+
+// Workspace of the EQB update (histograms, selection state, raw quantiles,
+// and the token bias when it has to be computed).
+struct EqbLayout {
+  uint32_t* hist;
+  uint32_t* state;
+  float* qraw;
+  float* alpha;
+};
+EqbLayout carve_eqb(Carver& c, int64_t N, int E, int key_bits) {
+  EqbLayout l;
+  l.hist = c.take<uint32_t>(moe::eqb_hist_bytes(E, key_bits) / 4);
+  l.state = c.take<uint32_t>(moe::eqb_state_bytes(E) / 4);
+  l.qraw = c.take<float>((size_t)E);
+  l.alpha = c.take<float>((size_t)N);
+  return l;
+}
+
+struct FwdLayout {
+  float* Z;
+  int32_t* ids0;
+  float* alpha;
+  int32_t* ids;
+  float* S;
+  float* margin;
+  float* beta_new;
+  int32_t* counts_before;
+  EqbLayout eqb;
+  uint32_t* chunk_counts;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_src;
+  int32_t* src_pos;
+  int32_t* tiles;
+  int32_t* n_tiles;
+  uint16_t* H;
+  uint16_t* Hs;
+  uint16_t* Y;
+  uint16_t* sh;
+  size_t bytes;
+  int64_t max_tiles;
+};
+
+FwdLayout carve_forward(void* ws, const moe_problem_t& p) {
+  Carver c(ws);
+  FwdLayout l{};
+  const int64_t N = p.N, pairs = p.N * (int64_t)p.K;
+  const int key_bits = (p.flags & MOE_KEY32) ? 32 : 16;
+  l.Z = c.take<float>((size_t)N * p.E);
+  l.ids0 = c.take<int32_t>((size_t)pairs);
+  l.alpha = c.take<float>((size_t)N);
+  l.ids = c.take<int32_t>((size_t)pairs);
+  l.S = c.take<float>((size_t)pairs);
+  l.margin = c.take<float>((size_t)N);
+  l.beta_new = c.take<float>((size_t)p.E);
+  l.counts_before = c.take<int32_t>((size_t)p.E);
+  l.eqb = carve_eqb(c, N, p.E, key_bits);
+  l.chunk_counts = c.take<uint32_t>((size_t)moe::perm_num_chunks(pairs) * p.E);
+  l.counts = c.take<int32_t>((size_t)p.E);
+  l.offsets = c.take<int32_t>((size_t)p.E + 1);
+  l.sorted_src = c.take<int32_t>((size_t)pairs);
+  l.src_pos = c.take<int32_t>((size_t)pairs);
+  l.max_tiles = moe::perm_max_tiles(pairs, p.E, moe::gemm_bm());
+  l.tiles = c.take<int32_t>((size_t)l.max_tiles * 4);
+  l.n_tiles = c.take<int32_t>(4);
+  l.H = c.take<uint16_t>((size_t)pairs * p.h);
+  l.Y = c.take<uint16_t>((size_t)pairs * p.d);
+  if (p.n_shared > 0) {
+    l.Hs = c.take<uint16_t>((size_t)N * p.h_shared);
+    l.sh = c.take<uint16_t>((size_t)N * p.d);
+  }
+  l.bytes = c.off;
+  return l;
+}
+
+moe_status_t check_problem(const moe_problem_t* p) {
+  if (!p) return fail(MOE_ERR_INVALID_ARGUMENT, "problem is NULL");
+  moe_status_t s = check_route_shape(p->N, p->E, p->K);
+  if (s != MOE_OK) return s;
+  if (p->d < 64 || p->d > 8192 || p->d % 64)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "d=%d must be a multiple of 64 in [64, 8192]", p->d);
+  if (p->h < 32 || p->h > 4096 || p->h % 32)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "h=%d must be a multiple of 32 in [32, 4096]", p->h);
+  if (p->n_shared != 0 && p->n_shared != 1)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "n_shared=%d must be 0 or 1", p->n_shared);
+  if (p->n_shared == 1 && (p->h_shared < 32 || p->h_shared > 4096 || p->h_shared % 32))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE, "h_shared=%d must be a multiple of 32 in [32, 4096]", p->h_shared);
+  if (p->flags & ~(MOE_RECOMPUTE_BIAS | MOE_KEY32))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", p->flags);
+  if (p->logits_in && p->logit_offset)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "logit_offset applies to computed logits only; logits_in is set");
+  if (p->logits_in && !aligned(p->logits_in, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "logits_in misaligned");
+  if (p->logit_offset && !aligned(p->logit_offset, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "logit_offset misaligned");
+  return MOE_OK;
+}
+
+#define MOE_TRY_HIP(expr, where)                   \
+  do {                                             \
+    hipError_t _e = (expr);                        \
+    if (_e != hipSuccess) return hip_fail(_e, where); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return 1; }
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED_SHAPE: return "MOE_ERR_UNSUPPORTED_SHAPE";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error_message(void) { return g_err.c_str(); }
+
+moe_status_t moe_route(const float* logits, const float* beta, int64_t N, int32_t E,
+                       int32_t K, int32_t* topk_ids, float* topk_weights, float* alpha,
+                       float* margin, void* stream) {
+  moe_status_t s = check_route_shape(N, E, K);
+  if (s != MOE_OK) return s;
+  if (!logits || !topk_ids || !topk_weights)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "logits, topk_ids and topk_weights are required");
+  const void* ptrs[] = {logits, beta, topk_ids, topk_weights, alpha, margin};
+  for (const void* q : ptrs)
+    if (q && !aligned(q, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "pointer not 4-byte aligned");
+  MOE_TRY_HIP(moe::launch_route(logits, beta, N, E, K, topk_ids, topk_weights, alpha, margin,
+                                (hipStream_t)stream), "moe_route");
+  return ok();
+}
+
+size_t moe_eqb_workspace_bytes(int64_t N, int32_t E, int32_t K, int32_t key_bits) {
+  (void)K;
+  if (N < 1 || E < 1 || (key_bits != 16 && key_bits != 32)) return 0;
+  Carver c(nullptr);
+  carve_eqb(c, N, E, key_bits);
+  return c.off;
+}
+
+moe_status_t moe_eqb_bias(const float* logits, const float* beta_in, const float* alpha,
+                          int64_t N, int32_t E, int32_t K, int32_t key_bits, float* beta_out,
+                          float* quantile_out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  moe_status_t s = check_route_shape(N, E, K);
+  if (s != MOE_OK) return s;
+  if (key_bits != 16 && key_bits != 32)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "key_bits=%d must be 16 or 32", key_bits);
+  if (!logits || !beta_out) return fail(MOE_ERR_INVALID_ARGUMENT, "logits and beta_out are required");
+  const void* ptrs[] = {logits, beta_in, alpha, beta_out, quantile_out};
+  for (const void* q : ptrs)
+    if (q && !aligned(q, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "pointer not 4-byte aligned");
+  const size_t need = moe_eqb_workspace_bytes(N, E, K, key_bits);
+  if (!workspace || !aligned(workspace, kAlign))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < required %zu", workspace_bytes, need);
+  Carver c(workspace);
+  EqbLayout l = carve_eqb(c, N, E, key_bits);
+  const hipStream_t st = (hipStream_t)stream;
+  const float* a = alpha;
+  if (!a) {
+    MOE_TRY_HIP(moe::launch_route(logits, beta_in, N, E, K, nullptr, nullptr, l.alpha, nullptr, st),
+                "moe_eqb_bias: token bias");
+    a = l.alpha;
+  }
+  moe::EqbWork w{l.hist, l.state, l.qraw};
+  MOE_TRY_HIP(moe::launch_eqb(logits, a, N, E, K, key_bits, beta_out, quantile_out, w, st),
+              "moe_eqb_bias");
+  return ok();
+}
+
+size_t moe_forward_workspace_bytes(const moe_problem_t* p) {
+  if (check_problem(p) != MOE_OK) return 0;
+  return carve_forward(nullptr, *p).bytes;
+}
+
+moe_status_t moe_forward(const moe_problem_t* p, const moe_weights_t* w, const uint16_t* x,
+                         const float* beta_in, uint16_t* y, moe_aux_t* aux, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  moe_status_t s = check_problem(p);
+  if (s != MOE_OK) return s;
+  if (!w || !x || !y) return fail(MOE_ERR_INVALID_ARGUMENT, "weights, x and y are required");
+  if (!p->logits_in && !w->w_router)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "w_router is required when logits_in is NULL");
+  if (!w->w_gate || !w->w_up || !w->w_down)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "routed expert weights are required");
+  if (p->n_shared == 1 && (!w->ws_gate || !w->ws_up || !w->ws_down))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "shared expert weights are required");
+  const void* p16[] = {x, y, w->w_router, w->w_gate, w->w_up, w->w_down,
+                       w->ws_gate, w->ws_up, w->ws_down};
+  for (const void* q : p16)
+    if (q && !aligned(q, 16)) return fail(MOE_ERR_INVALID_ARGUMENT, "bf16 buffers must be 16-byte aligned");
+  if (beta_in && !aligned(beta_in, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "beta_in misaligned");
+  moe_aux_t none{};
+  const moe_aux_t& A = aux ? *aux : none;
+  const void* pa[] = {A.logits, A.topk_ids, A.topk_weights, A.alpha, A.margin, A.beta_out,
+                      A.quantile_out, A.counts_before, A.counts, A.offsets, A.sorted_src,
+                      A.src_pos};
+  for (const void* q : pa)
+    if (q && !aligned(q, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "aux buffers must be 4-byte aligned");
+  const FwdLayout need = carve_forward(nullptr, *p);
+  if (!workspace || !aligned(workspace, kAlign))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+  if (workspace_bytes < need.bytes)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < required %zu", workspace_bytes, need.bytes);
+
+  FwdLayout l = carve_forward(workspace, *p);
+  const hipStream_t st = (hipStream_t)stream;
+  const int64_t N = p->N;
+  const int E = p->E, K = p->K, d = p->d, h = p->h;
+  const int key_bits = (p->flags & MOE_KEY32) ? 32 : 16;
+  const bool recompute = (p->flags & MOE_RECOMPUTE_BIAS) != 0;
+
+  // a1: router logits
+  const float* Z;
+  if (p->logits_in) {
+    Z = p->logits_in;
+    if (A.logits)
+      MOE_TRY_HIP(hipMemcpyAsync(A.logits, Z, (size_t)N * E * 4, hipMemcpyDeviceToDevice, st),
+                  "moe_forward: logits copy");
+  } else {
+    float* zout = A.logits ? A.logits : l.Z;
+    MOE_TRY_HIP(moe::launch_router_gemm(x, w->w_router, p->logit_offset, N, d, E, zout, st),
+                "moe_forward: router GEMM");
+    Z = zout;
+  }
+
+  // a2-a4: selection, token bias, optional exact quantile update, re-route
+  int32_t* ids = A.topk_ids ? A.topk_ids : l.ids;
+  float* S = A.topk_weights ? A.topk_weights : l.S;
+  float* alpha = A.alpha ? A.alpha : l.alpha;
+  float* margin = A.margin ? A.margin : l.margin;
+  if (recompute) {
+    MOE_TRY_HIP(moe::launch_route(Z, beta_in, N, E, K, l.ids0, nullptr, alpha, nullptr, st),
+                "moe_forward: first routing");
+    if (A.counts_before)
+      MOE_TRY_HIP(moe::launch_count(l.ids0, N * K, E, A.counts_before, st), "moe_forward: loads");
+    float* beta_new = A.beta_out ? A.beta_out : l.beta_new;
+    moe::EqbWork ew{l.eqb.hist, l.eqb.state, l.eqb.qraw};
+    MOE_TRY_HIP(moe::launch_eqb(Z, alpha, N, E, K, key_bits, beta_new, A.quantile_out, ew, st),
+                "moe_forward: quantile update");
+    MOE_TRY_HIP(moe::launch_route(Z, beta_new, N, E, K, ids, S, nullptr, margin, st),
+                "moe_forward: routing");
+  } else {
+    MOE_TRY_HIP(moe::launch_route(Z, beta_in, N, E, K, ids, S, alpha, margin, st),
+                "moe_forward: routing");
+    if (A.counts_before)
+      MOE_TRY_HIP(moe::launch_count(ids, N * K, E, A.counts_before, st), "moe_forward: loads");
+  }
+
+  // a5: stable grouping by expert and the m-tile table
+  moe::PermWork pw;
+  pw.chunk_counts = l.chunk_counts;
+  pw.counts = A.counts ? A.counts : l.counts;
+  pw.offsets = A.offsets ? A.offsets : l.offsets;
+  pw.sorted_src = A.sorted_src ? A.sorted_src : l.sorted_src;
+  pw.src_pos = A.src_pos ? A.src_pos : l.src_pos;
+  pw.tiles = l.tiles;
+  pw.n_tiles = l.n_tiles;
+  MOE_TRY_HIP(moe::launch_permute(ids, N, E, K, moe::gemm_bm(), pw, st), "moe_forward: grouping");
+
+  // a6-a8: routed experts (gather fused into the gate/up A loads)
+  MOE_TRY_HIP(moe::launch_gateup(x, pw.sorted_src, K, pw.tiles, pw.n_tiles, l.max_tiles, 0,
+                                 w->w_gate, w->w_up, d, h, l.H, st), "moe_forward: gate/up");
+  MOE_TRY_HIP(moe::launch_down(l.H, pw.tiles, pw.n_tiles, l.max_tiles, 0, w->w_down, d, h, l.Y, st),
+              "moe_forward: down");
+  // a9: shared expert over all tokens
+  if (p->n_shared == 1) {
+    MOE_TRY_HIP(moe::launch_gateup(x, nullptr, 1, nullptr, nullptr, 0, N, w->ws_gate, w->ws_up, d,
+                                   p->h_shared, l.Hs, st), "moe_forward: shared gate/up");
+    MOE_TRY_HIP(moe::launch_down(l.Hs, nullptr, nullptr, 0, N, w->ws_down, d, p->h_shared, l.sh, st),
+                "moe_forward: shared down");
+  }
+  // a10: weighted combine
+  MOE_TRY_HIP(moe::launch_combine(p->n_shared == 1 ? l.sh : nullptr, l.Y, S, pw.src_pos, N, K, d, y, st),
+              "moe_forward: combine");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,202 @@
+// Grouping of the (token, slot) pairs by expert: a stable counting sort.
+//
+// The routing equations of "Kolibri Pre-Training from Scratch" §6.1 send
+// token t to the experts I_t; the German guide "Kolibri 1 im Detail"
+// (section on routing) notes that tokens have to be brought to their experts
+// with no per-expert capacity.  On one GPU that is a permutation of the N*K
+// pairs into contiguous per-expert segments, tokens ascending within each
+// segment (pair index t*K+k; the K experts of a token are distinct, so this
+// is also the order of t).
+//
+// Kernels (all integer work, bit-exact and deterministic):
+//  1. perm_count_kernel: one wave per chunk of kChunk consecutive pairs
+//     counts the experts of its chunk in LDS -> chunk_counts[e][chunk].
+//  2. perm_scan_kernel: one block per expert turns its row of chunk counts
+//     into exclusive chunk bases and the expert total.
+//  3. perm_tiles_kernel: one block; exclusive sums of the counts (offsets)
+//     and the table of m-tiles (expert, first row, rows) that drives the
+//     grouped GEMMs from device memory.
+//  4. perm_scatter_kernel: one wave per chunk walks its pairs in order, 64 at
+//     a time; lanes holding the same expert are found with nine ballots over
+//     the bits of the expert id, so the rank among them is a popcount and the
+//     lowest such lane advances the expert's running position in LDS.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kChunk = 1024;        // pairs per chunk (one wave)
+constexpr int kPermWaves = 4;       // waves per block in the chunk kernels
+constexpr int kMaxE = 384;
+
+int perm_chunk_pairs() { return kChunk; }
+int64_t perm_num_chunks(int64_t pairs) { return (pairs + kChunk - 1) / kChunk; }
+int64_t perm_max_tiles(int64_t pairs, int E, int bm) { return pairs / bm + E; }
+
+__global__ __launch_bounds__(256) void perm_count_kernel(
+    const int32_t* __restrict__ ids, int64_t pairs, int E, int64_t n_chunks,
+    uint32_t* __restrict__ chunk_counts) {
+  __shared__ uint32_t cnt[kPermWaves][kMaxE];
+  const int w = threadIdx.x >> 6, lane = lane_id();
+  const int64_t chunk = (int64_t)blockIdx.x * kPermWaves + w;
+  for (int e = lane; e < E; e += kWave) cnt[w][e] = 0u;
+  __syncthreads();
+  if (chunk < n_chunks) {
+    const int64_t i0 = chunk * kChunk;
+    for (int j = lane; j < kChunk; j += kWave) {
+      const int64_t i = i0 + j;
+      if (i < pairs) atomicAdd(&cnt[w][ids[i]], 1u);
+    }
+  }
+  __syncthreads();
+  if (chunk < n_chunks)
+    for (int e = lane; e < E; e += kWave) chunk_counts[(size_t)e * n_chunks + chunk] = cnt[w][e];
+}
+
+// One block (256 threads) per expert: exclusive scan over the chunks.
+__global__ __launch_bounds__(256) void perm_scan_kernel(uint32_t* __restrict__ chunk_counts,
+                                                        int64_t n_chunks,
+                                                        int32_t* __restrict__ counts) {
+  __shared__ uint32_t wsum[4];
+  const int e = blockIdx.x;
+  const int w = threadIdx.x >> 6, lane = lane_id();
+  uint32_t* row = chunk_counts + (size_t)e * n_chunks;
+  uint32_t carry = 0u;
+  for (int64_t c0 = 0; c0 < n_chunks; c0 += 256) {
+    const int64_t c = c0 + threadIdx.x;
+    const uint32_t v = (c < n_chunks) ? row[c] : 0u;
+    const uint32_t incl = wave_inclusive_sum_u32(v);
+    if (lane == kWave - 1) wsum[w] = incl;
+    __syncthreads();
+    uint32_t before = carry;
+    for (int i = 0; i < w; ++i) before += wsum[i];
+    if (c < n_chunks) row[c] = before + incl - v;
+    const uint32_t block_total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+    carry += block_total;
+  }
+  if (threadIdx.x == 0) counts[e] = (int32_t)carry;
+}
+
+// One block: offsets (exclusive sums of counts) and the m-tile table.
+__global__ __launch_bounds__(256) void perm_tiles_kernel(const int32_t* __restrict__ counts,
+                                                         int E, int bm,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ tiles,
+                                                         int32_t* __restrict__ n_tiles) {
+  __shared__ int32_t s_cnt[kMaxE];
+  __shared__ int32_t s_tile[kMaxE];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    s_cnt[e] = counts[e];
+    s_tile[e] = (counts[e] + bm - 1) / bm;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t off = 0, toff = 0;
+    for (int e = 0; e < E; ++e) {
+      const int32_t c = s_cnt[e], t = s_tile[e];
+      s_cnt[e] = off;
+      s_tile[e] = toff;
+      off += c;
+      toff += t;
+    }
+    offsets[E] = off;
+    *n_tiles = toff;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const int32_t off = s_cnt[e];
+    offsets[e] = off;
+    const int32_t c = counts[e];
+    int32_t t = s_tile[e];
+    for (int32_t r = 0; r < c; r += bm, ++t) {
+      int32_t* ent = tiles + 4 * (size_t)t;
+      ent[0] = e;
+      ent[1] = off + r;
+      ent[2] = min(bm, c - r);
+      ent[3] = r;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void perm_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t pairs, int E, int64_t n_chunks,
+    const uint32_t* __restrict__ chunk_base, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_src, int32_t* __restrict__ src_pos) {
+  __shared__ uint32_t pos[kPermWaves][kMaxE];
+  const int w = threadIdx.x >> 6, lane = lane_id();
+  const int64_t chunk = (int64_t)blockIdx.x * kPermWaves + w;
+  if (chunk >= n_chunks) return;  // per-wave exit: no block barrier below
+  for (int e = lane; e < E; e += kWave)
+    pos[w][e] = (uint32_t)offsets[e] + chunk_base[(size_t)e * n_chunks + chunk];
+  __builtin_amdgcn_wave_barrier();
+  const int64_t i0 = chunk * kChunk;
+  for (int j = 0; j < kChunk; j += kWave) {
+    const int64_t i = i0 + j + lane;
+    const bool ok = i < pairs;
+    const uint32_t e = ok ? (uint32_t)ids[i] : 0u;
+    uint64_t mask = ballot(ok);
+    if (mask == 0ull) break;
+#pragma unroll
+    for (int b = 0; b < 9; ++b) {
+      const bool bit = (e >> b) & 1u;
+      const uint64_t bb = ballot(bit);
+      mask &= bit ? bb : ~bb;
+    }
+    const uint64_t lower = mask & lanemask_lt();
+    uint32_t dst = 0;
+    if (ok) {
+      dst = pos[w][e] + (uint32_t)__popcll(lower);
+      sorted_src[dst] = (int32_t)i;
+      src_pos[i] = (int32_t)dst;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (ok && lower == 0ull) pos[w][e] += (uint32_t)__popcll(mask);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+__global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ ids,
+                                                    int64_t pairs, int E,
+                                                    int32_t* __restrict__ counts) {
+  __shared__ uint32_t cnt[kMaxE];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0u;
+  __syncthreads();
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < pairs; i += stride)
+    atomicAdd(&cnt[ids[i]], 1u);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    if (cnt[e]) atomicAdd((uint32_t*)counts + e, cnt[e]);
+}
+
+hipError_t launch_permute(const int32_t* ids, int64_t N, int E, int K, int bm,
+                          const PermWork& w, hipStream_t stream) {
+  const int64_t pairs = N * (int64_t)K;
+  const int64_t n_chunks = perm_num_chunks(pairs);
+  const dim3 block(256);
+  const dim3 cgrid((unsigned)((n_chunks + kPermWaves - 1) / kPermWaves));
+  hipLaunchKernelGGL(perm_count_kernel, cgrid, block, 0, stream, ids, pairs, E, n_chunks,
+                     w.chunk_counts);
+  hipLaunchKernelGGL(perm_scan_kernel, dim3((unsigned)E), block, 0, stream, w.chunk_counts,
+                     n_chunks, w.counts);
+  hipLaunchKernelGGL(perm_tiles_kernel, dim3(1), block, 0, stream, w.counts, E, bm, w.offsets,
+                     w.tiles, w.n_tiles);
+  hipLaunchKernelGGL(perm_scatter_kernel, cgrid, block, 0, stream, ids, pairs, E, n_chunks,
+                     w.chunk_counts, w.offsets, w.sorted_src, w.src_pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_count(const int32_t* ids, int64_t pairs, int E, int32_t* counts,
+                        hipStream_t stream) {
+  hipError_t err = launch_fill_u32((uint32_t*)counts, 0u, (size_t)E, stream);
+  if (err != hipSuccess) return err;
+  int64_t blocks = (pairs + 4095) / 4096;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(count_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, ids, pairs, E,
+                     counts);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,141 @@
+"""The C ABI library on the CPU: it loads, exports every entry point the header
+declares, sizes workspaces, and rejects bad arguments before any HIP call."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+LIB = os.path.join(ROOT, "sigmoid_top_routing_router_amd", "libmoe_mi355x.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from sigmoid_top_routing_router_amd import _lib
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert "moe_forward" in names and "moe_route" in names and "moe_eqb_bias" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    from sigmoid_top_routing_router_amd import _lib
+    assert sorted(_lib.EXPORTED) == names
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.moe_abi_version() == 1
+    assert lib.moe_status_string(0) == b"MOE_OK"
+    assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """ctypes mirrors of the header's structs agree with the C compiler."""
+    import shutil
+    import subprocess
+    from sigmoid_top_routing_router_amd._lib import MoeAux, MoeProblem, MoeWeights
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    prog = tmp_path / "layout.c"
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', 'int main(void){']
+    for st, cls in (("moe_problem_t", MoeProblem), ("moe_weights_t", MoeWeights),
+                    ("moe_aux_t", MoeAux)):
+        lines.append(f'printf("{st} %zu\\n", sizeof({st}));')
+        for f, _ in cls._fields_:
+            lines.append(f'printf("{st}.{f} %zu\\n", offsetof({st}, {f}));')
+    lines.append('return 0;}')
+    prog.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run([cc, str(prog), "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                  check=True).stdout.splitlines())
+    for st, cls in (("moe_problem_t", MoeProblem), ("moe_weights_t", MoeWeights),
+                    ("moe_aux_t", MoeAux)):
+        assert int(got[st]) == C.sizeof(cls), st
+        for f, _ in cls._fields_:
+            assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, (st, f)
+
+
+def _problem(**kw):
+    from sigmoid_top_routing_router_amd._lib import MoeProblem
+    base = dict(N=16384, d=2560, E=384, K=6, h=512, n_shared=1, h_shared=512, flags=1,
+                logit_offset=None, logits_in=None)
+    base.update(kw)
+    return MoeProblem(**base)
+
+
+def test_forward_workspace_sizes(lib):
+    p = _problem()
+    b = lib.moe_forward_workspace_bytes(C.byref(p))
+    pairs = 16384 * 6
+    # at least H and the per-pair expert outputs in bf16 plus the logits
+    assert b >= pairs * (512 + 2560) * 2 + 16384 * 384 * 4
+    assert b < 2 * (pairs * (512 + 2560) * 2 + 16384 * 384 * 4 + 16384 * (512 + 2560) * 2)
+    for bad in (dict(K=0), dict(K=9), dict(E=6), dict(E=385), dict(d=100), dict(h=48),
+                dict(n_shared=2), dict(N=0), dict(flags=8)):
+        assert lib.moe_forward_workspace_bytes(C.byref(_problem(**bad))) == 0, bad
+
+
+def test_eqb_workspace_sizes(lib):
+    b16 = lib.moe_eqb_workspace_bytes(65536, 384, 6, 16)
+    b32 = lib.moe_eqb_workspace_bytes(65536, 384, 6, 32)
+    assert b16 >= 2 * 384 * 256 * 4 and b32 >= 4 * 384 * 256 * 4 and b32 > b16
+    assert lib.moe_eqb_workspace_bytes(65536, 384, 6, 8) == 0
+
+
+@pytest.mark.parametrize("N,E,K,status", [(0, 384, 6, 2), (10, 384, 0, 2), (10, 384, 9, 2),
+                                          (10, 6, 6, 2), (10, 385, 6, 2)])
+def test_route_rejects_shapes_without_gpu(lib, N, E, K, status):
+    buf = C.create_string_buffer(64)
+    p = C.cast(buf, C.c_void_p)
+    assert lib.moe_route(p, None, N, E, K, p, p, None, None, None) == status
+    assert lib.moe_last_error_message() != b""
+
+
+def test_route_rejects_null_and_misaligned(lib):
+    buf = C.create_string_buffer(64)
+    p = C.cast(buf, C.c_void_p).value
+    assert lib.moe_route(None, None, 4, 8, 2, p, p, None, None, None) == 1
+    assert lib.moe_route(p + 1, None, 4, 8, 2, p, p, None, None, None) == 1
+
+
+def test_eqb_rejects_bad_arguments(lib):
+    buf = C.create_string_buffer(1024)
+    p = C.cast(buf, C.c_void_p).value
+    assert lib.moe_eqb_bias(p, None, None, 4, 8, 2, 12, p, None, p, 1 << 20, None) == 1
+    # too small workspace
+    assert lib.moe_eqb_bias(p, None, None, 4, 8, 2, 16, p, None, p & ~255 or p, 16, None) in (1, 3)
+
+
+def test_forward_rejects_bad_arguments(lib):
+    from sigmoid_top_routing_router_amd._lib import MoeWeights
+    buf = C.create_string_buffer(4096)
+    p16 = (C.cast(buf, C.c_void_p).value + 15) // 16 * 16
+    w = MoeWeights(p16, p16, p16, p16, p16, p16, p16)
+    prob = _problem(N=4, d=64, E=4, K=2, h=32, h_shared=32)
+    # NULL x
+    assert lib.moe_forward(C.byref(prob), C.byref(w), None, None, p16, None, p16, 1 << 30, None) == 1
+    # misaligned weights
+    w2 = MoeWeights(p16 + 2, p16, p16, p16, p16, p16, p16)
+    assert lib.moe_forward(C.byref(prob), C.byref(w2), p16, None, p16, None, p16, 1 << 30, None) == 1
+    # offset together with logits_in
+    prob2 = _problem(N=4, d=64, E=4, K=2, h=32, h_shared=32, logit_offset=p16, logits_in=p16)
+    assert lib.moe_forward(C.byref(prob2), C.byref(w), p16, None, p16, None, p16, 1 << 30, None) == 1
+    # workspace too small (no HIP call made: the check comes first)
+    ws = (p16 + 255) // 256 * 256
+    assert lib.moe_forward(C.byref(prob), C.byref(w), p16, None, p16, None, ws, 64, None) == 3
+    # unsupported shape
+    prob3 = _problem(N=4, d=96, E=4, K=2, h=32, h_shared=32)
+    assert lib.moe_forward(C.byref(prob3), C.byref(w), p16, None, p16, None, ws, 1 << 30, None) == 2

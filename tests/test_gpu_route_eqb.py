@@ -1,0 +1,150 @@
+"""GPU parity of moe_route and moe_eqb_bias against the oracle on identical
+logits: selections, token biases, margins, quantiles and biases bit-exact;
+sigmoid weights within 1e-6 relative."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+from synth import make_bias, make_logits
+from tests.gpu_util import S_RTOL, bits_equal, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "toy_routing_eqb.json")
+
+
+@pytest.fixture(scope="module")
+def M():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sigmoid_top_routing_router_amd as M
+    M.load_library()
+    return M
+
+
+def _route_case(M, Z, beta, K):
+    ids, S, alpha, margin = M.route(dev(Z), K, dev(beta))
+    ids, S, alpha, margin = host(ids), host(S), host(alpha), host(margin)
+    ri, ra, rm = O.route(Z, beta, K)
+    rs = O.mixture_weights(Z, ri)
+    assert np.array_equal(ids, ri), f"ids differ in {np.sum(np.any(ids != ri, axis=1))} rows"
+    assert bits_equal(alpha, ra)
+    assert bits_equal(margin, rm)
+    err = np.max(np.abs(S.astype(np.float64) - rs) / np.abs(rs))
+    assert err <= S_RTOL, err
+    return ids
+
+
+ROUTE_CASES = [
+    # seed, N, E, K, tie_fraction, with_beta
+    (101, 1, 5, 2, 0.0, False),
+    (102, 7, 9, 8, 0.5, True),
+    (103, 1000, 384, 6, 0.0, True),
+    (104, 1000, 384, 6, 0.8, True),
+    (105, 4096, 128, 8, 0.0, True),
+    (106, 333, 64, 8, 0.3, True),
+    (107, 257, 100, 3, 0.9, True),
+    (108, 129, 383, 1, 0.2, False),
+    (109, 64, 65, 4, 0.0, True),
+]
+
+
+@pytest.mark.parametrize("seed,N,E,K,ties,with_beta", ROUTE_CASES)
+def test_route_parity(M, seed, N, E, K, ties, with_beta):
+    say("route", seed, N, E, K, ties, with_beta)
+    Z = make_logits(seed, N, E, 1.0, tie_fraction=ties)
+    beta = make_bias(seed + 1, E, 0.3 if ties == 0 else 0.25) if with_beta else None
+    if beta is not None and ties > 0:
+        beta = (np.round(beta * 8) / 8).astype(np.float32)
+    _route_case(M, Z, beta, K)
+
+
+def test_route_parity_full_size_skewed(M):
+    """N=65536, E=384, K=6 at the launch size of the benchmark."""
+    say("route full 65536x384")
+    Z = make_logits(111, 65536, 384, 0.6)
+    beta = make_bias(112, 384, 0.1)
+    _route_case(M, Z, beta, 6)
+
+
+def test_route_printed_toy_logits(M):
+    g = json.load(open(GOLD))
+    Z = np.array(g["logits"]["Z"], np.float32)
+    say("route toy")
+    ids = _route_case(M, Z, None, 2)
+    assert [sorted(r) for r in ids.tolist()] == g["logits"]["top2_with_beta0"]
+    beta = np.array(g["centring"]["beta"], np.float32)
+    ids = _route_case(M, Z, beta, 2)
+    assert [sorted(r) for r in ids.tolist()] == g["reroute"]["top2_sets"]
+
+
+def test_route_is_deterministic(M):
+    say("route determinism")
+    Z = make_logits(121, 5000, 384, 1.0, tie_fraction=0.5)
+    a = [host(t) for t in M.route(dev(Z), 6, None)]
+    b = [host(t) for t in M.route(dev(Z), 6, None)]
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+# ---------------------------------------------------------------- EQB
+def _eqb_case(M, Z, beta_in, K, key_bits, give_alpha):
+    _, alpha, _ = O.route(Z, beta_in, K)
+    bo, q = M.eqb_bias(dev(Z), K, beta_in=dev(beta_in),
+                       alpha=dev(alpha) if give_alpha else None, key_bits=key_bits)
+    bo, q = host(bo), host(q)
+    rb, rq, _ = O.eqb_expert_bias(Z, alpha, K, key_bits)
+    assert bits_equal(q, rq), f"quantiles differ at {np.nonzero(q != rq)[0][:10]}"
+    assert bits_equal(bo, rb)
+    return bo, q
+
+
+EQB_CASES = [
+    # seed, N, E, K, ties
+    (201, 40, 8, 2, 0.0),
+    (202, 1000, 384, 6, 0.0),
+    (203, 1000, 384, 6, 0.9),
+    (204, 4096, 128, 8, 0.3),
+    (205, 777, 100, 5, 0.5),
+    (206, 64, 384, 6, 0.0),
+]
+
+
+@pytest.mark.parametrize("key_bits", [16, 32])
+@pytest.mark.parametrize("give_alpha", [True, False])
+@pytest.mark.parametrize("seed,N,E,K,ties", EQB_CASES)
+def test_eqb_parity(M, seed, N, E, K, ties, key_bits, give_alpha):
+    say("eqb", seed, N, E, K, ties, key_bits, give_alpha)
+    Z = make_logits(seed, N, E, 1.0, tie_fraction=ties)
+    beta = make_bias(seed + 1, E, 0.1)
+    _eqb_case(M, Z, beta, K, key_bits, give_alpha)
+
+
+@pytest.mark.parametrize("key_bits", [16, 32])
+def test_eqb_parity_full_size(M, key_bits):
+    """N=65536, E=384, K=6 (r = 1024), with a Zipf-like skew in the logits."""
+    say("eqb full", key_bits)
+    Z = make_logits(211, 65536, 384, 0.6)
+    p = np.arange(1, 385, dtype=np.float64) ** -1.2
+    Z = (Z + (0.5 * np.log(p / p.sum())).astype(np.float32)[None, :]).astype(np.float32)
+    beta = make_bias(212, 384, 0.1)
+    bo, q = _eqb_case(M, Z, beta, 6, key_bits, give_alpha=False)
+    # exactness invariant on the keys: #{u > Q} <= r < #{u >= Q}
+    _, alpha, _ = O.route(Z, beta, 6)
+    u = O.eqb_keys_values((Z + alpha[:, None]).astype(np.float32), key_bits)
+    r = 65536 * 6 // 384
+    assert ((u > q[None, :]).sum(0) <= r).all() and ((u >= q[None, :]).sum(0) > r).all()
+
+
+@pytest.mark.parametrize("key_bits", [16, 32])
+def test_eqb_printed_toy(M, key_bits):
+    g = json.load(open(GOLD))
+    Z = np.array(g["logits"]["Z"], np.float32)
+    say("eqb toy", key_bits)
+    bo, q = _eqb_case(M, Z, None, 2, key_bits, give_alpha=False)
+    assert (-q).tolist() == g["expert_bias"]["beta_raw"]
+    assert bo.tolist() == g["centring"]["beta"]
