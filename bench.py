@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE layer forward pass on one MI355X.
+
+One step = one call of moe_forward over a resident batch: router logits,
+selection, one exact quantile update of the expert bias and re-routing
+(when the workload asks for it), grouping by expert, routed and shared
+SwiGLU experts and the weighted combine.  The default workload is the
+Kolibri-shaped prefill batch (N=16384 tokens, d=2560, E=384, K=6, hidden
+512, one shared expert, EQB update on).
+
+Prints one JSON line.  `value` is tokens per second over exactly --steps
+timed steps (inputs already in HBM, bracketed by device synchronisation).
+The `roofline` entry covers the dominant kernel (the routed gate/up GEMM),
+timed with HIP events on the library's stream during the same timed steps;
+`cpu_baseline` times the CPU oracle on a bounded sample of the same layer.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+GEMM_SRC = os.path.join(ROOT, "sigmoid_top_routing_router_amd", "csrc", "grouped_gemm.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def gateup_algorithmic(cfg, counts):
+    """Flops and bytes the routed gate/up GEMM must do or move: every pair
+    row times both d x h projections; each active expert's gate and up
+    weights once, x once, H written once (bf16)."""
+    pairs = cfg.N * cfg.K
+    flops = 2.0 * pairs * (2 * cfg.h) * cfg.d
+    active = int((counts > 0).sum())
+    bytes_ = active * 2 * cfg.h * cfg.d * 2 + cfg.N * cfg.d * 2 + pairs * cfg.h * 2
+    return flops, bytes_
+
+
+def traffic_for(workload):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    ent = t.get(workload)
+    if not ent or ent.get("source_sha256_16") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, L, sample_tokens):
+    """The oracle (untuned) timed on a bounded sample: the whole layer for
+    the first `sample_tokens` tokens of the same inputs (the quantile update
+    runs over that sample batch).  Weight decoding to float is excluded."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    n = min(sample_tokens, cfg.N)
+    w = {k: O.bf16_to_f32(getattr(L, k)) for k in
+         ("w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")}
+    x = O.bf16_to_f32(L.x[:n])
+    t0 = time.perf_counter()
+    O.moe_layer(x=x, **w, beta_in=L.beta_in, K=cfg.K, recompute_bias=cfg.recompute_bias,
+                logit_offset=L.logit_offset)
+    dt = time.perf_counter() - t0
+    what = "the whole batch" if n == cfg.N else f"the first {n} of {cfg.N} tokens"
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 oracle, whole layer (all steps) on {what} of the {cfg.name} "
+                      f"workload, one run of {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill",
+                    choices=["origin", "prefill", "decode", "skewed"])
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size "
+                         "kernel for scaling hardware byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import sigmoid_top_routing_router_amd as M
+    from synth import CONFIGS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    M.load_library()
+    cfg = CONFIGS[args.workload]
+    log("workload", cfg.describe())
+    L = make_inputs(cfg)
+    log("inputs ready")
+
+    def bf16(a):
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+
+    W = M.ExpertWeights(bf16(L.w_router), bf16(L.w_gate), bf16(L.w_up), bf16(L.w_down),
+                        bf16(L.ws_gate), bf16(L.ws_up), bf16(L.ws_down))
+    x = bf16(L.x)
+    beta = torch.from_numpy(L.beta_in).cuda()
+    off = None if L.logit_offset is None else torch.from_numpy(L.logit_offset).cuda()
+    ws_bytes = M.forward_workspace_bytes(cfg.N, cfg.d, cfg.E, cfg.K, cfg.h, cfg.n_shared,
+                                         cfg.h_shared, cfg.recompute_bias)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    y = torch.empty((cfg.N, cfg.d), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        M.forward(x, W, cfg.K, beta_in=beta, recompute_bias=cfg.recompute_bias,
+                  logit_offset=off, workspace=ws, out=y)
+
+    # loads of the final routing (for the algorithmic byte count), untimed
+    _, aux = M.forward(x, W, cfg.K, beta_in=beta, recompute_bias=cfg.recompute_bias,
+                       logit_offset=off, workspace=ws, out=y, aux=("counts", "counts_before"))
+    counts = aux["counts"].cpu().numpy()
+    counts_before = aux["counts_before"].cpu().numpy()
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"calibration copy of {n} bytes done")
+    log("first call done; warmup")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("timed steps")
+
+    M.stage_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stages, calls = M.stage_times()
+    M.stage_timing(False)
+    elapsed = t1 - t0
+    ms_step = 1e3 * elapsed / args.steps
+    tokens_s = cfg.N * args.steps / elapsed
+    stage_ms = {k: v / max(calls, 1) for k, v in stages.items()}
+    log("stage ms", json.dumps({k: round(v, 4) for k, v in stage_ms.items()}))
+
+    flops, bytes_ = gateup_algorithmic(cfg, counts)
+    t_gu = stage_ms["gate_up"] * 1e-3
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = bytes_ / (PEAK_HBM_GBS * 1e9)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": bytes_ / t_gu / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / t_gu / 1e12, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_for(args.workload)
+    roof["kernel"] = "gemm_kernel<gate/up> (routed experts)"
+    roof["per_launch"] = {"flops": flops, "bytes": bytes_, "avg_ms": stage_ms["gate_up"],
+                          "tflops": flops / t_gu / 1e12, "gbs": bytes_ / t_gu / 1e9,
+                          "mfma_frac": flops / t_gu / 1e12 / PEAK_BF16_TFLOPS}
+
+    layer_flops = 2.0 * cfg.N * cfg.E * cfg.d + 2.0 * cfg.N * cfg.K * 3 * cfg.h * cfg.d \
+        + 2.0 * cfg.N * cfg.n_shared * 3 * cfg.h_shared * cfg.d
+    out = {
+        "metric": "MoE layer fwd tokens/s at E=384,K=6,d=2560 (1 GPU); % MFMA / HBM roofline",
+        "value": tokens_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded normal inputs and random-init weights of the layer shape)",
+        "config": {**cfg.describe(), "parallelism": "none (1 GPU)"},
+        "layer_tflops": layer_flops / (ms_step * 1e-3) / 1e12,
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "loads": {"max_over_mean_before": float(counts_before.max() / counts_before.mean()),
+                  "max_over_mean_after": float(counts.max() / counts.mean())},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline ...")
+        out["cpu_baseline"] = cpu_baseline(cfg, L, args.cpu_sample_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

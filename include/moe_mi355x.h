@@ -174,6 +174,23 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_weights_t* w,
                          moe_aux_t* aux, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/*
+ * Stage timing (a profiling aid).  While enabled, every moe_forward call
+ * records a HIP timing event on its stream at each stage boundary (events are
+ * created on first use and reused; no device memory is allocated).
+ * moe_stage_times waits for the recorded events, writes the summed
+ * milliseconds of each stage since the previous read into
+ * ms[MOE_NUM_STAGES], the number of recorded calls into *calls, and clears
+ * the record.  Stages: 0 router GEMM, 1 routing (selection, token bias,
+ * quantile update, re-route, loads), 2 grouping, 3 routed gate/up GEMM,
+ * 4 routed down GEMM, 5 shared gate/up GEMM, 6 shared down GEMM, 7 combine.
+ * Errors: INVALID_ARGUMENT (NULL outputs), HIP.
+ */
+#define MOE_NUM_STAGES 8
+moe_status_t moe_stage_timing(int32_t enable);
+moe_status_t moe_stage_times(double* ms, int64_t* calls);
+const char* moe_stage_name(int32_t stage);
+
 /* Status name, e.g. "MOE_ERR_INVALID_ARGUMENT". */
 const char* moe_status_string(moe_status_t s);
 /* Detail of the last failed call on this thread ("" if none). */

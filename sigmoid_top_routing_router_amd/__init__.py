@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import MOE_KEY32, MOE_RECOMPUTE_BIAS, MoeAux, MoeError, MoeProblem, MoeWeights
 
 __all__ = ["route", "eqb_bias", "eqb_workspace_bytes", "forward", "forward_workspace_bytes",
-           "ExpertWeights", "MoeError", "load_library"]
+           "ExpertWeights", "MoeError", "load_library", "stage_timing", "stage_times"]
 
 AUX_FIELDS = [f for f, _ in MoeAux._fields_]
 
@@ -181,3 +181,17 @@ def forward(x, weights: ExpertWeights, K: int, beta_in=None, recompute_bias: boo
                                C.byref(a) if a is not None else None, _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)))
     return (y, aux_t) if aux else y
+
+
+def stage_timing(enable: bool = True):
+    """Turn per-stage HIP-event timing of forward() on or off (clears it)."""
+    _lib.check(_lib.load().moe_stage_timing(1 if enable else 0))
+
+
+def stage_times():
+    """(dict stage -> summed ms since the last read, number of calls)."""
+    lib = _lib.load()
+    ms = (C.c_double * _lib.NUM_STAGES)()
+    calls = C.c_int64(0)
+    _lib.check(lib.moe_stage_times(ms, C.byref(calls)))
+    return {lib.moe_stage_name(i).decode(): ms[i] for i in range(_lib.NUM_STAGES)}, calls.value

@@ -21,7 +21,9 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPOR
 
 EXPORTED = ["moe_route", "moe_eqb_workspace_bytes", "moe_eqb_bias",
             "moe_forward_workspace_bytes", "moe_forward", "moe_status_string",
-            "moe_last_error_message", "moe_abi_version"]
+            "moe_last_error_message", "moe_abi_version", "moe_stage_timing",
+            "moe_stage_times", "moe_stage_name"]
+NUM_STAGES = 8
 
 
 class MoeProblem(C.Structure):
@@ -83,6 +85,12 @@ def load(path: str = LIB_PATH):
     lib.moe_last_error_message.restype = C.c_char_p
     lib.moe_abi_version.argtypes = []
     lib.moe_abi_version.restype = C.c_int32
+    lib.moe_stage_timing.argtypes = [i32]
+    lib.moe_stage_timing.restype = C.c_int
+    lib.moe_stage_times.argtypes = [C.POINTER(C.c_double), C.POINTER(C.c_int64)]
+    lib.moe_stage_times.restype = C.c_int
+    lib.moe_stage_name.argtypes = [i32]
+    lib.moe_stage_name.restype = C.c_char_p
     _lib = lib
     return lib
 

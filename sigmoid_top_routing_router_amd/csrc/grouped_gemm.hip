@@ -9,37 +9,57 @@
 // All three products have both operands K-contiguous (x[N,d] with W[h,d];
 // H[rows,h] with W_down[d,h]; x with W_r[E,d]), so one tile engine serves
 // them:
-//  * 256 threads = 4 waves as 2 (M) x 2 (N); block tile 128 x 128 (rows of
-//    the B operand) x 64 (k); each wave owns 64 x 64 outputs as 2 x 2
-//    v_mfma_f32_32x32x16_bf16 accumulators (fp32).
-//  * A and B tiles are staged through LDS with one 16-byte global load per
-//    thread and chunk, double buffered so the loads of step k+1 are in flight
-//    while the MFMAs of step k run; LDS rows are padded to 144 bytes so the
-//    16-byte fragment reads of 8 consecutive rows cover all banks.
-//  * Gate/up: the B tile holds 64 gate rows followed by the 64 up rows of the
-//    same hidden columns, and each wave takes 32 of each, so SiLU(g) * u is
-//    formed in registers (lane layouts of the two accumulators coincide) and
-//    H is written once in bf16.  The gathered token rows of x are read
-//    directly into the A tile (the permuted copy of x is never built).
+//  * Block tile 256 (rows) x 256 (rows of the B operand) x 64 (k), 4 waves as
+//    2 x 2; each wave owns 128 x 128 outputs as 4 x 4 accumulators of
+//    v_mfma_f32_32x32x16_bf16 (256 fp32 per lane, held in AGPRs), so every
+//    16-byte fragment read from LDS feeds four MFMAs.  The tile size is what
+//    bounds the operand traffic from L2 per flop (the CU's register file
+//    holds at most this many fp32 accumulators).
+//  * Operands move global -> LDS with the gfx950 LDS-DMA load
+//    (global_load_lds_dwordx4: 64 lanes x 16 bytes per instruction, no VGPR
+//    staging), 8 rows x 128 bytes per instruction: every row access is one
+//    whole 128-byte cache line, which on this chip moves about twice the
+//    bytes per second of half-line accesses.  Two stages of 64 KB are double
+//    buffered in LDS; the loads of stage k+1 fly while stage k is consumed,
+//    and are retired with explicit vmcnt waits plus a bare s_barrier so the
+//    compiler does not drain outstanding loads at every barrier.
+//  * LDS rows are 128 bytes (64 bf16); the eight 16-byte chunks of row r sit
+//    at slot c ^ (r & 7), so the fragment reads of 8 consecutive rows hit 8
+//    different bank groups.  The swizzle is applied on the global side (each
+//    lane picks the chunk that belongs in its fixed LDS slot).
+//  * Within a stage the fragments of k-step s+1 are read from LDS while the
+//    MFMAs of k-step s run (two fragment register sets).
+//  * Gate/up: the B tile holds 128 gate rows then the 128 up rows of the same
+//    hidden columns; each wave takes 64 of each, so SiLU(g) * u is formed in
+//    registers (the lane layouts of the two accumulators coincide) and H is
+//    written once in bf16.  The gathered token rows of x are loaded directly
+//    into the A tile (the permuted copy of x is never built).
 //  * Ragged segments: an m-tile table (expert, first row, rows) produced on
 //    the device by the grouping kernels drives the grid; the grid is sized
 //    for the worst case and surplus blocks exit after reading the tile count.
-//    Waves whose 32-row MFMA blocks hold no valid rows skip their MFMAs.
+//    Waves skip the MFMAs of 32-row blocks that hold no valid rows; rows past
+//    the segment (and B rows past the matrix) are clamped to a valid row when
+//    loading and never stored.
 //  * XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
 //    block b works on the logical tile (b % 8) * share + b / 8; each XCD then
 //    walks a contiguous run of (m-tile, n-tile) pairs, n fastest, and the
 //    blocks that share an A tile or an expert's weights meet in that XCD's
 //    L2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-constexpr int BM = 128;
-constexpr int BN = 128;
+constexpr int BM = 256;
+constexpr int BN = 256;
 constexpr int BK = 64;
-constexpr int LDS_LD = BK + 8;                 // bf16 per LDS row (144 bytes)
-constexpr int TILE_ELEMS = BM * LDS_LD;        // one operand tile
+constexpr int STAGES = 2;
+constexpr int ROW_BYTES = BK * 2;                    // 128
+constexpr int TILE_BYTES = BM * ROW_BYTES;           // 32 KB per operand and stage
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;          // A then B
+constexpr int LDS_BYTES = STAGES * STAGE_BYTES;      // 128 KB
 constexpr int kXcd = 8;
 
 int gemm_bm() { return BM; }
@@ -58,20 +78,38 @@ struct GemmArgs {
   const uint16_t* B1;      // up weights (gate/up only)
   int64_t b_expert_stride; // elements between experts' matrices
   int b_rows;              // valid rows of one expert's B (h, d or E)
-  int kdim;                // reduction length
+  int kdim;                // reduction length (multiple of 32)
   int n_tiles_n;           // tiles along the output columns
   void* out;               // H / Y (bf16) or Z (fp32)
   int64_t ldo;             // elements per output row
   const float* offset;     // router: per-column fp32 offset or NULL
 };
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void dma16(const void* g, lds_void_t* l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_all_mem() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+}
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_u16(float v) {
   return (uint16_t)f32_to_bf16_rne_bits(v);
 }
 
 template <int MODE>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * TILE_ELEMS];
+__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
 
   // ---- which tile -------------------------------------------------------
   const int64_t m_tiles = a.tiles ? (int64_t)(*a.n_tiles) : (a.rows_dense + BM - 1) / BM;
@@ -102,134 +140,183 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- global load assignment: 4 chunks of 16 bytes per operand per thread
-  const int kc = (tid & 7) * 8;          // k offset of this thread's chunk
-  const int r_base = tid >> 3;           // rows r_base + 32*i
-  const uint16_t* a_ptr[4];
-  const uint16_t* b_ptr[4];
-  bool a_ok[4], b_ok[4];
+  // ---- LDS-DMA assignment.  Per stage and operand each wave issues 8 loads;
+  // load i covers tile rows 8*(4*i + wave) .. +7, lane l -> row +(l>>3), LDS
+  // slot (l&7) which holds global chunk (l&7) ^ (row&7) = (l&7) ^ ((l>>3)&7).
+  const int sub = lane >> 3;
+  const int chunk = (lane & 7) ^ (sub & 7);
+  // A rows: element offset of each of this lane's 8 rows (rows past the
+  // segment reuse the first row of the tile).
+  int64_t a_row_off[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * (4 * i + wave) + sub;
+    int64_t arow = row0 + ((r < rows) ? r : 0);
+    if (a.gather) arow = a.gather[arow] / a.gather_div;
+    a_row_off[i] = arow * a.lda;
+  }
   const uint16_t* Bexp0 = a.B0 + (int64_t)expert * a.b_expert_stride;
   const uint16_t* Bexp1 = (MODE == kGateUp) ? a.B1 + (int64_t)expert * a.b_expert_stride : nullptr;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = r_base + 32 * i;
-    a_ok[i] = r < rows;
-    int64_t arow = 0;
-    if (a_ok[i]) {
-      if (a.gather) arow = a.gather[row0 + r] / a.gather_div;
-      else arow = row0 + r;
-    }
-    a_ptr[i] = a.A + arow * a.lda + kc;
-    int brow;
-    const uint16_t* bbase;
-    if (MODE == kGateUp) {
-      // tile rows 0..63: gate rows nt*64 + r; 64..127: up rows nt*64 + r - 64
-      const int hc = nt * 64 + (r & 63);
-      brow = hc;
-      bbase = (r < 64) ? Bexp0 : Bexp1;
-    } else {
-      brow = nt * BN + r;
-      bbase = Bexp0;
-    }
-    b_ok[i] = brow < a.b_rows;
-    b_ptr[i] = bbase + (int64_t)(b_ok[i] ? brow : 0) * a.kdim + kc;
-  }
+  // K tail: kdim % 64 == 32 leaves a last stage with 32 valid k; its upper
+  // chunks are loaded from the lower half of the row and never multiplied.
+  const int nk = (a.kdim + BK - 1) / BK;
+  const bool k_tail = (a.kdim % BK) != 0;
 
-  uint4 ra[4], rb[4];
-  auto load_global = [&](int k0) {
-    const bool kin = (k0 + kc) < a.kdim;
+  auto issue_stage = [&](int ks, int slot) {
+    const bool half = k_tail && ks == nk - 1;
+    const int c = half ? (chunk & 3) : chunk;
+    const int64_t k0 = (int64_t)ks * BK + c * 8;
+    char* sbase = lds_raw + slot * STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = (a_ok[i] && kin) ? *reinterpret_cast<const uint4*>(a_ptr[i] + k0) : make_uint4(0, 0, 0, 0);
-      rb[i] = (b_ok[i] && kin) ? *reinterpret_cast<const uint4*>(b_ptr[i] + k0) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_lds = [&](int buf) {
-    uint16_t* As = lds + buf * 2 * TILE_ELEMS;
-    uint16_t* Bs = As + TILE_ELEMS;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = r_base + 32 * i;
-      *reinterpret_cast<uint4*>(As + r * LDS_LD + kc) = ra[i];
-      *reinterpret_cast<uint4*>(Bs + r * LDS_LD + kc) = rb[i];
+    for (int i = 0; i < 8; ++i) {
+      const int j = 4 * i + wave;
+      const int r = 8 * j + sub;
+      dma16(a.A + a_row_off[i] + k0, (lds_void_t*)(sbase + j * 1024));
+      int brow;
+      const uint16_t* bbase;
+      if (MODE == kGateUp) {
+        brow = nt * (BN / 2) + (r & (BN / 2 - 1));
+        bbase = (r < BN / 2) ? Bexp0 : Bexp1;
+      } else {
+        brow = nt * BN + r;
+        bbase = Bexp0;
+      }
+      if (brow >= a.b_rows) brow = 0;
+      dma16(bbase + (int64_t)brow * a.kdim + k0, (lds_void_t*)(sbase + TILE_BYTES + j * 1024));
     }
   };
 
-  floatx16_t acc[2][2];
+  floatx16_t acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // Row offsets of this wave's MFMA operands inside the LDS tiles.
-  const int a_row0 = wm * 64;
-  int b_row[2];
-  if (MODE == kGateUp) { b_row[0] = 32 * wn; b_row[1] = 64 + 32 * wn; }
-  else { b_row[0] = 64 * wn; b_row[1] = 64 * wn + 32; }
-  const bool mf_live0 = (a_row0) < rows;
-  const bool mf_live1 = (a_row0 + 32) < rows;
-  const int frag_k = (lane >> 5) * 8;
-  const int frag_r = lane & 31;
-
-  const int nk = (a.kdim + BK - 1) / BK;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_global((kt + 1) * BK);
-    const uint16_t* As = lds + cur * 2 * TILE_ELEMS;
-    const uint16_t* Bs = As + TILE_ELEMS;
-    if (mf_live0) {
+  // Fragment geometry.  A rows wm*128 + 32*m + (lane&31); B rows per mode.
+  int b_row[4];
+  if (MODE == kGateUp) {
+    b_row[0] = wn * 64; b_row[1] = wn * 64 + 32;
+    b_row[2] = BN / 2 + wn * 64; b_row[3] = BN / 2 + wn * 64 + 32;
+  } else {
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const int ko = ks * 16 + frag_k;
-        const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(Bs + (b_row[0] + frag_r) * LDS_LD + ko);
-        const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(Bs + (b_row[1] + frag_r) * LDS_LD + ko);
-        const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(As + (a_row0 + frag_r) * LDS_LD + ko);
-        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
-        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
-        if (mf_live1) {
-          const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(As + (a_row0 + 32 + frag_r) * LDS_LD + ko);
-          acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
-          acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
+    for (int f = 0; f < 4; ++f) b_row[f] = wn * 128 + 32 * f;
+  }
+  const int fr = lane & 31;
+  const int a_base = (wm * 128 + fr) * ROW_BYTES;
+  const int b_base = TILE_BYTES + fr * ROW_BYTES;
+  // 16-byte slot of k-step ks: chunk 2*ks + (lane>>5), swizzled by row & 7.
+  auto slot_of = [&](int ks) { return ((2 * ks + (lane >> 5)) ^ (lane & 7)) * 16; };
+
+  int live_m = (rows - wm * 128 + 31) / 32;
+  live_m = live_m < 0 ? 0 : (live_m > 4 ? 4 : live_m);
+  live_m = __builtin_amdgcn_readfirstlane(live_m);
+  const bool live_n = (MODE == kGateUp) ? true : (nt * BN + wn * 128) < a.b_rows;
+  const bool any = __builtin_amdgcn_readfirstlane((live_m > 0 && live_n) ? 1 : 0) != 0;
+
+  typedef bf16x8_t frag_t[4];
+  auto load_frags = [&](frag_t& A, frag_t& B, int slot, int ks) {
+    const char* sb = lds_raw + slot * STAGE_BYTES;
+    const int so = slot_of(ks);
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      B[f] = *reinterpret_cast<const bf16x8_t*>(sb + b_base + b_row[f] * ROW_BYTES + so);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      A[m] = *reinterpret_cast<const bf16x8_t*>(sb + a_base + 32 * m * ROW_BYTES + so);
+  };
+
+  // Every wave of the block follows the same barrier and load schedule,
+  // whatever MFMA work it has.  Stage kt lives in slot kt&1.  After the
+  // fragments of its last k-step have been read, each wave waits for the
+  // loads of stage kt+1, the block synchronises, and the loads of stage kt+2
+  // go into the slot just released, while the MFMAs of the last k-step of
+  // stage kt still run.
+  auto run = [&](auto tag) {
+    constexpr int MT = decltype(tag)::value;  // 0 full, 1 partial, 2 no MFMA work
+    frag_t A0, B0, A1, B1;
+    issue_stage(0, 0);
+    if (nk > 1) {
+      issue_stage(1, 1);
+      wait_vmcnt<16>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    block_barrier();
+    if (MT != 2) load_frags(A0, B0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int slot = kt & 1;
+      const bool half = k_tail && kt == nk - 1;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        frag_t& Ac = (ks & 1) ? A1 : A0;
+        frag_t& Bc = (ks & 1) ? B1 : B0;
+        frag_t& An = (ks & 1) ? A0 : A1;
+        frag_t& Bn = (ks & 1) ? B0 : B1;
+        if (ks < 3) {
+          if (MT != 2) load_frags(An, Bn, slot, ks + 1);
+        } else if (kt + 1 < nk) {
+          wait_all_mem();     // stage kt+1 landed; this wave's reads of slot done
+          block_barrier();    // ... and every other wave's
+          if (kt + 2 < nk) issue_stage(kt + 2, slot);
+          if (MT != 2) load_frags(An, Bn, slot ^ 1, 0);
+        }
+        if (ks >= 2 && half) continue;  // upper 32 k of a tail stage
+        if (MT == 0) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+              acc[m][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ac[m], Bc[f], acc[m][f], 0, 0, 0);
+        } else if (MT == 1) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            if (m < live_m)  // wave-uniform (scalar)
+#pragma unroll
+              for (int f = 0; f < 4; ++f)
+                acc[m][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ac[m], Bc[f], acc[m][f], 0, 0, 0);
         }
       }
     }
-    if (kt + 1 < nk) store_lds(cur ^ 1);
-    __syncthreads();
-  }
+  };
+  if (!any) run(std::integral_constant<int, 2>{});
+  else if (live_m == 4) run(std::integral_constant<int, 0>{});
+  else run(std::integral_constant<int, 1>{});
 
   // ---- epilogue: lane holds column (lane & 31) and, for register r, row
   // 8*(r/4) + 4*(lane/32) + r%4 of each 32 x 32 accumulator.
+  if (!any) return;
   const int ccol = lane & 31;
   const int rsub = 4 * (lane >> 5);
 #pragma unroll
-  for (int mf = 0; mf < 2; ++mf) {
+  for (int m = 0; m < 4; ++m) {
+    if (m >= live_m) break;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int rr = a_row0 + mf * 32 + 8 * (r >> 2) + rsub + (r & 3);
+      const int rr = wm * 128 + m * 32 + 8 * (r >> 2) + rsub + (r & 3);
       if (rr >= rows) continue;
       const int64_t orow = row0 + rr;
       if (MODE == kGateUp) {
-        const int hc = nt * 64 + 32 * wn + ccol;
-        if (hc < a.b_rows) {
-          const float g = acc[mf][0][r];
-          const float u = acc[mf][1][r];
-          const float hval = g / (1.0f + __expf(-g)) * u;
-          reinterpret_cast<uint16_t*>(a.out)[orow * a.ldo + hc] = f32_to_bf16_u16(hval);
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const int hc = nt * (BN / 2) + wn * 64 + 32 * f + ccol;
+          if (hc < a.b_rows) {
+            const float g = acc[m][f][r];
+            const float u = acc[m][f + 2][r];
+            const float hval = g / (1.0f + __expf(-g)) * u;
+            reinterpret_cast<uint16_t*>(a.out)[orow * a.ldo + hc] = f32_to_bf16_u16(hval);
+          }
         }
       } else {
 #pragma unroll
-        for (int nf = 0; nf < 2; ++nf) {
-          const int col = nt * BN + b_row[nf] + ccol;
+        for (int f = 0; f < 4; ++f) {
+          const int col = nt * BN + b_row[f] + ccol;
           if (col < a.b_rows) {
             if (MODE == kDown) {
-              reinterpret_cast<uint16_t*>(a.out)[orow * a.ldo + col] = f32_to_bf16_u16(acc[mf][nf][r]);
+              reinterpret_cast<uint16_t*>(a.out)[orow * a.ldo + col] = f32_to_bf16_u16(acc[m][f][r]);
             } else {
-              float z = acc[mf][nf][r];
+              float z = acc[m][f][r];
               if (a.offset) z += a.offset[col];
               reinterpret_cast<float*>(a.out)[orow * a.ldo + col] = z;
             }
@@ -240,6 +327,19 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
   }
 }
 
+template <int MODE>
+static hipError_t launch_mode(const GemmArgs& a, dim3 grid, hipStream_t stream) {
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<MODE>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  hipLaunchKernelGGL(gemm_kernel<MODE>, grid, dim3(256), LDS_BYTES, stream, a);
+  return hipGetLastError();
+}
+
 static hipError_t launch_gemm(int mode, const GemmArgs& a, int64_t max_m_tiles,
                               hipStream_t stream) {
   const int64_t work = max_m_tiles * a.n_tiles_n;
@@ -247,13 +347,12 @@ static hipError_t launch_gemm(int mode, const GemmArgs& a, int64_t max_m_tiles,
   const int64_t share = (work + kXcd - 1) / kXcd;
   const int64_t blocks = share * kXcd;
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)blocks), block(256);
+  const dim3 grid((unsigned)blocks);
   switch (mode) {
-    case kGateUp: hipLaunchKernelGGL(gemm_kernel<kGateUp>, grid, block, 0, stream, a); break;
-    case kDown: hipLaunchKernelGGL(gemm_kernel<kDown>, grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL(gemm_kernel<kRouter>, grid, block, 0, stream, a); break;
+    case kGateUp: return launch_mode<kGateUp>(a, grid, stream);
+    case kDown: return launch_mode<kDown>(a, grid, stream);
+    default: return launch_mode<kRouter>(a, grid, stream);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w_router,
@@ -276,7 +375,7 @@ hipError_t launch_gateup(const uint16_t* x, const int32_t* sorted_src, int K,
   a.A = x; a.lda = d; a.gather = tiles ? sorted_src : nullptr; a.gather_div = K;
   a.tiles = tiles; a.n_tiles = n_tiles; a.rows_dense = rows_dense;
   a.B0 = w_gate; a.B1 = w_up; a.b_expert_stride = (int64_t)h * d; a.b_rows = h; a.kdim = d;
-  a.n_tiles_n = (h + 63) / 64; a.out = H; a.ldo = h; a.offset = nullptr;
+  a.n_tiles_n = (h + BN / 2 - 1) / (BN / 2); a.out = H; a.ldo = h; a.offset = nullptr;
   const int64_t mt = tiles ? max_tiles : (rows_dense + BM - 1) / BM;
   return launch_gemm(kGateUp, a, mt, stream);
 }

@@ -5,7 +5,9 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/moe_mi355x.h"
 #include "kernels.h"
@@ -155,6 +157,50 @@ moe_status_t check_problem(const moe_problem_t* p) {
   return MOE_OK;
 }
 
+// ---- stage timing: S+1 boundary events per recorded call
+struct StageTimer {
+  std::mutex mu;
+  bool enabled = false;
+  std::vector<hipEvent_t> pool;  // reused across reads
+  size_t used = 0;               // events recorded since the last read
+};
+StageTimer g_timer;
+
+struct CallTimer {
+  bool on = false;
+  size_t base = 0;
+  int next = 0;
+  hipStream_t st = nullptr;
+  hipError_t start(hipStream_t s) {
+    {
+      std::lock_guard<std::mutex> g(g_timer.mu);
+      if (!g_timer.enabled) return hipSuccess;
+      on = true;
+      st = s;
+      base = g_timer.used;
+      g_timer.used += MOE_NUM_STAGES + 1;
+      while (g_timer.pool.size() < g_timer.used) {
+        hipEvent_t e;
+        hipError_t err = hipEventCreate(&e);
+        if (err != hipSuccess) return err;
+        g_timer.pool.push_back(e);
+      }
+    }
+    return mark();  // takes the lock itself
+  }
+  // Record the boundary after the current stage.
+  hipError_t mark() {
+    if (!on) return hipSuccess;
+    hipEvent_t e;
+    {
+      std::lock_guard<std::mutex> g(g_timer.mu);
+      e = g_timer.pool[base + next];
+    }
+    ++next;
+    return hipEventRecord(e, st);
+  }
+};
+
 #define MOE_TRY_HIP(expr, where)                   \
   do {                                             \
     hipError_t _e = (expr);                        \
@@ -166,6 +212,39 @@ moe_status_t check_problem(const moe_problem_t* p) {
 extern "C" {
 
 int32_t moe_abi_version(void) { return 1; }
+
+moe_status_t moe_stage_timing(int32_t enable) {
+  std::lock_guard<std::mutex> g(g_timer.mu);
+  g_timer.enabled = enable != 0;
+  g_timer.used = 0;
+  return ok();
+}
+
+moe_status_t moe_stage_times(double* ms, int64_t* calls) {
+  if (!ms || !calls) return fail(MOE_ERR_INVALID_ARGUMENT, "ms and calls are required");
+  std::lock_guard<std::mutex> g(g_timer.mu);
+  for (int s = 0; s < MOE_NUM_STAGES; ++s) ms[s] = 0.0;
+  const size_t per = MOE_NUM_STAGES + 1;
+  const size_t n = g_timer.used / per;
+  for (size_t c = 0; c < n; ++c) {
+    hipEvent_t* ev = g_timer.pool.data() + c * per;
+    MOE_TRY_HIP(hipEventSynchronize(ev[MOE_NUM_STAGES]), "moe_stage_times");
+    for (int s = 0; s < MOE_NUM_STAGES; ++s) {
+      float t = 0.0f;
+      MOE_TRY_HIP(hipEventElapsedTime(&t, ev[s], ev[s + 1]), "moe_stage_times");
+      ms[s] += t;
+    }
+  }
+  *calls = (int64_t)n;
+  g_timer.used = 0;
+  return ok();
+}
+
+const char* moe_stage_name(int32_t stage) {
+  static const char* names[MOE_NUM_STAGES] = {"router_gemm", "routing", "grouping", "gate_up",
+                                              "down", "shared_gate_up", "shared_down", "combine"};
+  return (stage >= 0 && stage < MOE_NUM_STAGES) ? names[stage] : "";
+}
 
 const char* moe_status_string(moe_status_t s) {
   switch (s) {
@@ -277,6 +356,9 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_weights_t* w, const u
   const int key_bits = (p->flags & MOE_KEY32) ? 32 : 16;
   const bool recompute = (p->flags & MOE_RECOMPUTE_BIAS) != 0;
 
+  CallTimer tm;
+  MOE_TRY_HIP(tm.start(st), "moe_forward: stage timer");
+
   // a1: router logits
   const float* Z;
   if (p->logits_in) {
@@ -290,6 +372,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_weights_t* w, const u
                 "moe_forward: router GEMM");
     Z = zout;
   }
+  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
 
   // a2-a4: selection, token bias, optional exact quantile update, re-route
   int32_t* ids = A.topk_ids ? A.topk_ids : l.ids;
@@ -314,6 +397,8 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_weights_t* w, const u
       MOE_TRY_HIP(moe::launch_count(ids, N * K, E, A.counts_before, st), "moe_forward: loads");
   }
 
+  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
+
   // a5: stable grouping by expert and the m-tile table
   moe::PermWork pw;
   pw.chunk_counts = l.chunk_counts;
@@ -324,22 +409,28 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_weights_t* w, const u
   pw.tiles = l.tiles;
   pw.n_tiles = l.n_tiles;
   MOE_TRY_HIP(moe::launch_permute(ids, N, E, K, moe::gemm_bm(), pw, st), "moe_forward: grouping");
+  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
 
   // a6-a8: routed experts (gather fused into the gate/up A loads)
   MOE_TRY_HIP(moe::launch_gateup(x, pw.sorted_src, K, pw.tiles, pw.n_tiles, l.max_tiles, 0,
                                  w->w_gate, w->w_up, d, h, l.H, st), "moe_forward: gate/up");
+  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
   MOE_TRY_HIP(moe::launch_down(l.H, pw.tiles, pw.n_tiles, l.max_tiles, 0, w->w_down, d, h, l.Y, st),
               "moe_forward: down");
+  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
   // a9: shared expert over all tokens
-  if (p->n_shared == 1) {
+  if (p->n_shared == 1)
     MOE_TRY_HIP(moe::launch_gateup(x, nullptr, 1, nullptr, nullptr, 0, N, w->ws_gate, w->ws_up, d,
                                    p->h_shared, l.Hs, st), "moe_forward: shared gate/up");
+  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
+  if (p->n_shared == 1)
     MOE_TRY_HIP(moe::launch_down(l.Hs, nullptr, nullptr, 0, N, w->ws_down, d, p->h_shared, l.sh, st),
                 "moe_forward: shared down");
-  }
+  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
   // a10: weighted combine
   MOE_TRY_HIP(moe::launch_combine(p->n_shared == 1 ? l.sh : nullptr, l.Y, S, pw.src_pos, N, K, d, y, st),
               "moe_forward: combine");
+  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
   return ok();
 }
 

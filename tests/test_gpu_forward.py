@@ -183,3 +183,24 @@ def test_forward_deterministic(M):
                                               ("prefill", 256, True), ("skewed", 192, False)])
 def test_forward_full_size(M, name, sample, free):
     run_case(M, CONFIGS[name], sample=sample, free_running=free)
+
+
+def test_stage_timing_records_every_stage(M):
+    cfg = scaled(CONFIGS["prefill"], 1024)
+    L = _inputs(cfg)
+    W = weights_dev(L)
+    x = bf16_dev(L.x)
+    say("stage timing")
+    M.stage_timing(True)
+    for _ in range(3):
+        M.forward(x, W, cfg.K, beta_in=dev(L.beta_in), recompute_bias=True)
+    times, calls = M.stage_times()
+    M.stage_timing(False)
+    assert calls == 3
+    assert all(v > 0 for v in times.values()), times
+    # nothing recorded while disabled
+    M.forward(x, W, cfg.K, beta_in=dev(L.beta_in), recompute_bias=True)
+    M.stage_timing(True)
+    times, calls = M.stage_times()
+    M.stage_timing(False)
+    assert calls == 0
