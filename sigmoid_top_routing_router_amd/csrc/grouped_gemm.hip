@@ -19,10 +19,12 @@
 //    (global_load_lds_dwordx4: 64 lanes x 16 bytes per instruction, no VGPR
 //    staging), 8 rows x 128 bytes per instruction: every row access is one
 //    whole 128-byte cache line, which on this chip moves about twice the
-//    bytes per second of half-line accesses.  Two stages of 64 KB are double
-//    buffered in LDS; the loads of stage k+1 fly while stage k is consumed,
-//    and are retired with explicit vmcnt waits plus a bare s_barrier so the
-//    compiler does not drain outstanding loads at every barrier.
+//    bytes per second of half-line accesses.  All 160 KB of LDS hold operand
+//    slots of 32 KB: two for A and three for B (the weights, whose first
+//    touch usually misses L2), so the A loads run one stage and the B loads
+//    two stages ahead of the MFMAs.  Loads are retired with explicit vmcnt
+//    waits plus a bare s_barrier so the compiler does not drain outstanding
+//    loads at every barrier.
 //  * LDS rows are 128 bytes (64 bf16); the eight 16-byte chunks of row r sit
 //    at slot c ^ (r & 7), so the fragment reads of 8 consecutive rows hit 8
 //    different bank groups.  The swizzle is applied on the global side (each
@@ -55,11 +57,12 @@ namespace moe {
 constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 64;
-constexpr int STAGES = 2;
+constexpr int A_SLOTS = 2;                           // A ring: stages kt, kt+1
+constexpr int B_SLOTS = 3;                           // B ring: stages kt .. kt+2
 constexpr int ROW_BYTES = BK * 2;                    // 128
 constexpr int TILE_BYTES = BM * ROW_BYTES;           // 32 KB per operand and stage
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;          // A then B
-constexpr int LDS_BYTES = STAGES * STAGE_BYTES;      // 128 KB
+constexpr int B_RING = A_SLOTS * TILE_BYTES;         // byte offset of the B ring
+constexpr int LDS_BYTES = (A_SLOTS + B_SLOTS) * TILE_BYTES;  // 160 KB
 constexpr int kXcd = 8;
 
 int gemm_bm() { return BM; }
@@ -108,7 +111,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_u16(float v) {
 }
 
 template <int MODE>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(512, 2) void gemm_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
 
   // ---- which tile -------------------------------------------------------
@@ -137,20 +140,19 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = tid >> 6;          // 0..7; waves w and w+4 share a SIMD
+  const int wg = wave >> 2;           // row half of the tile
+  const int wp = wave & 3;            // column quarter of the tile
 
-  // ---- LDS-DMA assignment.  Per stage and operand each wave issues 8 loads;
-  // load i covers tile rows 8*(4*i + wave) .. +7, lane l -> row +(l>>3), LDS
+  // ---- LDS-DMA assignment.  Per stage and operand each wave issues 4 loads;
+  // load i covers tile rows 8*(8*i + wave) .. +7, lane l -> row +(l>>3), LDS
   // slot (l&7) which holds global chunk (l&7) ^ (row&7) = (l&7) ^ ((l>>3)&7).
   const int sub = lane >> 3;
   const int chunk = (lane & 7) ^ (sub & 7);
-  // A rows: element offset of each of this lane's 8 rows (rows past the
-  // segment reuse the first row of the tile).
-  int64_t a_row_off[8];
+  int64_t a_row_off[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 8 * (4 * i + wave) + sub;
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * (8 * i + wave) + sub;
     int64_t arow = row0 + ((r < rows) ? r : 0);
     if (a.gather) arow = a.gather[arow] / a.gather_div;
     a_row_off[i] = arow * a.lda;
@@ -161,121 +163,151 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
   // chunks are loaded from the lower half of the row and never multiplied.
   const int nk = (a.kdim + BK - 1) / BK;
   const bool k_tail = (a.kdim % BK) != 0;
-
-  auto issue_stage = [&](int ks, int slot) {
+  auto k_off = [&](int ks) {
     const bool half = k_tail && ks == nk - 1;
     const int c = half ? (chunk & 3) : chunk;
-    const int64_t k0 = (int64_t)ks * BK + c * 8;
-    char* sbase = lds_raw + slot * STAGE_BYTES;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = 4 * i + wave;
-      const int r = 8 * j + sub;
-      dma16(a.A + a_row_off[i] + k0, (lds_void_t*)(sbase + j * 1024));
-      int brow;
-      const uint16_t* bbase;
-      if (MODE == kGateUp) {
-        brow = nt * (BN / 2) + (r & (BN / 2 - 1));
-        bbase = (r < BN / 2) ? Bexp0 : Bexp1;
-      } else {
-        brow = nt * BN + r;
-        bbase = Bexp0;
-      }
-      if (brow >= a.b_rows) brow = 0;
-      dma16(bbase + (int64_t)brow * a.kdim + k0, (lds_void_t*)(sbase + TILE_BYTES + j * 1024));
+    return (int64_t)ks * BK + c * 8;
+  };
+  auto dma_a = [&](int ks, int i) {
+    const int j = 8 * i + wave;
+    dma16(a.A + a_row_off[i] + k_off(ks),
+          (lds_void_t*)(lds_raw + (ks % A_SLOTS) * TILE_BYTES + j * 1024));
+  };
+  auto dma_b = [&](int ks, int i) {
+    const int j = 8 * i + wave;
+    const int r = 8 * j + sub;
+    int brow;
+    const uint16_t* bbase;
+    if (MODE == kGateUp) {
+      brow = nt * (BN / 2) + (r & (BN / 2 - 1));
+      bbase = (r < BN / 2) ? Bexp0 : Bexp1;
+    } else {
+      brow = nt * BN + r;
+      bbase = Bexp0;
     }
+    if (brow >= a.b_rows) brow = 0;
+    dma16(bbase + (int64_t)brow * a.kdim + k_off(ks),
+          (lds_void_t*)(lds_raw + B_RING + (ks % B_SLOTS) * TILE_BYTES + j * 1024));
   };
 
-  floatx16_t acc[4][4];
+  // ---- accumulators: wave (wg, wp) owns rows wg*128 .. +128 and two
+  // 32-column blocks of the B rows: gate/up -> gate rows wp*32 and the up
+  // rows of the same hidden columns; otherwise B rows wp*64 .. +64.
+  floatx16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  // Fragment geometry.  A rows wm*128 + 32*m + (lane&31); B rows per mode.
-  int b_row[4];
-  if (MODE == kGateUp) {
-    b_row[0] = wn * 64; b_row[1] = wn * 64 + 32;
-    b_row[2] = BN / 2 + wn * 64; b_row[3] = BN / 2 + wn * 64 + 32;
-  } else {
-#pragma unroll
-    for (int f = 0; f < 4; ++f) b_row[f] = wn * 128 + 32 * f;
-  }
+  int b_row[2];
+  if (MODE == kGateUp) { b_row[0] = wp * 32; b_row[1] = BN / 2 + wp * 32; }
+  else { b_row[0] = wp * 64; b_row[1] = wp * 64 + 32; }
   const int fr = lane & 31;
-  const int a_base = (wm * 128 + fr) * ROW_BYTES;
-  const int b_base = TILE_BYTES + fr * ROW_BYTES;
-  // 16-byte slot of k-step ks: chunk 2*ks + (lane>>5), swizzled by row & 7.
+  const int a_base = (wg * 128 + fr) * ROW_BYTES;
+  const int b_base = B_RING + fr * ROW_BYTES;
   auto slot_of = [&](int ks) { return ((2 * ks + (lane >> 5)) ^ (lane & 7)) * 16; };
 
-  int live_m = (rows - wm * 128 + 31) / 32;
+  int live_m = (rows - wg * 128 + 31) / 32;
   live_m = live_m < 0 ? 0 : (live_m > 4 ? 4 : live_m);
   live_m = __builtin_amdgcn_readfirstlane(live_m);
-  const bool live_n = (MODE == kGateUp) ? true : (nt * BN + wn * 128) < a.b_rows;
+  const bool live_n = (MODE == kGateUp) ? true : (nt * BN + wp * 64) < a.b_rows;
   const bool any = __builtin_amdgcn_readfirstlane((live_m > 0 && live_n) ? 1 : 0) != 0;
 
-  typedef bf16x8_t frag_t[4];
-  auto load_frags = [&](frag_t& A, frag_t& B, int slot, int ks) {
-    const char* sb = lds_raw + slot * STAGE_BYTES;
-    const int so = slot_of(ks);
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-      B[f] = *reinterpret_cast<const bf16x8_t*>(sb + b_base + b_row[f] * ROW_BYTES + so);
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      A[m] = *reinterpret_cast<const bf16x8_t*>(sb + a_base + 32 * m * ROW_BYTES + so);
+  typedef bf16x8_t afrag_t[4];
+  typedef bf16x8_t bfrag_t[2];
+  auto wait_groups = [&](int younger) {  // younger load groups of 4 instructions
+    if (younger >= 3) wait_vmcnt<12>();
+    else if (younger == 2) wait_vmcnt<8>();
+    else if (younger == 1) wait_vmcnt<4>();
+    else wait_vmcnt<0>();
   };
 
-  // Every wave of the block follows the same barrier and load schedule,
-  // whatever MFMA work it has.  Stage kt lives in slot kt&1.  After the
-  // fragments of its last k-step have been read, each wave waits for the
-  // loads of stage kt+1, the block synchronises, and the loads of stage kt+2
-  // go into the slot just released, while the MFMAs of the last k-step of
-  // stage kt still run.
+  // Schedule (every wave, whatever its MFMA work): the prologue loads A0 B0
+  // A1 B1 B2; the barrier at the last k-step of stage kt releases A slot kt%2
+  // and B slot kt%3, and the loads of A(kt+2) and B(kt+3) are then spread
+  // over four k-steps, one per group of four MFMAs, pinned with scheduling
+  // barriers next to the LDS reads of the next k-step's fragments.  Two waves
+  // share each SIMD, so one wave's loads and LDS reads overlap the other's
+  // MFMAs.
   auto run = [&](auto tag) {
     constexpr int MT = decltype(tag)::value;  // 0 full, 1 partial, 2 no MFMA work
-    frag_t A0, B0, A1, B1;
-    issue_stage(0, 0);
+    afrag_t A0, A1;
+    bfrag_t B0, B1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma_a(0, i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma_b(0, i);
     if (nk > 1) {
-      issue_stage(1, 1);
-      wait_vmcnt<16>();
-    } else {
-      wait_vmcnt<0>();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma_a(1, i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma_b(1, i);
     }
+    if (nk > 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma_b(2, i);
+    }
+    wait_groups(min(nk - 1, 1) * 2 + (nk > 2 ? 1 : 0));
     block_barrier();
-    if (MT != 2) load_frags(A0, B0, 0, 0);
+    auto read_frags = [&](afrag_t& A, bfrag_t& B, int kt, int ks, int q) {
+      // fragments of quarter q (A frag q; B frag q for q < 2)
+      const char* sa = lds_raw + (kt % A_SLOTS) * TILE_BYTES;
+      const char* sbb = lds_raw + (kt % B_SLOTS) * TILE_BYTES;
+      const int so = slot_of(ks);
+      A[q] = *reinterpret_cast<const bf16x8_t*>(sa + a_base + 32 * q * ROW_BYTES + so);
+      if (q < 2) B[q] = *reinterpret_cast<const bf16x8_t*>(sbb + b_base + b_row[q] * ROW_BYTES + so);
+    };
+    if (MT != 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) read_frags(A0, B0, 0, 0, q);
+    }
     for (int kt = 0; kt < nk; ++kt) {
-      const int slot = kt & 1;
       const bool half = k_tail && kt == nk - 1;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        frag_t& Ac = (ks & 1) ? A1 : A0;
-        frag_t& Bc = (ks & 1) ? B1 : B0;
-        frag_t& An = (ks & 1) ? A0 : A1;
-        frag_t& Bn = (ks & 1) ? B0 : B1;
-        if (ks < 3) {
-          if (MT != 2) load_frags(An, Bn, slot, ks + 1);
-        } else if (kt + 1 < nk) {
-          wait_all_mem();     // stage kt+1 landed; this wave's reads of slot done
-          block_barrier();    // ... and every other wave's
-          if (kt + 2 < nk) issue_stage(kt + 2, slot);
-          if (MT != 2) load_frags(An, Bn, slot ^ 1, 0);
+        afrag_t& Ac = (ks & 1) ? A1 : A0;
+        bfrag_t& Bc = (ks & 1) ? B1 : B0;
+        afrag_t& An = (ks & 1) ? A0 : A1;
+        bfrag_t& Bn = (ks & 1) ? B0 : B1;
+        int nkt = kt, nks = ks + 1;
+        bool have_next = true;
+        if (ks == 3) {
+          nkt = kt + 1; nks = 0;
+          have_next = kt + 1 < nk;
+          if (have_next) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (kt + 2 < nk) wait_vmcnt<4>(); else wait_vmcnt<0>();
+            block_barrier();  // every wave done with A slot kt%2 and B slot kt%3
+          }
         }
-        if (ks >= 2 && half) continue;  // upper 32 k of a tail stage
-        if (MT == 0) {
+        // pending loads: ks=3 -> A(kt+2) 0,1 ; ks=0 -> A(kt+1) 2,3 ;
+        // ks=1 -> B(kt+2) 0,1 ; ks=2 -> B(kt+2) 2,3
+        int dma_kind = 0, dma_stage = 0, dma_first = 0;  // 0 none, 1 A, 2 B
+        if (ks == 3 && kt + 2 < nk) { dma_kind = 1; dma_stage = kt + 2; dma_first = 0; }
+        else if (ks == 0 && kt >= 1 && kt + 1 < nk) { dma_kind = 1; dma_stage = kt + 1; dma_first = 2; }
+        else if (ks == 1 && kt >= 1 && kt + 2 < nk) { dma_kind = 2; dma_stage = kt + 2; dma_first = 0; }
+        else if (ks == 2 && kt >= 1 && kt + 2 < nk) { dma_kind = 2; dma_stage = kt + 2; dma_first = 2; }
+        const bool do_mfma = !(ks >= 2 && half);
 #pragma unroll
-          for (int m = 0; m < 4; ++m)
+        for (int h2 = 0; h2 < 2; ++h2) {
+          if (dma_kind == 1) dma_a(dma_stage, dma_first + h2);
+          else if (dma_kind == 2) dma_b(dma_stage, dma_first + h2);
+          if (MT != 2 && have_next) {
+            read_frags(An, Bn, nkt, nks, 2 * h2);
+            read_frags(An, Bn, nkt, nks, 2 * h2 + 1);
+          }
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int f = 0; f < 4; ++f)
-              acc[m][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ac[m], Bc[f], acc[m][f], 0, 0, 0);
-        } else if (MT == 1) {
+          for (int mm = 0; mm < 2; ++mm) {
+            const int m = 2 * h2 + mm;
+            if (do_mfma && (MT == 0 || (MT == 1 && m < live_m))) {
 #pragma unroll
-          for (int m = 0; m < 4; ++m)
-            if (m < live_m)  // wave-uniform (scalar)
-#pragma unroll
-              for (int f = 0; f < 4; ++f)
+              for (int f = 0; f < 2; ++f)
                 acc[m][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ac[m], Bc[f], acc[m][f], 0, 0, 0);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
@@ -294,23 +326,20 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
     if (m >= live_m) break;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int rr = wm * 128 + m * 32 + 8 * (r >> 2) + rsub + (r & 3);
+      const int rr = wg * 128 + m * 32 + 8 * (r >> 2) + rsub + (r & 3);
       if (rr >= rows) continue;
       const int64_t orow = row0 + rr;
       if (MODE == kGateUp) {
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const int hc = nt * (BN / 2) + wn * 64 + 32 * f + ccol;
-          if (hc < a.b_rows) {
-            const float g = acc[m][f][r];
-            const float u = acc[m][f + 2][r];
-            const float hval = g / (1.0f + __expf(-g)) * u;
-            reinterpret_cast<uint16_t*>(a.out)[orow * a.ldo + hc] = f32_to_bf16_u16(hval);
-          }
+        const int hc = nt * (BN / 2) + wp * 32 + ccol;
+        if (hc < a.b_rows) {
+          const float g = acc[m][0][r];
+          const float u = acc[m][1][r];
+          const float hval = g / (1.0f + __expf(-g)) * u;
+          reinterpret_cast<uint16_t*>(a.out)[orow * a.ldo + hc] = f32_to_bf16_u16(hval);
         }
       } else {
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
+        for (int f = 0; f < 2; ++f) {
           const int col = nt * BN + b_row[f] + ccol;
           if (col < a.b_rows) {
             if (MODE == kDown) {
@@ -336,7 +365,7 @@ static hipError_t launch_mode(const GemmArgs& a, dim3 grid, hipStream_t stream) 
     if (e != hipSuccess) return e;
     configured = true;
   }
-  hipLaunchKernelGGL(gemm_kernel<MODE>, grid, dim3(256), LDS_BYTES, stream, a);
+  hipLaunchKernelGGL(gemm_kernel<MODE>, grid, dim3(512), LDS_BYTES, stream, a);
   return hipGetLastError();
 }
 
