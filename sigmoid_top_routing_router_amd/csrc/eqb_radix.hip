@@ -14,14 +14,15 @@
 //    lane of a wave takes one column of one row (coalesced 256-byte row
 //    segments), builds the key of fp32(Z + alpha) and counts the current byte
 //    into a padded per-column LDS histogram (stride 257 words so that the 64
-//    columns fall into different banks); the non-zero bins are then added to
-//    the global [E][256] histogram with integer atomics (order-independent,
-//    so the result is deterministic).
+//    columns fall into different banks).  Every lane remembers the lowest and
+//    highest bin it touched, so only that range of each column (one expert's
+//    values fall into few bins) is added to the global [E][256] histogram,
+//    with integer atomics (order-independent, so deterministic).
 //  * eqb_scan_kernel: one wave per expert scans its 256 bins from the top,
 //    finds the bin that holds the wanted rank and narrows the key prefix.
-// After the last pass eqb_centre_kernel subtracts the mean of the raw biases:
-// one thread sums them in expert order in fp64, every thread then writes
-// fp32(fp64(beta_raw) - mean).
+// After the last pass the last scan block to finish subtracts the mean of the
+// raw biases: one thread sums them in expert order in fp64, every thread then
+// writes fp32(fp64(beta_raw) - mean).
 #include "common.h"
 #include "kernels.h"
 
@@ -29,9 +30,12 @@ namespace moe {
 
 constexpr int kEqbCols = 64;
 constexpr int kEqbPad = 257;
+constexpr int kEqbMaxE = 384;
 
+// Histograms of all passes, then a 64-word tail whose first word is the
+// ticket counter of the centring step (zeroed together with the histograms).
 size_t eqb_hist_bytes(int E, int key_bits) {
-  return (size_t)(key_bits / 8) * (size_t)E * 256u * sizeof(uint32_t);
+  return ((size_t)(key_bits / 8) * (size_t)E * 256u + 64u) * sizeof(uint32_t);
 }
 size_t eqb_state_bytes(int E) { return (size_t)(2 * E + 4) * sizeof(uint32_t); }
 
@@ -41,6 +45,7 @@ __global__ __launch_bounds__(256) void eqb_hist_kernel(
     int pass, int64_t rows_per_block, const uint32_t* __restrict__ prefix,
     uint32_t* __restrict__ hist) {
   __shared__ uint32_t lh[kEqbCols * kEqbPad];
+  __shared__ int lo_s[4][kEqbCols], hi_s[4][kEqbCols];
   const int cl = threadIdx.x & (kEqbCols - 1);
   const int rs = threadIdx.x >> 6;
   const int e = blockIdx.x * kEqbCols + cl;
@@ -52,77 +57,113 @@ __global__ __launch_bounds__(256) void eqb_hist_kernel(
   const uint32_t want = (pass > 0 && col_ok) ? prefix[e] : 0u;
   const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
   const int64_t r1 = min(N, r0 + rows_per_block);
+  int lo = 256, hi = -1;
   if (col_ok) {
     uint32_t* my = lh + cl * kEqbPad;
-    for (int64_t t = r0 + rs; t < r1; t += 4) {
-      const float v = Z[t * E + e] + alpha[t];
+    auto count = [&](float v) {
       const uint32_t key = (KB == 16) ? bf16_order_key(f32_to_bf16_rne_bits(v))
                                       : f32_order_key(v);
-      if (pass == 0 || (key >> (shift + 8)) == want)
-        atomicAdd(my + ((key >> shift) & 0xFFu), 1u);
+      if (pass == 0 || (key >> (shift + 8)) == want) {
+        const int b = (int)((key >> shift) & 0xFFu);
+        atomicAdd(my + b, 1u);
+        lo = min(lo, b);
+        hi = max(hi, b);
+      }
+    };
+    int64_t t = r0 + rs;
+    for (; t + 12 < r1; t += 16) {  // four rows of this lane per trip, loads first
+      float z[4], al[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        z[u] = Z[(t + 4 * u) * E + e];
+        al[u] = alpha[t + 4 * u];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) count(z[u] + al[u]);
     }
+    for (; t < r1; t += 4) count(Z[t * E + e] + alpha[t]);
   }
+  lo_s[rs][cl] = lo;
+  hi_s[rs][cl] = hi;
   __syncthreads();
-  for (int i = threadIdx.x; i < kEqbCols * 256; i += 256) {
-    const int c = i >> 8, b = i & 255;
+  // flush: wave w takes columns w, w+4, ...; its lanes walk the touched bins
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int c = w; c < kEqbCols; c += 4) {
     const int ee = blockIdx.x * kEqbCols + c;
-    const uint32_t cnt = lh[c * kEqbPad + b];
-    if (cnt != 0u && ee < E) atomicAdd(hist + (size_t)ee * 256 + b, cnt);
+    if (ee >= E) break;
+    const int clo = min(min(lo_s[0][c], lo_s[1][c]), min(lo_s[2][c], lo_s[3][c]));
+    const int chi = max(max(hi_s[0][c], hi_s[1][c]), max(hi_s[2][c], hi_s[3][c]));
+    for (int b = clo + lane; b <= chi; b += 64) {
+      const uint32_t cnt = lh[c * kEqbPad + b];
+      if (cnt != 0u) atomicAdd(hist + (size_t)ee * 256 + b, cnt);
+    }
   }
 }
 
 // One wave per expert.  rank0 is the wanted 1-based rank for pass 0 (r+1).
+// In the last pass the quantile is decoded, and the last block to finish
+// (integer ticket counter, zeroed before the first pass) centres the biases.
 __global__ __launch_bounds__(256) void eqb_scan_kernel(
     const uint32_t* __restrict__ hist, uint32_t* __restrict__ prefix,
     uint32_t* __restrict__ rank, int E, int pass, int last, int key_bits,
-    uint32_t rank0, float* __restrict__ qraw, float* __restrict__ quantile_out) {
+    uint32_t rank0, float* __restrict__ qraw, float* __restrict__ quantile_out,
+    uint32_t* __restrict__ ticket, float* __restrict__ beta_out) {
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= E) return;
   const int lane = lane_id();
-  const uint4 v = reinterpret_cast<const uint4*>(hist + (size_t)e * 256)[lane];
-  const uint32_t s = v.x + v.y + v.z + v.w;
-  const uint32_t incl = wave_inclusive_sum_u32(s);
-  const uint32_t total = readlane_u32(incl, 63);
-  const uint32_t want = (pass == 0) ? rank0 : rank[e];
-  // Bins of this lane from the top: 4l+3, 4l+2, 4l+1, 4l.
-  uint32_t c = total - incl;  // entries in the bins above this lane's four
-  int found = -1;
-  uint32_t nr = 0;
-  const uint32_t bins[4] = {v.w, v.z, v.y, v.x};
+  if (e < E) {
+    const uint4 v = reinterpret_cast<const uint4*>(hist + (size_t)e * 256)[lane];
+    const uint32_t s = v.x + v.y + v.z + v.w;
+    const uint32_t incl = wave_inclusive_sum_u32(s);
+    const uint32_t total = readlane_u32(incl, 63);
+    const uint32_t want = (pass == 0) ? rank0 : rank[e];
+    // Bins of this lane from the top: 4l+3, 4l+2, 4l+1, 4l.
+    uint32_t c = total - incl;  // entries in the bins above this lane's four
+    int found = -1;
+    uint32_t nr = 0;
+    const uint32_t bins[4] = {v.w, v.z, v.y, v.x};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (found < 0 && c < want && want <= c + bins[i]) { found = 4 * lane + 3 - i; nr = want - c; }
-    c += bins[i];
-  }
-  const uint64_t hit = ballot(found >= 0);
-  const int src = hit ? (__ffsll((unsigned long long)hit) - 1) : 0;
-  const uint32_t bin = readlane_u32((uint32_t)found, src);
-  const uint32_t new_rank = readlane_u32(nr, src);
-  if (lane == 0) {
-    const uint32_t p = ((pass == 0) ? 0u : (prefix[e] << 8)) | (bin & 0xFFu);
-    prefix[e] = p;
-    rank[e] = new_rank;
-    if (last) {
-      const float q = (key_bits == 16) ? bf16_bits_to_f32(bf16_from_order_key(p))
-                                       : f32_from_order_key(p);
-      qraw[e] = q;
-      if (quantile_out) quantile_out[e] = q;
+    for (int i = 0; i < 4; ++i) {
+      if (found < 0 && c < want && want <= c + bins[i]) { found = 4 * lane + 3 - i; nr = want - c; }
+      c += bins[i];
+    }
+    const uint64_t hit = ballot(found >= 0);
+    const int src = hit ? (__ffsll((unsigned long long)hit) - 1) : 0;
+    const uint32_t bin = readlane_u32((uint32_t)found, src);
+    const uint32_t new_rank = readlane_u32(nr, src);
+    if (lane == 0) {
+      const uint32_t p = ((pass == 0) ? 0u : (prefix[e] << 8)) | (bin & 0xFFu);
+      prefix[e] = p;
+      rank[e] = new_rank;
+      if (last) {
+        const float q = (key_bits == 16) ? bf16_bits_to_f32(bf16_from_order_key(p))
+                                         : f32_from_order_key(p);
+        qraw[e] = q;
+        if (quantile_out) quantile_out[e] = q;
+      }
     }
   }
-}
-
-__global__ __launch_bounds__(256) void eqb_centre_kernel(const float* __restrict__ qraw,
-                                                         int E, float* __restrict__ beta_out) {
+  if (!last) return;
+  __shared__ bool is_last;
   __shared__ double mean_s;
+  __shared__ float q_s[kEqbMaxE];
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) is_last = atomicAdd(ticket, 1u) == gridDim.x - 1;
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+  for (int i = threadIdx.x; i < E; i += blockDim.x)
+    q_s[i] = reinterpret_cast<volatile const float*>(qraw)[i];
+  __syncthreads();
   if (threadIdx.x == 0) {
     double acc = 0.0;
-    for (int e = 0; e < E; ++e) acc += (double)(-qraw[e]);
+    for (int i = 0; i < E; ++i) acc += (double)(-q_s[i]);
     mean_s = acc / (double)E;
   }
   __syncthreads();
   const double mean = mean_s;
-  for (int e = threadIdx.x; e < E; e += blockDim.x)
-    beta_out[e] = (float)((double)(-qraw[e]) - mean);
+  for (int i = threadIdx.x; i < E; i += blockDim.x)
+    beta_out[i] = (float)((double)(-q_s[i]) - mean);
 }
 
 hipError_t launch_eqb(const float* Z, const float* alpha, int64_t N, int E, int K,
@@ -134,10 +175,11 @@ hipError_t launch_eqb(const float* Z, const float* alpha, int64_t N, int E, int 
   if (err != hipSuccess) return err;
   uint32_t* prefix = w.state;
   uint32_t* rank = w.state + E;
+  uint32_t* ticket = w.hist + (size_t)passes * E * 256;
   const int col_groups = (E + kEqbCols - 1) / kEqbCols;
-  int64_t chunks = (1536 + col_groups - 1) / col_groups;
+  int64_t chunks = (512 + col_groups - 1) / col_groups;
   int64_t rows_per_block = (N + chunks - 1) / chunks;
-  if (rows_per_block < 256) rows_per_block = 256;
+  if (rows_per_block < 64) rows_per_block = 64;
   rows_per_block = (rows_per_block + 3) / 4 * 4;
   chunks = (N + rows_per_block - 1) / rows_per_block;
   const dim3 hgrid((unsigned)col_groups, (unsigned)chunks), block(256);
@@ -152,9 +194,8 @@ hipError_t launch_eqb(const float* Z, const float* alpha, int64_t N, int E, int 
                          rows_per_block, prefix, hp);
     hipLaunchKernelGGL(eqb_scan_kernel, sgrid, block, 0, stream, hp, prefix, rank, E, p,
                        p == passes - 1 ? 1 : 0, key_bits, (uint32_t)(r + 1), w.qraw,
-                       quantile_out);
+                       quantile_out, ticket, beta_out);
   }
-  hipLaunchKernelGGL(eqb_centre_kernel, dim3(1), block, 0, stream, w.qraw, E, beta_out);
   return hipGetLastError();
 }
 

@@ -14,8 +14,8 @@
 //  2. perm_scan_kernel: one block per expert turns its row of chunk counts
 //     into exclusive chunk bases and the expert total.
 //  3. perm_tiles_kernel: one block; exclusive sums of the counts (offsets)
-//     and the table of m-tiles (expert, first row, rows) that drives the
-//     grouped GEMMs from device memory.
+//     by a block-wide scan, and the table of m-tiles (expert, first row, rows)
+//     that drives the grouped GEMMs from device memory.
 //  4. perm_scatter_kernel: one wave per chunk walks its pairs in order, 64 at
 //     a time; lanes holding the same expert are found with nine ballots over
 //     the bits of the expert id, so the rank among them is a popcount and the
@@ -25,7 +25,7 @@
 
 namespace moe {
 
-constexpr int kChunk = 1024;        // pairs per chunk (one wave)
+constexpr int kChunk = 512;         // pairs per chunk (one wave)
 constexpr int kPermWaves = 4;       // waves per block in the chunk kernels
 constexpr int kMaxE = 384;
 
@@ -78,45 +78,45 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(uint32_t* __restrict__ c
   if (threadIdx.x == 0) counts[e] = (int32_t)carry;
 }
 
-// One block: offsets (exclusive sums of counts) and the m-tile table.
+// One block of 256 threads: offsets (exclusive sums of counts) and the m-tile
+// table.  Thread i owns experts 2i and 2i+1 (E <= 512); a block-wide scan in
+// thread order gives the sums in expert order.
 __global__ __launch_bounds__(256) void perm_tiles_kernel(const int32_t* __restrict__ counts,
                                                          int E, int bm,
                                                          int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ tiles,
                                                          int32_t* __restrict__ n_tiles) {
-  __shared__ int32_t s_cnt[kMaxE];
-  __shared__ int32_t s_tile[kMaxE];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    s_cnt[e] = counts[e];
-    s_tile[e] = (counts[e] + bm - 1) / bm;
-  }
+  __shared__ uint32_t wsum_c[4], wsum_t[4];
+  const int tid = threadIdx.x, w = tid >> 6, lane = lane_id();
+  const int e0 = 2 * tid, e1 = 2 * tid + 1;
+  const uint32_t c0 = e0 < E ? (uint32_t)counts[e0] : 0u;
+  const uint32_t c1 = e1 < E ? (uint32_t)counts[e1] : 0u;
+  const uint32_t t0 = (c0 + bm - 1) / bm, t1 = (c1 + bm - 1) / bm;
+  const uint32_t ic = wave_inclusive_sum_u32(c0 + c1);
+  const uint32_t it = wave_inclusive_sum_u32(t0 + t1);
+  if (lane == kWave - 1) { wsum_c[w] = ic; wsum_t[w] = it; }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t off = 0, toff = 0;
-    for (int e = 0; e < E; ++e) {
-      const int32_t c = s_cnt[e], t = s_tile[e];
-      s_cnt[e] = off;
-      s_tile[e] = toff;
-      off += c;
-      toff += t;
-    }
-    offsets[E] = off;
-    *n_tiles = toff;
+  uint32_t bc = 0, bt = 0;
+  for (int i = 0; i < w; ++i) { bc += wsum_c[i]; bt += wsum_t[i]; }
+  const uint32_t off0 = bc + ic - (c0 + c1), toff0 = bt + it - (t0 + t1);
+  if (tid == 255) {
+    offsets[E] = (int32_t)(bc + ic);
+    *n_tiles = (int32_t)(bt + it);
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    const int32_t off = s_cnt[e];
-    offsets[e] = off;
-    const int32_t c = counts[e];
-    int32_t t = s_tile[e];
-    for (int32_t r = 0; r < c; r += bm, ++t) {
-      int32_t* ent = tiles + 4 * (size_t)t;
-      ent[0] = e;
-      ent[1] = off + r;
-      ent[2] = min(bm, c - r);
-      ent[3] = r;
+  auto emit = [&](int e, uint32_t c, uint32_t off, uint32_t toff) {
+    offsets[e] = (int32_t)off;
+    uint32_t t = toff;
+    for (uint32_t r = 0; r < c; r += bm, ++t) {
+      int4 ent;
+      ent.x = e;
+      ent.y = (int32_t)(off + r);
+      ent.z = (int32_t)min((uint32_t)bm, c - r);
+      ent.w = (int32_t)r;
+      reinterpret_cast<int4*>(tiles)[t] = ent;
     }
-  }
+  };
+  if (e0 < E) emit(e0, c0, off0, toff0);
+  if (e1 < E) emit(e1, c1, off0 + c0, toff0 + t0);
 }
 
 __global__ __launch_bounds__(256) void perm_scatter_kernel(
