@@ -318,41 +318,71 @@ __global__ __launch_bounds__(512, 2) void gemm_kernel(GemmArgs a) {
 
   // ---- epilogue: lane holds column (lane & 31) and, for register r, row
   // 8*(r/4) + 4*(lane/32) + r%4 of each 32 x 32 accumulator.
-  if (!any) return;
-  const int ccol = lane & 31;
-  const int rsub = 4 * (lane >> 5);
+  if (MODE == kRouter) {
+    if (!any) return;
+    const int ccol = lane & 31;
+    const int rsub = 4 * (lane >> 5);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    if (m >= live_m) break;
+    for (int m = 0; m < 4; ++m) {
+      if (m >= live_m) break;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rr = wg * 128 + m * 32 + 8 * (r >> 2) + rsub + (r & 3);
-      if (rr >= rows) continue;
-      const int64_t orow = row0 + rr;
-      if (MODE == kGateUp) {
-        const int hc = nt * (BN / 2) + wp * 32 + ccol;
-        if (hc < a.b_rows) {
-          const float g = acc[m][0][r];
-          const float u = acc[m][1][r];
-          const float hval = g / (1.0f + __expf(-g)) * u;
-          reinterpret_cast<uint16_t*>(a.out)[orow * a.ldo + hc] = f32_to_bf16_u16(hval);
-        }
-      } else {
+      for (int r = 0; r < 16; ++r) {
+        const int rr = wg * 128 + m * 32 + 8 * (r >> 2) + rsub + (r & 3);
+        if (rr >= rows) continue;
+        const int64_t orow = row0 + rr;
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
           const int col = nt * BN + b_row[f] + ccol;
           if (col < a.b_rows) {
-            if (MODE == kDown) {
-              reinterpret_cast<uint16_t*>(a.out)[orow * a.ldo + col] = f32_to_bf16_u16(acc[m][f][r]);
-            } else {
-              float z = acc[m][f][r];
-              if (a.offset) z += a.offset[col];
-              reinterpret_cast<float*>(a.out)[orow * a.ldo + col] = z;
-            }
+            float z = acc[m][f][r];
+            if (a.offset) z += a.offset[col];
+            reinterpret_cast<float*>(a.out)[orow * a.ldo + col] = z;
           }
         }
       }
     }
+    return;
+  }
+  // bf16 outputs (H or Y) go through LDS: every wave converts its
+  // accumulators (hardware round-to-nearest-even) into a row-major tile, then
+  // the block writes whole rows with 16-byte stores.
+  constexpr int OCOLS = (MODE == kGateUp) ? BN / 2 : BN;   // tile columns
+  constexpr int OSTRIDE = OCOLS * 2 + 16;                  // bytes per LDS row
+  __syncthreads();  // all fragment reads of the last stage are done
+  if (any) {
+    const int ccol = lane & 31;
+    const int rsub = 4 * (lane >> 5);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if (m >= live_m) break;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rr = wg * 128 + m * 32 + 8 * (r >> 2) + rsub + (r & 3);
+        char* lrow = lds_raw + rr * OSTRIDE;
+        if (MODE == kGateUp) {
+          const float g = acc[m][0][r];
+          const float u = acc[m][1][r];
+          const float hval = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+          *reinterpret_cast<__bf16*>(lrow + (wp * 32 + ccol) * 2) = (__bf16)hval;
+        } else {
+#pragma unroll
+          for (int f = 0; f < 2; ++f)
+            *reinterpret_cast<__bf16*>(lrow + (b_row[f] + ccol) * 2) = (__bf16)acc[m][f][r];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int CPR = OCOLS / 8;  // 16-byte chunks per tile row
+  const int col0 = nt * OCOLS;
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+  for (int c = tid; c < BM * CPR; c += 512) {
+    const int rr = c / CPR, ch = c % CPR;
+    if (rr >= rows) break;  // chunks are walked in row order
+    const int col = col0 + ch * 8;
+    if (col >= a.b_rows) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(lds_raw + rr * OSTRIDE + ch * 16);
+    *reinterpret_cast<uint4*>(out + (row0 + rr) * a.ldo + col) = v;
   }
 }
 
