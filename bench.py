@@ -63,6 +63,62 @@ def traffic_for(workload):
     return ent.get("bytes_per_launch")
 
 
+ROUTED_GATEUP = "gemm_kernel<0, true>"
+COPY_KERNEL = "copyBuffer"
+
+
+def _counter_means(csv_dir, counter):
+    """Mean per-dispatch value of `counter` (KiB) for the routed gate/up kernel
+    and the largest plain copy in one rocprofv3 --pmc output directory."""
+    import csv
+    import glob
+    gu, cp = [], []
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                if ROUTED_GATEUP in r["Kernel_Name"]:
+                    gu.append(float(r["Counter_Value"]))
+                elif COPY_KERNEL in r["Kernel_Name"]:
+                    cp.append(float(r["Counter_Value"]))
+    if not gu or not cp:
+        raise SystemExit(f"{csv_dir}: no {counter} rows for the routed gate/up kernel or the copy")
+    return sum(gu) / len(gu), max(cp), len(gu)
+
+
+def record_traffic(workload, fetch_dir, write_dir, copy_mib):
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+    WRITE_SIZE, each with --calibrate-copy-mib) into HBM bytes per launch of
+    the routed gate/up GEMM.  Each counter is scaled by the factor that makes
+    it read the known size of the calibration copy (copy_mib MiB read and
+    written)."""
+    known_kib = copy_mib * 1024.0
+    f_gu, f_cp, n_f = _counter_means(fetch_dir, "FETCH_SIZE")
+    w_gu, w_cp, n_w = _counter_means(write_dir, "WRITE_SIZE")
+    f_scale, w_scale = known_kib / f_cp, known_kib / w_cp
+    fetch_b = f_gu * f_scale * 1024.0
+    write_b = w_gu * w_scale * 1024.0
+    t = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    t[workload] = {
+        "kernel": "routed gate/up GEMM (" + ROUTED_GATEUP + ")",
+        "bytes_per_launch": fetch_b + write_b,
+        "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
+        "fetch_kib_raw_mean": f_gu, "write_kib_raw_mean": w_gu,
+        "launches": [n_f, n_w],
+        "copy_calibration": {"copy_mib": copy_mib, "fetch_kib": f_cp, "write_kib": w_cp,
+                             "fetch_scale": f_scale, "write_scale": w_scale},
+        "source_sha256_16": kernel_source_hash(),
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1)
+    print(json.dumps(t[workload]))
+
+
 def cpu_baseline(cfg, L, sample_tokens):
     """The oracle (untuned) timed on a bounded sample: the whole layer for
     the first `sample_tokens` tokens of the same inputs (the quantile update
@@ -100,7 +156,14 @@ def main():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "kernel for scaling hardware byte counters)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU run: write the routed gate/up HBM bytes per launch from two "
+                         "rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE) of "
+                         "this script run with --calibrate-copy-mib")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.workload, *args.record_traffic, args.calibrate_copy_mib or 1024)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(see the sharding notes in DESIGN.md); use --gpus 1", file=sys.stderr)
@@ -184,7 +247,7 @@ def main():
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_for(args.workload)
-    roof["kernel"] = "gemm_kernel<gate/up> (routed experts)"
+    roof["kernel"] = "gemm_kernel<0, true> (routed gate/up GEMM)"
     roof["per_launch"] = {"flops": flops, "bytes": bytes_, "avg_ms": stage_ms["gate_up"],
                           "tflops": flops / t_gu / 1e12, "gbs": bytes_ / t_gu / 1e9,
                           "mfma_frac": flops / t_gu / 1e12 / PEAK_BF16_TFLOPS}

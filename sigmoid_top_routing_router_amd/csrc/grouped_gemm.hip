@@ -9,12 +9,12 @@
 // All three products have both operands K-contiguous (x[N,d] with W[h,d];
 // H[rows,h] with W_down[d,h]; x with W_r[E,d]), so one tile engine serves
 // them:
-//  * Block tile 256 (rows) x 256 (rows of the B operand) x 64 (k), 4 waves as
-//    2 x 2; each wave owns 128 x 128 outputs as 4 x 4 accumulators of
-//    v_mfma_f32_32x32x16_bf16 (256 fp32 per lane, held in AGPRs), so every
-//    16-byte fragment read from LDS feeds four MFMAs.  The tile size is what
-//    bounds the operand traffic from L2 per flop (the CU's register file
-//    holds at most this many fp32 accumulators).
+//  * Block tile 256 (rows) x 256 (rows of the B operand) x 64 (k), 8 waves as
+//    2 (rows) x 4 (columns), two waves per SIMD; each wave owns 128 x 64
+//    outputs as 4 x 2 accumulators of v_mfma_f32_32x32x16_bf16 (128 fp32 per
+//    lane), so one wave's LDS reads and loads overlap the other's MFMAs.  The
+//    256 x 256 tile is what bounds the operand traffic from L2 per flop (the
+//    CU's register file holds at most this many fp32 accumulators).
 //  * Operands move global -> LDS with the gfx950 LDS-DMA load
 //    (global_load_lds_dwordx4: 64 lanes x 16 bytes per instruction, no VGPR
 //    staging), 8 rows x 128 bytes per instruction: every row access is one
@@ -36,6 +36,9 @@
 //    registers (the lane layouts of the two accumulators coincide) and H is
 //    written once in bf16.  The gathered token rows of x are loaded directly
 //    into the A tile (the permuted copy of x is never built).
+//  * Epilogue: bf16 results (H, Y) are converted in registers (hardware
+//    round-to-nearest-even), staged row-major in the then idle LDS and written
+//    as whole 16-byte row chunks; router logits are stored directly in fp32.
 //  * Ragged segments: an m-tile table (expert, first row, rows) produced on
 //    the device by the grouping kernels drives the grid; the grid is sized
 //    for the worst case and surplus blocks exit after reading the tile count.
@@ -110,12 +113,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_u16(float v) {
   return (uint16_t)f32_to_bf16_rne_bits(v);
 }
 
-template <int MODE>
+// GROUPED: rows come from the m-tile table (routed experts); otherwise the
+// rows are 0 .. rows_dense-1 (router, shared expert).
+template <int MODE, bool GROUPED>
 __global__ __launch_bounds__(512, 2) void gemm_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
 
   // ---- which tile -------------------------------------------------------
-  const int64_t m_tiles = a.tiles ? (int64_t)(*a.n_tiles) : (a.rows_dense + BM - 1) / BM;
+  const int64_t m_tiles = GROUPED ? (int64_t)(*a.n_tiles) : (a.rows_dense + BM - 1) / BM;
   const int64_t work = m_tiles * a.n_tiles_n;
   const int64_t share = (work + kXcd - 1) / kXcd;
   const int64_t local = blockIdx.x / kXcd;
@@ -128,7 +133,7 @@ __global__ __launch_bounds__(512, 2) void gemm_kernel(GemmArgs a) {
   int expert = 0;
   int64_t row0;
   int rows;
-  if (a.tiles) {
+  if (GROUPED) {
     const int4 ent = reinterpret_cast<const int4*>(a.tiles)[mt];
     expert = ent.x;
     row0 = ent.y;
@@ -154,7 +159,7 @@ __global__ __launch_bounds__(512, 2) void gemm_kernel(GemmArgs a) {
   for (int i = 0; i < 4; ++i) {
     const int r = 8 * (8 * i + wave) + sub;
     int64_t arow = row0 + ((r < rows) ? r : 0);
-    if (a.gather) arow = a.gather[arow] / a.gather_div;
+    if (GROUPED && a.gather) arow = a.gather[arow] / a.gather_div;
     a_row_off[i] = arow * a.lda;
   }
   const uint16_t* Bexp0 = a.B0 + (int64_t)expert * a.b_expert_stride;
@@ -386,16 +391,16 @@ __global__ __launch_bounds__(512, 2) void gemm_kernel(GemmArgs a) {
   }
 }
 
-template <int MODE>
+template <int MODE, bool GROUPED>
 static hipError_t launch_mode(const GemmArgs& a, dim3 grid, hipStream_t stream) {
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<MODE>,
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<MODE, GROUPED>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  hipLaunchKernelGGL(gemm_kernel<MODE>, grid, dim3(512), LDS_BYTES, stream, a);
+  hipLaunchKernelGGL((gemm_kernel<MODE, GROUPED>), grid, dim3(512), LDS_BYTES, stream, a);
   return hipGetLastError();
 }
 
@@ -407,10 +412,15 @@ static hipError_t launch_gemm(int mode, const GemmArgs& a, int64_t max_m_tiles,
   const int64_t blocks = share * kXcd;
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks);
+  const bool grouped = a.tiles != nullptr;
   switch (mode) {
-    case kGateUp: return launch_mode<kGateUp>(a, grid, stream);
-    case kDown: return launch_mode<kDown>(a, grid, stream);
-    default: return launch_mode<kRouter>(a, grid, stream);
+    case kGateUp:
+      return grouped ? launch_mode<kGateUp, true>(a, grid, stream)
+                     : launch_mode<kGateUp, false>(a, grid, stream);
+    case kDown:
+      return grouped ? launch_mode<kDown, true>(a, grid, stream)
+                     : launch_mode<kDown, false>(a, grid, stream);
+    default: return launch_mode<kRouter, false>(a, grid, stream);
   }
 }
 
