@@ -46,7 +46,10 @@ typedef enum {
 
 /* Size limits of every entry point: 1 <= N <= 2^24, 1 <= K <= 8,
  * K < E <= 384, and for the layer also d % 64 == 0 (64 <= d <= 8192),
- * h % 32 == 0 (32 <= h <= 4096), hs % 32 == 0, n_shared in {0, 1}. */
+ * h % 32 == 0 (32 <= h <= 4096), hs % 32 == 0, n_shared in {0, 1}, and
+ * N*d, N*K*h and N*hs each below 2^31 (every bf16 GEMM operand under 4 GiB;
+ * e.g. N <= 838,860 at d = 2560, K = 6, h = 512).  A larger layer is rejected
+ * with MOE_ERR_UNSUPPORTED_SHAPE. */
 #define MOE_MAX_E 384
 #define MOE_MAX_K 8
 

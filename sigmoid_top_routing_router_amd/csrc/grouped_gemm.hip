@@ -89,12 +89,24 @@ struct GemmArgs {
   void* out;               // H / Y (bf16) or Z (fp32)
   int64_t ldo;             // elements per output row
   const float* offset;     // router: per-column fp32 offset or NULL
+  uint32_t a_bytes;        // size of the whole A buffer (< 4 GiB)
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-__device__ __forceinline__ void dma16(const void* g, lds_void_t* l) {
-  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+// Raw buffer resource over `bytes` bytes at `base` (stride 0; reads past the
+// end return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+// LDS-DMA: 16 bytes per lane from (resource, per-lane voff + uniform soff) to
+// LDS at l + 16 * lane.  The buffer form (buffer_load_dwordx4 ... lds) is
+// counted on vmcnt only, so the compiler keeps exact lgkmcnt waits for the
+// LDS fragment reads around it.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                      lds_void_t* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff, soff, 0, 0);
 }
 
 template <int N>
@@ -154,44 +166,41 @@ __global__ __launch_bounds__(512, 2) void gemm_kernel(GemmArgs a) {
   // slot (l&7) which holds global chunk (l&7) ^ (row&7) = (l&7) ^ ((l>>3)&7).
   const int sub = lane >> 3;
   const int chunk = (lane & 7) ^ (sub & 7);
-  int64_t a_row_off[4];
+  // Byte offsets of each lane's 16-byte piece, fixed for the whole tile; the
+  // stage's k offset goes in the scalar offset of the load.  Rows past the
+  // segment load the segment's first row (never stored); B rows past the
+  // matrix load its row 0.
+  uint32_t a_voff[4], b_voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 8 * (8 * i + wave) + sub;
     int64_t arow = row0 + ((r < rows) ? r : 0);
     if (GROUPED && a.gather) arow = a.gather[arow] / a.gather_div;
-    a_row_off[i] = arow * a.lda;
+    a_voff[i] = (uint32_t)(arow * a.lda * 2) + (uint32_t)chunk * 16u;
+    int brow = (MODE == kGateUp) ? nt * (BN / 2) + (r & (BN / 2 - 1)) : nt * BN + r;
+    if (brow >= a.b_rows) brow = 0;
+    b_voff[i] = (uint32_t)brow * (uint32_t)a.kdim * 2u + (uint32_t)chunk * 16u;
   }
-  const uint16_t* Bexp0 = a.B0 + (int64_t)expert * a.b_expert_stride;
-  const uint16_t* Bexp1 = (MODE == kGateUp) ? a.B1 + (int64_t)expert * a.b_expert_stride : nullptr;
-  // K tail: kdim % 64 == 32 leaves a last stage with 32 valid k; its upper
-  // chunks are loaded from the lower half of the row and never multiplied.
+  const uint32_t b_bytes = (uint32_t)a.b_rows * (uint32_t)a.kdim * 2u;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, a.a_bytes);
+  const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(a.B0 + (int64_t)expert * a.b_expert_stride, b_bytes);
+  const __amdgpu_buffer_rsrc_t rb1 =
+      make_rsrc((MODE == kGateUp ? a.B1 : a.B0) + (int64_t)expert * a.b_expert_stride, b_bytes);
+  // K tail: kdim % 64 == 32 leaves a last stage with 32 valid k.  Its upper
+  // chunks read past the end of the row (the next row, or zeros past the end
+  // of the buffer) and are never multiplied.
   const int nk = (a.kdim + BK - 1) / BK;
   const bool k_tail = (a.kdim % BK) != 0;
-  auto k_off = [&](int ks) {
-    const bool half = k_tail && ks == nk - 1;
-    const int c = half ? (chunk & 3) : chunk;
-    return (int64_t)ks * BK + c * 8;
-  };
+  // load i covers tile rows 8*(8*i + wave) .. +7; for gate/up, loads 0 and 1
+  // fill the 128 gate rows of the B tile and loads 2 and 3 the up rows.
   auto dma_a = [&](int ks, int i) {
     const int j = 8 * i + wave;
-    dma16(a.A + a_row_off[i] + k_off(ks),
+    dma16(ra, a_voff[i], (uint32_t)ks * (BK * 2),
           (lds_void_t*)(lds_raw + (ks % A_SLOTS) * TILE_BYTES + j * 1024));
   };
   auto dma_b = [&](int ks, int i) {
     const int j = 8 * i + wave;
-    const int r = 8 * j + sub;
-    int brow;
-    const uint16_t* bbase;
-    if (MODE == kGateUp) {
-      brow = nt * (BN / 2) + (r & (BN / 2 - 1));
-      bbase = (r < BN / 2) ? Bexp0 : Bexp1;
-    } else {
-      brow = nt * BN + r;
-      bbase = Bexp0;
-    }
-    if (brow >= a.b_rows) brow = 0;
-    dma16(bbase + (int64_t)brow * a.kdim + k_off(ks),
+    dma16((MODE == kGateUp && i >= 2) ? rb1 : rb0, b_voff[i], (uint32_t)ks * (BK * 2),
           (lds_void_t*)(lds_raw + B_RING + (ks % B_SLOTS) * TILE_BYTES + j * 1024));
   };
 
@@ -221,22 +230,26 @@ __global__ __launch_bounds__(512, 2) void gemm_kernel(GemmArgs a) {
 
   typedef bf16x8_t afrag_t[4];
   typedef bf16x8_t bfrag_t[2];
-  auto wait_groups = [&](int younger) {  // younger load groups of 4 instructions
-    if (younger >= 3) wait_vmcnt<12>();
-    else if (younger == 2) wait_vmcnt<8>();
-    else if (younger == 1) wait_vmcnt<4>();
-    else wait_vmcnt<0>();
-  };
 
-  // Schedule (every wave, whatever its MFMA work): the prologue loads A0 B0
-  // A1 B1 B2; the barrier at the last k-step of stage kt releases A slot kt%2
-  // and B slot kt%3, and the loads of A(kt+2) and B(kt+3) are then spread
-  // over four k-steps, one per group of four MFMAs, pinned with scheduling
-  // barriers next to the LDS reads of the next k-step's fragments.  Two waves
-  // share each SIMD, so one wave's loads and LDS reads overlap the other's
-  // MFMAs.
-  auto run = [&](auto tag) {
-    constexpr int MT = decltype(tag)::value;  // 0 full, 1 partial, 2 no MFMA work
+  // Schedule (every wave, whatever its MFMA work).  The prologue loads A0 B0
+  // A1 B1 B2.  Stage kt runs four k-steps; the barrier at its last k-step
+  // releases A slot kt%2 and B slot kt%3, after which the loads of A(kt+2)
+  // (two instructions at once, two in the next stage's first k-step) and of
+  // B(kt+3) (two per k-step in that stage's second and third k-steps) are
+  // issued, each pinned with scheduling barriers next to the LDS reads of
+  // the next k-step's fragments.  Two waves share each SIMD, so one wave's
+  // loads and LDS reads overlap the other's MFMAs.
+  //
+  // The steady-state stages (1 <= kt <= nk-3) are compiled without any
+  // branch: every condition below is a compile-time constant there, so the
+  // compiler's wait counting stays exact and the MFMAs of a k-step wait only
+  // for the fragments read one k-step earlier.  The first stage and the last
+  // two are peeled with run-time conditions.  LIVE (0, 2 or 4) is the number
+  // of 32-row accumulator blocks this wave multiplies, also a compile-time
+  // constant; rows past the segment inside a live block are computed and
+  // never stored.
+  auto run = [&](auto live_tag) {
+    constexpr int LIVE = decltype(live_tag)::value;
     afrag_t A0, A1;
     bfrag_t B0, B1;
 #pragma unroll
@@ -253,73 +266,86 @@ __global__ __launch_bounds__(512, 2) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) dma_b(2, i);
     }
-    wait_groups(min(nk - 1, 1) * 2 + (nk > 2 ? 1 : 0));
+    if (nk > 2) wait_vmcnt<12>();
+    else if (nk > 1) wait_vmcnt<8>();
+    else wait_vmcnt<0>();
     block_barrier();
     auto read_frags = [&](afrag_t& A, bfrag_t& B, int kt, int ks, int q) {
       // fragments of quarter q (A frag q; B frag q for q < 2)
       const char* sa = lds_raw + (kt % A_SLOTS) * TILE_BYTES;
       const char* sbb = lds_raw + (kt % B_SLOTS) * TILE_BYTES;
       const int so = slot_of(ks);
-      A[q] = *reinterpret_cast<const bf16x8_t*>(sa + a_base + 32 * q * ROW_BYTES + so);
+      if (q < LIVE)
+        A[q] = *reinterpret_cast<const bf16x8_t*>(sa + a_base + 32 * q * ROW_BYTES + so);
       if (q < 2) B[q] = *reinterpret_cast<const bf16x8_t*>(sbb + b_base + b_row[q] * ROW_BYTES + so);
     };
-    if (MT != 2) {
+    if (LIVE > 0) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) read_frags(A0, B0, 0, 0, q);
     }
-    for (int kt = 0; kt < nk; ++kt) {
-      const bool half = k_tail && kt == nk - 1;
+    // One stage.  The flags are bools (peeled stages) or std::integral_constant
+    // (steady state):
+    //   ld_a2  - loads 0,1 of A(kt+2) after the last barrier of this stage
+    //   ld_a1  - loads 2,3 of A(kt+1) in the first k-step
+    //   ld_b   - the four loads of B(kt+2) in k-steps 1 and 2
+    //   next   - a next stage exists (barrier + its first fragments)
+    //   vm4    - at the barrier the four B(kt+2) loads may still be in flight
+    //   half   - the last 32 k of this stage are padding
+    auto stage = [&](int kt, auto ld_a2, auto ld_a1, auto ld_b, auto next, auto vm4,
+                     auto half) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         afrag_t& Ac = (ks & 1) ? A1 : A0;
         bfrag_t& Bc = (ks & 1) ? B1 : B0;
         afrag_t& An = (ks & 1) ? A0 : A1;
         bfrag_t& Bn = (ks & 1) ? B0 : B1;
-        int nkt = kt, nks = ks + 1;
-        bool have_next = true;
-        if (ks == 3) {
-          nkt = kt + 1; nks = 0;
-          have_next = kt + 1 < nk;
-          if (have_next) {
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            if (kt + 2 < nk) wait_vmcnt<4>(); else wait_vmcnt<0>();
-            block_barrier();  // every wave done with A slot kt%2 and B slot kt%3
-          }
+        const int nkt = (ks == 3) ? kt + 1 : kt;
+        const int nks = (ks == 3) ? 0 : ks + 1;
+        const bool have_next = (ks < 3) || next;
+        if (ks == 3 && next) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          if (vm4) wait_vmcnt<4>(); else wait_vmcnt<0>();
+          block_barrier();  // every wave done with A slot kt%2 and B slot kt%3
         }
-        // pending loads: ks=3 -> A(kt+2) 0,1 ; ks=0 -> A(kt+1) 2,3 ;
-        // ks=1 -> B(kt+2) 0,1 ; ks=2 -> B(kt+2) 2,3
-        int dma_kind = 0, dma_stage = 0, dma_first = 0;  // 0 none, 1 A, 2 B
-        if (ks == 3 && kt + 2 < nk) { dma_kind = 1; dma_stage = kt + 2; dma_first = 0; }
-        else if (ks == 0 && kt >= 1 && kt + 1 < nk) { dma_kind = 1; dma_stage = kt + 1; dma_first = 2; }
-        else if (ks == 1 && kt >= 1 && kt + 2 < nk) { dma_kind = 2; dma_stage = kt + 2; dma_first = 0; }
-        else if (ks == 2 && kt >= 1 && kt + 2 < nk) { dma_kind = 2; dma_stage = kt + 2; dma_first = 2; }
         const bool do_mfma = !(ks >= 2 && half);
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          if (dma_kind == 1) dma_a(dma_stage, dma_first + h2);
-          else if (dma_kind == 2) dma_b(dma_stage, dma_first + h2);
-          if (MT != 2 && have_next) {
+          if (ks == 3 && ld_a2) dma_a(kt + 2, h2);
+          if (ks == 0 && ld_a1) dma_a(kt + 1, 2 + h2);
+          if (ks == 1 && ld_b) dma_b(kt + 2, h2);
+          if (ks == 2 && ld_b) dma_b(kt + 2, 2 + h2);
+          if (LIVE > 0 && have_next) {
             read_frags(An, Bn, nkt, nks, 2 * h2);
             read_frags(An, Bn, nkt, nks, 2 * h2 + 1);
           }
           __builtin_amdgcn_sched_barrier(0);
+          if (do_mfma) {
 #pragma unroll
-          for (int mm = 0; mm < 2; ++mm) {
-            const int m = 2 * h2 + mm;
-            if (do_mfma && (MT == 0 || (MT == 1 && m < live_m))) {
+            for (int mm = 0; mm < 2; ++mm) {
+              const int m = 2 * h2 + mm;
+              if (m < LIVE) {
 #pragma unroll
-              for (int f = 0; f < 2; ++f)
-                acc[m][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ac[m], Bc[f], acc[m][f], 0, 0, 0);
+                for (int f = 0; f < 2; ++f)
+                  acc[m][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ac[m], Bc[f], acc[m][f], 0, 0, 0);
+              }
             }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-    }
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    // stage 0: its B(2) came with the prologue; A(1) is whole
+    stage(0, nk > 2, F{}, F{}, nk > 1, nk > 2, nk == 1 && k_tail);
+    // steady state: 1 <= kt <= nk-3
+    for (int kt = 1; kt + 2 < nk; ++kt) stage(kt, T{}, T{}, T{}, T{}, T{}, F{});
+    if (nk >= 3) stage(nk - 2, F{}, T{}, F{}, T{}, F{}, F{});
+    if (nk >= 2) stage(nk - 1, F{}, F{}, F{}, F{}, F{}, k_tail);
   };
-  if (!any) run(std::integral_constant<int, 2>{});
-  else if (live_m == 4) run(std::integral_constant<int, 0>{});
-  else run(std::integral_constant<int, 1>{});
+  if (!any) run(std::integral_constant<int, 0>{});
+  else if (live_m > 2) run(std::integral_constant<int, 4>{});
+  else run(std::integral_constant<int, 2>{});
 
   // ---- epilogue: lane holds column (lane & 31) and, for register r, row
   // 8*(r/4) + 4*(lane/32) + r%4 of each 32 x 32 accumulator.
@@ -432,10 +458,11 @@ hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w_router,
   a.tiles = nullptr; a.n_tiles = nullptr; a.rows_dense = N;
   a.B0 = w_router; a.B1 = nullptr; a.b_expert_stride = 0; a.b_rows = E; a.kdim = d;
   a.n_tiles_n = (E + BN - 1) / BN; a.out = Z; a.ldo = E; a.offset = offset;
+  a.a_bytes = (uint32_t)(N * d * 2);
   return launch_gemm(kRouter, a, (N + BM - 1) / BM, stream);
 }
 
-hipError_t launch_gateup(const uint16_t* x, const int32_t* sorted_src, int K,
+hipError_t launch_gateup(const uint16_t* x, int64_t x_rows, const int32_t* sorted_src, int K,
                          const int32_t* tiles, const int32_t* n_tiles, int64_t max_tiles,
                          int64_t rows_dense, const uint16_t* w_gate,
                          const uint16_t* w_up, int d, int h, uint16_t* H,
@@ -445,11 +472,12 @@ hipError_t launch_gateup(const uint16_t* x, const int32_t* sorted_src, int K,
   a.tiles = tiles; a.n_tiles = n_tiles; a.rows_dense = rows_dense;
   a.B0 = w_gate; a.B1 = w_up; a.b_expert_stride = (int64_t)h * d; a.b_rows = h; a.kdim = d;
   a.n_tiles_n = (h + BN / 2 - 1) / (BN / 2); a.out = H; a.ldo = h; a.offset = nullptr;
+  a.a_bytes = (uint32_t)(x_rows * d * 2);
   const int64_t mt = tiles ? max_tiles : (rows_dense + BM - 1) / BM;
   return launch_gemm(kGateUp, a, mt, stream);
 }
 
-hipError_t launch_down(const uint16_t* H, const int32_t* tiles, const int32_t* n_tiles,
+hipError_t launch_down(const uint16_t* H, int64_t h_rows, const int32_t* tiles, const int32_t* n_tiles,
                        int64_t max_tiles, int64_t rows_dense, const uint16_t* w_down,
                        int d, int h, uint16_t* Y, hipStream_t stream) {
   GemmArgs a{};
@@ -457,6 +485,7 @@ hipError_t launch_down(const uint16_t* H, const int32_t* tiles, const int32_t* n
   a.tiles = tiles; a.n_tiles = n_tiles; a.rows_dense = rows_dense;
   a.B0 = w_down; a.B1 = nullptr; a.b_expert_stride = (int64_t)d * h; a.b_rows = d; a.kdim = h;
   a.n_tiles_n = (d + BN - 1) / BN; a.out = Y; a.ldo = d; a.offset = nullptr;
+  a.a_bytes = (uint32_t)(h_rows * h * 2);
   const int64_t mt = tiles ? max_tiles : (rows_dense + BM - 1) / BM;
   return launch_gemm(kDown, a, mt, stream);
 }

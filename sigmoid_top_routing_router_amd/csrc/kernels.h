@@ -53,21 +53,22 @@ hipError_t launch_count(const int32_t* ids, int64_t pairs, int E, int32_t* count
                         hipStream_t stream);
 
 // ---------------------------------------------------------------- GEMMs
-// Router logits Z[N,E] = x[N,d] W_r[E,d]^T (+ offset[E]) in fp32.
+// Router logits Z[N,E] = x[N,d] W_r[E,d]^T (+ offset[E]) in fp32; N*d*2 < 4 GiB.
 hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w_router,
                               const float* offset, int64_t N, int d, int E, float* Z,
                               hipStream_t stream);
 // Grouped SwiGLU gate/up: for every m-tile of the table, H rows =
 // silu(X W_g^T) * (X W_u^T) (bf16).  When `tiles` is NULL the rows are the
 // tokens 0..N-1 of one expert (shared expert), otherwise A rows are gathered
-// through sorted_src / K.
-hipError_t launch_gateup(const uint16_t* x, const int32_t* sorted_src, int K,
+// through sorted_src / K.  x has x_rows rows; x_rows * d * 2 < 4 GiB.
+hipError_t launch_gateup(const uint16_t* x, int64_t x_rows, const int32_t* sorted_src, int K,
                          const int32_t* tiles, const int32_t* n_tiles, int64_t max_tiles,
                          int64_t rows_dense, const uint16_t* w_gate,
                          const uint16_t* w_up, int d, int h, uint16_t* H,
                          hipStream_t stream);
-// Grouped down projection: Y rows = H rows W_d^T (bf16 out).
-hipError_t launch_down(const uint16_t* H, const int32_t* tiles, const int32_t* n_tiles,
+// Grouped down projection: Y rows = H rows W_d^T (bf16 out).  H has h_rows
+// rows; h_rows * h * 2 < 4 GiB.
+hipError_t launch_down(const uint16_t* H, int64_t h_rows, const int32_t* tiles, const int32_t* n_tiles,
                        int64_t max_tiles, int64_t rows_dense, const uint16_t* w_down,
                        int d, int h, uint16_t* Y, hipStream_t stream);
 int gemm_bm();

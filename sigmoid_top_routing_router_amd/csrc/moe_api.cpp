@@ -148,6 +148,15 @@ moe_status_t check_problem(const moe_problem_t* p) {
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "n_shared=%d must be 0 or 1", p->n_shared);
   if (p->n_shared == 1 && (p->h_shared < 32 || p->h_shared > 4096 || p->h_shared % 32))
     return fail(MOE_ERR_UNSUPPORTED_SHAPE, "h_shared=%d must be a multiple of 32 in [32, 4096]", p->h_shared);
+  // the GEMMs address x, H and the shared H with 32-bit byte offsets
+  const uint64_t lim = 0xFFFFFFFFull;
+  if ((uint64_t)p->N * (uint64_t)p->d * 2u > lim ||
+      (uint64_t)p->N * (uint64_t)p->K * (uint64_t)p->h * 2u > lim ||
+      (p->n_shared == 1 && (uint64_t)p->N * (uint64_t)p->h_shared * 2u > lim))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE,
+                "N=%lld too large: x [N,d], the routed hidden rows [N*K,h] and the shared "
+                "hidden rows [N,h_shared] must each be below 4 GiB in bf16",
+                (long long)p->N);
   if (p->flags & ~(MOE_RECOMPUTE_BIAS | MOE_KEY32))
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", p->flags);
   if (p->logits_in && p->logit_offset)
@@ -412,19 +421,19 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_weights_t* w, const u
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
 
   // a6-a8: routed experts (gather fused into the gate/up A loads)
-  MOE_TRY_HIP(moe::launch_gateup(x, pw.sorted_src, K, pw.tiles, pw.n_tiles, l.max_tiles, 0,
+  MOE_TRY_HIP(moe::launch_gateup(x, N, pw.sorted_src, K, pw.tiles, pw.n_tiles, l.max_tiles, 0,
                                  w->w_gate, w->w_up, d, h, l.H, st), "moe_forward: gate/up");
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
-  MOE_TRY_HIP(moe::launch_down(l.H, pw.tiles, pw.n_tiles, l.max_tiles, 0, w->w_down, d, h, l.Y, st),
+  MOE_TRY_HIP(moe::launch_down(l.H, N * K, pw.tiles, pw.n_tiles, l.max_tiles, 0, w->w_down, d, h, l.Y, st),
               "moe_forward: down");
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
   // a9: shared expert over all tokens
   if (p->n_shared == 1)
-    MOE_TRY_HIP(moe::launch_gateup(x, nullptr, 1, nullptr, nullptr, 0, N, w->ws_gate, w->ws_up, d,
+    MOE_TRY_HIP(moe::launch_gateup(x, N, nullptr, 1, nullptr, nullptr, 0, N, w->ws_gate, w->ws_up, d,
                                    p->h_shared, l.Hs, st), "moe_forward: shared gate/up");
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
   if (p->n_shared == 1)
-    MOE_TRY_HIP(moe::launch_down(l.Hs, nullptr, nullptr, 0, N, w->ws_down, d, p->h_shared, l.sh, st),
+    MOE_TRY_HIP(moe::launch_down(l.Hs, N, nullptr, nullptr, 0, N, w->ws_down, d, p->h_shared, l.sh, st),
                 "moe_forward: shared down");
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
   // a10: weighted combine
