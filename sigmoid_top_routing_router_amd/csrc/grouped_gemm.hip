@@ -168,39 +168,50 @@ __global__ __launch_bounds__(512, 2) void gemm_kernel(GemmArgs a) {
   const int chunk = (lane & 7) ^ (sub & 7);
   // Byte offsets of each lane's 16-byte piece, fixed for the whole tile; the
   // stage's k offset goes in the scalar offset of the load.  Rows past the
-  // segment load the segment's first row (never stored); B rows past the
-  // matrix load its row 0.
+  // segment and B rows past the matrix get an offset beyond the end of the
+  // buffer: the load returns zeros without a memory access, and those rows
+  // are never stored.
+  constexpr uint32_t kNoRow = 0xFFFFFFFFu - 16u * 1024u;  // past any 4 GiB buffer
   uint32_t a_voff[4], b_voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 8 * (8 * i + wave) + sub;
-    int64_t arow = row0 + ((r < rows) ? r : 0);
-    if (GROUPED && a.gather) arow = a.gather[arow] / a.gather_div;
-    a_voff[i] = (uint32_t)(arow * a.lda * 2) + (uint32_t)chunk * 16u;
-    int brow = (MODE == kGateUp) ? nt * (BN / 2) + (r & (BN / 2 - 1)) : nt * BN + r;
-    if (brow >= a.b_rows) brow = 0;
-    b_voff[i] = (uint32_t)brow * (uint32_t)a.kdim * 2u + (uint32_t)chunk * 16u;
+    if (r < rows) {
+      int64_t arow = row0 + r;
+      if (GROUPED && a.gather) arow = a.gather[arow] / a.gather_div;
+      a_voff[i] = (uint32_t)(arow * a.lda * 2) + (uint32_t)chunk * 16u;
+    } else {
+      a_voff[i] = kNoRow;
+    }
+    const int brow = (MODE == kGateUp) ? nt * (BN / 2) + (r & (BN / 2 - 1)) : nt * BN + r;
+    b_voff[i] = (brow < a.b_rows) ? (uint32_t)brow * (uint32_t)a.kdim * 2u + (uint32_t)chunk * 16u
+                                  : kNoRow;
   }
   const uint32_t b_bytes = (uint32_t)a.b_rows * (uint32_t)a.kdim * 2u;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, a.a_bytes);
   const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(a.B0 + (int64_t)expert * a.b_expert_stride, b_bytes);
   const __amdgpu_buffer_rsrc_t rb1 =
       make_rsrc((MODE == kGateUp ? a.B1 : a.B0) + (int64_t)expert * a.b_expert_stride, b_bytes);
-  // K tail: kdim % 64 == 32 leaves a last stage with 32 valid k.  Its upper
-  // chunks read past the end of the row (the next row, or zeros past the end
-  // of the buffer) and are never multiplied.
+  // K tail: kdim % 64 == 32 leaves a last stage with 32 valid k.  There the
+  // upper four chunks of each row are loaded from the lower four (64 bytes
+  // lower), so every access stays inside its row; they are never multiplied.
   const int nk = (a.kdim + BK - 1) / BK;
   const bool k_tail = (a.kdim % BK) != 0;
+  const uint32_t tail_adj = (chunk >= 4) ? 64u : 0u;
+  auto voff_at = [&](uint32_t v, int ks) {
+    return (k_tail && ks == nk - 1) ? v - tail_adj : v;
+  };
   // load i covers tile rows 8*(8*i + wave) .. +7; for gate/up, loads 0 and 1
   // fill the 128 gate rows of the B tile and loads 2 and 3 the up rows.
   auto dma_a = [&](int ks, int i) {
     const int j = 8 * i + wave;
-    dma16(ra, a_voff[i], (uint32_t)ks * (BK * 2),
+    dma16(ra, voff_at(a_voff[i], ks), (uint32_t)ks * (BK * 2),
           (lds_void_t*)(lds_raw + (ks % A_SLOTS) * TILE_BYTES + j * 1024));
   };
   auto dma_b = [&](int ks, int i) {
     const int j = 8 * i + wave;
-    dma16((MODE == kGateUp && i >= 2) ? rb1 : rb0, b_voff[i], (uint32_t)ks * (BK * 2),
+    dma16((MODE == kGateUp && i >= 2) ? rb1 : rb0, voff_at(b_voff[i], ks),
+          (uint32_t)ks * (BK * 2),
           (lds_void_t*)(lds_raw + B_RING + (ks % B_SLOTS) * TILE_BYTES + j * 1024));
   };
 
