@@ -184,12 +184,13 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_weights_t* w,
  * moe_stage_times waits for the recorded events, writes the summed
  * milliseconds of each stage since the previous read into
  * ms[MOE_NUM_STAGES], the number of recorded calls into *calls, and clears
- * the record.  Stages: 0 router GEMM, 1 routing (selection, token bias,
- * quantile update, re-route, loads), 2 grouping, 3 routed gate/up GEMM,
- * 4 routed down GEMM, 5 shared gate/up GEMM, 6 shared down GEMM, 7 combine.
+ * the record.  Stages: 0 router GEMM and shared-expert gate/up GEMM (one
+ * launch), 1 routing (selection, token bias, quantile update, re-route,
+ * loads), 2 grouping, 3 routed gate/up GEMM, 4 routed down GEMM, 5 shared
+ * down GEMM, 6 weighted combine.
  * Errors: INVALID_ARGUMENT (NULL outputs), HIP.
  */
-#define MOE_NUM_STAGES 8
+#define MOE_NUM_STAGES 7
 moe_status_t moe_stage_timing(int32_t enable);
 moe_status_t moe_stage_times(double* ms, int64_t* calls);
 const char* moe_stage_name(int32_t stage);

@@ -23,7 +23,7 @@ EXPORTED = ["moe_route", "moe_eqb_workspace_bytes", "moe_eqb_bias",
             "moe_forward_workspace_bytes", "moe_forward", "moe_status_string",
             "moe_last_error_message", "moe_abi_version", "moe_stage_timing",
             "moe_stage_times", "moe_stage_name"]
-NUM_STAGES = 8
+NUM_STAGES = 7
 
 
 class MoeProblem(C.Structure):

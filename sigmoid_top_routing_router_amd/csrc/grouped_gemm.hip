@@ -125,23 +125,23 @@ __device__ __forceinline__ uint16_t f32_to_bf16_u16(float v) {
   return (uint16_t)f32_to_bf16_rne_bits(v);
 }
 
-// GROUPED: rows come from the m-tile table (routed experts); otherwise the
-// rows are 0 .. rows_dense-1 (router, shared expert).
-template <int MODE, bool GROUPED>
-__global__ __launch_bounds__(512, 2) void gemm_kernel(GemmArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
-
-  // ---- which tile -------------------------------------------------------
-  const int64_t m_tiles = GROUPED ? (int64_t)(*a.n_tiles) : (a.rows_dense + BM - 1) / BM;
-  const int64_t work = m_tiles * a.n_tiles_n;
+// Logical tile of this block: workgroups are dealt round-robin to the XCDs,
+// so block b takes tile (b % 8) * share + b / 8 and each XCD walks a
+// contiguous run.  Returns false for surplus blocks.
+__device__ __forceinline__ bool xcd_tile(int64_t work, int64_t& logical) {
   const int64_t share = (work + kXcd - 1) / kXcd;
   const int64_t local = blockIdx.x / kXcd;
-  if (local >= share) return;
-  const int64_t logical = (int64_t)(blockIdx.x % kXcd) * share + local;
-  if (logical >= work) return;
-  const int64_t mt = logical / a.n_tiles_n;
-  const int nt = (int)(logical % a.n_tiles_n);
+  if (local >= share) return false;
+  logical = (int64_t)(blockIdx.x % kXcd) * share + local;
+  return logical < work;
+}
 
+// One 256 x 256 output tile (m-tile mt, n-tile nt).  GROUPED: rows come from
+// the m-tile table (routed experts); otherwise the rows are
+// 0 .. rows_dense-1 (router, shared expert).
+template <int MODE, bool GROUPED>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
+                                          char* lds_raw) {
   int expert = 0;
   int64_t row0;
   int rows;
@@ -429,6 +429,31 @@ __global__ __launch_bounds__(512, 2) void gemm_kernel(GemmArgs a) {
 }
 
 template <int MODE, bool GROUPED>
+__global__ __launch_bounds__(512, 2) void gemm_kernel(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  const int64_t m_tiles = GROUPED ? (int64_t)(*a.n_tiles) : (a.rows_dense + BM - 1) / BM;
+  int64_t logical;
+  if (!xcd_tile(m_tiles * a.n_tiles_n, logical)) return;
+  gemm_tile<MODE, GROUPED>(a, logical / a.n_tiles_n, (int)(logical % a.n_tiles_n), lds_raw);
+}
+
+// The two products over x before routing in one launch: the router logits
+// (first r.n_tiles_n column tiles of every m-tile) and the shared expert's
+// gate/up (the next g.n_tiles_n).  The column tiles of one m-tile are
+// neighbours in the XCD walk, so each x row block is fetched from HBM once.
+__global__ __launch_bounds__(512, 2) void gemm_x_kernel(GemmArgs r, GemmArgs g) {
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  const int64_t m_tiles = (r.rows_dense + BM - 1) / BM;
+  const int n_all = r.n_tiles_n + g.n_tiles_n;
+  int64_t logical;
+  if (!xcd_tile(m_tiles * n_all, logical)) return;
+  const int64_t mt = logical / n_all;
+  const int nt = (int)(logical % n_all);
+  if (nt < r.n_tiles_n) gemm_tile<kRouter, false>(r, mt, nt, lds_raw);
+  else gemm_tile<kGateUp, false>(g, mt, nt - r.n_tiles_n, lds_raw);
+}
+
+template <int MODE, bool GROUPED>
 static hipError_t launch_mode(const GemmArgs& a, dim3 grid, hipStream_t stream) {
   static bool configured = false;
   if (!configured) {
@@ -461,16 +486,47 @@ static hipError_t launch_gemm(int mode, const GemmArgs& a, int64_t max_m_tiles,
   }
 }
 
-hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w_router,
-                              const float* offset, int64_t N, int d, int E, float* Z,
-                              hipStream_t stream) {
+static GemmArgs router_args(const uint16_t* x, const uint16_t* w_router, const float* offset,
+                            int64_t N, int d, int E, float* Z) {
   GemmArgs a{};
   a.A = x; a.lda = d; a.gather = nullptr; a.gather_div = 1;
   a.tiles = nullptr; a.n_tiles = nullptr; a.rows_dense = N;
   a.B0 = w_router; a.B1 = nullptr; a.b_expert_stride = 0; a.b_rows = E; a.kdim = d;
   a.n_tiles_n = (E + BN - 1) / BN; a.out = Z; a.ldo = E; a.offset = offset;
   a.a_bytes = (uint32_t)(N * d * 2);
-  return launch_gemm(kRouter, a, (N + BM - 1) / BM, stream);
+  return a;
+}
+
+static GemmArgs gateup_args(const uint16_t* x, int64_t x_rows, const int32_t* sorted_src, int K,
+                            const int32_t* tiles, const int32_t* n_tiles, int64_t rows_dense,
+                            const uint16_t* w_gate, const uint16_t* w_up, int d, int h,
+                            uint16_t* H) {
+  GemmArgs a{};
+  a.A = x; a.lda = d; a.gather = tiles ? sorted_src : nullptr; a.gather_div = K;
+  a.tiles = tiles; a.n_tiles = n_tiles; a.rows_dense = rows_dense;
+  a.B0 = w_gate; a.B1 = w_up; a.b_expert_stride = (int64_t)h * d; a.b_rows = h; a.kdim = d;
+  a.n_tiles_n = (h + BN / 2 - 1) / (BN / 2); a.out = H; a.ldo = h; a.offset = nullptr;
+  a.a_bytes = (uint32_t)(x_rows * d * 2);
+  return a;
+}
+
+static GemmArgs down_args(const uint16_t* H, int64_t h_rows, const int32_t* tiles,
+                          const int32_t* n_tiles, int64_t rows_dense, const uint16_t* w_down,
+                          int d, int h, uint16_t* Y) {
+  GemmArgs a{};
+  a.A = H; a.lda = h; a.gather = nullptr; a.gather_div = 1;
+  a.tiles = tiles; a.n_tiles = n_tiles; a.rows_dense = rows_dense;
+  a.B0 = w_down; a.B1 = nullptr; a.b_expert_stride = (int64_t)d * h; a.b_rows = d; a.kdim = h;
+  a.n_tiles_n = (d + BN - 1) / BN; a.out = Y; a.ldo = d; a.offset = nullptr;
+  a.a_bytes = (uint32_t)(h_rows * h * 2);
+  return a;
+}
+
+hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w_router,
+                              const float* offset, int64_t N, int d, int E, float* Z,
+                              hipStream_t stream) {
+  return launch_gemm(kRouter, router_args(x, w_router, offset, N, d, E, Z), (N + BM - 1) / BM,
+                     stream);
 }
 
 hipError_t launch_gateup(const uint16_t* x, int64_t x_rows, const int32_t* sorted_src, int K,
@@ -478,12 +534,8 @@ hipError_t launch_gateup(const uint16_t* x, int64_t x_rows, const int32_t* sorte
                          int64_t rows_dense, const uint16_t* w_gate,
                          const uint16_t* w_up, int d, int h, uint16_t* H,
                          hipStream_t stream) {
-  GemmArgs a{};
-  a.A = x; a.lda = d; a.gather = tiles ? sorted_src : nullptr; a.gather_div = K;
-  a.tiles = tiles; a.n_tiles = n_tiles; a.rows_dense = rows_dense;
-  a.B0 = w_gate; a.B1 = w_up; a.b_expert_stride = (int64_t)h * d; a.b_rows = h; a.kdim = d;
-  a.n_tiles_n = (h + BN / 2 - 1) / (BN / 2); a.out = H; a.ldo = h; a.offset = nullptr;
-  a.a_bytes = (uint32_t)(x_rows * d * 2);
+  const GemmArgs a = gateup_args(x, x_rows, sorted_src, K, tiles, n_tiles, rows_dense, w_gate,
+                                 w_up, d, h, H);
   const int64_t mt = tiles ? max_tiles : (rows_dense + BM - 1) / BM;
   return launch_gemm(kGateUp, a, mt, stream);
 }
@@ -491,14 +543,35 @@ hipError_t launch_gateup(const uint16_t* x, int64_t x_rows, const int32_t* sorte
 hipError_t launch_down(const uint16_t* H, int64_t h_rows, const int32_t* tiles, const int32_t* n_tiles,
                        int64_t max_tiles, int64_t rows_dense, const uint16_t* w_down,
                        int d, int h, uint16_t* Y, hipStream_t stream) {
-  GemmArgs a{};
-  a.A = H; a.lda = h; a.gather = nullptr; a.gather_div = 1;
-  a.tiles = tiles; a.n_tiles = n_tiles; a.rows_dense = rows_dense;
-  a.B0 = w_down; a.B1 = nullptr; a.b_expert_stride = (int64_t)d * h; a.b_rows = d; a.kdim = h;
-  a.n_tiles_n = (d + BN - 1) / BN; a.out = Y; a.ldo = d; a.offset = nullptr;
-  a.a_bytes = (uint32_t)(h_rows * h * 2);
+  const GemmArgs a = down_args(H, h_rows, tiles, n_tiles, rows_dense, w_down, d, h, Y);
   const int64_t mt = tiles ? max_tiles : (rows_dense + BM - 1) / BM;
   return launch_gemm(kDown, a, mt, stream);
+}
+
+static dim3 xcd_grid(int64_t work) {
+  const int64_t share = (work + kXcd - 1) / kXcd;
+  return dim3((unsigned)(share * kXcd));
+}
+
+hipError_t launch_router_shared_gateup(const uint16_t* x, int64_t N, int d,
+                                       const uint16_t* w_router, const float* offset, int E,
+                                       float* Z, const uint16_t* ws_gate,
+                                       const uint16_t* ws_up, int hs, uint16_t* Hs,
+                                       hipStream_t stream) {
+  const GemmArgs r = router_args(x, w_router, offset, N, d, E, Z);
+  const GemmArgs g = gateup_args(x, N, nullptr, 1, nullptr, nullptr, N, ws_gate, ws_up, d, hs, Hs);
+  const int64_t work = ((N + BM - 1) / BM) * (r.n_tiles_n + g.n_tiles_n);
+  if (work <= 0) return hipSuccess;
+  if (work > 0x7FFFFFF0LL) return hipErrorInvalidConfiguration;
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_x_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  hipLaunchKernelGGL(gemm_x_kernel, xcd_grid(work), dim3(512), LDS_BYTES, stream, r, g);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -72,6 +72,13 @@ hipError_t launch_down(const uint16_t* H, int64_t h_rows, const int32_t* tiles, 
                        int64_t max_tiles, int64_t rows_dense, const uint16_t* w_down,
                        int d, int h, uint16_t* Y, hipStream_t stream);
 int gemm_bm();
+// Router logits and the shared expert's gate/up in one launch (both read x).
+hipError_t launch_router_shared_gateup(const uint16_t* x, int64_t N, int d,
+                                       const uint16_t* w_router, const float* offset, int E,
+                                       float* Z, const uint16_t* ws_gate,
+                                       const uint16_t* ws_up, int hs, uint16_t* Hs,
+                                       hipStream_t stream);
+
 
 // ---------------------------------------------------------------- combine
 // y[t] = sh[t] + sum_k S[t,k] * Y[src_pos[t,k]]  (sh may be NULL)

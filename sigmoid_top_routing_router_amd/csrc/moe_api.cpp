@@ -250,8 +250,8 @@ moe_status_t moe_stage_times(double* ms, int64_t* calls) {
 }
 
 const char* moe_stage_name(int32_t stage) {
-  static const char* names[MOE_NUM_STAGES] = {"router_gemm", "routing", "grouping", "gate_up",
-                                              "down", "shared_gate_up", "shared_down", "combine"};
+  static const char* names[MOE_NUM_STAGES] = {"router_shared_gate_up", "routing", "grouping",
+                                              "gate_up", "down", "shared_down", "combine"};
   return (stage >= 0 && stage < MOE_NUM_STAGES) ? names[stage] : "";
 }
 
@@ -368,17 +368,29 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_weights_t* w, const u
   CallTimer tm;
   MOE_TRY_HIP(tm.start(st), "moe_forward: stage timer");
 
-  // a1: router logits
+  // a1 router logits and a9 (first half) the shared expert's gate/up: both
+  // read x, so they share one launch
   const float* Z;
+  const bool shared = p->n_shared == 1;
   if (p->logits_in) {
     Z = p->logits_in;
     if (A.logits)
       MOE_TRY_HIP(hipMemcpyAsync(A.logits, Z, (size_t)N * E * 4, hipMemcpyDeviceToDevice, st),
                   "moe_forward: logits copy");
+    if (shared)
+      MOE_TRY_HIP(moe::launch_gateup(x, N, nullptr, 1, nullptr, nullptr, 0, N, w->ws_gate,
+                                     w->ws_up, d, p->h_shared, l.Hs, st),
+                  "moe_forward: shared gate/up");
   } else {
     float* zout = A.logits ? A.logits : l.Z;
-    MOE_TRY_HIP(moe::launch_router_gemm(x, w->w_router, p->logit_offset, N, d, E, zout, st),
-                "moe_forward: router GEMM");
+    if (shared)
+      MOE_TRY_HIP(moe::launch_router_shared_gateup(x, N, d, w->w_router, p->logit_offset, E,
+                                                   zout, w->ws_gate, w->ws_up, p->h_shared,
+                                                   l.Hs, st),
+                  "moe_forward: router GEMM + shared gate/up");
+    else
+      MOE_TRY_HIP(moe::launch_router_gemm(x, w->w_router, p->logit_offset, N, d, E, zout, st),
+                  "moe_forward: router GEMM");
     Z = zout;
   }
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
@@ -427,17 +439,13 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_weights_t* w, const u
   MOE_TRY_HIP(moe::launch_down(l.H, N * K, pw.tiles, pw.n_tiles, l.max_tiles, 0, w->w_down, d, h, l.Y, st),
               "moe_forward: down");
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
-  // a9: shared expert over all tokens
-  if (p->n_shared == 1)
-    MOE_TRY_HIP(moe::launch_gateup(x, N, nullptr, 1, nullptr, nullptr, 0, N, w->ws_gate, w->ws_up, d,
-                                   p->h_shared, l.Hs, st), "moe_forward: shared gate/up");
-  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
-  if (p->n_shared == 1)
-    MOE_TRY_HIP(moe::launch_down(l.Hs, N, nullptr, nullptr, 0, N, w->ws_down, d, p->h_shared, l.sh, st),
-                "moe_forward: shared down");
+  // a9 (second half): the shared expert's down projection
+  if (shared)
+    MOE_TRY_HIP(moe::launch_down(l.Hs, N, nullptr, nullptr, 0, N, w->ws_down, d, p->h_shared,
+                                 l.sh, st), "moe_forward: shared down");
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
   // a10: weighted combine
-  MOE_TRY_HIP(moe::launch_combine(p->n_shared == 1 ? l.sh : nullptr, l.Y, S, pw.src_pos, N, K, d, y, st),
+  MOE_TRY_HIP(moe::launch_combine(shared ? l.sh : nullptr, l.Y, S, pw.src_pos, N, K, d, y, st),
               "moe_forward: combine");
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
   return ok();
