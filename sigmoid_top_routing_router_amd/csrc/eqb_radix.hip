@@ -31,6 +31,9 @@ namespace moe {
 constexpr int kEqbCols = 64;
 constexpr int kEqbPad = 257;
 constexpr int kEqbMaxE = 384;
+constexpr int kEqbThreads = 512;              // 8 waves: 8 rows at a time
+constexpr int kEqbRowLanes = kEqbThreads / kEqbCols;
+constexpr int kEqbUnroll = 12;                // rows per lane with loads in flight
 
 // Histograms of all passes, then a 64-word tail whose first word is the
 // ticket counter of the centring step (zeroed together with the histograms).
@@ -40,16 +43,16 @@ size_t eqb_hist_bytes(int E, int key_bits) {
 size_t eqb_state_bytes(int E) { return (size_t)(2 * E + 4) * sizeof(uint32_t); }
 
 template <int KB>
-__global__ __launch_bounds__(256) void eqb_hist_kernel(
+__global__ __launch_bounds__(kEqbThreads) void eqb_hist_kernel(
     const float* __restrict__ Z, const float* __restrict__ alpha, int64_t N, int E,
     int pass, int64_t rows_per_block, const uint32_t* __restrict__ prefix,
     uint32_t* __restrict__ hist) {
   __shared__ uint32_t lh[kEqbCols * kEqbPad];
-  __shared__ int lo_s[4][kEqbCols], hi_s[4][kEqbCols];
+  __shared__ int lo_s[kEqbRowLanes][kEqbCols], hi_s[kEqbRowLanes][kEqbCols];
   const int cl = threadIdx.x & (kEqbCols - 1);
   const int rs = threadIdx.x >> 6;
   const int e = blockIdx.x * kEqbCols + cl;
-  for (int i = threadIdx.x; i < kEqbCols * kEqbPad; i += 256) lh[i] = 0u;
+  for (int i = threadIdx.x; i < kEqbCols * kEqbPad; i += kEqbThreads) lh[i] = 0u;
   __syncthreads();
 
   const int shift = KB - 8 * (pass + 1);
@@ -71,28 +74,33 @@ __global__ __launch_bounds__(256) void eqb_hist_kernel(
       }
     };
     int64_t t = r0 + rs;
-    for (; t + 12 < r1; t += 16) {  // four rows of this lane per trip, loads first
-      float z[4], al[4];
+    constexpr int kTrip = kEqbUnroll * kEqbRowLanes;
+    for (; t + (kTrip - kEqbRowLanes) < r1; t += kTrip) {  // loads of the whole trip first
+      float z[kEqbUnroll], al[kEqbUnroll];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        z[u] = Z[(t + 4 * u) * E + e];
-        al[u] = alpha[t + 4 * u];
+      for (int u = 0; u < kEqbUnroll; ++u) {
+        z[u] = Z[(t + kEqbRowLanes * u) * E + e];
+        al[u] = alpha[t + kEqbRowLanes * u];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) count(z[u] + al[u]);
+      for (int u = 0; u < kEqbUnroll; ++u) count(z[u] + al[u]);
     }
-    for (; t < r1; t += 4) count(Z[t * E + e] + alpha[t]);
+    for (; t < r1; t += kEqbRowLanes) count(Z[t * E + e] + alpha[t]);
   }
   lo_s[rs][cl] = lo;
   hi_s[rs][cl] = hi;
   __syncthreads();
-  // flush: wave w takes columns w, w+4, ...; its lanes walk the touched bins
+  // flush: wave w takes columns w, w+8, ...; its lanes walk the touched bins
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int c = w; c < kEqbCols; c += 4) {
+  for (int c = w; c < kEqbCols; c += kEqbRowLanes) {
     const int ee = blockIdx.x * kEqbCols + c;
     if (ee >= E) break;
-    const int clo = min(min(lo_s[0][c], lo_s[1][c]), min(lo_s[2][c], lo_s[3][c]));
-    const int chi = max(max(hi_s[0][c], hi_s[1][c]), max(hi_s[2][c], hi_s[3][c]));
+    int clo = lo_s[0][c], chi = hi_s[0][c];
+#pragma unroll
+    for (int q = 1; q < kEqbRowLanes; ++q) {
+      clo = min(clo, lo_s[q][c]);
+      chi = max(chi, hi_s[q][c]);
+    }
     for (int b = clo + lane; b <= chi; b += 64) {
       const uint32_t cnt = lh[c * kEqbPad + b];
       if (cnt != 0u) atomicAdd(hist + (size_t)ee * 256 + b, cnt);
@@ -177,12 +185,13 @@ hipError_t launch_eqb(const float* Z, const float* alpha, int64_t N, int E, int 
   uint32_t* rank = w.state + E;
   uint32_t* ticket = w.hist + (size_t)passes * E * 256;
   const int col_groups = (E + kEqbCols - 1) / kEqbCols;
+  // about two blocks (66 KB of LDS each) per CU, each over a slab of rows
   int64_t chunks = (512 + col_groups - 1) / col_groups;
   int64_t rows_per_block = (N + chunks - 1) / chunks;
-  if (rows_per_block < 64) rows_per_block = 64;
-  rows_per_block = (rows_per_block + 3) / 4 * 4;
+  if (rows_per_block < 96) rows_per_block = 96;
+  rows_per_block = (rows_per_block + kEqbRowLanes - 1) / kEqbRowLanes * kEqbRowLanes;
   chunks = (N + rows_per_block - 1) / rows_per_block;
-  const dim3 hgrid((unsigned)col_groups, (unsigned)chunks), block(256);
+  const dim3 hgrid((unsigned)col_groups, (unsigned)chunks), block(kEqbThreads);
   const dim3 sgrid((unsigned)((E + 3) / 4));
   for (int p = 0; p < passes; ++p) {
     uint32_t* hp = w.hist + (size_t)p * E * 256;
@@ -192,7 +201,7 @@ hipError_t launch_eqb(const float* Z, const float* alpha, int64_t N, int E, int 
     else
       hipLaunchKernelGGL(eqb_hist_kernel<32>, hgrid, block, 0, stream, Z, alpha, N, E, p,
                          rows_per_block, prefix, hp);
-    hipLaunchKernelGGL(eqb_scan_kernel, sgrid, block, 0, stream, hp, prefix, rank, E, p,
+    hipLaunchKernelGGL(eqb_scan_kernel, sgrid, dim3(256), 0, stream, hp, prefix, rank, E, p,
                        p == passes - 1 ? 1 : 0, key_bits, (uint32_t)(r + 1), w.qraw,
                        quantile_out, ticket, beta_out);
   }

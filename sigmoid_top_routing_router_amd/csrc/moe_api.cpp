@@ -401,7 +401,9 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_weights_t* w, const u
   float* alpha = A.alpha ? A.alpha : l.alpha;
   float* margin = A.margin ? A.margin : l.margin;
   if (recompute) {
-    MOE_TRY_HIP(moe::launch_route(Z, beta_in, N, E, K, l.ids0, nullptr, alpha, nullptr, st),
+    // first pass: alpha only, unless the loads before the update are wanted
+    MOE_TRY_HIP(moe::launch_route(Z, beta_in, N, E, K, A.counts_before ? l.ids0 : nullptr,
+                                  nullptr, alpha, nullptr, st),
                 "moe_forward: first routing");
     if (A.counts_before)
       MOE_TRY_HIP(moe::launch_count(l.ids0, N * K, E, A.counts_before, st), "moe_forward: loads");

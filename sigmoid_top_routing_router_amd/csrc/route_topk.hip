@@ -14,12 +14,16 @@
 // rounds of a wave-wide max over the lanes' current heads then pick the
 // winners in global order; ties between lanes go to the lower expert id
 // through a second (rare) min-reduction.  The row is read once from HBM.
+//
+// ALPHA_ONLY (the first pass of a bias update, which needs alpha alone): the
+// value of the (K+1)-th largest key does not depend on how ties are ordered,
+// so only keys are sorted and popped, with no tie-break and no ids.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-template <int NV>
+template <int NV, bool ALPHA_ONLY>
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ Z, const float* __restrict__ beta, int64_t N, int E,
     int K, int32_t* __restrict__ ids, float* __restrict__ S,
@@ -60,6 +64,34 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
       zv[j] = cur[j];
       key[j] = (e < E) ? f32_order_key(cur[j] + bv[j]) : 0u;  // 0: below every finite value
       eid[j] = (uint32_t)e;
+    }
+    if (ALPHA_ONLY) {
+#pragma unroll
+      for (int i = 1; i < NV; ++i) {
+#pragma unroll
+        for (int j = i; j > 0; --j) {
+          const uint32_t k0 = key[j - 1], k1 = key[j];
+          key[j - 1] = max(k0, k1);
+          key[j] = min(k0, k1);
+        }
+      }
+      uint32_t m = 0u;
+#pragma unroll
+      for (int k = 0; k <= MOE_KMAX_INTERNAL; ++k) {
+        if (k > K) break;  // uniform
+        m = wave_max_u32(key[0]);
+        // one lane holding the maximum pops it (ties: the value is the same)
+        const int win = __ffsll((unsigned long long)ballot(key[0] == m)) - 1;
+        if (lane == win) {
+#pragma unroll
+          for (int j = 0; j + 1 < NV; ++j) key[j] = key[j + 1];
+          key[NV - 1] = 0u;
+        }
+      }
+      if (lane == 0) alpha[row] = -f32_from_order_key(m);
+#pragma unroll
+      for (int j = 0; j < NV; ++j) cur[j] = nxt[j];
+      continue;
     }
     // Per-lane sort, key descending; equal keys keep ascending expert order
     // (insertion sort moves an entry only past strictly smaller keys).
@@ -128,9 +160,18 @@ hipError_t launch_route(const float* Z, const float* beta, int64_t N, int E, int
   int64_t blocks = (N + 3) / 4;
   if (blocks > 2048) blocks = 2048;  // 8192 waves walk the rows with a grid stride
   const dim3 grid((unsigned)blocks), block(256);
+  // alpha alone: keys-only variant
+  const bool alpha_only = ids == nullptr && S == nullptr && margin == nullptr && alpha != nullptr;
   switch (nv) {
-#define MOE_ROUTE_CASE(V) \
-    case V: hipLaunchKernelGGL(route_topk_kernel<V>, grid, block, 0, stream, Z, beta, N, E, K, ids, S, alpha, margin); break;
+#define MOE_ROUTE_CASE(V)                                                                   \
+    case V:                                                                                 \
+      if (alpha_only)                                                                       \
+        hipLaunchKernelGGL((route_topk_kernel<V, true>), grid, block, 0, stream, Z, beta, N, \
+                           E, K, ids, S, alpha, margin);                                    \
+      else                                                                                  \
+        hipLaunchKernelGGL((route_topk_kernel<V, false>), grid, block, 0, stream, Z, beta,  \
+                           N, E, K, ids, S, alpha, margin);                                 \
+      break;
     MOE_ROUTE_CASE(1) MOE_ROUTE_CASE(2) MOE_ROUTE_CASE(3)
     MOE_ROUTE_CASE(4) MOE_ROUTE_CASE(5) MOE_ROUTE_CASE(6)
 #undef MOE_ROUTE_CASE
