@@ -104,6 +104,45 @@ moe_status_t moe_eqb_bias(const float* logits, const float* beta_in,
                           int32_t key_bits, float* beta_out, float* quantile_out,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Exact quantile update over a batch that arrives in several parts
+ * (microbatches), with the result of moe_eqb_bias on the whole batch.
+ * [KPT] §7.3: the quantile of a distributed batch is exact when the
+ * per-expert 256-bin histograms of each radix pass are summed over all parts
+ * before the bin holding the wanted rank is chosen; the sum is independent of
+ * how the batch is split (summing local quantiles instead would not be).
+ * On one GPU the parts are added into one state buffer, in any order.
+ *
+ * Use, with passes = key_bits / 8:
+ *   moe_eqb_begin(E, key_bits, state)                 zero the histograms
+ *   for pass in 0 .. passes-1:
+ *     for every part:  moe_eqb_accumulate(pass, Z_part, alpha_part, N_part, ...)
+ *     moe_eqb_select(pass, n_total, E, K, ...)        n_total = sum of N_part
+ * The last moe_eqb_select writes beta_out (centred, as moe_eqb_bias) and the
+ * raw quantiles.  Calls are stream-ordered: all calls of one update go to one
+ * stream (or are ordered by events).
+ *
+ *  state        device buffer of moe_eqb_state_bytes(E, key_bits) bytes,
+ *               256-byte aligned, owned by the caller; it carries the update
+ *               from moe_eqb_begin to the last moe_eqb_select.
+ *  Z_part       [N_part, E] fp32 logits of one part; alpha_part [N_part] its
+ *               token biases (alpha = -(B_(K+1)), e.g. from moe_route).
+ *  n_total      the rows of all parts together (sets r = floor(n_total*K/E));
+ *               a value other than the sum of N_part gives an unspecified bias.
+ *  beta_out     [E] fp32, required at the last pass; quantile_out [E] or NULL.
+ * Errors: INVALID_ARGUMENT (pass out of range, NULL or misaligned pointers),
+ * UNSUPPORTED_SHAPE, WORKSPACE_TOO_SMALL (state too small), HIP.
+ */
+size_t moe_eqb_state_bytes(int32_t E, int32_t key_bits);
+moe_status_t moe_eqb_begin(int32_t E, int32_t key_bits, void* state, size_t state_bytes,
+                           void* stream);
+moe_status_t moe_eqb_accumulate(int32_t pass, const float* logits, const float* alpha,
+                                int64_t N, int32_t E, int32_t key_bits, void* state,
+                                size_t state_bytes, void* stream);
+moe_status_t moe_eqb_select(int32_t pass, int64_t n_total, int32_t E, int32_t K,
+                            int32_t key_bits, float* beta_out, float* quantile_out,
+                            void* state, size_t state_bytes, void* stream);
+
 /* Problem description of moe_forward. */
 typedef struct {
   int64_t N;          /* tokens */

@@ -173,6 +173,20 @@ def eqb_expert_bias(Z: np.ndarray, alpha: np.ndarray, K: int, key_bits: int = 16
     return beta_new, Q, beta_raw
 
 
+def eqb_expert_bias_parts(Z_parts, alpha_parts, K: int, key_bits: int = 16):
+    """The update of eqb_expert_bias over a batch given in parts (microbatches,
+    or the shards of a distributed batch).  [KPT] §7.3: the quantile that sets
+    the bias is the one of the whole batch, exactly, however the rows are
+    split; averaging per-part quantiles would not give it.  So the definition
+    is the whole-batch update on the rows of all parts together.
+
+    Returns (beta_new [E] fp32, Q [E] fp32, beta_raw [E] fp32).
+    """
+    Z = np.concatenate([np.asarray(z, F32) for z in Z_parts], axis=0)
+    alpha = np.concatenate([np.asarray(a, F32) for a in alpha_parts], axis=0)
+    return eqb_expert_bias(Z, alpha, K, key_bits)
+
+
 # ---------------------------------------------------------------------------
 # Grouping by expert (dispatch) and the expert MLPs
 # ---------------------------------------------------------------------------

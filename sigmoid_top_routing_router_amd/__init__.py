@@ -15,7 +15,8 @@ from typing import Optional
 from . import _lib
 from ._lib import MOE_KEY32, MOE_RECOMPUTE_BIAS, MoeAux, MoeError, MoeProblem, MoeWeights
 
-__all__ = ["route", "eqb_bias", "eqb_workspace_bytes", "forward", "forward_workspace_bytes",
+__all__ = ["route", "eqb_bias", "eqb_workspace_bytes", "EqbState", "eqb_bias_parts",
+           "forward", "forward_workspace_bytes",
            "ExpertWeights", "MoeError", "load_library", "stage_timing", "stage_times"]
 
 AUX_FIELDS = [f for f, _ in MoeAux._fields_]
@@ -102,6 +103,64 @@ def eqb_bias(logits, K: int, beta_in=None, alpha=None, key_bits: int = 16,
                                 _ptr(beta_out), _ptr(q), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(stream)))
     return beta_out, q
+
+
+class EqbState:
+    """Exact quantile update over a batch that arrives in parts
+    (moe_eqb_begin / moe_eqb_accumulate / moe_eqb_select).  Owns the device
+    state buffer; use: ``st = EqbState(E, K, n_total)``, then for every pass
+    ``st.accumulate(pass_, Z_part, alpha_part)`` over all parts and
+    ``st.select(pass_)``; the last select returns (beta_out, quantile)."""
+
+    def __init__(self, E: int, K: int, n_total: int, key_bits: int = 16, device=None,
+                 stream=None):
+        torch = _torch()
+        self.lib = _lib.load()
+        self.E, self.K, self.n_total, self.key_bits = E, K, n_total, key_bits
+        self.passes = key_bits // 8
+        self.stream = stream
+        nbytes = int(self.lib.moe_eqb_state_bytes(E, key_bits))
+        if nbytes == 0:
+            raise ValueError(f"unsupported E={E} / key_bits={key_bits}")
+        self.state = torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
+        _lib.check(self.lib.moe_eqb_begin(E, key_bits, _ptr(self.state), nbytes,
+                                          _stream(stream)))
+
+    def accumulate(self, pass_: int, logits, alpha):
+        torch = _torch()
+        logits = _dev(logits, "logits", torch.float32)
+        N, E = logits.shape
+        if E != self.E:
+            raise ValueError(f"logits have E={E}, state has E={self.E}")
+        alpha = _dev(alpha, "alpha", torch.float32, (N,))
+        _lib.check(self.lib.moe_eqb_accumulate(pass_, _ptr(logits), _ptr(alpha), N, E,
+                                               self.key_bits, _ptr(self.state),
+                                               self.state.numel(), _stream(self.stream)))
+
+    def select(self, pass_: int):
+        torch = _torch()
+        last = pass_ == self.passes - 1
+        beta = torch.empty((self.E,), dtype=torch.float32, device=self.state.device) if last else None
+        q = torch.empty((self.E,), dtype=torch.float32, device=self.state.device) if last else None
+        _lib.check(self.lib.moe_eqb_select(pass_, self.n_total, self.E, self.K, self.key_bits,
+                                           _ptr(beta), _ptr(q), _ptr(self.state),
+                                           self.state.numel(), _stream(self.stream)))
+        return (beta, q) if last else None
+
+
+def eqb_bias_parts(logits_parts, alpha_parts, K: int, key_bits: int = 16, stream=None):
+    """moe_eqb_bias over the concatenation of the parts, computed part by part
+    (histograms summed over the parts for every radix pass).  Returns
+    (beta_out [E], quantile [E])."""
+    n_total = sum(int(z.shape[0]) for z in logits_parts)
+    E = int(logits_parts[0].shape[1])
+    st = EqbState(E, K, n_total, key_bits, device=logits_parts[0].device, stream=stream)
+    out = None
+    for p in range(st.passes):
+        for z, a in zip(logits_parts, alpha_parts):
+            st.accumulate(p, z, a)
+        out = st.select(p)
+    return out
 
 
 @dataclass

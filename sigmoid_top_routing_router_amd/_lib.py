@@ -19,7 +19,8 @@ MOE_KEY32 = 0x2
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED_SHAPE",
                 3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
 
-EXPORTED = ["moe_route", "moe_eqb_workspace_bytes", "moe_eqb_bias",
+EXPORTED = ["moe_route", "moe_eqb_workspace_bytes", "moe_eqb_bias", "moe_eqb_state_bytes",
+            "moe_eqb_begin", "moe_eqb_accumulate", "moe_eqb_select",
             "moe_forward_workspace_bytes", "moe_forward", "moe_status_string",
             "moe_last_error_message", "moe_abi_version", "moe_stage_timing",
             "moe_stage_times", "moe_stage_name"]
@@ -74,6 +75,14 @@ def load(path: str = LIB_PATH):
     lib.moe_eqb_workspace_bytes.restype = C.c_size_t
     lib.moe_eqb_bias.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, C.c_size_t, vp]
     lib.moe_eqb_bias.restype = C.c_int
+    lib.moe_eqb_state_bytes.argtypes = [i32, i32]
+    lib.moe_eqb_state_bytes.restype = C.c_size_t
+    lib.moe_eqb_begin.argtypes = [i32, i32, vp, C.c_size_t, vp]
+    lib.moe_eqb_begin.restype = C.c_int
+    lib.moe_eqb_accumulate.argtypes = [i32, vp, vp, i64, i32, i32, vp, C.c_size_t, vp]
+    lib.moe_eqb_accumulate.restype = C.c_int
+    lib.moe_eqb_select.argtypes = [i32, i64, i32, i32, i32, vp, vp, vp, C.c_size_t, vp]
+    lib.moe_eqb_select.restype = C.c_int
     lib.moe_forward_workspace_bytes.argtypes = [C.POINTER(MoeProblem)]
     lib.moe_forward_workspace_bytes.restype = C.c_size_t
     lib.moe_forward.argtypes = [C.POINTER(MoeProblem), C.POINTER(MoeWeights), vp, vp, vp,

@@ -174,38 +174,57 @@ __global__ __launch_bounds__(256) void eqb_scan_kernel(
     beta_out[i] = (float)((double)(-q_s[i]) - mean);
 }
 
+static int64_t eqb_rows_per_block(int64_t N, int E) {
+  const int col_groups = (E + kEqbCols - 1) / kEqbCols;
+  // about two blocks (70 KB of LDS each) per CU, each over a slab of rows
+  const int64_t chunks = (512 + col_groups - 1) / col_groups;
+  int64_t rows_per_block = (N + chunks - 1) / chunks;
+  if (rows_per_block < 96) rows_per_block = 96;
+  return (rows_per_block + kEqbRowLanes - 1) / kEqbRowLanes * kEqbRowLanes;
+}
+
+hipError_t launch_eqb_hist(const float* Z, const float* alpha, int64_t N, int E, int key_bits,
+                           int pass, const uint32_t* prefix, uint32_t* hist_pass,
+                           hipStream_t stream) {
+  const int col_groups = (E + kEqbCols - 1) / kEqbCols;
+  const int64_t rows_per_block = eqb_rows_per_block(N, E);
+  const int64_t chunks = (N + rows_per_block - 1) / rows_per_block;
+  const dim3 grid((unsigned)col_groups, (unsigned)chunks), block(kEqbThreads);
+  if (key_bits == 16)
+    hipLaunchKernelGGL(eqb_hist_kernel<16>, grid, block, 0, stream, Z, alpha, N, E, pass,
+                       rows_per_block, prefix, hist_pass);
+  else
+    hipLaunchKernelGGL(eqb_hist_kernel<32>, grid, block, 0, stream, Z, alpha, N, E, pass,
+                       rows_per_block, prefix, hist_pass);
+  return hipGetLastError();
+}
+
+hipError_t launch_eqb_scan(const EqbWork& w, int E, int K, int key_bits, int pass,
+                           int64_t n_total, float* beta_out, float* quantile_out,
+                           hipStream_t stream) {
+  const int passes = key_bits / 8;
+  const int64_t r = (n_total * (int64_t)K) / E;
+  hipLaunchKernelGGL(eqb_scan_kernel, dim3((unsigned)((E + 3) / 4)), dim3(256), 0, stream,
+                     w.hist + (size_t)pass * E * 256, w.state, w.state + E, E, pass,
+                     pass == passes - 1 ? 1 : 0, key_bits, (uint32_t)(r + 1), w.qraw,
+                     quantile_out, w.hist + (size_t)passes * E * 256, beta_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_eqb(const float* Z, const float* alpha, int64_t N, int E, int K,
                       int key_bits, float* beta_out, float* quantile_out,
                       const EqbWork& w, hipStream_t stream) {
   const int passes = key_bits / 8;
-  const int64_t r = (N * (int64_t)K) / E;
   hipError_t err = launch_fill_u32(w.hist, 0u, eqb_hist_bytes(E, key_bits) / 4, stream);
   if (err != hipSuccess) return err;
-  uint32_t* prefix = w.state;
-  uint32_t* rank = w.state + E;
-  uint32_t* ticket = w.hist + (size_t)passes * E * 256;
-  const int col_groups = (E + kEqbCols - 1) / kEqbCols;
-  // about two blocks (66 KB of LDS each) per CU, each over a slab of rows
-  int64_t chunks = (512 + col_groups - 1) / col_groups;
-  int64_t rows_per_block = (N + chunks - 1) / chunks;
-  if (rows_per_block < 96) rows_per_block = 96;
-  rows_per_block = (rows_per_block + kEqbRowLanes - 1) / kEqbRowLanes * kEqbRowLanes;
-  chunks = (N + rows_per_block - 1) / rows_per_block;
-  const dim3 hgrid((unsigned)col_groups, (unsigned)chunks), block(kEqbThreads);
-  const dim3 sgrid((unsigned)((E + 3) / 4));
   for (int p = 0; p < passes; ++p) {
-    uint32_t* hp = w.hist + (size_t)p * E * 256;
-    if (key_bits == 16)
-      hipLaunchKernelGGL(eqb_hist_kernel<16>, hgrid, block, 0, stream, Z, alpha, N, E, p,
-                         rows_per_block, prefix, hp);
-    else
-      hipLaunchKernelGGL(eqb_hist_kernel<32>, hgrid, block, 0, stream, Z, alpha, N, E, p,
-                         rows_per_block, prefix, hp);
-    hipLaunchKernelGGL(eqb_scan_kernel, sgrid, dim3(256), 0, stream, hp, prefix, rank, E, p,
-                       p == passes - 1 ? 1 : 0, key_bits, (uint32_t)(r + 1), w.qraw,
-                       quantile_out, ticket, beta_out);
+    err = launch_eqb_hist(Z, alpha, N, E, key_bits, p, w.state,
+                          w.hist + (size_t)p * E * 256, stream);
+    if (err != hipSuccess) return err;
+    err = launch_eqb_scan(w, E, K, key_bits, p, N, beta_out, quantile_out, stream);
+    if (err != hipSuccess) return err;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace moe

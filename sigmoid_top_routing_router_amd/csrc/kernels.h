@@ -30,6 +30,17 @@ size_t eqb_state_bytes(int E);
 hipError_t launch_eqb(const float* Z, const float* alpha, int64_t N, int E, int K,
                       int key_bits, float* beta_out, float* quantile_out,
                       const EqbWork& w, hipStream_t stream);
+// The pieces of launch_eqb, for a batch that arrives in several parts: the
+// histogram of one pass over one part (added into hist_pass = hist + pass*E*256;
+// prefix = w.state), and the selection step of one pass over the summed
+// histogram (rank from n_total, the rows of all parts; after the last pass
+// the raw quantiles and the centred bias are written).
+hipError_t launch_eqb_hist(const float* Z, const float* alpha, int64_t N, int E, int key_bits,
+                           int pass, const uint32_t* prefix, uint32_t* hist_pass,
+                           hipStream_t stream);
+hipError_t launch_eqb_scan(const EqbWork& w, int E, int K, int key_bits, int pass,
+                           int64_t n_total, float* beta_out, float* quantile_out,
+                           hipStream_t stream);
 
 // ---------------------------------------------------------------- grouping
 // Stable counting sort of the (t,k) pairs by expert, plus the m-tile table of

@@ -323,6 +323,87 @@ moe_status_t moe_eqb_bias(const float* logits, const float* beta_in, const float
   return ok();
 }
 
+// ---- exact quantile update over a batch that arrives in several parts
+// State: histograms (+ ticket tail), selection state, raw quantiles.
+static moe::EqbWork carve_eqb_state(Carver& c, int E, int key_bits) {
+  moe::EqbWork w;
+  w.hist = c.take<uint32_t>(moe::eqb_hist_bytes(E, key_bits) / 4);
+  w.state = c.take<uint32_t>(moe::eqb_state_bytes(E) / 4);
+  w.qraw = c.take<float>((size_t)E);
+  return w;
+}
+
+static moe_status_t check_eqb_state(int32_t E, int32_t key_bits, const void* state,
+                                    size_t state_bytes) {
+  if (E < 2 || E > MOE_MAX_E) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "E=%d outside [2, %d]", E, MOE_MAX_E);
+  if (key_bits != 16 && key_bits != 32)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "key_bits=%d must be 16 or 32", key_bits);
+  if (!state || !aligned(state, kAlign))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "state must be non-NULL and 256-byte aligned");
+  const size_t need = moe_eqb_state_bytes(E, key_bits);
+  if (state_bytes < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "state %zu < required %zu", state_bytes, need);
+  return MOE_OK;
+}
+
+size_t moe_eqb_state_bytes(int32_t E, int32_t key_bits) {
+  if (E < 2 || E > MOE_MAX_E || (key_bits != 16 && key_bits != 32)) return 0;
+  Carver c(nullptr);
+  carve_eqb_state(c, E, key_bits);
+  return c.off;
+}
+
+moe_status_t moe_eqb_begin(int32_t E, int32_t key_bits, void* state, size_t state_bytes,
+                           void* stream) {
+  moe_status_t s = check_eqb_state(E, key_bits, state, state_bytes);
+  if (s != MOE_OK) return s;
+  Carver c(state);
+  const moe::EqbWork w = carve_eqb_state(c, E, key_bits);
+  MOE_TRY_HIP(moe::launch_fill_u32(w.hist, 0u, moe::eqb_hist_bytes(E, key_bits) / 4,
+                                   (hipStream_t)stream), "moe_eqb_begin");
+  return ok();
+}
+
+moe_status_t moe_eqb_accumulate(int32_t pass, const float* logits, const float* alpha,
+                                int64_t N, int32_t E, int32_t key_bits, void* state,
+                                size_t state_bytes, void* stream) {
+  moe_status_t s = check_eqb_state(E, key_bits, state, state_bytes);
+  if (s != MOE_OK) return s;
+  if (N < 1 || N > (int64_t(1) << 24)) return fail(MOE_ERR_UNSUPPORTED_SHAPE, "N=%lld outside [1, 2^24]", (long long)N);
+  if (pass < 0 || pass >= key_bits / 8)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "pass=%d outside [0, %d)", pass, key_bits / 8);
+  if (!logits || !alpha) return fail(MOE_ERR_INVALID_ARGUMENT, "logits and alpha are required");
+  if (!aligned(logits, 4) || !aligned(alpha, 4))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "pointer not 4-byte aligned");
+  Carver c(state);
+  const moe::EqbWork w = carve_eqb_state(c, E, key_bits);
+  MOE_TRY_HIP(moe::launch_eqb_hist(logits, alpha, N, E, key_bits, pass, w.state,
+                                   w.hist + (size_t)pass * E * 256, (hipStream_t)stream),
+              "moe_eqb_accumulate");
+  return ok();
+}
+
+moe_status_t moe_eqb_select(int32_t pass, int64_t n_total, int32_t E, int32_t K,
+                            int32_t key_bits, float* beta_out, float* quantile_out,
+                            void* state, size_t state_bytes, void* stream) {
+  moe_status_t s = check_eqb_state(E, key_bits, state, state_bytes);
+  if (s != MOE_OK) return s;
+  s = check_route_shape(n_total, E, K);
+  if (s != MOE_OK) return s;
+  if (pass < 0 || pass >= key_bits / 8)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "pass=%d outside [0, %d)", pass, key_bits / 8);
+  const bool last = pass == key_bits / 8 - 1;
+  if (last && !beta_out) return fail(MOE_ERR_INVALID_ARGUMENT, "beta_out is required at the last pass");
+  if ((beta_out && !aligned(beta_out, 4)) || (quantile_out && !aligned(quantile_out, 4)))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "pointer not 4-byte aligned");
+  Carver c(state);
+  const moe::EqbWork w = carve_eqb_state(c, E, key_bits);
+  MOE_TRY_HIP(moe::launch_eqb_scan(w, E, K, key_bits, pass, n_total, last ? beta_out : nullptr,
+                                   last ? quantile_out : nullptr, (hipStream_t)stream),
+              "moe_eqb_select");
+  return ok();
+}
+
 size_t moe_forward_workspace_bytes(const moe_problem_t* p) {
   if (check_problem(p) != MOE_OK) return 0;
   return carve_forward(nullptr, *p).bytes;

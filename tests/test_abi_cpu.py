@@ -139,3 +139,45 @@ def test_forward_rejects_bad_arguments(lib):
     # unsupported shape
     prob3 = _problem(N=4, d=96, E=4, K=2, h=32, h_shared=32)
     assert lib.moe_forward(C.byref(prob3), C.byref(w), p16, None, p16, None, ws, 1 << 30, None) == 2
+
+
+def test_eqb_state_sizes(lib):
+    s16 = lib.moe_eqb_state_bytes(384, 16)
+    s32 = lib.moe_eqb_state_bytes(384, 32)
+    assert s16 >= 2 * 384 * 256 * 4 and s32 >= 4 * 384 * 256 * 4 and s32 > s16
+    for E, kb in ((1, 16), (385, 16), (384, 8)):
+        assert lib.moe_eqb_state_bytes(E, kb) == 0
+
+
+def test_eqb_parts_reject_bad_arguments(lib):
+    """Every check comes before any HIP call: these run without a GPU."""
+    buf = C.create_string_buffer(1 << 20)
+    base = C.cast(buf, C.c_void_p).value
+    st = (base + 255) // 256 * 256
+    need = lib.moe_eqb_state_bytes(8, 16)
+    # begin: bad key_bits, misaligned state, too small state, bad E
+    assert lib.moe_eqb_begin(8, 12, st, need, None) == 1
+    assert lib.moe_eqb_begin(8, 16, st + 4, need, None) == 1
+    assert lib.moe_eqb_begin(8, 16, st, need - 1, None) == 3
+    assert lib.moe_eqb_begin(400, 16, st, 1 << 19, None) == 2
+    # accumulate: pass out of range, NULL alpha, bad N
+    assert lib.moe_eqb_accumulate(2, st, st, 4, 8, 16, st, need, None) == 1
+    assert lib.moe_eqb_accumulate(-1, st, st, 4, 8, 16, st, need, None) == 1
+    assert lib.moe_eqb_accumulate(0, st, None, 4, 8, 16, st, need, None) == 1
+    assert lib.moe_eqb_accumulate(0, st, st, 0, 8, 16, st, need, None) == 2
+    # select: beta_out required at the last pass; K and E checked
+    assert lib.moe_eqb_select(1, 4, 8, 2, 16, None, None, st, need, None) == 1
+    need32 = lib.moe_eqb_state_bytes(8, 32)
+    assert lib.moe_eqb_select(4, 4, 8, 2, 32, st, None, st, need32, None) == 1
+    assert lib.moe_eqb_select(3, 4, 8, 2, 32, st, None, st, need, None) == 3
+    assert lib.moe_eqb_select(0, 4, 8, 8, 16, st, None, st, need, None) == 2
+    assert lib.moe_last_error_message() != b""
+
+
+def test_forward_rejects_operands_over_four_gib(lib):
+    # x [N, d] in bf16 at or above 4 GiB: N * 8192 * 2 >= 2^32
+    assert lib.moe_forward_workspace_bytes(C.byref(_problem(N=1 << 18, d=8192))) == 0
+    # the routed hidden rows [N*K, h]: 2^20 * 8 * 512 * 2 = 8 GiB
+    assert lib.moe_forward_workspace_bytes(C.byref(_problem(N=1 << 20, d=64, K=8))) == 0
+    # just below the limits is accepted
+    assert lib.moe_forward_workspace_bytes(C.byref(_problem(N=1 << 17, d=8192, K=2))) > 0

@@ -109,6 +109,25 @@ def test_average_of_local_quantiles_is_not_the_global_quantile():
     assert Q[0] == a["global"]
 
 
+def test_eqb_over_parts_uses_the_global_quantile():
+    """[KPT] §7.3 split: tokens t1, t2 on one rank and t3, t4 on the other.
+    The update over the two parts reaches the printed global quantile 1.5 for
+    e1 (not the 1.0 of averaged local quantiles) and the whole-batch biases."""
+    a = TOY["average_of_quantiles"]
+    parts = [Z_TOY[:2], Z_TOY[2:]]
+    alphas = [O.route(z, None, K_TOY)[1] for z in parts]  # alpha is per token
+    # the e1 column of v = Z + alpha on each rank is the printed one
+    assert [float(v) for v in (parts[0][:, 0] + alphas[0])] == a["rank_a"]
+    assert [float(v) for v in (parts[1][:, 0] + alphas[1])] == a["rank_b"]
+    for kb in (16, 32):
+        beta, Q, beta_raw = O.eqb_expert_bias_parts(parts, alphas, K_TOY, kb)
+        assert Q[0] == a["global"]
+        _, alpha, _ = O.route(Z_TOY, None, K_TOY)
+        beta1, Q1, _ = O.eqb_expert_bias(Z_TOY, alpha, K_TOY, kb)
+        assert np.array_equal(beta.view(np.uint32), beta1.view(np.uint32))
+        assert np.array_equal(Q.view(np.uint32), Q1.view(np.uint32))
+
+
 def _radix_select_desc(keys, rank, base, digits):
     """Test-only radix selection of the rank-th largest key (1-based),
     most significant digit first, as in the two-digit analogue."""
