@@ -143,6 +143,38 @@ moe_status_t moe_eqb_select(int32_t pass, int64_t n_total, int32_t E, int32_t K,
                             int32_t key_bits, float* beta_out, float* quantile_out,
                             void* state, size_t state_bytes, void* stream);
 
+/*
+ * moe_route_stats - routing diagnostics of one batch, on the device.
+ * [KPT] §6.2: MaxVio = max_e c_e / (K N / E) - 1 over the expert loads c_e.
+ * [KPT] §9: intervention rate = mean_t (1 - |I^u_t ∩ I_t| / K), the share of
+ * routed slots that the bias moved away from the router's own top-K I^u_t;
+ * it approaches 1 - K/E when the bias decides the selection.  Near-ties are
+ * tokens whose margin B_(K) - B_(K+1) is below tau (selections there may
+ * differ under rounding).
+ *
+ *  topk_ids          [N,K] int32 routed ids (e.g. moe_route with the bias);
+ *                    ids outside [0,E) are not counted.
+ *  topk_ids_unbiased [N,K] int32 or NULL: the top-K of the logits alone
+ *                    (moe_route with beta = NULL); NULL gives a NaN rate.
+ *  margin            [N] fp32 or NULL (near_ties = 0).
+ *  counts            [E] int32 out: the loads c_e.
+ *  stats             one moe_route_stats_t out, in device memory, 8-byte
+ *                    aligned.  The integer fields are exact; the rates are
+ *                    formed in fp64 from them.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, HIP.
+ */
+typedef struct {
+  double max_vio;            /* max_e c_e / (K N / E) - 1 */
+  double intervention_rate;  /* 1 - overlap / (K N), or NaN */
+  int64_t overlap;           /* sum_t |I^u_t ∩ I_t| */
+  int64_t near_ties;         /* #{t : margin_t < tau} */
+  int32_t max_load;          /* max_e c_e */
+  int32_t min_load;          /* min_e c_e */
+} moe_route_stats_t;
+moe_status_t moe_route_stats(const int32_t* topk_ids, const int32_t* topk_ids_unbiased,
+                             const float* margin, int64_t N, int32_t E, int32_t K, float tau,
+                             int32_t* counts, moe_route_stats_t* stats, void* stream);
+
 /* Problem description of moe_forward. */
 typedef struct {
   int64_t N;          /* tokens */

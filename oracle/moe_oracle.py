@@ -271,6 +271,12 @@ def intervention_rate(ids_router: np.ndarray, ids_routed: np.ndarray) -> float:
     return float(np.mean(1.0 - overlap / K))
 
 
+def near_tie_count(margin: np.ndarray, tau: float) -> int:
+    """Tokens whose selection margin B_(K) - B_(K+1) is below tau (the
+    boundary cases where rounding may change the selection)."""
+    return int(np.sum(np.asarray(margin, F64) < float(np.float32(tau))))
+
+
 # ---------------------------------------------------------------------------
 # The whole layer
 # ---------------------------------------------------------------------------

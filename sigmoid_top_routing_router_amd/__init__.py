@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import MOE_KEY32, MOE_RECOMPUTE_BIAS, MoeAux, MoeError, MoeProblem, MoeWeights
 
 __all__ = ["route", "eqb_bias", "eqb_workspace_bytes", "EqbState", "eqb_bias_parts",
-           "forward", "forward_workspace_bytes",
+           "route_stats", "read_route_stats", "forward", "forward_workspace_bytes",
            "ExpertWeights", "MoeError", "load_library", "stage_timing", "stage_times"]
 
 AUX_FIELDS = [f for f, _ in MoeAux._fields_]
@@ -78,6 +78,32 @@ def route(logits, K: int, beta=None, stream=None):
     _lib.check(lib.moe_route(_ptr(logits), _ptr(beta), N, E, K, _ptr(ids), _ptr(w),
                              _ptr(alpha), _ptr(margin), _stream(stream)))
     return ids, w, alpha, margin
+
+
+def route_stats(topk_ids, E: int, topk_ids_unbiased=None, margin=None, tau: float = 1e-3,
+                stream=None):
+    """Routing diagnostics on the device (moe_route_stats): returns
+    (counts [E] int32, stats) where stats is a 40-byte device tensor holding a
+    moe_route_stats_t; read_route_stats(stats) copies it to a dict."""
+    torch = _torch()
+    lib = _lib.load()
+    topk_ids = _dev(topk_ids, "topk_ids", torch.int32)
+    N, K = topk_ids.shape
+    topk_ids_unbiased = _dev(topk_ids_unbiased, "topk_ids_unbiased", torch.int32, (N, K))
+    margin = _dev(margin, "margin", torch.float32, (N,))
+    counts = torch.empty((E,), dtype=torch.int32, device=topk_ids.device)
+    stats = torch.empty((C.sizeof(_lib.MoeRouteStats) // 8,), dtype=torch.float64,
+                        device=topk_ids.device)
+    _lib.check(lib.moe_route_stats(_ptr(topk_ids), _ptr(topk_ids_unbiased), _ptr(margin), N, E,
+                                   K, float(tau), _ptr(counts), _ptr(stats), _stream(stream)))
+    return counts, stats
+
+
+def read_route_stats(stats) -> dict:
+    """Copy a moe_route_stats_t from the device (synchronises) into a dict."""
+    raw = stats.cpu().numpy().tobytes()
+    st = _lib.MoeRouteStats.from_buffer_copy(raw)
+    return {f: getattr(st, f) for f, _ in _lib.MoeRouteStats._fields_}
 
 
 def eqb_workspace_bytes(N: int, E: int, K: int, key_bits: int = 16) -> int:

@@ -20,7 +20,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPOR
                 3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
 
 EXPORTED = ["moe_route", "moe_eqb_workspace_bytes", "moe_eqb_bias", "moe_eqb_state_bytes",
-            "moe_eqb_begin", "moe_eqb_accumulate", "moe_eqb_select",
+            "moe_eqb_begin", "moe_eqb_accumulate", "moe_eqb_select", "moe_route_stats",
             "moe_forward_workspace_bytes", "moe_forward", "moe_status_string",
             "moe_last_error_message", "moe_abi_version", "moe_stage_timing",
             "moe_stage_times", "moe_stage_name"]
@@ -47,6 +47,12 @@ class MoeAux(C.Structure):
                 ("counts_before", C.c_void_p), ("counts", C.c_void_p),
                 ("offsets", C.c_void_p), ("sorted_src", C.c_void_p),
                 ("src_pos", C.c_void_p)]
+
+
+class MoeRouteStats(C.Structure):
+    _fields_ = [("max_vio", C.c_double), ("intervention_rate", C.c_double),
+                ("overlap", C.c_int64), ("near_ties", C.c_int64), ("max_load", C.c_int32),
+                ("min_load", C.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -83,6 +89,8 @@ def load(path: str = LIB_PATH):
     lib.moe_eqb_accumulate.restype = C.c_int
     lib.moe_eqb_select.argtypes = [i32, i64, i32, i32, i32, vp, vp, vp, C.c_size_t, vp]
     lib.moe_eqb_select.restype = C.c_int
+    lib.moe_route_stats.argtypes = [vp, vp, vp, i64, i32, i32, C.c_float, vp, vp, vp]
+    lib.moe_route_stats.restype = C.c_int
     lib.moe_forward_workspace_bytes.argtypes = [C.POINTER(MoeProblem)]
     lib.moe_forward_workspace_bytes.restype = C.c_size_t
     lib.moe_forward.argtypes = [C.POINTER(MoeProblem), C.POINTER(MoeWeights), vp, vp, vp,

@@ -97,6 +97,23 @@ hipError_t launch_combine(const uint16_t* sh, const uint16_t* Y, const float* S,
                           const int32_t* src_pos, int64_t N, int K, int d,
                           uint16_t* y, hipStream_t stream);
 
+// ---------------------------------------------------------------- diagnostics
+// Same layout as moe_route_stats_t of the public header.
+struct RouteStatsDev {
+  double max_vio;
+  double intervention_rate;
+  int64_t overlap;
+  int64_t near_ties;
+  int32_t max_load;
+  int32_t min_load;
+};
+// Loads counts[E] of the routed ids [N,K]; MaxVio; the overlap with the
+// unbiased top-K ids_u [N,K] (NULL: intervention rate NaN); the number of
+// tokens with margin < tau (margin NULL: 0).  Device outputs only.
+hipError_t launch_route_stats(const int32_t* ids, const int32_t* ids_u, const float* margin,
+                              int64_t N, int E, int K, float tau, int32_t* counts,
+                              RouteStatsDev* st, hipStream_t stream);
+
 // ---------------------------------------------------------------- misc
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t stream);
 

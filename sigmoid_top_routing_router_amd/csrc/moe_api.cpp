@@ -1,6 +1,7 @@
 // C ABI of the MoE layer library: argument checks, workspace carving and the
 // launch sequence on the caller's stream.  No allocation, no host/device
 // synchronisation, no device-to-host copies.
+#include <cstddef>
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -320,6 +321,30 @@ moe_status_t moe_eqb_bias(const float* logits, const float* beta_in, const float
   moe::EqbWork w{l.hist, l.state, l.qraw};
   MOE_TRY_HIP(moe::launch_eqb(logits, a, N, E, K, key_bits, beta_out, quantile_out, w, st),
               "moe_eqb_bias");
+  return ok();
+}
+
+static_assert(sizeof(moe_route_stats_t) == sizeof(moe::RouteStatsDev), "stats layout");
+static_assert(offsetof(moe_route_stats_t, overlap) == offsetof(moe::RouteStatsDev, overlap),
+              "stats layout");
+static_assert(offsetof(moe_route_stats_t, max_load) == offsetof(moe::RouteStatsDev, max_load),
+              "stats layout");
+
+moe_status_t moe_route_stats(const int32_t* topk_ids, const int32_t* topk_ids_unbiased,
+                             const float* margin, int64_t N, int32_t E, int32_t K, float tau,
+                             int32_t* counts, moe_route_stats_t* stats, void* stream) {
+  moe_status_t s = check_route_shape(N, E, K);
+  if (s != MOE_OK) return s;
+  if (!topk_ids || !counts || !stats)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "topk_ids, counts and stats are required");
+  const void* p4[] = {topk_ids, topk_ids_unbiased, margin, counts};
+  for (const void* q : p4)
+    if (q && !aligned(q, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "pointer not 4-byte aligned");
+  if (!aligned(stats, 8)) return fail(MOE_ERR_INVALID_ARGUMENT, "stats not 8-byte aligned");
+  MOE_TRY_HIP(moe::launch_route_stats(topk_ids, topk_ids_unbiased, margin, N, E, K, tau, counts,
+                                      reinterpret_cast<moe::RouteStatsDev*>(stats),
+                                      (hipStream_t)stream),
+              "moe_route_stats");
   return ok();
 }
 

@@ -181,3 +181,31 @@ def test_forward_rejects_operands_over_four_gib(lib):
     assert lib.moe_forward_workspace_bytes(C.byref(_problem(N=1 << 20, d=64, K=8))) == 0
     # just below the limits is accepted
     assert lib.moe_forward_workspace_bytes(C.byref(_problem(N=1 << 17, d=8192, K=2))) > 0
+
+
+def test_route_stats_rejects_bad_arguments(lib):
+    buf = C.create_string_buffer(4096)
+    p = (C.cast(buf, C.c_void_p).value + 15) // 16 * 16
+    assert lib.moe_route_stats(None, None, None, 4, 8, 2, 1e-3, p, p, None) == 1
+    assert lib.moe_route_stats(p, None, None, 4, 8, 2, 1e-3, None, p, None) == 1
+    assert lib.moe_route_stats(p, None, None, 4, 8, 2, 1e-3, p, p + 4, None) == 1
+    assert lib.moe_route_stats(p, p + 2, None, 4, 8, 2, 1e-3, p, p, None) == 1
+    assert lib.moe_route_stats(p, None, None, 4, 8, 9, 1e-3, p, p, None) == 2
+    assert lib.moe_route_stats(p, None, None, 0, 8, 2, 1e-3, p, p, None) == 2
+
+
+def test_route_stats_struct_matches_header(tmp_path):
+    import subprocess
+    from sigmoid_top_routing_router_amd._lib import MoeRouteStats
+    src = tmp_path / "s.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "moe_mi355x.h"\n'
+                   'int main(void){printf("%zu %zu %zu %zu\\n", sizeof(moe_route_stats_t),'
+                   ' offsetof(moe_route_stats_t, overlap), offsetof(moe_route_stats_t, near_ties),'
+                   ' offsetof(moe_route_stats_t, min_load));return 0;}\n')
+    exe = tmp_path / "s"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert got == [C.sizeof(MoeRouteStats), MoeRouteStats.overlap.offset,
+                   MoeRouteStats.near_ties.offset, MoeRouteStats.min_load.offset]

@@ -289,3 +289,10 @@ def test_recompute_balances_a_collapsed_router():
                       logit_offset=off, compute_output=False)
     assert out["counts_before"][:2].tolist() == [T, T]
     assert O.max_vio(out["counts"], T, K, E) < O.max_vio(out["counts_before"], T, K, E)
+
+
+def test_near_tie_count_threshold_is_strict():
+    m = np.array([0.0, 5e-4, np.float32(1e-3), 2e-3, 0.5], np.float32)
+    assert O.near_tie_count(m, 1e-3) == 2
+    assert O.near_tie_count(m, 0.0) == 0
+    assert O.near_tie_count(m, 1.0) == 5
