@@ -41,6 +41,8 @@ from __future__ import annotations
 
 from typing import Optional
 
+import math
+
 import numpy as np
 
 F32 = np.float32
@@ -275,6 +277,47 @@ def near_tie_count(margin: np.ndarray, tau: float) -> int:
     """Tokens whose selection margin B_(K) - B_(K+1) is below tau (the
     boundary cases where rounding may change the selection)."""
     return int(np.sum(np.asarray(margin, F64) < float(np.float32(tau))))
+
+
+# ---------------------------------------------------------------------------
+# Load-Error Injection ([KPT] §8): balance inside each microbatch
+# ---------------------------------------------------------------------------
+def lei_injection(ids: np.ndarray, E: int, lam: float, tau: float):
+    """The per-expert term that LEI adds to every token's score gradient.
+
+    f_e = c_e / (K |B| / E) with c_e the loads of the microbatch B, rho = f - 1,
+    xi = ||rho||_inf / tau, scale = tanh(xi) / xi (1 at xi = 0 by continuity);
+    the injection is lam * scale * rho_e.  fp64 throughout.
+
+    Returns (rho [E] f64, xi, scale, injection [E] f64).
+    """
+    ids = np.asarray(ids)
+    T, K = ids.shape
+    counts = np.bincount(ids.ravel(), minlength=E).astype(F64)
+    f = counts / (K * T / E)
+    rho = f - 1.0
+    xi = float(np.max(np.abs(rho))) / tau
+    scale = 1.0 if xi == 0.0 else math.tanh(xi) / xi
+    return rho, xi, scale, lam * scale * rho
+
+
+def lei_backward(Z: np.ndarray, ids: np.ndarray, G: Optional[np.ndarray], lam: float,
+                 tau: float):
+    """Score and logit gradients with LEI ([KPT] §8).
+
+    G [T,E]: incoming gradient with respect to the sigmoid scores
+    S_{t,e} = sigma(Z_{t,e}) (None: zero).  G'_{t,e} = G_{t,e} + injection_e
+    for every token and expert; the logits receive G' * sigma(Z)(1 - sigma(Z))
+    by the chain rule.  fp64.
+
+    Returns (G' [T,E] f64, dZ [T,E] f64).
+    """
+    Z = np.asarray(Z, F64)
+    T, E = Z.shape
+    _, _, _, inj = lei_injection(ids, E, lam, tau)
+    Gp = (np.zeros((T, E), F64) if G is None else np.asarray(G, F64)) + inj[None, :]
+    s = 1.0 / (1.0 + np.exp(-Z))
+    return Gp, Gp * s * (1.0 - s)
 
 
 # ---------------------------------------------------------------------------

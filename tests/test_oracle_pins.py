@@ -209,3 +209,49 @@ def test_expert_weight_counts():
     assert per == g["weights_per_expert"]
     assert round(per * g["experts_touched_per_token"] / 1e6, 1) == g["weights_touched_per_token_millions_1dp"]
     assert round(per * g["experts_per_block"] / 1e9, 2) == g["weights_per_block_billions_2dp"]
+
+
+LEI = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "lei_check.json")))
+
+
+def test_lei_printed_check():
+    """[KPT] §8 numerical check on the collapsed running example."""
+    ids, _, _ = O.route(Z_TOY, None, K_TOY)
+    assert np.bincount(ids.ravel(), minlength=4).tolist() == LEI["loads"]
+    rho, xi, scale, inj = O.lei_injection(ids, 4, LEI["lambda"], LEI["tau"])
+    assert rho.tolist() == LEI["rho"]
+    assert xi == LEI["xi"]
+    assert round(scale, 4) == LEI["tanh_xi_over_xi_4dp"]
+    assert np.allclose(inj, LEI["lambda"] * scale * np.array(LEI["rho"]), rtol=0, atol=0)
+    # score gradients all receive the injection; the logit of (t1, e1) gets it
+    # times sigma'(2.0)
+    Gp, dZ = O.lei_backward(Z_TOY, ids, None, LEI["lambda"], LEI["tau"])
+    assert np.array_equal(Gp, np.tile(inj, (4, 1)))
+    t, e = LEI["token"], LEI["expert"]
+    assert float(Z_TOY[t, e]) == 2.0
+    sp = dZ[t, e] / inj[e]
+    assert round(sp, 3) == LEI["sigma_prime_at_2_3dp"]
+    assert abs(dZ[t, e] - LEI["lambda"] * LEI["tanh_xi_over_xi_4dp"]
+               * LEI["sigma_prime_at_2_3dp"]) < 1e-9
+
+
+def test_lei_bound_and_balanced_limit():
+    """|injection| <= lam * tau * tanh(xi) < lam * tau however lopsided the
+    loads ([KPT] §8); a perfectly balanced microbatch gets no injection and
+    the scale is 1 (its continuous limit at xi = 0)."""
+    rng = np.random.default_rng(5)
+    for lam, tau, skew in ((1e-5, 1.0, 0.0), (1e-3, 0.25, 3.0), (0.5, 2.0, 8.0)):
+        T, E, K = 512, 64, 4
+        p = np.exp(-skew * np.arange(E) / E)
+        p /= p.sum()
+        ids = np.stack([rng.choice(E, K, replace=False, p=p) for _ in range(T)])
+        rho, xi, scale, inj = O.lei_injection(ids, E, lam, tau)
+        assert np.max(np.abs(inj)) <= lam * tau * math.tanh(xi) * (1 + 1e-12)
+        assert np.max(np.abs(inj)) < lam * tau
+        assert np.isclose(xi, np.max(np.abs(rho)) / tau)
+    ids = np.tile(np.arange(4), (8, 1)).reshape(-1, 2)  # every expert loaded equally
+    rho, xi, scale, inj = O.lei_injection(ids, 4, 1e-5, 1.0)
+    assert xi == 0.0 and scale == 1.0 and not inj.any()
+    # small imbalance: tanh(xi)/xi = 1 - xi^2/3 + O(xi^4), the injection ~ lam * rho
+    _, xi, scale, _ = O.lei_injection(np.array([[0, 1]] * 999 + [[0, 2]]), 1000, 1.0, 1e6)
+    assert 0 < xi < 1e-3 and abs(scale - (1 - xi * xi / 3)) < xi ** 4
