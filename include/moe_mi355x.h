@@ -175,6 +175,35 @@ moe_status_t moe_route_stats(const int32_t* topk_ids, const int32_t* topk_ids_un
                              const float* margin, int64_t N, int32_t E, int32_t K, float tau,
                              int32_t* counts, moe_route_stats_t* stats, void* stream);
 
+/*
+ * moe_lei_backward - Load-Error Injection on the routing-score gradient of
+ * one microbatch ([KPT] §8).  With the loads c_e of the microbatch's routed
+ * ids, f_e = c_e / (K N / E), rho = f - 1, xi = ||rho||_inf / tau:
+ *   grad_scores_out[t,e] = grad_scores[t,e] + lam * tanh(xi)/xi * rho_e
+ * for every token and expert (the factor is 1 at xi = 0; the injection stays
+ * below lam * tau), and through S = sigma(Z):
+ *   grad_logits_out[t,e] = grad_scores_out[t,e] * sigma(Z)(1 - sigma(Z)).
+ * The pages use lam = 1e-5, tau = 1.  rho, xi and the factor are formed in
+ * fp64, the injection rounded once to fp32, the rest in fp32.
+ *
+ *  logits          [N,E] fp32 (required for grad_logits_out).
+ *  topk_ids        [N,K] int32 routed ids of the microbatch (ids outside
+ *                  [0,E) are not counted).
+ *  grad_scores     [N,E] fp32 gradient with respect to the sigmoid scores,
+ *                  or NULL (zero); grad_scores_out may be the same buffer.
+ *  grad_scores_out [N,E] fp32 out or NULL; grad_logits_out [N,E] fp32 out or
+ *                  NULL (at least one; it must not alias an input).
+ *  injection_out   [E] fp32 out or NULL: lam * tanh(xi)/xi * rho_e.
+ *  workspace       moe_lei_workspace_bytes(E) bytes, 256-byte aligned.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, WORKSPACE_TOO_SMALL, HIP.
+ */
+size_t moe_lei_workspace_bytes(int32_t E);
+moe_status_t moe_lei_backward(const float* logits, const int32_t* topk_ids,
+                              const float* grad_scores, int64_t N, int32_t E, int32_t K,
+                              float lam, float tau, float* grad_scores_out,
+                              float* grad_logits_out, float* injection_out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Problem description of moe_forward. */
 typedef struct {
   int64_t N;          /* tokens */

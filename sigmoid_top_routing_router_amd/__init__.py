@@ -16,7 +16,8 @@ from . import _lib
 from ._lib import MOE_KEY32, MOE_RECOMPUTE_BIAS, MoeAux, MoeError, MoeProblem, MoeWeights
 
 __all__ = ["route", "eqb_bias", "eqb_workspace_bytes", "EqbState", "eqb_bias_parts",
-           "route_stats", "read_route_stats", "forward", "forward_workspace_bytes",
+           "route_stats", "read_route_stats", "lei_backward", "forward",
+           "forward_workspace_bytes",
            "ExpertWeights", "MoeError", "load_library", "stage_timing", "stage_times"]
 
 AUX_FIELDS = [f for f, _ in MoeAux._fields_]
@@ -104,6 +105,36 @@ def read_route_stats(stats) -> dict:
     raw = stats.cpu().numpy().tobytes()
     st = _lib.MoeRouteStats.from_buffer_copy(raw)
     return {f: getattr(st, f) for f, _ in _lib.MoeRouteStats._fields_}
+
+
+def lei_backward(topk_ids, E: int, logits=None, grad_scores=None, lam: float = 1e-5,
+                 tau: float = 1.0, scores_out: bool = True, logits_out: bool = True,
+                 inplace: bool = False, stream=None):
+    """Load-Error Injection on the score gradient of one microbatch
+    (moe_lei_backward).  Returns (grad_scores' [N,E] or None,
+    grad_logits [N,E] or None, injection [E]).  With inplace=True the
+    injection is added into grad_scores itself."""
+    torch = _torch()
+    lib = _lib.load()
+    topk_ids = _dev(topk_ids, "topk_ids", torch.int32)
+    N, K = topk_ids.shape
+    logits = _dev(logits, "logits", torch.float32, (N, E))
+    grad_scores = _dev(grad_scores, "grad_scores", torch.float32, (N, E))
+    dev_ = topk_ids.device
+    if inplace:
+        if grad_scores is None:
+            raise ValueError("inplace needs grad_scores")
+        gout = grad_scores
+    else:
+        gout = torch.empty((N, E), dtype=torch.float32, device=dev_) if scores_out else None
+    dz = torch.empty((N, E), dtype=torch.float32, device=dev_) if logits_out else None
+    inj = torch.empty((E,), dtype=torch.float32, device=dev_)
+    need = int(lib.moe_lei_workspace_bytes(E))
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev_)
+    _lib.check(lib.moe_lei_backward(_ptr(logits), _ptr(topk_ids), _ptr(grad_scores), N, E, K,
+                                    float(lam), float(tau), _ptr(gout), _ptr(dz), _ptr(inj),
+                                    _ptr(ws), ws.numel(), _stream(stream)))
+    return gout, dz, inj
 
 
 def eqb_workspace_bytes(N: int, E: int, K: int, key_bits: int = 16) -> int:

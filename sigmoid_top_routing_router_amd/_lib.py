@@ -21,6 +21,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPOR
 
 EXPORTED = ["moe_route", "moe_eqb_workspace_bytes", "moe_eqb_bias", "moe_eqb_state_bytes",
             "moe_eqb_begin", "moe_eqb_accumulate", "moe_eqb_select", "moe_route_stats",
+            "moe_lei_workspace_bytes", "moe_lei_backward",
             "moe_forward_workspace_bytes", "moe_forward", "moe_status_string",
             "moe_last_error_message", "moe_abi_version", "moe_stage_timing",
             "moe_stage_times", "moe_stage_name"]
@@ -91,6 +92,11 @@ def load(path: str = LIB_PATH):
     lib.moe_eqb_select.restype = C.c_int
     lib.moe_route_stats.argtypes = [vp, vp, vp, i64, i32, i32, C.c_float, vp, vp, vp]
     lib.moe_route_stats.restype = C.c_int
+    lib.moe_lei_workspace_bytes.argtypes = [i32]
+    lib.moe_lei_workspace_bytes.restype = C.c_size_t
+    lib.moe_lei_backward.argtypes = [vp, vp, vp, i64, i32, i32, C.c_float, C.c_float, vp, vp, vp,
+                                     vp, C.c_size_t, vp]
+    lib.moe_lei_backward.restype = C.c_int
     lib.moe_forward_workspace_bytes.argtypes = [C.POINTER(MoeProblem)]
     lib.moe_forward_workspace_bytes.restype = C.c_size_t
     lib.moe_forward.argtypes = [C.POINTER(MoeProblem), C.POINTER(MoeWeights), vp, vp, vp,

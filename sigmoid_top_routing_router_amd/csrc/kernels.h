@@ -114,6 +114,16 @@ hipError_t launch_route_stats(const int32_t* ids, const int32_t* ids_u, const fl
                               int64_t N, int E, int K, float tau, int32_t* counts,
                               RouteStatsDev* st, hipStream_t stream);
 
+// ---------------------------------------------------------------- LEI
+// Load-Error Injection on the score gradient of one microbatch: loads of the
+// routed ids [N,K] into counts[E] (scratch), the per-expert injection into
+// inj[E] (scratch; also copied to inj_out when given), then Gout = G + inj
+// (G NULL: zero; Gout may equal G) and dZ = Gout * sigma'(Z).  Gout or dZ may
+// be NULL; Z is read only for dZ.
+hipError_t launch_lei(const float* Z, const int32_t* ids, const float* G, int64_t N, int E,
+                      int K, float lam, float tau, float* Gout, float* dZ, float* inj_out,
+                      int32_t* counts, float* inj, hipStream_t stream);
+
 // ---------------------------------------------------------------- misc
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t stream);
 

@@ -1,6 +1,7 @@
 // C ABI of the MoE layer library: argument checks, workspace carving and the
 // launch sequence on the caller's stream.  No allocation, no host/device
 // synchronisation, no device-to-host copies.
+#include <cmath>
 #include <cstddef>
 #include <hip/hip_runtime.h>
 
@@ -345,6 +346,48 @@ moe_status_t moe_route_stats(const int32_t* topk_ids, const int32_t* topk_ids_un
                                       reinterpret_cast<moe::RouteStatsDev*>(stats),
                                       (hipStream_t)stream),
               "moe_route_stats");
+  return ok();
+}
+
+size_t moe_lei_workspace_bytes(int32_t E) {
+  if (E < 2 || E > MOE_MAX_E) return 0;
+  Carver c(nullptr);
+  c.take<int32_t>((size_t)E);
+  c.take<float>((size_t)E);
+  return c.off;
+}
+
+moe_status_t moe_lei_backward(const float* logits, const int32_t* topk_ids,
+                              const float* grad_scores, int64_t N, int32_t E, int32_t K,
+                              float lam, float tau, float* grad_scores_out,
+                              float* grad_logits_out, float* injection_out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  moe_status_t s = check_route_shape(N, E, K);
+  if (s != MOE_OK) return s;
+  if (!topk_ids) return fail(MOE_ERR_INVALID_ARGUMENT, "topk_ids is required");
+  if (!grad_scores_out && !grad_logits_out)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "grad_scores_out or grad_logits_out is required");
+  if (grad_logits_out && !logits)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "logits are required for grad_logits_out");
+  if (!(tau > 0.0f) || !std::isfinite(tau) || !std::isfinite(lam))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "lam must be finite and tau finite and > 0");
+  const void* p4[] = {logits, topk_ids, grad_scores, grad_scores_out, grad_logits_out,
+                      injection_out};
+  for (const void* q : p4)
+    if (q && !aligned(q, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "pointer not 4-byte aligned");
+  if (grad_logits_out && (grad_logits_out == grad_scores || grad_logits_out == logits))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "grad_logits_out must not alias an input");
+  const size_t need = moe_lei_workspace_bytes(E);
+  if (!workspace || !aligned(workspace, kAlign))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < required %zu", workspace_bytes, need);
+  Carver c(workspace);
+  int32_t* counts = c.take<int32_t>((size_t)E);
+  float* inj = c.take<float>((size_t)E);
+  MOE_TRY_HIP(moe::launch_lei(logits, topk_ids, grad_scores, N, E, K, lam, tau, grad_scores_out,
+                              grad_logits_out, injection_out, counts, inj, (hipStream_t)stream),
+              "moe_lei_backward");
   return ok();
 }
 

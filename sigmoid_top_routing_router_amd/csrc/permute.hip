@@ -163,8 +163,10 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0u;
   __syncthreads();
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < pairs; i += stride)
-    atomicAdd(&cnt[ids[i]], 1u);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < pairs; i += stride) {
+    const int32_t e = ids[i];
+    if ((uint32_t)e < (uint32_t)E) atomicAdd(&cnt[e], 1u);  // ids outside [0,E) are not counted
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x)
     if (cnt[e]) atomicAdd((uint32_t*)counts + e, cnt[e]);

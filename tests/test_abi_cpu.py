@@ -209,3 +209,29 @@ def test_route_stats_struct_matches_header(tmp_path):
                                           check=True).stdout.split()]
     assert got == [C.sizeof(MoeRouteStats), MoeRouteStats.overlap.offset,
                    MoeRouteStats.near_ties.offset, MoeRouteStats.min_load.offset]
+
+
+def test_lei_rejects_bad_arguments(lib):
+    buf = C.create_string_buffer(1 << 16)
+    base = C.cast(buf, C.c_void_p).value
+    p = (base + 255) // 256 * 256
+    need = lib.moe_lei_workspace_bytes(8)
+    assert need >= 8 * 8 and lib.moe_lei_workspace_bytes(1) == 0
+    args = dict(logits=p, ids=p, g=None, N=4, E=8, K=2, lam=1e-5, tau=1.0, gout=p + 1024,
+                dz=p + 2048, inj=None, ws=p + 4096, wsb=need)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.moe_lei_backward(a["logits"], a["ids"], a["g"], a["N"], a["E"], a["K"],
+                                    a["lam"], a["tau"], a["gout"], a["dz"], a["inj"], a["ws"],
+                                    a["wsb"], None)
+    assert call(ids=None) == 1
+    assert call(gout=None, dz=None) == 1
+    assert call(logits=None) == 1            # grad_logits needs the logits
+    assert call(tau=0.0) == 1
+    assert call(tau=float("nan")) == 1
+    assert call(lam=float("inf")) == 1
+    assert call(dz=p) == 1                   # aliases the logits
+    assert call(ws=p + 4100) == 1            # misaligned workspace
+    assert call(wsb=need - 1) == 3
+    assert call(K=9) == 2
