@@ -337,7 +337,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
               if (m < LIVE) {
 #pragma unroll
                 for (int f = 0; f < 2; ++f)
-                  acc[m][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ac[m], Bc[f], acc[m][f], 0, 0, 0);
+                  acc[m][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Bc[f], Ac[m], acc[m][f], 0, 0, 0);
               }
             }
           }
@@ -358,27 +358,39 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
   else if (live_m > 2) run(std::integral_constant<int, 4>{});
   else run(std::integral_constant<int, 2>{});
 
-  // ---- epilogue: lane holds column (lane & 31) and, for register r, row
-  // 8*(r/4) + 4*(lane/32) + r%4 of each 32 x 32 accumulator.
+  // ---- epilogue.  The MFMAs take the B fragment as their first operand, so
+  // each 32 x 32 accumulator holds the tile transposed: lane l has output row
+  // (l & 31) and, for register r, output column 8*(r/4) + 4*(l/32) + r%4, i.e.
+  // four consecutive columns per group of four registers.
+  const int orow_l = lane & 31;
+  const int ocol_l = 4 * (lane >> 5);
   if (MODE == kRouter) {
     if (!any) return;
-    const int ccol = lane & 31;
-    const int rsub = 4 * (lane >> 5);
+    float* Zo = reinterpret_cast<float*>(a.out);
+    const bool vec = (a.ldo % 4) == 0;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       if (m >= live_m) break;
+      const int rr = wg * 128 + m * 32 + orow_l;
+      if (rr >= rows) continue;
+      const int64_t orow = row0 + rr;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rr = wg * 128 + m * 32 + 8 * (r >> 2) + rsub + (r & 3);
-        if (rr >= rows) continue;
-        const int64_t orow = row0 + rr;
+      for (int f = 0; f < 2; ++f) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const int col = nt * BN + b_row[f] + ccol;
-          if (col < a.b_rows) {
-            float z = acc[m][f][r];
-            if (a.offset) z += a.offset[col];
-            reinterpret_cast<float*>(a.out)[orow * a.ldo + col] = z;
+        for (int q = 0; q < 4; ++q) {
+          const int col = nt * BN + b_row[f] + 8 * q + ocol_l;
+          float z[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            z[j] = acc[m][f][4 * q + j];
+            if (a.offset && col + j < a.b_rows) z[j] += a.offset[col + j];
+          }
+          if (vec && col + 3 < a.b_rows) {
+            *reinterpret_cast<float4*>(Zo + orow * a.ldo + col) = make_float4(z[0], z[1], z[2], z[3]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (col + j < a.b_rows) Zo[orow * a.ldo + col + j] = z[j];
           }
         }
       }
@@ -386,30 +398,43 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
     return;
   }
   // bf16 outputs (H or Y) go through LDS: every wave converts its
-  // accumulators (hardware round-to-nearest-even) into a row-major tile, then
-  // the block writes whole rows with 16-byte stores.
+  // accumulators (hardware round-to-nearest-even, two values per
+  // instruction) and writes four consecutive columns per 8-byte LDS store
+  // into a row-major tile; the row stride of 2 (mod 32) words spreads the 32
+  // rows of one store over all banks.  Then the block writes whole rows with
+  // 16-byte global stores.
   constexpr int OCOLS = (MODE == kGateUp) ? BN / 2 : BN;   // tile columns
-  constexpr int OSTRIDE = OCOLS * 2 + 16;                  // bytes per LDS row
+  constexpr int OSTRIDE = OCOLS * 2 + 8;                   // bytes per LDS row
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  auto pack2 = [](float x, float y) {
+    const bf16x2_t v = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(uint32_t, v);
+  };
   __syncthreads();  // all fragment reads of the last stage are done
   if (any) {
-    const int ccol = lane & 31;
-    const int rsub = 4 * (lane >> 5);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       if (m >= live_m) break;
+      char* lrow = lds_raw + (wg * 128 + m * 32 + orow_l) * OSTRIDE;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rr = wg * 128 + m * 32 + 8 * (r >> 2) + rsub + (r & 3);
-        char* lrow = lds_raw + rr * OSTRIDE;
+      for (int q = 0; q < 4; ++q) {
         if (MODE == kGateUp) {
-          const float g = acc[m][0][r];
-          const float u = acc[m][1][r];
-          const float hval = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
-          *reinterpret_cast<__bf16*>(lrow + (wp * 32 + ccol) * 2) = (__bf16)hval;
+          float hv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float g = acc[m][0][4 * q + j];
+            const float u = acc[m][1][4 * q + j];
+            hv[j] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+          }
+          *reinterpret_cast<uint2*>(lrow + (wp * 32 + 8 * q + ocol_l) * 2) =
+              make_uint2(pack2(hv[0], hv[1]), pack2(hv[2], hv[3]));
         } else {
 #pragma unroll
-          for (int f = 0; f < 2; ++f)
-            *reinterpret_cast<__bf16*>(lrow + (b_row[f] + ccol) * 2) = (__bf16)acc[m][f][r];
+          for (int f = 0; f < 2; ++f) {
+            *reinterpret_cast<uint2*>(lrow + (b_row[f] + 8 * q + ocol_l) * 2) =
+                make_uint2(pack2(acc[m][f][4 * q], acc[m][f][4 * q + 1]),
+                           pack2(acc[m][f][4 * q + 2], acc[m][f][4 * q + 3]));
+          }
         }
       }
     }
@@ -423,8 +448,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
     if (rr >= rows) break;  // chunks are walked in row order
     const int col = col0 + ch * 8;
     if (col >= a.b_rows) continue;
-    const uint4 v = *reinterpret_cast<const uint4*>(lds_raw + rr * OSTRIDE + ch * 16);
-    *reinterpret_cast<uint4*>(out + (row0 + rr) * a.ldo + col) = v;
+    const char* src = lds_raw + rr * OSTRIDE + ch * 16;  // 8-byte aligned
+    const uint2 lo = *reinterpret_cast<const uint2*>(src);
+    const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
+    *reinterpret_cast<uint4*>(out + (row0 + rr) * a.ldo + col) = make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
 }
 
