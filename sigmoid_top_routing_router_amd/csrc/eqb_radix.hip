@@ -176,8 +176,9 @@ __global__ __launch_bounds__(256) void eqb_scan_kernel(
 
 static int64_t eqb_rows_per_block(int64_t N, int E) {
   const int col_groups = (E + kEqbCols - 1) / kEqbCols;
-  // about two blocks (70 KB of LDS each) per CU, each over a slab of rows
-  const int64_t chunks = (512 + col_groups - 1) / col_groups;
+  // at most two blocks (70 KB of LDS each) per CU of the 256, so that the
+  // whole grid is resident at once (no second round)
+  const int64_t chunks = 512 / col_groups;
   int64_t rows_per_block = (N + chunks - 1) / chunks;
   if (rows_per_block < 96) rows_per_block = 96;
   return (rows_per_block + kEqbRowLanes - 1) / kEqbRowLanes * kEqbRowLanes;

@@ -153,15 +153,43 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
   }
 }
 
+// Blocks of 256 threads of one variant that the device holds at once
+// (occupancy x compute units), queried once per variant and device.
+static int64_t route_resident_blocks(int nv, bool alpha_only) {
+  static int64_t cache[2][8][7] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 8) return 2048;
+  int64_t& c = cache[alpha_only ? 1 : 0][dev][nv];
+  if (c) return c;
+  const void* fn = nullptr;
+  switch (nv) {
+#define MOE_ROUTE_FN(V) \
+    case V: fn = alpha_only ? (const void*)route_topk_kernel<V, true> : (const void*)route_topk_kernel<V, false>; break;
+    MOE_ROUTE_FN(1) MOE_ROUTE_FN(2) MOE_ROUTE_FN(3) MOE_ROUTE_FN(4) MOE_ROUTE_FN(5) MOE_ROUTE_FN(6)
+#undef MOE_ROUTE_FN
+    default: return 2048;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      per_cu <= 0 || cus <= 0)
+    return 2048;
+  c = (int64_t)per_cu * cus;
+  return c;
+}
+
 hipError_t launch_route(const float* Z, const float* beta, int64_t N, int E, int K,
                         int32_t* ids, float* S, float* alpha, float* margin,
                         hipStream_t stream) {
   const int nv = (E + kWave - 1) / kWave;
-  int64_t blocks = (N + 3) / 4;
-  if (blocks > 2048) blocks = 2048;  // 8192 waves walk the rows with a grid stride
-  const dim3 grid((unsigned)blocks), block(256);
   // alpha alone: keys-only variant
   const bool alpha_only = ids == nullptr && S == nullptr && margin == nullptr && alpha != nullptr;
+  // The waves walk the rows with a grid stride; the grid is capped at what is
+  // resident at once, so that no wave waits for a second round.
+  int64_t blocks = (N + 3) / 4;
+  const int64_t cap = route_resident_blocks(nv, alpha_only);
+  if (blocks > cap) blocks = cap;
+  const dim3 grid((unsigned)blocks), block(256);
   switch (nv) {
 #define MOE_ROUTE_CASE(V)                                                                   \
     case V:                                                                                 \
