@@ -8,16 +8,18 @@
 //
 // One wave per token row (a wave walks rows with a grid stride and loads the
 // next row while selecting the current one).  Lane l holds the experts l,
-// l+64, ... (at most six for E <= 384), turns each biased score into an
-// order-preserving 32-bit key
-// and sorts its own few entries (key descending, expert ascending).  K+1
-// rounds of a wave-wide max over the lanes' current heads then pick the
-// winners in global order; ties between lanes go to the lower expert id
-// through a second (rare) min-reduction.  The row is read once from HBM.
+// l+64, ... (at most six for E <= 384) and turns each biased score into an
+// order-preserving 32-bit key.  The selection order is key descending, then
+// expert ascending (-0 and +0 share a key).  The row is read once from HBM.
+//
+// Full selection: K+1 rounds of a wave-wide max over the lanes' maxima give a
+// lower bound L on the (K+1)-th largest key; the few entries with key >= L
+// are compacted into LDS and ranked exactly (see the comments in the code).
 //
 // ALPHA_ONLY (the first pass of a bias update, which needs alpha alone): the
 // value of the (K+1)-th largest key does not depend on how ties are ordered,
-// so only keys are sorted and popped, with no tie-break and no ids.
+// so each lane sorts its keys and K+1 rounds pop the wave-wide maximum, with
+// no ids.
 #include "common.h"
 #include "kernels.h"
 
@@ -30,6 +32,8 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     float* __restrict__ alpha, float* __restrict__ margin) {
   const int lane = lane_id();
   const int64_t nwaves = (int64_t)gridDim.x * 4;
+  // per wave: candidate composites of the current row (at most 64 * NV)
+  __shared__ uint64_t cand[4][ALPHA_ONLY ? 1 : kWave * NV];
   int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= N) return;  // whole wave leaves together
 
@@ -56,14 +60,10 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     if (nrow < N) load_row(nrow, nxt);
 
     uint32_t key[NV];
-    uint32_t eid[NV];
-    float zv[NV];
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int e = lane + kWave * j;
-      zv[j] = cur[j];
       key[j] = (e < E) ? f32_order_key(cur[j] + bv[j]) : 0u;  // 0: below every finite value
-      eid[j] = (uint32_t)e;
     }
     if (ALPHA_ONLY) {
 #pragma unroll
@@ -93,61 +93,76 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
       for (int j = 0; j < NV; ++j) cur[j] = nxt[j];
       continue;
     }
-    // Per-lane sort, key descending; equal keys keep ascending expert order
-    // (insertion sort moves an entry only past strictly smaller keys).
+    // Full selection.  (1) L = the (K+1)-th largest of the 64 lane maxima,
+    // counted with multiplicity: the K+1 lanes popped hold K+1 distinct
+    // entries >= L, so the row's (K+1)-th largest key is >= L and every entry
+    // of the top K+1 is a candidate (key >= L).  (2) The candidates, usually
+    // a handful, are compacted into LDS as 64-bit composites
+    // (key << 32) | (2^32 - 1 - expert): distinct, and ordered exactly as
+    // (key descending, expert ascending).  (3) Each candidate's rank is the
+    // number of larger composites; ranks 0..K-1 are the selection in order,
+    // ranks K-1 and K give the margin and alpha.
+    uint32_t lm = key[0];
 #pragma unroll
-    for (int i = 1; i < NV; ++i) {
-#pragma unroll
-      for (int j = i; j > 0; --j) {
-        const bool sw = key[j] > key[j - 1];
-        const uint32_t k0 = key[j - 1], k1 = key[j];
-        const uint32_t e0 = eid[j - 1], e1 = eid[j];
-        const float z0 = zv[j - 1], z1 = zv[j];
-        key[j - 1] = sw ? k1 : k0; key[j] = sw ? k0 : k1;
-        eid[j - 1] = sw ? e1 : e0; eid[j] = sw ? e0 : e1;
-        zv[j - 1] = sw ? z1 : z0; zv[j] = sw ? z0 : z1;
-      }
-    }
-
-    uint32_t key_k = 0u, key_k1 = 0u;  // keys of the K-th and (K+1)-th winners
-    uint32_t my_id = 0;
-    float my_z = 0.0f;
+    for (int j = 1; j < NV; ++j) lm = max(lm, key[j]);
+    uint32_t L = 0u;
 #pragma unroll
     for (int k = 0; k <= MOE_KMAX_INTERNAL; ++k) {
       if (k > K) break;  // uniform
-      const uint32_t head = key[0];
-      const uint32_t m = wave_max_u32(head);
-      const uint64_t tied = ballot(head == m);
-      int win;
-      if (__popcll(tied) == 1) {
-        win = __ffsll((unsigned long long)tied) - 1;
-      } else {
-        const uint32_t cand = (head == m) ? eid[0] : 0xFFFFFFFFu;
-        const uint32_t best = wave_min_u32(cand);
-        win = __ffsll((unsigned long long)ballot(head == m && eid[0] == best)) - 1;
-      }
-      const uint32_t wid = readlane_u32(eid[0], win);
-      const float wz = __uint_as_float(readlane_u32(__float_as_uint(zv[0]), win));
-      if (k == K - 1) key_k = m;
-      if (k == K) key_k1 = m;
-      if (lane == k) { my_id = wid; my_z = wz; }
-      if (lane == win) {
+      L = wave_max_u32(lm);
+      const int win = __ffsll((unsigned long long)ballot(lm == L)) - 1;
+      if (lane == win) lm = 0u;
+    }
+    uint32_t c = 0;
 #pragma unroll
-        for (int j = 0; j + 1 < NV; ++j) { key[j] = key[j + 1]; eid[j] = eid[j + 1]; zv[j] = zv[j + 1]; }
-        key[NV - 1] = 0u;
+    for (int j = 0; j < NV; ++j) c += (key[j] >= L) ? 1u : 0u;
+    // exclusive prefix of the per-lane counts (c <= 6), bit by bit
+    uint32_t off = 0, total = 0;
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+      const uint64_t m = ballot(((c >> b) & 1u) != 0u);
+      off += (uint32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
+      total += (uint32_t)__popcll(m) << b;
+    }
+    uint64_t* cl = cand[threadIdx.x >> 6];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      if (key[j] >= L) {
+        const uint32_t e = (uint32_t)(lane + kWave * j);
+        cl[off++] = ((uint64_t)key[j] << 32) | (uint64_t)(0xFFFFFFFFu - e);
       }
     }
-
-    if (lane < K) {
-      if (ids) ids[row * K + lane] = (int32_t)my_id;
-      if (S) S[row * K + lane] = (float)(1.0 / (1.0 + exp(-(double)my_z)));
+    // the wave's own LDS writes are complete before its reads below
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    uint32_t key_k = 0u, key_k1 = 0u;
+    for (uint32_t i = (uint32_t)lane; i < total; i += kWave) {
+      const uint64_t ci = cl[i];
+      uint32_t rank = 0;
+      for (uint32_t j = 0; j < total; ++j) rank += (cl[j] > ci) ? 1u : 0u;
+      if (rank < (uint32_t)K) {
+        const uint32_t e = 0xFFFFFFFFu - (uint32_t)ci;
+        if (ids) ids[row * K + rank] = (int32_t)e;
+        if (S) {
+          const float z = Z[row * (int64_t)E + e];
+          S[row * K + rank] = (float)(1.0 / (1.0 + exp(-(double)z)));
+        }
+      }
+      if (rank == (uint32_t)K - 1) key_k = (uint32_t)(ci >> 32);
+      if (rank == (uint32_t)K) key_k1 = (uint32_t)(ci >> 32);
     }
+    const uint64_t hk = ballot(key_k != 0u), hk1 = ballot(key_k1 != 0u);
+    key_k = readlane_u32(key_k, __ffsll((unsigned long long)hk) - 1);
+    key_k1 = readlane_u32(key_k1, __ffsll((unsigned long long)hk1) - 1);
     if (lane == 0) {
       const float vK = f32_from_order_key(key_k);
       const float vK1 = f32_from_order_key(key_k1);
       if (alpha) alpha[row] = -vK1;
       if (margin) margin[row] = vK - vK1;
     }
+    // the next row's candidates overwrite this row's list
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int j = 0; j < NV; ++j) cur[j] = nxt[j];
   }
