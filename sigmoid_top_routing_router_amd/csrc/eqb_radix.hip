@@ -20,9 +20,9 @@
 //    with integer atomics (order-independent, so deterministic).
 //  * eqb_scan_kernel: one wave per expert scans its 256 bins from the top,
 //    finds the bin that holds the wanted rank and narrows the key prefix.
-// After the last pass the last scan block to finish subtracts the mean of the
-// raw biases: one thread sums them in expert order in fp64, every thread then
-// writes fp32(fp64(beta_raw) - mean).
+// After the last pass a one-block kernel subtracts the mean of the raw biases:
+// one thread sums them in expert order in fp64, every thread then writes
+// fp32(fp64(beta_raw) - mean).
 #include "common.h"
 #include "kernels.h"
 
@@ -35,10 +35,9 @@ constexpr int kEqbThreads = 512;              // 8 waves: 8 rows at a time
 constexpr int kEqbRowLanes = kEqbThreads / kEqbCols;
 constexpr int kEqbUnroll = 12;                // rows per lane with loads in flight
 
-// Histograms of all passes, then a 64-word tail whose first word is the
-// ticket counter of the centring step (zeroed together with the histograms).
+// Histograms of all passes.
 size_t eqb_hist_bytes(int E, int key_bits) {
-  return ((size_t)(key_bits / 8) * (size_t)E * 256u + 64u) * sizeof(uint32_t);
+  return (size_t)(key_bits / 8) * (size_t)E * 256u * sizeof(uint32_t);
 }
 size_t eqb_state_bytes(int E) { return (size_t)(2 * E + 4) * sizeof(uint32_t); }
 
@@ -109,59 +108,55 @@ __global__ __launch_bounds__(kEqbThreads) void eqb_hist_kernel(
 }
 
 // One wave per expert.  rank0 is the wanted 1-based rank for pass 0 (r+1).
-// In the last pass the quantile is decoded, and the last block to finish
-// (integer ticket counter, zeroed before the first pass) centres the biases.
+// In the last pass the quantile is decoded into qraw (and quantile_out).
 __global__ __launch_bounds__(256) void eqb_scan_kernel(
     const uint32_t* __restrict__ hist, uint32_t* __restrict__ prefix,
     uint32_t* __restrict__ rank, int E, int pass, int last, int key_bits,
-    uint32_t rank0, float* __restrict__ qraw, float* __restrict__ quantile_out,
-    uint32_t* __restrict__ ticket, float* __restrict__ beta_out) {
+    uint32_t rank0, float* __restrict__ qraw, float* __restrict__ quantile_out) {
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = lane_id();
-  if (e < E) {
-    const uint4 v = reinterpret_cast<const uint4*>(hist + (size_t)e * 256)[lane];
-    const uint32_t s = v.x + v.y + v.z + v.w;
-    const uint32_t incl = wave_inclusive_sum_u32(s);
-    const uint32_t total = readlane_u32(incl, 63);
-    const uint32_t want = (pass == 0) ? rank0 : rank[e];
-    // Bins of this lane from the top: 4l+3, 4l+2, 4l+1, 4l.
-    uint32_t c = total - incl;  // entries in the bins above this lane's four
-    int found = -1;
-    uint32_t nr = 0;
-    const uint32_t bins[4] = {v.w, v.z, v.y, v.x};
+  if (e >= E) return;
+  const uint4 v = reinterpret_cast<const uint4*>(hist + (size_t)e * 256)[lane];
+  const uint32_t s = v.x + v.y + v.z + v.w;
+  const uint32_t incl = wave_inclusive_sum_u32(s);
+  const uint32_t total = readlane_u32(incl, 63);
+  const uint32_t want = (pass == 0) ? rank0 : rank[e];
+  // Bins of this lane from the top: 4l+3, 4l+2, 4l+1, 4l.
+  uint32_t c = total - incl;  // entries in the bins above this lane's four
+  int found = -1;
+  uint32_t nr = 0;
+  const uint32_t bins[4] = {v.w, v.z, v.y, v.x};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (found < 0 && c < want && want <= c + bins[i]) { found = 4 * lane + 3 - i; nr = want - c; }
-      c += bins[i];
-    }
-    const uint64_t hit = ballot(found >= 0);
-    const int src = hit ? (__ffsll((unsigned long long)hit) - 1) : 0;
-    const uint32_t bin = readlane_u32((uint32_t)found, src);
-    const uint32_t new_rank = readlane_u32(nr, src);
-    if (lane == 0) {
-      const uint32_t p = ((pass == 0) ? 0u : (prefix[e] << 8)) | (bin & 0xFFu);
-      prefix[e] = p;
-      rank[e] = new_rank;
-      if (last) {
-        const float q = (key_bits == 16) ? bf16_bits_to_f32(bf16_from_order_key(p))
-                                         : f32_from_order_key(p);
-        qraw[e] = q;
-        if (quantile_out) quantile_out[e] = q;
-      }
+  for (int i = 0; i < 4; ++i) {
+    if (found < 0 && c < want && want <= c + bins[i]) { found = 4 * lane + 3 - i; nr = want - c; }
+    c += bins[i];
+  }
+  const uint64_t hit = ballot(found >= 0);
+  const int src = hit ? (__ffsll((unsigned long long)hit) - 1) : 0;
+  const uint32_t bin = readlane_u32((uint32_t)found, src);
+  const uint32_t new_rank = readlane_u32(nr, src);
+  if (lane == 0) {
+    const uint32_t p = ((pass == 0) ? 0u : (prefix[e] << 8)) | (bin & 0xFFu);
+    prefix[e] = p;
+    rank[e] = new_rank;
+    if (last) {
+      const float q = (key_bits == 16) ? bf16_bits_to_f32(bf16_from_order_key(p))
+                                       : f32_from_order_key(p);
+      qraw[e] = q;
+      if (quantile_out) quantile_out[e] = q;
     }
   }
-  if (!last) return;
-  __shared__ bool is_last;
+}
+
+// Centring of the raw biases -Q_e: one thread sums them in expert order in
+// fp64, every thread writes fp32(fp64(-Q_e) - mean).  A kernel of its own
+// (one block) after the last scan, so the quantiles of all scan blocks are
+// visible without device-wide fences.
+__global__ __launch_bounds__(256) void eqb_centre_kernel(const float* __restrict__ qraw, int E,
+                                                         float* __restrict__ beta_out) {
   __shared__ double mean_s;
   __shared__ float q_s[kEqbMaxE];
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) is_last = atomicAdd(ticket, 1u) == gridDim.x - 1;
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  for (int i = threadIdx.x; i < E; i += blockDim.x)
-    q_s[i] = reinterpret_cast<volatile const float*>(qraw)[i];
+  for (int i = threadIdx.x; i < E; i += blockDim.x) q_s[i] = qraw[i];
   __syncthreads();
   if (threadIdx.x == 0) {
     double acc = 0.0;
@@ -205,10 +200,12 @@ hipError_t launch_eqb_scan(const EqbWork& w, int E, int K, int key_bits, int pas
                            hipStream_t stream) {
   const int passes = key_bits / 8;
   const int64_t r = (n_total * (int64_t)K) / E;
+  const bool last = pass == passes - 1;
   hipLaunchKernelGGL(eqb_scan_kernel, dim3((unsigned)((E + 3) / 4)), dim3(256), 0, stream,
                      w.hist + (size_t)pass * E * 256, w.state, w.state + E, E, pass,
-                     pass == passes - 1 ? 1 : 0, key_bits, (uint32_t)(r + 1), w.qraw,
-                     quantile_out, w.hist + (size_t)passes * E * 256, beta_out);
+                     last ? 1 : 0, key_bits, (uint32_t)(r + 1), w.qraw, quantile_out);
+  if (last && beta_out)
+    hipLaunchKernelGGL(eqb_centre_kernel, dim3(1), dim3(256), 0, stream, w.qraw, E, beta_out);
   return hipGetLastError();
 }
 

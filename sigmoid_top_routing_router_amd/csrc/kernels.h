@@ -17,7 +17,7 @@ hipError_t launch_route(const float* Z, const float* beta, int64_t N, int E, int
 
 // ---------------------------------------------------------------- EQB
 // Workspace carved by the caller (all 256-byte aligned):
-//   hist  [passes][E][256] uint32 (passes = key_bits / 8) + 64-word tail
+//   hist  [passes][E][256] uint32 (passes = key_bits / 8)
 //   state [2*E + 4] uint32 (per-expert key prefix and remaining rank, counter)
 //   qraw  [E] fp32 (raw quantiles)
 struct EqbWork {

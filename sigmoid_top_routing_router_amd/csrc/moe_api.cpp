@@ -392,7 +392,7 @@ moe_status_t moe_lei_backward(const float* logits, const int32_t* topk_ids,
 }
 
 // ---- exact quantile update over a batch that arrives in several parts
-// State: histograms (+ ticket tail), selection state, raw quantiles.
+// State: histograms, selection state, raw quantiles.
 static moe::EqbWork carve_eqb_state(Carver& c, int E, int key_bits) {
   moe::EqbWork w;
   w.hist = c.take<uint32_t>(moe::eqb_hist_bytes(E, key_bits) / 4);
