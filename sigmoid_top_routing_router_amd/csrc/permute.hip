@@ -8,7 +8,8 @@
 // segment (pair index t*K+k; the K experts of a token are distinct, so this
 // is also the order of t).
 //
-// Kernels (all integer work, bit-exact and deterministic):
+// Kernels (all integer work, bit-exact and deterministic); batches of at most
+// 16384 pairs use perm_small_kernel, one block doing all four steps:
 //  1. perm_count_kernel: one wave per chunk of kChunk consecutive pairs
 //     counts the experts of its chunk in LDS -> chunk_counts[e][chunk].
 //  2. perm_scan_kernel: one block per expert turns its row of chunk counts
@@ -172,9 +173,108 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
     if (cnt[e]) atomicAdd((uint32_t*)counts + e, cnt[e]);
 }
 
+// Small batches (pairs <= kSmallPairs): the whole stable counting sort in one
+// block of 16 waves.  Wave w owns the contiguous chunk of pairs
+// [w*len, (w+1)*len): (1) it counts its chunk's experts into LDS; (2) thread e
+// walks the 16 wave counts of expert e in order, giving each wave its base
+// inside the expert's segment, and the expert totals; (3) a block-wide scan
+// gives the offsets and the m-tile table; (4) each wave scatters its chunk in
+// order, 64 pairs at a time, with the same nine-ballot ranking as
+// perm_scatter_kernel.  One launch instead of four.
+constexpr int kSmallWaves = 16;
+constexpr int64_t kSmallPairs = 16384;
+
+__global__ __launch_bounds__(1024) void perm_small_kernel(
+    const int32_t* __restrict__ ids, int64_t pairs, int E, int bm,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_src, int32_t* __restrict__ src_pos,
+    int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+  __shared__ uint32_t wcnt[kSmallWaves][kMaxE];  // counts, then bases per wave
+  __shared__ uint32_t tot[kMaxE];
+  __shared__ uint32_t wsum_c[kSmallWaves], wsum_t[kSmallWaves];
+  const int tid = threadIdx.x, w = tid >> 6, lane = lane_id();
+  const int64_t len = (pairs + kSmallWaves - 1) / kSmallWaves;
+  const int64_t i0 = (int64_t)w * len;
+  const int64_t i1 = min(pairs, i0 + len);
+  for (int i = tid; i < kSmallWaves * kMaxE; i += blockDim.x) (&wcnt[0][0])[i] = 0u;
+  __syncthreads();
+  for (int64_t i = i0 + lane; i < i1; i += kWave) atomicAdd(&wcnt[w][ids[i]], 1u);
+  __syncthreads();
+  // (2) bases of the waves inside each expert's segment (exclusive), totals
+  for (int e = tid; e < E; e += blockDim.x) {
+    uint32_t run = 0;
+    for (int q = 0; q < kSmallWaves; ++q) {
+      const uint32_t c = wcnt[q][e];
+      wcnt[q][e] = run;
+      run += c;
+    }
+    tot[e] = run;
+  }
+  __syncthreads();
+  // (3) offsets and the m-tile table: a scan in expert order; E <= 384 fits
+  // one expert per thread of the first 384 threads (7 waves)
+  const uint32_t c = tid < E ? tot[tid] : 0u;
+  const uint32_t t = (c + bm - 1) / bm;
+  const uint32_t ic = wave_inclusive_sum_u32(c);
+  const uint32_t it = wave_inclusive_sum_u32(t);
+  if (lane == kWave - 1) { wsum_c[w] = ic; wsum_t[w] = it; }
+  __syncthreads();
+  uint32_t bc = 0, bt = 0;
+  for (int q = 0; q < w; ++q) { bc += wsum_c[q]; bt += wsum_t[q]; }
+  const uint32_t off = bc + ic - c;
+  uint32_t toff = bt + it - t;
+  if (tid == blockDim.x - 1) {
+    offsets[E] = (int32_t)(bc + ic);
+    *n_tiles = (int32_t)(bt + it);
+  }
+  if (tid < E) {
+    counts[tid] = (int32_t)c;
+    offsets[tid] = (int32_t)off;
+    for (uint32_t r = 0; r < c; r += bm, ++toff) {
+      int4 ent;
+      ent.x = tid;
+      ent.y = (int32_t)(off + r);
+      ent.z = (int32_t)min((uint32_t)bm, c - r);
+      ent.w = (int32_t)r;
+      reinterpret_cast<int4*>(tiles)[toff] = ent;
+    }
+    tot[tid] = off;  // segment starts, for the scatter
+  }
+  __syncthreads();
+  // (4) scatter, each wave its chunk in order
+  for (int e = lane; e < E; e += kWave) wcnt[w][e] += tot[e];
+  __builtin_amdgcn_wave_barrier();
+  for (int64_t j = i0; j < i1; j += kWave) {
+    const int64_t i = j + lane;
+    const bool ok = i < i1;
+    const uint32_t e = ok ? (uint32_t)ids[i] : 0u;
+    uint64_t mask = ballot(ok);
+#pragma unroll
+    for (int b = 0; b < 9; ++b) {
+      const bool bit = (e >> b) & 1u;
+      const uint64_t bb = ballot(bit);
+      mask &= bit ? bb : ~bb;
+    }
+    const uint64_t lower = mask & lanemask_lt();
+    if (ok) {
+      const uint32_t dst = wcnt[w][e] + (uint32_t)__popcll(lower);
+      sorted_src[dst] = (int32_t)i;
+      src_pos[i] = (int32_t)dst;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (ok && lower == 0ull) wcnt[w][e] += (uint32_t)__popcll(mask);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 hipError_t launch_permute(const int32_t* ids, int64_t N, int E, int K, int bm,
                           const PermWork& w, hipStream_t stream) {
   const int64_t pairs = N * (int64_t)K;
+  if (pairs <= kSmallPairs) {
+    hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(1024), 0, stream, ids, pairs, E, bm,
+                       w.counts, w.offsets, w.sorted_src, w.src_pos, w.tiles, w.n_tiles);
+    return hipGetLastError();
+  }
   const int64_t n_chunks = perm_num_chunks(pairs);
   const dim3 block(256);
   const dim3 cgrid((unsigned)((n_chunks + kPermWaves - 1) / kPermWaves));
