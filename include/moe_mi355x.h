@@ -278,9 +278,11 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_weights_t* w,
                          void* stream);
 
 /*
- * Stage timing (a profiling aid).  While enabled, every moe_forward call
- * records a HIP timing event on its stream at each stage boundary (events are
- * created on first use and reused; no device memory is allocated).
+ * Stage timing (a profiling aid).  moe_stage_timing(1): every moe_forward
+ * call records a HIP timing event on its stream at each stage boundary;
+ * moe_stage_timing(2): only the two events around stage 3 (the routed
+ * gate/up GEMM), which disturb the stream least; 0 turns timing off.  Events
+ * are created on first use and reused; no device memory is allocated.
  * moe_stage_times waits for the recorded events, writes the summed
  * milliseconds of each stage since the previous read into
  * ms[MOE_NUM_STAGES], the number of recorded calls into *calls, and clears
@@ -288,7 +290,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_weights_t* w,
  * launch), 1 routing (selection, token bias, quantile update, re-route,
  * loads), 2 grouping, 3 routed gate/up GEMM, 4 routed down GEMM, 5 shared
  * down GEMM, 6 weighted combine.
- * Errors: INVALID_ARGUMENT (NULL outputs), HIP.
+ * Errors: INVALID_ARGUMENT (NULL outputs, enable outside 0..2), HIP.
  */
 #define MOE_NUM_STAGES 7
 moe_status_t moe_stage_timing(int32_t enable);

@@ -299,9 +299,12 @@ def forward(x, weights: ExpertWeights, K: int, beta_in=None, recompute_bias: boo
     return (y, aux_t) if aux else y
 
 
-def stage_timing(enable: bool = True):
-    """Turn per-stage HIP-event timing of forward() on or off (clears it)."""
-    _lib.check(_lib.load().moe_stage_timing(1 if enable else 0))
+def stage_timing(enable=True):
+    """Per-stage HIP-event timing of forward(): True or 1 = every stage,
+    2 = only the routed gate/up GEMM (two events per call), False or 0 = off.
+    Clears what was recorded."""
+    mode = int(enable) if not isinstance(enable, bool) else (1 if enable else 0)
+    _lib.check(_lib.load().moe_stage_timing(mode))
 
 
 def stage_times():

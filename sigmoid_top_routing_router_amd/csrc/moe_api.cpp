@@ -169,9 +169,11 @@ moe_status_t check_problem(const moe_problem_t* p) {
 }
 
 // ---- stage timing: S+1 boundary events per recorded call
+constexpr int kGateUpStage = 3;  // the routed gate/up GEMM
 struct StageTimer {
   std::mutex mu;
   bool enabled = false;
+  bool gateup_only = false;      // record only the boundaries of stage 3
   std::vector<hipEvent_t> pool;  // reused across reads
   size_t used = 0;               // events recorded since the last read
 };
@@ -179,6 +181,7 @@ StageTimer g_timer;
 
 struct CallTimer {
   bool on = false;
+  bool gateup_only = false;
   size_t base = 0;
   int next = 0;
   hipStream_t st = nullptr;
@@ -187,6 +190,7 @@ struct CallTimer {
       std::lock_guard<std::mutex> g(g_timer.mu);
       if (!g_timer.enabled) return hipSuccess;
       on = true;
+      gateup_only = g_timer.gateup_only;
       st = s;
       base = g_timer.used;
       g_timer.used += MOE_NUM_STAGES + 1;
@@ -202,12 +206,13 @@ struct CallTimer {
   // Record the boundary after the current stage.
   hipError_t mark() {
     if (!on) return hipSuccess;
+    const int b = next++;
+    if (gateup_only && b != kGateUpStage && b != kGateUpStage + 1) return hipSuccess;
     hipEvent_t e;
     {
       std::lock_guard<std::mutex> g(g_timer.mu);
-      e = g_timer.pool[base + next];
+      e = g_timer.pool[base + b];
     }
-    ++next;
     return hipEventRecord(e, st);
   }
 };
@@ -225,8 +230,10 @@ extern "C" {
 int32_t moe_abi_version(void) { return 1; }
 
 moe_status_t moe_stage_timing(int32_t enable) {
+  if (enable < 0 || enable > 2) return fail(MOE_ERR_INVALID_ARGUMENT, "enable=%d outside [0, 2]", enable);
   std::lock_guard<std::mutex> g(g_timer.mu);
   g_timer.enabled = enable != 0;
+  g_timer.gateup_only = enable == 2;
   g_timer.used = 0;
   return ok();
 }
@@ -239,6 +246,14 @@ moe_status_t moe_stage_times(double* ms, int64_t* calls) {
   const size_t n = g_timer.used / per;
   for (size_t c = 0; c < n; ++c) {
     hipEvent_t* ev = g_timer.pool.data() + c * per;
+    if (g_timer.gateup_only) {
+      MOE_TRY_HIP(hipEventSynchronize(ev[kGateUpStage + 1]), "moe_stage_times");
+      float t = 0.0f;
+      MOE_TRY_HIP(hipEventElapsedTime(&t, ev[kGateUpStage], ev[kGateUpStage + 1]),
+                  "moe_stage_times");
+      ms[kGateUpStage] += t;
+      continue;
+    }
     MOE_TRY_HIP(hipEventSynchronize(ev[MOE_NUM_STAGES]), "moe_stage_times");
     for (int s = 0; s < MOE_NUM_STAGES; ++s) {
       float t = 0.0f;

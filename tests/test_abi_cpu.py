@@ -235,3 +235,8 @@ def test_lei_rejects_bad_arguments(lib):
     assert call(ws=p + 4100) == 1            # misaligned workspace
     assert call(wsb=need - 1) == 3
     assert call(K=9) == 2
+
+
+def test_stage_timing_modes(lib):
+    assert lib.moe_stage_timing(3) == 1 and lib.moe_stage_timing(-1) == 1
+    assert lib.moe_stage_timing(2) == 0 and lib.moe_stage_timing(0) == 0

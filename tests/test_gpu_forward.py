@@ -204,3 +204,11 @@ def test_stage_timing_records_every_stage(M):
     times, calls = M.stage_times()
     M.stage_timing(False)
     assert calls == 0
+    # light mode: only the routed gate/up GEMM is timed
+    M.stage_timing(2)
+    for _ in range(2):
+        M.forward(x, W, cfg.K, beta_in=dev(L.beta_in), recompute_bias=True)
+    times, calls = M.stage_times()
+    M.stage_timing(False)
+    assert calls == 2 and times["gate_up"] > 0
+    assert all(v == 0 for k, v in times.items() if k != "gate_up"), times
