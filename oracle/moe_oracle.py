@@ -321,6 +321,110 @@ def lei_backward(Z: np.ndarray, ids: np.ndarray, G: Optional[np.ndarray], lam: f
 
 
 # ---------------------------------------------------------------------------
+# FP8 experts ([K1D] FP8 section): E4M3 weights in 128 x 128 blocks with one
+# fp32 scale each, activations quantised per 1 x 128 group of a row.
+# ---------------------------------------------------------------------------
+E4M3_MAX = 448.0  # largest finite E4M3 value ([KPT] §4.4)
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa
+    bits; exponent 0 is subnormal; 0x7F and 0xFF are NaN, there is no inf)."""
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    v = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    v = np.where((e == 15) & (m == 7), np.nan, v)
+    return (sign * v).astype(F64)
+
+
+_E4M3_POS = e4m3_decode(np.arange(0x7F, dtype=np.uint8))  # codes 0..126, ascending
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 code, ties to the even code (even mantissa), magnitudes
+    above 448 saturated to 448; the sign is kept (so -0.0 -> 0x80)."""
+    x = np.asarray(x, F64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.searchsorted(_E4M3_POS, a, side="left")  # first value >= a
+    hi = np.minimum(hi, 126)
+    lo = np.maximum(hi - 1, 0)
+    d_hi = _E4M3_POS[hi] - a
+    d_lo = a - _E4M3_POS[lo]
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+
+
+def _quantize_group(v: np.ndarray):
+    """One group (any shape) of fp32 values: s = fp32(amax) / 448 in fp32, the
+    codes of fp32(v / s) clamped to +-448 (an all-zero group: s = 0, codes 0)."""
+    v = np.asarray(v, F32)
+    amax = np.float32(np.max(np.abs(v))) if v.size else np.float32(0)
+    if amax == 0:
+        return np.zeros(v.shape, np.uint8), np.float32(0)
+    s = np.float32(amax / np.float32(E4M3_MAX))
+    q = np.clip((v / s).astype(F32), -E4M3_MAX, E4M3_MAX)
+    return e4m3_encode(q), s
+
+
+def quantize_weight_blocks(W: np.ndarray, block: int = 128):
+    """[R, C] -> (codes [R, C] uint8, scales [ceil(R/b), ceil(C/b)] fp32),
+    one scale per block x block tile."""
+    W = np.asarray(W, F32)
+    R, C = W.shape
+    codes = np.zeros((R, C), np.uint8)
+    scales = np.zeros(((R + block - 1) // block, (C + block - 1) // block), F32)
+    for i in range(scales.shape[0]):
+        for j in range(scales.shape[1]):
+            blk = W[i * block:(i + 1) * block, j * block:(j + 1) * block]
+            q, sc = _quantize_group(blk)
+            codes[i * block:(i + 1) * block, j * block:(j + 1) * block] = q
+            scales[i, j] = sc
+    return codes, scales
+
+
+def quantize_row_groups(X: np.ndarray, group: int = 128):
+    """[N, C] -> (codes [N, C] uint8, scales [N, ceil(C/g)] fp32), one scale
+    per 1 x group piece of a row (the dynamic activation quantisation)."""
+    X = np.asarray(X, F32)
+    N, C = X.shape
+    codes = np.zeros((N, C), np.uint8)
+    scales = np.zeros((N, (C + group - 1) // group), F32)
+    for j in range(scales.shape[1]):
+        for n in range(N):
+            q, sc = _quantize_group(X[n, j * group:(j + 1) * group])
+            codes[n, j * group:(j + 1) * group] = q
+            scales[n, j] = sc
+    return codes, scales
+
+
+def dequantize_blocks(codes: np.ndarray, scales: np.ndarray, block: int = 128) -> np.ndarray:
+    v = e4m3_decode(codes)
+    sc = np.repeat(np.repeat(np.asarray(scales, F64), block, axis=0), block, axis=1)
+    return v * sc[:v.shape[0], :v.shape[1]]
+
+
+def dequantize_row_groups(codes: np.ndarray, scales: np.ndarray, group: int = 128) -> np.ndarray:
+    v = e4m3_decode(codes)
+    sc = np.repeat(np.asarray(scales, F64), group, axis=1)
+    return v * sc[:, :v.shape[1]]
+
+
+def swiglu_fp8(x_codes, x_scales, g_codes, g_scales, u_codes, u_scales, d_codes, d_scales):
+    """One SwiGLU expert on FP8 operands: G = X W_g^T and U = X W_u^T on the
+    dequantised values (fp64), H = SiLU(G) * U held in bf16, H quantised per
+    1 x 128 group, then H W_d^T on the dequantised values."""
+    X = dequantize_row_groups(x_codes, x_scales)
+    G = X @ dequantize_blocks(g_codes, g_scales).T
+    U = X @ dequantize_blocks(u_codes, u_scales).T
+    Hb = bf16_to_f32(f32_to_bf16_rne(silu(G) * U))
+    hq, hs = quantize_row_groups(Hb)
+    return dequantize_row_groups(hq, hs) @ dequantize_blocks(d_codes, d_scales).T
+
+
+# ---------------------------------------------------------------------------
 # The whole layer
 # ---------------------------------------------------------------------------
 def moe_layer(x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
