@@ -424,6 +424,48 @@ def swiglu_fp8(x_codes, x_scales, g_codes, g_scales, u_codes, u_scales, d_codes,
     return dequantize_row_groups(hq, hs) @ dequantize_blocks(d_codes, d_scales).T
 
 
+def quantize_expert_weights(w_gate, w_up, w_down, ws_gate, ws_up, ws_down) -> dict:
+    """Block-quantise every expert matrix ([E,h,d]/[E,h,d]/[E,d,h] routed,
+    [S,hs,d]/[S,hs,d]/[S,d,hs] shared) -> dict of codes and scales under the
+    names w_gate/s_gate, w_up/s_up, w_down/s_down, ws_gate/ss_gate,
+    ws_up/ss_up, ws_down/ss_down."""
+    out = {}
+    for name, W in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down),
+                    ("ws_gate", ws_gate), ("ws_up", ws_up), ("ws_down", ws_down)):
+        W = np.asarray(W, F32)
+        pairs = [quantize_weight_blocks(m) for m in W]
+        sname = "s" + name[1:] if name.startswith("w_") else "ss" + name[2:]
+        out[name] = np.stack([c for c, _ in pairs]) if pairs else np.zeros((0,) + W.shape[1:], np.uint8)
+        out[sname] = np.stack([sc for _, sc in pairs]) if pairs else \
+            np.zeros((0, (W.shape[1] + 127) // 128, (W.shape[2] + 127) // 128), F32)
+    return out
+
+
+def moe_combine_fp8(x, q: dict, ids, S, token_subset=None) -> np.ndarray:
+    """y_t = f_shared(x_t) + sum_{e in I_t} S_{t,e} f_e(x_t) ([KPT] §6.1) with
+    FP8 experts ([K1D] FP8 section): the rows of x are quantised per 1 x 128
+    group and every expert is ``swiglu_fp8`` on its tokens' codes, with the
+    weights' codes and block scales in ``q`` (see quantize_expert_weights).
+    Returns fp64 [T', d]."""
+    x = np.asarray(x, F32)
+    toks = np.arange(x.shape[0]) if token_subset is None else np.asarray(token_subset)
+    xq, xs = quantize_row_groups(x[toks])
+    ids_s = np.asarray(ids)[toks]
+    S_s = np.asarray(S, F64)[toks]
+    y = np.zeros((len(toks), x.shape[1]), F64)
+    for s in range(q["ws_gate"].shape[0]):
+        y += swiglu_fp8(xq, xs, q["ws_gate"][s], q["ss_gate"][s], q["ws_up"][s], q["ss_up"][s],
+                        q["ws_down"][s], q["ss_down"][s])
+    for e in range(q["w_gate"].shape[0]):
+        rows, slots = np.nonzero(ids_s == e)
+        if rows.size == 0:
+            continue
+        f = swiglu_fp8(xq[rows], xs[rows], q["w_gate"][e], q["s_gate"][e], q["w_up"][e],
+                       q["s_up"][e], q["w_down"][e], q["s_down"][e])
+        y[rows] += S_s[rows, slots][:, None] * f
+    return y
+
+
 # ---------------------------------------------------------------------------
 # The whole layer
 # ---------------------------------------------------------------------------

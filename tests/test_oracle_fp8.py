@@ -84,3 +84,103 @@ def test_weight_blocks_ragged():
     sc = np.repeat(np.repeat(s.astype(np.float64), 128, 0), 128, 1)[:300, :200]
     tol = np.maximum(np.abs(W.astype(np.float64)) * 2.0 ** -4, sc * 2.0 ** -10) * (1 + 1e-6)
     assert np.all(np.abs(D - W) <= tol)
+
+
+# ---------------------------------------------------------------------------
+# FP8 experts.  The only rounding between the dequantised operands and the
+# output is that of H (bf16, then E4M3 in 1 x 128 groups), so an FP8 expert
+# must equal the fp64 SwiGLU of the dequantised x and weights within the
+# error that this rounding can carry through W_down:
+#   |dH_j| <= |H_j| 2^-8 + max(|Hb_j| 2^-4, s_g 2^-10)
+# (half a bf16 step, then half an E4M3 step or a subnormal step of the group
+# scale s_g).  The planted mistakes below show the bound is tight enough to
+# catch a transposed block-scale index and a missing quantisation of x.
+# ---------------------------------------------------------------------------
+def _blocky(rng, R, Cc, sd):
+    """Gaussian matrix whose 128 x 128 blocks differ in size by up to 100x."""
+    W = rng.standard_normal((R, Cc)) * sd
+    for i in range(0, R, 128):
+        for j in range(0, Cc, 128):
+            W[i:i + 128, j:j + 128] *= 10.0 ** rng.uniform(-1, 1)
+    return W.astype(np.float32)
+
+
+def _outlier_rows(rng, n, d, big=300.0):
+    """bf16-exact activations with one large value per 128-group (in a fixed
+    column of each group, returned as well), so that quantising the row
+    moves its small values a lot."""
+    X = rng.standard_normal((n, d)).astype(np.float32)
+    cols = np.arange(0, d, 128) + rng.integers(0, 128, d // 128)
+    X[:, cols] = big
+    return O.bf16_to_f32(O.f32_to_bf16_rne(X)), cols
+
+
+def _expert_bound(Xd, Gd, Ud, Dd):
+    H = O.silu(Xd @ Gd.T) * (Xd @ Ud.T)
+    Hb = O.bf16_to_f32(O.f32_to_bf16_rne(H)).astype(np.float64)
+    sg = np.repeat(np.abs(Hb).reshape(H.shape[0], -1, 128).max(axis=2) / 448.0, 128, axis=1)
+    err = np.abs(H) * 2.0 ** -8 + np.maximum(np.abs(Hb) * 2.0 ** -4, sg * 2.0 ** -10)
+    return H, (err @ np.abs(Dd).T) * (1 + 1e-6) + 1e-12
+
+
+def test_swiglu_fp8_within_h_rounding_bound():
+    rng = np.random.default_rng(21)
+    d = h = 256
+    Wg, Wu, Wd = _blocky(rng, h, d, 0.05), _blocky(rng, h, d, 0.05), _blocky(rng, d, h, 0.05)
+    # outliers of 1e5 push the other values of their group into the E4M3
+    # subnormals; zero weight columns under them keep them out of G and U
+    X, cols = _outlier_rows(rng, 16, d, 1e5)
+    Wg[:, cols] = 0.0
+    Wu[:, cols] = 0.0
+    xq, xs = O.quantize_row_groups(X)
+    gq, gs = O.quantize_weight_blocks(Wg)
+    uq, us = O.quantize_weight_blocks(Wu)
+    dq, ds = O.quantize_weight_blocks(Wd)
+    y = O.swiglu_fp8(xq, xs, gq, gs, uq, us, dq, ds)
+    Xd = O.dequantize_row_groups(xq, xs)
+    Gd, Ud, Dd = O.dequantize_blocks(gq, gs), O.dequantize_blocks(uq, us), O.dequantize_blocks(dq, ds)
+    H, bound = _expert_bound(Xd, Gd, Ud, Dd)
+    assert np.all(np.abs(y - H @ Dd.T) <= bound)
+    # planted: the gate scales read transposed
+    y_t = O.swiglu_fp8(xq, xs, gq, gs.T.copy(), uq, us, dq, ds)
+    assert np.any(np.abs(y_t - H @ Dd.T) > bound)
+    # planted: x used without its quantisation
+    H_raw = O.silu(X.astype(np.float64) @ Gd.T) * (X.astype(np.float64) @ Ud.T)
+    assert np.any(np.abs(H_raw @ Dd.T - H @ Dd.T) > bound)
+
+
+def test_moe_combine_fp8_within_bound_and_subset():
+    rng = np.random.default_rng(22)
+    N, d, E, K, h, hs = 24, 256, 4, 2, 128, 128
+    x, _ = _outlier_rows(rng, N, d)
+    w_gate = np.stack([_blocky(rng, h, d, 0.05) for _ in range(E)])
+    w_up = np.stack([_blocky(rng, h, d, 0.05) for _ in range(E)])
+    w_down = np.stack([_blocky(rng, d, h, 0.05) for _ in range(E)])
+    ws = [np.stack([_blocky(rng, *shp, 0.05)]) for shp in ((hs, d), (hs, d), (d, hs))]
+    Z = rng.standard_normal((N, E)).astype(np.float32)
+    ids, _, _ = O.route(Z, None, K)
+    S = O.mixture_weights(Z, ids)
+    q = O.quantize_expert_weights(w_gate, w_up, w_down, *ws)
+    y = O.moe_combine_fp8(x, q, ids, S)
+    # reference: fp64 layer on the dequantised x rows and weights
+    xq, xs = O.quantize_row_groups(x)
+    Xd = O.dequantize_row_groups(xq, xs)
+    deq = {k: np.stack([O.dequantize_blocks(c, s) for c, s in zip(q[k], q[sk])])
+           for k, sk in (("w_gate", "s_gate"), ("w_up", "s_up"), ("w_down", "s_down"),
+                         ("ws_gate", "ss_gate"), ("ws_up", "ss_up"), ("ws_down", "ss_down"))}
+    y_ref = O.moe_combine(Xd, deq["w_gate"], deq["w_up"], deq["w_down"], deq["ws_gate"],
+                          deq["ws_up"], deq["ws_down"], ids, S)
+    bound = _expert_bound(Xd, deq["ws_gate"][0], deq["ws_up"][0], deq["ws_down"][0])[1]
+    for e in range(E):
+        rows, slots = np.nonzero(ids == e)
+        b = _expert_bound(Xd[rows], deq["w_gate"][e], deq["w_up"][e], deq["w_down"][e])[1]
+        bound[rows] += np.asarray(S, np.float64)[rows, slots][:, None] * b
+    assert np.all(np.abs(y - y_ref) <= bound)
+    # planted: the mixture weight dropped on the routed experts
+    y_noS = O.moe_combine_fp8(x, q, ids, np.ones_like(S))
+    assert np.any(np.abs(y_noS - y_ref) > bound)
+    # rows are quantised independently, so a token subset is a row selection
+    # (up to the summation order of the fp64 products)
+    sub = [5, 0, 17]
+    assert np.allclose(O.moe_combine_fp8(x, q, ids, S, token_subset=sub), y[sub],
+                       rtol=1e-12, atol=1e-9)
