@@ -165,8 +165,8 @@ def main():
         record_traffic(args.workload, *args.record_traffic, args.calibrate_copy_mib or 1024)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md); use --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the layer has no multi-GPU path "
+              "(no expert or data sharding across devices); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

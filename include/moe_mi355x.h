@@ -278,6 +278,69 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_weights_t* w,
                          void* stream);
 
 /*
+ * FP8 (E4M3) experts, [K1D] FP8 section: expert weights stored as E4M3 in
+ * 128 x 128 blocks with one fp32 scale per block, activations quantised on
+ * the fly in 1 x 128 groups of a row; the router stays bf16.  The pages fix
+ * the format but not the scale rule; here every group or block uses
+ * s = fp32(amax) / 448 (448 = largest E4M3 value) and each value v becomes
+ * the E4M3 code of min(max(fp32(v / s), -448), 448), rounded to nearest even;
+ * an all-zero group gets s = 0 and zero codes.  A value is code * scale.
+ *
+ * moe_fp8_quantize_blocks - `count` bf16 matrices w [count,rows,cols] ->
+ *   codes [count,rows,cols] (uint8) and scales
+ *   [count, ceil(rows/128), ceil(cols/128)] fp32 (ragged edge blocks use
+ *   their valid part).  1 <= rows, cols <= 65536, count >= 0.
+ * moe_fp8_quantize_rows - bf16 rows x [n,cols] -> codes [n,cols] and scales
+ *   [n, cols/128]; cols % 128 == 0 (128 <= cols <= 65536), n >= 0, x
+ *   4-byte aligned.
+ * Both enqueue one kernel on `stream`; outputs are fully overwritten.
+ * Errors: INVALID_ARGUMENT (NULL or misaligned pointers), UNSUPPORTED_SHAPE, HIP.
+ */
+moe_status_t moe_fp8_quantize_blocks(const uint16_t* w, int64_t count, int32_t rows,
+                                     int32_t cols, uint8_t* codes, float* scales, void* stream);
+moe_status_t moe_fp8_quantize_rows(const uint16_t* x, int64_t n, int32_t cols, uint8_t* codes,
+                                   float* scales, void* stream);
+
+/* Weights of moe_forward_fp8.  Codes are E4M3 bytes, row-major, 16-byte
+ * aligned; scales fp32 [.., rows/128, cols/128] as moe_fp8_quantize_blocks
+ * writes them. */
+typedef struct {
+  const uint16_t* w_router;  /* [E,d] bf16 (may be NULL when logits_in is set) */
+  const uint8_t* w_gate;     /* [E,h,d]   codes */
+  const float* s_gate;       /* [E,h/128,d/128] */
+  const uint8_t* w_up;       /* [E,h,d] */
+  const float* s_up;         /* [E,h/128,d/128] */
+  const uint8_t* w_down;     /* [E,d,h] */
+  const float* s_down;       /* [E,d/128,h/128] */
+  const uint8_t* ws_gate;    /* [n_shared,hs,d] */
+  const float* ss_gate;      /* [n_shared,hs/128,d/128] */
+  const uint8_t* ws_up;      /* [n_shared,hs,d] */
+  const float* ss_up;        /* [n_shared,hs/128,d/128] */
+  const uint8_t* ws_down;    /* [n_shared,d,hs] */
+  const float* ss_down;      /* [n_shared,d/128,hs/128] */
+} moe_fp8_weights_t;
+
+/*
+ * moe_forward_fp8 - moe_forward with E4M3 experts (routed and shared).
+ * Routing, bias update, grouping and combine are those of moe_forward (the
+ * same kernels; ids, weights, loads and grouping equal moe_forward's for
+ * the same logits).  x is quantised per 1 x 128 group; each expert computes
+ * G = X W_g^T and U = X W_u^T from the codes with fp32 accumulation, one
+ * scale product per 128 k; H = SiLU(G) * U is rounded to bf16 and quantised
+ * per 1 x 128 group; then H W_d^T, held in bf16 per pair; the combine
+ * accumulates in fp32.  Requires d % 128 == 0, h % 128 == 0 and (with a
+ * shared expert) hs % 128 == 0, besides the limits of moe_forward.
+ * Arguments and errors as moe_forward; workspace of at least
+ * moe_forward_fp8_workspace_bytes(p).  Stage timing covers it as well (the
+ * quantisation of x is part of stage 0).
+ */
+size_t moe_forward_fp8_workspace_bytes(const moe_problem_t* p);
+moe_status_t moe_forward_fp8(const moe_problem_t* p, const moe_fp8_weights_t* w,
+                             const uint16_t* x, const float* beta_in, uint16_t* y,
+                             moe_aux_t* aux, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
  * Stage timing (a profiling aid).  moe_stage_timing(1): every moe_forward
  * call records a HIP timing event on its stream at each stage boundary;
  * moe_stage_timing(2): only the two events around stage 3 (the routed

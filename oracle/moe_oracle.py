@@ -400,14 +400,17 @@ def quantize_row_groups(X: np.ndarray, group: int = 128):
     return codes, scales
 
 
+_E4M3_ALL = e4m3_decode(np.arange(256, dtype=np.uint8))  # the value of every code
+
+
 def dequantize_blocks(codes: np.ndarray, scales: np.ndarray, block: int = 128) -> np.ndarray:
-    v = e4m3_decode(codes)
+    v = _E4M3_ALL[np.asarray(codes, np.uint8)]
     sc = np.repeat(np.repeat(np.asarray(scales, F64), block, axis=0), block, axis=1)
     return v * sc[:v.shape[0], :v.shape[1]]
 
 
 def dequantize_row_groups(codes: np.ndarray, scales: np.ndarray, group: int = 128) -> np.ndarray:
-    v = e4m3_decode(codes)
+    v = _E4M3_ALL[np.asarray(codes, np.uint8)]
     sc = np.repeat(np.asarray(scales, F64), group, axis=1)
     return v * sc[:, :v.shape[1]]
 

@@ -13,11 +13,13 @@ from dataclasses import dataclass
 from typing import Optional
 
 from . import _lib
-from ._lib import MOE_KEY32, MOE_RECOMPUTE_BIAS, MoeAux, MoeError, MoeProblem, MoeWeights
+from ._lib import (MOE_KEY32, MOE_RECOMPUTE_BIAS, MoeAux, MoeError, MoeFp8Weights, MoeProblem,
+                   MoeWeights)
 
 __all__ = ["route", "eqb_bias", "eqb_workspace_bytes", "EqbState", "eqb_bias_parts",
            "route_stats", "read_route_stats", "lei_backward", "forward",
-           "forward_workspace_bytes",
+           "forward_workspace_bytes", "fp8_quantize_blocks", "fp8_quantize_rows",
+           "Fp8ExpertWeights", "quantize_experts", "forward_fp8", "forward_fp8_workspace_bytes",
            "ExpertWeights", "MoeError", "load_library", "stage_timing", "stage_times"]
 
 AUX_FIELDS = [f for f, _ in MoeAux._fields_]
@@ -244,13 +246,124 @@ def forward_workspace_bytes(N, d, E, K, h, n_shared=1, h_shared=None,
     return int(_lib.load().moe_forward_workspace_bytes(C.byref(p)))
 
 
+def forward_fp8_workspace_bytes(N, d, E, K, h, n_shared=1, h_shared=None,
+                                recompute_bias=False, key_bits=16) -> int:
+    flags = (MOE_RECOMPUTE_BIAS if recompute_bias else 0) | (MOE_KEY32 if key_bits == 32 else 0)
+    p = _problem(N, d, E, K, h, n_shared, h_shared or h, flags, None, None)
+    return int(_lib.load().moe_forward_fp8_workspace_bytes(C.byref(p)))
+
+
+def fp8_quantize_blocks(w, stream=None):
+    """bf16 [count, R, C] (or [R, C]) -> (E4M3 codes uint8 of the same shape,
+    fp32 scales [count, ceil(R/128), ceil(C/128)] (or without count)), one
+    scale per 128 x 128 block."""
+    torch = _torch()
+    w = _dev(w, "w", _bf16())
+    squeeze = w.dim() == 2
+    w3 = w.unsqueeze(0) if squeeze else w
+    if w3.dim() != 3:
+        raise ValueError("w must be [R, C] or [count, R, C]")
+    cnt, R, Cc = w3.shape
+    codes = torch.empty((cnt, R, Cc), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((cnt, (R + 127) // 128, (Cc + 127) // 128), dtype=torch.float32,
+                         device=w.device)
+    _lib.check(_lib.load().moe_fp8_quantize_blocks(_ptr(w3), cnt, R, Cc, _ptr(codes),
+                                                   _ptr(scales), _stream(stream)))
+    return (codes[0], scales[0]) if squeeze else (codes, scales)
+
+
+def fp8_quantize_rows(x, stream=None):
+    """bf16 rows [n, C] (C % 128 == 0) -> (codes uint8 [n, C], fp32 scales
+    [n, C/128]), one scale per 1 x 128 group."""
+    torch = _torch()
+    x = _dev(x, "x", _bf16())
+    n, Cc = x.shape
+    codes = torch.empty((n, Cc), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((n, Cc // 128), dtype=torch.float32, device=x.device)
+    _lib.check(_lib.load().moe_fp8_quantize_rows(_ptr(x), n, Cc, _ptr(codes), _ptr(scales),
+                                                 _stream(stream)))
+    return codes, scales
+
+
+@dataclass
+class Fp8ExpertWeights:
+    """E4M3 expert weights with 128 x 128 block scales (torch tensors on the
+    GPU); the router stays bf16."""
+    w_router: object                   # [E, d] bf16
+    w_gate: object                     # [E, h, d] uint8 codes
+    s_gate: object                     # [E, h/128, d/128] fp32
+    w_up: object
+    s_up: object
+    w_down: object                     # [E, d, h]
+    s_down: object                     # [E, d/128, h/128]
+    ws_gate: object = None             # [S, hs, d]
+    ss_gate: object = None
+    ws_up: object = None
+    ss_up: object = None
+    ws_down: object = None             # [S, d, hs]
+    ss_down: object = None
+
+
+def quantize_experts(weights: ExpertWeights, stream=None) -> Fp8ExpertWeights:
+    """Quantise the expert weights of a bf16 layer with the library's block
+    quantiser; the router is kept as it is."""
+    q = {}
+    for name in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
+        t = getattr(weights, name)
+        codes, scales = (None, None) if t is None else fp8_quantize_blocks(t, stream)
+        q[name] = codes
+        q["s" + name[1:] if name.startswith("w_") else "ss" + name[2:]] = scales
+    return Fp8ExpertWeights(w_router=weights.w_router, **q)
+
+
+def _aux_tensors(aux, N, E, K, device):
+    torch = _torch()
+    shapes = {"logits": ((N, E), torch.float32), "topk_ids": ((N, K), torch.int32),
+              "topk_weights": ((N, K), torch.float32), "alpha": ((N,), torch.float32),
+              "margin": ((N,), torch.float32), "beta_out": ((E,), torch.float32),
+              "quantile_out": ((E,), torch.float32), "counts_before": ((E,), torch.int32),
+              "counts": ((E,), torch.int32), "offsets": ((E + 1,), torch.int32),
+              "sorted_src": ((N * K,), torch.int32), "src_pos": ((N, K), torch.int32)}
+    aux_t = {}
+    for name in aux:
+        if name not in shapes:
+            raise ValueError(f"unknown aux output {name!r}")
+        shp, dt = shapes[name]
+        aux_t[name] = torch.empty(shp, dtype=dt, device=device)
+    return aux_t
+
+
+def _run_forward(fp8, x, wstruct, N, d, E, K, h, n_shared, h_shared, beta_in, recompute_bias,
+                 key_bits, logit_offset, logits_in, aux, workspace, out, stream):
+    torch = _torch()
+    lib = _lib.load()
+    beta_in = _dev(beta_in, "beta_in", torch.float32, (E,))
+    logit_offset = _dev(logit_offset, "logit_offset", torch.float32, (E,))
+    logits_in = _dev(logits_in, "logits_in", torch.float32, (N, E))
+    flags = (MOE_RECOMPUTE_BIAS if recompute_bias else 0) | (MOE_KEY32 if key_bits == 32 else 0)
+    p = _problem(N, d, E, K, h, n_shared, h_shared, flags, logit_offset, logits_in)
+    ws_fn = lib.moe_forward_fp8_workspace_bytes if fp8 else lib.moe_forward_workspace_bytes
+    fwd = lib.moe_forward_fp8 if fp8 else lib.moe_forward
+    need = int(ws_fn(C.byref(p)))
+    if need == 0:  # rejected shape: the call reports why
+        _lib.check(fwd(C.byref(p), None, None, None, None, None, None, 0, None))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    y = out if out is not None else torch.empty((N, d), dtype=torch.bfloat16, device=x.device)
+    _dev(y, "out", _bf16(), (N, d))
+    aux_t = _aux_tensors(aux, N, E, K, x.device)
+    a = MoeAux(*[_ptr(aux_t.get(f)) for f in AUX_FIELDS]) if aux_t else None
+    _lib.check(fwd(C.byref(p), C.byref(wstruct), _ptr(x), _ptr(beta_in), _ptr(y),
+                   C.byref(a) if a is not None else None, _ptr(workspace),
+                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    return (y, aux_t) if aux else y
+
+
 def forward(x, weights: ExpertWeights, K: int, beta_in=None, recompute_bias: bool = False,
             key_bits: int = 16, logit_offset=None, logits_in=None, aux=(),
             workspace=None, out=None, stream=None):
     """MoE layer forward.  x: [N, d] bf16.  Returns y [N, d] bf16, or
     (y, dict) when ``aux`` names optional outputs (see moe_aux_t)."""
-    torch = _torch()
-    lib = _lib.load()
     x = _dev(x, "x", _bf16())
     N, d = x.shape
     wg = _dev(weights.w_gate, "w_gate", _bf16())
@@ -265,38 +378,44 @@ def forward(x, weights: ExpertWeights, K: int, beta_in=None, recompute_bias: boo
         _dev(weights.ws_gate, "ws_gate", _bf16(), (n_shared, h_shared, d))
         _dev(weights.ws_up, "ws_up", _bf16(), (n_shared, h_shared, d))
         _dev(weights.ws_down, "ws_down", _bf16(), (n_shared, d, h_shared))
-    beta_in = _dev(beta_in, "beta_in", torch.float32, (E,))
-    logit_offset = _dev(logit_offset, "logit_offset", torch.float32, (E,))
-    logits_in = _dev(logits_in, "logits_in", torch.float32, (N, E))
-    flags = (MOE_RECOMPUTE_BIAS if recompute_bias else 0) | (MOE_KEY32 if key_bits == 32 else 0)
-    p = _problem(N, d, E, K, h, n_shared, h_shared, flags, logit_offset, logits_in)
-    need = int(lib.moe_forward_workspace_bytes(C.byref(p)))
-    if need == 0:
-        _lib.check(lib.moe_forward(C.byref(p), None, None, None, None, None, None, 0, None))
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    y = out if out is not None else torch.empty((N, d), dtype=torch.bfloat16, device=x.device)
-    _dev(y, "out", _bf16(), (N, d))
     w = MoeWeights(_ptr(weights.w_router), _ptr(wg), _ptr(weights.w_up),
                    _ptr(weights.w_down), _ptr(weights.ws_gate), _ptr(weights.ws_up),
                    _ptr(weights.ws_down))
-    aux_t = {}
-    shapes = {"logits": ((N, E), torch.float32), "topk_ids": ((N, K), torch.int32),
-              "topk_weights": ((N, K), torch.float32), "alpha": ((N,), torch.float32),
-              "margin": ((N,), torch.float32), "beta_out": ((E,), torch.float32),
-              "quantile_out": ((E,), torch.float32), "counts_before": ((E,), torch.int32),
-              "counts": ((E,), torch.int32), "offsets": ((E + 1,), torch.int32),
-              "sorted_src": ((N * K,), torch.int32), "src_pos": ((N, K), torch.int32)}
-    for name in aux:
-        if name not in shapes:
-            raise ValueError(f"unknown aux output {name!r}")
-        shp, dt = shapes[name]
-        aux_t[name] = torch.empty(shp, dtype=dt, device=x.device)
-    a = MoeAux(*[_ptr(aux_t.get(f)) for f in AUX_FIELDS]) if aux_t else None
-    _lib.check(lib.moe_forward(C.byref(p), C.byref(w), _ptr(x), _ptr(beta_in), _ptr(y),
-                               C.byref(a) if a is not None else None, _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), _stream(stream)))
-    return (y, aux_t) if aux else y
+    return _run_forward(False, x, w, N, d, E, K, h, n_shared, h_shared, beta_in, recompute_bias,
+                        key_bits, logit_offset, logits_in, aux, workspace, out, stream)
+
+
+def forward_fp8(x, weights: Fp8ExpertWeights, K: int, beta_in=None,
+                recompute_bias: bool = False, key_bits: int = 16, logit_offset=None,
+                logits_in=None, aux=(), workspace=None, out=None, stream=None):
+    """MoE layer forward with E4M3 experts (moe_forward_fp8).  x: [N, d] bf16;
+    weights from ``quantize_experts`` or given codes and scales."""
+    torch = _torch()
+    x = _dev(x, "x", _bf16())
+    N, d = x.shape
+    u8, f32 = torch.uint8, torch.float32
+    wg = _dev(weights.w_gate, "w_gate", u8)
+    E, h, _ = wg.shape
+    _dev(weights.w_up, "w_up", u8, (E, h, d))
+    _dev(weights.w_down, "w_down", u8, (E, d, h))
+    for name, shp in (("s_gate", (E, h // 128, d // 128)), ("s_up", (E, h // 128, d // 128)),
+                      ("s_down", (E, d // 128, h // 128))):
+        _dev(getattr(weights, name), name, f32, shp)
+    if weights.w_router is not None:
+        _dev(weights.w_router, "w_router", _bf16(), (E, d))
+    n_shared = 0 if weights.ws_gate is None else int(weights.ws_gate.shape[0])
+    hs = h if n_shared == 0 else int(weights.ws_gate.shape[1])
+    if n_shared:
+        _dev(weights.ws_gate, "ws_gate", u8, (n_shared, hs, d))
+        _dev(weights.ws_up, "ws_up", u8, (n_shared, hs, d))
+        _dev(weights.ws_down, "ws_down", u8, (n_shared, d, hs))
+        for name, shp in (("ss_gate", (n_shared, hs // 128, d // 128)),
+                          ("ss_up", (n_shared, hs // 128, d // 128)),
+                          ("ss_down", (n_shared, d // 128, hs // 128))):
+            _dev(getattr(weights, name), name, f32, shp)
+    w = MoeFp8Weights(*[_ptr(getattr(weights, f)) for f, _ in MoeFp8Weights._fields_])
+    return _run_forward(True, x, w, N, d, E, K, h, n_shared, hs, beta_in, recompute_bias,
+                        key_bits, logit_offset, logits_in, aux, workspace, out, stream)
 
 
 def stage_timing(enable=True):

@@ -22,7 +22,9 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPOR
 EXPORTED = ["moe_route", "moe_eqb_workspace_bytes", "moe_eqb_bias", "moe_eqb_state_bytes",
             "moe_eqb_begin", "moe_eqb_accumulate", "moe_eqb_select", "moe_route_stats",
             "moe_lei_workspace_bytes", "moe_lei_backward",
-            "moe_forward_workspace_bytes", "moe_forward", "moe_status_string",
+            "moe_forward_workspace_bytes", "moe_forward", "moe_fp8_quantize_blocks",
+            "moe_fp8_quantize_rows", "moe_forward_fp8_workspace_bytes", "moe_forward_fp8",
+            "moe_status_string",
             "moe_last_error_message", "moe_abi_version", "moe_stage_timing",
             "moe_stage_times", "moe_stage_name"]
 NUM_STAGES = 7
@@ -39,6 +41,14 @@ class MoeWeights(C.Structure):
     _fields_ = [("w_router", C.c_void_p), ("w_gate", C.c_void_p), ("w_up", C.c_void_p),
                 ("w_down", C.c_void_p), ("ws_gate", C.c_void_p), ("ws_up", C.c_void_p),
                 ("ws_down", C.c_void_p)]
+
+
+class MoeFp8Weights(C.Structure):
+    _fields_ = [("w_router", C.c_void_p), ("w_gate", C.c_void_p), ("s_gate", C.c_void_p),
+                ("w_up", C.c_void_p), ("s_up", C.c_void_p), ("w_down", C.c_void_p),
+                ("s_down", C.c_void_p), ("ws_gate", C.c_void_p), ("ss_gate", C.c_void_p),
+                ("ws_up", C.c_void_p), ("ss_up", C.c_void_p), ("ws_down", C.c_void_p),
+                ("ss_down", C.c_void_p)]
 
 
 class MoeAux(C.Structure):
@@ -102,6 +112,15 @@ def load(path: str = LIB_PATH):
     lib.moe_forward.argtypes = [C.POINTER(MoeProblem), C.POINTER(MoeWeights), vp, vp, vp,
                                 C.POINTER(MoeAux), vp, C.c_size_t, vp]
     lib.moe_forward.restype = C.c_int
+    lib.moe_fp8_quantize_blocks.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+    lib.moe_fp8_quantize_blocks.restype = C.c_int
+    lib.moe_fp8_quantize_rows.argtypes = [vp, i64, i32, vp, vp, vp]
+    lib.moe_fp8_quantize_rows.restype = C.c_int
+    lib.moe_forward_fp8_workspace_bytes.argtypes = [C.POINTER(MoeProblem)]
+    lib.moe_forward_fp8_workspace_bytes.restype = C.c_size_t
+    lib.moe_forward_fp8.argtypes = [C.POINTER(MoeProblem), C.POINTER(MoeFp8Weights), vp, vp, vp,
+                                    C.POINTER(MoeAux), vp, C.c_size_t, vp]
+    lib.moe_forward_fp8.restype = C.c_int
     lib.moe_status_string.argtypes = [C.c_int]
     lib.moe_status_string.restype = C.c_char_p
     lib.moe_last_error_message.argtypes = []

@@ -90,6 +90,14 @@ struct GemmArgs {
   int64_t ldo;             // elements per output row
   const float* offset;     // router: per-column fp32 offset or NULL
   uint32_t a_bytes;        // size of the whole A buffer (< 4 GiB)
+  // FP8 operands only (A and B are E4M3 codes; lda and kdim count bytes):
+  const float* sa;         // A scales [A rows][kdim/128] (1 x 128 groups)
+  const float* sb0;        // B scales [E][ceil(b_rows/128)][kdim/128] (128 x 128 blocks)
+  const float* sb1;        // up-projection scales (gate/up only)
+  int64_t sb_es;           // floats between experts' scale matrices
+  // gate/up only: when set, H leaves as E4M3 codes (out, ldo bytes per row)
+  // with one fp32 scale per 1 x 128 group of a row (out_scale [rows][ldo/128])
+  float* out_scale;
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -134,6 +142,164 @@ __device__ __forceinline__ bool xcd_tile(int64_t work, int64_t& logical) {
   if (local >= share) return false;
   logical = (int64_t)(blockIdx.x % kXcd) * share + local;
   return logical < work;
+}
+
+// Second half of the bf16-output epilogue: the tile staged in LDS (row
+// stride OSTRIDE bytes) goes to global memory in whole rows, as bf16 or, for
+// gate/up with a.out_scale set, as E4M3 codes with one scale per row group.
+template <int MODE>
+__device__ __forceinline__ void epilogue_store(const GemmArgs& a, int nt, int64_t row0, int rows,
+                                               int tid, const char* lds_raw) {
+  constexpr int OCOLS = (MODE == kGateUp) ? BN / 2 : BN;
+  constexpr int OSTRIDE = OCOLS * 2 + 8;
+  constexpr int CPR = OCOLS / 8;  // 16-byte chunks per tile row
+  const int col0 = nt * OCOLS;
+  if (MODE == kGateUp && a.out_scale) {
+    // Quantised H: the 128 columns of a tile row are one 1 x 128 group
+    // (ldo % 128 == 0), held by 16 neighbouring lanes of 8 values each.  The
+    // bf16 values are quantised as a separate pass over H would do it:
+    // s = amax / 448, codes of min(max(v / s, -448), 448).
+    uint8_t* q = reinterpret_cast<uint8_t*>(a.out);
+    const int groups = (int)(a.ldo / 128);
+    for (int c = tid; c < BM * CPR; c += 512) {
+      const int rr = c / CPR, ch = c % CPR;
+      if (rr >= rows) break;  // the 16 lanes of a row leave together
+      const char* src = lds_raw + rr * OSTRIDE + ch * 16;
+      const uint2 lo = *reinterpret_cast<const uint2*>(src);
+      const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
+      const uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
+      float v[8];
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = __uint_as_float(w[j] << 16);
+        v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+        m = max(m, max(w[j] << 17 >> 1, (w[j] & 0x7FFF0000u)));
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+      const float amax = __uint_as_float(m);
+      const float sc = amax / 448.0f;
+      uint32_t cw[2] = {0u, 0u};
+      if (amax != 0.0f) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float t[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) t[i] = fminf(fmaxf(v[4 * j + i] / sc, -448.0f), 448.0f);
+          int pk = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+          pk = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], pk, true);
+          cw[j] = (uint32_t)pk;
+        }
+      }
+      *reinterpret_cast<uint2*>(q + (row0 + rr) * a.ldo + col0 + ch * 8) = make_uint2(cw[0], cw[1]);
+      if (ch == 0) a.out_scale[(row0 + rr) * groups + nt] = (amax != 0.0f) ? sc : 0.0f;
+    }
+    return;
+  }
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+  for (int c = tid; c < BM * CPR; c += 512) {
+    const int rr = c / CPR, ch = c % CPR;
+    if (rr >= rows) break;  // chunks are walked in row order
+    const int col = col0 + ch * 8;
+    if (col >= a.b_rows) continue;
+    const char* src = lds_raw + rr * OSTRIDE + ch * 16;  // 8-byte aligned
+    const uint2 lo = *reinterpret_cast<const uint2*>(src);
+    const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
+    *reinterpret_cast<uint4*>(out + (row0 + rr) * a.ldo + col) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+}
+
+// Epilogue of one tile: accumulators acc[m][f] of wave (wg, wp) -> the output
+// (router: fp32 logits + offset; gate/up: SiLU(g) * u in bf16; down: bf16).
+template <int MODE>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, floatx16_t (&acc)[4][2], int nt,
+                                              int64_t row0, int rows, int lane, int wg, int wp,
+                                              int tid, const int (&b_row)[2], bool any,
+                                              int live_m, char* lds_raw) {
+  // ---- epilogue.  The MFMAs take the B fragment as their first operand, so
+  // each 32 x 32 accumulator holds the tile transposed: lane l has output row
+  // (l & 31) and, for register r, output column 8*(r/4) + 4*(l/32) + r%4, i.e.
+  // four consecutive columns per group of four registers.
+  const int orow_l = lane & 31;
+  const int ocol_l = 4 * (lane >> 5);
+  if (MODE == kRouter) {
+    if (!any) return;
+    float* Zo = reinterpret_cast<float*>(a.out);
+    const bool vec = (a.ldo % 4) == 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if (m >= live_m) break;
+      const int rr = wg * 128 + m * 32 + orow_l;
+      if (rr >= rows) continue;
+      const int64_t orow = row0 + rr;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = nt * BN + b_row[f] + 8 * q + ocol_l;
+          float z[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            z[j] = acc[m][f][4 * q + j];
+            if (a.offset && col + j < a.b_rows) z[j] += a.offset[col + j];
+          }
+          if (vec && col + 3 < a.b_rows) {
+            *reinterpret_cast<float4*>(Zo + orow * a.ldo + col) = make_float4(z[0], z[1], z[2], z[3]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (col + j < a.b_rows) Zo[orow * a.ldo + col + j] = z[j];
+          }
+        }
+      }
+    }
+    return;
+  }
+  // bf16 outputs (H or Y) go through LDS: every wave converts its
+  // accumulators (hardware round-to-nearest-even, two values per
+  // instruction) and writes four consecutive columns per 8-byte LDS store
+  // into a row-major tile; the row stride of 2 (mod 32) words spreads the 32
+  // rows of one store over all banks.  Then the block writes whole rows with
+  // 16-byte global stores.
+  constexpr int OCOLS = (MODE == kGateUp) ? BN / 2 : BN;   // tile columns
+  constexpr int OSTRIDE = OCOLS * 2 + 8;                   // bytes per LDS row
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  auto pack2 = [](float x, float y) {
+    const bf16x2_t v = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(uint32_t, v);
+  };
+  __syncthreads();  // all fragment reads of the last stage are done
+  if (any) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if (m >= live_m) break;
+      char* lrow = lds_raw + (wg * 128 + m * 32 + orow_l) * OSTRIDE;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (MODE == kGateUp) {
+          float hv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float g = acc[m][0][4 * q + j];
+            const float u = acc[m][1][4 * q + j];
+            hv[j] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+          }
+          *reinterpret_cast<uint2*>(lrow + (wp * 32 + 8 * q + ocol_l) * 2) =
+              make_uint2(pack2(hv[0], hv[1]), pack2(hv[2], hv[3]));
+        } else {
+#pragma unroll
+          for (int f = 0; f < 2; ++f) {
+            *reinterpret_cast<uint2*>(lrow + (b_row[f] + 8 * q + ocol_l) * 2) =
+                make_uint2(pack2(acc[m][f][4 * q], acc[m][f][4 * q + 1]),
+                           pack2(acc[m][f][4 * q + 2], acc[m][f][4 * q + 3]));
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  epilogue_store<MODE>(a, nt, row0, rows, tid, lds_raw);
 }
 
 // One 256 x 256 output tile (m-tile mt, n-tile nt).  GROUPED: rows come from
@@ -358,53 +524,231 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
   else if (live_m > 2) run(std::integral_constant<int, 4>{});
   else run(std::integral_constant<int, 2>{});
 
-  // ---- epilogue.  The MFMAs take the B fragment as their first operand, so
-  // each 32 x 32 accumulator holds the tile transposed: lane l has output row
-  // (l & 31) and, for register r, output column 8*(r/4) + 4*(l/32) + r%4, i.e.
-  // four consecutive columns per group of four registers.
-  const int orow_l = lane & 31;
-  const int ocol_l = 4 * (lane >> 5);
-  if (MODE == kRouter) {
-    if (!any) return;
-    float* Zo = reinterpret_cast<float*>(a.out);
-    const bool vec = (a.ldo % 4) == 0;
+  gemm_epilogue<MODE>(a, acc, nt, row0, rows, lane, wg, wp, tid, b_row, any, live_m, lds_raw);
+}
+
+// ---------------------------------------------------------------- FP8 tiles
+// The same 256 x 256 tile engine over E4M3 operands ("Kolibri 1 im Detail",
+// FP8 section: 128 x 128 weight blocks with fp32 scales, activations in
+// 1 x 128 groups).  A stage is 128 k: 128 bytes per row, so loads, LDS ring
+// and swizzle are those of the bf16 engine, and exactly one scale block in
+// k.  One v_mfma_f32_16x16x128_f8f6f4 covers the whole stage for a 16 x 16
+// block, so its product (four values per lane, formed from zero) is added
+// into the fp32 accumulator times s_A(row, kb) * s_B(block, kb): one scaling
+// FMA per accumulator element per 128 k.  kdim is a multiple of 128.
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+template <int MODE, bool GROUPED>
+__device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int nt,
+                                              char* lds_raw) {
+  static_assert(MODE != kRouter, "the router product stays bf16");
+  int expert = 0;
+  int64_t row0;
+  int rows;
+  if (GROUPED) {
+    const int4 ent = reinterpret_cast<const int4*>(a.tiles)[mt];
+    expert = ent.x;
+    row0 = ent.y;
+    rows = ent.z;
+  } else {
+    row0 = mt * BM;
+    rows = (int)min((int64_t)BM, a.rows_dense - row0);
+  }
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wg = wave >> 2;
+  const int wp = wave & 3;
+  const int sub = lane >> 3;
+  const int chunk = (lane & 7) ^ (sub & 7);
+  constexpr uint32_t kNoRow = 0xFFFFFFFFu - 64u * 1024u;  // past any 4 GiB buffer
+  uint32_t a_voff[4], b_voff[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      if (m >= live_m) break;
-      const int rr = wg * 128 + m * 32 + orow_l;
-      if (rr >= rows) continue;
-      const int64_t orow = row0 + rr;
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * (8 * i + wave) + sub;
+    if (r < rows) {
+      int64_t arow = row0 + r;
+      if (GROUPED && a.gather) arow = a.gather[arow] / a.gather_div;
+      a_voff[i] = (uint32_t)(arow * a.lda) + (uint32_t)chunk * 16u;
+    } else {
+      a_voff[i] = kNoRow;
+    }
+    const int brow = (MODE == kGateUp) ? nt * (BN / 2) + (r & (BN / 2 - 1)) : nt * BN + r;
+    b_voff[i] = (brow < a.b_rows) ? (uint32_t)brow * (uint32_t)a.kdim + (uint32_t)chunk * 16u
+                                  : kNoRow;
+  }
+  const uint32_t b_bytes = (uint32_t)a.b_rows * (uint32_t)a.kdim;
+  const uint8_t* A8 = reinterpret_cast<const uint8_t*>(a.A);
+  const uint8_t* B08 = reinterpret_cast<const uint8_t*>(a.B0);
+  const uint8_t* B18 = reinterpret_cast<const uint8_t*>(MODE == kGateUp ? a.B1 : a.B0);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A8, a.a_bytes);
+  const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(B08 + (int64_t)expert * a.b_expert_stride, b_bytes);
+  const __amdgpu_buffer_rsrc_t rb1 = make_rsrc(B18 + (int64_t)expert * a.b_expert_stride, b_bytes);
+  const int nk = a.kdim / 128;
+  auto dma_a = [&](int ks, int i) {
+    const int j = 8 * i + wave;
+    dma16(ra, a_voff[i], (uint32_t)ks * 128u,
+          (lds_void_t*)(lds_raw + (ks % A_SLOTS) * TILE_BYTES + j * 1024));
+  };
+  auto dma_b = [&](int ks, int i) {
+    const int j = 8 * i + wave;
+    dma16((MODE == kGateUp && i >= 2) ? rb1 : rb0, b_voff[i], (uint32_t)ks * 128u,
+          (lds_void_t*)(lds_raw + B_RING + (ks % B_SLOTS) * TILE_BYTES + j * 1024));
+  };
+
+  // ---- accumulators: wave (wg, wp) owns tile rows wg*128 .. +128 as eight
+  // 16-row blocks, and four 16-column blocks of B rows: gate/up -> gate rows
+  // wp*32, wp*32+16 and the up rows of the same hidden columns; down -> B
+  // rows wp*64 + 16*f.  The MFMAs take the B fragment first, so lane l holds
+  // output row (l & 15) of a block and its four consecutive columns
+  // 4*(l >> 4) .. +3.
+  floatx4_t acc[8][4];
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = nt * BN + b_row[f] + 8 * q + ocol_l;
-          float z[4];
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  int b_col[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            z[j] = acc[m][f][4 * q + j];
-            if (a.offset && col + j < a.b_rows) z[j] += a.offset[col + j];
+  for (int f = 0; f < 4; ++f)
+    b_col[f] = (MODE == kGateUp) ? (f >> 1) * (BN / 2) + wp * 32 + (f & 1) * 16 : wp * 64 + 16 * f;
+  const int fr = lane & 15;
+  const int quad = lane >> 4;
+
+  int live_m = (rows - wg * 128 + 31) / 32;
+  live_m = live_m < 0 ? 0 : (live_m > 4 ? 4 : live_m);
+  live_m = __builtin_amdgcn_readfirstlane(live_m);
+  const bool live_n = (MODE == kGateUp) ? true : (nt * BN + wp * 64) < a.b_rows;
+  const bool any = __builtin_amdgcn_readfirstlane((live_m > 0 && live_n) ? 1 : 0) != 0;
+
+  // ---- scales.  Row block m of a lane is tile row wg*128 + 16*m + (l & 15),
+  // so the four lanes with the same l & 15 share their eight rows: lane l
+  // loads the activation scales of blocks m = 2*(l>>4) and +1 (its A rows,
+  // through the gather for the routed gate/up) and the others read them
+  // across lanes.  Gate/up column blocks take the gate (f < 2) or up
+  // (f >= 2) weight block nt; the 64 down columns of a wave lie in one
+  // 128-row weight block.  Offsets fit 32 bits: rows * kdim < 4 GiB.
+  const int nkb = nk;
+  uint32_t sa_off[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int rr = wg * 128 + (2 * quad + j) * 16 + fr;
+    int64_t arow = row0 + (rr < rows ? rr : 0);
+    if (GROUPED && a.gather) arow = a.gather[arow] / a.gather_div;
+    sa_off[j] = (uint32_t)arow * (uint32_t)nkb;
+  }
+  const int nblk = (a.b_rows + 127) / 128;
+  const int bblk = (MODE == kGateUp) ? nt : min((nt * BN + wp * 64) / 128, nblk - 1);
+  const float* sbp0 = a.sb0 + (int64_t)expert * a.sb_es + (int64_t)bblk * nkb;
+  const float* sbp1 = ((MODE == kGateUp) ? a.sb1 : a.sb0) + (int64_t)expert * a.sb_es +
+                      (int64_t)bblk * nkb;
+
+  // Schedule: the prologue loads A0 B0 A1 B1 B2.  Stage kt first loads the
+  // scales of stage kt+1, then A(kt+1) rows 2,3 and B(kt+2), and after its
+  // closing barrier (A slot kt%2 and B slot kt%3 free) A(kt+2) rows 0,1.  The
+  // scale loads are issued before the operand loads of the stage, so the
+  // closing wait for all but the last four loads covers them.  LIVE (0, 2 or
+  // 4) is the number of 32-row halves of its rows this wave multiplies.
+  auto run = [&](auto live_tag) {
+    constexpr int LIVE = decltype(live_tag)::value;
+    constexpr int MB = 2 * LIVE;  // 16-row blocks
+    constexpr int NS = (MODE == kGateUp) ? 2 : 1;
+    float sa_n[2] = {0.f, 0.f}, sb_n[2] = {0.f, 0.f};
+    auto load_scales = [&](int kt) {
+      if (MB > 0) {
+        sa_n[0] = a.sa[sa_off[0] + kt];
+        sa_n[1] = a.sa[sa_off[1] + kt];
+        sb_n[0] = sbp0[kt];
+        if (NS > 1) sb_n[1] = sbp1[kt];
+      }
+    };
+    load_scales(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma_a(0, i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma_b(0, i);
+    if (nk > 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma_a(1, i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma_b(1, i);
+    }
+    if (nk > 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma_b(2, i);
+    }
+    if (nk > 2) wait_vmcnt<12>();
+    else if (nk > 1) wait_vmcnt<8>();
+    else wait_vmcnt<0>();
+    block_barrier();
+
+    for (int kt = 0; kt < nk; ++kt) {
+      float sa_c[2], sb_c[2];
+      sa_c[0] = sa_n[0];
+      sa_c[1] = sa_n[1];
+      sb_c[0] = sb_n[0];
+      sb_c[1] = sb_n[1];
+      if (kt + 1 < nk) load_scales(kt + 1);
+      if (kt >= 1 && kt + 1 < nk) { dma_a(kt + 1, 2); dma_a(kt + 1, 3); }
+      if (kt >= 1 && kt + 2 < nk) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma_b(kt + 2, i);
+      }
+      if (MB > 0) {
+        const char* sa_lds = lds_raw + (kt % A_SLOTS) * TILE_BYTES;
+        const char* sb_lds = lds_raw + B_RING + (kt % B_SLOTS) * TILE_BYTES;
+        // lane l reads 32 bytes of its row: chunks 2*(l>>4) and +1 (swizzled;
+        // every fragment starts on a multiple of 16 rows, so row & 7 = l & 7)
+        const int s0 = ((2 * quad) ^ (lane & 7)) * 16;
+        const int s1 = ((2 * quad + 1) ^ (lane & 7)) * 16;
+        auto frag = [&](const char* rowp) {
+          const uint4 lo = *reinterpret_cast<const uint4*>(rowp + s0);
+          const uint4 hi = *reinterpret_cast<const uint4*>(rowp + s1);
+          return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        };
+        i32x8_t Bf[4], Af[2];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) Bf[f] = frag(sb_lds + (b_col[f] + fr) * ROW_BYTES);
+        const char* a_rows = sa_lds + (wg * 128 + fr) * ROW_BYTES;
+        Af[0] = frag(a_rows);
+        // block m+1's fragment is read while block m multiplies; the
+        // scheduling barriers keep the compiler from hoisting further reads
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+          __builtin_amdgcn_sched_barrier(0);
+          const float sa_m = __shfl(sa_c[m & 1], fr + 16 * (m >> 1));
+          if (m + 1 < MB) Af[(m + 1) & 1] = frag(a_rows + (m + 1) * 16 * ROW_BYTES);
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            const floatx4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                Bf[f], Af[m & 1], floatx4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+            const float fac = sa_m * sb_c[(NS > 1) ? (f >> 1) : 0];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[m][f][r] = fmaf(p[r], fac, acc[m][f][r]);
+            // keeps the compiler from sinking the FMAs below later blocks'
+            // MFMAs, which would hold every product live at once
+            asm volatile("" : "+v"(acc[m][f]));
           }
-          if (vec && col + 3 < a.b_rows) {
-            *reinterpret_cast<float4*>(Zo + orow * a.ldo + col) = make_float4(z[0], z[1], z[2], z[3]);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (col + j < a.b_rows) Zo[orow * a.ldo + col + j] = z[j];
-          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
+      if (kt + 1 < nk) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (kt >= 1 && kt + 2 < nk) wait_vmcnt<4>(); else wait_vmcnt<0>();
+        block_barrier();  // every wave done with A slot kt%2 and B slot kt%3
+        if (kt + 2 < nk) { dma_a(kt + 2, 0); dma_a(kt + 2, 1); }
+      }
     }
-    return;
-  }
-  // bf16 outputs (H or Y) go through LDS: every wave converts its
-  // accumulators (hardware round-to-nearest-even, two values per
-  // instruction) and writes four consecutive columns per 8-byte LDS store
-  // into a row-major tile; the row stride of 2 (mod 32) words spreads the 32
-  // rows of one store over all banks.  Then the block writes whole rows with
-  // 16-byte global stores.
-  constexpr int OCOLS = (MODE == kGateUp) ? BN / 2 : BN;   // tile columns
-  constexpr int OSTRIDE = OCOLS * 2 + 8;                   // bytes per LDS row
+  };
+  if (!any) run(std::integral_constant<int, 0>{});
+  else if (live_m <= 2) run(std::integral_constant<int, 2>{});
+  else run(std::integral_constant<int, 4>{});
+
+  // ---- epilogue: stage the bf16 tile in LDS (four consecutive columns per
+  // 8-byte store), then write whole rows
+  constexpr int OCOLS = (MODE == kGateUp) ? BN / 2 : BN;
+  constexpr int OSTRIDE = OCOLS * 2 + 8;
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   auto pack2 = [](float x, float y) {
     const bf16x2_t v = {(__bf16)x, (__bf16)y};
@@ -413,46 +757,45 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
   __syncthreads();  // all fragment reads of the last stage are done
   if (any) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      if (m >= live_m) break;
-      char* lrow = lds_raw + (wg * 128 + m * 32 + orow_l) * OSTRIDE;
+    for (int m = 0; m < 8; ++m) {
+      if (m >= 2 * live_m) break;
+      char* lrow = lds_raw + (wg * 128 + m * 16 + fr) * OSTRIDE;
+      if (MODE == kGateUp) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (MODE == kGateUp) {
+        for (int f = 0; f < 2; ++f) {
           float hv[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float g = acc[m][0][4 * q + j];
-            const float u = acc[m][1][4 * q + j];
+            const float g = acc[m][f][j];
+            const float u = acc[m][f + 2][j];
             hv[j] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
           }
-          *reinterpret_cast<uint2*>(lrow + (wp * 32 + 8 * q + ocol_l) * 2) =
+          *reinterpret_cast<uint2*>(lrow + (b_col[f] + 4 * quad) * 2) =
               make_uint2(pack2(hv[0], hv[1]), pack2(hv[2], hv[3]));
-        } else {
-#pragma unroll
-          for (int f = 0; f < 2; ++f) {
-            *reinterpret_cast<uint2*>(lrow + (b_row[f] + 8 * q + ocol_l) * 2) =
-                make_uint2(pack2(acc[m][f][4 * q], acc[m][f][4 * q + 1]),
-                           pack2(acc[m][f][4 * q + 2], acc[m][f][4 * q + 3]));
-          }
         }
+      } else {
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          *reinterpret_cast<uint2*>(lrow + (b_col[f] + 4 * quad) * 2) =
+              make_uint2(pack2(acc[m][f][0], acc[m][f][1]), pack2(acc[m][f][2], acc[m][f][3]));
       }
     }
   }
   __syncthreads();
-  constexpr int CPR = OCOLS / 8;  // 16-byte chunks per tile row
-  const int col0 = nt * OCOLS;
-  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-  for (int c = tid; c < BM * CPR; c += 512) {
-    const int rr = c / CPR, ch = c % CPR;
-    if (rr >= rows) break;  // chunks are walked in row order
-    const int col = col0 + ch * 8;
-    if (col >= a.b_rows) continue;
-    const char* src = lds_raw + rr * OSTRIDE + ch * 16;  // 8-byte aligned
-    const uint2 lo = *reinterpret_cast<const uint2*>(src);
-    const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
-    *reinterpret_cast<uint4*>(out + (row0 + rr) * a.ldo + col) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-  }
+  epilogue_store<MODE>(a, nt, row0, rows, tid, lds_raw);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(512, 2) void gemm_fp8_kernel(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  const bool grouped = a.tiles != nullptr;
+  const int64_t m_tiles = grouped ? (int64_t)(*a.n_tiles) : (a.rows_dense + BM - 1) / BM;
+  int64_t logical;
+  if (!xcd_tile(m_tiles * a.n_tiles_n, logical)) return;
+  if (grouped)
+    gemm_tile_fp8<MODE, true>(a, logical / a.n_tiles_n, (int)(logical % a.n_tiles_n), lds_raw);
+  else
+    gemm_tile_fp8<MODE, false>(a, logical / a.n_tiles_n, (int)(logical % a.n_tiles_n), lds_raw);
 }
 
 template <int MODE, bool GROUPED>
@@ -478,6 +821,20 @@ __global__ __launch_bounds__(512, 2) void gemm_x_kernel(GemmArgs r, GemmArgs g) 
   const int nt = (int)(logical % n_all);
   if (nt < r.n_tiles_n) gemm_tile<kRouter, false>(r, mt, nt, lds_raw);
   else gemm_tile<kGateUp, false>(g, mt, nt - r.n_tiles_n, lds_raw);
+}
+
+// As gemm_x_kernel with the shared expert's gate/up on E4M3 operands (the
+// router stays bf16).
+__global__ __launch_bounds__(512, 2) void gemm_x_fp8_kernel(GemmArgs r, GemmArgs g) {
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
+  const int64_t m_tiles = (r.rows_dense + BM - 1) / BM;
+  const int n_all = r.n_tiles_n + g.n_tiles_n;
+  int64_t logical;
+  if (!xcd_tile(m_tiles * n_all, logical)) return;
+  const int64_t mt = logical / n_all;
+  const int nt = (int)(logical % n_all);
+  if (nt < r.n_tiles_n) gemm_tile<kRouter, false>(r, mt, nt, lds_raw);
+  else gemm_tile_fp8<kGateUp, false>(g, mt, nt - r.n_tiles_n, lds_raw);
 }
 
 template <int MODE, bool GROUPED>
@@ -598,6 +955,95 @@ hipError_t launch_router_shared_gateup(const uint16_t* x, int64_t N, int d,
     configured = true;
   }
   hipLaunchKernelGGL(gemm_x_kernel, xcd_grid(work), dim3(512), LDS_BYTES, stream, r, g);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- FP8 launches
+static GemmArgs gateup_fp8_args(const uint8_t* xq, const float* xs, int64_t x_rows,
+                                const int32_t* sorted_src, int K, const int32_t* tiles,
+                                const int32_t* n_tiles, int64_t rows_dense, const uint8_t* wg,
+                                const float* sg, const uint8_t* wu, const float* su, int d, int h,
+                                uint8_t* Hq, float* Hs) {
+  GemmArgs a{};
+  a.A = reinterpret_cast<const uint16_t*>(xq); a.lda = d;
+  a.gather = tiles ? sorted_src : nullptr; a.gather_div = K;
+  a.tiles = tiles; a.n_tiles = n_tiles; a.rows_dense = rows_dense;
+  a.B0 = reinterpret_cast<const uint16_t*>(wg); a.B1 = reinterpret_cast<const uint16_t*>(wu);
+  a.b_expert_stride = (int64_t)h * d; a.b_rows = h; a.kdim = d;
+  a.n_tiles_n = h / (BN / 2); a.out = Hq; a.ldo = h; a.offset = nullptr;
+  a.a_bytes = (uint32_t)(x_rows * d);
+  a.sa = xs; a.sb0 = sg; a.sb1 = su; a.sb_es = (int64_t)(h / 128) * (d / 128);
+  a.out_scale = Hs;
+  return a;
+}
+
+static hipError_t launch_fp8(int mode, const GemmArgs& a, int64_t max_m_tiles,
+                             hipStream_t stream) {
+  const int64_t work = max_m_tiles * a.n_tiles_n;
+  if (work <= 0) return hipSuccess;
+  if (work > 0x7FFFFFF0LL) return hipErrorInvalidConfiguration;
+  const void* fn = mode == kGateUp ? (const void*)gemm_fp8_kernel<kGateUp>
+                                   : (const void*)gemm_fp8_kernel<kDown>;
+  static bool configured[2] = {false, false};
+  if (!configured[mode]) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (e != hipSuccess) return e;
+    configured[mode] = true;
+  }
+  if (mode == kGateUp)
+    hipLaunchKernelGGL(gemm_fp8_kernel<kGateUp>, xcd_grid(work), dim3(512), LDS_BYTES, stream, a);
+  else
+    hipLaunchKernelGGL(gemm_fp8_kernel<kDown>, xcd_grid(work), dim3(512), LDS_BYTES, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup_fp8(const uint8_t* xq, const float* xs, int64_t x_rows,
+                             const int32_t* sorted_src, int K, const int32_t* tiles,
+                             const int32_t* n_tiles, int64_t max_tiles, int64_t rows_dense,
+                             const uint8_t* wg, const float* sg, const uint8_t* wu,
+                             const float* su, int d, int h, uint8_t* Hq, float* Hs,
+                             hipStream_t stream) {
+  const GemmArgs a = gateup_fp8_args(xq, xs, x_rows, sorted_src, K, tiles, n_tiles, rows_dense,
+                                     wg, sg, wu, su, d, h, Hq, Hs);
+  return launch_fp8(kGateUp, a, tiles ? max_tiles : (rows_dense + BM - 1) / BM, stream);
+}
+
+hipError_t launch_down_fp8(const uint8_t* Hq, const float* Hs, int64_t h_rows,
+                           const int32_t* tiles, const int32_t* n_tiles, int64_t max_tiles,
+                           int64_t rows_dense, const uint8_t* wd, const float* sd, int d, int h,
+                           uint16_t* Y, hipStream_t stream) {
+  GemmArgs a{};
+  a.A = reinterpret_cast<const uint16_t*>(Hq); a.lda = h; a.gather = nullptr; a.gather_div = 1;
+  a.tiles = tiles; a.n_tiles = n_tiles; a.rows_dense = rows_dense;
+  a.B0 = reinterpret_cast<const uint16_t*>(wd); a.B1 = nullptr;
+  a.b_expert_stride = (int64_t)d * h; a.b_rows = d; a.kdim = h;
+  a.n_tiles_n = (d + BN - 1) / BN; a.out = Y; a.ldo = d; a.offset = nullptr;
+  a.a_bytes = (uint32_t)(h_rows * h);
+  a.sa = Hs; a.sb0 = sd; a.sb1 = sd; a.sb_es = (int64_t)(d / 128) * (h / 128);
+  a.out_scale = nullptr;
+  return launch_fp8(kDown, a, tiles ? max_tiles : (rows_dense + BM - 1) / BM, stream);
+}
+
+hipError_t launch_router_shared_gateup_fp8(const uint16_t* x, const uint8_t* xq, const float* xs,
+                                           int64_t N, int d, const uint16_t* w_router,
+                                           const float* offset, int E, float* Z,
+                                           const uint8_t* wsg, const float* ssg,
+                                           const uint8_t* wsu, const float* ssu, int hs,
+                                           uint8_t* Hsq, float* Hss, hipStream_t stream) {
+  const GemmArgs r = router_args(x, w_router, offset, N, d, E, Z);
+  const GemmArgs g = gateup_fp8_args(xq, xs, N, nullptr, 1, nullptr, nullptr, N, wsg, ssg, wsu,
+                                     ssu, d, hs, Hsq, Hss);
+  const int64_t work = ((N + BM - 1) / BM) * (r.n_tiles_n + g.n_tiles_n);
+  if (work <= 0) return hipSuccess;
+  if (work > 0x7FFFFFF0LL) return hipErrorInvalidConfiguration;
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_x_fp8_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  hipLaunchKernelGGL(gemm_x_fp8_kernel, xcd_grid(work), dim3(512), LDS_BYTES, stream, r, g);
   return hipGetLastError();
 }
 

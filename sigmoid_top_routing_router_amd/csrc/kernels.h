@@ -124,6 +124,37 @@ hipError_t launch_lei(const float* Z, const int32_t* ids, const float* G, int64_
                       int K, float lam, float tau, float* Gout, float* dZ, float* inj_out,
                       int32_t* counts, float* inj, hipStream_t stream);
 
+// ---------------------------------------------------------------- FP8
+// Rows of X [N,C] bf16 (C % 128 == 0) -> E4M3 codes Q [N,C] and one fp32
+// scale per 1 x 128 group, S [N, C/128].
+hipError_t launch_quant_rows(const uint16_t* X, int64_t N, int C, uint8_t* Q, float* S,
+                             hipStream_t stream);
+// `count` matrices W [count][R][C] bf16 -> codes Q [count][R][C] and one fp32
+// scale per 128 x 128 block, S [count][ceil(R/128)][ceil(C/128)].
+hipError_t launch_quant_blocks(const uint16_t* W, int64_t count, int R, int C, uint8_t* Q,
+                               float* S, hipStream_t stream);
+
+// E4M3 GEMMs (d % 128 == 0, h % 128 == 0).  Weight scales are
+// [E][rows/128][cols/128]; activation scales [rows][cols/128].  The gate/up
+// GEMMs leave H as E4M3 codes [rows][h] with scales [rows][h/128] (quantised
+// in the epilogue from the bf16-rounded SiLU(g) * u).
+hipError_t launch_gateup_fp8(const uint8_t* xq, const float* xs, int64_t x_rows,
+                             const int32_t* sorted_src, int K, const int32_t* tiles,
+                             const int32_t* n_tiles, int64_t max_tiles, int64_t rows_dense,
+                             const uint8_t* wg, const float* sg, const uint8_t* wu,
+                             const float* su, int d, int h, uint8_t* Hq, float* Hs,
+                             hipStream_t stream);
+hipError_t launch_down_fp8(const uint8_t* Hq, const float* Hs, int64_t h_rows,
+                           const int32_t* tiles, const int32_t* n_tiles, int64_t max_tiles,
+                           int64_t rows_dense, const uint8_t* wd, const float* sd, int d, int h,
+                           uint16_t* Y, hipStream_t stream);
+hipError_t launch_router_shared_gateup_fp8(const uint16_t* x, const uint8_t* xq, const float* xs,
+                                           int64_t N, int d, const uint16_t* w_router,
+                                           const float* offset, int E, float* Z,
+                                           const uint8_t* wsg, const float* ssg,
+                                           const uint8_t* wsu, const float* ssu, int hs,
+                                           uint8_t* Hsq, float* Hss, hipStream_t stream);
+
 // ---------------------------------------------------------------- misc
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t stream);
 

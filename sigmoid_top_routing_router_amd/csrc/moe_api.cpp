@@ -102,11 +102,18 @@ struct FwdLayout {
   uint16_t* Hs;
   uint16_t* Y;
   uint16_t* sh;
+  // FP8 experts: x, H and the shared H as E4M3 codes with 1 x 128 scales
+  uint8_t* xq;
+  float* xs;
+  uint8_t* Hq;
+  float* Hqs;
+  uint8_t* Hsq;
+  float* Hss;
   size_t bytes;
   int64_t max_tiles;
 };
 
-FwdLayout carve_forward(void* ws, const moe_problem_t& p) {
+FwdLayout carve_forward(void* ws, const moe_problem_t& p, bool fp8 = false) {
   Carver c(ws);
   FwdLayout l{};
   const int64_t N = p.N, pairs = p.N * (int64_t)p.K;
@@ -128,10 +135,22 @@ FwdLayout carve_forward(void* ws, const moe_problem_t& p) {
   l.max_tiles = moe::perm_max_tiles(pairs, p.E, moe::gemm_bm());
   l.tiles = c.take<int32_t>((size_t)l.max_tiles * 4);
   l.n_tiles = c.take<int32_t>(4);
-  l.H = c.take<uint16_t>((size_t)pairs * p.h);
+  if (fp8) {
+    l.xq = c.take<uint8_t>((size_t)N * p.d);
+    l.xs = c.take<float>((size_t)N * (p.d / 128));
+    l.Hq = c.take<uint8_t>((size_t)pairs * p.h);
+    l.Hqs = c.take<float>((size_t)pairs * (p.h / 128));
+  } else {
+    l.H = c.take<uint16_t>((size_t)pairs * p.h);
+  }
   l.Y = c.take<uint16_t>((size_t)pairs * p.d);
   if (p.n_shared > 0) {
-    l.Hs = c.take<uint16_t>((size_t)N * p.h_shared);
+    if (fp8) {
+      l.Hsq = c.take<uint8_t>((size_t)N * p.h_shared);
+      l.Hss = c.take<float>((size_t)N * (p.h_shared / 128));
+    } else {
+      l.Hs = c.take<uint16_t>((size_t)N * p.h_shared);
+    }
     l.sh = c.take<uint16_t>((size_t)N * p.d);
   }
   l.bytes = c.off;
@@ -167,6 +186,26 @@ moe_status_t check_problem(const moe_problem_t* p) {
   if (p->logit_offset && !aligned(p->logit_offset, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "logit_offset misaligned");
   return MOE_OK;
 }
+
+// The FP8 path quantises in 1 x 128 groups and multiplies 128 x 128 blocks.
+moe_status_t check_problem_fp8(const moe_problem_t* p) {
+  moe_status_t s = check_problem(p);
+  if (s != MOE_OK) return s;
+  if (p->d % 128 || p->h % 128 || (p->n_shared == 1 && p->h_shared % 128))
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE,
+                "FP8 experts need d, h and h_shared to be multiples of 128 (d=%d h=%d hs=%d)",
+                p->d, p->h, p->h_shared);
+  return MOE_OK;
+}
+
+// Expert weights of one forward call: bf16 (moe_weights_t) or E4M3 codes
+// with block scales (moe_fp8_weights_t).
+struct Experts {
+  bool fp8 = false;
+  const uint16_t* w_router = nullptr;
+  const moe_weights_t* b = nullptr;
+  const moe_fp8_weights_t* q = nullptr;
+};
 
 // ---- stage timing: S+1 boundary events per recorded call
 constexpr int kGateUpStage = 3;  // the routed gate/up GEMM
@@ -224,6 +263,153 @@ struct CallTimer {
   } while (0)
 
 }  // namespace
+
+// The layer for either expert precision.  Shape and weight checks are the
+// callers'; everything else is common.
+static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, const uint16_t* x,
+                                 const float* beta_in, uint16_t* y, moe_aux_t* aux,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!p->logits_in && !ex.w_router)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "w_router is required when logits_in is NULL");
+  if (!aligned(x, 16) || !aligned(y, 16))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "x and y must be 16-byte aligned");
+  if (beta_in && !aligned(beta_in, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "beta_in misaligned");
+  moe_aux_t none{};
+  const moe_aux_t& A = aux ? *aux : none;
+  const void* pa[] = {A.logits, A.topk_ids, A.topk_weights, A.alpha, A.margin, A.beta_out,
+                      A.quantile_out, A.counts_before, A.counts, A.offsets, A.sorted_src,
+                      A.src_pos};
+  for (const void* q : pa)
+    if (q && !aligned(q, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "aux buffers must be 4-byte aligned");
+  const FwdLayout need = carve_forward(nullptr, *p, ex.fp8);
+  if (!workspace || !aligned(workspace, kAlign))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+  if (workspace_bytes < need.bytes)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < required %zu", workspace_bytes, need.bytes);
+
+  FwdLayout l = carve_forward(workspace, *p, ex.fp8);
+  const moe_weights_t* w = ex.b;
+  const moe_fp8_weights_t* q = ex.q;
+  const hipStream_t st = (hipStream_t)stream;
+  const int64_t N = p->N;
+  const int E = p->E, K = p->K, d = p->d, h = p->h;
+  const int key_bits = (p->flags & MOE_KEY32) ? 32 : 16;
+  const bool recompute = (p->flags & MOE_RECOMPUTE_BIAS) != 0;
+
+  CallTimer tm;
+  MOE_TRY_HIP(tm.start(st), "moe_forward: stage timer");
+
+  // Router logits and the shared expert's gate/up: both read x, so they
+  // share one launch.  FP8 experts first quantise x per 1 x 128 group; the
+  // router reads the bf16 x.
+  const float* Z;
+  const bool shared = p->n_shared == 1;
+  const int hs = p->h_shared;
+  if (ex.fp8)
+    MOE_TRY_HIP(moe::launch_quant_rows(x, N, d, l.xq, l.xs, st), "moe_forward: quantise x");
+  if (p->logits_in) {
+    Z = p->logits_in;
+    if (A.logits)
+      MOE_TRY_HIP(hipMemcpyAsync(A.logits, Z, (size_t)N * E * 4, hipMemcpyDeviceToDevice, st),
+                  "moe_forward: logits copy");
+    if (shared && ex.fp8)
+      MOE_TRY_HIP(moe::launch_gateup_fp8(l.xq, l.xs, N, nullptr, 1, nullptr, nullptr, 0, N,
+                                         q->ws_gate, q->ss_gate, q->ws_up, q->ss_up, d, hs,
+                                         l.Hsq, l.Hss, st),
+                  "moe_forward: shared gate/up");
+    else if (shared)
+      MOE_TRY_HIP(moe::launch_gateup(x, N, nullptr, 1, nullptr, nullptr, 0, N, w->ws_gate,
+                                     w->ws_up, d, hs, l.Hs, st),
+                  "moe_forward: shared gate/up");
+  } else {
+    float* zout = A.logits ? A.logits : l.Z;
+    if (shared && ex.fp8)
+      MOE_TRY_HIP(moe::launch_router_shared_gateup_fp8(x, l.xq, l.xs, N, d, ex.w_router,
+                                                       p->logit_offset, E, zout, q->ws_gate,
+                                                       q->ss_gate, q->ws_up, q->ss_up, hs,
+                                                       l.Hsq, l.Hss, st),
+                  "moe_forward: router GEMM + shared gate/up");
+    else if (shared)
+      MOE_TRY_HIP(moe::launch_router_shared_gateup(x, N, d, ex.w_router, p->logit_offset, E,
+                                                   zout, w->ws_gate, w->ws_up, hs, l.Hs, st),
+                  "moe_forward: router GEMM + shared gate/up");
+    else
+      MOE_TRY_HIP(moe::launch_router_gemm(x, ex.w_router, p->logit_offset, N, d, E, zout, st),
+                  "moe_forward: router GEMM");
+    Z = zout;
+  }
+  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
+
+  // selection, token bias, optional exact quantile update, re-route
+  int32_t* ids = A.topk_ids ? A.topk_ids : l.ids;
+  float* S = A.topk_weights ? A.topk_weights : l.S;
+  float* alpha = A.alpha ? A.alpha : l.alpha;
+  float* margin = A.margin ? A.margin : l.margin;
+  if (recompute) {
+    // first pass: alpha only, unless the loads before the update are wanted
+    MOE_TRY_HIP(moe::launch_route(Z, beta_in, N, E, K, A.counts_before ? l.ids0 : nullptr,
+                                  nullptr, alpha, nullptr, st),
+                "moe_forward: first routing");
+    if (A.counts_before)
+      MOE_TRY_HIP(moe::launch_count(l.ids0, N * K, E, A.counts_before, st), "moe_forward: loads");
+    float* beta_new = A.beta_out ? A.beta_out : l.beta_new;
+    moe::EqbWork ew{l.eqb.hist, l.eqb.state, l.eqb.qraw};
+    MOE_TRY_HIP(moe::launch_eqb(Z, alpha, N, E, K, key_bits, beta_new, A.quantile_out, ew, st),
+                "moe_forward: quantile update");
+    MOE_TRY_HIP(moe::launch_route(Z, beta_new, N, E, K, ids, S, nullptr, margin, st),
+                "moe_forward: routing");
+  } else {
+    MOE_TRY_HIP(moe::launch_route(Z, beta_in, N, E, K, ids, S, alpha, margin, st),
+                "moe_forward: routing");
+    if (A.counts_before)
+      MOE_TRY_HIP(moe::launch_count(ids, N * K, E, A.counts_before, st), "moe_forward: loads");
+  }
+
+  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
+
+  // stable grouping by expert and the m-tile table
+  moe::PermWork pw;
+  pw.chunk_counts = l.chunk_counts;
+  pw.counts = A.counts ? A.counts : l.counts;
+  pw.offsets = A.offsets ? A.offsets : l.offsets;
+  pw.sorted_src = A.sorted_src ? A.sorted_src : l.sorted_src;
+  pw.src_pos = A.src_pos ? A.src_pos : l.src_pos;
+  pw.tiles = l.tiles;
+  pw.n_tiles = l.n_tiles;
+  MOE_TRY_HIP(moe::launch_permute(ids, N, E, K, moe::gemm_bm(), pw, st), "moe_forward: grouping");
+  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
+
+  // routed experts (the gather is fused into the gate/up A loads)
+  if (ex.fp8)
+    MOE_TRY_HIP(moe::launch_gateup_fp8(l.xq, l.xs, N, pw.sorted_src, K, pw.tiles, pw.n_tiles,
+                                       l.max_tiles, 0, q->w_gate, q->s_gate, q->w_up, q->s_up,
+                                       d, h, l.Hq, l.Hqs, st), "moe_forward: gate/up");
+  else
+    MOE_TRY_HIP(moe::launch_gateup(x, N, pw.sorted_src, K, pw.tiles, pw.n_tiles, l.max_tiles, 0,
+                                   w->w_gate, w->w_up, d, h, l.H, st), "moe_forward: gate/up");
+  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
+  if (ex.fp8)
+    MOE_TRY_HIP(moe::launch_down_fp8(l.Hq, l.Hqs, N * K, pw.tiles, pw.n_tiles, l.max_tiles, 0,
+                                     q->w_down, q->s_down, d, h, l.Y, st), "moe_forward: down");
+  else
+    MOE_TRY_HIP(moe::launch_down(l.H, N * K, pw.tiles, pw.n_tiles, l.max_tiles, 0, w->w_down, d,
+                                 h, l.Y, st), "moe_forward: down");
+  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
+  // the shared expert's down projection
+  if (shared && ex.fp8)
+    MOE_TRY_HIP(moe::launch_down_fp8(l.Hsq, l.Hss, N, nullptr, nullptr, 0, N, q->ws_down,
+                                     q->ss_down, d, hs, l.sh, st), "moe_forward: shared down");
+  else if (shared)
+    MOE_TRY_HIP(moe::launch_down(l.Hs, N, nullptr, nullptr, 0, N, w->ws_down, d, hs, l.sh, st),
+                "moe_forward: shared down");
+  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
+  // weighted combine
+  MOE_TRY_HIP(moe::launch_combine(shared ? l.sh : nullptr, l.Y, S, pw.src_pos, N, K, d, y, st),
+              "moe_forward: combine");
+  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
+  return ok();
+}
+
 
 extern "C" {
 
@@ -492,128 +678,81 @@ size_t moe_forward_workspace_bytes(const moe_problem_t* p) {
   return carve_forward(nullptr, *p).bytes;
 }
 
+size_t moe_forward_fp8_workspace_bytes(const moe_problem_t* p) {
+  if (check_problem_fp8(p) != MOE_OK) return 0;
+  return carve_forward(nullptr, *p, true).bytes;
+}
+
 moe_status_t moe_forward(const moe_problem_t* p, const moe_weights_t* w, const uint16_t* x,
                          const float* beta_in, uint16_t* y, moe_aux_t* aux, void* workspace,
                          size_t workspace_bytes, void* stream) {
   moe_status_t s = check_problem(p);
   if (s != MOE_OK) return s;
   if (!w || !x || !y) return fail(MOE_ERR_INVALID_ARGUMENT, "weights, x and y are required");
-  if (!p->logits_in && !w->w_router)
-    return fail(MOE_ERR_INVALID_ARGUMENT, "w_router is required when logits_in is NULL");
   if (!w->w_gate || !w->w_up || !w->w_down)
     return fail(MOE_ERR_INVALID_ARGUMENT, "routed expert weights are required");
   if (p->n_shared == 1 && (!w->ws_gate || !w->ws_up || !w->ws_down))
     return fail(MOE_ERR_INVALID_ARGUMENT, "shared expert weights are required");
-  const void* p16[] = {x, y, w->w_router, w->w_gate, w->w_up, w->w_down,
-                       w->ws_gate, w->ws_up, w->ws_down};
+  const void* p16[] = {w->w_router, w->w_gate, w->w_up, w->w_down, w->ws_gate, w->ws_up, w->ws_down};
   for (const void* q : p16)
     if (q && !aligned(q, 16)) return fail(MOE_ERR_INVALID_ARGUMENT, "bf16 buffers must be 16-byte aligned");
-  if (beta_in && !aligned(beta_in, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "beta_in misaligned");
-  moe_aux_t none{};
-  const moe_aux_t& A = aux ? *aux : none;
-  const void* pa[] = {A.logits, A.topk_ids, A.topk_weights, A.alpha, A.margin, A.beta_out,
-                      A.quantile_out, A.counts_before, A.counts, A.offsets, A.sorted_src,
-                      A.src_pos};
-  for (const void* q : pa)
-    if (q && !aligned(q, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "aux buffers must be 4-byte aligned");
-  const FwdLayout need = carve_forward(nullptr, *p);
-  if (!workspace || !aligned(workspace, kAlign))
-    return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
-  if (workspace_bytes < need.bytes)
-    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < required %zu", workspace_bytes, need.bytes);
+  Experts ex;
+  ex.w_router = w->w_router;
+  ex.b = w;
+  return forward_impl(p, ex, x, beta_in, y, aux, workspace, workspace_bytes, stream);
+}
 
-  FwdLayout l = carve_forward(workspace, *p);
-  const hipStream_t st = (hipStream_t)stream;
-  const int64_t N = p->N;
-  const int E = p->E, K = p->K, d = p->d, h = p->h;
-  const int key_bits = (p->flags & MOE_KEY32) ? 32 : 16;
-  const bool recompute = (p->flags & MOE_RECOMPUTE_BIAS) != 0;
+moe_status_t moe_forward_fp8(const moe_problem_t* p, const moe_fp8_weights_t* w,
+                             const uint16_t* x, const float* beta_in, uint16_t* y,
+                             moe_aux_t* aux, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  moe_status_t s = check_problem_fp8(p);
+  if (s != MOE_OK) return s;
+  if (!w || !x || !y) return fail(MOE_ERR_INVALID_ARGUMENT, "weights, x and y are required");
+  if (!w->w_gate || !w->w_up || !w->w_down || !w->s_gate || !w->s_up || !w->s_down)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "routed expert codes and scales are required");
+  if (p->n_shared == 1 && (!w->ws_gate || !w->ws_up || !w->ws_down || !w->ss_gate ||
+                           !w->ss_up || !w->ss_down))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "shared expert codes and scales are required");
+  const void* p16[] = {w->w_router, w->w_gate, w->w_up, w->w_down, w->ws_gate, w->ws_up, w->ws_down};
+  for (const void* q : p16)
+    if (q && !aligned(q, 16)) return fail(MOE_ERR_INVALID_ARGUMENT, "weight buffers must be 16-byte aligned");
+  const void* p4[] = {w->s_gate, w->s_up, w->s_down, w->ss_gate, w->ss_up, w->ss_down};
+  for (const void* q : p4)
+    if (q && !aligned(q, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "scale buffers must be 4-byte aligned");
+  Experts ex;
+  ex.fp8 = true;
+  ex.w_router = w->w_router;
+  ex.q = w;
+  return forward_impl(p, ex, x, beta_in, y, aux, workspace, workspace_bytes, stream);
+}
 
-  CallTimer tm;
-  MOE_TRY_HIP(tm.start(st), "moe_forward: stage timer");
+moe_status_t moe_fp8_quantize_blocks(const uint16_t* w, int64_t count, int32_t rows,
+                                     int32_t cols, uint8_t* codes, float* scales, void* stream) {
+  if (count < 0 || count > 65535 || rows < 1 || rows > 65536 || cols < 1 || cols > 65536)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE,
+                "count=%lld rows=%d cols=%d: need 0 <= count <= 65535, 1 <= rows, cols <= 65536",
+                (long long)count, rows, cols);
+  if (count == 0) return ok();
+  if (!w || !codes || !scales) return fail(MOE_ERR_INVALID_ARGUMENT, "w, codes and scales are required");
+  if (!aligned(w, 2) || !aligned(scales, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "misaligned buffer");
+  MOE_TRY_HIP(moe::launch_quant_blocks(w, count, rows, cols, codes, scales, (hipStream_t)stream),
+              "moe_fp8_quantize_blocks");
+  return ok();
+}
 
-  // a1 router logits and a9 (first half) the shared expert's gate/up: both
-  // read x, so they share one launch
-  const float* Z;
-  const bool shared = p->n_shared == 1;
-  if (p->logits_in) {
-    Z = p->logits_in;
-    if (A.logits)
-      MOE_TRY_HIP(hipMemcpyAsync(A.logits, Z, (size_t)N * E * 4, hipMemcpyDeviceToDevice, st),
-                  "moe_forward: logits copy");
-    if (shared)
-      MOE_TRY_HIP(moe::launch_gateup(x, N, nullptr, 1, nullptr, nullptr, 0, N, w->ws_gate,
-                                     w->ws_up, d, p->h_shared, l.Hs, st),
-                  "moe_forward: shared gate/up");
-  } else {
-    float* zout = A.logits ? A.logits : l.Z;
-    if (shared)
-      MOE_TRY_HIP(moe::launch_router_shared_gateup(x, N, d, w->w_router, p->logit_offset, E,
-                                                   zout, w->ws_gate, w->ws_up, p->h_shared,
-                                                   l.Hs, st),
-                  "moe_forward: router GEMM + shared gate/up");
-    else
-      MOE_TRY_HIP(moe::launch_router_gemm(x, w->w_router, p->logit_offset, N, d, E, zout, st),
-                  "moe_forward: router GEMM");
-    Z = zout;
-  }
-  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
-
-  // a2-a4: selection, token bias, optional exact quantile update, re-route
-  int32_t* ids = A.topk_ids ? A.topk_ids : l.ids;
-  float* S = A.topk_weights ? A.topk_weights : l.S;
-  float* alpha = A.alpha ? A.alpha : l.alpha;
-  float* margin = A.margin ? A.margin : l.margin;
-  if (recompute) {
-    // first pass: alpha only, unless the loads before the update are wanted
-    MOE_TRY_HIP(moe::launch_route(Z, beta_in, N, E, K, A.counts_before ? l.ids0 : nullptr,
-                                  nullptr, alpha, nullptr, st),
-                "moe_forward: first routing");
-    if (A.counts_before)
-      MOE_TRY_HIP(moe::launch_count(l.ids0, N * K, E, A.counts_before, st), "moe_forward: loads");
-    float* beta_new = A.beta_out ? A.beta_out : l.beta_new;
-    moe::EqbWork ew{l.eqb.hist, l.eqb.state, l.eqb.qraw};
-    MOE_TRY_HIP(moe::launch_eqb(Z, alpha, N, E, K, key_bits, beta_new, A.quantile_out, ew, st),
-                "moe_forward: quantile update");
-    MOE_TRY_HIP(moe::launch_route(Z, beta_new, N, E, K, ids, S, nullptr, margin, st),
-                "moe_forward: routing");
-  } else {
-    MOE_TRY_HIP(moe::launch_route(Z, beta_in, N, E, K, ids, S, alpha, margin, st),
-                "moe_forward: routing");
-    if (A.counts_before)
-      MOE_TRY_HIP(moe::launch_count(ids, N * K, E, A.counts_before, st), "moe_forward: loads");
-  }
-
-  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
-
-  // a5: stable grouping by expert and the m-tile table
-  moe::PermWork pw;
-  pw.chunk_counts = l.chunk_counts;
-  pw.counts = A.counts ? A.counts : l.counts;
-  pw.offsets = A.offsets ? A.offsets : l.offsets;
-  pw.sorted_src = A.sorted_src ? A.sorted_src : l.sorted_src;
-  pw.src_pos = A.src_pos ? A.src_pos : l.src_pos;
-  pw.tiles = l.tiles;
-  pw.n_tiles = l.n_tiles;
-  MOE_TRY_HIP(moe::launch_permute(ids, N, E, K, moe::gemm_bm(), pw, st), "moe_forward: grouping");
-  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
-
-  // a6-a8: routed experts (gather fused into the gate/up A loads)
-  MOE_TRY_HIP(moe::launch_gateup(x, N, pw.sorted_src, K, pw.tiles, pw.n_tiles, l.max_tiles, 0,
-                                 w->w_gate, w->w_up, d, h, l.H, st), "moe_forward: gate/up");
-  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
-  MOE_TRY_HIP(moe::launch_down(l.H, N * K, pw.tiles, pw.n_tiles, l.max_tiles, 0, w->w_down, d, h, l.Y, st),
-              "moe_forward: down");
-  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
-  // a9 (second half): the shared expert's down projection
-  if (shared)
-    MOE_TRY_HIP(moe::launch_down(l.Hs, N, nullptr, nullptr, 0, N, w->ws_down, d, p->h_shared,
-                                 l.sh, st), "moe_forward: shared down");
-  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
-  // a10: weighted combine
-  MOE_TRY_HIP(moe::launch_combine(shared ? l.sh : nullptr, l.Y, S, pw.src_pos, N, K, d, y, st),
-              "moe_forward: combine");
-  MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
+moe_status_t moe_fp8_quantize_rows(const uint16_t* x, int64_t n, int32_t cols, uint8_t* codes,
+                                   float* scales, void* stream) {
+  if (n < 0 || n > (int64_t(1) << 27) || cols < 128 || cols > 65536 || cols % 128)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE,
+                "n=%lld cols=%d: need 0 <= n <= 2^27 and cols a multiple of 128 in [128, 65536]",
+                (long long)n, cols);
+  if (n == 0) return ok();
+  if (!x || !codes || !scales) return fail(MOE_ERR_INVALID_ARGUMENT, "x, codes and scales are required");
+  if (!aligned(x, 4) || !aligned(codes, 2) || !aligned(scales, 4))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "misaligned buffer");
+  MOE_TRY_HIP(moe::launch_quant_rows(x, n, cols, codes, scales, (hipStream_t)stream),
+              "moe_fp8_quantize_rows");
   return ok();
 }
 

@@ -18,6 +18,13 @@ Recipe
   products with the std are taken in float32, then rounded to bfloat16 with
   round-to-nearest-even (torch's CPU conversion) and stored as raw uint16
   bits.  The toy workload keeps float32 values as well.
+* FP8 experts (``make_fp8_experts``): a synthetic E4M3 checkpoint drawn
+  from ``SeedSequence([cfg.seed, 8])`` spawned into 6 streams [gate, up, down,
+  shared gate, shared up, shared down], one child per expert.  Each code has a
+  uniform sign, an exponent field in 9..15 with probabilities
+  (.05 .10 .15 .25 .25 .15 .05) and a uniform 3-bit mantissa (magnitudes 4 to
+  448, the NaN pattern replaced by 448); each 128 x 128 block scale is
+  float32(w_std / 100 * exp(0.3 z)), z standard normal.
 * Logit offsets (an input knob, added to the logits before the bias):
   "toy_collapse" adds +3 to experts 0 and 1 so that routing collapses onto
   them as in the running example; "zipf1.2" adds float32(0.5*ln p_e) with
@@ -93,6 +100,46 @@ def _expert_tensor(ss: np.random.SeedSequence, E: int, rows: int, cols: int,
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(fill, range(E)))
     return out, f32
+
+
+_FP8_EXP_FIELDS = np.arange(9, 16)
+_FP8_EXP_P = np.array([0.05, 0.10, 0.15, 0.25, 0.25, 0.15, 0.05])
+
+
+def _fp8_tensor(ss: np.random.SeedSequence, E: int, rows: int, cols: int, std: float):
+    codes = np.empty((E, rows, cols), dtype=np.uint8)
+    scales = np.empty((E, -(-rows // 128), -(-cols // 128)), dtype=np.float32)
+    kids = ss.spawn(E)
+
+    def fill(e):
+        g = np.random.Generator(np.random.PCG64(kids[e]))
+        sign = g.integers(0, 2, (rows, cols), dtype=np.uint8)
+        ef = g.choice(_FP8_EXP_FIELDS, size=(rows, cols), p=_FP8_EXP_P).astype(np.uint8)
+        man = g.integers(0, 8, (rows, cols), dtype=np.uint8)
+        man[(ef == 15) & (man == 7)] = 6
+        codes[e] = (sign << 7) | (ef << 3) | man
+        scales[e] = (std / 100.0 * np.exp(0.3 * g.standard_normal(scales.shape[1:]))).astype(
+            np.float32)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, range(E)))
+    return codes, scales
+
+
+def make_fp8_experts(cfg: LayerConfig) -> dict:
+    """Synthetic E4M3 expert weights of cfg's shapes: codes and 128 x 128
+    block scales under the names w_gate/s_gate, w_up/s_up, w_down/s_down,
+    ws_gate/ss_gate, ws_up/ss_up, ws_down/ss_down."""
+    st = np.random.SeedSequence([cfg.seed, 8]).spawn(6)
+    out = {}
+    shapes = [("w_gate", "s_gate", cfg.E, cfg.h, cfg.d), ("w_up", "s_up", cfg.E, cfg.h, cfg.d),
+              ("w_down", "s_down", cfg.E, cfg.d, cfg.h),
+              ("ws_gate", "ss_gate", cfg.n_shared, cfg.h_shared, cfg.d),
+              ("ws_up", "ss_up", cfg.n_shared, cfg.h_shared, cfg.d),
+              ("ws_down", "ss_down", cfg.n_shared, cfg.d, cfg.h_shared)]
+    for ss, (cn, sn, E, r, c) in zip(st, shapes):
+        out[cn], out[sn] = _fp8_tensor(ss, E, r, c, cfg.w_std)
+    return out
 
 
 def logit_offset_for(cfg: LayerConfig) -> Optional[np.ndarray]:

@@ -44,14 +44,14 @@ def test_struct_layouts_match_header(tmp_path):
     """ctypes mirrors of the header's structs agree with the C compiler."""
     import shutil
     import subprocess
-    from sigmoid_top_routing_router_amd._lib import MoeAux, MoeProblem, MoeWeights
+    from sigmoid_top_routing_router_amd._lib import MoeAux, MoeFp8Weights, MoeProblem, MoeWeights
     cc = shutil.which("gcc") or shutil.which("cc")
     if cc is None:
         pytest.skip("no C compiler")
     prog = tmp_path / "layout.c"
     lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', 'int main(void){']
     for st, cls in (("moe_problem_t", MoeProblem), ("moe_weights_t", MoeWeights),
-                    ("moe_aux_t", MoeAux)):
+                    ("moe_aux_t", MoeAux), ("moe_fp8_weights_t", MoeFp8Weights)):
         lines.append(f'printf("{st} %zu\\n", sizeof({st}));')
         for f, _ in cls._fields_:
             lines.append(f'printf("{st}.{f} %zu\\n", offsetof({st}, {f}));')
@@ -62,7 +62,7 @@ def test_struct_layouts_match_header(tmp_path):
     got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
                                                   check=True).stdout.splitlines())
     for st, cls in (("moe_problem_t", MoeProblem), ("moe_weights_t", MoeWeights),
-                    ("moe_aux_t", MoeAux)):
+                    ("moe_aux_t", MoeAux), ("moe_fp8_weights_t", MoeFp8Weights)):
         assert int(got[st]) == C.sizeof(cls), st
         for f, _ in cls._fields_:
             assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, (st, f)
@@ -240,3 +240,49 @@ def test_lei_rejects_bad_arguments(lib):
 def test_stage_timing_modes(lib):
     assert lib.moe_stage_timing(3) == 1 and lib.moe_stage_timing(-1) == 1
     assert lib.moe_stage_timing(2) == 0 and lib.moe_stage_timing(0) == 0
+
+
+def test_fp8_workspace_sizes(lib):
+    p = _problem()
+    b8 = lib.moe_forward_fp8_workspace_bytes(C.byref(p))
+    b16 = lib.moe_forward_workspace_bytes(C.byref(p))
+    pairs = 16384 * 6
+    # E4M3 x and H plus bf16 per-pair outputs: between the codes and the bf16 sizes
+    assert pairs * (512 + 2560 * 2) < b8 < b16
+    for bad in (dict(d=192), dict(h=96), dict(h_shared=64), dict(d=100)):
+        assert lib.moe_forward_fp8_workspace_bytes(C.byref(_problem(**bad))) == 0, bad
+    # h_shared is free when there is no shared expert
+    assert lib.moe_forward_fp8_workspace_bytes(C.byref(_problem(n_shared=0, h_shared=64))) > 0
+
+
+def test_fp8_entry_points_reject_bad_arguments(lib):
+    from sigmoid_top_routing_router_amd._lib import MoeFp8Weights
+    buf = C.create_string_buffer(4096)
+    p16 = (C.cast(buf, C.c_void_p).value + 255) // 256 * 256
+    full = [p16] * 13
+    prob = _problem(N=4, d=128, E=4, K=2, h=128, h_shared=128)
+    w = MoeFp8Weights(*full)
+    # NULL block scales of the routed gate
+    w_nos = MoeFp8Weights(*(full[:2] + [None] + full[3:]))
+    assert lib.moe_forward_fp8(C.byref(prob), C.byref(w_nos), p16, None, p16, None, p16,
+                               1 << 30, None) == 1
+    # misaligned codes
+    w_mis = MoeFp8Weights(*(full[:1] + [p16 + 8] + full[2:]))
+    assert lib.moe_forward_fp8(C.byref(prob), C.byref(w_mis), p16, None, p16, None, p16,
+                               1 << 30, None) == 1
+    # widths that are not multiples of 128
+    prob_d = _problem(N=4, d=64, E=4, K=2, h=128, h_shared=128)
+    assert lib.moe_forward_fp8(C.byref(prob_d), C.byref(w), p16, None, p16, None, p16,
+                               1 << 30, None) == 2
+    # workspace too small
+    assert lib.moe_forward_fp8(C.byref(prob), C.byref(w), p16, None, p16, None, p16, 64,
+                               None) == 3
+    # quantisers: shapes checked first, empty inputs enqueue nothing
+    assert lib.moe_fp8_quantize_rows(p16, 4, 100, p16, p16, None) == 2
+    assert lib.moe_fp8_quantize_rows(p16, -1, 128, p16, p16, None) == 2
+    assert lib.moe_fp8_quantize_rows(p16 + 2, 4, 128, p16, p16, None) == 1
+    assert lib.moe_fp8_quantize_rows(None, 0, 128, None, None, None) == 0
+    assert lib.moe_fp8_quantize_blocks(p16, -1, 128, 128, p16, p16, None) == 2
+    assert lib.moe_fp8_quantize_blocks(p16, 1, 0, 128, p16, p16, None) == 2
+    assert lib.moe_fp8_quantize_blocks(p16, 1, 128, 128, p16, None, None) == 1
+    assert lib.moe_fp8_quantize_blocks(None, 0, 128, 128, None, None, None) == 0

@@ -1,0 +1,190 @@
+"""GPU parity of the FP8 (E4M3) path against the oracle ("Kolibri 1 im
+Detail", FP8 section: 128 x 128 weight blocks with fp32 scales, activations
+quantised per 1 x 128 group, router in bf16).
+
+* moe_fp8_quantize_rows / moe_fp8_quantize_blocks: codes and scales
+  bit-exact (both sides divide in fp32 and round to nearest even).
+* moe_forward_fp8 on a synthetic E4M3 checkpoint: routing, loads and grouping
+  bit-exact and equal to moe_forward's for the same logits; the layer output
+  within 2e-2 relative L2 of the oracle's FP8 layer (fp64 on the dequantised
+  operands) on every token, or on a seeded sample at the full sizes."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+from synth import CONFIGS, make_fp8_experts, make_inputs, scaled
+from tests.gpu_util import (S_RTOL, Y_REL_L2, bf16_dev, bits_equal, check_logits, dev, host,
+                            rel_l2, say, weights_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def M():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sigmoid_top_routing_router_amd as M
+    M.load_library()
+    return M
+
+
+def _bf16_bits(rng, shape, kind):
+    x = rng.standard_normal(shape).astype(np.float32)
+    if kind == "outliers":
+        x[..., ::97] *= 1e4
+    elif kind == "tiny":
+        x *= 1e-30
+    from synth import to_bf16_bits
+    b = to_bf16_bits(x)
+    return b
+
+
+@pytest.mark.parametrize("n,cols,kind", [(1, 128, "normal"), (257, 512, "normal"),
+                                          (300, 2560, "outliers"), (64, 384, "tiny")])
+def test_quantize_rows_bitexact(M, n, cols, kind):
+    say("fp8 quantize rows", n, cols, kind)
+    rng = np.random.default_rng(n + cols)
+    xb = _bf16_bits(rng, (n, cols), kind)
+    if n > 3:
+        xb[3, 128:256] = 0            # an all-zero group
+        xb[2, 0:128] = 0x8000         # -0.0 everywhere
+    q, s = M.fp8_quantize_rows(bf16_dev(xb))
+    rq, rs = O.quantize_row_groups(O.bf16_to_f32(xb))
+    assert np.array_equal(host(q), rq), "codes differ"
+    assert bits_equal(host(s), rs), "scales differ"
+
+
+@pytest.mark.parametrize("count,R,C", [(1, 128, 128), (3, 300, 200), (2, 256, 384), (1, 1, 1)])
+def test_quantize_blocks_bitexact(M, count, R, C):
+    say("fp8 quantize blocks", count, R, C)
+    rng = np.random.default_rng(count * 1000 + R + C)
+    wb = _bf16_bits(rng, (count, R, C), "normal")
+    q, s = M.fp8_quantize_blocks(bf16_dev(wb))
+    q, s = host(q), host(s)
+    for i in range(count):
+        rq, rs = O.quantize_weight_blocks(O.bf16_to_f32(wb[i]))
+        assert np.array_equal(q[i], rq), f"codes of matrix {i} differ"
+        assert bits_equal(s[i], rs), f"scales of matrix {i} differ"
+
+
+def test_quantize_blocks_full_size_sampled(M):
+    """The routed gate weights of the Kolibri-shaped layer, [384, 512, 2560]:
+    a seeded sample of 24 blocks against the oracle."""
+    L = make_inputs(CONFIGS["prefill"])
+    say("fp8 quantize blocks full size")
+    q, s = M.fp8_quantize_blocks(bf16_dev(L.w_gate))
+    q, s = host(q), host(s)
+    rng = np.random.default_rng(5)
+    for _ in range(24):
+        e, bi, bj = int(rng.integers(384)), int(rng.integers(4)), int(rng.integers(20))
+        blk = O.bf16_to_f32(L.w_gate[e, bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128])
+        rq, rs = O.quantize_weight_blocks(blk)
+        assert np.array_equal(q[e, bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128], rq)
+        assert bits_equal(s[e, bi, bj], rs[0, 0])
+
+
+_CACHE = {}
+
+
+def _case_inputs(cfg):
+    key = (cfg.name, cfg.N, cfg.n_shared)
+    if key not in _CACHE:
+        if len(_CACHE) > 1:
+            _CACHE.clear()
+        _CACHE[key] = (make_inputs(cfg), make_fp8_experts(cfg))
+    return _CACHE[key]
+
+
+def _fp8_dev(M, L, q, shared):
+    W = M.Fp8ExpertWeights(w_router=bf16_dev(L.w_router),
+                           **{k: dev(v) for k, v in q.items() if not k.startswith(("ws", "ss"))})
+    if shared:
+        for k in ("ws_gate", "ss_gate", "ws_up", "ss_up", "ws_down", "ss_down"):
+            setattr(W, k, dev(q[k]))
+    return W
+
+
+def run_fp8_case(M, cfg, sample=None, use_logits_in=False):
+    import torch
+    L, q = _case_inputs(cfg)
+    shared = cfg.n_shared > 0
+    say("fp8 forward", cfg.name, cfg.N, "shared", shared, "sample", sample,
+        "logits_in", use_logits_in)
+    x = bf16_dev(L.x)
+    xf = O.bf16_to_f32(L.x)
+    wr = O.bf16_to_f32(L.w_router)
+    logits_in = O.router_logits(xf, wr, L.logit_offset) if use_logits_in else None
+    kw = dict(beta_in=dev(L.beta_in), recompute_bias=cfg.recompute_bias,
+              logit_offset=None if use_logits_in else dev(L.logit_offset),
+              logits_in=dev(logits_in), aux=M.AUX_FIELDS)
+    y, A = M.forward_fp8(x, _fp8_dev(M, L, q, shared), cfg.K, **kw)
+    torch.cuda.synchronize()
+    y = O.bf16_to_f32(host(y))
+    A = {k: host(v) for k, v in A.items()}
+    # the same routing as the bf16 layer on the same logits
+    _, Ab = M.forward(x, weights_dev(L), cfg.K, **kw)
+    torch.cuda.synchronize()
+    keys = ["logits", "topk_ids", "topk_weights", "alpha", "margin", "counts", "offsets",
+            "sorted_src", "src_pos"] + (["beta_out", "quantile_out"] if cfg.recompute_bias else [])
+    for k in keys:
+        assert bits_equal(A[k], host(Ab[k])), f"{k} differs from the bf16 layer's"
+    N = cfg.N
+    rows = np.arange(N) if sample is None else np.sort(
+        np.random.default_rng(cfg.seed).choice(N, sample, replace=False))
+    if not use_logits_in:
+        check_logits(A["logits"][rows], O.router_logits(xf[rows], wr, L.logit_offset))
+    ref = O.moe_layer(x=xf, w_router=None, w_gate=None, w_up=None, w_down=None, ws_gate=None,
+                      ws_up=None, ws_down=None, beta_in=L.beta_in, K=cfg.K,
+                      recompute_bias=cfg.recompute_bias, logits_in=A["logits"],
+                      compute_output=False)
+    assert np.array_equal(A["topk_ids"], ref["topk_ids"])
+    assert np.array_equal(A["sorted_src"], ref["sorted_src"])
+    S_err = np.max(np.abs(A["topk_weights"].astype(np.float64) - ref["topk_weights"])
+                   / np.abs(ref["topk_weights"]))
+    assert S_err <= S_RTOL, S_err
+    qo = dict(q)
+    if not shared:
+        for k in ("ws_gate", "ss_gate", "ws_up", "ss_up", "ws_down", "ss_down"):
+            qo[k] = q[k][:0]
+    yref = O.moe_combine_fp8(xf, qo, ref["topk_ids"], ref["topk_weights"], token_subset=rows)
+    err = rel_l2(y[rows], yref)
+    say("fp8 forward", cfg.name, "rel L2", f"{err:.3e}")
+    assert err <= Y_REL_L2, err
+    return err
+
+
+SMALL = [("origin", 300), ("decode", 64), ("prefill", 1), ("skewed", 600)]
+
+
+@pytest.mark.parametrize("name,N", SMALL)
+def test_forward_fp8_small(M, name, N):
+    cfg = scaled(CONFIGS[name], N)
+    run_fp8_case(M, cfg, sample=None if cfg.E <= 128 else min(N, 32))
+
+
+def test_forward_fp8_logits_in_and_no_shared(M):
+    cfg = scaled(CONFIGS["origin"], 520)
+    run_fp8_case(M, cfg, use_logits_in=True)
+    run_fp8_case(M, replace(cfg, n_shared=0), sample=64)
+
+
+def test_forward_fp8_prefill_full_sampled(M):
+    """The Kolibri-shaped prefill batch (N=16384, E=384, K=6, d=2560, h=512),
+    sampled tokens."""
+    run_fp8_case(M, CONFIGS["prefill"], sample=32)
+
+
+def test_forward_fp8_rejects_unaligned_width(M):
+    cfg = CONFIGS["toy"]  # d = 64
+    L = make_inputs(cfg)
+    W = M.Fp8ExpertWeights(w_router=bf16_dev(L.w_router), w_gate=dev(np.zeros((4, 32, 64), np.uint8)),
+                           s_gate=dev(np.zeros((4, 0, 0), np.float32)),
+                           w_up=dev(np.zeros((4, 32, 64), np.uint8)),
+                           s_up=dev(np.zeros((4, 0, 0), np.float32)),
+                           w_down=dev(np.zeros((4, 64, 32), np.uint8)),
+                           s_down=dev(np.zeros((4, 0, 0), np.float32)))
+    with pytest.raises(M.MoeError, match="UNSUPPORTED_SHAPE"):
+        M.forward_fp8(bf16_dev(L.x), W, cfg.K)
