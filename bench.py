@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 GEMM_SRC = os.path.join(ROOT, "sigmoid_top_routing_router_amd", "csrc", "grouped_gemm.hip")
 
@@ -41,14 +42,20 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def gateup_algorithmic(cfg, counts):
+def gateup_algorithmic(cfg, counts, fp8=False):
     """Flops and bytes the routed gate/up GEMM must do or move: every pair
     row times both d x h projections; each active expert's gate and up
-    weights once, x once, H written once (bf16)."""
+    weights once, x once, H written once (bf16; with FP8 experts: E4M3 codes
+    plus one fp32 scale per 128 x 128 weight block and per 1 x 128 group of
+    x and of H)."""
     pairs = cfg.N * cfg.K
     flops = 2.0 * pairs * (2 * cfg.h) * cfg.d
     active = int((counts > 0).sum())
-    bytes_ = active * 2 * cfg.h * cfg.d * 2 + cfg.N * cfg.d * 2 + pairs * cfg.h * 2
+    if fp8:
+        bytes_ = (active * 2 * (cfg.h * cfg.d + (cfg.h // 128) * (cfg.d // 128) * 4)
+                  + cfg.N * cfg.d * (1 + 4 / 128) + pairs * cfg.h * (1 + 4 / 128))
+    else:
+        bytes_ = active * 2 * cfg.h * cfg.d * 2 + cfg.N * cfg.d * 2 + pairs * cfg.h * 2
     return flops, bytes_
 
 
@@ -153,6 +160,8 @@ def main():
                     choices=["origin", "prefill", "decode", "skewed"])
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8", action="store_true",
+                    help="E4M3 experts (moe_forward_fp8) quantised from the same bf16 weights")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "kernel for scaling hardware byte counters)")
@@ -161,6 +170,8 @@ def main():
                          "rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE) of "
                          "this script run with --calibrate-copy-mib")
     args = ap.parse_args()
+    if args.fp8 and (args.record_traffic or args.calibrate_copy_mib):
+        ap.error("--fp8 has no traffic record")
     if args.record_traffic:
         record_traffic(args.workload, *args.record_traffic, args.calibrate_copy_mib or 1024)
         return
@@ -188,21 +199,27 @@ def main():
 
     W = M.ExpertWeights(bf16(L.w_router), bf16(L.w_gate), bf16(L.w_up), bf16(L.w_down),
                         bf16(L.ws_gate), bf16(L.ws_up), bf16(L.ws_down))
+    fwd, ws_fn = M.forward, M.forward_workspace_bytes
+    if args.fp8:
+        # E4M3 experts quantised from the bf16 weights by the library (untimed)
+        W = M.quantize_experts(W)
+        torch.cuda.synchronize()
+        fwd, ws_fn = M.forward_fp8, M.forward_fp8_workspace_bytes
     x = bf16(L.x)
     beta = torch.from_numpy(L.beta_in).cuda()
     off = None if L.logit_offset is None else torch.from_numpy(L.logit_offset).cuda()
-    ws_bytes = M.forward_workspace_bytes(cfg.N, cfg.d, cfg.E, cfg.K, cfg.h, cfg.n_shared,
-                                         cfg.h_shared, cfg.recompute_bias)
+    ws_bytes = ws_fn(cfg.N, cfg.d, cfg.E, cfg.K, cfg.h, cfg.n_shared, cfg.h_shared,
+                     cfg.recompute_bias)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     y = torch.empty((cfg.N, cfg.d), dtype=torch.bfloat16, device="cuda")
 
     def step():
-        M.forward(x, W, cfg.K, beta_in=beta, recompute_bias=cfg.recompute_bias,
-                  logit_offset=off, workspace=ws, out=y)
+        fwd(x, W, cfg.K, beta_in=beta, recompute_bias=cfg.recompute_bias,
+            logit_offset=off, workspace=ws, out=y)
 
     # loads of the final routing (for the algorithmic byte count), untimed
-    _, aux = M.forward(x, W, cfg.K, beta_in=beta, recompute_bias=cfg.recompute_bias,
-                       logit_offset=off, workspace=ws, out=y, aux=("counts", "counts_before"))
+    _, aux = fwd(x, W, cfg.K, beta_in=beta, recompute_bias=cfg.recompute_bias,
+                 logit_offset=off, workspace=ws, out=y, aux=("counts", "counts_before"))
     counts = aux["counts"].cpu().numpy()
     counts_before = aux["counts_before"].cpu().numpy()
     if args.calibrate_copy_mib > 0:
@@ -245,22 +262,24 @@ def main():
     tokens_s = cfg.N * args.steps / elapsed
     gateup_ms = gu_times["gate_up"] / max(gu_calls, 1)
 
-    flops, bytes_ = gateup_algorithmic(cfg, counts)
+    flops, bytes_ = gateup_algorithmic(cfg, counts, args.fp8)
+    peak_mfma = PEAK_FP8_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
     t_gu = gateup_ms * 1e-3
-    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_mfma = flops / (peak_mfma * 1e12)
     t_hbm = bytes_ / (PEAK_HBM_GBS * 1e9)
     if t_hbm >= t_mfma:
         roof = {"bound": "hbm", "achieved": bytes_ / t_gu / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": flops / t_gu / 1e12, "peak": PEAK_BF16_TFLOPS,
+        roof = {"bound": "mfma", "achieved": flops / t_gu / 1e12, "peak": peak_mfma,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = traffic_for(args.workload)
-    roof["kernel"] = "gemm_kernel<0, true> (routed gate/up GEMM)"
+    roof["traffic"] = None if args.fp8 else traffic_for(args.workload)
+    roof["kernel"] = ("gemm_fp8_kernel<0> (routed gate/up GEMM, E4M3)" if args.fp8
+                      else "gemm_kernel<0, true> (routed gate/up GEMM)")
     roof["per_launch"] = {"flops": flops, "bytes": bytes_, "avg_ms": gateup_ms,
                           "tflops": flops / t_gu / 1e12, "gbs": bytes_ / t_gu / 1e9,
-                          "mfma_frac": flops / t_gu / 1e12 / PEAK_BF16_TFLOPS}
+                          "mfma_frac": flops / t_gu / 1e12 / peak_mfma}
 
     layer_flops = 2.0 * cfg.N * cfg.E * cfg.d + 2.0 * cfg.N * cfg.K * 3 * cfg.h * cfg.d \
         + 2.0 * cfg.N * cfg.n_shared * 3 * cfg.h_shared * cfg.d
@@ -268,9 +287,12 @@ def main():
         "metric": "MoE layer fwd tokens/s at E=384,K=6,d=2560 (1 GPU); % MFMA / HBM roofline",
         "value": tokens_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8 e4m3 experts (bf16 router)" if args.fp8 else "bf16",
         "data": "synthetic (seeded normal inputs and random-init weights of the layer shape)",
-        "config": {**cfg.describe(), "parallelism": "none (1 GPU)"},
+        "config": {**cfg.describe(), "parallelism": "none (1 GPU)",
+                   **({"experts": "e4m3, 128x128 block scales, 1x128 activation groups"}
+                      if args.fp8 else {})},
         "layer_tflops": layer_flops / (ms_step * 1e-3) / 1e12,
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "loads": {"max_over_mean_before": float(counts_before.max() / counts_before.mean()),
