@@ -15,9 +15,9 @@
 //    lane), so one wave's LDS reads and loads overlap the other's MFMAs.  The
 //    256 x 256 tile is what bounds the operand traffic from L2 per flop (the
 //    CU's register file holds at most this many fp32 accumulators).
-//  * Operands move global -> LDS with the gfx950 LDS-DMA load
-//    (global_load_lds_dwordx4: 64 lanes x 16 bytes per instruction, no VGPR
-//    staging), 8 rows x 128 bytes per instruction: every row access is one
+//  * Operands move global -> LDS with the gfx950 LDS-DMA load in its buffer
+//    form (buffer_load_dwordx4 ... lds: 64 lanes x 16 bytes per instruction,
+//    no VGPR staging), 8 rows x 128 bytes per instruction: every row access is one
 //    whole 128-byte cache line, which on this chip moves about twice the
 //    bytes per second of half-line accesses.  All 160 KB of LDS hold operand
 //    slots of 32 KB: two for A and three for B (the weights, whose first
@@ -26,9 +26,13 @@
 //    waits plus a bare s_barrier so the compiler does not drain outstanding
 //    loads at every barrier.
 //  * LDS rows are 128 bytes (64 bf16); the eight 16-byte chunks of row r sit
-//    at slot c ^ (r & 7), so the fragment reads of 8 consecutive rows hit 8
-//    different bank groups.  The swizzle is applied on the global side (each
-//    lane picks the chunk that belongs in its fixed LDS slot).
+//    at slot c ^ ((r >> 1) & 7).  The LDS serves a 16-byte read for 16 lanes
+//    per cycle from 64 four-byte banks (256 bytes), i.e. from two adjacent
+//    rows; 16 consecutive rows with one chunk then fall on 16 distinct
+//    16-byte bank groups (even and odd rows on the two halves, (r >> 1) & 7
+//    spreading each half), so the fragment reads are free of bank conflicts.
+//    The swizzle is applied on the global side (each lane picks the chunk
+//    that belongs in its fixed LDS slot).
 //  * Within a stage the fragments of k-step s+1 are read from LDS while the
 //    MFMAs of k-step s run (two fragment register sets).
 //  * Gate/up: the B tile holds 128 gate rows then the 128 up rows of the same
@@ -43,8 +47,8 @@
 //    the device by the grouping kernels drives the grid; the grid is sized
 //    for the worst case and surplus blocks exit after reading the tile count.
 //    Waves skip the MFMAs of 32-row blocks that hold no valid rows; rows past
-//    the segment (and B rows past the matrix) are clamped to a valid row when
-//    loading and never stored.
+//    the segment (and B rows past the matrix) load zeros through an offset
+//    beyond the buffer and are never stored.
 //  * XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
 //    block b works on the logical tile (b % 8) * share + b / 8; each XCD then
 //    walks a contiguous run of (m-tile, n-tile) pairs, n fastest, and the
@@ -53,12 +57,13 @@
 #include <type_traits>
 
 #include "common.h"
+#include "gemm_args.h"
 #include "kernels.h"
 
 namespace moe {
 
 constexpr int BM = 256;
-constexpr int BN = 256;
+constexpr int BN = kTileN;
 constexpr int BK = 64;
 constexpr int A_SLOTS = 2;                           // A ring: stages kt, kt+1
 constexpr int B_SLOTS = 3;                           // B ring: stages kt .. kt+2
@@ -70,57 +75,6 @@ constexpr int kXcd = 8;
 
 int gemm_bm() { return BM; }
 
-enum Mode { kGateUp = 0, kDown = 1, kRouter = 2 };
-
-struct GemmArgs {
-  const uint16_t* A;       // x (gate/up, router) or H (down)
-  int64_t lda;             // elements per A row
-  const int32_t* gather;   // sorted_src (routed gate/up) or NULL
-  int gather_div;          // K (pair index -> token)
-  const int32_t* tiles;    // m-tile table or NULL (dense rows)
-  const int32_t* n_tiles;  // device count of table entries
-  int64_t rows_dense;      // rows when tiles == NULL
-  const uint16_t* B0;      // gate / down / router weights
-  const uint16_t* B1;      // up weights (gate/up only)
-  int64_t b_expert_stride; // elements between experts' matrices
-  int b_rows;              // valid rows of one expert's B (h, d or E)
-  int kdim;                // reduction length (multiple of 32)
-  int n_tiles_n;           // tiles along the output columns
-  void* out;               // H / Y (bf16) or Z (fp32)
-  int64_t ldo;             // elements per output row
-  const float* offset;     // router: per-column fp32 offset or NULL
-  uint32_t a_bytes;        // size of the whole A buffer (< 4 GiB)
-  // FP8 operands only (A and B are E4M3 codes; lda and kdim count bytes):
-  const float* sa;         // A scales [A rows][kdim/128] (1 x 128 groups)
-  const float* sb0;        // B scales [E][ceil(b_rows/128)][kdim/128] (128 x 128 blocks)
-  const float* sb1;        // up-projection scales (gate/up only)
-  int64_t sb_es;           // floats between experts' scale matrices
-  // gate/up only: when set, H leaves as E4M3 codes (out, ldo bytes per row)
-  // with one fp32 scale per 1 x 128 group of a row (out_scale [rows][ldo/128])
-  float* out_scale;
-};
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// Raw buffer resource over `bytes` bytes at `base` (stride 0; reads past the
-// end return zero).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-// LDS-DMA: 16 bytes per lane from (resource, per-lane voff + uniform soff) to
-// LDS at l + 16 * lane.  The buffer form (buffer_load_dwordx4 ... lds) is
-// counted on vmcnt only, so the compiler keeps exact lgkmcnt waits for the
-// LDS fragment reads around it.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
-                                      lds_void_t* l) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff, soff, 0, 0);
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 __device__ __forceinline__ void wait_all_mem() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 }
@@ -328,10 +282,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
   const int wp = wave & 3;            // column quarter of the tile
 
   // ---- LDS-DMA assignment.  Per stage and operand each wave issues 4 loads;
-  // load i covers tile rows 8*(8*i + wave) .. +7, lane l -> row +(l>>3), LDS
-  // slot (l&7) which holds global chunk (l&7) ^ (row&7) = (l&7) ^ ((l>>3)&7).
+  // load i covers tile rows r = 8*(8*i + wave) .. +7, lane l -> row +(l>>3),
+  // LDS slot (l&7), which holds global chunk (l&7) ^ ((r >> 1) & 7); that is
+  // (l&7) ^ ((4*wave + (l>>4)) & 7) for every i.
   const int sub = lane >> 3;
-  const int chunk = (lane & 7) ^ (sub & 7);
+  const int chunk = (lane & 7) ^ ((4 * wave + (sub >> 1)) & 7);
   // Byte offsets of each lane's 16-byte piece, fixed for the whole tile; the
   // stage's k offset goes in the scalar offset of the load.  Rows past the
   // segment and B rows past the matrix get an offset beyond the end of the
@@ -397,7 +352,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
   const int fr = lane & 31;
   const int a_base = (wg * 128 + fr) * ROW_BYTES;
   const int b_base = B_RING + fr * ROW_BYTES;
-  auto slot_of = [&](int ks) { return ((2 * ks + (lane >> 5)) ^ (lane & 7)) * 16; };
+  // fragment rows start on multiples of 32, so (row >> 1) & 7 = (l >> 1) & 7
+  auto slot_of = [&](int ks) { return ((2 * ks + (lane >> 5)) ^ ((lane >> 1) & 7)) * 16; };
 
   int live_m = (rows - wg * 128 + 31) / 32;
   live_m = live_m < 0 ? 0 : (live_m > 4 ? 4 : live_m);
@@ -561,7 +517,7 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
   const int wg = wave >> 2;
   const int wp = wave & 3;
   const int sub = lane >> 3;
-  const int chunk = (lane & 7) ^ (sub & 7);
+  const int chunk = (lane & 7) ^ ((4 * wave + (sub >> 1)) & 7);  // as in the bf16 tile
   constexpr uint32_t kNoRow = 0xFFFFFFFFu - 64u * 1024u;  // past any 4 GiB buffer
   uint32_t a_voff[4], b_voff[4];
 #pragma unroll
@@ -698,9 +654,10 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
         const char* sa_lds = lds_raw + (kt % A_SLOTS) * TILE_BYTES;
         const char* sb_lds = lds_raw + B_RING + (kt % B_SLOTS) * TILE_BYTES;
         // lane l reads 32 bytes of its row: chunks 2*(l>>4) and +1 (swizzled;
-        // every fragment starts on a multiple of 16 rows, so row & 7 = l & 7)
-        const int s0 = ((2 * quad) ^ (lane & 7)) * 16;
-        const int s1 = ((2 * quad + 1) ^ (lane & 7)) * 16;
+        // fragments start on multiples of 16 rows, so (row >> 1) & 7 =
+        // (l >> 1) & 7)
+        const int s0 = ((2 * quad) ^ ((lane >> 1) & 7)) * 16;
+        const int s1 = ((2 * quad + 1) ^ ((lane >> 1) & 7)) * 16;
         auto frag = [&](const char* rowp) {
           const uint4 lo = *reinterpret_cast<const uint4*>(rowp + s0);
           const uint4 hi = *reinterpret_cast<const uint4*>(rowp + s1);
@@ -870,41 +827,8 @@ static hipError_t launch_gemm(int mode, const GemmArgs& a, int64_t max_m_tiles,
   }
 }
 
-static GemmArgs router_args(const uint16_t* x, const uint16_t* w_router, const float* offset,
-                            int64_t N, int d, int E, float* Z) {
-  GemmArgs a{};
-  a.A = x; a.lda = d; a.gather = nullptr; a.gather_div = 1;
-  a.tiles = nullptr; a.n_tiles = nullptr; a.rows_dense = N;
-  a.B0 = w_router; a.B1 = nullptr; a.b_expert_stride = 0; a.b_rows = E; a.kdim = d;
-  a.n_tiles_n = (E + BN - 1) / BN; a.out = Z; a.ldo = E; a.offset = offset;
-  a.a_bytes = (uint32_t)(N * d * 2);
-  return a;
-}
 
-static GemmArgs gateup_args(const uint16_t* x, int64_t x_rows, const int32_t* sorted_src, int K,
-                            const int32_t* tiles, const int32_t* n_tiles, int64_t rows_dense,
-                            const uint16_t* w_gate, const uint16_t* w_up, int d, int h,
-                            uint16_t* H) {
-  GemmArgs a{};
-  a.A = x; a.lda = d; a.gather = tiles ? sorted_src : nullptr; a.gather_div = K;
-  a.tiles = tiles; a.n_tiles = n_tiles; a.rows_dense = rows_dense;
-  a.B0 = w_gate; a.B1 = w_up; a.b_expert_stride = (int64_t)h * d; a.b_rows = h; a.kdim = d;
-  a.n_tiles_n = (h + BN / 2 - 1) / (BN / 2); a.out = H; a.ldo = h; a.offset = nullptr;
-  a.a_bytes = (uint32_t)(x_rows * d * 2);
-  return a;
-}
 
-static GemmArgs down_args(const uint16_t* H, int64_t h_rows, const int32_t* tiles,
-                          const int32_t* n_tiles, int64_t rows_dense, const uint16_t* w_down,
-                          int d, int h, uint16_t* Y) {
-  GemmArgs a{};
-  a.A = H; a.lda = h; a.gather = nullptr; a.gather_div = 1;
-  a.tiles = tiles; a.n_tiles = n_tiles; a.rows_dense = rows_dense;
-  a.B0 = w_down; a.B1 = nullptr; a.b_expert_stride = (int64_t)d * h; a.b_rows = d; a.kdim = h;
-  a.n_tiles_n = (d + BN - 1) / BN; a.out = Y; a.ldo = d; a.offset = nullptr;
-  a.a_bytes = (uint32_t)(h_rows * h * 2);
-  return a;
-}
 
 hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w_router,
                               const float* offset, int64_t N, int d, int E, float* Z,
@@ -959,23 +883,6 @@ hipError_t launch_router_shared_gateup(const uint16_t* x, int64_t N, int d,
 }
 
 // ---------------------------------------------------------------- FP8 launches
-static GemmArgs gateup_fp8_args(const uint8_t* xq, const float* xs, int64_t x_rows,
-                                const int32_t* sorted_src, int K, const int32_t* tiles,
-                                const int32_t* n_tiles, int64_t rows_dense, const uint8_t* wg,
-                                const float* sg, const uint8_t* wu, const float* su, int d, int h,
-                                uint8_t* Hq, float* Hs) {
-  GemmArgs a{};
-  a.A = reinterpret_cast<const uint16_t*>(xq); a.lda = d;
-  a.gather = tiles ? sorted_src : nullptr; a.gather_div = K;
-  a.tiles = tiles; a.n_tiles = n_tiles; a.rows_dense = rows_dense;
-  a.B0 = reinterpret_cast<const uint16_t*>(wg); a.B1 = reinterpret_cast<const uint16_t*>(wu);
-  a.b_expert_stride = (int64_t)h * d; a.b_rows = h; a.kdim = d;
-  a.n_tiles_n = h / (BN / 2); a.out = Hq; a.ldo = h; a.offset = nullptr;
-  a.a_bytes = (uint32_t)(x_rows * d);
-  a.sa = xs; a.sb0 = sg; a.sb1 = su; a.sb_es = (int64_t)(h / 128) * (d / 128);
-  a.out_scale = Hs;
-  return a;
-}
 
 static hipError_t launch_fp8(int mode, const GemmArgs& a, int64_t max_m_tiles,
                              hipStream_t stream) {
@@ -1012,15 +919,7 @@ hipError_t launch_down_fp8(const uint8_t* Hq, const float* Hs, int64_t h_rows,
                            const int32_t* tiles, const int32_t* n_tiles, int64_t max_tiles,
                            int64_t rows_dense, const uint8_t* wd, const float* sd, int d, int h,
                            uint16_t* Y, hipStream_t stream) {
-  GemmArgs a{};
-  a.A = reinterpret_cast<const uint16_t*>(Hq); a.lda = h; a.gather = nullptr; a.gather_div = 1;
-  a.tiles = tiles; a.n_tiles = n_tiles; a.rows_dense = rows_dense;
-  a.B0 = reinterpret_cast<const uint16_t*>(wd); a.B1 = nullptr;
-  a.b_expert_stride = (int64_t)d * h; a.b_rows = d; a.kdim = h;
-  a.n_tiles_n = (d + BN - 1) / BN; a.out = Y; a.ldo = d; a.offset = nullptr;
-  a.a_bytes = (uint32_t)(h_rows * h);
-  a.sa = Hs; a.sb0 = sd; a.sb1 = sd; a.sb_es = (int64_t)(d / 128) * (h / 128);
-  a.out_scale = nullptr;
+  const GemmArgs a = down_fp8_args(Hq, Hs, h_rows, tiles, n_tiles, rows_dense, wd, sd, d, h, Y);
   return launch_fp8(kDown, a, tiles ? max_tiles : (rows_dense + BM - 1) / BM, stream);
 }
 

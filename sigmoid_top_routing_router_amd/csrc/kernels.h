@@ -155,6 +155,30 @@ hipError_t launch_router_shared_gateup_fp8(const uint16_t* x, const uint8_t* xq,
                                            const uint8_t* wsu, const float* ssu, int hs,
                                            uint8_t* Hsq, float* Hss, hipStream_t stream);
 
+// Weight-streaming variants of the routed (grouped) products for batches of
+// at most 64 tokens (every tile then holds at most 64 rows); same arguments
+// and results as the launchers above, `tiles` required.
+constexpr int64_t kSmallBatch = 64;
+hipError_t launch_gateup_small(const uint16_t* x, int64_t x_rows, const int32_t* sorted_src,
+                               int K, const int32_t* tiles, const int32_t* n_tiles,
+                               int64_t max_tiles, int64_t rows_dense, const uint16_t* w_gate,
+                               const uint16_t* w_up, int d, int h, uint16_t* H,
+                               hipStream_t stream);
+hipError_t launch_down_small(const uint16_t* H, int64_t h_rows, const int32_t* tiles,
+                             const int32_t* n_tiles, int64_t max_tiles, int64_t rows_dense,
+                             const uint16_t* w_down, int d, int h, uint16_t* Y,
+                             hipStream_t stream);
+hipError_t launch_gateup_fp8_small(const uint8_t* xq, const float* xs, int64_t x_rows,
+                                   const int32_t* sorted_src, int K, const int32_t* tiles,
+                                   const int32_t* n_tiles, int64_t max_tiles, int64_t rows_dense,
+                                   const uint8_t* wg, const float* sg, const uint8_t* wu,
+                                   const float* su, int d, int h, uint8_t* Hq, float* Hs,
+                                   hipStream_t stream);
+hipError_t launch_down_fp8_small(const uint8_t* Hq, const float* Hs, int64_t h_rows,
+                                 const int32_t* tiles, const int32_t* n_tiles, int64_t max_tiles,
+                                 int64_t rows_dense, const uint8_t* wd, const float* sd, int d,
+                                 int h, uint16_t* Y, hipStream_t stream);
+
 // ---------------------------------------------------------------- misc
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t stream);
 

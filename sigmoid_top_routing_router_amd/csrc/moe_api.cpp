@@ -305,6 +305,11 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
   const float* Z;
   const bool shared = p->n_shared == 1;
   const int hs = p->h_shared;
+  // A batch of at most 64 tokens reads every touched routed weight once and
+  // does little arithmetic: the routed GEMMs then stream the weights straight
+  // into registers (the dense router and shared-expert products keep the tile
+  // engine, whose few blocks already cover their weights).
+  const bool small = N <= moe::kSmallBatch;
   if (ex.fp8)
     MOE_TRY_HIP(moe::launch_quant_rows(x, N, d, l.xq, l.xs, st), "moe_forward: quantise x");
   if (p->logits_in) {
@@ -380,20 +385,24 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
 
   // routed experts (the gather is fused into the gate/up A loads)
+  auto gateup = small ? moe::launch_gateup_small : moe::launch_gateup;
+  auto gateup8 = small ? moe::launch_gateup_fp8_small : moe::launch_gateup_fp8;
+  auto down = small ? moe::launch_down_small : moe::launch_down;
+  auto down8 = small ? moe::launch_down_fp8_small : moe::launch_down_fp8;
   if (ex.fp8)
-    MOE_TRY_HIP(moe::launch_gateup_fp8(l.xq, l.xs, N, pw.sorted_src, K, pw.tiles, pw.n_tiles,
-                                       l.max_tiles, 0, q->w_gate, q->s_gate, q->w_up, q->s_up,
-                                       d, h, l.Hq, l.Hqs, st), "moe_forward: gate/up");
+    MOE_TRY_HIP(gateup8(l.xq, l.xs, N, pw.sorted_src, K, pw.tiles, pw.n_tiles, l.max_tiles, 0,
+                        q->w_gate, q->s_gate, q->w_up, q->s_up, d, h, l.Hq, l.Hqs, st),
+                "moe_forward: gate/up");
   else
-    MOE_TRY_HIP(moe::launch_gateup(x, N, pw.sorted_src, K, pw.tiles, pw.n_tiles, l.max_tiles, 0,
-                                   w->w_gate, w->w_up, d, h, l.H, st), "moe_forward: gate/up");
+    MOE_TRY_HIP(gateup(x, N, pw.sorted_src, K, pw.tiles, pw.n_tiles, l.max_tiles, 0, w->w_gate,
+                       w->w_up, d, h, l.H, st), "moe_forward: gate/up");
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
   if (ex.fp8)
-    MOE_TRY_HIP(moe::launch_down_fp8(l.Hq, l.Hqs, N * K, pw.tiles, pw.n_tiles, l.max_tiles, 0,
-                                     q->w_down, q->s_down, d, h, l.Y, st), "moe_forward: down");
+    MOE_TRY_HIP(down8(l.Hq, l.Hqs, N * K, pw.tiles, pw.n_tiles, l.max_tiles, 0, q->w_down,
+                      q->s_down, d, h, l.Y, st), "moe_forward: down");
   else
-    MOE_TRY_HIP(moe::launch_down(l.H, N * K, pw.tiles, pw.n_tiles, l.max_tiles, 0, w->w_down, d,
-                                 h, l.Y, st), "moe_forward: down");
+    MOE_TRY_HIP(down(l.H, N * K, pw.tiles, pw.n_tiles, l.max_tiles, 0, w->w_down, d, h, l.Y, st),
+                "moe_forward: down");
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
   // the shared expert's down projection
   if (shared && ex.fp8)

@@ -63,7 +63,7 @@ def run_case(M, cfg, key_bits=16, sample=None, free_running=False, use_logits_in
     rows = np.arange(N) if sample is None else np.sort(
         np.random.default_rng(cfg.seed).choice(N, sample, replace=False))
 
-    # a1: logits
+    # router logits
     Zg = A["logits"]
     if use_logits_in:
         assert bits_equal(Zg, logits_in)
@@ -71,7 +71,7 @@ def run_case(M, cfg, key_bits=16, sample=None, free_running=False, use_logits_in
         zref = O.router_logits(xf[rows], wr, L.logit_offset)
         check_logits(Zg[rows], zref)
 
-    # a2-a5 on identical logits: bit-exact
+    # selection, bias update and grouping on identical logits: bit-exact
     ref = O.moe_layer(x=xf, w_router=None, **oracle_weights(L), beta_in=L.beta_in, K=cfg.K,
                       recompute_bias=cfg.recompute_bias, key_bits=key_bits, logits_in=Zg,
                       compute_output=False)
@@ -90,7 +90,7 @@ def run_case(M, cfg, key_bits=16, sample=None, free_running=False, use_logits_in
                    / np.abs(ref["topk_weights"]))
     assert S_err <= S_RTOL, S_err
 
-    # a6-a10: layer output on the sampled tokens (routing of the GPU = oracle's on Zg)
+    # experts and combine: the output on the sampled tokens (routing of the GPU = oracle's on Zg)
     yref = O.moe_combine(xf, **oracle_weights(L), ids=ref["topk_ids"], S=ref["topk_weights"],
                          token_subset=rows)
     err = rel_l2(y[rows], yref)
@@ -147,6 +147,19 @@ def test_forward_tiny_shapes(M):
         cfg = replace(base, name=f"tiny_{N}_{E}_{K}", N=N, E=E, K=K, offset=None,
                       recompute_bias=(N > 1), dtype="bf16")
         run_case(M, cfg)
+
+
+def test_forward_small_batch_concentrated(M):
+    """Batches of at most 64 tokens take the weight-streaming expert GEMMs.
+    With the collapse offset every token picks experts 0 and 1, so those
+    tiles hold all 64 rows (four 16-row passes); h = 96 leaves a half k-set
+    in the down projection and a partly empty block of hidden columns."""
+    base = CONFIGS["toy"]
+    for N in (64, 17):
+        cfg = replace(base, name=f"small_collapse_{N}", N=N, d=256, E=8, K=2, h=96,
+                      h_shared=96, recompute_bias=False, dtype="bf16")
+        _, A = run_case(M, cfg)
+        assert A["counts"][0] == N and A["counts"][1] == N
 
 
 def test_forward_without_shared_expert(M):

@@ -171,6 +171,16 @@ def test_forward_fp8_logits_in_and_no_shared(M):
     run_fp8_case(M, replace(cfg, n_shared=0), sample=64)
 
 
+def test_forward_fp8_small_batch_concentrated(M):
+    """The weight-streaming E4M3 GEMMs with every token on experts 0 and 1
+    (64 rows: four passes), and a batch of 17 tokens."""
+    base = CONFIGS["toy"]
+    for N in (64, 17):
+        cfg = replace(base, name=f"fp8_small_collapse_{N}", N=N, d=256, E=8, K=2, h=256,
+                      h_shared=128, recompute_bias=False, dtype="bf16")
+        run_fp8_case(M, cfg)
+
+
 def test_forward_fp8_prefill_full_sampled(M):
     """The Kolibri-shaped prefill batch (N=16384, E=384, K=6, d=2560, h=512),
     sampled tokens."""
