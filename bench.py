@@ -30,7 +30,8 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-GEMM_SRC = os.path.join(ROOT, "sigmoid_top_routing_router_amd", "csrc", "grouped_gemm.hip")
+GEMM_SRC = [os.path.join(ROOT, "sigmoid_top_routing_router_amd", "csrc", f)
+            for f in ("grouped_gemm.hip", "gemm_args.h")]
 
 
 def log(*a):
@@ -38,8 +39,12 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    with open(GEMM_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the tile engine's sources (the kernel the traffic record covers)."""
+    h = hashlib.sha256()
+    for path in GEMM_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def gateup_algorithmic(cfg, counts, fp8=False):
