@@ -50,7 +50,10 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
 }
 
 // One block of 256 threads per 128 x 128 tile of one matrix: thread t takes
-// rows t/2 (two threads per row), 64 columns each.
+// row t/2 of the tile, 64 columns.  VEC: C % 8 == 0 and W 16-byte aligned, so
+// the 64 columns move as 16-byte loads (eight bf16) and 8-byte code stores;
+// otherwise element by element.
+template <bool VEC>
 __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __restrict__ W,
                                                            int R, int C,
                                                            uint8_t* __restrict__ Q,
@@ -64,15 +67,41 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __res
   const int r = br * 128 + (threadIdx.x >> 1);
   const int c0 = bc * 128 + (threadIdx.x & 1) * 64;
   uint32_t m = 0;
-  if (r < R)
+  uint4 v[8];
+  if (VEC) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool in = r < R && c0 + 8 * j < C;
+      v[j] = in ? *reinterpret_cast<const uint4*>(Wm + (int64_t)r * C + c0 + 8 * j)
+                : make_uint4(0, 0, 0, 0);
+      const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = max(m, max(w[i] << 17 >> 1, w[i] & 0x7FFF0000u));
+    }
+  } else if (r < R) {
     for (int j = 0; j < 64 && c0 + j < C; ++j)
       m = max(m, __float_as_uint(fabsf(bf16_to_f32(Wm[(int64_t)r * C + c0 + j]))));
+  }
   m = wave_max_u32(m);
   if (lane_id() == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
   const float amax = __uint_as_float(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
   const float s = amax / kE4M3Max;
-  if (r < R) {
+  if (VEC) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (!(r < R && c0 + 8 * j < C)) continue;
+      const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+      uint32_t lo = 0, hi = 0;
+      if (amax != 0.0f) {
+        lo = fp8x2(quant_input(bf16_to_f32(w[0] & 0xFFFFu), s), quant_input(bf16_to_f32(w[0] >> 16), s)) |
+             (fp8x2(quant_input(bf16_to_f32(w[1] & 0xFFFFu), s), quant_input(bf16_to_f32(w[1] >> 16), s)) << 16);
+        hi = fp8x2(quant_input(bf16_to_f32(w[2] & 0xFFFFu), s), quant_input(bf16_to_f32(w[2] >> 16), s)) |
+             (fp8x2(quant_input(bf16_to_f32(w[3] & 0xFFFFu), s), quant_input(bf16_to_f32(w[3] >> 16), s)) << 16);
+      }
+      *reinterpret_cast<uint2*>(Qm + (int64_t)r * C + c0 + 8 * j) = make_uint2(lo, hi);
+    }
+  } else if (r < R) {
     for (int j = 0; j < 64 && c0 + j < C; j += 2) {
       const float a = bf16_to_f32(Wm[(int64_t)r * C + c0 + j]);
       const bool two = c0 + j + 1 < C;
@@ -98,7 +127,10 @@ hipError_t launch_quant_blocks(const uint16_t* W, int64_t count, int R, int C, u
                                float* S, hipStream_t stream) {
   if (count <= 0) return hipSuccess;
   const dim3 grid((unsigned)((C + 127) / 128), (unsigned)((R + 127) / 128), (unsigned)count);
-  hipLaunchKernelGGL(quant_blocks_kernel, grid, dim3(256), 0, stream, W, R, C, Q, S);
+  if (C % 8 == 0 && (uintptr_t)W % 16 == 0 && (uintptr_t)Q % 8 == 0)
+    hipLaunchKernelGGL(quant_blocks_kernel<true>, grid, dim3(256), 0, stream, W, R, C, Q, S);
+  else
+    hipLaunchKernelGGL(quant_blocks_kernel<false>, grid, dim3(256), 0, stream, W, R, C, Q, S);
   return hipGetLastError();
 }
 

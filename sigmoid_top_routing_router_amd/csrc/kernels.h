@@ -179,6 +179,23 @@ hipError_t launch_down_fp8_small(const uint8_t* Hq, const float* Hs, int64_t h_r
                                  int64_t rows_dense, const uint8_t* wd, const float* sd, int d,
                                  int h, uint16_t* Y, hipStream_t stream);
 
+// Dense products of a batch of at most 64 tokens (router, shared expert),
+// split over 64-row weight blocks and 256-wide k chunks; `part` holds
+// dense_small_part_floats() fp32 partial sums.  x / H are bf16, or E4M3
+// codes with 1 x 128 scales when fp8 (weights then codes with 128 x 128
+// block scales); the gate/up result is H in bf16, or E4M3 codes + scales.
+size_t dense_small_part_floats(int64_t N, int d, int E, int hs);
+hipError_t launch_router_dense_small(const uint16_t* x, const uint16_t* w_router,
+                                     const float* offset, int64_t N, int d, int E, float* Z,
+                                     float* part, hipStream_t stream);
+hipError_t launch_shared_gateup_dense_small(const void* x, const float* xs, int64_t N, int d,
+                                            const void* wg, const float* sg, const void* wu,
+                                            const float* su, int hs, bool fp8, void* H,
+                                            float* Hs, float* part, hipStream_t stream);
+hipError_t launch_shared_down_dense_small(const void* H, const float* Hs, int64_t N, int d,
+                                          const void* wd, const float* sd, int hs, bool fp8,
+                                          uint16_t* Y, float* part, hipStream_t stream);
+
 // ---------------------------------------------------------------- misc
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t stream);
 

@@ -109,6 +109,7 @@ struct FwdLayout {
   float* Hqs;
   uint8_t* Hsq;
   float* Hss;
+  float* part;  // split-K partial sums of the dense products of a small batch
   size_t bytes;
   int64_t max_tiles;
 };
@@ -153,6 +154,8 @@ FwdLayout carve_forward(void* ws, const moe_problem_t& p, bool fp8 = false) {
     }
     l.sh = c.take<uint16_t>((size_t)N * p.d);
   }
+  if (N <= moe::kSmallBatch)
+    l.part = c.take<float>(moe::dense_small_part_floats(N, p.d, p.E, p.n_shared ? p.h_shared : 0));
   l.bytes = c.off;
   return l;
 }
@@ -305,14 +308,36 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
   const float* Z;
   const bool shared = p->n_shared == 1;
   const int hs = p->h_shared;
-  // A batch of at most 64 tokens reads every touched routed weight once and
-  // does little arithmetic: the routed GEMMs then stream the weights straight
-  // into registers (the dense router and shared-expert products keep the tile
-  // engine, whose few blocks already cover their weights).
+  // A batch of at most 64 tokens reads every touched weight once and does
+  // little arithmetic: its routed GEMMs stream the weights straight into
+  // registers, and its dense products are split over many small blocks.
   const bool small = N <= moe::kSmallBatch;
   if (ex.fp8)
     MOE_TRY_HIP(moe::launch_quant_rows(x, N, d, l.xq, l.xs, st), "moe_forward: quantise x");
-  if (p->logits_in) {
+  if (small) {
+    if (p->logits_in) {
+      Z = p->logits_in;
+      if (A.logits)
+        MOE_TRY_HIP(hipMemcpyAsync(A.logits, Z, (size_t)N * E * 4, hipMemcpyDeviceToDevice, st),
+                    "moe_forward: logits copy");
+    } else {
+      float* zout = A.logits ? A.logits : l.Z;
+      MOE_TRY_HIP(moe::launch_router_dense_small(x, ex.w_router, p->logit_offset, N, d, E, zout,
+                                                 l.part, st),
+                  "moe_forward: router GEMM");
+      Z = zout;
+    }
+    if (shared && ex.fp8)
+      MOE_TRY_HIP(moe::launch_shared_gateup_dense_small(l.xq, l.xs, N, d, q->ws_gate, q->ss_gate,
+                                                        q->ws_up, q->ss_up, hs, true, l.Hsq,
+                                                        l.Hss, l.part, st),
+                  "moe_forward: shared gate/up");
+    else if (shared)
+      MOE_TRY_HIP(moe::launch_shared_gateup_dense_small(x, nullptr, N, d, w->ws_gate, nullptr,
+                                                        w->ws_up, nullptr, hs, false, l.Hs,
+                                                        nullptr, l.part, st),
+                  "moe_forward: shared gate/up");
+  } else if (p->logits_in) {
     Z = p->logits_in;
     if (A.logits)
       MOE_TRY_HIP(hipMemcpyAsync(A.logits, Z, (size_t)N * E * 4, hipMemcpyDeviceToDevice, st),
@@ -405,7 +430,13 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
                 "moe_forward: down");
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
   // the shared expert's down projection
-  if (shared && ex.fp8)
+  if (shared && small)
+    MOE_TRY_HIP(moe::launch_shared_down_dense_small(
+                    ex.fp8 ? (const void*)l.Hsq : (const void*)l.Hs, ex.fp8 ? l.Hss : nullptr, N,
+                    d, ex.fp8 ? (const void*)q->ws_down : (const void*)w->ws_down,
+                    ex.fp8 ? q->ss_down : nullptr, hs, ex.fp8, l.sh, l.part, st),
+                "moe_forward: shared down");
+  else if (shared && ex.fp8)
     MOE_TRY_HIP(moe::launch_down_fp8(l.Hsq, l.Hss, N, nullptr, nullptr, 0, N, q->ws_down,
                                      q->ss_down, d, hs, l.sh, st), "moe_forward: shared down");
   else if (shared)
