@@ -280,8 +280,12 @@ def main():
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None if args.fp8 else traffic_for(args.workload)
-    roof["kernel"] = ("gemm_fp8_kernel<0> (routed gate/up GEMM, E4M3)" if args.fp8
-                      else "gemm_kernel<0, true> (routed gate/up GEMM)")
+    if cfg.N <= 64:  # batches of at most 64 tokens take the weight-streaming kernel
+        roof["kernel"] = (f"skinny_kernel<0, {'true' if args.fp8 else 'false'}> "
+                          "(routed gate/up GEMM, weight-streaming)")
+    else:
+        roof["kernel"] = ("gemm_fp8_kernel<0> (routed gate/up GEMM, E4M3)" if args.fp8
+                          else "gemm_kernel<0, true> (routed gate/up GEMM)")
     roof["per_launch"] = {"flops": flops, "bytes": bytes_, "avg_ms": gateup_ms,
                           "tflops": flops / t_gu / 1e12, "gbs": bytes_ / t_gu / 1e9,
                           "mfma_frac": flops / t_gu / 1e12 / peak_mfma}
