@@ -67,6 +67,13 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   uint32_t b = max(readlane_u32(v, 32), readlane_u32(v, 48));
   return max(a, b);
 }
+// Maximum over each DPP row of 16 lanes (every lane of the row gets it).
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kDppQuadSwap1>(v));
+  v = max(v, dpp_u32<kDppQuadSwap2>(v));
+  v = max(v, dpp_u32<kDppRowHalfMirror>(v));
+  return max(v, dpp_u32<kDppRowMirror>(v));
+}
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   v = min(v, dpp_u32<kDppQuadSwap1>(v));
   v = min(v, dpp_u32<kDppQuadSwap2>(v));

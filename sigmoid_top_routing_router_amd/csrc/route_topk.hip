@@ -168,18 +168,157 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
   }
 }
 
+// ---------------------------------------------------------------- 16 lanes per row
+// The same selection (same candidates, ranks and outputs) with a quarter wave
+// per row, for E % 4 == 0 and a 16-byte aligned Z: lane g of a row's 16 lanes
+// holds the experts 4g + 64j + c (c < 4, j < NC), read as float4, so one wave
+// selects four rows at once and every cross-lane step is a 16-lane DPP row
+// (the lane maxima, the K+1 pops that give L) or a ballot masked to the row.
+// Per row this issues about a third of the one-wave kernel's instructions,
+// which was bound by them.  Rows past N (the last quad) re-read row N-1 and
+// store nothing.
+template <int NC>
+__global__ __launch_bounds__(256) void route_group_kernel(
+    const float* __restrict__ Z, const float* __restrict__ beta, int64_t N, int E, int K,
+    int32_t* __restrict__ ids, float* __restrict__ S, float* __restrict__ alpha,
+    float* __restrict__ margin) {
+  constexpr int NVL = 4 * NC;  // experts per lane
+  const int lane = lane_id();
+  const int g = lane & 15;     // lane within the row's 16
+  const int grp = lane >> 4;   // row of the wave's quad
+  const int wib = threadIdx.x >> 6;
+  __shared__ uint64_t cand[4][4][16 * NVL];
+  __shared__ uint32_t kk[4][4][2];
+  const int64_t nquads = (N + 3) / 4;
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  int64_t quad = (int64_t)blockIdx.x * 4 + wib;
+  if (quad >= nquads) return;  // whole wave leaves together
+
+  float bv[NVL];
+#pragma unroll
+  for (int j = 0; j < NC; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = 4 * g + 64 * j + c;
+      bv[4 * j + c] = (beta && e < E) ? beta[e] : 0.0f;
+    }
+  auto load_row = [&](int64_t q, float4 (&v)[NC]) {
+    const int64_t r = min(q * 4 + grp, N - 1);
+    const float* zr = Z + r * (int64_t)E;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int e0 = 4 * g + 64 * j;
+      v[j] = (e0 < E) ? *reinterpret_cast<const float4*>(zr + e0) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  float4 cur[NC], nxt[NC];
+  load_row(quad, cur);
+  const uint64_t gmask = 0xFFFFull << (16 * grp);
+  uint64_t* cl = cand[wib][grp];
+  uint32_t* kl = kk[wib][grp];
+  for (; quad < nquads; quad += nwaves) {
+    const int64_t nq = quad + nwaves;
+    if (nq < nquads) load_row(nq, nxt);
+    const int64_t row = quad * 4 + grp;
+    const bool row_ok = row < N;
+
+    uint32_t key[NVL];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const float zc[4] = {cur[j].x, cur[j].y, cur[j].z, cur[j].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int e = 4 * g + 64 * j + c;
+        key[4 * j + c] = (e < E) ? f32_order_key(zc[c] + bv[4 * j + c]) : 0u;
+      }
+    }
+    // (1) L = the (K+1)-th largest of the row's 16 lane maxima (with
+    // multiplicity): every entry of the row's top K+1 has key >= L.
+    uint32_t lm = key[0];
+#pragma unroll
+    for (int i = 1; i < NVL; ++i) lm = max(lm, key[i]);
+    uint32_t L = 0u;
+#pragma unroll
+    for (int k = 0; k <= MOE_KMAX_INTERNAL; ++k) {
+      if (k > K) break;  // uniform
+      L = row16_max_u32(lm);
+      const int win = __ffsll((unsigned long long)(ballot(lm == L) & gmask)) - 1;
+      if (lane == win) lm = 0u;
+    }
+    // (2) compact the candidates (key >= L) of the row into its LDS list as
+    // composites (key << 32) | (2^32 - 1 - expert), in lane order
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) cnt += (key[i] >= L) ? 1u : 0u;
+    uint32_t off = 0, total = 0;
+#pragma unroll
+    for (int b = 0; b < 5; ++b) {  // cnt <= 24
+      const uint64_t m = ballot(((cnt >> b) & 1u) != 0u) & gmask;
+      off += (uint32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
+      total += (uint32_t)__popcll(m) << b;
+    }
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int i = 4 * j + c;
+        if (key[i] >= L) {
+          const uint32_t e = (uint32_t)(4 * g + 64 * j + c);
+          cl[off++] = ((uint64_t)key[i] << 32) | (uint64_t)(0xFFFFFFFFu - e);
+        }
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own list is written
+    // (3) rank = number of larger composites
+    for (uint32_t i = (uint32_t)g; i < total; i += 16) {
+      const uint64_t ci = cl[i];
+      uint32_t rank = 0;
+#pragma unroll 4
+      for (uint32_t j = 0; j < total; ++j) rank += (cl[j] > ci) ? 1u : 0u;
+      if (row_ok && rank < (uint32_t)K) {
+        const uint32_t e = 0xFFFFFFFFu - (uint32_t)ci;
+        if (ids) ids[row * K + rank] = (int32_t)e;
+        if (S) {
+          const float z = Z[row * (int64_t)E + e];
+          S[row * K + rank] = (float)(1.0 / (1.0 + exp(-(double)z)));
+        }
+      }
+      if (rank == (uint32_t)K - 1) kl[0] = (uint32_t)(ci >> 32);
+      if (rank == (uint32_t)K) kl[1] = (uint32_t)(ci >> 32);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    if (g == 0 && row_ok) {
+      const float vK = f32_from_order_key(kl[0]);
+      const float vK1 = f32_from_order_key(kl[1]);
+      if (alpha) alpha[row] = -vK1;
+      if (margin) margin[row] = vK - vK1;
+    }
+    // the next quad's candidates overwrite this quad's lists
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < NC; ++j) cur[j] = nxt[j];
+  }
+}
+
 // Blocks of 256 threads of one variant that the device holds at once
 // (occupancy x compute units), queried once per variant and device.
-static int64_t route_resident_blocks(int nv, bool alpha_only) {
-  static int64_t cache[2][8][7] = {};
+// kind 0: one wave per row, 1: its keys-only variant, 2: 16 lanes per row.
+static int64_t route_resident_blocks(int nv, int kind) {
+  static int64_t cache[3][8][7] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 8) return 2048;
-  int64_t& c = cache[alpha_only ? 1 : 0][dev][nv];
+  int64_t& c = cache[kind][dev][nv];
   if (c) return c;
   const void* fn = nullptr;
   switch (nv) {
-#define MOE_ROUTE_FN(V) \
-    case V: fn = alpha_only ? (const void*)route_topk_kernel<V, true> : (const void*)route_topk_kernel<V, false>; break;
+#define MOE_ROUTE_FN(V)                                                        \
+    case V:                                                                    \
+      fn = kind == 2 ? (const void*)route_group_kernel<V>                      \
+           : kind == 1 ? (const void*)route_topk_kernel<V, true>               \
+                       : (const void*)route_topk_kernel<V, false>;             \
+      break;
     MOE_ROUTE_FN(1) MOE_ROUTE_FN(2) MOE_ROUTE_FN(3) MOE_ROUTE_FN(4) MOE_ROUTE_FN(5) MOE_ROUTE_FN(6)
 #undef MOE_ROUTE_FN
     default: return 2048;
@@ -199,12 +338,32 @@ hipError_t launch_route(const float* Z, const float* beta, int64_t N, int E, int
   const int nv = (E + kWave - 1) / kWave;
   // alpha alone: keys-only variant
   const bool alpha_only = ids == nullptr && S == nullptr && margin == nullptr && alpha != nullptr;
+  const dim3 block(256);
+  if (E % 4 == 0 && (uintptr_t)Z % 16 == 0) {
+    // 16 lanes per row; the waves walk quads of rows with a grid stride
+    int64_t blocks = ((N + 3) / 4 + 3) / 4;
+    const int64_t cap = route_resident_blocks(nv, 2);
+    if (blocks > cap) blocks = cap;
+    const dim3 grid((unsigned)blocks);
+    switch (nv) {
+#define MOE_ROUTE_GROUP_CASE(V)                                                           \
+      case V:                                                                             \
+        hipLaunchKernelGGL((route_group_kernel<V>), grid, block, 0, stream, Z, beta, N, E, K, \
+                           ids, S, alpha, margin);                                        \
+        break;
+      MOE_ROUTE_GROUP_CASE(1) MOE_ROUTE_GROUP_CASE(2) MOE_ROUTE_GROUP_CASE(3)
+      MOE_ROUTE_GROUP_CASE(4) MOE_ROUTE_GROUP_CASE(5) MOE_ROUTE_GROUP_CASE(6)
+#undef MOE_ROUTE_GROUP_CASE
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   // The waves walk the rows with a grid stride; the grid is capped at what is
   // resident at once, so that no wave waits for a second round.
   int64_t blocks = (N + 3) / 4;
-  const int64_t cap = route_resident_blocks(nv, alpha_only);
+  const int64_t cap = route_resident_blocks(nv, alpha_only ? 1 : 0);
   if (blocks > cap) blocks = cap;
-  const dim3 grid((unsigned)blocks), block(256);
+  const dim3 grid((unsigned)blocks);
   switch (nv) {
 #define MOE_ROUTE_CASE(V)                                                                   \
     case V:                                                                                 \
