@@ -73,7 +73,10 @@ constexpr int B_RING = A_SLOTS * TILE_BYTES;         // byte offset of the B rin
 constexpr int LDS_BYTES = (A_SLOTS + B_SLOTS) * TILE_BYTES;  // 160 KB
 constexpr int kXcd = 8;
 
+constexpr int kXRows = 32;                           // extra rows of a grouped tile
+
 int gemm_bm() { return BM; }
+int gemm_xrows() { return kXRows; }
 
 __device__ __forceinline__ void wait_all_mem() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
@@ -101,7 +104,7 @@ __device__ __forceinline__ bool xcd_tile(int64_t work, int64_t& logical) {
 // Second half of the bf16-output epilogue: the tile staged in LDS (row
 // stride OSTRIDE bytes) goes to global memory in whole rows, as bf16 or, for
 // gate/up with a.out_scale set, as E4M3 codes with one scale per row group.
-template <int MODE>
+template <int MODE, int TROWS = BM>
 __device__ __forceinline__ void epilogue_store(const GemmArgs& a, int nt, int64_t row0, int rows,
                                                int tid, const char* lds_raw) {
   constexpr int OCOLS = (MODE == kGateUp) ? BN / 2 : BN;
@@ -115,7 +118,7 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& a, int nt, int64_
     // s = amax / 448, codes of min(max(v / s, -448), 448).
     uint8_t* q = reinterpret_cast<uint8_t*>(a.out);
     const int groups = (int)(a.ldo / 128);
-    for (int c = tid; c < BM * CPR; c += 512) {
+    for (int c = tid; c < TROWS * CPR; c += 512) {
       const int rr = c / CPR, ch = c % CPR;
       if (rr >= rows) break;  // the 16 lanes of a row leave together
       const char* src = lds_raw + rr * OSTRIDE + ch * 16;
@@ -152,7 +155,7 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& a, int nt, int64_
     return;
   }
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-  for (int c = tid; c < BM * CPR; c += 512) {
+  for (int c = tid; c < TROWS * CPR; c += 512) {
     const int rr = c / CPR, ch = c % CPR;
     if (rr >= rows) break;  // chunks are walked in row order
     const int col = col0 + ch * 8;
@@ -166,11 +169,12 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& a, int nt, int64_
 
 // Epilogue of one tile: accumulators acc[m][f] of wave (wg, wp) -> the output
 // (router: fp32 logits + offset; gate/up: SiLU(g) * u in bf16; down: bf16).
-template <int MODE>
-__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, floatx16_t (&acc)[4][2], int nt,
-                                              int64_t row0, int rows, int lane, int wg, int wp,
-                                              int tid, const int (&b_row)[2], bool any,
-                                              int live_m, char* lds_raw) {
+template <int MODE, int XR>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, floatx16_t (&acc)[4][2],
+                                              floatx16_t& accx, int nt, int64_t row0, int rows,
+                                              int lane, int wg, int wp, int tid,
+                                              const int (&b_row)[2], bool any, int live_m,
+                                              char* lds_raw) {
   // ---- epilogue.  The MFMAs take the B fragment as their first operand, so
   // each 32 x 32 accumulator holds the tile transposed: lane l has output row
   // (l & 31) and, for register r, output column 8*(r/4) + 4*(l/32) + r%4, i.e.
@@ -223,6 +227,15 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, floatx16_t (&ac
     const bf16x2_t v = {(__bf16)x, (__bf16)y};
     return __builtin_bit_cast(uint32_t, v);
   };
+  auto silu_mul = [](float g, float u) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u; };
+  // Extra rows (XR > 0), gate/up: the gate block of rows 256.. is held by
+  // wave (0, wp), the up block of the same hidden columns by wave (1, wp); the
+  // latter passes its accumulators through LDS, past the staged tile.
+  constexpr int kExOff = 80 * 1024;
+  static_assert(XR == 0 || MODE != kGateUp || (BM + XR) * OSTRIDE <= kExOff,
+                "staging overlaps the exchange area");
+  static_assert((BM + XR) * OSTRIDE <= LDS_BYTES, "staged tile exceeds the LDS");
+  float4* ex = reinterpret_cast<float4*>(lds_raw + kExOff) + wp * 256;
   __syncthreads();  // all fragment reads of the last stage are done
   if (any) {
 #pragma unroll
@@ -232,12 +245,14 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, floatx16_t (&ac
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (MODE == kGateUp) {
+          // with extra rows, waves of the second row half hold up in acc[m][0]
           float hv[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float g = acc[m][0][4 * q + j];
-            const float u = acc[m][1][4 * q + j];
-            hv[j] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+            const float v0 = acc[m][0][4 * q + j], v1 = acc[m][1][4 * q + j];
+            const float g = (XR > 0 && wg) ? v1 : v0;
+            const float u = (XR > 0 && wg) ? v0 : v1;
+            hv[j] = silu_mul(g, u);
           }
           *reinterpret_cast<uint2*>(lrow + (wp * 32 + 8 * q + ocol_l) * 2) =
               make_uint2(pack2(hv[0], hv[1]), pack2(hv[2], hv[3]));
@@ -251,17 +266,64 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, floatx16_t (&ac
         }
       }
     }
+    if constexpr (XR > 0) {
+      if (MODE == kGateUp) {
+        if (wg == 1) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            ex[q * 64 + lane] = make_float4(accx[4 * q], accx[4 * q + 1], accx[4 * q + 2],
+                                            accx[4 * q + 3]);
+        }
+      } else {
+        char* lrow = lds_raw + (BM + orow_l) * OSTRIDE;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<uint2*>(lrow + (b_row[0] + 8 * q + ocol_l) * 2) =
+              make_uint2(pack2(accx[4 * q], accx[4 * q + 1]),
+                         pack2(accx[4 * q + 2], accx[4 * q + 3]));
+      }
+    }
   }
   __syncthreads();
-  epilogue_store<MODE>(a, nt, row0, rows, tid, lds_raw);
+  if constexpr (XR > 0 && MODE == kGateUp) {
+    if (any && wg == 0) {
+      char* lrow = lds_raw + (BM + orow_l) * OSTRIDE;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 u = ex[q * 64 + lane];
+        *reinterpret_cast<uint2*>(lrow + (wp * 32 + 8 * q + ocol_l) * 2) =
+            make_uint2(pack2(silu_mul(accx[4 * q], u.x), silu_mul(accx[4 * q + 1], u.y)),
+                       pack2(silu_mul(accx[4 * q + 2], u.z), silu_mul(accx[4 * q + 3], u.w)));
+      }
+    }
+    __syncthreads();
+  }
+  epilogue_store<MODE, BM + XR>(a, nt, row0, rows, tid, lds_raw);
 }
 
 // One 256 x 256 output tile (m-tile mt, n-tile nt).  GROUPED: rows come from
 // the m-tile table (routed experts); otherwise the rows are
 // 0 .. rows_dense-1 (router, shared expert).
-template <int MODE, bool GROUPED>
+//
+// XR = 32: a grouped tile of 257 .. 288 rows (the last tile of an expert
+// segment, whose remainder rides along instead of streaming the expert's
+// weights once more).  The A slots hold 288 rows, so the B ring has two
+// slots (2 x 36 + 2 x 32 KB); each wave adds one 32 x 32 accumulator for rows
+// 256 .. 287 against the B fragment it already holds in b_row[0] (for
+// gate/up the waves of the second row half take the up rows there).  The
+// 32 extra A rows are one more load per wave and stage: waves 0-3 load them,
+// waves 4-7 issue the same instruction with no memory access into an unused
+// LDS area, so that every wave counts the same loads.
+template <int MODE, bool GROUPED, int XR = 0>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
                                           char* lds_raw) {
+  static_assert(XR == 0 || (XR == 32 && GROUPED && MODE != kRouter), "extra rows: grouped only");
+  constexpr int A_TILE = (BM + XR) * ROW_BYTES;          // bytes per A slot
+  constexpr int NB_SLOTS = XR ? 2 : B_SLOTS;
+  constexpr int B_BASE = A_SLOTS * A_TILE;               // byte offset of the B ring
+  constexpr int X_DUMMY = B_BASE + NB_SLOTS * TILE_BYTES;  // target of the idle loads
+  constexpr int NA_LD = XR ? 5 : 4;                      // A loads per wave and stage
+  static_assert(X_DUMMY + (XR ? 4096 : 0) <= LDS_BYTES, "LDS ring too large");
   int expert = 0;
   int64_t row0;
   int rows;
@@ -284,7 +346,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
   // ---- LDS-DMA assignment.  Per stage and operand each wave issues 4 loads;
   // load i covers tile rows r = 8*(8*i + wave) .. +7, lane l -> row +(l>>3),
   // LDS slot (l&7), which holds global chunk (l&7) ^ ((r >> 1) & 7); that is
-  // (l&7) ^ ((4*wave + (l>>4)) & 7) for every i.
+  // (l&7) ^ ((4*wave + (l>>4)) & 7) for every i.  The extra A load (XR) of
+  // waves 0-3 covers rows 256 + 8*wave .. +7, with the same chunk.
   const int sub = lane >> 3;
   const int chunk = (lane & 7) ^ ((4 * wave + (sub >> 1)) & 7);
   // Byte offsets of each lane's 16-byte piece, fixed for the whole tile; the
@@ -293,20 +356,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
   // buffer: the load returns zeros without a memory access, and those rows
   // are never stored.
   constexpr uint32_t kNoRow = 0xFFFFFFFFu - 16u * 1024u;  // past any 4 GiB buffer
-  uint32_t a_voff[4], b_voff[4];
+  uint32_t a_voff[NA_LD], b_voff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NA_LD; ++i) {
     const int r = 8 * (8 * i + wave) + sub;
-    if (r < rows) {
+    if (r < rows && (i < 4 || wave < 4)) {
       int64_t arow = row0 + r;
       if (GROUPED && a.gather) arow = a.gather[arow] / a.gather_div;
       a_voff[i] = (uint32_t)(arow * a.lda * 2) + (uint32_t)chunk * 16u;
     } else {
       a_voff[i] = kNoRow;
     }
-    const int brow = (MODE == kGateUp) ? nt * (BN / 2) + (r & (BN / 2 - 1)) : nt * BN + r;
-    b_voff[i] = (brow < a.b_rows) ? (uint32_t)brow * (uint32_t)a.kdim * 2u + (uint32_t)chunk * 16u
-                                  : kNoRow;
+    if (i < 4) {
+      const int brow = (MODE == kGateUp) ? nt * (BN / 2) + (r & (BN / 2 - 1)) : nt * BN + r;
+      b_voff[i] = (brow < a.b_rows) ? (uint32_t)brow * (uint32_t)a.kdim * 2u + (uint32_t)chunk * 16u
+                                    : kNoRow;
+    }
   }
   const uint32_t b_bytes = (uint32_t)a.b_rows * (uint32_t)a.kdim * 2u;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, a.a_bytes);
@@ -326,32 +391,41 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
   // fill the 128 gate rows of the B tile and loads 2 and 3 the up rows.
   auto dma_a = [&](int ks, int i) {
     const int j = 8 * i + wave;
-    dma16(ra, voff_at(a_voff[i], ks), (uint32_t)ks * (BK * 2),
-          (lds_void_t*)(lds_raw + (ks % A_SLOTS) * TILE_BYTES + j * 1024));
+    char* dst = (i < 4 || wave < 4) ? lds_raw + (ks % A_SLOTS) * A_TILE + j * 1024
+                                    : lds_raw + X_DUMMY + (wave - 4) * 1024;
+    dma16(ra, voff_at(a_voff[i], ks), (uint32_t)ks * (BK * 2), (lds_void_t*)dst);
   };
   auto dma_b = [&](int ks, int i) {
     const int j = 8 * i + wave;
     dma16((MODE == kGateUp && i >= 2) ? rb1 : rb0, voff_at(b_voff[i], ks),
           (uint32_t)ks * (BK * 2),
-          (lds_void_t*)(lds_raw + B_RING + (ks % B_SLOTS) * TILE_BYTES + j * 1024));
+          (lds_void_t*)(lds_raw + B_BASE + (ks % NB_SLOTS) * TILE_BYTES + j * 1024));
   };
 
   // ---- accumulators: wave (wg, wp) owns rows wg*128 .. +128 and two
   // 32-column blocks of the B rows: gate/up -> gate rows wp*32 and the up
-  // rows of the same hidden columns; otherwise B rows wp*64 .. +64.
+  // rows of the same hidden columns; otherwise B rows wp*64 .. +64.  With
+  // extra rows, b_row[0] is the block the wave multiplies rows 256.. with:
+  // the two halves of the wave's column range (down) or gate and up
+  // (gate/up) are taken by the two row halves.
   floatx16_t acc[4][2];
+  floatx16_t accx;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) accx[r] = 0.0f;
   int b_row[2];
   if (MODE == kGateUp) { b_row[0] = wp * 32; b_row[1] = BN / 2 + wp * 32; }
   else { b_row[0] = wp * 64; b_row[1] = wp * 64 + 32; }
+  if (XR > 0 && wg == 1) { const int t = b_row[0]; b_row[0] = b_row[1]; b_row[1] = t; }
   const int fr = lane & 31;
   const int a_base = (wg * 128 + fr) * ROW_BYTES;
-  const int b_base = B_RING + fr * ROW_BYTES;
+  const int x_base = (BM + fr) * ROW_BYTES;
+  const int b_base = B_BASE + fr * ROW_BYTES;
   // fragment rows start on multiples of 32, so (row >> 1) & 7 = (l >> 1) & 7
   auto slot_of = [&](int ks) { return ((2 * ks + (lane >> 5)) ^ ((lane >> 1) & 7)) * 16; };
 
@@ -363,6 +437,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
 
   typedef bf16x8_t afrag_t[4];
   typedef bf16x8_t bfrag_t[2];
+  using T = std::true_type;
+  using F = std::false_type;
+
+  auto read_frags = [&](afrag_t& A, bfrag_t& B, int kt, int ks, int q, auto live_tag) {
+    // fragments of quarter q (A frag q; B frag q for q < 2)
+    constexpr int LIVE = decltype(live_tag)::value;
+    const char* sa = lds_raw + (kt % A_SLOTS) * A_TILE;
+    const char* sbb = lds_raw + (kt % NB_SLOTS) * TILE_BYTES;
+    const int so = slot_of(ks);
+    if (q < LIVE)
+      A[q] = *reinterpret_cast<const bf16x8_t*>(sa + a_base + 32 * q * ROW_BYTES + so);
+    if (q < 2) B[q] = *reinterpret_cast<const bf16x8_t*>(sbb + b_base + b_row[q] * ROW_BYTES + so);
+  };
 
   // Schedule (every wave, whatever its MFMA work).  The prologue loads A0 B0
   // A1 B1 B2.  Stage kt runs four k-steps; the barrier at its last k-step
@@ -403,18 +490,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
     else if (nk > 1) wait_vmcnt<8>();
     else wait_vmcnt<0>();
     block_barrier();
-    auto read_frags = [&](afrag_t& A, bfrag_t& B, int kt, int ks, int q) {
-      // fragments of quarter q (A frag q; B frag q for q < 2)
-      const char* sa = lds_raw + (kt % A_SLOTS) * TILE_BYTES;
-      const char* sbb = lds_raw + (kt % B_SLOTS) * TILE_BYTES;
-      const int so = slot_of(ks);
-      if (q < LIVE)
-        A[q] = *reinterpret_cast<const bf16x8_t*>(sa + a_base + 32 * q * ROW_BYTES + so);
-      if (q < 2) B[q] = *reinterpret_cast<const bf16x8_t*>(sbb + b_base + b_row[q] * ROW_BYTES + so);
-    };
     if (LIVE > 0) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) read_frags(A0, B0, 0, 0, q);
+      for (int q = 0; q < 4; ++q) read_frags(A0, B0, 0, 0, q, live_tag);
     }
     // One stage.  The flags are bools (peeled stages) or std::integral_constant
     // (steady state):
@@ -448,8 +526,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
           if (ks == 1 && ld_b) dma_b(kt + 2, h2);
           if (ks == 2 && ld_b) dma_b(kt + 2, 2 + h2);
           if (LIVE > 0 && have_next) {
-            read_frags(An, Bn, nkt, nks, 2 * h2);
-            read_frags(An, Bn, nkt, nks, 2 * h2 + 1);
+            read_frags(An, Bn, nkt, nks, 2 * h2, live_tag);
+            read_frags(An, Bn, nkt, nks, 2 * h2 + 1, live_tag);
           }
           __builtin_amdgcn_sched_barrier(0);
           if (do_mfma) {
@@ -467,8 +545,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
         }
       }
     };
-    using T = std::true_type;
-    using F = std::false_type;
     // stage 0: its B(2) came with the prologue; A(1) is whole
     stage(0, nk > 2, F{}, F{}, nk > 1, nk > 2, nk == 1 && k_tail);
     // steady state: 1 <= kt <= nk-3
@@ -476,11 +552,116 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
     if (nk >= 3) stage(nk - 2, F{}, T{}, F{}, T{}, F{}, F{});
     if (nk >= 2) stage(nk - 1, F{}, F{}, F{}, F{}, F{}, k_tail);
   };
-  if (!any) run(std::integral_constant<int, 0>{});
-  else if (live_m > 2) run(std::integral_constant<int, 4>{});
-  else run(std::integral_constant<int, 2>{});
 
-  gemm_epilogue<MODE>(a, acc, nt, row0, rows, lane, wg, wp, tid, b_row, any, live_m, lds_raw);
+  // The same schedule with two B slots (extra rows).  B(kt+2) can only be
+  // loaded once every wave is done with slot kt%2, so A(kt+2) and B(kt+2)
+  // both follow the barrier of stage kt: loads 0,1 of each at once, the rest
+  // (A 2,3 and the extra load, B 2,3) in the first k-step of stage kt+1.
+  // The barrier of a stage then waits for every load in flight.  The extra
+  // A fragment of k-step s+1 is read with quarter 3 and its MFMA follows
+  // those of quarters 2 and 3.
+  auto run_x = [&](auto live_tag) {
+    constexpr int LIVE = decltype(live_tag)::value;
+    afrag_t A0, A1;
+    bfrag_t B0, B1;
+    bf16x8_t X0, X1;
+    auto read_x = [&](bf16x8_t& X, int kt, int ks) {
+      X = *reinterpret_cast<const bf16x8_t*>(lds_raw + (kt % A_SLOTS) * A_TILE + x_base +
+                                             slot_of(ks));
+    };
+#pragma unroll
+    for (int i = 0; i < NA_LD; ++i) dma_a(0, i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma_b(0, i);
+    if (nk > 1) {
+#pragma unroll
+      for (int i = 0; i < NA_LD; ++i) dma_a(1, i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma_b(1, i);
+    }
+    if (nk > 1) wait_vmcnt<NA_LD + 4>();
+    else wait_vmcnt<0>();
+    block_barrier();
+    if (LIVE > 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) read_frags(A0, B0, 0, 0, q, live_tag);
+      read_x(X0, 0, 0);
+    }
+    //   ld_2nd - loads A 2,3,4 and B 2,3 of stage kt+1 in the first k-step
+    //   ld_1st - loads 0,1 of A(kt+2) and B(kt+2) after the last barrier
+    //   next   - a next stage exists (barrier + its first fragments)
+    //   half   - the last 32 k of this stage are padding
+    auto stage = [&](int kt, auto ld_2nd, auto ld_1st, auto next, auto half) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        afrag_t& Ac = (ks & 1) ? A1 : A0;
+        bfrag_t& Bc = (ks & 1) ? B1 : B0;
+        bf16x8_t& Xc = (ks & 1) ? X1 : X0;
+        afrag_t& An = (ks & 1) ? A0 : A1;
+        bfrag_t& Bn = (ks & 1) ? B0 : B1;
+        bf16x8_t& Xn = (ks & 1) ? X0 : X1;
+        const int nkt = (ks == 3) ? kt + 1 : kt;
+        const int nks = (ks == 3) ? 0 : ks + 1;
+        const bool have_next = (ks < 3) || next;
+        if (ks == 3 && next) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          wait_vmcnt<0>();
+          block_barrier();  // every wave done with A slot kt%2 and B slot kt%2
+        }
+        const bool do_mfma = !(ks >= 2 && half);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          if (ks == 3 && ld_1st) {
+            dma_a(kt + 2, h2);
+            dma_b(kt + 2, h2);
+          }
+          if (ks == 0 && ld_2nd) {
+            dma_a(kt + 1, 2 + h2);
+            dma_b(kt + 1, 2 + h2);
+            if (h2 == 1) dma_a(kt + 1, 4);
+          }
+          if (LIVE > 0 && have_next) {
+            read_frags(An, Bn, nkt, nks, 2 * h2, live_tag);
+            read_frags(An, Bn, nkt, nks, 2 * h2 + 1, live_tag);
+            if (h2 == 1) read_x(Xn, nkt, nks);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (do_mfma) {
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm) {
+              const int m = 2 * h2 + mm;
+              if (m < LIVE) {
+#pragma unroll
+                for (int f = 0; f < 2; ++f)
+                  acc[m][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Bc[f], Ac[m], acc[m][f], 0, 0, 0);
+              }
+            }
+            if (h2 == 1 && LIVE > 0)
+              accx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Bc[0], Xc, accx, 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    // stage 0: A(1) and B(1) are whole from the prologue
+    stage(0, F{}, nk > 2, nk > 1, nk == 1 && k_tail);
+    for (int kt = 1; kt + 2 < nk; ++kt) stage(kt, T{}, T{}, T{}, F{});
+    if (nk >= 3) stage(nk - 2, T{}, F{}, T{}, F{});
+    if (nk >= 2) stage(nk - 1, F{}, F{}, F{}, k_tail);
+  };
+
+  if constexpr (XR > 0) {
+    // rows > 256: every wave has four live row blocks
+    if (!any) run_x(std::integral_constant<int, 0>{});
+    else run_x(std::integral_constant<int, 4>{});
+  } else {
+    if (!any) run(std::integral_constant<int, 0>{});
+    else if (live_m > 2) run(std::integral_constant<int, 4>{});
+    else run(std::integral_constant<int, 2>{});
+  }
+
+  gemm_epilogue<MODE, XR>(a, acc, accx, nt, row0, rows, lane, wg, wp, tid, b_row, any, live_m,
+                          lds_raw);
 }
 
 // ---------------------------------------------------------------- FP8 tiles
@@ -761,7 +942,15 @@ __global__ __launch_bounds__(512, 2) void gemm_kernel(GemmArgs a) {
   const int64_t m_tiles = GROUPED ? (int64_t)(*a.n_tiles) : (a.rows_dense + BM - 1) / BM;
   int64_t logical;
   if (!xcd_tile(m_tiles * a.n_tiles_n, logical)) return;
-  gemm_tile<MODE, GROUPED>(a, logical / a.n_tiles_n, (int)(logical % a.n_tiles_n), lds_raw);
+  const int64_t mt = logical / a.n_tiles_n;
+  const int nt = (int)(logical % a.n_tiles_n);
+  if constexpr (GROUPED && MODE != kRouter) {
+    if (reinterpret_cast<const int4*>(a.tiles)[mt].z > BM) {
+      gemm_tile<MODE, true, kXRows>(a, mt, nt, lds_raw);
+      return;
+    }
+  }
+  gemm_tile<MODE, GROUPED>(a, mt, nt, lds_raw);
 }
 
 // The two products over x before routing in one launch: the router logits

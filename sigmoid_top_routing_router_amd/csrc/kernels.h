@@ -57,7 +57,8 @@ struct PermWork {
 int perm_chunk_pairs();
 int64_t perm_num_chunks(int64_t pairs);
 int64_t perm_max_tiles(int64_t pairs, int E, int bm);
-hipError_t launch_permute(const int32_t* ids, int64_t N, int E, int K, int bm,
+// Tiles hold bm rows; the last tile of a segment up to bm + xr rows.
+hipError_t launch_permute(const int32_t* ids, int64_t N, int E, int K, int bm, int xr,
                           const PermWork& w, hipStream_t stream);
 // Expert loads only (no permutation): counts[E] must be a device buffer.
 hipError_t launch_count(const int32_t* ids, int64_t pairs, int E, int32_t* counts,
@@ -83,6 +84,9 @@ hipError_t launch_down(const uint16_t* H, int64_t h_rows, const int32_t* tiles, 
                        int64_t max_tiles, int64_t rows_dense, const uint16_t* w_down,
                        int d, int h, uint16_t* Y, hipStream_t stream);
 int gemm_bm();
+// Rows beyond gemm_bm() that one grouped bf16 m-tile may hold (the FP8 tiles
+// hold gemm_bm() rows at most).
+int gemm_xrows();
 // Router logits and the shared expert's gate/up in one launch (both read x).
 hipError_t launch_router_shared_gateup(const uint16_t* x, int64_t N, int d,
                                        const uint16_t* w_router, const float* offset, int E,

@@ -16,7 +16,10 @@
 //     into exclusive chunk bases and the expert total.
 //  3. perm_tiles_kernel: one block; exclusive sums of the counts (offsets)
 //     by a block-wide scan, and the table of m-tiles (expert, first row, rows)
-//     that drives the grouped GEMMs from device memory.
+//     that drives the grouped GEMMs from device memory.  A segment is cut
+//     into tiles of bm rows, except that its last tile takes up to bm + xr
+//     rows: a remainder of at most xr rows rides with the tile before it
+//     instead of streaming the expert's weights once more.
 //  4. perm_scatter_kernel: one wave per chunk walks its pairs in order, 64 at
 //     a time; lanes holding the same expert are found with nine ballots over
 //     the bits of the expert id, so the rank among them is a popcount and the
@@ -33,6 +36,28 @@ constexpr int kMaxE = 384;
 int perm_chunk_pairs() { return kChunk; }
 int64_t perm_num_chunks(int64_t pairs) { return (pairs + kChunk - 1) / kChunk; }
 int64_t perm_max_tiles(int64_t pairs, int E, int bm) { return pairs / bm + E; }
+
+// Number of m-tiles of a segment of c rows: bm rows each, the last one up to
+// bm + xr rows (never more tiles than ceil(c / bm)).
+__device__ __forceinline__ uint32_t seg_tiles(uint32_t c, int bm, int xr) {
+  if (c == 0u) return 0u;
+  if (c <= (uint32_t)(bm + xr)) return 1u;
+  return (c - (uint32_t)xr + (uint32_t)bm - 1u) / (uint32_t)bm;
+}
+
+// Writes the nt m-tiles of expert e (segment start off, c rows) at t0.
+__device__ __forceinline__ void emit_tiles(int32_t* tiles, uint32_t t0, int e, uint32_t off,
+                                           uint32_t c, uint32_t nt, int bm) {
+  for (uint32_t i = 0; i < nt; ++i) {
+    const uint32_t r = i * (uint32_t)bm;
+    int4 ent;
+    ent.x = e;
+    ent.y = (int32_t)(off + r);
+    ent.z = (int32_t)(i + 1 == nt ? c - r : (uint32_t)bm);
+    ent.w = (int32_t)r;
+    reinterpret_cast<int4*>(tiles)[t0 + i] = ent;
+  }
+}
 
 __global__ __launch_bounds__(256) void perm_count_kernel(
     const int32_t* __restrict__ ids, int64_t pairs, int E, int64_t n_chunks,
@@ -83,7 +108,7 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(uint32_t* __restrict__ c
 // table.  Thread i owns experts 2i and 2i+1 (E <= 512); a block-wide scan in
 // thread order gives the sums in expert order.
 __global__ __launch_bounds__(256) void perm_tiles_kernel(const int32_t* __restrict__ counts,
-                                                         int E, int bm,
+                                                         int E, int bm, int xr,
                                                          int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ tiles,
                                                          int32_t* __restrict__ n_tiles) {
@@ -92,7 +117,7 @@ __global__ __launch_bounds__(256) void perm_tiles_kernel(const int32_t* __restri
   const int e0 = 2 * tid, e1 = 2 * tid + 1;
   const uint32_t c0 = e0 < E ? (uint32_t)counts[e0] : 0u;
   const uint32_t c1 = e1 < E ? (uint32_t)counts[e1] : 0u;
-  const uint32_t t0 = (c0 + bm - 1) / bm, t1 = (c1 + bm - 1) / bm;
+  const uint32_t t0 = seg_tiles(c0, bm, xr), t1 = seg_tiles(c1, bm, xr);
   const uint32_t ic = wave_inclusive_sum_u32(c0 + c1);
   const uint32_t it = wave_inclusive_sum_u32(t0 + t1);
   if (lane == kWave - 1) { wsum_c[w] = ic; wsum_t[w] = it; }
@@ -104,20 +129,14 @@ __global__ __launch_bounds__(256) void perm_tiles_kernel(const int32_t* __restri
     offsets[E] = (int32_t)(bc + ic);
     *n_tiles = (int32_t)(bt + it);
   }
-  auto emit = [&](int e, uint32_t c, uint32_t off, uint32_t toff) {
-    offsets[e] = (int32_t)off;
-    uint32_t t = toff;
-    for (uint32_t r = 0; r < c; r += bm, ++t) {
-      int4 ent;
-      ent.x = e;
-      ent.y = (int32_t)(off + r);
-      ent.z = (int32_t)min((uint32_t)bm, c - r);
-      ent.w = (int32_t)r;
-      reinterpret_cast<int4*>(tiles)[t] = ent;
-    }
-  };
-  if (e0 < E) emit(e0, c0, off0, toff0);
-  if (e1 < E) emit(e1, c1, off0 + c0, toff0 + t0);
+  if (e0 < E) {
+    offsets[e0] = (int32_t)off0;
+    emit_tiles(tiles, toff0, e0, off0, c0, t0, bm);
+  }
+  if (e1 < E) {
+    offsets[e1] = (int32_t)(off0 + c0);
+    emit_tiles(tiles, toff0 + t0, e1, off0 + c0, c1, t1, bm);
+  }
 }
 
 __global__ __launch_bounds__(256) void perm_scatter_kernel(
@@ -185,7 +204,7 @@ constexpr int kSmallWaves = 16;
 constexpr int64_t kSmallPairs = 16384;
 
 __global__ __launch_bounds__(1024) void perm_small_kernel(
-    const int32_t* __restrict__ ids, int64_t pairs, int E, int bm,
+    const int32_t* __restrict__ ids, int64_t pairs, int E, int bm, int xr,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_src, int32_t* __restrict__ src_pos,
     int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
@@ -214,7 +233,7 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(
   // (3) offsets and the m-tile table: a scan in expert order; E <= 384 fits
   // one expert per thread of the first 384 threads (7 waves)
   const uint32_t c = tid < E ? tot[tid] : 0u;
-  const uint32_t t = (c + bm - 1) / bm;
+  const uint32_t t = seg_tiles(c, bm, xr);
   const uint32_t ic = wave_inclusive_sum_u32(c);
   const uint32_t it = wave_inclusive_sum_u32(t);
   if (lane == kWave - 1) { wsum_c[w] = ic; wsum_t[w] = it; }
@@ -230,14 +249,7 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(
   if (tid < E) {
     counts[tid] = (int32_t)c;
     offsets[tid] = (int32_t)off;
-    for (uint32_t r = 0; r < c; r += bm, ++toff) {
-      int4 ent;
-      ent.x = tid;
-      ent.y = (int32_t)(off + r);
-      ent.z = (int32_t)min((uint32_t)bm, c - r);
-      ent.w = (int32_t)r;
-      reinterpret_cast<int4*>(tiles)[toff] = ent;
-    }
+    emit_tiles(tiles, toff, tid, off, c, t, bm);
     tot[tid] = off;  // segment starts, for the scatter
   }
   __syncthreads();
@@ -267,11 +279,11 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(
   }
 }
 
-hipError_t launch_permute(const int32_t* ids, int64_t N, int E, int K, int bm,
+hipError_t launch_permute(const int32_t* ids, int64_t N, int E, int K, int bm, int xr,
                           const PermWork& w, hipStream_t stream) {
   const int64_t pairs = N * (int64_t)K;
   if (pairs <= kSmallPairs) {
-    hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(1024), 0, stream, ids, pairs, E, bm,
+    hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(1024), 0, stream, ids, pairs, E, bm, xr,
                        w.counts, w.offsets, w.sorted_src, w.src_pos, w.tiles, w.n_tiles);
     return hipGetLastError();
   }
@@ -282,7 +294,7 @@ hipError_t launch_permute(const int32_t* ids, int64_t N, int E, int K, int bm,
                      w.chunk_counts);
   hipLaunchKernelGGL(perm_scan_kernel, dim3((unsigned)E), block, 0, stream, w.chunk_counts,
                      n_chunks, w.counts);
-  hipLaunchKernelGGL(perm_tiles_kernel, dim3(1), block, 0, stream, w.counts, E, bm, w.offsets,
+  hipLaunchKernelGGL(perm_tiles_kernel, dim3(1), block, 0, stream, w.counts, E, bm, xr, w.offsets,
                      w.tiles, w.n_tiles);
   hipLaunchKernelGGL(perm_scatter_kernel, cgrid, block, 0, stream, ids, pairs, E, n_chunks,
                      w.chunk_counts, w.offsets, w.sorted_src, w.src_pos);

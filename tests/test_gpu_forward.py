@@ -162,6 +162,26 @@ def test_forward_small_batch_concentrated(M):
         assert A["counts"][0] == N and A["counts"][1] == N
 
 
+# Expert loads just above a multiple of 256 rows: the last m-tile of such a
+# segment holds up to 288 rows (the extra-rows tile), larger remainders get
+# a tile of their own.  The loads of each case (from the oracle's routing):
+#  a) 286 284 284 276 262 256 278 274      - single 288-row tiles, one 256
+#  b) 542 520 502 530 534 508 507 557      - 256 + extra-rows tiles, 256+256+45
+#  c) 2891 2687 1817 719 393 108 59 26     - many tiles, a 281-row last tile
+#  d) 251 280 285 278 277 274 277 278
+# d and h set the k loops (gate/up, down): 192/160 -> 3/3 stages with a 32-k
+# tail in down, 64/160 -> 1/3, 128/96 -> 2/2 (b_rows = 128 leaves whole
+# waves of the down tile without columns), 576/352 -> 9/6 (steady state).
+@pytest.mark.parametrize("N,K,offset,d,h", [(1100, 2, None, 192, 160), (2100, 2, None, 64, 160),
+                                            (2900, 3, "zipf1.2", 128, 96),
+                                            (1100, 2, None, 576, 352)])
+def test_forward_tail_rows(M, N, K, offset, d, h):
+    cfg = replace(CONFIGS["toy"], name=f"tail_{N}_{K}_{d}", N=N, d=d, E=8, K=K, h=h,
+                  h_shared=h, offset=offset, recompute_bias=offset is None, dtype="bf16")
+    _, A = run_case(M, cfg)
+    assert np.any((A["counts"] % 256 > 0) & (A["counts"] % 256 <= 32) & (A["counts"] > 256))
+
+
 def test_forward_without_shared_expert(M):
     cfg = replace(scaled(CONFIGS["prefill"], 200), n_shared=0, name="noshared")
     run_case(M, cfg)
