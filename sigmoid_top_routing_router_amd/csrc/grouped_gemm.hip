@@ -307,23 +307,26 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, floatx16_t (&ac
 //
 // XR = 32: a grouped tile of 257 .. 288 rows (the last tile of an expert
 // segment, whose remainder rides along instead of streaming the expert's
-// weights once more).  The A slots hold 288 rows, so the B ring has two
-// slots (2 x 36 + 2 x 32 KB); each wave adds one 32 x 32 accumulator for rows
-// 256 .. 287 against the B fragment it already holds in b_row[0] (for
-// gate/up the waves of the second row half take the up rows there).  The
-// 32 extra A rows are one more load per wave and stage: waves 0-3 load them,
-// waves 4-7 issue the same instruction with no memory access into an unused
-// LDS area, so that every wave counts the same loads.
+// weights once more).  The A slots hold 288 rows (2 x 36 KB), which leaves
+// 88 KB for B: the B ring is kept in quarters (64 B rows, 8 KB) and has 11 of
+// them, so stage s occupies quarters 4s .. 4s+3 mod 11.  Each wave adds one
+// 32 x 32 accumulator for rows 256 .. 287 against the B fragment it already
+// holds in b_row[0] (for gate/up the waves of the second row half take the
+// up rows there).  The 32 extra A rows are one more load per wave and stage:
+// waves 0-3 load them and waves 4-7 repeat those loads (same rows, same LDS
+// bytes), so that every wave counts the same loads.
 template <int MODE, bool GROUPED, int XR = 0>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
                                           char* lds_raw) {
   static_assert(XR == 0 || (XR == 32 && GROUPED && MODE != kRouter), "extra rows: grouped only");
   constexpr int A_TILE = (BM + XR) * ROW_BYTES;          // bytes per A slot
-  constexpr int NB_SLOTS = XR ? 2 : B_SLOTS;
   constexpr int B_BASE = A_SLOTS * A_TILE;               // byte offset of the B ring
-  constexpr int X_DUMMY = B_BASE + NB_SLOTS * TILE_BYTES;  // target of the idle loads
+  constexpr int QUARTER = 64 * ROW_BYTES;                // 64 B rows of one stage
+  constexpr int NB_Q = XR ? 11 : 4 * B_SLOTS;            // quarters in the B ring
   constexpr int NA_LD = XR ? 5 : 4;                      // A loads per wave and stage
-  static_assert(X_DUMMY + (XR ? 4096 : 0) <= LDS_BYTES, "LDS ring too large");
+  static_assert(B_BASE + NB_Q * QUARTER <= LDS_BYTES, "LDS ring too large");
+  // ring position of quarter j of stage kt
+  auto bq = [](int kt, int j) { return XR ? (4 * kt + j) % NB_Q : (kt % B_SLOTS) * 4 + j; };
   int expert = 0;
   int64_t row0;
   int rows;
@@ -359,8 +362,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
   uint32_t a_voff[NA_LD], b_voff[4];
 #pragma unroll
   for (int i = 0; i < NA_LD; ++i) {
-    const int r = 8 * (8 * i + wave) + sub;
-    if (r < rows && (i < 4 || wave < 4)) {
+    const int r = (i < 4) ? 8 * (8 * i + wave) + sub : BM + 8 * (wave & 3) + sub;
+    if (r < rows) {
       int64_t arow = row0 + r;
       if (GROUPED && a.gather) arow = a.gather[arow] / a.gather_div;
       a_voff[i] = (uint32_t)(arow * a.lda * 2) + (uint32_t)chunk * 16u;
@@ -390,16 +393,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
   // load i covers tile rows 8*(8*i + wave) .. +7; for gate/up, loads 0 and 1
   // fill the 128 gate rows of the B tile and loads 2 and 3 the up rows.
   auto dma_a = [&](int ks, int i) {
-    const int j = 8 * i + wave;
-    char* dst = (i < 4 || wave < 4) ? lds_raw + (ks % A_SLOTS) * A_TILE + j * 1024
-                                    : lds_raw + X_DUMMY + (wave - 4) * 1024;
-    dma16(ra, voff_at(a_voff[i], ks), (uint32_t)ks * (BK * 2), (lds_void_t*)dst);
+    const int j = (i < 4) ? 8 * i + wave : 32 + (wave & 3);
+    dma16(ra, voff_at(a_voff[i], ks), (uint32_t)ks * (BK * 2),
+          (lds_void_t*)(lds_raw + (ks % A_SLOTS) * A_TILE + j * 1024));
   };
+  // B load i of stage ks fills quarter i (B rows 64*i .. +63)
   auto dma_b = [&](int ks, int i) {
-    const int j = 8 * i + wave;
     dma16((MODE == kGateUp && i >= 2) ? rb1 : rb0, voff_at(b_voff[i], ks),
           (uint32_t)ks * (BK * 2),
-          (lds_void_t*)(lds_raw + B_BASE + (ks % NB_SLOTS) * TILE_BYTES + j * 1024));
+          (lds_void_t*)(lds_raw + B_BASE + bq(ks, i) * QUARTER + wave * 1024));
   };
 
   // ---- accumulators: wave (wg, wp) owns rows wg*128 .. +128 and two
@@ -425,7 +427,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
   const int fr = lane & 31;
   const int a_base = (wg * 128 + fr) * ROW_BYTES;
   const int x_base = (BM + fr) * ROW_BYTES;
-  const int b_base = B_BASE + fr * ROW_BYTES;
+  const int b_off[2] = {((b_row[0] & 63) + fr) * ROW_BYTES, ((b_row[1] & 63) + fr) * ROW_BYTES};
   // fragment rows start on multiples of 32, so (row >> 1) & 7 = (l >> 1) & 7
   auto slot_of = [&](int ks) { return ((2 * ks + (lane >> 5)) ^ ((lane >> 1) & 7)) * 16; };
 
@@ -444,21 +446,26 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
     // fragments of quarter q (A frag q; B frag q for q < 2)
     constexpr int LIVE = decltype(live_tag)::value;
     const char* sa = lds_raw + (kt % A_SLOTS) * A_TILE;
-    const char* sbb = lds_raw + (kt % NB_SLOTS) * TILE_BYTES;
     const int so = slot_of(ks);
     if (q < LIVE)
       A[q] = *reinterpret_cast<const bf16x8_t*>(sa + a_base + 32 * q * ROW_BYTES + so);
-    if (q < 2) B[q] = *reinterpret_cast<const bf16x8_t*>(sbb + b_base + b_row[q] * ROW_BYTES + so);
+    if (q < 2)
+      B[q] = *reinterpret_cast<const bf16x8_t*>(lds_raw + B_BASE + bq(kt, b_row[q] >> 6) * QUARTER +
+                                                b_off[q] + so);
   };
 
   // Schedule (every wave, whatever its MFMA work).  The prologue loads A0 B0
   // A1 B1 B2.  Stage kt runs four k-steps; the barrier at its last k-step
-  // releases A slot kt%2 and B slot kt%3, after which the loads of A(kt+2)
-  // (two instructions at once, two in the next stage's first k-step) and of
-  // B(kt+3) (two per k-step in that stage's second and third k-steps) are
-  // issued, each pinned with scheduling barriers next to the LDS reads of
+  // releases A slot kt%2 and the B quarters of stage kt, after which the
+  // loads of A(kt+2) (two instructions at once, the rest in the next stage's
+  // first k-step) and of B(kt+3) (in that stage's second and third k-steps)
+  // are issued, each pinned with scheduling barriers next to the LDS reads of
   // the next k-step's fragments.  Two waves share each SIMD, so one wave's
-  // loads and LDS reads overlap the other's MFMAs.
+  // loads and LDS reads overlap the other's MFMAs.  With extra rows the B ring
+  // is one quarter short of three stages: quarter 3 of stage kt+2 only frees
+  // at the barrier of stage kt, so it is loaded in the second k-step of stage
+  // kt+1, ahead of quarters 0-2 of B(kt+3), and the barrier waits for three
+  // loads instead of four.
   //
   // The steady-state stages (1 <= kt <= nk-3) are compiled without any
   // branch: every condition below is a compile-time constant there, so the
@@ -470,101 +477,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
   // never stored.
   auto run = [&](auto live_tag) {
     constexpr int LIVE = decltype(live_tag)::value;
+    constexpr int NB3 = XR ? 3 : 4;  // B(kt+3) loads issued ahead of the barrier
     afrag_t A0, A1;
     bfrag_t B0, B1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma_a(0, i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dma_b(0, i);
-    if (nk > 1) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dma_a(1, i);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dma_b(1, i);
-    }
-    if (nk > 2) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dma_b(2, i);
-    }
-    if (nk > 2) wait_vmcnt<12>();
-    else if (nk > 1) wait_vmcnt<8>();
-    else wait_vmcnt<0>();
-    block_barrier();
-    if (LIVE > 0) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) read_frags(A0, B0, 0, 0, q, live_tag);
-    }
-    // One stage.  The flags are bools (peeled stages) or std::integral_constant
-    // (steady state):
-    //   ld_a2  - loads 0,1 of A(kt+2) after the last barrier of this stage
-    //   ld_a1  - loads 2,3 of A(kt+1) in the first k-step
-    //   ld_b   - the four loads of B(kt+2) in k-steps 1 and 2
-    //   next   - a next stage exists (barrier + its first fragments)
-    //   vm4    - at the barrier the four B(kt+2) loads may still be in flight
-    //   half   - the last 32 k of this stage are padding
-    auto stage = [&](int kt, auto ld_a2, auto ld_a1, auto ld_b, auto next, auto vm4,
-                     auto half) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        afrag_t& Ac = (ks & 1) ? A1 : A0;
-        bfrag_t& Bc = (ks & 1) ? B1 : B0;
-        afrag_t& An = (ks & 1) ? A0 : A1;
-        bfrag_t& Bn = (ks & 1) ? B0 : B1;
-        const int nkt = (ks == 3) ? kt + 1 : kt;
-        const int nks = (ks == 3) ? 0 : ks + 1;
-        const bool have_next = (ks < 3) || next;
-        if (ks == 3 && next) {
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-          if (vm4) wait_vmcnt<4>(); else wait_vmcnt<0>();
-          block_barrier();  // every wave done with A slot kt%2 and B slot kt%3
-        }
-        const bool do_mfma = !(ks >= 2 && half);
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          if (ks == 3 && ld_a2) dma_a(kt + 2, h2);
-          if (ks == 0 && ld_a1) dma_a(kt + 1, 2 + h2);
-          if (ks == 1 && ld_b) dma_b(kt + 2, h2);
-          if (ks == 2 && ld_b) dma_b(kt + 2, 2 + h2);
-          if (LIVE > 0 && have_next) {
-            read_frags(An, Bn, nkt, nks, 2 * h2, live_tag);
-            read_frags(An, Bn, nkt, nks, 2 * h2 + 1, live_tag);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          if (do_mfma) {
-#pragma unroll
-            for (int mm = 0; mm < 2; ++mm) {
-              const int m = 2 * h2 + mm;
-              if (m < LIVE) {
-#pragma unroll
-                for (int f = 0; f < 2; ++f)
-                  acc[m][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Bc[f], Ac[m], acc[m][f], 0, 0, 0);
-              }
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    };
-    // stage 0: its B(2) came with the prologue; A(1) is whole
-    stage(0, nk > 2, F{}, F{}, nk > 1, nk > 2, nk == 1 && k_tail);
-    // steady state: 1 <= kt <= nk-3
-    for (int kt = 1; kt + 2 < nk; ++kt) stage(kt, T{}, T{}, T{}, T{}, T{}, F{});
-    if (nk >= 3) stage(nk - 2, F{}, T{}, F{}, T{}, F{}, F{});
-    if (nk >= 2) stage(nk - 1, F{}, F{}, F{}, F{}, F{}, k_tail);
-  };
-
-  // The same schedule with two B slots (extra rows).  B(kt+2) can only be
-  // loaded once every wave is done with slot kt%2, so A(kt+2) and B(kt+2)
-  // both follow the barrier of stage kt: loads 0,1 of each at once, the rest
-  // (A 2,3 and the extra load, B 2,3) in the first k-step of stage kt+1.
-  // The barrier of a stage then waits for every load in flight.  The extra
-  // A fragment of k-step s+1 is read with quarter 3 and its MFMA follows
-  // those of quarters 2 and 3.
-  auto run_x = [&](auto live_tag) {
-    constexpr int LIVE = decltype(live_tag)::value;
-    afrag_t A0, A1;
-    bfrag_t B0, B1;
-    bf16x8_t X0, X1;
+    bf16x8_t X0, X1;  // extra-row A fragments
     auto read_x = [&](bf16x8_t& X, int kt, int ks) {
       X = *reinterpret_cast<const bf16x8_t*>(lds_raw + (kt % A_SLOTS) * A_TILE + x_base +
                                              slot_of(ks));
@@ -579,19 +495,30 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
 #pragma unroll
       for (int i = 0; i < 4; ++i) dma_b(1, i);
     }
-    if (nk > 1) wait_vmcnt<NA_LD + 4>();
+    if (nk > 2) {
+#pragma unroll
+      for (int i = 0; i < NB3; ++i) dma_b(2, i);
+    }
+    if (nk > 2) wait_vmcnt<NA_LD + 4 + NB3>();
+    else if (nk > 1) wait_vmcnt<NA_LD + 4>();
     else wait_vmcnt<0>();
     block_barrier();
     if (LIVE > 0) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) read_frags(A0, B0, 0, 0, q, live_tag);
-      read_x(X0, 0, 0);
+      if (XR > 0) read_x(X0, 0, 0);
     }
-    //   ld_2nd - loads A 2,3,4 and B 2,3 of stage kt+1 in the first k-step
-    //   ld_1st - loads 0,1 of A(kt+2) and B(kt+2) after the last barrier
+    // One stage.  The flags are bools (peeled stages) or std::integral_constant
+    // (steady state):
+    //   ld_a2  - loads 0,1 of A(kt+2) after the last barrier of this stage
+    //   ld_a1  - the other loads of A(kt+1) in the first k-step (with extra
+    //            rows also quarter 3 of B(kt+1) in the second)
+    //   ld_b   - the loads of B(kt+2) in k-steps 1 and 2
     //   next   - a next stage exists (barrier + its first fragments)
+    //   vmb    - at the barrier the B(kt+2) loads may still be in flight
     //   half   - the last 32 k of this stage are padding
-    auto stage = [&](int kt, auto ld_2nd, auto ld_1st, auto next, auto half) {
+    auto stage = [&](int kt, auto ld_a2, auto ld_a1, auto ld_b, auto next, auto vmb,
+                     auto half) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         afrag_t& Ac = (ks & 1) ? A1 : A0;
@@ -605,25 +532,29 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
         const bool have_next = (ks < 3) || next;
         if (ks == 3 && next) {
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-          wait_vmcnt<0>();
-          block_barrier();  // every wave done with A slot kt%2 and B slot kt%2
+          if (vmb) wait_vmcnt<NB3>(); else wait_vmcnt<0>();
+          block_barrier();  // every wave done with A slot kt%2 and the B quarters of kt
         }
         const bool do_mfma = !(ks >= 2 && half);
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          if (ks == 3 && ld_1st) {
-            dma_a(kt + 2, h2);
-            dma_b(kt + 2, h2);
-          }
-          if (ks == 0 && ld_2nd) {
+          if (ks == 3 && ld_a2) dma_a(kt + 2, h2);
+          if (ks == 0 && ld_a1) {
             dma_a(kt + 1, 2 + h2);
-            dma_b(kt + 1, 2 + h2);
-            if (h2 == 1) dma_a(kt + 1, 4);
+            if (XR > 0 && h2 == 1) dma_a(kt + 1, 4);
+          }
+          if (XR > 0) {
+            if (ks == 1 && h2 == 0 && ld_a1) dma_b(kt + 1, 3);
+            if (ks == 1 && h2 == 1 && ld_b) dma_b(kt + 2, 0);
+            if (ks == 2 && ld_b) dma_b(kt + 2, 1 + h2);
+          } else {
+            if (ks == 1 && ld_b) dma_b(kt + 2, h2);
+            if (ks == 2 && ld_b) dma_b(kt + 2, 2 + h2);
           }
           if (LIVE > 0 && have_next) {
             read_frags(An, Bn, nkt, nks, 2 * h2, live_tag);
             read_frags(An, Bn, nkt, nks, 2 * h2 + 1, live_tag);
-            if (h2 == 1) read_x(Xn, nkt, nks);
+            if (XR > 0 && h2 == 1) read_x(Xn, nkt, nks);
           }
           __builtin_amdgcn_sched_barrier(0);
           if (do_mfma) {
@@ -636,24 +567,24 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
                   acc[m][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Bc[f], Ac[m], acc[m][f], 0, 0, 0);
               }
             }
-            if (h2 == 1 && LIVE > 0)
+            if (XR > 0 && h2 == 1 && LIVE > 0)
               accx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Bc[0], Xc, accx, 0, 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     };
-    // stage 0: A(1) and B(1) are whole from the prologue
-    stage(0, F{}, nk > 2, nk > 1, nk == 1 && k_tail);
-    for (int kt = 1; kt + 2 < nk; ++kt) stage(kt, T{}, T{}, T{}, F{});
-    if (nk >= 3) stage(nk - 2, T{}, F{}, T{}, F{});
-    if (nk >= 2) stage(nk - 1, F{}, F{}, F{}, k_tail);
+    // stage 0: its B(2) came with the prologue; A(1) and B(1) are whole
+    stage(0, nk > 2, F{}, F{}, nk > 1, nk > 2, nk == 1 && k_tail);
+    // steady state: 1 <= kt <= nk-3
+    for (int kt = 1; kt + 2 < nk; ++kt) stage(kt, T{}, T{}, T{}, T{}, T{}, F{});
+    if (nk >= 3) stage(nk - 2, F{}, T{}, F{}, T{}, F{}, F{});
+    if (nk >= 2) stage(nk - 1, F{}, F{}, F{}, F{}, F{}, k_tail);
   };
-
   if constexpr (XR > 0) {
     // rows > 256: every wave has four live row blocks
-    if (!any) run_x(std::integral_constant<int, 0>{});
-    else run_x(std::integral_constant<int, 4>{});
+    if (!any) run(std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 4>{});
   } else {
     if (!any) run(std::integral_constant<int, 0>{});
     else if (live_m > 2) run(std::integral_constant<int, 4>{});
