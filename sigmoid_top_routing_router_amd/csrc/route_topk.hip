@@ -174,10 +174,27 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 // holds the experts 4g + 64j + c (c < 4, j < NC), read as float4, so one wave
 // selects four rows at once and every cross-lane step is a 16-lane DPP row
 // (the lane maxima, the K+1 pops that give L) or a ballot masked to the row.
-// Per row this issues about a third of the one-wave kernel's instructions,
-// which was bound by them.  Rows past N (the last quad) re-read row N-1 and
-// store nothing.
-template <int NC>
+// Rows past N (the last quad) re-read row N-1 and store nothing.  FULL: E is
+// 64 * NC, so no lane holds a slot past E.  The next quad's rows load while
+// this quad is selected.
+//
+// Keys: the bias is read once as beta + 0, which turns -0 into +0.  Under
+// round to nearest a sum is -0 only when both operands are -0, so no biased
+// score z + b is -0 and the order-preserving map needs no test for it (the
+// two zeros share a key, as in f32_order_key).  The sigmoid weight
+// is evaluated in fp32 (relative error a few ulp, within the 1e-6 of the
+// weights); logits below -80, where e^-z nears the fp32 range, take the fp64
+// form.
+__device__ __forceinline__ uint32_t order_key_nonneg_zero(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ float sigmoid_weight(float z) {
+  if (z < -80.0f) return (float)(1.0 / (1.0 + exp(-(double)z)));
+  return 1.0f / (1.0f + expf(-z));
+}
+
+template <int NC, bool FULL>
 __global__ __launch_bounds__(256) void route_group_kernel(
     const float* __restrict__ Z, const float* __restrict__ beta, int64_t N, int E, int K,
     int32_t* __restrict__ ids, float* __restrict__ S, float* __restrict__ alpha,
@@ -200,7 +217,7 @@ __global__ __launch_bounds__(256) void route_group_kernel(
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int e = 4 * g + 64 * j + c;
-      bv[4 * j + c] = (beta && e < E) ? beta[e] : 0.0f;
+      bv[4 * j + c] = (beta && (FULL || e < E)) ? beta[e] + 0.0f : 0.0f;
     }
   auto load_row = [&](int64_t q, float4 (&v)[NC]) {
     const int64_t r = min(q * 4 + grp, N - 1);
@@ -208,20 +225,17 @@ __global__ __launch_bounds__(256) void route_group_kernel(
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
       const int e0 = 4 * g + 64 * j;
-      v[j] = (e0 < E) ? *reinterpret_cast<const float4*>(zr + e0) : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[j] = (FULL || e0 < E) ? *reinterpret_cast<const float4*>(zr + e0)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
-  float4 cur[NC], nxt[NC];
-  load_row(quad, cur);
   const uint64_t gmask = 0xFFFFull << (16 * grp);
   uint64_t* cl = cand[wib][grp];
   uint32_t* kl = kk[wib][grp];
-  for (; quad < nquads; quad += nwaves) {
-    const int64_t nq = quad + nwaves;
-    if (nq < nquads) load_row(nq, nxt);
-    const int64_t row = quad * 4 + grp;
-    const bool row_ok = row < N;
 
+  auto select = [&](int64_t q, const float4 (&cur)[NC]) {
+    const int64_t row = q * 4 + grp;
+    const bool row_ok = row < N;
     uint32_t key[NVL];
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
@@ -229,7 +243,7 @@ __global__ __launch_bounds__(256) void route_group_kernel(
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int e = 4 * g + 64 * j + c;
-        key[4 * j + c] = (e < E) ? f32_order_key(zc[c] + bv[4 * j + c]) : 0u;
+        key[4 * j + c] = (FULL || e < E) ? order_key_nonneg_zero(zc[c] + bv[4 * j + c]) : 0u;
       }
     }
     // (1) L = the (K+1)-th largest of the row's 16 lane maxima (with
@@ -278,10 +292,7 @@ __global__ __launch_bounds__(256) void route_group_kernel(
       if (row_ok && rank < (uint32_t)K) {
         const uint32_t e = 0xFFFFFFFFu - (uint32_t)ci;
         if (ids) ids[row * K + rank] = (int32_t)e;
-        if (S) {
-          const float z = Z[row * (int64_t)E + e];
-          S[row * K + rank] = (float)(1.0 / (1.0 + exp(-(double)z)));
-        }
+        if (S) S[row * K + rank] = sigmoid_weight(Z[row * (int64_t)E + e]);
       }
       if (rank == (uint32_t)K - 1) kl[0] = (uint32_t)(ci >> 32);
       if (rank == (uint32_t)K) kl[1] = (uint32_t)(ci >> 32);
@@ -297,6 +308,14 @@ __global__ __launch_bounds__(256) void route_group_kernel(
     // the next quad's candidates overwrite this quad's lists
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_wave_barrier();
+  };
+
+  float4 cur[NC], nxt[NC];
+  load_row(quad, cur);
+  for (; quad < nquads; quad += nwaves) {
+    const int64_t nq = quad + nwaves;
+    if (nq < nquads) load_row(nq, nxt);
+    select(quad, cur);
 #pragma unroll
     for (int j = 0; j < NC; ++j) cur[j] = nxt[j];
   }
@@ -315,7 +334,7 @@ static int64_t route_resident_blocks(int nv, int kind) {
   switch (nv) {
 #define MOE_ROUTE_FN(V)                                                        \
     case V:                                                                    \
-      fn = kind == 2 ? (const void*)route_group_kernel<V>                      \
+      fn = kind == 2 ? (const void*)route_group_kernel<V, false>               \
            : kind == 1 ? (const void*)route_topk_kernel<V, true>               \
                        : (const void*)route_topk_kernel<V, false>;             \
       break;
@@ -348,8 +367,12 @@ hipError_t launch_route(const float* Z, const float* beta, int64_t N, int E, int
     switch (nv) {
 #define MOE_ROUTE_GROUP_CASE(V)                                                           \
       case V:                                                                             \
-        hipLaunchKernelGGL((route_group_kernel<V>), grid, block, 0, stream, Z, beta, N, E, K, \
-                           ids, S, alpha, margin);                                        \
+        if (E == 64 * V)                                                                  \
+          hipLaunchKernelGGL((route_group_kernel<V, true>), grid, block, 0, stream, Z, beta, N, \
+                             E, K, ids, S, alpha, margin);                                \
+        else                                                                              \
+          hipLaunchKernelGGL((route_group_kernel<V, false>), grid, block, 0, stream, Z, beta, \
+                             N, E, K, ids, S, alpha, margin);                             \
         break;
       MOE_ROUTE_GROUP_CASE(1) MOE_ROUTE_GROUP_CASE(2) MOE_ROUTE_GROUP_CASE(3)
       MOE_ROUTE_GROUP_CASE(4) MOE_ROUTE_GROUP_CASE(5) MOE_ROUTE_GROUP_CASE(6)
