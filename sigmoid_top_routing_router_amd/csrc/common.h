@@ -34,13 +34,28 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
 }
 // Order-preserving 16-bit key of a bf16 pattern (-0 folded onto +0).
+// 16-bit order-preserving key of a bfloat16 value b (low 16 bits): zero and
+// positive b map to 0x8000 + |b|, negative b to 0x8000 - |b|, so -0 and +0
+// share 0x8000.
 __device__ __forceinline__ uint32_t bf16_order_key(uint32_t b) {
-  b &= 0xFFFFu;
-  if (b == 0x8000u) b = 0u;
-  return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+  const uint32_t m = b & 0x7FFFu;
+  return (b & 0x8000u) ? (0x8000u - m) : (0x8000u | m);
 }
 __device__ __forceinline__ uint32_t bf16_from_order_key(uint32_t k) {
-  return (k & 0x8000u) ? (k ^ 0x8000u) : (~k & 0xFFFFu);
+  k &= 0xFFFFu;
+  return (k & 0x8000u) ? (k & 0x7FFFu) : (0x8000u | (0x8000u - k));
+}
+// The keys of two bfloat16 values packed in one word (low and high half), with
+// 16-bit packed integer operations: ~b + 1 for negative halves (0x7FFF - |b|
+// + 1), b ^ 0x8000 for the others.
+__device__ __forceinline__ uint32_t bf16_order_key2(uint32_t p) {
+  typedef short s16x2_t __attribute__((ext_vector_type(2)));
+  typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+  const s16x2_t sgn = __builtin_bit_cast(s16x2_t, p) >> (short)15;  // 0 or -1 per half
+  const uint32_t su = __builtin_bit_cast(uint32_t, sgn);
+  const u16x2_t k = __builtin_bit_cast(u16x2_t, p ^ (su | 0x80008000u)) -
+                    __builtin_bit_cast(u16x2_t, sgn);
+  return __builtin_bit_cast(uint32_t, k);
 }
 
 // ---------------------------------------------------------------- DPP

@@ -41,10 +41,10 @@ size_t eqb_hist_bytes(int E, int key_bits) {
 }
 size_t eqb_state_bytes(int E) { return (size_t)(2 * E + 4) * sizeof(uint32_t); }
 
-template <int KB>
+template <int KB, int PASS>
 __global__ __launch_bounds__(kEqbThreads) void eqb_hist_kernel(
     const float* __restrict__ Z, const float* __restrict__ alpha, int64_t N, int E,
-    int pass, int64_t rows_per_block, const uint32_t* __restrict__ prefix,
+    int64_t rows_per_block, const uint32_t* __restrict__ prefix,
     uint32_t* __restrict__ hist) {
   __shared__ uint32_t lh[kEqbCols * kEqbPad];
   __shared__ int lo_s[kEqbRowLanes][kEqbCols], hi_s[kEqbRowLanes][kEqbCols];
@@ -54,23 +54,24 @@ __global__ __launch_bounds__(kEqbThreads) void eqb_hist_kernel(
   for (int i = threadIdx.x; i < kEqbCols * kEqbPad; i += kEqbThreads) lh[i] = 0u;
   __syncthreads();
 
-  const int shift = KB - 8 * (pass + 1);
+  constexpr int shift = KB - 8 * (PASS + 1);
   const bool col_ok = e < E;
-  const uint32_t want = (pass > 0 && col_ok) ? prefix[e] : 0u;
+  const uint32_t want = (PASS > 0 && col_ok) ? prefix[e] : 0u;
   const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
   const int64_t r1 = min(N, r0 + rows_per_block);
   int lo = 256, hi = -1;
   if (col_ok) {
     uint32_t* my = lh + cl * kEqbPad;
-    auto count = [&](float v) {
-      const uint32_t key = (KB == 16) ? bf16_order_key(f32_to_bf16_rne_bits(v))
-                                      : f32_order_key(v);
-      if (pass == 0 || (key >> (shift + 8)) == want) {
+    auto bump = [&](uint32_t key) {  // key: the KB-bit order key of one value
+      if (PASS == 0 || (key >> (shift + 8)) == want) {
         const int b = (int)((key >> shift) & 0xFFu);
         atomicAdd(my + b, 1u);
         lo = min(lo, b);
         hi = max(hi, b);
       }
+    };
+    auto key_of = [&](float v) {
+      return (KB == 16) ? bf16_order_key(f32_to_bf16_rne_bits(v)) : f32_order_key(v);
     };
     int64_t t = r0 + rs;
     constexpr int kTrip = kEqbUnroll * kEqbRowLanes;
@@ -81,10 +82,23 @@ __global__ __launch_bounds__(kEqbThreads) void eqb_hist_kernel(
         z[u] = Z[(t + kEqbRowLanes * u) * E + e];
         al[u] = alpha[t + kEqbRowLanes * u];
       }
+      if constexpr (KB == 16) {
+        // two rows per conversion (v_cvt_pk_bf16_f32, round to nearest even)
+        // and per packed key
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
-      for (int u = 0; u < kEqbUnroll; ++u) count(z[u] + al[u]);
+        for (int u = 0; u < kEqbUnroll; u += 2) {
+          const bf16x2_t bb = {(__bf16)(z[u] + al[u]), (__bf16)(z[u + 1] + al[u + 1])};
+          const uint32_t k2 = bf16_order_key2(__builtin_bit_cast(uint32_t, bb));
+          bump(k2 & 0xFFFFu);
+          bump(k2 >> 16);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kEqbUnroll; ++u) bump(key_of(z[u] + al[u]));
+      }
     }
-    for (; t < r1; t += kEqbRowLanes) count(Z[t * E + e] + alpha[t]);
+    for (; t < r1; t += kEqbRowLanes) bump(key_of(Z[t * E + e] + alpha[t]));
   }
   lo_s[rs][cl] = lo;
   hi_s[rs][cl] = hi;
@@ -186,12 +200,23 @@ hipError_t launch_eqb_hist(const float* Z, const float* alpha, int64_t N, int E,
   const int64_t rows_per_block = eqb_rows_per_block(N, E);
   const int64_t chunks = (N + rows_per_block - 1) / rows_per_block;
   const dim3 grid((unsigned)col_groups, (unsigned)chunks), block(kEqbThreads);
-  if (key_bits == 16)
-    hipLaunchKernelGGL(eqb_hist_kernel<16>, grid, block, 0, stream, Z, alpha, N, E, pass,
-                       rows_per_block, prefix, hist_pass);
-  else
-    hipLaunchKernelGGL(eqb_hist_kernel<32>, grid, block, 0, stream, Z, alpha, N, E, pass,
-                       rows_per_block, prefix, hist_pass);
+#define MOE_EQB_HIST(KB, P)                                                                  \
+  hipLaunchKernelGGL((eqb_hist_kernel<KB, P>), grid, block, 0, stream, Z, alpha, N, E,     \
+                     rows_per_block, prefix, hist_pass)
+  if (key_bits == 16) {
+    if (pass == 0) MOE_EQB_HIST(16, 0);
+    else if (pass == 1) MOE_EQB_HIST(16, 1);
+    else return hipErrorInvalidValue;
+  } else {
+    switch (pass) {
+      case 0: MOE_EQB_HIST(32, 0); break;
+      case 1: MOE_EQB_HIST(32, 1); break;
+      case 2: MOE_EQB_HIST(32, 2); break;
+      case 3: MOE_EQB_HIST(32, 3); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+#undef MOE_EQB_HIST
   return hipGetLastError();
 }
 

@@ -140,6 +140,54 @@ def test_eqb_parity_full_size(M, key_bits):
     assert ((u > q[None, :]).sum(0) <= r).all() and ((u >= q[None, :]).sum(0) > r).all()
 
 
+def _signed_zero_logits(seed, N, E):
+    """Columns with a block of ones, a cluster of signed zeros and values
+    that round to a bfloat16 zero (+-1e-41) or to a negative bfloat16
+    subnormal (-3e-39), and -1 below; the block of ones grows with the
+    column (period 12) so that the wanted rank falls at different places of
+    the cluster."""
+    rng = np.random.default_rng(seed)
+    pattern = np.array([0.0, -0.0, -1e-41, 1e-41, -3e-39], np.float32)
+    Z = np.full((N, E), -1.0, np.float32)
+    for e in range(E):
+        ones = 2 * (e % 12)
+        Z[:ones, e] = 1.0
+        Z[ones:ones + 30, e] = pattern[rng.integers(0, 5, 30)]
+        Z[:, e] = Z[rng.permutation(N), e]
+    return Z
+
+
+@pytest.mark.parametrize("key_bits", [16, 32])
+def test_eqb_signed_zeros_and_subnormals(M, key_bits):
+    """-0 and +0 are one value of the selection (bfloat16 keys also merge
+    the values that round to -0); the quantile lands in the zero cluster."""
+    say("eqb signed zeros", key_bits)
+    N, E, K = 64, 8, 2  # r = 16
+    Z = _signed_zero_logits(221, N, E)
+    alpha = np.zeros(N, np.float32)
+    alpha[::3] = -0.0
+    bo, q = M.eqb_bias(dev(Z), K, alpha=dev(alpha), key_bits=key_bits)
+    bo, q = host(bo), host(q)
+    rb, rq, _ = O.eqb_expert_bias(Z, alpha, K, key_bits)
+    assert bits_equal(q, rq), (q, rq)
+    assert bits_equal(bo, rb)
+    assert np.any(q == 0.0)
+
+
+def test_route_signed_zeros(M):
+    """Logits and biases with both zeros: -0 + -0 is the only -0 sum, and it
+    ties with +0 (ids by expert order, alpha and margin bit-exact)."""
+    say("route signed zeros")
+    Z = _signed_zero_logits(222, 64, 8)
+    beta = np.array([-0.0, 0.0, -0.0, 0.0, -0.0, -0.0, 0.0, 0.0], np.float32)
+    for K in (1, 2, 5):
+        _route_case(M, Z, beta, K)
+    # the 384-wide kernel (16 lanes per row) on the same kind of data
+    Z = _signed_zero_logits(223, 200, 384)
+    beta = np.where(np.arange(384) % 2 == 0, -0.0, 0.0).astype(np.float32)
+    _route_case(M, Z, beta, 6)
+
+
 @pytest.mark.parametrize("key_bits", [16, 32])
 def test_eqb_printed_toy(M, key_bits):
     g = json.load(open(GOLD))
