@@ -155,6 +155,33 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& a, int nt, int64_
     return;
   }
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+  if constexpr (MODE == kDown) {
+    // Every LDS read of the tile first, then the stores: a lane keeps one
+    // 16-byte chunk column (512 % CPR == 0) and up to TROWS / 16 rows of it.
+    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+    constexpr int ITERS = (TROWS * CPR + 511) / 512;
+    const int ch = tid % CPR;
+    const int col = col0 + ch * 8;
+    u32x2_t lo[ITERS], hi[ITERS];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int rr = (tid + it * 512) / CPR;
+      if (rr < rows) {
+        const char* src = lds_raw + rr * OSTRIDE + ch * 16;  // 8-byte aligned
+        lo[it] = *reinterpret_cast<const u32x2_t*>(src);
+        hi[it] = *reinterpret_cast<const u32x2_t*>(src + 8);
+      }
+    }
+    if (col >= a.b_rows) return;
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int rr = (tid + it * 512) / CPR;
+      if (rr < rows)
+        *reinterpret_cast<uint4*>(out + (row0 + rr) * a.ldo + col) =
+            make_uint4(lo[it].x, lo[it].y, hi[it].x, hi[it].y);
+    }
+    return;
+  }
   for (int c = tid; c < TROWS * CPR; c += 512) {
     const int rr = c / CPR, ch = c % CPR;
     if (rr >= rows) break;  // chunks are walked in row order
