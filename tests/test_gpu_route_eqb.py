@@ -188,6 +188,21 @@ def test_route_signed_zeros(M):
     _route_case(M, Z, beta, 6)
 
 
+@pytest.mark.parametrize("E", [384, 100, 383])
+def test_route_extreme_logits(M, E):
+    """Very negative logits: mixture weights near the bottom of the fp32
+    range (z around -100, where the weight is a subnormal float) and far
+    below 1 but normal (z around -50), for the 16-lanes-per-row kernel
+    (E = 384 and 100) and the one-wave kernel (E = 383)."""
+    say("route extreme logits", E)
+    rng = np.random.default_rng(224)
+    Z = rng.standard_normal((200, E)).astype(np.float32)
+    Z[:100] -= 100.0
+    Z[100:] -= 50.0
+    beta = make_bias(225, E, 0.1)
+    _route_case(M, Z, beta, 6)
+
+
 @pytest.mark.parametrize("key_bits", [16, 32])
 def test_eqb_printed_toy(M, key_bits):
     g = json.load(open(GOLD))
