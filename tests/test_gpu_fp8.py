@@ -181,6 +181,21 @@ def test_forward_fp8_small_batch_concentrated(M):
         run_fp8_case(M, cfg)
 
 
+# Loads just above a multiple of 256 rows: the E4M3 tiles keep 256 rows, so
+# every remainder, short or long, is an m-tile of its own.  Loads (oracle):
+#  a) 282 251 286 280 286 257 271 287       - 256 + short tails, one 251
+#  b) 533 533 508 531 527 512 530 526       - 2 x 256 + short tails, one 252
+#  c) 2891 2687 1817 719 393 108 59 26      - long segments, tails of both kinds
+#  d) 1481 1221 799 452 250 132 91 74       - as c, d = 256 and h = 128
+@pytest.mark.parametrize("N,K,offset,d,h", [(1100, 2, None, 256, 256), (2100, 2, None, 128, 128),
+                                            (2900, 3, "zipf1.2", 128, 256),
+                                            (1500, 3, "zipf1.2", 256, 128)])
+def test_forward_fp8_segment_tails(M, N, K, offset, d, h):
+    cfg = replace(CONFIGS["toy"], name=f"fp8_tail_{N}_{K}_{d}_{h}", N=N, d=d, E=8, K=K, h=h,
+                  h_shared=h, offset=offset, recompute_bias=offset is None, dtype="bf16")
+    run_fp8_case(M, cfg)
+
+
 def test_forward_fp8_prefill_full_sampled(M):
     """The Kolibri-shaped prefill batch (N=16384, E=384, K=6, d=2560, h=512),
     sampled tokens."""
