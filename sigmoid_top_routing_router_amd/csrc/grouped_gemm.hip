@@ -46,6 +46,8 @@
 //  * Ragged segments: an m-tile table (expert, first row, rows) produced on
 //    the device by the grouping kernels drives the grid; the grid is sized
 //    for the worst case and surplus blocks exit after reading the tile count.
+//    The last tile of a segment may hold up to 288 rows; such tiles run a
+//    variant with 288-row A slots (see gemm_tile).
 //    Waves skip the MFMAs of 32-row blocks that hold no valid rows; rows past
 //    the segment (and B rows past the matrix) load zeros through an offset
 //    beyond the buffer and are never stored.
