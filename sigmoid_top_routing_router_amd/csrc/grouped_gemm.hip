@@ -654,7 +654,7 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
   }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar descriptors
   const int wg = wave >> 2;
   const int wp = wave & 3;
   const int sub = lane >> 3;
@@ -683,15 +683,25 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
   const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(B08 + (int64_t)expert * a.b_expert_stride, b_bytes);
   const __amdgpu_buffer_rsrc_t rb1 = make_rsrc(B18 + (int64_t)expert * a.b_expert_stride, b_bytes);
   const int nk = a.kdim / 128;
+  // LDS: A ring of two 32 KB slots; B ring of 11 quarters (64 B rows, 8 KB),
+  // stage s in quarters 4s .. 4s+3 mod 11; then two 1.5 KB slots of scales
+  // (with the A ring's parity): the 256 row scales of A, and 64 copies each
+  // of the two weight-block scales the tile uses.
+  constexpr int QUARTER = 8 * 1024;
+  constexpr int NB_Q = 11;
+  constexpr int B_BASE8 = A_SLOTS * TILE_BYTES;
+  constexpr int SC_BASE = B_BASE8 + NB_Q * QUARTER;
+  constexpr int SC_SLOT = 1536;
+  static_assert(SC_BASE + 2 * SC_SLOT <= LDS_BYTES, "LDS layout");
+  auto bq = [](int kt, int j) { return (4 * kt + j) % NB_Q; };
   auto dma_a = [&](int ks, int i) {
     const int j = 8 * i + wave;
     dma16(ra, a_voff[i], (uint32_t)ks * 128u,
           (lds_void_t*)(lds_raw + (ks % A_SLOTS) * TILE_BYTES + j * 1024));
   };
-  auto dma_b = [&](int ks, int i) {
-    const int j = 8 * i + wave;
+  auto dma_b = [&](int ks, int i) {  // quarter i: B rows 64*i .. +63
     dma16((MODE == kGateUp && i >= 2) ? rb1 : rb0, b_voff[i], (uint32_t)ks * 128u,
-          (lds_void_t*)(lds_raw + B_RING + (ks % B_SLOTS) * TILE_BYTES + j * 1024));
+          (lds_void_t*)(lds_raw + B_BASE8 + bq(ks, i) * QUARTER + wave * 1024));
   };
 
   // ---- accumulators: wave (wg, wp) owns tile rows wg*128 .. +128 as eight
@@ -718,126 +728,153 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
   const bool live_n = (MODE == kGateUp) ? true : (nt * BN + wp * 64) < a.b_rows;
   const bool any = __builtin_amdgcn_readfirstlane((live_m > 0 && live_n) ? 1 : 0) != 0;
 
-  // ---- scales.  Row block m of a lane is tile row wg*128 + 16*m + (l & 15),
-  // so the four lanes with the same l & 15 share their eight rows: lane l
-  // loads the activation scales of blocks m = 2*(l>>4) and +1 (its A rows,
-  // through the gather for the routed gate/up) and the others read them
-  // across lanes.  Gate/up column blocks take the gate (f < 2) or up
-  // (f >= 2) weight block nt; the 64 down columns of a wave lie in one
-  // 128-row weight block.  Offsets fit 32 bits: rows * kdim < 4 GiB.
+  // ---- scales, staged through LDS with 4-byte LDS-DMA loads (one per wave
+  // and stage, so every wave counts the same loads).  Waves 0-3: lane l
+  // loads the scale of tile row 64*wave + l (through the gather for the
+  // routed gate/up; rows past the segment load zero).  Waves 4, 5: the first
+  // weight-block scale of the tile (gate block nt; down: the block of
+  // columns 0-127), waves 6, 7: the second (up block nt; down: columns
+  // 128-255); the two waves of a pair write the same bytes.  Offsets fit 32
+  // bits: rows * kdim < 4 GiB.
   const int nkb = nk;
-  uint32_t sa_off[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int rr = wg * 128 + (2 * quad + j) * 16 + fr;
-    int64_t arow = row0 + (rr < rows ? rr : 0);
-    if (GROUPED && a.gather) arow = a.gather[arow] / a.gather_div;
-    sa_off[j] = (uint32_t)arow * (uint32_t)nkb;
-  }
   const int nblk = (a.b_rows + 127) / 128;
-  const int bblk = (MODE == kGateUp) ? nt : min((nt * BN + wp * 64) / 128, nblk - 1);
-  const float* sbp0 = a.sb0 + (int64_t)expert * a.sb_es + (int64_t)bblk * nkb;
-  const float* sbp1 = ((MODE == kGateUp) ? a.sb1 : a.sb0) + (int64_t)expert * a.sb_es +
-                      (int64_t)bblk * nkb;
+  uint32_t sc_voff;
+  __amdgpu_buffer_rsrc_t rsc;
+  if (wave < 4) {
+    const int r = 64 * wave + lane;
+    if (r < rows) {
+      int64_t arow = row0 + r;
+      if (GROUPED && a.gather) arow = a.gather[arow] / a.gather_div;
+      sc_voff = (uint32_t)arow * (uint32_t)nkb * 4u;
+    } else {
+      sc_voff = kNoRow;
+    }
+    rsc = make_rsrc(a.sa, a.a_bytes / 128u * 4u);
+  } else {
+    const int second = wave >= 6 ? 1 : 0;
+    const int bblk = (MODE == kGateUp) ? nt : min(2 * nt + second, nblk - 1);
+    const float* base = (MODE == kGateUp && second) ? a.sb1 : a.sb0;
+    sc_voff = (uint32_t)(((int64_t)expert * a.sb_es + (int64_t)bblk * nkb) * 4);
+    rsc = make_rsrc(base, 0xFFFFFFF0u);
+  }
+  auto dma_sc = [&](int ks) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsc, (lds_void_t*)(lds_raw + SC_BASE + (ks % 2) * SC_SLOT + (wave < 6 ? 0 : 256) +
+                           (wave < 4 ? wave * 256 : 1024)),
+        4, sc_voff, (uint32_t)ks * 4u, 0, 0);
+  };
 
-  // Schedule: the prologue loads A0 B0 A1 B1 B2.  Stage kt first loads the
-  // scales of stage kt+1, then A(kt+1) rows 2,3 and B(kt+2), and after its
-  // closing barrier (A slot kt%2 and B slot kt%3 free) A(kt+2) rows 0,1.  The
-  // scale loads are issued before the operand loads of the stage, so the
-  // closing wait for all but the last four loads covers them.  LIVE (0, 2 or
-  // 4) is the number of 32-row halves of its rows this wave multiplies.
+  // Schedule (the bf16 engine's, with one MFMA per 16 x 16 block and stage):
+  // the prologue loads A0 B0 A1 B1 and quarters 0-2 of B2 (with the scales of
+  // stages 0 and 1).  Stage kt loads the rest of A(kt+1) and quarter 3 of
+  // B(kt+1), then quarters 0-2 of B(kt+2), spread over its row blocks; its
+  // closing barrier waits for all but those three and is followed by loads
+  // 0,1 of A(kt+2) and its scales.  The steady-state stages are compiled
+  // without branches, so the waits stay exact.  LIVE (0, 2 or 4) is the
+  // number of 32-row halves of its rows this wave multiplies.
   auto run = [&](auto live_tag) {
     constexpr int LIVE = decltype(live_tag)::value;
     constexpr int MB = 2 * LIVE;  // 16-row blocks
-    constexpr int NS = (MODE == kGateUp) ? 2 : 1;
-    float sa_n[2] = {0.f, 0.f}, sb_n[2] = {0.f, 0.f};
-    auto load_scales = [&](int kt) {
+    const int s0 = ((2 * quad) ^ ((lane >> 1) & 7)) * 16;
+    const int s1 = ((2 * quad + 1) ^ ((lane >> 1) & 7)) * 16;
+    // lane l reads 32 bytes of its row: chunks 2*(l>>4) and +1 (swizzled;
+    // fragments start on multiples of 16 rows, so (row >> 1) & 7 =
+    // (l >> 1) & 7)
+    auto frag = [&](const char* rowp) {
+      typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(rowp + s0);
+      const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(rowp + s1);
+      return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+    i32x8_t Bf[4], Af[2];
+    float sa_r[8], sb_r[2];
+    auto a_row = [&](int kt, int m) {
+      return lds_raw + (kt % A_SLOTS) * TILE_BYTES + (wg * 128 + 16 * m + fr) * ROW_BYTES;
+    };
+    auto read_stage = [&](int kt) {  // B fragments, A block 0 and the scales of stage kt
       if (MB > 0) {
-        sa_n[0] = a.sa[sa_off[0] + kt];
-        sa_n[1] = a.sa[sa_off[1] + kt];
-        sb_n[0] = sbp0[kt];
-        if (NS > 1) sb_n[1] = sbp1[kt];
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          Bf[f] = frag(lds_raw + B_BASE8 + bq(kt, b_col[f] >> 6) * QUARTER +
+                       ((b_col[f] & 63) + fr) * ROW_BYTES);
+        Af[0] = frag(a_row(kt, 0));
+        const char* sc = lds_raw + SC_BASE + (kt % 2) * SC_SLOT;
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+          sa_r[m] = *reinterpret_cast<const float*>(sc + (wg * 128 + 16 * m + fr) * 4);
+        sb_r[0] = *reinterpret_cast<const float*>(sc + 1024);
+        sb_r[1] = *reinterpret_cast<const float*>(sc + 1280);
       }
     };
-    load_scales(0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma_a(0, i);
+    dma_sc(0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma_b(0, i);
     if (nk > 1) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) dma_a(1, i);
+      dma_sc(1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) dma_b(1, i);
     }
     if (nk > 2) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma_b(2, i);
+      for (int i = 0; i < 3; ++i) dma_b(2, i);
     }
     if (nk > 2) wait_vmcnt<12>();
-    else if (nk > 1) wait_vmcnt<8>();
+    else if (nk > 1) wait_vmcnt<9>();
     else wait_vmcnt<0>();
     block_barrier();
-
-    for (int kt = 0; kt < nk; ++kt) {
-      float sa_c[2], sb_c[2];
-      sa_c[0] = sa_n[0];
-      sa_c[1] = sa_n[1];
-      sb_c[0] = sb_n[0];
-      sb_c[1] = sb_n[1];
-      if (kt + 1 < nk) load_scales(kt + 1);
-      if (kt >= 1 && kt + 1 < nk) { dma_a(kt + 1, 2); dma_a(kt + 1, 3); }
-      if (kt >= 1 && kt + 2 < nk) {
+    read_stage(0);
+    //   ld_a2 - loads 0,1 of A(kt+2) and its scales after the closing barrier
+    //   ld_a1 - loads 2,3 of A(kt+1) and quarter 3 of B(kt+1)
+    //   ld_b  - quarters 0-2 of B(kt+2)
+    //   next  - a next stage exists (barrier + its fragments)
+    //   vmb   - at the barrier the B(kt+2) quarters may still be in flight
+    auto stage = [&](int kt, auto ld_a2, auto ld_a1, auto ld_b, auto next, auto vmb) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma_b(kt + 2, i);
-      }
-      if (MB > 0) {
-        const char* sa_lds = lds_raw + (kt % A_SLOTS) * TILE_BYTES;
-        const char* sb_lds = lds_raw + B_RING + (kt % B_SLOTS) * TILE_BYTES;
-        // lane l reads 32 bytes of its row: chunks 2*(l>>4) and +1 (swizzled;
-        // fragments start on multiples of 16 rows, so (row >> 1) & 7 =
-        // (l >> 1) & 7)
-        const int s0 = ((2 * quad) ^ ((lane >> 1) & 7)) * 16;
-        const int s1 = ((2 * quad + 1) ^ ((lane >> 1) & 7)) * 16;
-        auto frag = [&](const char* rowp) {
-          const uint4 lo = *reinterpret_cast<const uint4*>(rowp + s0);
-          const uint4 hi = *reinterpret_cast<const uint4*>(rowp + s1);
-          return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        };
-        i32x8_t Bf[4], Af[2];
-#pragma unroll
-        for (int f = 0; f < 4; ++f) Bf[f] = frag(sb_lds + (b_col[f] + fr) * ROW_BYTES);
-        const char* a_rows = sa_lds + (wg * 128 + fr) * ROW_BYTES;
-        Af[0] = frag(a_rows);
-        // block m+1's fragment is read while block m multiplies; the
-        // scheduling barriers keep the compiler from hoisting further reads
-#pragma unroll
-        for (int m = 0; m < MB; ++m) {
-          __builtin_amdgcn_sched_barrier(0);
-          const float sa_m = __shfl(sa_c[m & 1], fr + 16 * (m >> 1));
-          if (m + 1 < MB) Af[(m + 1) & 1] = frag(a_rows + (m + 1) * 16 * ROW_BYTES);
+      for (int m = 0; m < 8; ++m) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (m == 1 && ld_a1) { dma_a(kt + 1, 2); dma_a(kt + 1, 3); }
+        if (m == 3 && ld_a1) dma_b(kt + 1, 3);
+        if (m == 3 && ld_b) dma_b(kt + 2, 0);
+        if (m == 5 && ld_b) { dma_b(kt + 2, 1); dma_b(kt + 2, 2); }
+        if (m < MB) {
+          if (m + 1 < MB) Af[(m + 1) & 1] = frag(a_row(kt, m + 1));
 #pragma unroll
           for (int f = 0; f < 4; ++f) {
             const floatx4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 Bf[f], Af[m & 1], floatx4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-            const float fac = sa_m * sb_c[(NS > 1) ? (f >> 1) : 0];
+            const float fac = sa_r[m] * sb_r[(MODE == kGateUp) ? (f >> 1) : (wp >> 1)];
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[m][f][r] = fmaf(p[r], fac, acc[m][f][r]);
             // keeps the compiler from sinking the FMAs below later blocks'
             // MFMAs, which would hold every product live at once
             asm volatile("" : "+v"(acc[m][f]));
           }
-          __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (kt + 1 < nk) {
+      if (next) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (kt >= 1 && kt + 2 < nk) wait_vmcnt<4>(); else wait_vmcnt<0>();
-        block_barrier();  // every wave done with A slot kt%2 and B slot kt%3
-        if (kt + 2 < nk) { dma_a(kt + 2, 0); dma_a(kt + 2, 1); }
+        if (vmb) wait_vmcnt<3>(); else wait_vmcnt<0>();
+        block_barrier();  // every wave done with A slot kt%2, B(kt) and the scales of kt
+        if (ld_a2) {
+          dma_a(kt + 2, 0);
+          dma_a(kt + 2, 1);
+          dma_sc(kt + 2);
+        }
+        read_stage(kt + 1);
       }
-    }
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    stage(0, nk > 2, F{}, F{}, nk > 1, nk > 2);
+    for (int kt = 1; kt + 2 < nk; ++kt) stage(kt, T{}, T{}, T{}, T{}, T{});
+    if (nk >= 3) stage(nk - 2, F{}, T{}, F{}, T{}, F{});
+    if (nk >= 2) stage(nk - 1, F{}, F{}, F{}, F{}, F{});
   };
   if (!any) run(std::integral_constant<int, 0>{});
   else if (live_m <= 2) run(std::integral_constant<int, 2>{});
