@@ -371,7 +371,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;          // 0..7; waves w and w+4 share a SIMD
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7; w and w+4 share a SIMD
   const int wg = wave >> 2;           // row half of the tile
   const int wp = wave & 3;            // column quarter of the tile
 
