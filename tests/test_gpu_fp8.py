@@ -187,9 +187,13 @@ def test_forward_fp8_small_batch_concentrated(M):
 #  b) 533 533 508 531 527 512 530 526       - 2 x 256 + short tails, one 252
 #  c) 2891 2687 1817 719 393 108 59 26      - long segments, tails of both kinds
 #  d) 1481 1221 799 452 250 132 91 74       - as c, d = 256 and h = 128
+#  e) N = 900, d = h = 384: three 128-k stages (first, middle, last, no
+#     steady state) in both products
+# The other cases give 1 and 2 stages; the full-size prefill test 20 and 4.
 @pytest.mark.parametrize("N,K,offset,d,h", [(1100, 2, None, 256, 256), (2100, 2, None, 128, 128),
                                             (2900, 3, "zipf1.2", 128, 256),
-                                            (1500, 3, "zipf1.2", 256, 128)])
+                                            (1500, 3, "zipf1.2", 256, 128),
+                                            (900, 2, None, 384, 384)])
 def test_forward_fp8_segment_tails(M, N, K, offset, d, h):
     cfg = replace(CONFIGS["toy"], name=f"fp8_tail_{N}_{K}_{d}_{h}", N=N, d=d, E=8, K=K, h=h,
                   h_shared=h, offset=offset, recompute_bias=offset is None, dtype="bf16")
