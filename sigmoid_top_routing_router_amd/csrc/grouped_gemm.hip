@@ -341,9 +341,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, floatx16_t (&ac
 // them, so stage s occupies quarters 4s .. 4s+3 mod 11.  Each wave adds one
 // 32 x 32 accumulator for rows 256 .. 287 against the B fragment it already
 // holds in b_row[0] (for gate/up the waves of the second row half take the
-// up rows there).  The 32 extra A rows are one more load per wave and stage:
-// waves 0-3 load them and waves 4-7 repeat those loads (same rows, same LDS
-// bytes), so that every wave counts the same loads.
+// up rows there).  The 32 extra A rows are one more load per wave and stage,
+// four rows from half of the wave's lanes.
 template <int MODE, bool GROUPED, int XR = 0>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
                                           char* lds_raw) {
@@ -379,7 +378,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
   // load i covers tile rows r = 8*(8*i + wave) .. +7, lane l -> row +(l>>3),
   // LDS slot (l&7), which holds global chunk (l&7) ^ ((r >> 1) & 7); that is
   // (l&7) ^ ((4*wave + (l>>4)) & 7) for every i.  The extra A load (XR) of
-  // waves 0-3 covers rows 256 + 8*wave .. +7, with the same chunk.
+  // wave w covers rows 256 + 4*w .. +3 from lanes 0-31, whose chunk is
+  // (l&7) ^ ((2*w + (l>>4)) & 7).
   const int sub = lane >> 3;
   const int chunk = (lane & 7) ^ ((4 * wave + (sub >> 1)) & 7);
   // Byte offsets of each lane's 16-byte piece, fixed for the whole tile; the
@@ -391,11 +391,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
   uint32_t a_voff[NA_LD], b_voff[4];
 #pragma unroll
   for (int i = 0; i < NA_LD; ++i) {
-    const int r = (i < 4) ? 8 * (8 * i + wave) + sub : BM + 8 * (wave & 3) + sub;
+    // the extra load (XR) of wave w: rows 256 + 4w .. +3 from lanes 0-31
+    const int r = (i < 4) ? 8 * (8 * i + wave) + sub : BM + 4 * wave + (sub & 3);
+    const int ch = (i < 4) ? chunk : ((lane & 7) ^ ((2 * wave + (sub >> 1)) & 7));
     if (r < rows) {
       int64_t arow = row0 + r;
       if (GROUPED && a.gather) arow = a.gather[arow] / a.gather_div;
-      a_voff[i] = (uint32_t)(arow * a.lda * 2) + (uint32_t)chunk * 16u;
+      a_voff[i] = (uint32_t)(arow * a.lda * 2) + (uint32_t)ch * 16u;
     } else {
       a_voff[i] = kNoRow;
     }
@@ -416,19 +418,27 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
   const int nk = (a.kdim + BK - 1) / BK;
   const bool k_tail = (a.kdim % BK) != 0;
   const uint32_t tail_adj = (chunk >= 4) ? 64u : 0u;
-  auto voff_at = [&](uint32_t v, int ks) {
-    return (k_tail && ks == nk - 1) ? v - tail_adj : v;
+  const uint32_t tail_adj_x = (((lane & 7) ^ ((2 * wave + (sub >> 1)) & 7)) >= 4) ? 64u : 0u;
+  auto voff_at = [&](uint32_t v, int ks, uint32_t adj) {
+    return (k_tail && ks == nk - 1) ? v - adj : v;
   };
   // load i covers tile rows 8*(8*i + wave) .. +7; for gate/up, loads 0 and 1
   // fill the 128 gate rows of the B tile and loads 2 and 3 the up rows.
   auto dma_a = [&](int ks, int i) {
-    const int j = (i < 4) ? 8 * i + wave : 32 + (wave & 3);
-    dma16(ra, voff_at(a_voff[i], ks), (uint32_t)ks * (BK * 2),
-          (lds_void_t*)(lds_raw + (ks % A_SLOTS) * A_TILE + j * 1024));
+    if (i == 4) {
+      // half a load: lanes 0-31 write 512 bytes (four rows); every wave
+      // still issues the instruction, so the waits count the same loads
+      if (lane < 32)
+        dma16(ra, voff_at(a_voff[i], ks, tail_adj_x), (uint32_t)ks * (BK * 2),
+              (lds_void_t*)(lds_raw + (ks % A_SLOTS) * A_TILE + (BM + 4 * wave) * ROW_BYTES));
+      return;
+    }
+    dma16(ra, voff_at(a_voff[i], ks, tail_adj), (uint32_t)ks * (BK * 2),
+          (lds_void_t*)(lds_raw + (ks % A_SLOTS) * A_TILE + (8 * i + wave) * 1024));
   };
   // B load i of stage ks fills quarter i (B rows 64*i .. +63)
   auto dma_b = [&](int ks, int i) {
-    dma16((MODE == kGateUp && i >= 2) ? rb1 : rb0, voff_at(b_voff[i], ks),
+    dma16((MODE == kGateUp && i >= 2) ? rb1 : rb0, voff_at(b_voff[i], ks, tail_adj),
           (uint32_t)ks * (BK * 2),
           (lds_void_t*)(lds_raw + B_BASE + bq(ks, i) * QUARTER + wave * 1024));
   };
