@@ -992,12 +992,11 @@ __global__ __launch_bounds__(512, 2) void gemm_x_fp8_kernel(GemmArgs r, GemmArgs
 
 template <int MODE, bool GROUPED>
 static hipError_t launch_mode(const GemmArgs& a, dim3 grid, hipStream_t stream) {
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<MODE, GROUPED>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  static std::atomic<uint32_t> configured{0};
+  {
+    const hipError_t e =
+        set_lds_limit_once((const void*)gemm_kernel<MODE, GROUPED>, LDS_BYTES, configured);
     if (e != hipSuccess) return e;
-    configured = true;
   }
   hipLaunchKernelGGL((gemm_kernel<MODE, GROUPED>), grid, dim3(512), LDS_BYTES, stream, a);
   return hipGetLastError();
@@ -1067,12 +1066,11 @@ hipError_t launch_router_shared_gateup(const uint16_t* x, int64_t N, int d,
   const int64_t work = ((N + BM - 1) / BM) * (r.n_tiles_n + g.n_tiles_n);
   if (work <= 0) return hipSuccess;
   if (work > 0x7FFFFFF0LL) return hipErrorInvalidConfiguration;
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_x_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  static std::atomic<uint32_t> configured{0};
+  {
+    const hipError_t e =
+        set_lds_limit_once((const void*)gemm_x_kernel, LDS_BYTES, configured);
     if (e != hipSuccess) return e;
-    configured = true;
   }
   hipLaunchKernelGGL(gemm_x_kernel, xcd_grid(work), dim3(512), LDS_BYTES, stream, r, g);
   return hipGetLastError();
@@ -1087,11 +1085,10 @@ static hipError_t launch_fp8(int mode, const GemmArgs& a, int64_t max_m_tiles,
   if (work > 0x7FFFFFF0LL) return hipErrorInvalidConfiguration;
   const void* fn = mode == kGateUp ? (const void*)gemm_fp8_kernel<kGateUp>
                                    : (const void*)gemm_fp8_kernel<kDown>;
-  static bool configured[2] = {false, false};
-  if (!configured[mode]) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  static std::atomic<uint32_t> configured[2] = {{0}, {0}};
+  {
+    const hipError_t e = set_lds_limit_once(fn, LDS_BYTES, configured[mode]);
     if (e != hipSuccess) return e;
-    configured[mode] = true;
   }
   if (mode == kGateUp)
     hipLaunchKernelGGL(gemm_fp8_kernel<kGateUp>, xcd_grid(work), dim3(512), LDS_BYTES, stream, a);
@@ -1131,12 +1128,11 @@ hipError_t launch_router_shared_gateup_fp8(const uint16_t* x, const uint8_t* xq,
   const int64_t work = ((N + BM - 1) / BM) * (r.n_tiles_n + g.n_tiles_n);
   if (work <= 0) return hipSuccess;
   if (work > 0x7FFFFFF0LL) return hipErrorInvalidConfiguration;
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_x_fp8_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  static std::atomic<uint32_t> configured{0};
+  {
+    const hipError_t e =
+        set_lds_limit_once((const void*)gemm_x_fp8_kernel, LDS_BYTES, configured);
     if (e != hipSuccess) return e;
-    configured = true;
   }
   hipLaunchKernelGGL(gemm_x_fp8_kernel, xcd_grid(work), dim3(512), LDS_BYTES, stream, r, g);
   return hipGetLastError();

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #define MOE_KMAX_INTERNAL 8
 
 namespace moe {
@@ -202,5 +204,20 @@ hipError_t launch_shared_down_dense_small(const void* H, const float* Hs, int64_
 
 // ---------------------------------------------------------------- misc
 hipError_t launch_fill_u32(uint32_t* p, uint32_t value, size_t n, hipStream_t stream);
+
+// Raises a kernel's dynamic LDS limit to `bytes` once per device (the
+// attribute has to be set before the first launch that needs more than the
+// default).  `done` holds one bit per device id below 32; concurrent callers
+// may both set it, which is harmless.
+inline hipError_t set_lds_limit_once(const void* fn, int bytes, std::atomic<uint32_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint32_t bit = (dev >= 0 && dev < 32) ? (1u << dev) : 0u;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 }  // namespace moe

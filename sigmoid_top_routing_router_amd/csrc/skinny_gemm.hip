@@ -327,12 +327,11 @@ hipError_t launch_skinny_mode(const GemmArgs& a, int64_t m_tiles, hipStream_t st
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   constexpr int lds = Ring<FP8>::kLds;
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute((const void*)skinny_kernel<MODE, FP8>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  static std::atomic<uint32_t> configured{0};
+  {
+    const hipError_t e =
+        set_lds_limit_once((const void*)skinny_kernel<MODE, FP8>, lds, configured);
     if (e != hipSuccess) return e;
-    configured = true;
   }
   hipLaunchKernelGGL((skinny_kernel<MODE, FP8>), dim3((unsigned)blocks), dim3(256), lds, stream,
                      a, n_chunks);
