@@ -646,10 +646,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
-template <int MODE, bool GROUPED>
+// XR = 32: a grouped tile of 257 .. 288 rows, as in the bf16 engine: 288-row
+// A slots (the 32 extra rows are one more load per wave and stage, four rows
+// from half of the lanes), a B ring of 10 quarters, and one more 16-row block
+// per wave (rows 256 + 16*wg ..) against the wave's four B fragments, so the
+// gate and up values of those rows meet in the same lanes.
+template <int MODE, bool GROUPED, int XR = 0>
 __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int nt,
                                               char* lds_raw) {
   static_assert(MODE != kRouter, "the router product stays bf16");
+  static_assert(XR == 0 || (XR == 32 && GROUPED), "extra rows: grouped only");
   int expert = 0;
   int64_t row0;
   int rows;
@@ -670,20 +676,25 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
   const int sub = lane >> 3;
   const int chunk = (lane & 7) ^ ((4 * wave + (sub >> 1)) & 7);  // as in the bf16 tile
   constexpr uint32_t kNoRow = 0xFFFFFFFFu - 64u * 1024u;  // past any 4 GiB buffer
-  uint32_t a_voff[4], b_voff[4];
+  constexpr int NA_LD = XR ? 5 : 4;
+  uint32_t a_voff[NA_LD], b_voff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 8 * (8 * i + wave) + sub;
+  for (int i = 0; i < NA_LD; ++i) {
+    // the extra load (XR) of wave w: rows 256 + 4w .. +3 from lanes 0-31
+    const int r = (i < 4) ? 8 * (8 * i + wave) + sub : BM + 4 * wave + (sub & 3);
+    const int ch = (i < 4) ? chunk : ((lane & 7) ^ ((2 * wave + (sub >> 1)) & 7));
     if (r < rows) {
       int64_t arow = row0 + r;
       if (GROUPED && a.gather) arow = a.gather[arow] / a.gather_div;
-      a_voff[i] = (uint32_t)(arow * a.lda) + (uint32_t)chunk * 16u;
+      a_voff[i] = (uint32_t)(arow * a.lda) + (uint32_t)ch * 16u;
     } else {
       a_voff[i] = kNoRow;
     }
-    const int brow = (MODE == kGateUp) ? nt * (BN / 2) + (r & (BN / 2 - 1)) : nt * BN + r;
-    b_voff[i] = (brow < a.b_rows) ? (uint32_t)brow * (uint32_t)a.kdim + (uint32_t)chunk * 16u
-                                  : kNoRow;
+    if (i < 4) {
+      const int brow = (MODE == kGateUp) ? nt * (BN / 2) + (r & (BN / 2 - 1)) : nt * BN + r;
+      b_voff[i] = (brow < a.b_rows) ? (uint32_t)brow * (uint32_t)a.kdim + (uint32_t)chunk * 16u
+                                    : kNoRow;
+    }
   }
   const uint32_t b_bytes = (uint32_t)a.b_rows * (uint32_t)a.kdim;
   const uint8_t* A8 = reinterpret_cast<const uint8_t*>(a.A);
@@ -693,21 +704,34 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
   const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(B08 + (int64_t)expert * a.b_expert_stride, b_bytes);
   const __amdgpu_buffer_rsrc_t rb1 = make_rsrc(B18 + (int64_t)expert * a.b_expert_stride, b_bytes);
   const int nk = a.kdim / 128;
-  // LDS: A ring of two 32 KB slots; B ring of 11 quarters (64 B rows, 8 KB),
-  // stage s in quarters 4s .. 4s+3 mod 11; then two 1.5 KB slots of scales
-  // (with the A ring's parity): the 256 row scales of A, and 64 copies each
-  // of the two weight-block scales the tile uses.
+  // LDS: A ring of two slots (32 KB, or 36 KB with extra rows); B ring of
+  // NB_Q quarters (64 B rows, 8 KB), stage s in quarters 4s .. 4s+3 mod NB_Q;
+  // then two slots of scales (with the A ring's parity): the row scales of
+  // A (256, or 288 with the 32 extra rows and a copy of those), and 64
+  // copies each of the two weight-block scales the tile uses.
+  constexpr int A_TILE8 = (BM + XR) * ROW_BYTES;
   constexpr int QUARTER = 8 * 1024;
-  constexpr int NB_Q = 11;
-  constexpr int B_BASE8 = A_SLOTS * TILE_BYTES;
+  constexpr int NB_Q = XR ? 10 : 11;
+  constexpr int NPRE = NB_Q - 8;  // quarters of B(kt+2) free during stage kt
+  constexpr int B_BASE8 = A_SLOTS * A_TILE8;
   constexpr int SC_BASE = B_BASE8 + NB_Q * QUARTER;
-  constexpr int SC_SLOT = 1536;
+  constexpr int SB0_OFF = XR ? 1280 : 1024;  // in a scale slot
+  constexpr int SB1_OFF = SB0_OFF + 256;
+  constexpr int SC_SLOT = SB1_OFF + 256;
+  constexpr int NSC = XR ? 2 : 1;            // scale loads per wave and stage
   static_assert(SC_BASE + 2 * SC_SLOT <= LDS_BYTES, "LDS layout");
   auto bq = [](int kt, int j) { return (4 * kt + j) % NB_Q; };
   auto dma_a = [&](int ks, int i) {
-    const int j = 8 * i + wave;
+    if (i == 4) {
+      // half a load: lanes 0-31 write 512 bytes (four rows); every wave
+      // still issues the instruction, so the waits count the same loads
+      if (lane < 32)
+        dma16(ra, a_voff[i], (uint32_t)ks * 128u,
+              (lds_void_t*)(lds_raw + (ks % A_SLOTS) * A_TILE8 + (BM + 4 * wave) * ROW_BYTES));
+      return;
+    }
     dma16(ra, a_voff[i], (uint32_t)ks * 128u,
-          (lds_void_t*)(lds_raw + (ks % A_SLOTS) * TILE_BYTES + j * 1024));
+          (lds_void_t*)(lds_raw + (ks % A_SLOTS) * A_TILE8 + (8 * i + wave) * 1024));
   };
   auto dma_b = [&](int ks, int i) {  // quarter i: B rows 64*i .. +63
     dma16((MODE == kGateUp && i >= 2) ? rb1 : rb0, b_voff[i], (uint32_t)ks * 128u,
@@ -719,12 +743,15 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
   // wp*32, wp*32+16 and the up rows of the same hidden columns; down -> B
   // rows wp*64 + 16*f.  The MFMAs take the B fragment first, so lane l holds
   // output row (l & 15) of a block and its four consecutive columns
-  // 4*(l >> 4) .. +3.
+  // 4*(l >> 4) .. +3.  With extra rows, accx holds block 256 + 16*wg.
   floatx4_t acc[8][4];
+  floatx4_t accx[4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) accx[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   int b_col[4];
 #pragma unroll
   for (int f = 0; f < 4; ++f)
@@ -738,53 +765,61 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
   const bool live_n = (MODE == kGateUp) ? true : (nt * BN + wp * 64) < a.b_rows;
   const bool any = __builtin_amdgcn_readfirstlane((live_m > 0 && live_n) ? 1 : 0) != 0;
 
-  // ---- scales, staged through LDS with 4-byte LDS-DMA loads (one per wave
-  // and stage, so every wave counts the same loads).  Waves 0-3: lane l
-  // loads the scale of tile row 64*wave + l (through the gather for the
-  // routed gate/up; rows past the segment load zero).  Waves 4, 5: the first
-  // weight-block scale of the tile (gate block nt; down: the block of
-  // columns 0-127), waves 6, 7: the second (up block nt; down: columns
-  // 128-255); the two waves of a pair write the same bytes.  Offsets fit 32
+  // ---- scales, staged through LDS with 4-byte LDS-DMA loads (the same
+  // number per wave and stage, so every wave counts the same loads).  Waves
+  // 0-3: lane l loads the scale of tile row 64*wave + l (through the gather
+  // for the routed gate/up; rows past the segment load zero); with extra rows
+  // a second load brings rows 256 + (l & 31) (lanes 32-63 repeat 0-31).
+  // Waves 4, 5: the first weight-block scale of the tile (gate block nt;
+  // down: the block of columns 0-127), waves 6, 7: the second (up block nt;
+  // down: columns 128-255); the two waves of a pair write the same bytes, and
+  // with extra rows their second load repeats the first.  Offsets fit 32
   // bits: rows * kdim < 4 GiB.
   const int nkb = nk;
   const int nblk = (a.b_rows + 127) / 128;
-  uint32_t sc_voff;
+  uint32_t sc_voff, sc_voff_x = kNoRow;
   __amdgpu_buffer_rsrc_t rsc;
   if (wave < 4) {
-    const int r = 64 * wave + lane;
-    if (r < rows) {
+    auto row_off = [&](int r) {
+      if (r >= rows) return kNoRow;
       int64_t arow = row0 + r;
       if (GROUPED && a.gather) arow = a.gather[arow] / a.gather_div;
-      sc_voff = (uint32_t)arow * (uint32_t)nkb * 4u;
-    } else {
-      sc_voff = kNoRow;
-    }
+      return (uint32_t)arow * (uint32_t)nkb * 4u;
+    };
+    sc_voff = row_off(64 * wave + lane);
+    if (XR > 0) sc_voff_x = row_off(BM + (lane & 31));
     rsc = make_rsrc(a.sa, a.a_bytes / 128u * 4u);
   } else {
     const int second = wave >= 6 ? 1 : 0;
     const int bblk = (MODE == kGateUp) ? nt : min(2 * nt + second, nblk - 1);
     const float* base = (MODE == kGateUp && second) ? a.sb1 : a.sb0;
     sc_voff = (uint32_t)(((int64_t)expert * a.sb_es + (int64_t)bblk * nkb) * 4);
+    sc_voff_x = sc_voff;
     rsc = make_rsrc(base, 0xFFFFFFF0u);
   }
-  auto dma_sc = [&](int ks) {
+  auto dma_sc = [&](int ks, int which) {
+    const int dst = (wave < 4) ? (which ? 1024 : wave * 256) : (wave < 6 ? SB0_OFF : SB1_OFF);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsc, (lds_void_t*)(lds_raw + SC_BASE + (ks % 2) * SC_SLOT + (wave < 6 ? 0 : 256) +
-                           (wave < 4 ? wave * 256 : 1024)),
-        4, sc_voff, (uint32_t)ks * 4u, 0, 0);
+        rsc, (lds_void_t*)(lds_raw + SC_BASE + (ks % 2) * SC_SLOT + dst), 4,
+        which ? sc_voff_x : sc_voff, (uint32_t)ks * 4u, 0, 0);
+  };
+  auto dma_scales = [&](int ks) {
+    dma_sc(ks, 0);
+    if (XR > 0) dma_sc(ks, 1);
   };
 
   // Schedule (the bf16 engine's, with one MFMA per 16 x 16 block and stage):
-  // the prologue loads A0 B0 A1 B1 and quarters 0-2 of B2 (with the scales of
-  // stages 0 and 1).  Stage kt loads the rest of A(kt+1) and quarter 3 of
-  // B(kt+1), then quarters 0-2 of B(kt+2), spread over its row blocks; its
-  // closing barrier waits for all but those three and is followed by loads
-  // 0,1 of A(kt+2) and its scales.  The steady-state stages are compiled
-  // without branches, so the waits stay exact.  LIVE (0, 2 or 4) is the
-  // number of 32-row halves of its rows this wave multiplies.
+  // the prologue loads A0 B0 A1 B1 and the first NPRE quarters of B2 (with
+  // the scales of stages 0 and 1).  Stage kt loads the rest of A(kt+1) and of
+  // B(kt+1), then the first NPRE quarters of B(kt+2), spread over its row
+  // blocks; its closing barrier waits for all but those and is followed by
+  // loads 0,1 of A(kt+2) and its scales.  The steady-state stages are
+  // compiled without branches, so the waits stay exact.  LIVE (0, 2 or 4) is
+  // the number of 32-row halves of its rows this wave multiplies.
   auto run = [&](auto live_tag) {
     constexpr int LIVE = decltype(live_tag)::value;
     constexpr int MB = 2 * LIVE;  // 16-row blocks
+    constexpr bool XB = XR > 0 && LIVE > 0;  // the extra block
     const int s0 = ((2 * quad) ^ ((lane >> 1) & 7)) * 16;
     const int s1 = ((2 * quad + 1) ^ ((lane >> 1) & 7)) * 16;
     // lane l reads 32 bytes of its row: chunks 2*(l>>4) and +1 (swizzled;
@@ -798,9 +833,11 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     };
     i32x8_t Bf[4], Af[2];
-    float sa_r[8], sb_r[2];
+    float sa_r[8], sa_x = 0.f, sb_r[2];
+    // row of block m (8: the extra block)
     auto a_row = [&](int kt, int m) {
-      return lds_raw + (kt % A_SLOTS) * TILE_BYTES + (wg * 128 + 16 * m + fr) * ROW_BYTES;
+      const int r = (m < 8) ? wg * 128 + 16 * m + fr : BM + 16 * wg + fr;
+      return lds_raw + (kt % A_SLOTS) * A_TILE8 + r * ROW_BYTES;
     };
     auto read_stage = [&](int kt) {  // B fragments, A block 0 and the scales of stage kt
       if (MB > 0) {
@@ -813,34 +850,49 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
 #pragma unroll
         for (int m = 0; m < MB; ++m)
           sa_r[m] = *reinterpret_cast<const float*>(sc + (wg * 128 + 16 * m + fr) * 4);
-        sb_r[0] = *reinterpret_cast<const float*>(sc + 1024);
-        sb_r[1] = *reinterpret_cast<const float*>(sc + 1280);
+        if (XB) sa_x = *reinterpret_cast<const float*>(sc + 1024 + (16 * wg + fr) * 4);
+        sb_r[0] = *reinterpret_cast<const float*>(sc + SB0_OFF);
+        sb_r[1] = *reinterpret_cast<const float*>(sc + SB1_OFF);
+      }
+    };
+    auto mfma_block = [&](floatx4_t (&c)[4], const i32x8_t& A, float sa) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const floatx4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            Bf[f], A, floatx4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+        const float fac = sa * sb_r[(MODE == kGateUp) ? (f >> 1) : (wp >> 1)];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) c[f][r] = fmaf(p[r], fac, c[f][r]);
+        // keeps the compiler from sinking the FMAs below later blocks'
+        // MFMAs, which would hold every product live at once
+        asm volatile("" : "+v"(c[f]));
       }
     };
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma_a(0, i);
-    dma_sc(0);
+    for (int i = 0; i < NA_LD; ++i) dma_a(0, i);
+    dma_scales(0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma_b(0, i);
     if (nk > 1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma_a(1, i);
-      dma_sc(1);
+      for (int i = 0; i < NA_LD; ++i) dma_a(1, i);
+      dma_scales(1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) dma_b(1, i);
     }
     if (nk > 2) {
 #pragma unroll
-      for (int i = 0; i < 3; ++i) dma_b(2, i);
+      for (int i = 0; i < NPRE; ++i) dma_b(2, i);
     }
-    if (nk > 2) wait_vmcnt<12>();
-    else if (nk > 1) wait_vmcnt<9>();
+    constexpr int STAGE_LD = NA_LD + NSC + 4;  // loads of one stage
+    if (nk > 2) wait_vmcnt<STAGE_LD + NPRE>();
+    else if (nk > 1) wait_vmcnt<STAGE_LD>();
     else wait_vmcnt<0>();
     block_barrier();
     read_stage(0);
     //   ld_a2 - loads 0,1 of A(kt+2) and its scales after the closing barrier
-    //   ld_a1 - loads 2,3 of A(kt+1) and quarter 3 of B(kt+1)
-    //   ld_b  - quarters 0-2 of B(kt+2)
+    //   ld_a1 - the other loads of A(kt+1), and quarters NPRE.. of B(kt+1)
+    //   ld_b  - quarters 0 .. NPRE-1 of B(kt+2)
     //   next  - a next stage exists (barrier + its fragments)
     //   vmb   - at the barrier the B(kt+2) quarters may still be in flight
     auto stage = [&](int kt, auto ld_a2, auto ld_a1, auto ld_b, auto next, auto vmb) {
@@ -848,33 +900,34 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
       for (int m = 0; m < 8; ++m) {
         __builtin_amdgcn_sched_barrier(0);
         if (m == 1 && ld_a1) { dma_a(kt + 1, 2); dma_a(kt + 1, 3); }
-        if (m == 3 && ld_a1) dma_b(kt + 1, 3);
-        if (m == 3 && ld_b) dma_b(kt + 2, 0);
-        if (m == 5 && ld_b) { dma_b(kt + 2, 1); dma_b(kt + 2, 2); }
+        if (m == 2 && ld_a1 && XR > 0) dma_a(kt + 1, 4);
+        if (NPRE == 3) {
+          if (m == 3 && ld_a1) dma_b(kt + 1, 3);
+          if (m == 3 && ld_b) dma_b(kt + 2, 0);
+          if (m == 5 && ld_b) { dma_b(kt + 2, 1); dma_b(kt + 2, 2); }
+        } else {
+          if (m == 3 && ld_a1) dma_b(kt + 1, 2);
+          if (m == 4 && ld_a1) dma_b(kt + 1, 3);
+          if (m == 5 && ld_b) dma_b(kt + 2, 0);
+          if (m == 6 && ld_b) dma_b(kt + 2, 1);
+        }
         if (m < MB) {
           if (m + 1 < MB) Af[(m + 1) & 1] = frag(a_row(kt, m + 1));
-#pragma unroll
-          for (int f = 0; f < 4; ++f) {
-            const floatx4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                Bf[f], Af[m & 1], floatx4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-            const float fac = sa_r[m] * sb_r[(MODE == kGateUp) ? (f >> 1) : (wp >> 1)];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[m][f][r] = fmaf(p[r], fac, acc[m][f][r]);
-            // keeps the compiler from sinking the FMAs below later blocks'
-            // MFMAs, which would hold every product live at once
-            asm volatile("" : "+v"(acc[m][f]));
-          }
+          else if (XB) Af[(m + 1) & 1] = frag(a_row(kt, 8));
+          mfma_block(acc[m], Af[m & 1], sa_r[m]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (XB) mfma_block(accx, Af[0], sa_x);
+      __builtin_amdgcn_sched_barrier(0);
       if (next) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (vmb) wait_vmcnt<3>(); else wait_vmcnt<0>();
+        if (vmb) wait_vmcnt<NPRE>(); else wait_vmcnt<0>();
         block_barrier();  // every wave done with A slot kt%2, B(kt) and the scales of kt
         if (ld_a2) {
           dma_a(kt + 2, 0);
           dma_a(kt + 2, 1);
-          dma_sc(kt + 2);
+          dma_scales(kt + 2);
         }
         read_stage(kt + 1);
       }
@@ -886,48 +939,59 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
     if (nk >= 3) stage(nk - 2, F{}, T{}, F{}, T{}, F{});
     if (nk >= 2) stage(nk - 1, F{}, F{}, F{}, F{}, F{});
   };
-  if (!any) run(std::integral_constant<int, 0>{});
-  else if (live_m <= 2) run(std::integral_constant<int, 2>{});
-  else run(std::integral_constant<int, 4>{});
+  if constexpr (XR > 0) {
+    // rows > 256: every wave has four live row blocks
+    if (!any) run(std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 4>{});
+  } else {
+    if (!any) run(std::integral_constant<int, 0>{});
+    else if (live_m <= 2) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 4>{});
+  }
 
   // ---- epilogue: stage the bf16 tile in LDS (four consecutive columns per
   // 8-byte store), then write whole rows
   constexpr int OCOLS = (MODE == kGateUp) ? BN / 2 : BN;
   constexpr int OSTRIDE = OCOLS * 2 + 8;
+  static_assert((BM + XR) * OSTRIDE <= LDS_BYTES, "staged tile exceeds the LDS");
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   auto pack2 = [](float x, float y) {
     const bf16x2_t v = {(__bf16)x, (__bf16)y};
     return __builtin_bit_cast(uint32_t, v);
+  };
+  auto stage_block = [&](const floatx4_t (&c)[4], int row) {
+    char* lrow = lds_raw + row * OSTRIDE;
+    if (MODE == kGateUp) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        float hv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float g = c[f][j];
+          const float u = c[f + 2][j];
+          hv[j] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+        }
+        *reinterpret_cast<uint2*>(lrow + (b_col[f] + 4 * quad) * 2) =
+            make_uint2(pack2(hv[0], hv[1]), pack2(hv[2], hv[3]));
+      }
+    } else {
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+        *reinterpret_cast<uint2*>(lrow + (b_col[f] + 4 * quad) * 2) =
+            make_uint2(pack2(c[f][0], c[f][1]), pack2(c[f][2], c[f][3]));
+    }
   };
   __syncthreads();  // all fragment reads of the last stage are done
   if (any) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       if (m >= 2 * live_m) break;
-      char* lrow = lds_raw + (wg * 128 + m * 16 + fr) * OSTRIDE;
-      if (MODE == kGateUp) {
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          float hv[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float g = acc[m][f][j];
-            const float u = acc[m][f + 2][j];
-            hv[j] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
-          }
-          *reinterpret_cast<uint2*>(lrow + (b_col[f] + 4 * quad) * 2) =
-              make_uint2(pack2(hv[0], hv[1]), pack2(hv[2], hv[3]));
-        }
-      } else {
-#pragma unroll
-        for (int f = 0; f < 4; ++f)
-          *reinterpret_cast<uint2*>(lrow + (b_col[f] + 4 * quad) * 2) =
-              make_uint2(pack2(acc[m][f][0], acc[m][f][1]), pack2(acc[m][f][2], acc[m][f][3]));
-      }
+      stage_block(acc[m], wg * 128 + m * 16 + fr);
     }
+    if (XR > 0) stage_block(accx, BM + 16 * wg + fr);
   }
   __syncthreads();
-  epilogue_store<MODE>(a, nt, row0, rows, tid, lds_raw);
+  epilogue_store<MODE, BM + XR>(a, nt, row0, rows, tid, lds_raw);
 }
 
 template <int MODE>
@@ -937,10 +1001,16 @@ __global__ __launch_bounds__(512, 2) void gemm_fp8_kernel(GemmArgs a) {
   const int64_t m_tiles = grouped ? (int64_t)(*a.n_tiles) : (a.rows_dense + BM - 1) / BM;
   int64_t logical;
   if (!xcd_tile(m_tiles * a.n_tiles_n, logical)) return;
-  if (grouped)
-    gemm_tile_fp8<MODE, true>(a, logical / a.n_tiles_n, (int)(logical % a.n_tiles_n), lds_raw);
-  else
-    gemm_tile_fp8<MODE, false>(a, logical / a.n_tiles_n, (int)(logical % a.n_tiles_n), lds_raw);
+  const int64_t mt = logical / a.n_tiles_n;
+  const int nt = (int)(logical % a.n_tiles_n);
+  if (grouped) {
+    if (reinterpret_cast<const int4*>(a.tiles)[mt].z > BM)
+      gemm_tile_fp8<MODE, true, kXRows>(a, mt, nt, lds_raw);
+    else
+      gemm_tile_fp8<MODE, true>(a, mt, nt, lds_raw);
+  } else {
+    gemm_tile_fp8<MODE, false>(a, mt, nt, lds_raw);
+  }
 }
 
 template <int MODE, bool GROUPED>

@@ -86,8 +86,7 @@ hipError_t launch_down(const uint16_t* H, int64_t h_rows, const int32_t* tiles, 
                        int64_t max_tiles, int64_t rows_dense, const uint16_t* w_down,
                        int d, int h, uint16_t* Y, hipStream_t stream);
 int gemm_bm();
-// Rows beyond gemm_bm() that one grouped bf16 m-tile may hold (the FP8 tiles
-// hold gemm_bm() rows at most).
+// Rows beyond gemm_bm() that one grouped m-tile may hold (bf16 and E4M3).
 int gemm_xrows();
 // Router logits and the shared expert's gate/up in one launch (both read x).
 hipError_t launch_router_shared_gateup(const uint16_t* x, int64_t N, int d,

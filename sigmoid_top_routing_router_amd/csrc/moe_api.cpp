@@ -406,8 +406,7 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
   pw.src_pos = A.src_pos ? A.src_pos : l.src_pos;
   pw.tiles = l.tiles;
   pw.n_tiles = l.n_tiles;
-  MOE_TRY_HIP(moe::launch_permute(ids, N, E, K, moe::gemm_bm(), ex.fp8 ? 0 : moe::gemm_xrows(),
-                                  pw, st),
+  MOE_TRY_HIP(moe::launch_permute(ids, N, E, K, moe::gemm_bm(), moe::gemm_xrows(), pw, st),
               "moe_forward: grouping");
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
 

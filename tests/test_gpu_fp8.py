@@ -181,10 +181,11 @@ def test_forward_fp8_small_batch_concentrated(M):
         run_fp8_case(M, cfg)
 
 
-# Loads just above a multiple of 256 rows: the E4M3 tiles keep 256 rows, so
-# every remainder, short or long, is an m-tile of its own.  Loads (oracle):
-#  a) 282 251 286 280 286 257 271 287       - 256 + short tails, one 251
-#  b) 533 533 508 531 527 512 530 526       - 2 x 256 + short tails, one 252
+# Loads just above a multiple of 256 rows: the last m-tile of a segment
+# holds up to 288 rows (the extra-rows tile), a longer remainder gets a tile
+# of its own.  Loads (oracle):
+#  a) 282 251 286 280 286 257 271 287       - 288-row tiles, one 251
+#  b) 533 533 508 531 527 512 530 526       - 256 + extra-rows tiles, one 252
 #  c) 2891 2687 1817 719 393 108 59 26      - long segments, tails of both kinds
 #  d) 1481 1221 799 452 250 132 91 74       - as c, d = 256 and h = 128
 #  e) N = 900, d = h = 384: three 128-k stages (first, middle, last, no
