@@ -57,6 +57,26 @@ def test_quantize_rows_bitexact(M, n, cols, kind):
     assert bits_equal(host(s), rs), "scales differ"
 
 
+@pytest.mark.parametrize("n,cols,shift", [(37, 384, 1), (64, 256, 3), (300, 2560, 0)])
+def test_quantize_rows_alignment(M, n, cols, shift):
+    """x shifted by `shift` 4-byte words off a 16-byte boundary takes the
+    wave-per-group kernel, an aligned x the 16-lane one; both must give the
+    oracle's codes and scales."""
+    import torch
+    say("fp8 quantize rows alignment", n, cols, shift)
+    rng = np.random.default_rng(7 * n + cols + shift)
+    xb = _bf16_bits(rng, (n, cols), "outliers")
+    xb[n // 2, :128] = 0
+    flat = bf16_dev(np.concatenate([np.zeros(2 * shift, np.uint16), xb.reshape(-1)]))
+    x = flat[2 * shift:].view(n, cols)
+    assert x.data_ptr() % 16 == (4 * shift) % 16
+    q, s = M.fp8_quantize_rows(x)
+    rq, rs = O.quantize_row_groups(O.bf16_to_f32(xb))
+    assert np.array_equal(host(q), rq), "codes differ"
+    assert bits_equal(host(s), rs), "scales differ"
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("count,R,C", [(1, 128, 128), (3, 300, 200), (2, 256, 384), (1, 1, 1)])
 def test_quantize_blocks_bitexact(M, count, R, C):
     say("fp8 quantize blocks", count, R, C)
