@@ -124,9 +124,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // LDS at l + 16 * lane.  The buffer form (buffer_load_dwordx4 ... lds) is
 // counted on vmcnt only, so the compiler keeps exact lgkmcnt waits for the
 // LDS fragment reads around it.
+// Cache-policy operand of a buffer load: the non-temporal bit marks the lines
+// as streaming, so the caches give them up first.
+constexpr int kCpolNT = 2;
+
+template <int CPOL = 0>
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
                                       lds_void_t* l) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff, soff, 0, CPOL);
 }
 
 template <int N>

@@ -343,7 +343,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, floatx16_t (&ac
 // holds in b_row[0] (for gate/up the waves of the second row half take the
 // up rows there).  The 32 extra A rows are one more load per wave and stage,
 // four rows from half of the wave's lanes.
-template <int MODE, bool GROUPED, int XR = 0>
+template <int MODE, bool GROUPED, int XR = 0, bool BNT = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
                                           char* lds_raw) {
   static_assert(XR == 0 || (XR == 32 && GROUPED && MODE != kRouter), "extra rows: grouped only");
@@ -438,7 +438,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
   };
   // B load i of stage ks fills quarter i (B rows 64*i .. +63)
   auto dma_b = [&](int ks, int i) {
-    dma16((MODE == kGateUp && i >= 2) ? rb1 : rb0, voff_at(b_voff[i], ks, tail_adj),
+    dma16<BNT ? kCpolNT : 0>((MODE == kGateUp && i >= 2) ? rb1 : rb0, voff_at(b_voff[i], ks, tail_adj),
           (uint32_t)ks * (BK * 2),
           (lds_void_t*)(lds_raw + B_BASE + bq(ks, i) * QUARTER + wave * 1024));
   };
@@ -651,7 +651,7 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 // from half of the lanes), a B ring of 10 quarters, and one more 16-row block
 // per wave (rows 256 + 16*wg ..) against the wave's four B fragments, so the
 // gate and up values of those rows meet in the same lanes.
-template <int MODE, bool GROUPED, int XR = 0>
+template <int MODE, bool GROUPED, int XR = 0, bool BNT = false>
 __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int nt,
                                               char* lds_raw) {
   static_assert(MODE != kRouter, "the router product stays bf16");
@@ -734,7 +734,7 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
           (lds_void_t*)(lds_raw + (ks % A_SLOTS) * A_TILE8 + (8 * i + wave) * 1024));
   };
   auto dma_b = [&](int ks, int i) {  // quarter i: B rows 64*i .. +63
-    dma16((MODE == kGateUp && i >= 2) ? rb1 : rb0, b_voff[i], (uint32_t)ks * 128u,
+    dma16<BNT ? kCpolNT : 0>((MODE == kGateUp && i >= 2) ? rb1 : rb0, b_voff[i], (uint32_t)ks * 128u,
           (lds_void_t*)(lds_raw + B_BASE8 + bq(ks, i) * QUARTER + wave * 1024));
   };
 
@@ -994,6 +994,19 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
   epilogue_store<MODE, BM + XR>(a, nt, row0, rows, tid, lds_raw);
 }
 
+// A segment held by one m-tile (its first tile is also its last) multiplies
+// each of its expert's B tiles once, so those loads are marked non-temporal
+// and leave L2 to the A rows, which the segment's column tiles share.
+// Segments of several m-tiles reuse their B tiles and keep the default
+// policy.  Tile entries are (expert, first row, rows, row offset in the
+// segment); only the last tile of a segment can differ from BM rows.
+__device__ __forceinline__ bool single_tile_segment(const GemmArgs& a, int4 ent, int64_t mt,
+                                                    int64_t m_tiles) {
+  if (ent.w != 0) return false;
+  if (ent.z != BM) return true;
+  return mt + 1 == m_tiles || reinterpret_cast<const int4*>(a.tiles)[mt + 1].x != ent.x;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(512, 2) void gemm_fp8_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
@@ -1004,10 +1017,15 @@ __global__ __launch_bounds__(512, 2) void gemm_fp8_kernel(GemmArgs a) {
   const int64_t mt = logical / a.n_tiles_n;
   const int nt = (int)(logical % a.n_tiles_n);
   if (grouped) {
-    if (reinterpret_cast<const int4*>(a.tiles)[mt].z > BM)
-      gemm_tile_fp8<MODE, true, kXRows>(a, mt, nt, lds_raw);
-    else
-      gemm_tile_fp8<MODE, true>(a, mt, nt, lds_raw);
+    const int4 ent = reinterpret_cast<const int4*>(a.tiles)[mt];
+    const bool once = single_tile_segment(a, ent, mt, m_tiles);
+    if (ent.z > BM) {
+      if (once) gemm_tile_fp8<MODE, true, kXRows, true>(a, mt, nt, lds_raw);
+      else gemm_tile_fp8<MODE, true, kXRows>(a, mt, nt, lds_raw);
+    } else {
+      if (once) gemm_tile_fp8<MODE, true, 0, true>(a, mt, nt, lds_raw);
+      else gemm_tile_fp8<MODE, true>(a, mt, nt, lds_raw);
+    }
   } else {
     gemm_tile_fp8<MODE, false>(a, mt, nt, lds_raw);
   }
@@ -1022,8 +1040,15 @@ __global__ __launch_bounds__(512, 2) void gemm_kernel(GemmArgs a) {
   const int64_t mt = logical / a.n_tiles_n;
   const int nt = (int)(logical % a.n_tiles_n);
   if constexpr (GROUPED && MODE != kRouter) {
-    if (reinterpret_cast<const int4*>(a.tiles)[mt].z > BM) {
-      gemm_tile<MODE, true, kXRows>(a, mt, nt, lds_raw);
+    const int4 ent = reinterpret_cast<const int4*>(a.tiles)[mt];
+    const bool once = single_tile_segment(a, ent, mt, m_tiles);
+    if (ent.z > BM) {
+      if (once) gemm_tile<MODE, true, kXRows, true>(a, mt, nt, lds_raw);
+      else gemm_tile<MODE, true, kXRows>(a, mt, nt, lds_raw);
+      return;
+    }
+    if (once) {
+      gemm_tile<MODE, true, 0, true>(a, mt, nt, lds_raw);
       return;
     }
   }
