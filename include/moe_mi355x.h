@@ -260,6 +260,11 @@ typedef struct {
  * a stable counting sort; the expert MLPs run as grouped bf16 MFMA GEMMs
  * with fp32 accumulation; the hidden activations and the per-pair expert
  * outputs are held in bf16; the combine accumulates in fp32.
+ * Above 64 tokens the shared expert's two products run on a second,
+ * library-owned non-blocking stream (one per device and host thread, created
+ * on first use, default priority), forked from `stream` at the call's start
+ * and joined back into it before the combine: `stream` still orders the whole
+ * call, and capturing `stream` into a HIP graph captures both branches.
  *
  *  p        problem (sizes, flags, optional logits_in / logit_offset).
  *  w        weights (see moe_weights_t).
@@ -352,7 +357,9 @@ moe_status_t moe_forward_fp8(const moe_problem_t* p, const moe_fp8_weights_t* w,
  * the record.  Stages: 0 router GEMM and shared-expert gate/up GEMM (one
  * launch), 1 routing (selection, token bias, quantile update, re-route,
  * loads), 2 grouping, 3 routed gate/up GEMM, 4 routed down GEMM, 5 shared
- * down GEMM, 6 weighted combine.
+ * down GEMM, 6 weighted combine.  With the shared expert on the side stream
+ * (above 64 tokens) stage 0 is the router GEMM alone, the shared expert's
+ * work overlaps stages 0-4 and stage 5 is the wait for it at the join.
  * Errors: INVALID_ARGUMENT (NULL outputs, enable outside 0..2), HIP.
  */
 #define MOE_NUM_STAGES 7

@@ -259,6 +259,56 @@ struct CallTimer {
   }
 };
 
+// The shared expert does not depend on the routing, so at batch sizes that
+// use the tile engine its two products run on a second stream, next to the
+// router GEMM, the routing, the grouping and the routed experts, filling the
+// compute units those leave idle.  One non-blocking stream (default
+// priority) and its fork and join events per device and host thread, created
+// on first use and kept until the process ends; where they cannot be created
+// the products run in order on the caller's stream instead.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool failed = false;
+};
+constexpr int kMaxSideDevices = 64;
+
+SideStream* side_stream() {
+  thread_local SideStream tab[kMaxSideDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  SideStream& t = tab[dev];
+  if (t.failed) return nullptr;
+  if (!t.s) {
+    if (hipStreamCreateWithFlags(&t.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&t.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&t.join, hipEventDisableTiming) != hipSuccess) {
+      (void)hipGetLastError();
+      t.failed = true;
+      return nullptr;
+    }
+  }
+  return &t;
+}
+
+// Makes the caller's stream wait for the side stream's work once, at the
+// latest when it goes out of scope (also on an error return, so that a
+// captured graph never holds an unjoined branch).
+struct SideJoin {
+  hipStream_t st = nullptr;
+  SideStream* side = nullptr;
+  hipError_t join() {
+    if (!side) return hipSuccess;
+    SideStream* t = side;
+    side = nullptr;
+    return hipStreamWaitEvent(st, t->join, 0);
+  }
+  ~SideJoin() { (void)join(); }
+};
+
 #define MOE_TRY_HIP(expr, where)                   \
   do {                                             \
     hipError_t _e = (expr);                        \
@@ -302,8 +352,9 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
   CallTimer tm;
   MOE_TRY_HIP(tm.start(st), "moe_forward: stage timer");
 
-  // Router logits and the shared expert's gate/up: both read x, so they
-  // share one launch.  FP8 experts first quantise x per 1 x 128 group; the
+  // Router logits and the shared expert's gate/up: on one stream both read
+  // x, so they share one launch; with the side stream the shared expert runs
+  // there instead.  FP8 experts first quantise x per 1 x 128 group; the
   // router reads the bf16 x.
   const float* Z;
   const bool shared = p->n_shared == 1;
@@ -314,6 +365,14 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
   const bool small = N <= moe::kSmallBatch;
   if (ex.fp8)
     MOE_TRY_HIP(moe::launch_quant_rows(x, N, d, l.xq, l.xs, st), "moe_forward: quantise x");
+  SideJoin sj;
+  SideStream* side = (!small && shared) ? side_stream() : nullptr;
+  // the side stream starts from the caller's stream as it stands before the
+  // router GEMM (the fork), but its work is enqueued after that GEMM, whose
+  // blocks are then dispatched first
+  if (side) MOE_TRY_HIP(hipEventRecord(side->fork, st), "moe_forward: fork");
+  // the shared expert's products on the caller's stream (no side stream)
+  const bool shared_here = shared && !side;
   if (small) {
     if (p->logits_in) {
       Z = p->logits_in;
@@ -342,24 +401,24 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
     if (A.logits)
       MOE_TRY_HIP(hipMemcpyAsync(A.logits, Z, (size_t)N * E * 4, hipMemcpyDeviceToDevice, st),
                   "moe_forward: logits copy");
-    if (shared && ex.fp8)
+    if (shared_here && ex.fp8)
       MOE_TRY_HIP(moe::launch_gateup_fp8(l.xq, l.xs, N, nullptr, 1, nullptr, nullptr, 0, N,
                                          q->ws_gate, q->ss_gate, q->ws_up, q->ss_up, d, hs,
                                          l.Hsq, l.Hss, st),
                   "moe_forward: shared gate/up");
-    else if (shared)
+    else if (shared_here)
       MOE_TRY_HIP(moe::launch_gateup(x, N, nullptr, 1, nullptr, nullptr, 0, N, w->ws_gate,
                                      w->ws_up, d, hs, l.Hs, st),
                   "moe_forward: shared gate/up");
   } else {
     float* zout = A.logits ? A.logits : l.Z;
-    if (shared && ex.fp8)
+    if (shared_here && ex.fp8)
       MOE_TRY_HIP(moe::launch_router_shared_gateup_fp8(x, l.xq, l.xs, N, d, ex.w_router,
                                                        p->logit_offset, E, zout, q->ws_gate,
                                                        q->ss_gate, q->ws_up, q->ss_up, hs,
                                                        l.Hsq, l.Hss, st),
                   "moe_forward: router GEMM + shared gate/up");
-    else if (shared)
+    else if (shared_here)
       MOE_TRY_HIP(moe::launch_router_shared_gateup(x, N, d, ex.w_router, p->logit_offset, E,
                                                    zout, w->ws_gate, w->ws_up, hs, l.Hs, st),
                   "moe_forward: router GEMM + shared gate/up");
@@ -367,6 +426,30 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
       MOE_TRY_HIP(moe::launch_router_gemm(x, ex.w_router, p->logit_offset, N, d, E, zout, st),
                   "moe_forward: router GEMM");
     Z = zout;
+  }
+  if (side) {
+    // the shared expert on the side stream: gate/up, then down into l.sh,
+    // which the combine reads after the join
+    const hipStream_t s2 = side->s;
+    MOE_TRY_HIP(hipStreamWaitEvent(s2, side->fork, 0), "moe_forward: fork");
+    sj.st = st;
+    sj.side = side;
+    if (ex.fp8) {
+      MOE_TRY_HIP(moe::launch_gateup_fp8(l.xq, l.xs, N, nullptr, 1, nullptr, nullptr, 0, N,
+                                         q->ws_gate, q->ss_gate, q->ws_up, q->ss_up, d, hs,
+                                         l.Hsq, l.Hss, s2),
+                  "moe_forward: shared gate/up");
+      MOE_TRY_HIP(moe::launch_down_fp8(l.Hsq, l.Hss, N, nullptr, nullptr, 0, N, q->ws_down,
+                                       q->ss_down, d, hs, l.sh, s2),
+                  "moe_forward: shared down");
+    } else {
+      MOE_TRY_HIP(moe::launch_gateup(x, N, nullptr, 1, nullptr, nullptr, 0, N, w->ws_gate,
+                                     w->ws_up, d, hs, l.Hs, s2),
+                  "moe_forward: shared gate/up");
+      MOE_TRY_HIP(moe::launch_down(l.Hs, N, nullptr, nullptr, 0, N, w->ws_down, d, hs, l.sh, s2),
+                  "moe_forward: shared down");
+    }
+    MOE_TRY_HIP(hipEventRecord(side->join, s2), "moe_forward: join");
   }
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
 
@@ -437,12 +520,13 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
                     d, ex.fp8 ? (const void*)q->ws_down : (const void*)w->ws_down,
                     ex.fp8 ? q->ss_down : nullptr, hs, ex.fp8, l.sh, l.part, st),
                 "moe_forward: shared down");
-  else if (shared && ex.fp8)
+  else if (shared_here && ex.fp8)
     MOE_TRY_HIP(moe::launch_down_fp8(l.Hsq, l.Hss, N, nullptr, nullptr, 0, N, q->ws_down,
                                      q->ss_down, d, hs, l.sh, st), "moe_forward: shared down");
-  else if (shared)
+  else if (shared_here)
     MOE_TRY_HIP(moe::launch_down(l.Hs, N, nullptr, nullptr, 0, N, w->ws_down, d, hs, l.sh, st),
                 "moe_forward: shared down");
+  MOE_TRY_HIP(sj.join(), "moe_forward: join");
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
   // weighted combine
   MOE_TRY_HIP(moe::launch_combine(shared ? l.sh : nullptr, l.Y, S, pw.src_pos, N, K, d, y, st),

@@ -61,3 +61,63 @@ def test_forward_graph_replay_matches_eager(M, name, N):
         run()  # eager work between replays
         torch.cuda.synchronize()
         assert np.array_equal(host(y), ref)
+
+
+def test_forward_threads_and_streams(M):
+    """Above 64 tokens the shared expert runs on a library-owned side stream
+    per device and host thread, forked from the caller's stream and joined
+    back before the combine.  Two host threads, each on its own stream with
+    its own workspace, and calls on the default stream must all give the
+    single-call result, every call only ordered by its own stream."""
+    import threading
+
+    import torch
+    cfg = scaled(CONFIGS["prefill"], 1500)
+    say("threads and streams", cfg.name, cfg.N)
+    L = make_inputs(cfg)
+    W = weights_dev(L)
+    x = bf16_dev(L.x)
+    beta = dev(L.beta_in)
+    off = dev(L.logit_offset)
+    nbytes = M.forward_workspace_bytes(cfg.N, cfg.d, cfg.E, cfg.K, cfg.h, cfg.n_shared,
+                                       cfg.h_shared, cfg.recompute_bias)
+
+    def call(ws, y):
+        M.forward(x, W, cfg.K, beta_in=beta, recompute_bias=cfg.recompute_bias,
+                  logit_offset=off, workspace=ws, out=y)
+
+    ws0 = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    y0 = torch.empty((cfg.N, cfg.d), dtype=torch.bfloat16, device="cuda")
+    call(ws0, y0)
+    torch.cuda.synchronize()
+    ref = host(y0).copy()
+
+    outs, errors = [None, None], []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+            y = torch.empty((cfg.N, cfg.d), dtype=torch.bfloat16, device="cuda")
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    y.zero_()
+                    call(ws, y)
+            s.synchronize()
+            outs[i] = host(y).copy()
+        except Exception as e:  # reported below, on the test's thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for _ in range(3):
+        y0.zero_()
+        call(ws0, y0)  # the main thread keeps working on the default stream
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    assert np.array_equal(host(y0), ref)
+    for i in range(2):
+        assert np.array_equal(outs[i], ref), f"thread {i} differs"
