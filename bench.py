@@ -156,6 +156,78 @@ def cpu_baseline(cfg, L, sample_tokens):
                       f"workload, one run of {dt:.1f} s"}
 
 
+def bench_parts(M, torch, cfg, Z, beta, iters):
+    """Standalone timing of the routing steps through the C-ABI: moe_route
+    (selection, weights, token bias) and moe_eqb_bias (one exact quantile
+    update: histogram zeroing, two radix passes over the logits, scans,
+    centring) on the workload's own logits.  Each sample brackets one call
+    with HIP events on the current stream.  "warm": a spin kernel before the
+    first event keeps the GPU busy while the host enqueues, so the events
+    time the call alone, with the logits possibly in the 256 MB MALL.
+    "cold": a 1 GiB device fill before each sample evicts the caches, so the
+    logits come from HBM.  Reports median, p10 and p90 over `iters` samples,
+    and GB/s of the algorithmic bytes: (4E + 8K + 8) per token for
+    moe_route (logits read; ids, weights, alpha, margin written) and
+    2 (4E + 4) per token for moe_eqb_bias (logits and alpha read once per
+    radix pass)."""
+    import ctypes
+    import numpy as np
+    from sigmoid_top_routing_router_amd import _lib
+    lib = _lib.load()
+    N, E, K = cfg.N, cfg.E, cfg.K
+    dev = Z.device
+    ids = torch.empty((N, K), dtype=torch.int32, device=dev)
+    w = torch.empty((N, K), dtype=torch.float32, device=dev)
+    alpha = torch.empty((N,), dtype=torch.float32, device=dev)
+    margin = torch.empty((N,), dtype=torch.float32, device=dev)
+    beta_out = torch.empty((E,), dtype=torch.float32, device=dev)
+    q = torch.empty((E,), dtype=torch.float32, device=dev)
+    ws_n = max(int(lib.moe_eqb_workspace_bytes(N, E, K, 16)), 256)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def call_route():
+        _lib.check(lib.moe_route(p(Z), p(beta), N, E, K, p(ids), p(w), p(alpha), p(margin), st))
+
+    def call_eqb():
+        _lib.check(lib.moe_eqb_bias(p(Z), p(beta), p(alpha), N, E, K, 16, p(beta_out), p(q),
+                                    p(ws), ws_n, st))
+
+    parts = [("moe_route", call_route, (4 * E + 8 * K + 8) * N),
+             ("moe_eqb_bias", call_eqb, 2 * (4 * E + 4) * N)]
+    call_route()  # alpha for the quantile update
+    torch.cuda.synchronize()
+    out = []
+    for name, fn, nbytes in parts:
+        for mode in ("warm", "cold"):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(iters)]
+            for e0, e1 in ev:
+                if mode == "cold":
+                    scratch.fill_(1)
+                else:
+                    torch.cuda._sleep(100000)
+                e0.record()
+                fn()
+                e1.record()
+            torch.cuda.synchronize()
+            us = np.array([1e3 * e0.elapsed_time(e1) for e0, e1 in ev])
+            med = float(np.median(us))
+            out.append({"part": name, "mode": mode, "median_us": round(med, 2),
+                        "p10_us": round(float(np.percentile(us, 10)), 2),
+                        "p90_us": round(float(np.percentile(us, 90)), 2),
+                        "bytes": nbytes, "gbs": round(nbytes / med / 1e3, 1),
+                        "hbm_frac": round(nbytes / med / 1e3 / PEAK_HBM_GBS, 3)})
+            log(json.dumps(out[-1]))
+    del scratch
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +242,9 @@ def main():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "kernel for scaling hardware byte counters)")
+    ap.add_argument("--parts", action="store_true",
+                    help="instead of the layer: time moe_route and moe_eqb_bias alone on the "
+                         "workload's logits (warm and cold, median/p10/p90 of --steps samples)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU run: write the routed gate/up HBM bytes per launch from two "
                          "rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE) of "
@@ -221,6 +296,16 @@ def main():
     def step():
         fwd(x, W, cfg.K, beta_in=beta, recompute_bias=cfg.recompute_bias,
             logit_offset=off, workspace=ws, out=y)
+
+    if args.parts:
+        _, aux = fwd(x, W, cfg.K, beta_in=beta, recompute_bias=cfg.recompute_bias,
+                     logit_offset=off, workspace=ws, out=y, aux=("logits",))
+        del ws, y
+        parts = bench_parts(M, torch, cfg, aux["logits"], beta, max(args.steps, 20))
+        print(json.dumps({"metric": "routing steps alone (HIP events per call)",
+                          "config": cfg.describe(), "samples": max(args.steps, 20),
+                          "parts": parts}), flush=True)
+        return
 
     # loads of the final routing (for the algorithmic byte count), untimed
     _, aux = fwd(x, W, cfg.K, beta_in=beta, recompute_bias=cfg.recompute_bias,
