@@ -242,6 +242,9 @@ def main():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "kernel for scaling hardware byte counters)")
+    ap.add_argument("--inference", action="store_true",
+                    help="route with the given bias only (no quantile update in the step), "
+                         "the layer as inference runs it")
     ap.add_argument("--parts", action="store_true",
                     help="instead of the layer: time moe_route and moe_eqb_bias alone on the "
                          "workload's logits (warm and cold, median/p10/p90 of --steps samples)")
@@ -270,6 +273,9 @@ def main():
         sys.exit(2)
     M.load_library()
     cfg = CONFIGS[args.workload]
+    if args.inference:
+        from dataclasses import replace
+        cfg = replace(cfg, recompute_bias=False)
     log("workload", cfg.describe())
     L = make_inputs(cfg)
     log("inputs ready")
