@@ -2,7 +2,9 @@
 the bias update, grouping, experts, combine) is captured once on a stream and
 replayed; every replay, with eager work and synchronisations in between, is
 bit-identical to the eager call (the path is deterministic, uses fill kernels
-instead of memsets and never synchronises with the host)."""
+instead of memsets and never synchronises with the host).  With bf16 and
+with E4M3 experts; above 64 tokens the capture also records the shared
+expert's branch on the library's side stream."""
 import numpy as np
 import pytest
 
@@ -22,25 +24,30 @@ def M():
     return M
 
 
-@pytest.mark.parametrize("name,N", [("prefill", 3000), ("decode", None), ("skewed", 2048)])
-def test_forward_graph_replay_matches_eager(M, name, N):
+@pytest.mark.parametrize("name,N,fp8", [("prefill", 3000, False), ("decode", None, False),
+                                        ("skewed", 2048, False), ("prefill", 3000, True),
+                                        ("decode", None, True)])
+def test_forward_graph_replay_matches_eager(M, name, N, fp8):
     import torch
     cfg = CONFIGS[name] if N is None else scaled(CONFIGS[name], N)
-    say("graph", cfg.name, cfg.N)
+    say("graph", cfg.name, cfg.N, "fp8" if fp8 else "bf16")
     L = make_inputs(cfg)
     W = weights_dev(L)
+    fwd, ws_fn = M.forward, M.forward_workspace_bytes
+    if fp8:
+        W = M.quantize_experts(W)
+        fwd, ws_fn = M.forward_fp8, M.forward_fp8_workspace_bytes
     x = bf16_dev(L.x)
     beta = dev(L.beta_in)
     off = dev(L.logit_offset)
-    ws = torch.empty(M.forward_workspace_bytes(cfg.N, cfg.d, cfg.E, cfg.K, cfg.h, cfg.n_shared,
-                                               cfg.h_shared, cfg.recompute_bias),
+    ws = torch.empty(ws_fn(cfg.N, cfg.d, cfg.E, cfg.K, cfg.h, cfg.n_shared, cfg.h_shared,
+                           cfg.recompute_bias),
                      dtype=torch.uint8, device="cuda")
     y = torch.empty((cfg.N, cfg.d), dtype=torch.bfloat16, device="cuda")
-    ids = torch.empty((cfg.N, cfg.K), dtype=torch.int32, device="cuda")
 
     def run():
-        M.forward(x, W, cfg.K, beta_in=beta, recompute_bias=cfg.recompute_bias,
-                  logit_offset=off, workspace=ws, out=y)
+        fwd(x, W, cfg.K, beta_in=beta, recompute_bias=cfg.recompute_bias,
+            logit_offset=off, workspace=ws, out=y)
 
     run()  # warm up (kernel attributes, occupancy queries) outside the capture
     torch.cuda.synchronize()
