@@ -11,7 +11,9 @@ namespace moe {
 
 constexpr int kTileN = 256;  // output columns (B rows) of one n-tile of the tile engine
 
-enum Mode { kGateUp = 0, kDown = 1, kRouter = 2 };
+// kRouterNarrow: the router product in 256 x 128 tiles (a launch mode of
+// gemm_kernel; the tile itself is gemm_tile<kRouter, ..., NARROW = true>)
+enum Mode { kGateUp = 0, kDown = 1, kRouter = 2, kRouterNarrow = 3 };
 
 struct GemmArgs {
   const uint16_t* A;       // x (gate/up, router) or H (down)

@@ -182,6 +182,18 @@ def test_forward_tail_rows(M, N, K, offset, d, h):
     assert np.any((A["counts"] % 256 > 0) & (A["counts"] % 256 <= 32) & (A["counts"] > 256))
 
 
+@pytest.mark.parametrize("E", [200, 136, 100])
+def test_forward_router_column_tails(M, E):
+    """The router GEMM alone (shared expert on the side stream) with column
+    counts that fill no tile: E = 200 and 136 take one 256-wide tile whose
+    waves own 64 columns each (E = 200: the last wave 8 live columns;
+    E = 136: one wave 8, the last none); E = 100 takes the 256 x 128 tile,
+    whose last 32-column block holds 4 live columns.  Logits, routing and
+    output against the oracle."""
+    cfg = replace(scaled(CONFIGS["prefill"], 700), E=E, name=f"router_tail_{E}")
+    run_case(M, cfg)
+
+
 def test_forward_without_shared_expert(M):
     cfg = replace(scaled(CONFIGS["prefill"], 200), n_shared=0, name="noshared")
     run_case(M, cfg)
