@@ -120,6 +120,7 @@ SMALL = [
     ("origin", 300),
     ("prefill", 500),
     ("decode", 64),
+    ("prefill", 65),   # first size on the tile engine and the side stream
     ("skewed", 1000),
 ]
 

@@ -176,7 +176,7 @@ def run_fp8_case(M, cfg, sample=None, use_logits_in=False):
     return err
 
 
-SMALL = [("origin", 300), ("decode", 64), ("prefill", 1), ("skewed", 600)]
+SMALL = [("origin", 300), ("decode", 64), ("prefill", 65), ("prefill", 1), ("skewed", 600)]
 
 
 @pytest.mark.parametrize("name,N", SMALL)
