@@ -182,7 +182,7 @@ def bench_parts(M, torch, cfg, Z, beta, iters):
     margin = torch.empty((N,), dtype=torch.float32, device=dev)
     beta_out = torch.empty((E,), dtype=torch.float32, device=dev)
     q = torch.empty((E,), dtype=torch.float32, device=dev)
-    ws_n = max(int(lib.moe_eqb_workspace_bytes(N, E, K, 16)), 256)
+    ws_n = max(int(lib.moe_eqb_workspace_bytes(N, E, 16)), 256)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)

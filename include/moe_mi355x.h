@@ -94,11 +94,12 @@ moe_status_t moe_route(const float* logits, const float* beta, int64_t N,
  *  alpha        [N] fp32 token bias or NULL.
  *  beta_out     [E] fp32 out: centred bias.
  *  quantile_out [E] fp32 out or NULL: the raw quantiles Q_r (beta_raw = -Q).
- *  workspace    device scratch of at least moe_eqb_workspace_bytes(...),
- *               256-byte aligned.
+ *  workspace    device scratch of at least moe_eqb_workspace_bytes(N, E,
+ *               key_bits) bytes, 256-byte aligned; 0 from the query means
+ *               N < 1, E < 1 or key_bits not 16 / 32.
  * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, WORKSPACE_TOO_SMALL, HIP.
  */
-size_t moe_eqb_workspace_bytes(int64_t N, int32_t E, int32_t K, int32_t key_bits);
+size_t moe_eqb_workspace_bytes(int64_t N, int32_t E, int32_t key_bits);
 moe_status_t moe_eqb_bias(const float* logits, const float* beta_in,
                           const float* alpha, int64_t N, int32_t E, int32_t K,
                           int32_t key_bits, float* beta_out, float* quantile_out,
@@ -265,6 +266,11 @@ typedef struct {
  * on first use, default priority), forked from `stream` at the call's start
  * and joined back into it before the combine: `stream` still orders the whole
  * call, and capturing `stream` into a HIP graph captures both branches.
+ * Graph capture: make one uncaptured call of the same entry point with the
+ * same problem, on the same device and host thread, before capturing.  The first call on a thread creates the side
+ * stream and its events, and the first call on a device sets the kernels' LDS
+ * attributes and queries their occupancy; none of these are stream work, and
+ * they are not meant to run under capture.
  *
  *  p        problem (sizes, flags, optional logits_in / logit_offset).
  *  w        weights (see moe_weights_t).

@@ -30,6 +30,9 @@ design notes of the repository):
   * Grouping: a stable sort of the (t, k) pairs by expert; within an expert
     tokens ascend.
   * Expert MLPs in fp64 with no intermediate rounding.
+  * FP8 experts: scale = fp32(amax / 448) per group, codes are the nearest
+    E4M3 values of v / scale clamped to +-448; the hidden activations H are
+    quantised per 1 x 128 group straight from fp64.
 
 Parity pins: every function here is checked in ``tests/test_oracle_*.py``
 against the pages' worked example, closed forms, brute force on tiny inputs
@@ -385,6 +388,35 @@ def quantize_weight_blocks(W: np.ndarray, block: int = 128):
     return codes, scales
 
 
+def _quantize_group_f64(v: np.ndarray):
+    """One group of fp64 values (the SwiGLU hidden activations H, which the
+    oracle holds unrounded): s = fp32(amax / 448), an fp32 scale as every
+    scale of the FP8 path; the codes of min(max(v / s, -448), 448) with v / s
+    taken in fp64 (an all-zero group: s = 0, codes 0)."""
+    v = np.asarray(v, F64)
+    amax = float(np.max(np.abs(v))) if v.size else 0.0
+    s = np.float32(amax / E4M3_MAX)
+    if s == 0:
+        return np.zeros(v.shape, np.uint8), np.float32(0)
+    q = np.clip(v / F64(s), -E4M3_MAX, E4M3_MAX)
+    return e4m3_encode(q), s
+
+
+def quantize_row_groups_f64(X: np.ndarray, group: int = 128):
+    """As quantize_row_groups for fp64 rows (each 1 x group piece through
+    _quantize_group_f64)."""
+    X = np.asarray(X, F64)
+    N, C = X.shape
+    codes = np.zeros((N, C), np.uint8)
+    scales = np.zeros((N, (C + group - 1) // group), F32)
+    for j in range(scales.shape[1]):
+        for n in range(N):
+            q, sc = _quantize_group_f64(X[n, j * group:(j + 1) * group])
+            codes[n, j * group:(j + 1) * group] = q
+            scales[n, j] = sc
+    return codes, scales
+
+
 def quantize_row_groups(X: np.ndarray, group: int = 128):
     """[N, C] -> (codes [N, C] uint8, scales [N, ceil(C/g)] fp32), one scale
     per 1 x group piece of a row (the dynamic activation quantisation)."""
@@ -416,14 +448,15 @@ def dequantize_row_groups(codes: np.ndarray, scales: np.ndarray, group: int = 12
 
 
 def swiglu_fp8(x_codes, x_scales, g_codes, g_scales, u_codes, u_scales, d_codes, d_scales):
-    """One SwiGLU expert on FP8 operands: G = X W_g^T and U = X W_u^T on the
-    dequantised values (fp64), H = SiLU(G) * U held in bf16, H quantised per
-    1 x 128 group, then H W_d^T on the dequantised values."""
+    """One SwiGLU expert on FP8 operands ([K1D] FP8 section): G = X W_g^T and
+    U = X W_u^T on the dequantised values, H = SiLU(G) * U, all in fp64; H,
+    the activation entering the down projection, is quantised dynamically per
+    1 x 128 group straight from fp64 (the pages name no other rounding of
+    it); then H W_d^T on the dequantised values."""
     X = dequantize_row_groups(x_codes, x_scales)
     G = X @ dequantize_blocks(g_codes, g_scales).T
     U = X @ dequantize_blocks(u_codes, u_scales).T
-    Hb = bf16_to_f32(f32_to_bf16_rne(silu(G) * U))
-    hq, hs = quantize_row_groups(Hb)
+    hq, hs = quantize_row_groups_f64(silu(G) * U)
     return dequantize_row_groups(hq, hs) @ dequantize_blocks(d_codes, d_scales).T
 
 

@@ -8,6 +8,7 @@ a non-GPU tensor raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
 from dataclasses import dataclass
 from typing import Optional
@@ -59,6 +60,15 @@ def _stream(stream):
     return C.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Allocation context of a call: with an explicit stream, the outputs and
+    temporaries of the call are allocated on that stream, so torch's caching
+    allocator does not hand their memory to other work before the call's
+    kernels on that stream are done."""
+    torch = _torch()
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _bf16():
     torch = _torch()
     return (torch.bfloat16, torch.uint16, torch.int16)
@@ -73,13 +83,14 @@ def route(logits, K: int, beta=None, stream=None):
     logits = _dev(logits, "logits", torch.float32)
     N, E = logits.shape
     beta = _dev(beta, "beta", torch.float32, (E,))
-    dev = logits.device
-    ids = torch.empty((N, K), dtype=torch.int32, device=dev)
-    w = torch.empty((N, K), dtype=torch.float32, device=dev)
-    alpha = torch.empty((N,), dtype=torch.float32, device=dev)
-    margin = torch.empty((N,), dtype=torch.float32, device=dev)
-    _lib.check(lib.moe_route(_ptr(logits), _ptr(beta), N, E, K, _ptr(ids), _ptr(w),
-                             _ptr(alpha), _ptr(margin), _stream(stream)))
+    with _on(stream):
+        dev = logits.device
+        ids = torch.empty((N, K), dtype=torch.int32, device=dev)
+        w = torch.empty((N, K), dtype=torch.float32, device=dev)
+        alpha = torch.empty((N,), dtype=torch.float32, device=dev)
+        margin = torch.empty((N,), dtype=torch.float32, device=dev)
+        _lib.check(lib.moe_route(_ptr(logits), _ptr(beta), N, E, K, _ptr(ids), _ptr(w),
+                                 _ptr(alpha), _ptr(margin), _stream(stream)))
     return ids, w, alpha, margin
 
 
@@ -94,11 +105,12 @@ def route_stats(topk_ids, E: int, topk_ids_unbiased=None, margin=None, tau: floa
     N, K = topk_ids.shape
     topk_ids_unbiased = _dev(topk_ids_unbiased, "topk_ids_unbiased", torch.int32, (N, K))
     margin = _dev(margin, "margin", torch.float32, (N,))
-    counts = torch.empty((E,), dtype=torch.int32, device=topk_ids.device)
-    stats = torch.empty((C.sizeof(_lib.MoeRouteStats) // 8,), dtype=torch.float64,
-                        device=topk_ids.device)
-    _lib.check(lib.moe_route_stats(_ptr(topk_ids), _ptr(topk_ids_unbiased), _ptr(margin), N, E,
-                                   K, float(tau), _ptr(counts), _ptr(stats), _stream(stream)))
+    with _on(stream):
+        counts = torch.empty((E,), dtype=torch.int32, device=topk_ids.device)
+        stats = torch.empty((C.sizeof(_lib.MoeRouteStats) // 8,), dtype=torch.float64,
+                            device=topk_ids.device)
+        _lib.check(lib.moe_route_stats(_ptr(topk_ids), _ptr(topk_ids_unbiased), _ptr(margin), N, E,
+                                       K, float(tau), _ptr(counts), _ptr(stats), _stream(stream)))
     return counts, stats
 
 
@@ -122,25 +134,26 @@ def lei_backward(topk_ids, E: int, logits=None, grad_scores=None, lam: float = 1
     N, K = topk_ids.shape
     logits = _dev(logits, "logits", torch.float32, (N, E))
     grad_scores = _dev(grad_scores, "grad_scores", torch.float32, (N, E))
-    dev_ = topk_ids.device
-    if inplace:
-        if grad_scores is None:
-            raise ValueError("inplace needs grad_scores")
-        gout = grad_scores
-    else:
-        gout = torch.empty((N, E), dtype=torch.float32, device=dev_) if scores_out else None
-    dz = torch.empty((N, E), dtype=torch.float32, device=dev_) if logits_out else None
-    inj = torch.empty((E,), dtype=torch.float32, device=dev_)
-    need = int(lib.moe_lei_workspace_bytes(E))
-    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev_)
-    _lib.check(lib.moe_lei_backward(_ptr(logits), _ptr(topk_ids), _ptr(grad_scores), N, E, K,
-                                    float(lam), float(tau), _ptr(gout), _ptr(dz), _ptr(inj),
-                                    _ptr(ws), ws.numel(), _stream(stream)))
+    with _on(stream):
+        dev_ = topk_ids.device
+        if inplace:
+            if grad_scores is None:
+                raise ValueError("inplace needs grad_scores")
+            gout = grad_scores
+        else:
+            gout = torch.empty((N, E), dtype=torch.float32, device=dev_) if scores_out else None
+        dz = torch.empty((N, E), dtype=torch.float32, device=dev_) if logits_out else None
+        inj = torch.empty((E,), dtype=torch.float32, device=dev_)
+        need = int(lib.moe_lei_workspace_bytes(E))
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev_)
+        _lib.check(lib.moe_lei_backward(_ptr(logits), _ptr(topk_ids), _ptr(grad_scores), N, E, K,
+                                        float(lam), float(tau), _ptr(gout), _ptr(dz), _ptr(inj),
+                                        _ptr(ws), ws.numel(), _stream(stream)))
     return gout, dz, inj
 
 
-def eqb_workspace_bytes(N: int, E: int, K: int, key_bits: int = 16) -> int:
-    return int(_lib.load().moe_eqb_workspace_bytes(N, E, K, key_bits))
+def eqb_workspace_bytes(N: int, E: int, key_bits: int = 16) -> int:
+    return int(_lib.load().moe_eqb_workspace_bytes(N, E, key_bits))
 
 
 def eqb_bias(logits, K: int, beta_in=None, alpha=None, key_bits: int = 16,
@@ -153,14 +166,15 @@ def eqb_bias(logits, K: int, beta_in=None, alpha=None, key_bits: int = 16,
     N, E = logits.shape
     beta_in = _dev(beta_in, "beta_in", torch.float32, (E,))
     alpha = _dev(alpha, "alpha", torch.float32, (N,))
-    need = int(lib.moe_eqb_workspace_bytes(N, E, K, key_bits))
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=logits.device)
-    beta_out = torch.empty((E,), dtype=torch.float32, device=logits.device)
-    q = torch.empty((E,), dtype=torch.float32, device=logits.device)
-    _lib.check(lib.moe_eqb_bias(_ptr(logits), _ptr(beta_in), _ptr(alpha), N, E, K, key_bits,
-                                _ptr(beta_out), _ptr(q), _ptr(workspace),
-                                workspace.numel() * workspace.element_size(), _stream(stream)))
+    with _on(stream):
+        need = int(lib.moe_eqb_workspace_bytes(N, E, key_bits))
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=logits.device)
+        beta_out = torch.empty((E,), dtype=torch.float32, device=logits.device)
+        q = torch.empty((E,), dtype=torch.float32, device=logits.device)
+        _lib.check(lib.moe_eqb_bias(_ptr(logits), _ptr(beta_in), _ptr(alpha), N, E, K, key_bits,
+                                    _ptr(beta_out), _ptr(q), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)))
     return beta_out, q
 
 
@@ -264,11 +278,12 @@ def fp8_quantize_blocks(w, stream=None):
     if w3.dim() != 3:
         raise ValueError("w must be [R, C] or [count, R, C]")
     cnt, R, Cc = w3.shape
-    codes = torch.empty((cnt, R, Cc), dtype=torch.uint8, device=w.device)
-    scales = torch.empty((cnt, (R + 127) // 128, (Cc + 127) // 128), dtype=torch.float32,
-                         device=w.device)
-    _lib.check(_lib.load().moe_fp8_quantize_blocks(_ptr(w3), cnt, R, Cc, _ptr(codes),
-                                                   _ptr(scales), _stream(stream)))
+    with _on(stream):
+        codes = torch.empty((cnt, R, Cc), dtype=torch.uint8, device=w.device)
+        scales = torch.empty((cnt, (R + 127) // 128, (Cc + 127) // 128), dtype=torch.float32,
+                             device=w.device)
+        _lib.check(_lib.load().moe_fp8_quantize_blocks(_ptr(w3), cnt, R, Cc, _ptr(codes),
+                                                       _ptr(scales), _stream(stream)))
     return (codes[0], scales[0]) if squeeze else (codes, scales)
 
 
@@ -278,10 +293,11 @@ def fp8_quantize_rows(x, stream=None):
     torch = _torch()
     x = _dev(x, "x", _bf16())
     n, Cc = x.shape
-    codes = torch.empty((n, Cc), dtype=torch.uint8, device=x.device)
-    scales = torch.empty((n, Cc // 128), dtype=torch.float32, device=x.device)
-    _lib.check(_lib.load().moe_fp8_quantize_rows(_ptr(x), n, Cc, _ptr(codes), _ptr(scales),
-                                                 _stream(stream)))
+    with _on(stream):
+        codes = torch.empty((n, Cc), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((n, Cc // 128), dtype=torch.float32, device=x.device)
+        _lib.check(_lib.load().moe_fp8_quantize_rows(_ptr(x), n, Cc, _ptr(codes), _ptr(scales),
+                                                     _stream(stream)))
     return codes, scales
 
 
@@ -347,15 +363,16 @@ def _run_forward(fp8, x, wstruct, N, d, E, K, h, n_shared, h_shared, beta_in, re
     need = int(ws_fn(C.byref(p)))
     if need == 0:  # rejected shape: the call reports why
         _lib.check(fwd(C.byref(p), None, None, None, None, None, None, 0, None))
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    y = out if out is not None else torch.empty((N, d), dtype=torch.bfloat16, device=x.device)
-    _dev(y, "out", _bf16(), (N, d))
-    aux_t = _aux_tensors(aux, N, E, K, x.device)
-    a = MoeAux(*[_ptr(aux_t.get(f)) for f in AUX_FIELDS]) if aux_t else None
-    _lib.check(fwd(C.byref(p), C.byref(wstruct), _ptr(x), _ptr(beta_in), _ptr(y),
-                   C.byref(a) if a is not None else None, _ptr(workspace),
-                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    with _on(stream):
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        y = out if out is not None else torch.empty((N, d), dtype=torch.bfloat16, device=x.device)
+        _dev(y, "out", _bf16(), (N, d))
+        aux_t = _aux_tensors(aux, N, E, K, x.device)
+        a = MoeAux(*[_ptr(aux_t.get(f)) for f in AUX_FIELDS]) if aux_t else None
+        _lib.check(fwd(C.byref(p), C.byref(wstruct), _ptr(x), _ptr(beta_in), _ptr(y),
+                       C.byref(a) if a is not None else None, _ptr(workspace),
+                       workspace.numel() * workspace.element_size(), _stream(stream)))
     return (y, aux_t) if aux else y
 
 

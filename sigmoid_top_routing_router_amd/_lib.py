@@ -88,7 +88,7 @@ def load(path: str = LIB_PATH):
     vp, i64, i32 = C.c_void_p, C.c_int64, C.c_int32
     lib.moe_route.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp, vp, vp]
     lib.moe_route.restype = C.c_int
-    lib.moe_eqb_workspace_bytes.argtypes = [i64, i32, i32, i32]
+    lib.moe_eqb_workspace_bytes.argtypes = [i64, i32, i32]
     lib.moe_eqb_workspace_bytes.restype = C.c_size_t
     lib.moe_eqb_bias.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, C.c_size_t, vp]
     lib.moe_eqb_bias.restype = C.c_int

@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256) void dense_small_finalize(const float* part, i
 }
 
 // E4M3 gate/up: one wave per (token, 1 x 128 group of H); lane l takes the
-// hidden columns 2l, 2l+1 of the group.  H is rounded to bf16, then quantised
+// hidden columns 2l, 2l+1 of the group.  H is quantised from its fp32 value
 // with s = amax / 448 as the tile engine's epilogue does.
 __global__ __launch_bounds__(256) void dense_small_finalize_fp8(const float* part, int chunks,
                                                                 int64_t N, int R, int R0,
@@ -212,8 +212,8 @@ __global__ __launch_bounds__(256) void dense_small_finalize_fp8(const float* par
     const float gg = sum_chunks(part, chunks, N, R, t, c);
     const float uu = sum_chunks(part, chunks, N, R, t, R0 + c);
     const float h = gg * __builtin_amdgcn_rcpf(1.0f + __expf(-gg)) * uu;
-    hb[j] = bf16_bits_to_f32(f32_to_bf16_rne_bits(h));
-    m = max(m, __float_as_uint(fabsf(hb[j])));
+    hb[j] = h;
+    m = max(m, __float_as_uint(fabsf(h)));
   }
   m = wave_max_u32(m);
   const float amax = __uint_as_float(m);

@@ -103,9 +103,52 @@ __device__ __forceinline__ bool xcd_tile(int64_t work, int64_t& logical) {
   return logical < work;
 }
 
+// Quantised H of the E4M3 gate/up tile: the tile's fp32 values are staged in
+// LDS (row stride QSTRIDE bytes); the 128 columns of a tile row are one
+// 1 x 128 group (ldo % 128 == 0), held by 16 neighbouring lanes of 8 values
+// each, quantised as s = amax / 448 and the E4M3 codes of
+// min(max(v / s, -448), 448), straight from fp32.
+constexpr int QSTRIDE = (kTileN / 2) * 4 + 16;
+template <int TROWS>
+__device__ __forceinline__ void epilogue_store_q(const GemmArgs& a, int nt, int64_t row0,
+                                                 int rows, int tid, const char* lds_raw) {
+  constexpr int CPR = (kTileN / 2) / 8;  // 8-value pieces per tile row
+  const int col0 = nt * (kTileN / 2);
+  uint8_t* q = reinterpret_cast<uint8_t*>(a.out);
+  const int groups = (int)(a.ldo / 128);
+  for (int c = tid; c < TROWS * CPR; c += 512) {
+    const int rr = c / CPR, ch = c % CPR;
+    if (rr >= rows) break;  // the 16 lanes of a row leave together
+    const char* src = lds_raw + rr * QSTRIDE + ch * 32;
+    const float4 lo = *reinterpret_cast<const float4*>(src);
+    const float4 hi = *reinterpret_cast<const float4*>(src + 16);
+    const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(fabsf(v[j])));
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    const float amax = __uint_as_float(m);
+    const float sc = amax / 448.0f;
+    uint32_t cw[2] = {0u, 0u};
+    if (amax != 0.0f) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float t[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] = fminf(fmaxf(v[4 * j + i] / sc, -448.0f), 448.0f);
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], pk, true);
+        cw[j] = (uint32_t)pk;
+      }
+    }
+    *reinterpret_cast<uint2*>(q + (row0 + rr) * a.ldo + col0 + ch * 8) = make_uint2(cw[0], cw[1]);
+    if (ch == 0) a.out_scale[(row0 + rr) * groups + nt] = (amax != 0.0f) ? sc : 0.0f;
+  }
+}
+
 // Second half of the bf16-output epilogue: the tile staged in LDS (row
-// stride OSTRIDE bytes) goes to global memory in whole rows, as bf16 or, for
-// gate/up with a.out_scale set, as E4M3 codes with one scale per row group.
+// stride OSTRIDE bytes) goes to global memory in whole rows.
 template <int MODE, int TROWS = BM>
 __device__ __forceinline__ void epilogue_store(const GemmArgs& a, int nt, int64_t row0, int rows,
                                                int tid, const char* lds_raw) {
@@ -113,49 +156,6 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& a, int nt, int64_
   constexpr int OSTRIDE = OCOLS * 2 + 8;
   constexpr int CPR = OCOLS / 8;  // 16-byte chunks per tile row
   const int col0 = nt * OCOLS;
-  if (MODE == kGateUp && a.out_scale) {
-    // Quantised H: the 128 columns of a tile row are one 1 x 128 group
-    // (ldo % 128 == 0), held by 16 neighbouring lanes of 8 values each.  The
-    // bf16 values are quantised as a separate pass over H would do it:
-    // s = amax / 448, codes of min(max(v / s, -448), 448).
-    uint8_t* q = reinterpret_cast<uint8_t*>(a.out);
-    const int groups = (int)(a.ldo / 128);
-    for (int c = tid; c < TROWS * CPR; c += 512) {
-      const int rr = c / CPR, ch = c % CPR;
-      if (rr >= rows) break;  // the 16 lanes of a row leave together
-      const char* src = lds_raw + rr * OSTRIDE + ch * 16;
-      const uint2 lo = *reinterpret_cast<const uint2*>(src);
-      const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
-      const uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
-      float v[8];
-      uint32_t m = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[2 * j] = __uint_as_float(w[j] << 16);
-        v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-        m = max(m, max(w[j] << 17 >> 1, (w[j] & 0x7FFF0000u)));
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-      const float amax = __uint_as_float(m);
-      const float sc = amax / 448.0f;
-      uint32_t cw[2] = {0u, 0u};
-      if (amax != 0.0f) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          float t[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) t[i] = fminf(fmaxf(v[4 * j + i] / sc, -448.0f), 448.0f);
-          int pk = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
-          pk = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], pk, true);
-          cw[j] = (uint32_t)pk;
-        }
-      }
-      *reinterpret_cast<uint2*>(q + (row0 + rr) * a.ldo + col0 + ch * 8) = make_uint2(cw[0], cw[1]);
-      if (ch == 0) a.out_scale[(row0 + rr) * groups + nt] = (amax != 0.0f) ? sc : 0.0f;
-    }
-    return;
-  }
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
   if constexpr (MODE == kDown) {
     // Every LDS read of the tile first, then the stores: a lane keeps one
@@ -962,10 +962,11 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
     else run(std::integral_constant<int, 4>{});
   }
 
-  // ---- epilogue: stage the bf16 tile in LDS (four consecutive columns per
-  // 8-byte store), then write whole rows
+  // ---- epilogue: stage the tile in LDS (four consecutive columns per lane
+  // and store; gate/up: H in fp32, 16 bytes; down: bf16, 8 bytes), then write
+  // whole rows (gate/up: quantised to E4M3)
   constexpr int OCOLS = (MODE == kGateUp) ? BN / 2 : BN;
-  constexpr int OSTRIDE = OCOLS * 2 + 8;
+  constexpr int OSTRIDE = (MODE == kGateUp) ? QSTRIDE : OCOLS * 2 + 8;
   static_assert((BM + XR) * OSTRIDE <= LDS_BYTES, "staged tile exceeds the LDS");
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   auto pack2 = [](float x, float y) {
@@ -984,8 +985,8 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
           const float u = c[f + 2][j];
           hv[j] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
         }
-        *reinterpret_cast<uint2*>(lrow + (b_col[f] + 4 * quad) * 2) =
-            make_uint2(pack2(hv[0], hv[1]), pack2(hv[2], hv[3]));
+        *reinterpret_cast<float4*>(lrow + (b_col[f] + 4 * quad) * 4) =
+            make_float4(hv[0], hv[1], hv[2], hv[3]);
       }
     } else {
 #pragma unroll
@@ -1004,7 +1005,8 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
     if (XR > 0) stage_block(accx, BM + 16 * wg + fr);
   }
   __syncthreads();
-  epilogue_store<MODE, BM + XR>(a, nt, row0, rows, tid, lds_raw);
+  if constexpr (MODE == kGateUp) epilogue_store_q<BM + XR>(a, nt, row0, rows, tid, lds_raw);
+  else epilogue_store<MODE, BM + XR>(a, nt, row0, rows, tid, lds_raw);
 }
 
 // A segment held by one m-tile (its first tile is also its last) multiplies

@@ -538,7 +538,7 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 1; }
+int32_t moe_abi_version(void) { return 2; }
 
 moe_status_t moe_stage_timing(int32_t enable) {
   if (enable < 0 || enable > 2) return fail(MOE_ERR_INVALID_ARGUMENT, "enable=%d outside [0, 2]", enable);
@@ -611,8 +611,7 @@ moe_status_t moe_route(const float* logits, const float* beta, int64_t N, int32_
   return ok();
 }
 
-size_t moe_eqb_workspace_bytes(int64_t N, int32_t E, int32_t K, int32_t key_bits) {
-  (void)K;
+size_t moe_eqb_workspace_bytes(int64_t N, int32_t E, int32_t key_bits) {
   if (N < 1 || E < 1 || (key_bits != 16 && key_bits != 32)) return 0;
   Carver c(nullptr);
   carve_eqb(c, N, E, key_bits);
@@ -631,7 +630,7 @@ moe_status_t moe_eqb_bias(const float* logits, const float* beta_in, const float
   const void* ptrs[] = {logits, beta_in, alpha, beta_out, quantile_out};
   for (const void* q : ptrs)
     if (q && !aligned(q, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "pointer not 4-byte aligned");
-  const size_t need = moe_eqb_workspace_bytes(N, E, K, key_bits);
+  const size_t need = moe_eqb_workspace_bytes(N, E, key_bits);
   if (!workspace || !aligned(workspace, kAlign))
     return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
   if (workspace_bytes < need)

@@ -20,6 +20,8 @@
 // value of the (K+1)-th largest key does not depend on how ties are ordered,
 // so each lane sorts its keys and K+1 rounds pop the wave-wide maximum, with
 // no ids.
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -324,12 +326,14 @@ __global__ __launch_bounds__(256) void route_group_kernel(
 // Blocks of 256 threads of one variant that the device holds at once
 // (occupancy x compute units), queried once per variant and device.
 // kind 0: one wave per row, 1: its keys-only variant, 2: 16 lanes per row.
+// Host threads may race to fill an entry; each computes the same value.
 static int64_t route_resident_blocks(int nv, int kind) {
-  static int64_t cache[3][8][7] = {};
+  static std::atomic<int64_t> cache[3][8][7] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 8) return 2048;
-  int64_t& c = cache[kind][dev][nv];
-  if (c) return c;
+  std::atomic<int64_t>& c = cache[kind][dev][nv];
+  const int64_t known = c.load(std::memory_order_relaxed);
+  if (known) return known;
   const void* fn = nullptr;
   switch (nv) {
 #define MOE_ROUTE_FN(V)                                                        \
@@ -347,8 +351,9 @@ static int64_t route_resident_blocks(int nv, int kind) {
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       per_cu <= 0 || cus <= 0)
     return 2048;
-  c = (int64_t)per_cu * cus;
-  return c;
+  const int64_t v = (int64_t)per_cu * cus;
+  c.store(v, std::memory_order_relaxed);
+  return v;
 }
 
 hipError_t launch_route(const float* Z, const float* beta, int64_t N, int E, int K,

@@ -20,13 +20,15 @@
 //  * E4M3: v_mfma_f32_16x16x128_f8f6f4 covers one 128-k scale block; its
 //    product (from zero) is added to the fp32 accumulator times
 //    s_A(row, kb) * s_B(block, kb);
-//  * epilogues as in the tile engine: gate/up SiLU(g) * u in bf16 or
-//    quantised to E4M3 per 1 x 128 group (amax across the block's four waves
-//    through LDS), down bf16.
+//  * epilogues as in the tile engine: gate/up SiLU(g) * u in bf16 or, from
+//    its fp32 value, quantised to E4M3 per 1 x 128 group (amax across the
+//    block's four waves through LDS), down bf16.
 // Only the routed (grouped) products use it; the grid covers the m-tile
 // table's capacity and surplus blocks exit.
-// The blocks need no LDS ring, so several blocks share a CU and the loads of
-// all of them overlap.
+// Each wave streams its weight rows through a ring of its own in LDS (bf16:
+// 4 x 10 KB k-sets per wave, 160 KB per block; E4M3: 3 x 11 KB per wave,
+// 132 KB per block), so one block occupies a CU; the bytes in flight
+// come from the three (two) k-sets each wave keeps loading ahead.
 #include "common.h"
 #include "gemm_args.h"
 #include "kernels.h"
@@ -256,17 +258,16 @@ __global__ __launch_bounds__(256) void skinny_kernel(GemmArgs a, int n_chunks) {
       }
       if (FP8 && a.out_scale) {
         // the block's 128 hidden columns of row t are one 1 x 128 group: amax
-        // of the bf16 values over the 4 lanes of the row in each wave, then
+        // of the fp32 values over the 4 lanes of the row in each wave, then
         // over the waves through LDS
         float v[8];
         uint32_t m = 0;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            v[4 * mb + 2 * j] = __uint_as_float(hb[mb][j] << 16);
-            v[4 * mb + 2 * j + 1] = __uint_as_float(hb[mb][j] & 0xFFFF0000u);
-            m = max(m, max(hb[mb][j] << 17 >> 1, hb[mb][j] & 0x7FFF0000u));
+          for (int r = 0; r < 4; ++r) {
+            v[4 * mb + r] = hv[mb][r];
+            m = max(m, __float_as_uint(fabsf(hv[mb][r])));
           }
         m = max(m, (uint32_t)__shfl_xor((int)m, 16));
         m = max(m, (uint32_t)__shfl_xor((int)m, 32));

@@ -83,6 +83,45 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
+def check_output(y, yref, label=""):
+    """Layer output against the oracle's: the pooled relative L2 over the
+    rows and the relative L2 of every row (token) on its own, each within
+    Y_REL_L2.  Returns (pooled, worst row)."""
+    y = np.asarray(y, np.float64)
+    yref = np.asarray(yref, np.float64)
+    pooled = rel_l2(y, yref)
+    per = np.linalg.norm(y - yref, axis=1) / np.maximum(np.linalg.norm(yref, axis=1), 1e-300)
+    worst = float(per.max()) if per.size else 0.0
+    say(label, "rel L2 pooled", f"{pooled:.3e}", "worst token", f"{worst:.3e}",
+        "at row", int(per.argmax()) if per.size else -1)
+    assert pooled <= Y_REL_L2, f"{label}: pooled rel L2 {pooled:.3e}"
+    assert worst <= Y_REL_L2, f"{label}: token {int(per.argmax())} rel L2 {worst:.3e}"
+    return pooled, worst
+
+
+def free_running_mismatch(own, A, Zg):
+    """Selections of the GPU (its own logits and bias) against the oracle's
+    (its own logits and bias).  Both select the K largest of B = Z + beta;
+    every entry of B moves by at most |dZ_t| + |dbeta| (plus the rounding of
+    the fp32 add), so a token's selection can only differ where the oracle's
+    margin B_(K) - B_(K+1) is below 2 (max_e |dZ_t,e| + max_e |dbeta_e|).
+    The allowance per token is NEAR_TIE + that bound (the near-tie threshold
+    covers the rounding).  Returns a dict of counts; 'beyond' must be 0."""
+    diff = np.any(np.sort(own["topk_ids"], 1) != np.sort(A["topk_ids"], 1), axis=1)
+    dz = np.max(np.abs(Zg.astype(np.float64) - own["logits"].astype(np.float64)), axis=1)
+    dbeta = 0.0
+    if "beta_out" in own and "beta_out" in A:
+        dbeta = float(np.max(np.abs(A["beta_out"].astype(np.float64)
+                                    - own["beta_out"].astype(np.float64))))
+    allow = NEAR_TIE + 2.0 * (dz + dbeta)
+    margin = own["margin"].astype(np.float64)
+    beyond = diff & ~(margin < allow)
+    return {"tokens": int(diff.size), "mismatches": int(diff.sum()),
+            "near_ties": int(np.sum(margin < NEAR_TIE)),
+            "max_abs_dbeta": dbeta, "max_abs_dz": float(dz.max()),
+            "beyond_bound": int(beyond.sum()), "diff": diff}
+
+
 def bits_equal(a, b):
     a = np.ascontiguousarray(a)
     b = np.ascontiguousarray(b)

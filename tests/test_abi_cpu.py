@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
 
@@ -89,10 +89,10 @@ def test_forward_workspace_sizes(lib):
 
 
 def test_eqb_workspace_sizes(lib):
-    b16 = lib.moe_eqb_workspace_bytes(65536, 384, 6, 16)
-    b32 = lib.moe_eqb_workspace_bytes(65536, 384, 6, 32)
+    b16 = lib.moe_eqb_workspace_bytes(65536, 384, 16)
+    b32 = lib.moe_eqb_workspace_bytes(65536, 384, 32)
     assert b16 >= 2 * 384 * 256 * 4 and b32 >= 4 * 384 * 256 * 4 and b32 > b16
-    assert lib.moe_eqb_workspace_bytes(65536, 384, 6, 8) == 0
+    assert lib.moe_eqb_workspace_bytes(65536, 384, 8) == 0
 
 
 @pytest.mark.parametrize("N,E,K,status", [(0, 384, 6, 2), (10, 384, 0, 2), (10, 384, 9, 2),

@@ -3,9 +3,12 @@
 For every case: router logits within 1e-4 relative; given the GPU's logits,
 the selections, token biases, margins, expert biases, quantiles, loads,
 offsets and the permutation bit-exact; sigmoid weights within 1e-6; the
-layer output within 2e-2 relative L2 (on all tokens, or on a seeded sample of
-tokens at the full sizes).  Where asked, a free-running comparison (oracle
-on its own logits) allows selection differences only at near-ties."""
+layer output within 2e-2 relative L2, pooled and for every token on its own
+(on all tokens, or on a seeded sample of tokens at the full sizes).  Where
+asked, a free-running comparison (the oracle on its own logits and its own
+bias update): selections may differ only where the oracle's margin is below
+the near-tie threshold plus twice the largest logit and bias differences,
+and the output is within 2e-2 relative L2 of the oracle's own output."""
 from dataclasses import replace
 
 import numpy as np
@@ -13,8 +16,9 @@ import pytest
 
 from oracle import moe_oracle as O
 from synth import CONFIGS, make_inputs, scaled
-from tests.gpu_util import (NEAR_TIE, S_RTOL, Y_REL_L2, bf16_dev, bits_equal, check_logits,
-                            dev, host, oracle_weights, rel_l2, say, weights_dev)
+from tests.gpu_util import (S_RTOL, Y_REL_L2, bf16_dev, bits_equal, check_logits, check_output,
+                            dev, free_running_mismatch, host, oracle_weights, rel_l2, say,
+                            weights_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -90,27 +94,29 @@ def run_case(M, cfg, key_bits=16, sample=None, free_running=False, use_logits_in
                    / np.abs(ref["topk_weights"]))
     assert S_err <= S_RTOL, S_err
 
-    # experts and combine: the output on the sampled tokens (routing of the GPU = oracle's on Zg)
+    # experts and combine, (ii) the GPU's routing forced into the oracle (= the
+    # oracle's on Zg): pooled and per-token relative L2 on the sampled tokens
     yref = O.moe_combine(xf, **oracle_weights(L), ids=ref["topk_ids"], S=ref["topk_weights"],
                          token_subset=rows)
-    err = rel_l2(y[rows], yref)
-    say(cfg.name, "rel L2", f"{err:.3e}")
-    assert err <= Y_REL_L2, err
+    check_output(y[rows], yref, f"{cfg.name} forced ids")
 
     if free_running:
+        # (i) the oracle on its own logits and its own bias update
         own = O.moe_layer(x=xf, w_router=wr, **oracle_weights(L), beta_in=L.beta_in, K=cfg.K,
                           recompute_bias=cfg.recompute_bias, key_bits=key_bits,
                           logit_offset=L.logit_offset, compute_output=False)
-        diff = np.any(np.sort(own["topk_ids"], 1) != np.sort(A["topk_ids"], 1), axis=1)
-        near = own["margin"] < NEAR_TIE
-        say(cfg.name, "free-running mismatches", int(diff.sum()), "near-ties", int(near.sum()))
-        if not cfg.recompute_bias:
-            assert not np.any(diff & ~near)
-        else:
-            # the bias itself comes from the logits; allow the tokens whose selection
-            # changed through a bias difference only if the biases differ at all
-            if bits_equal(own["beta_out"], A["beta_out"]):
-                assert not np.any(diff & ~near)
+        fr = free_running_mismatch(own, A, Zg)
+        diff = fr.pop("diff")
+        say(cfg.name, "free-running", fr)
+        assert fr["beyond_bound"] == 0, fr
+        yown = O.moe_combine(xf, **oracle_weights(L), ids=own["topk_ids"],
+                             S=own["topk_weights"], token_subset=rows)
+        pooled = rel_l2(y[rows], yown)
+        say(cfg.name, "free-running rel L2", f"{pooled:.3e}")
+        assert pooled <= Y_REL_L2, pooled
+        same = ~diff[rows]
+        if same.any():
+            check_output(y[rows][same], yown[same], f"{cfg.name} free-running, same selection")
     return y, A
 
 
@@ -225,8 +231,8 @@ def test_forward_deterministic(M):
 
 
 # Full sizes of the workloads (the benchmark's launch configuration).
-@pytest.mark.parametrize("name,sample,free", [("origin", 256, False), ("decode", None, True),
-                                              ("prefill", 256, True), ("skewed", 192, False)])
+@pytest.mark.parametrize("name,sample,free", [("origin", 256, True), ("decode", None, True),
+                                              ("prefill", 256, True), ("skewed", 256, True)])
 def test_forward_full_size(M, name, sample, free):
     run_case(M, CONFIGS[name], sample=sample, free_running=free)
 

@@ -7,7 +7,8 @@ quantised per 1 x 128 group, router in bf16).
 * moe_forward_fp8 on a synthetic E4M3 checkpoint: routing, loads and grouping
   bit-exact and equal to moe_forward's for the same logits; the layer output
   within 2e-2 relative L2 of the oracle's FP8 layer (fp64 on the dequantised
-  operands) on every token, or on a seeded sample at the full sizes."""
+  operands, H quantised from fp64), pooled and for every token on its own,
+  on all tokens, or on 256 seeded tokens at the full size."""
 from dataclasses import replace
 
 import numpy as np
@@ -15,8 +16,8 @@ import pytest
 
 from oracle import moe_oracle as O
 from synth import CONFIGS, make_fp8_experts, make_inputs, scaled
-from tests.gpu_util import (S_RTOL, Y_REL_L2, bf16_dev, bits_equal, check_logits, dev, host,
-                            rel_l2, say, weights_dev)
+from tests.gpu_util import (S_RTOL, bf16_dev, bits_equal, check_logits, check_output, dev,
+                            host, say, weights_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -170,9 +171,7 @@ def run_fp8_case(M, cfg, sample=None, use_logits_in=False):
         for k in ("ws_gate", "ss_gate", "ws_up", "ss_up", "ws_down", "ss_down"):
             qo[k] = q[k][:0]
     yref = O.moe_combine_fp8(xf, qo, ref["topk_ids"], ref["topk_weights"], token_subset=rows)
-    err = rel_l2(y[rows], yref)
-    say("fp8 forward", cfg.name, "rel L2", f"{err:.3e}")
-    assert err <= Y_REL_L2, err
+    err, _ = check_output(y[rows], yref, f"fp8 forward {cfg.name}")
     return err
 
 
@@ -182,7 +181,7 @@ SMALL = [("origin", 300), ("decode", 64), ("prefill", 65), ("prefill", 1), ("ske
 @pytest.mark.parametrize("name,N", SMALL)
 def test_forward_fp8_small(M, name, N):
     cfg = scaled(CONFIGS[name], N)
-    run_fp8_case(M, cfg, sample=None if cfg.E <= 128 else min(N, 32))
+    run_fp8_case(M, cfg)
 
 
 def test_forward_fp8_logits_in_and_no_shared(M):
@@ -223,8 +222,8 @@ def test_forward_fp8_segment_tails(M, N, K, offset, d, h):
 
 def test_forward_fp8_prefill_full_sampled(M):
     """The Kolibri-shaped prefill batch (N=16384, E=384, K=6, d=2560, h=512),
-    sampled tokens."""
-    run_fp8_case(M, CONFIGS["prefill"], sample=32)
+    256 sampled tokens."""
+    run_fp8_case(M, CONFIGS["prefill"], sample=256)
 
 
 def test_forward_fp8_rejects_unaligned_width(M):

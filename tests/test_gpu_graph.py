@@ -128,3 +128,43 @@ def test_forward_threads_and_streams(M):
     assert np.array_equal(host(y0), ref)
     for i in range(2):
         assert np.array_equal(outs[i], ref), f"thread {i} differs"
+
+
+def test_explicit_stream_argument(M):
+    """forward, eqb_bias and lei_backward with stream= a stream that is not
+    the current one: the binding allocates the outputs and temporaries of the
+    call on that stream, so the caching allocator cannot hand their memory to
+    work on the current stream while the call's kernels still run.  The
+    current stream is kept busy with allocations and writes of the same sizes
+    meanwhile; every result must equal the plain call's."""
+    import torch
+    cfg = scaled(CONFIGS["prefill"], 1500)
+    say("explicit stream argument", cfg.name, cfg.N)
+    L = make_inputs(cfg)
+    W = weights_dev(L)
+    x = bf16_dev(L.x)
+    beta = dev(L.beta_in)
+    kw = dict(beta_in=beta, recompute_bias=True, aux=("logits", "topk_ids"))
+    y_ref, A = M.forward(x, W, cfg.K, **kw)
+    Z = A["logits"]
+    b_ref, q_ref = M.eqb_bias(Z, cfg.K, beta_in=beta)
+    g_ref = M.lei_backward(A["topk_ids"], cfg.E, logits=Z)
+    torch.cuda.synchronize()
+    refs = [host(y_ref), host(b_ref), host(q_ref)] + [host(t) for t in g_ref]
+    nbytes = M.forward_workspace_bytes(cfg.N, cfg.d, cfg.E, cfg.K, cfg.h, cfg.n_shared,
+                                       cfg.h_shared, True)
+    s = torch.cuda.Stream()
+    for rep in range(3):
+        s.wait_stream(torch.cuda.current_stream())
+        torch.cuda._sleep(2_000_000)  # the current stream runs behind the side stream
+        y, _ = M.forward(x, W, cfg.K, stream=s, **kw)
+        b, q = M.eqb_bias(Z, cfg.K, beta_in=beta, stream=s)
+        g = M.lei_backward(A["topk_ids"], cfg.E, logits=Z, stream=s)
+        # work on the current stream that would reuse freed temporaries
+        junk = [torch.full((nbytes,), 0x5A, dtype=torch.uint8, device="cuda") for _ in range(2)]
+        del junk
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        got = [host(y), host(b), host(q)] + [host(t) for t in g]
+        for i, (a, r) in enumerate(zip(got, refs)):
+            assert np.array_equal(a, r), f"result {i} differs on repetition {rep}"

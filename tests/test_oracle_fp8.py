@@ -70,6 +70,44 @@ def test_row_group_quantisation_bounds():
             assert np.all(np.abs(d - x) <= tol)
 
 
+def test_row_group_quantisation_of_fp64_values():
+    """H is quantised from fp64: the scale is fp32(amax / 448), the largest
+    magnitude of a group lands on +-448, every value is within half an E4M3
+    step (normal) or half a subnormal step of the scale, and values that are
+    exactly a code times the scale come back unchanged."""
+    rng = np.random.default_rng(14)
+    X = rng.standard_normal((29, 384)) * np.exp(2 * rng.standard_normal((29, 1)))
+    X[4, :128] = 0.0
+    X[5, 128:256] *= 1e-7                                  # deep in the subnormals
+    X[5, 128] = 3.0
+    q, s = O.quantize_row_groups_f64(X, 128)
+    assert s.dtype == np.float32 and s[4, 0] == 0 and not q[4, :128].any()
+    D = O.dequantize_row_groups(q, s, 128)
+    for n in range(29):
+        for j in range(3):
+            x = X[n, j * 128:(j + 1) * 128]
+            if s[n, j] == 0:
+                continue
+            assert np.float32(np.abs(x).max() / 448.0) == s[n, j]
+            assert np.max(np.abs(O.e4m3_decode(q[n, j * 128:(j + 1) * 128]))) == 448.0
+            tol = np.maximum(np.abs(x) * 2.0 ** -4, np.float64(s[n, j]) * 2.0 ** -10) * (1 + 1e-9)
+            assert np.all(np.abs(D[n, j * 128:(j + 1) * 128] - x) <= tol)
+    # exact multiples of the scale: codes times a power-of-two scale
+    codes = rng.integers(0, 0x7F, (3, 128)).astype(np.uint8)
+    codes[:, 0] = 0x7E                                     # 448 sets the scale
+    vals = O.e4m3_decode(codes) * 2.0 ** -5
+    q2, s2 = O.quantize_row_groups_f64(vals, 128)
+    assert np.all(s2 == np.float32(2.0 ** -5)) and np.array_equal(q2, codes)
+    # a value just off a midpoint between two codes is decided by its fp64
+    # value, not by an fp32 rounding of it
+    mid = (O.e4m3_decode(np.array([0x30]))[0] + O.e4m3_decode(np.array([0x31]))[0]) / 2
+    row = np.zeros((1, 128))
+    row[0, 0] = 448.0
+    row[0, 1] = mid * (1 + 2.0 ** -40)
+    q3, _ = O.quantize_row_groups_f64(row, 128)
+    assert q3[0, 1] == 0x31
+
+
 def test_weight_blocks_ragged():
     rng = np.random.default_rng(13)
     W = (rng.standard_normal((300, 200)) * 0.02).astype(np.float32)
@@ -88,11 +126,11 @@ def test_weight_blocks_ragged():
 
 # ---------------------------------------------------------------------------
 # FP8 experts.  The only rounding between the dequantised operands and the
-# output is that of H (bf16, then E4M3 in 1 x 128 groups), so an FP8 expert
+# output is the E4M3 quantisation of H in 1 x 128 groups, so an FP8 expert
 # must equal the fp64 SwiGLU of the dequantised x and weights within the
 # error that this rounding can carry through W_down:
-#   |dH_j| <= |H_j| 2^-8 + max(|Hb_j| 2^-4, s_g 2^-10)
-# (half a bf16 step, then half an E4M3 step or a subnormal step of the group
+#   |dH_j| <= max(|H_j| 2^-4, s_g 2^-10)
+# (half an E4M3 step of a normal value, or half a subnormal step of the group
 # scale s_g).  The planted mistakes below show the bound is tight enough to
 # catch a transposed block-scale index and a missing quantisation of x.
 # ---------------------------------------------------------------------------
@@ -117,9 +155,8 @@ def _outlier_rows(rng, n, d, big=300.0):
 
 def _expert_bound(Xd, Gd, Ud, Dd):
     H = O.silu(Xd @ Gd.T) * (Xd @ Ud.T)
-    Hb = O.bf16_to_f32(O.f32_to_bf16_rne(H)).astype(np.float64)
-    sg = np.repeat(np.abs(Hb).reshape(H.shape[0], -1, 128).max(axis=2) / 448.0, 128, axis=1)
-    err = np.abs(H) * 2.0 ** -8 + np.maximum(np.abs(Hb) * 2.0 ** -4, sg * 2.0 ** -10)
+    sg = np.repeat(np.abs(H).reshape(H.shape[0], -1, 128).max(axis=2) / 448.0, 128, axis=1)
+    err = np.maximum(np.abs(H) * 2.0 ** -4, sg * 2.0 ** -10)
     return H, (err @ np.abs(Dd).T) * (1 + 1e-6) + 1e-12
 
 
