@@ -12,7 +12,11 @@ Prints one JSON line.  `value` is tokens per second over exactly --steps
 timed steps (inputs already in HBM, bracketed by device synchronisation).
 The `roofline` entry covers the dominant kernel (the routed gate/up GEMM),
 timed with HIP events on the library's stream during the same timed steps;
-`cpu_baseline` times the CPU oracle on a bounded sample of the same layer.
+`cpu_baseline` times the CPU oracle on the same layer (median of 3 runs,
+per-step seconds, a single-thread run of the routing steps) and `parity`
+records the GPU's outputs of one call against the oracle's on that batch.
+`extras` holds the skewed (N=65536, Zipf offsets) and decode (N=64)
+workloads measured in the same run after the headline.
 """
 from __future__ import annotations
 
@@ -25,6 +29,19 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+
+def host_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+# The CPU baseline's BLAS uses the cores this process may run on (a value
+# already set in the environment is kept); set before numpy is imported.
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_v, str(host_threads()))
 
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
@@ -131,29 +148,194 @@ def record_traffic(workload, fetch_dir, write_dir, copy_mib):
     print(json.dumps(t[workload]))
 
 
-def cpu_baseline(cfg, L, sample_tokens):
-    """The oracle (untuned) timed on a bounded sample: the whole layer for
-    the first `sample_tokens` tokens of the same inputs (the quantile update
-    runs over that sample batch).  Weight decoding to float is excluded."""
-    import numpy as np
-    from oracle import moe_oracle as O
+def _blas_info():
+    """(threads of the BLAS pool, vendor string) from threadpoolctl."""
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    n = min(sample_tokens, cfg.N)
+        pools = []
+    if not pools:
+        return host_threads(), "unknown"
+    threads = max(int(i.get("num_threads", 1)) for i in pools)
+    vendor = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in pools)
+    return threads, vendor
+
+
+def cpu_baseline(cfg, L, gpu, runs=3):
+    """The CPU baseline leg: the oracle (untuned) on the same inputs.
+
+    * Timing: the whole layer (every step) on the whole batch, `runs` runs,
+      median; the per-step seconds of the median run; routing, the quantile
+      update and the permutation once more on one thread (on the logits of
+      the first run, so the router product is not part of it).  Weight
+      decoding to float is excluded.
+    * Parity record of the same run: the GPU's outputs of one call on these
+      inputs (`gpu`: logits, selections, margins, bias, y) against the
+      oracle's, (i) free-running (the oracle on its own logits and bias) and
+      (ii) with the GPU's logits given to the oracle (routing compared bit
+      for bit, output per token)."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    threads, vendor = _blas_info()
     w = {k: O.bf16_to_f32(getattr(L, k)) for k in
          ("w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")}
-    x = O.bf16_to_f32(L.x[:n])
+    x = O.bf16_to_f32(L.x)
+    kw = dict(beta_in=L.beta_in, K=cfg.K, recompute_bias=cfg.recompute_bias)
+    times, steps, own = [], [], None
+    for r in range(runs):
+        tm = {}
+        t0 = time.perf_counter()
+        out = O.moe_layer(x=x, **w, logit_offset=L.logit_offset, timings=tm, **kw)
+        times.append(time.perf_counter() - t0)
+        steps.append(tm)
+        if own is None:
+            own = out
+        log(f"cpu baseline run {r}: {times[-1]:.2f} s")
+    med = int(np.argsort(times)[len(times) // 2])
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            tm1 = {}
+            O.moe_layer(x=x, **w, logits_in=own["logits"], compute_output=False, timings=tm1,
+                        **kw)
+    except ImportError:  # pragma: no cover
+        tm1 = None
+    base = {"value": cfg.N / times[med], "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 oracle, whole layer (all steps) on the whole {cfg.name} batch "
+                      f"(N={cfg.N}), median of {runs} runs "
+                      f"({', '.join(f'{t:.2f}' for t in times)} s)",
+            "runs_s": [round(t, 3) for t in times],
+            "steps_s": {k: round(v, 4) for k, v in steps[med].items()},
+            "blas": vendor, "threads_env": os.environ.get("OMP_NUM_THREADS")}
+    if tm1 is not None:
+        t_route = sum(tm1.get(k, 0.0) for k in ("route", "eqb", "permutation"))
+        base["single_thread"] = {"what": "routing (both passes, mixture weights), quantile "
+                                         "update and permutation on one thread",
+                                 "seconds": round(t_route, 4),
+                                 "tokens_per_s": cfg.N / t_route,
+                                 "steps_s": {k: round(v, 4) for k, v in tm1.items()}}
+
+    # ---- parity record (not timed)
+    def per_token(a, b):
+        a = np.asarray(a, np.float64)
+        b = np.asarray(b, np.float64)
+        return np.linalg.norm(a - b, axis=1) / np.maximum(np.linalg.norm(b, axis=1), 1e-300)
+
+    y_gpu = O.bf16_to_f32(gpu["y"])
+    Zg = gpu["logits"]
+    diff = np.any(np.sort(own["topk_ids"], 1) != np.sort(gpu["topk_ids"], 1), axis=1)
+    dz = np.max(np.abs(Zg.astype(np.float64) - own["logits"]), axis=1)
+    dbeta = float(np.max(np.abs(gpu["beta_out"].astype(np.float64) - own["beta_out"]))) \
+        if cfg.recompute_bias else 0.0
+    margin = own["margin"].astype(np.float64)
+    allow = 1e-3 + 2.0 * (dz + dbeta)
+    rms = np.sqrt(np.mean(own["logits"].astype(np.float64) ** 2, axis=1, keepdims=True))
+    zrel = float(np.max(np.abs(Zg - own["logits"]) / np.maximum(np.abs(own["logits"]), rms)))
+    pt_free = per_token(y_gpu, own["y"])
+    same = ~diff
+    forced = O.moe_layer(x=x, **w, logits_in=Zg, **kw)
+    pt_forced = per_token(y_gpu, forced["y"])
+    bit = {k: bool(np.array_equal(np.asarray(gpu[k]).view(np.uint32) if gpu[k].dtype == np.float32
+                                  else gpu[k],
+                                  np.asarray(forced[k]).view(np.uint32)
+                                  if np.asarray(forced[k]).dtype == np.float32 else forced[k]))
+           for k in ("topk_ids", "margin", "counts", "sorted_src")
+           + (("beta_out",) if cfg.recompute_bias else ())}
+    parity = {
+        "tokens": cfg.N,
+        "logits_max_rel_err": zrel,
+        "free_running": {
+            "selection_mismatches": int(diff.sum()),
+            "near_ties_margin_below_1e-3": int(np.sum(margin < 1e-3)),
+            "max_abs_dbeta": dbeta, "max_abs_dlogit": float(dz.max()),
+            "mismatches_beyond_bound": int(np.sum(diff & ~(margin < allow))),
+            "y_rel_l2": float(np.linalg.norm(y_gpu - own["y"]) / np.linalg.norm(own["y"])),
+            "y_worst_token_rel_l2_same_selection": float(pt_free[same].max()) if same.any() else 0.0,
+        },
+        "gpu_logits_given": {
+            "bit_exact": bit,
+            "y_rel_l2": float(np.linalg.norm(y_gpu - forced["y"]) / np.linalg.norm(forced["y"])),
+            "y_worst_token_rel_l2": float(pt_forced.max()),
+            "tokens_above_2e-2": int(np.sum(pt_forced > 2e-2)),
+        },
+    }
+    return base, parity
+
+
+def run_extra(M, torch, name, steps, warmup):
+    """Another workload of the same layer shape in the same run: step time
+    and tokens/s (`steps` timed steps between device synchronisations), and
+    the stage times of `steps` further steps (HIP events between stages).
+    skewed: the routed expert GEMMs (gate/up + down) as a fraction of the
+    bf16 MFMA peak.  decode: the whole layer as GB/s of its algorithmic
+    bytes (every touched expert's three matrices once, the shared expert,
+    the router, x and y)."""
+    import numpy as np
+    from synth import CONFIGS, make_inputs
+    cfg = CONFIGS[name]
+    L = make_inputs(cfg)
+
+    def bf16(a):
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+
+    W = M.ExpertWeights(bf16(L.w_router), bf16(L.w_gate), bf16(L.w_up), bf16(L.w_down),
+                        bf16(L.ws_gate), bf16(L.ws_up), bf16(L.ws_down))
+    x = bf16(L.x)
+    beta = torch.from_numpy(L.beta_in).cuda()
+    off = None if L.logit_offset is None else torch.from_numpy(L.logit_offset).cuda()
+    ws = torch.empty(M.forward_workspace_bytes(cfg.N, cfg.d, cfg.E, cfg.K, cfg.h, cfg.n_shared,
+                                               cfg.h_shared, cfg.recompute_bias),
+                     dtype=torch.uint8, device="cuda")
+    y = torch.empty((cfg.N, cfg.d), dtype=torch.bfloat16, device="cuda")
+    del L
+
+    def step():
+        M.forward(x, W, cfg.K, beta_in=beta, recompute_bias=cfg.recompute_bias,
+                  logit_offset=off, workspace=ws, out=y)
+
+    _, aux = M.forward(x, W, cfg.K, beta_in=beta, recompute_bias=cfg.recompute_bias,
+                       logit_offset=off, workspace=ws, out=y, aux=("counts",))
+    counts = aux["counts"].cpu().numpy()
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    O.moe_layer(x=x, **w, beta_in=L.beta_in, K=cfg.K, recompute_bias=cfg.recompute_bias,
-                logit_offset=L.logit_offset)
-    dt = time.perf_counter() - t0
-    what = "the whole batch" if n == cfg.N else f"the first {n} of {cfg.N} tokens"
-    return {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"fp64 oracle, whole layer (all steps) on {what} of the {cfg.name} "
-                      f"workload, one run of {dt:.1f} s"}
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    M.stage_timing(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    st, calls = M.stage_times()
+    M.stage_timing(False)
+    st = {k: v / max(calls, 1) for k, v in st.items()}
+    out = {"config": cfg.describe(), "steps": steps, "ms_per_step": 1e3 * dt,
+           "tokens_per_s": cfg.N / dt,
+           "stages_ms": {k: round(v, 4) for k, v in st.items()},
+           "max_over_mean_load": float(counts.max() / counts.mean())}
+    pairs = cfg.N * cfg.K
+    if name == "skewed":
+        fl = 2.0 * pairs * 3 * cfg.h * cfg.d
+        t = (st["gate_up"] + st["down"]) * 1e-3
+        out["routed_gemm"] = {"flops": fl, "ms": 1e3 * t, "tflops": fl / t / 1e12,
+                              "mfma_frac": fl / t / 1e12 / PEAK_BF16_TFLOPS,
+                              "gate_up_mfma_frac": 2.0 * pairs * 2 * cfg.h * cfg.d
+                              / (st["gate_up"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                              "down_mfma_frac": 2.0 * pairs * cfg.h * cfg.d
+                              / (st["down"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    if name == "decode":
+        touched = int((counts > 0).sum())
+        nbytes = ((touched * 3 * cfg.h * cfg.d + cfg.n_shared * 3 * cfg.h_shared * cfg.d
+                   + cfg.E * cfg.d) * 2 + 2 * cfg.N * cfg.d * 2)
+        out["layer_hbm"] = {"algorithmic_bytes": nbytes, "experts_touched": touched,
+                            "gbs": nbytes / dt / 1e9,
+                            "frac": nbytes / dt / 1e9 / PEAK_HBM_GBS}
+    log(name, json.dumps(out))
+    return out
 
 
 def bench_parts(M, torch, cfg, Z, beta, iters):
@@ -235,8 +417,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill",
                     choices=["origin", "prefill", "decode", "skewed"])
-    ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
+    ap.add_argument("--cpu-runs", type=int, default=3,
+                    help="runs of the CPU oracle (median reported)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the skewed and decode workloads measured after the headline")
     ap.add_argument("--fp8", action="store_true",
                     help="E4M3 experts (moe_forward_fp8) quantised from the same bf16 weights")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -313,11 +498,17 @@ def main():
                           "parts": parts}), flush=True)
         return
 
-    # loads of the final routing (for the algorithmic byte count), untimed
+    # loads of the final routing (for the algorithmic byte count) and the
+    # outputs the parity record compares with the oracle, untimed
+    aux_names = ("counts", "counts_before", "logits", "topk_ids", "margin", "sorted_src") \
+        + (("beta_out",) if cfg.recompute_bias else ())
     _, aux = fwd(x, W, cfg.K, beta_in=beta, recompute_bias=cfg.recompute_bias,
-                 logit_offset=off, workspace=ws, out=y, aux=("counts", "counts_before"))
-    counts = aux["counts"].cpu().numpy()
-    counts_before = aux["counts_before"].cpu().numpy()
+                 logit_offset=off, workspace=ws, out=y, aux=aux_names)
+    gpu_out = {k: v.cpu().numpy() for k, v in aux.items()}
+    gpu_out["y"] = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    del aux
+    counts = gpu_out["counts"]
+    counts_before = gpu_out["counts_before"]
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -399,9 +590,15 @@ def main():
                   "max_over_mean_after": float(counts.max() / counts.mean())},
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_extras and args.workload == "prefill" and not args.fp8 \
+            and not args.inference:
+        del ws, y, x, W
+        torch.cuda.empty_cache()
+        out["extras"] = {n: run_extra(M, torch, n, s, 3) for n, s in (("skewed", 10),
+                                                                      ("decode", 50))}
+    if not args.no_cpu_baseline and not args.fp8:
         log("cpu baseline ...")
-        out["cpu_baseline"] = cpu_baseline(cfg, L, args.cpu_sample_tokens)
+        out["cpu_baseline"], out["parity"] = cpu_baseline(cfg, L, gpu_out, args.cpu_runs)
     print(json.dumps(out), flush=True)
 
 

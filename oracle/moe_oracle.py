@@ -45,6 +45,7 @@ from __future__ import annotations
 from typing import Optional
 
 import math
+import time
 
 import numpy as np
 
@@ -75,6 +76,15 @@ def f32_to_bf16_rne(v: np.ndarray) -> np.ndarray:
     lsb = (u >> np.uint64(16)) & np.uint64(1)
     r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
     return r.astype(np.uint16)
+
+
+def _lap(timings: Optional[dict], key: str, t0: float) -> float:
+    """Step timing for callers that ask for it: adds the seconds since t0 to
+    timings[key] and returns the current time.  No arithmetic of the method."""
+    t = time.perf_counter()
+    if timings is not None:
+        timings[key] = timings.get(key, 0.0) + (t - t0)
+    return t
 
 
 def _canon(a: np.ndarray) -> np.ndarray:
@@ -231,29 +241,39 @@ def swiglu(X: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
 
 
 def moe_combine(x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
-                ids, S, token_subset=None) -> np.ndarray:
+                ids, S, token_subset=None, timings: Optional[dict] = None) -> np.ndarray:
     """y_t = f_shared(x_t) + sum_{e in I_t} S_{t,e} f_e(x_t) ([KPT] §6.1).
 
     Weights are float arrays of shape [E,h,d]/[E,h,d]/[E,d,h] (routed) and
     [n_shared,hs,d]/[n_shared,hs,d]/[n_shared,d,hs] (shared; n_shared may be
     0).  ``token_subset`` restricts the output to those tokens (rows of the
-    result follow the subset).  Returns fp64 [T', d].
+    result follow the subset).  Returns fp64 [T', d].  ``timings`` (a dict,
+    optional) receives the seconds spent in the shared expert, the routed
+    experts and the weighted sum.
     """
+    t = time.perf_counter()
     x = np.asarray(x, F64)
     toks = np.arange(x.shape[0]) if token_subset is None else np.asarray(token_subset)
     xs = x[toks]
     ids_s = np.asarray(ids)[toks]
     S_s = np.asarray(S, F64)[toks]
     y = np.zeros_like(xs)
+    t = _lap(timings, "combine", t)
     for s in range(ws_gate.shape[0]):
-        y += swiglu(xs, ws_gate[s], ws_up[s], ws_down[s])
+        f = swiglu(xs, ws_gate[s], ws_up[s], ws_down[s])
+        t = _lap(timings, "shared_expert", t)
+        y += f
+        t = _lap(timings, "combine", t)
     E = w_gate.shape[0]
     for e in range(E):
         rows, slots = np.nonzero(ids_s == e)
         if rows.size == 0:
             continue
+        t = _lap(timings, "combine", t)
         f = swiglu(xs[rows], w_gate[e], w_up[e], w_down[e])
+        t = _lap(timings, "routed_experts", t)
         y[rows] += S_s[rows, slots][:, None] * f
+        t = _lap(timings, "combine", t)
     return y
 
 
@@ -508,7 +528,7 @@ def moe_combine_fp8(x, q: dict, ids, S, token_subset=None) -> np.ndarray:
 def moe_layer(x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
               beta_in, K: int, recompute_bias: bool = False, key_bits: int = 16,
               logit_offset=None, logits_in=None, token_subset=None,
-              compute_output: bool = True) -> dict:
+              compute_output: bool = True, timings: Optional[dict] = None) -> dict:
     """Forward pass of one MoE layer as [KPT] §6.1 and §7.1 state it.
 
     x [T,d] and all weights are float arrays (decode bf16 bits with
@@ -517,28 +537,37 @@ def moe_layer(x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
     that routing, expert quantile, centring) and the batch is routed again
     with beta_new ([KPT] §7.2 repairs the toy collapse this way).  The
     ``logits_in`` argument replaces the router product by given logits.
+    ``timings`` (a dict, optional) receives the seconds of each step: router,
+    route (both routings and the mixture weights), eqb, permutation,
+    shared_expert, routed_experts, combine.
     """
+    t = time.perf_counter()
     Z = router_logits(x, w_router, logit_offset) if logits_in is None \
         else np.asarray(logits_in, F32)
     T, E = Z.shape
     out = {"logits": Z}
+    t = _lap(timings, "router", t)
     ids0, alpha0, margin0 = route(Z, beta_in, K)
     out["counts_before"] = np.bincount(ids0.ravel(), minlength=E).astype(np.int32)
     beta = np.zeros(E, F32) if beta_in is None else np.asarray(beta_in, F32)
+    t = _lap(timings, "route", t)
     if recompute_bias:
         beta_new, Q, beta_raw = eqb_expert_bias(Z, alpha0, K, key_bits)
         out.update(alpha=alpha0, beta_out=beta_new, quantile=Q, beta_raw=beta_raw)
         beta = beta_new
+        t = _lap(timings, "eqb", t)
         ids, alpha, margin = route(Z, beta, K)
     else:
         ids, alpha, margin = ids0, alpha0, margin0
         out.update(alpha=alpha0)
     S = mixture_weights(Z, ids)
+    t = _lap(timings, "route", t)
     counts, offsets, sorted_src, src_pos = group_by_expert(ids, E)
     out.update(topk_ids=ids, topk_weights=S, margin=margin, counts=counts,
                offsets=offsets, sorted_src=sorted_src, src_pos=src_pos,
                route_alpha=alpha)
+    _lap(timings, "permutation", t)
     if compute_output:
         out["y"] = moe_combine(x, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
-                               ids, S, token_subset)
+                               ids, S, token_subset, timings)
     return out

@@ -48,6 +48,29 @@ def _compile(src: str) -> str:
     return obj
 
 
+PROBES = os.path.join(HERE, "..", "tests", "probes")
+
+
+def build_probes(verbose: bool = False):
+    """Test probes: small stand-alone HIP programs that measure a property of
+    the hardware that a parity tolerance rests on (tests/probes/*.hip ->
+    executables next to them)."""
+    out = []
+    for f in sorted(os.listdir(PROBES)) if os.path.isdir(PROBES) else []:
+        if not f.endswith(".hip"):
+            continue
+        src = os.path.join(PROBES, f)
+        exe = src[:-4]
+        cmd = [hipcc(), *HIPFLAGS, src, "-o", exe]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"probe build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        out.append(exe)
+        if verbose:
+            print(f"built {exe}")
+    return out
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     srcs = sources()
@@ -61,6 +84,7 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_probes(verbose)
     return LIB
 
 

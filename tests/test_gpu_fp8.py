@@ -7,8 +7,10 @@ quantised per 1 x 128 group, router in bf16).
 * moe_forward_fp8 on a synthetic E4M3 checkpoint: routing, loads and grouping
   bit-exact and equal to moe_forward's for the same logits; the layer output
   within 2e-2 relative L2 of the oracle's FP8 layer (fp64 on the dequantised
-  operands, H quantised from fp64), pooled and for every token on its own,
-  on all tokens, or on 256 seeded tokens at the full size."""
+  operands, H quantised from fp64), pooled, and within 5e-2 for every token
+  on its own (the E4M3 MFMA's block sums move a few H codes by one step;
+  see Y_REL_L2_FP8_TOKEN), on all tokens, or on 256 seeded tokens at the
+  full size."""
 from dataclasses import replace
 
 import numpy as np
@@ -16,8 +18,8 @@ import pytest
 
 from oracle import moe_oracle as O
 from synth import CONFIGS, make_fp8_experts, make_inputs, scaled
-from tests.gpu_util import (S_RTOL, bf16_dev, bits_equal, check_logits, check_output, dev,
-                            host, say, weights_dev)
+from tests.gpu_util import (S_RTOL, Y_REL_L2_FP8_TOKEN, bf16_dev, bits_equal, check_logits,
+                            check_output, dev, host, say, weights_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -171,7 +173,7 @@ def run_fp8_case(M, cfg, sample=None, use_logits_in=False):
         for k in ("ws_gate", "ss_gate", "ws_up", "ss_up", "ws_down", "ss_down"):
             qo[k] = q[k][:0]
     yref = O.moe_combine_fp8(xf, qo, ref["topk_ids"], ref["topk_weights"], token_subset=rows)
-    err, _ = check_output(y[rows], yref, f"fp8 forward {cfg.name}")
+    err, _ = check_output(y[rows], yref, f"fp8 forward {cfg.name}", Y_REL_L2_FP8_TOKEN)
     return err
 
 
@@ -237,3 +239,26 @@ def test_forward_fp8_rejects_unaligned_width(M):
                            s_down=dev(np.zeros((4, 0, 0), np.float32)))
     with pytest.raises(M.MoeError, match="UNSUPPORTED_SHAPE"):
         M.forward_fp8(bf16_dev(L.x), W, cfg.K)
+
+
+def test_fp8_mfma_block_sum_precision():
+    """The assumption behind Y_REL_L2_FP8_TOKEN: gfx950's E4M3 MFMA sums the
+    128 products of a block with an error of at most 2^-12 of their absolute
+    sum (and not exactly: one product of 448 among 127 of 2^-9 loses part of
+    the small ones).  Measured by tests/probes/fp8_block_sum (built by the
+    package build)."""
+    import json
+    import os
+    import subprocess
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    exe = os.path.join(os.path.dirname(__file__), "probes", "fp8_block_sum")
+    assert os.path.exists(exe), "tests/probes/fp8_block_sum is not built (run the package build)"
+    say("fp8 MFMA block-sum precision probe")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    m = json.loads(r.stdout.strip().splitlines()[-1])
+    say("fp8 MFMA block sum", m)
+    assert 0.0 < m["max_err_over_abs_sum"] <= 2.0 ** -12, m
+    assert m["one_large_block"] != m["exact"]
