@@ -337,7 +337,7 @@ typedef struct {
  * same kernels; ids, weights, loads and grouping equal moe_forward's for
  * the same logits).  x is quantised per 1 x 128 group; each expert computes
  * G = X W_g^T and U = X W_u^T from the codes with fp32 accumulation, one
- * scale product per 128 k; H = SiLU(G) * U is rounded to bf16 and quantised
+ * scale product per 128 k; H = SiLU(G) * U is quantised from its fp32 value
  * per 1 x 128 group; then H W_d^T, held in bf16 per pair; the combine
  * accumulates in fp32.  Requires d % 128 == 0, h % 128 == 0 and (with a
  * shared expert) hs % 128 == 0, besides the limits of moe_forward.
@@ -350,6 +350,28 @@ moe_status_t moe_forward_fp8(const moe_problem_t* p, const moe_fp8_weights_t* w,
                              const uint16_t* x, const float* beta_in, uint16_t* y,
                              moe_aux_t* aux, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/*
+ * moe_forward_noalloc - moe_forward for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  The same layer as moe_forward (same kernels, bit-equal
+ * results) with its workspace in a fixed device array owned by the library:
+ * MOE_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held until the process ends.
+ * The caller passes inputs, outputs and aux buffers as for moe_forward.
+ * The call allocates nothing and creates no stream or event: the shared
+ * expert runs on `stream` (no side stream) and stage timing is not recorded.
+ * A problem whose moe_forward_workspace_bytes(p) exceeds the array is
+ * rejected with MOE_ERR_WORKSPACE_TOO_SMALL before anything is enqueued (at
+ * d=2560, E=384, K=6, h=512 up to 1,483 tokens fit).  Every call on one GPU
+ * uses that GPU's one array, whose contents the call treats as undefined on
+ * entry and leaves as it ends: calls that overlap on one GPU (several
+ * streams or threads) race, so order them on one stream.
+ * Errors: as moe_forward.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status_t moe_forward_noalloc(const moe_problem_t* p, const moe_weights_t* w,
+                                 const uint16_t* x, const float* beta_in, uint16_t* y,
+                                 moe_aux_t* aux, void* stream);
 
 /*
  * Stage timing (a profiling aid).  moe_stage_timing(1): every moe_forward

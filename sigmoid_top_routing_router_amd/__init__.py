@@ -21,7 +21,8 @@ __all__ = ["route", "eqb_bias", "eqb_workspace_bytes", "EqbState", "eqb_bias_par
            "route_stats", "read_route_stats", "lei_backward", "forward",
            "forward_workspace_bytes", "fp8_quantize_blocks", "fp8_quantize_rows",
            "Fp8ExpertWeights", "quantize_experts", "forward_fp8", "forward_fp8_workspace_bytes",
-           "ExpertWeights", "MoeError", "load_library", "stage_timing", "stage_times"]
+           "ExpertWeights", "MoeError", "load_library", "stage_timing", "stage_times",
+           "forward_noalloc"]
 
 AUX_FIELDS = [f for f, _ in MoeAux._fields_]
 
@@ -376,11 +377,7 @@ def _run_forward(fp8, x, wstruct, N, d, E, K, h, n_shared, h_shared, beta_in, re
     return (y, aux_t) if aux else y
 
 
-def forward(x, weights: ExpertWeights, K: int, beta_in=None, recompute_bias: bool = False,
-            key_bits: int = 16, logit_offset=None, logits_in=None, aux=(),
-            workspace=None, out=None, stream=None):
-    """MoE layer forward.  x: [N, d] bf16.  Returns y [N, d] bf16, or
-    (y, dict) when ``aux`` names optional outputs (see moe_aux_t)."""
+def _bf16_weights(x, weights: ExpertWeights):
     x = _dev(x, "x", _bf16())
     N, d = x.shape
     wg = _dev(weights.w_gate, "w_gate", _bf16())
@@ -398,8 +395,44 @@ def forward(x, weights: ExpertWeights, K: int, beta_in=None, recompute_bias: boo
     w = MoeWeights(_ptr(weights.w_router), _ptr(wg), _ptr(weights.w_up),
                    _ptr(weights.w_down), _ptr(weights.ws_gate), _ptr(weights.ws_up),
                    _ptr(weights.ws_down))
+    return x, w, N, d, E, h, n_shared, h_shared
+
+
+def forward(x, weights: ExpertWeights, K: int, beta_in=None, recompute_bias: bool = False,
+            key_bits: int = 16, logit_offset=None, logits_in=None, aux=(),
+            workspace=None, out=None, stream=None):
+    """MoE layer forward.  x: [N, d] bf16.  Returns y [N, d] bf16, or
+    (y, dict) when ``aux`` names optional outputs (see moe_aux_t)."""
+    x, w, N, d, E, h, n_shared, h_shared = _bf16_weights(x, weights)
     return _run_forward(False, x, w, N, d, E, K, h, n_shared, h_shared, beta_in, recompute_bias,
                         key_bits, logit_offset, logits_in, aux, workspace, out, stream)
+
+
+def forward_noalloc(x, weights: ExpertWeights, K: int, beta_in=None,
+                    recompute_bias: bool = False, key_bits: int = 16, logit_offset=None,
+                    logits_in=None, aux=(), out=None, stream=None):
+    """moe_forward_noalloc: the layer forward with the library's fixed
+    per-GPU scratch array as its workspace (for callers that cannot allocate
+    device memory; problems needing more than 64 MiB of workspace are
+    rejected).  Arguments and results as forward(); pass ``out`` and aux
+    tensors from the caller to keep the call itself free of allocations."""
+    torch = _torch()
+    lib = _lib.load()
+    x, w, N, d, E, h, n_shared, h_shared = _bf16_weights(x, weights)
+    beta_in = _dev(beta_in, "beta_in", torch.float32, (E,))
+    logit_offset = _dev(logit_offset, "logit_offset", torch.float32, (E,))
+    logits_in = _dev(logits_in, "logits_in", torch.float32, (N, E))
+    flags = (MOE_RECOMPUTE_BIAS if recompute_bias else 0) | (MOE_KEY32 if key_bits == 32 else 0)
+    p = _problem(N, d, E, K, h, n_shared, h_shared, flags, logit_offset, logits_in)
+    with _on(stream):
+        y = out if out is not None else torch.empty((N, d), dtype=torch.bfloat16, device=x.device)
+        _dev(y, "out", _bf16(), (N, d))
+        aux_t = aux if isinstance(aux, dict) else _aux_tensors(aux, N, E, K, x.device)
+        a = MoeAux(*[_ptr(aux_t.get(f)) for f in AUX_FIELDS]) if aux_t else None
+        _lib.check(lib.moe_forward_noalloc(C.byref(p), C.byref(w), _ptr(x), _ptr(beta_in),
+                                           _ptr(y), C.byref(a) if a is not None else None,
+                                           _stream(stream)))
+    return (y, aux_t) if aux else y
 
 
 def forward_fp8(x, weights: Fp8ExpertWeights, K: int, beta_in=None,

@@ -24,10 +24,12 @@ EXPORTED = ["moe_route", "moe_eqb_workspace_bytes", "moe_eqb_bias", "moe_eqb_sta
             "moe_lei_workspace_bytes", "moe_lei_backward",
             "moe_forward_workspace_bytes", "moe_forward", "moe_fp8_quantize_blocks",
             "moe_fp8_quantize_rows", "moe_forward_fp8_workspace_bytes", "moe_forward_fp8",
+            "moe_forward_noalloc",
             "moe_status_string",
             "moe_last_error_message", "moe_abi_version", "moe_stage_timing",
             "moe_stage_times", "moe_stage_name"]
 NUM_STAGES = 7
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 
 
 class MoeProblem(C.Structure):
@@ -121,6 +123,9 @@ def load(path: str = LIB_PATH):
     lib.moe_forward_fp8.argtypes = [C.POINTER(MoeProblem), C.POINTER(MoeFp8Weights), vp, vp, vp,
                                     C.POINTER(MoeAux), vp, C.c_size_t, vp]
     lib.moe_forward_fp8.restype = C.c_int
+    lib.moe_forward_noalloc.argtypes = [C.POINTER(MoeProblem), C.POINTER(MoeWeights), vp, vp, vp,
+                                        C.POINTER(MoeAux), vp]
+    lib.moe_forward_noalloc.restype = C.c_int
     lib.moe_status_string.argtypes = [C.c_int]
     lib.moe_status_string.restype = C.c_char_p
     lib.moe_last_error_message.argtypes = []

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "../../include/moe_mi355x.h"
+#include "api_internal.h"
 #include "kernels.h"
 
 namespace {
@@ -205,6 +206,9 @@ moe_status_t check_problem_fp8(const moe_problem_t* p) {
 // with block scales (moe_fp8_weights_t).
 struct Experts {
   bool fp8 = false;
+  // everything on the caller's stream, no stage timing: no stream or event
+  // is ever created by the call
+  bool in_order = false;
   const uint16_t* w_router = nullptr;
   const moe_weights_t* b = nullptr;
   const moe_fp8_weights_t* q = nullptr;
@@ -350,7 +354,7 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
   const bool recompute = (p->flags & MOE_RECOMPUTE_BIAS) != 0;
 
   CallTimer tm;
-  MOE_TRY_HIP(tm.start(st), "moe_forward: stage timer");
+  if (!ex.in_order) MOE_TRY_HIP(tm.start(st), "moe_forward: stage timer");
 
   // Router logits and the shared expert's gate/up: on one stream both read
   // x, so they share one launch; with the side stream the shared expert runs
@@ -366,7 +370,7 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
   if (ex.fp8)
     MOE_TRY_HIP(moe::launch_quant_rows(x, N, d, l.xq, l.xs, st), "moe_forward: quantise x");
   SideJoin sj;
-  SideStream* side = (!small && shared) ? side_stream() : nullptr;
+  SideStream* side = (!small && shared && !ex.in_order) ? side_stream() : nullptr;
   // the side stream starts from the caller's stream as it stands before the
   // router GEMM (the fork), but its work is enqueued after that GEMM, whose
   // blocks are then dispatched first
@@ -810,6 +814,18 @@ size_t moe_forward_fp8_workspace_bytes(const moe_problem_t* p) {
 moe_status_t moe_forward(const moe_problem_t* p, const moe_weights_t* w, const uint16_t* x,
                          const float* beta_in, uint16_t* y, moe_aux_t* aux, void* workspace,
                          size_t workspace_bytes, void* stream) {
+  return moe::forward_bf16(p, w, x, beta_in, y, aux, workspace, workspace_bytes, stream, false);
+}
+
+}  // extern "C"
+
+// moe_forward's checks and launches; with in_order the call neither creates
+// nor uses the side stream (the shared expert runs on `stream`) and records no
+// stage timing.
+moe_status_t moe::forward_bf16(const moe_problem_t* p, const moe_weights_t* w, const uint16_t* x,
+                               const float* beta_in, uint16_t* y, moe_aux_t* aux,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               bool in_order) {
   moe_status_t s = check_problem(p);
   if (s != MOE_OK) return s;
   if (!w || !x || !y) return fail(MOE_ERR_INVALID_ARGUMENT, "weights, x and y are required");
@@ -823,8 +839,13 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_weights_t* w, const u
   Experts ex;
   ex.w_router = w->w_router;
   ex.b = w;
+  ex.in_order = in_order;
   return forward_impl(p, ex, x, beta_in, y, aux, workspace, workspace_bytes, stream);
 }
+
+moe_status_t moe::set_error(moe_status_t s, const char* msg) { return fail(s, "%s", msg); }
+
+extern "C" {
 
 moe_status_t moe_forward_fp8(const moe_problem_t* p, const moe_fp8_weights_t* w,
                              const uint16_t* x, const float* beta_in, uint16_t* y,
