@@ -346,8 +346,9 @@ def bench_parts(M, torch, cfg, Z, beta, iters):
     with HIP events on the current stream.  "warm": a spin kernel before the
     first event keeps the GPU busy while the host enqueues, so the events
     time the call alone, with the logits possibly in the 256 MB MALL.
-    "cold": a 1 GiB device fill before each sample evicts the caches, so the
-    logits come from HBM.  Reports median, p10 and p90 over `iters` samples,
+    "cold": a read of a 1 GiB device buffer before each sample evicts the
+    caches (with clean lines, so no write-back of the flush lands inside the
+    sample), and the logits come from HBM.  Reports median, p10 and p90 over `iters` samples,
     and GB/s of the algorithmic bytes: (4E + 8K + 8) per token for
     moe_route (logits read; ids, weights, alpha, margin written) and
     2 (4E + 4) per token for moe_eqb_bias (logits and alpha read once per
@@ -366,7 +367,7 @@ def bench_parts(M, torch, cfg, Z, beta, iters):
     q = torch.empty((E,), dtype=torch.float32, device=dev)
     ws_n = max(int(lib.moe_eqb_workspace_bytes(N, E, 16)), 256)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    scratch = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     p = lambda t: ctypes.c_void_p(t.data_ptr())
 
@@ -391,7 +392,7 @@ def bench_parts(M, torch, cfg, Z, beta, iters):
                   for _ in range(iters)]
             for e0, e1 in ev:
                 if mode == "cold":
-                    scratch.fill_(1)
+                    scratch.max()
                 else:
                     torch.cuda._sleep(100000)
                 e0.record()

@@ -101,6 +101,19 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
+// Inclusive prefix sum over the wave (lane order) with DPP: row_shr 1, 2, 4,
+// 8 inside each 16-lane row, then row_bcast15 (lane 15 of a row into the
+// next row) and row_bcast31 (lane 31 into rows 2 and 3).
+__device__ __forceinline__ uint32_t wave_inclusive_sum_dpp_u32(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false); // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false); // row_bcast:31
+  return v;
+}
+
 // Inclusive prefix sum over the wave (lane order), shuffle based.
 __device__ __forceinline__ uint32_t wave_inclusive_sum_u32(uint32_t v) {
   const int l = lane_id();

@@ -13,9 +13,11 @@
 namespace moe {
 
 // ---------------------------------------------------------------- routing
+// zero / zero_n: a buffer of zero_n words that the launch also clears (the
+// first EQB histogram, when the routing gives the token bias of an update).
 hipError_t launch_route(const float* Z, const float* beta, int64_t N, int E, int K,
                         int32_t* ids, float* S, float* alpha, float* margin,
-                        hipStream_t stream);
+                        hipStream_t stream, uint32_t* zero = nullptr, size_t zero_n = 0);
 
 // ---------------------------------------------------------------- EQB
 // Workspace carved by the caller (all 256-byte aligned):
@@ -29,9 +31,11 @@ struct EqbWork {
 };
 size_t eqb_hist_bytes(int E, int key_bits);
 size_t eqb_state_bytes(int E);
+// hist0_zeroed: the first pass's histogram (hist[0 .. E*256)) is already
+// zero (cleared by the routing launch that gave alpha); else a fill clears it.
 hipError_t launch_eqb(const float* Z, const float* alpha, int64_t N, int E, int K,
                       int key_bits, float* beta_out, float* quantile_out,
-                      const EqbWork& w, hipStream_t stream);
+                      const EqbWork& w, hipStream_t stream, bool hist0_zeroed = false);
 // The pieces of launch_eqb, for a batch that arrives in several parts: the
 // histogram of one pass over one part (added into hist_pass = hist + pass*E*256;
 // prefix = w.state), and the selection step of one pass over the summed

@@ -463,15 +463,17 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
   float* alpha = A.alpha ? A.alpha : l.alpha;
   float* margin = A.margin ? A.margin : l.margin;
   if (recompute) {
-    // first pass: alpha only, unless the loads before the update are wanted
+    // first pass: alpha only, unless the loads before the update are wanted;
+    // it also clears the first histogram of the quantile update
     MOE_TRY_HIP(moe::launch_route(Z, beta_in, N, E, K, A.counts_before ? l.ids0 : nullptr,
-                                  nullptr, alpha, nullptr, st),
+                                  nullptr, alpha, nullptr, st, l.eqb.hist, (size_t)E * 256),
                 "moe_forward: first routing");
     if (A.counts_before)
       MOE_TRY_HIP(moe::launch_count(l.ids0, N * K, E, A.counts_before, st), "moe_forward: loads");
     float* beta_new = A.beta_out ? A.beta_out : l.beta_new;
     moe::EqbWork ew{l.eqb.hist, l.eqb.state, l.eqb.qraw};
-    MOE_TRY_HIP(moe::launch_eqb(Z, alpha, N, E, K, key_bits, beta_new, A.quantile_out, ew, st),
+    MOE_TRY_HIP(moe::launch_eqb(Z, alpha, N, E, K, key_bits, beta_new, A.quantile_out, ew, st,
+                                true),
                 "moe_forward: quantile update");
     MOE_TRY_HIP(moe::launch_route(Z, beta_new, N, E, K, ids, S, nullptr, margin, st),
                 "moe_forward: routing");
@@ -644,12 +646,15 @@ moe_status_t moe_eqb_bias(const float* logits, const float* beta_in, const float
   const hipStream_t st = (hipStream_t)stream;
   const float* a = alpha;
   if (!a) {
-    MOE_TRY_HIP(moe::launch_route(logits, beta_in, N, E, K, nullptr, nullptr, l.alpha, nullptr, st),
+    // the routing that gives alpha also clears the first histogram
+    MOE_TRY_HIP(moe::launch_route(logits, beta_in, N, E, K, nullptr, nullptr, l.alpha, nullptr, st,
+                                  l.hist, (size_t)E * 256),
                 "moe_eqb_bias: token bias");
     a = l.alpha;
   }
   moe::EqbWork w{l.hist, l.state, l.qraw};
-  MOE_TRY_HIP(moe::launch_eqb(logits, a, N, E, K, key_bits, beta_out, quantile_out, w, st),
+  MOE_TRY_HIP(moe::launch_eqb(logits, a, N, E, K, key_bits, beta_out, quantile_out, w, st,
+                              alpha == nullptr),
               "moe_eqb_bias");
   return ok();
 }

@@ -27,11 +27,21 @@
 
 namespace moe {
 
+// Grid-stride clear of zero_n words (a buffer the next kernels accumulate
+// into), ahead of the routing work.
+__device__ __forceinline__ void clear_words(uint32_t* __restrict__ p, int64_t n) {
+  if (!p) return;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+
 template <int NV, bool ALPHA_ONLY>
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ Z, const float* __restrict__ beta, int64_t N, int E,
     int K, int32_t* __restrict__ ids, float* __restrict__ S,
-    float* __restrict__ alpha, float* __restrict__ margin) {
+    float* __restrict__ alpha, float* __restrict__ margin, uint32_t* __restrict__ zero,
+    int64_t zero_n) {
+  clear_words(zero, zero_n);
   const int lane = lane_id();
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   // per wave: candidate composites of the current row (at most 64 * NV)
@@ -200,7 +210,8 @@ template <int NC, bool FULL>
 __global__ __launch_bounds__(256) void route_group_kernel(
     const float* __restrict__ Z, const float* __restrict__ beta, int64_t N, int E, int K,
     int32_t* __restrict__ ids, float* __restrict__ S, float* __restrict__ alpha,
-    float* __restrict__ margin) {
+    float* __restrict__ margin, uint32_t* __restrict__ zero, int64_t zero_n) {
+  clear_words(zero, zero_n);
   constexpr int NVL = 4 * NC;  // experts per lane
   const int lane = lane_id();
   const int g = lane & 15;     // lane within the row's 16
@@ -358,7 +369,8 @@ static int64_t route_resident_blocks(int nv, int kind) {
 
 hipError_t launch_route(const float* Z, const float* beta, int64_t N, int E, int K,
                         int32_t* ids, float* S, float* alpha, float* margin,
-                        hipStream_t stream) {
+                        hipStream_t stream, uint32_t* zero, size_t zero_n) {
+  const int64_t zn = zero ? (int64_t)zero_n : 0;
   const int nv = (E + kWave - 1) / kWave;
   // alpha alone: keys-only variant
   const bool alpha_only = ids == nullptr && S == nullptr && margin == nullptr && alpha != nullptr;
@@ -374,10 +386,10 @@ hipError_t launch_route(const float* Z, const float* beta, int64_t N, int E, int
       case V:                                                                             \
         if (E == 64 * V)                                                                  \
           hipLaunchKernelGGL((route_group_kernel<V, true>), grid, block, 0, stream, Z, beta, N, \
-                             E, K, ids, S, alpha, margin);                                \
+                             E, K, ids, S, alpha, margin, zero, zn);                      \
         else                                                                              \
           hipLaunchKernelGGL((route_group_kernel<V, false>), grid, block, 0, stream, Z, beta, \
-                             N, E, K, ids, S, alpha, margin);                             \
+                             N, E, K, ids, S, alpha, margin, zero, zn);                   \
         break;
       MOE_ROUTE_GROUP_CASE(1) MOE_ROUTE_GROUP_CASE(2) MOE_ROUTE_GROUP_CASE(3)
       MOE_ROUTE_GROUP_CASE(4) MOE_ROUTE_GROUP_CASE(5) MOE_ROUTE_GROUP_CASE(6)
@@ -397,10 +409,10 @@ hipError_t launch_route(const float* Z, const float* beta, int64_t N, int E, int
     case V:                                                                                 \
       if (alpha_only)                                                                       \
         hipLaunchKernelGGL((route_topk_kernel<V, true>), grid, block, 0, stream, Z, beta, N, \
-                           E, K, ids, S, alpha, margin);                                    \
+                           E, K, ids, S, alpha, margin, zero, zn);                          \
       else                                                                                  \
         hipLaunchKernelGGL((route_topk_kernel<V, false>), grid, block, 0, stream, Z, beta,  \
-                           N, E, K, ids, S, alpha, margin);                                 \
+                           N, E, K, ids, S, alpha, margin, zero, zn);                       \
       break;
     MOE_ROUTE_CASE(1) MOE_ROUTE_CASE(2) MOE_ROUTE_CASE(3)
     MOE_ROUTE_CASE(4) MOE_ROUTE_CASE(5) MOE_ROUTE_CASE(6)
