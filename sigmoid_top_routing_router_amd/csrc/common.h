@@ -131,6 +131,28 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return l == 0 ? 0ull : (~0ull >> (64 - l));
 }
 
+// ---------------------------------------------------------------- routing
+// Order key of a biased score z + b with b read as b + 0 (never -0): under
+// round to nearest a sum is -0 only when both operands are -0, so no such
+// score is -0 and the order-preserving map needs no test for it.
+__device__ __forceinline__ uint32_t order_key_nonneg_zero(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+// Mixture weight sigma(z) in fp32 (a few ulp); logits below -80, where e^-z
+// nears the fp32 range, take the fp64 form.
+__device__ __forceinline__ float sigmoid_weight(float z) {
+  if (z < -80.0f) return (float)(1.0 / (1.0 + exp(-(double)z)));
+  return 1.0f / (1.0f + expf(-z));
+}
+// Grid-stride clear of n words (a buffer that later kernels accumulate into),
+// ahead of a kernel's own work.
+__device__ __forceinline__ void clear_words(uint32_t* __restrict__ p, int64_t n) {
+  if (!p) return;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+
 // ---------------------------------------------------------------- MFMA types
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));

@@ -27,14 +27,6 @@
 
 namespace moe {
 
-// Grid-stride clear of zero_n words (a buffer the next kernels accumulate
-// into), ahead of the routing work.
-__device__ __forceinline__ void clear_words(uint32_t* __restrict__ p, int64_t n) {
-  if (!p) return;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
-}
-
 template <int NV, bool ALPHA_ONLY>
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ Z, const float* __restrict__ beta, int64_t N, int E,
@@ -197,14 +189,6 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 // is evaluated in fp32 (relative error a few ulp, within the 1e-6 of the
 // weights); logits below -80, where e^-z nears the fp32 range, take the fp64
 // form.
-__device__ __forceinline__ uint32_t order_key_nonneg_zero(float v) {
-  const uint32_t u = __float_as_uint(v);
-  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
-}
-__device__ __forceinline__ float sigmoid_weight(float z) {
-  if (z < -80.0f) return (float)(1.0 / (1.0 + exp(-(double)z)));
-  return 1.0f / (1.0f + expf(-z));
-}
 
 template <int NC, bool FULL>
 __global__ __launch_bounds__(256) void route_group_kernel(
