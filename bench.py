@@ -411,6 +411,62 @@ def bench_parts(M, torch, cfg, Z, beta, iters):
     return out
 
 
+def library_ceilings(torch):
+    """Reference points of this GPU measured with the vendor libraries through
+    torch (hipBLASLt GEMMs, the runtime's copy): dense bf16 GEMMs, the routed
+    GEMMs' shapes as plain dense or batched products (no gather, uniform
+    experts), and a device copy.  Context for the kernels' fractions of the
+    datasheet peaks; none of it is part of the layer."""
+    dev = "cuda"
+    torch.manual_seed(0)
+
+    def timed(fn, it, warm):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(it):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / it
+
+    out = {}
+    for m, n, k, what in [(8192, 8192, 8192, "square"),
+                          (16384, 16384, 4096, "large"),
+                          (65536, 2560, 512, "down projection of 65,536 x 6 pairs as one dense GEMM "
+                                             "(a sixth of its rows)"),
+                          (16384, 1024, 2560, "gate/up of one 16,384-token shared expert")]:
+        A = torch.randn(m, k, device=dev, dtype=torch.bfloat16)
+        B = torch.randn(k, n, device=dev, dtype=torch.bfloat16)
+        ms = timed(lambda: A @ B, 20, 5)
+        out[f"gemm_bf16_{m}x{n}x{k}"] = {"what": what, "ms": round(ms, 4),
+                                         "tflops": round(2 * m * n * k / ms / 1e9, 1),
+                                         "frac": round(2 * m * n * k / ms / 1e9 / PEAK_BF16_TFLOPS, 3)}
+        log(json.dumps(out))
+        del A, B
+    E, rows = 384, 1024
+    A = torch.randn(E, rows, 2560, device=dev, dtype=torch.bfloat16)
+    B = torch.randn(E, 2560, 1024, device=dev, dtype=torch.bfloat16)
+    ms = timed(lambda: torch.bmm(A, B), 5, 2)
+    fl = 2 * E * rows * 1024 * 2560
+    out["bmm_bf16_384x1024x1024x2560"] = {
+        "what": "gate/up of 384 experts with 1,024 rows each, batched, no gather",
+        "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+        "frac": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 3)}
+    del A, B
+    X = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
+    Y = torch.empty_like(X)
+    ms = timed(lambda: Y.copy_(X), 10, 2)
+    out["copy_2GiB"] = {"what": "device copy, bytes read + written", "ms": round(ms, 4),
+                        "gbs": round(2 * X.numel() / ms / 1e6, 1),
+                        "frac": round(2 * X.numel() / ms / 1e6 / PEAK_HBM_GBS, 3)}
+    del X, Y
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -434,6 +490,9 @@ def main():
     ap.add_argument("--parts", action="store_true",
                     help="instead of the layer: time moe_route and moe_eqb_bias alone on the "
                          "workload's logits (warm and cold, median/p10/p90 of --steps samples)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="instead of the layer: time vendor-library GEMMs of related shapes "
+                         "and a device copy on this GPU (reference points for the fractions)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU run: write the routed gate/up HBM bytes per launch from two "
                          "rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE) of "
@@ -457,6 +516,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.ceilings:
+        print(json.dumps({"metric": "vendor-library reference points", "gpu":
+                          torch.cuda.get_device_name(0), "results": library_ceilings(torch)}))
+        return
     M.load_library()
     cfg = CONFIGS[args.workload]
     if args.inference:

@@ -89,6 +89,18 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
   v = max(v, dpp_u32<kDppRowHalfMirror>(v));
   return max(v, dpp_u32<kDppRowMirror>(v));
 }
+__device__ __forceinline__ float row16_max_f32(float v) {
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppQuadSwap1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppQuadSwap2>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppRowHalfMirror>(__float_as_uint(v))));
+  return fmaxf(v, __uint_as_float(dpp_u32<kDppRowMirror>(__float_as_uint(v))));
+}
+__device__ __forceinline__ uint32_t row16_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<kDppQuadSwap1>(v));
+  v = min(v, dpp_u32<kDppQuadSwap2>(v));
+  v = min(v, dpp_u32<kDppRowHalfMirror>(v));
+  return min(v, dpp_u32<kDppRowMirror>(v));
+}
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   v = min(v, dpp_u32<kDppQuadSwap1>(v));
   v = min(v, dpp_u32<kDppQuadSwap2>(v));

@@ -173,22 +173,40 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 }
 
 // ---------------------------------------------------------------- 16 lanes per row
-// The same selection (same candidates, ranks and outputs) with a quarter wave
-// per row, for E % 4 == 0 and a 16-byte aligned Z: lane g of a row's 16 lanes
-// holds the experts 4g + 64j + c (c < 4, j < NC), read as float4, so one wave
-// selects four rows at once and every cross-lane step is a 16-lane DPP row
-// (the lane maxima, the K+1 pops that give L) or a ballot masked to the row.
-// Rows past N (the last quad) re-read row N-1 and store nothing.  FULL: E is
-// 64 * NC, so no lane holds a slot past E.  The next quad's rows load while
-// this quad is selected.
+// The same selection (same outputs) with a quarter wave per row, for E % 4 == 0
+// and a 16-byte aligned Z: lane g of a row's 16 lanes holds the experts
+// 4g + 64j + c (c < 4, j < NC), read as float4, so one wave selects four rows
+// (a quad) at once and every cross-lane step is a 16-lane DPP row or a ballot
+// masked to the row.  Rows past N (the last quad) re-read row N-1 and store
+// nothing.  FULL: E is 64 * NC, so no lane holds a slot past E (other slots
+// score -inf, below every finite score).
 //
-// Keys: the bias is read once as beta + 0, which turns -0 into +0.  Under
-// round to nearest a sum is -0 only when both operands are -0, so no biased
-// score z + b is -0 and the order-preserving map needs no test for it (the
-// two zeros share a key, as in f32_order_key).  The sigmoid weight
-// is evaluated in fp32 (relative error a few ulp, within the 1e-6 of the
-// weights); logits below -80, where e^-z nears the fp32 range, take the fp64
-// form.
+// Memory schedule: the waves walk the quads with a grid stride.  The loads of
+// the next quad are issued before the current one is selected, and the
+// selection itself touches only registers and LDS: the unbiased logits of the
+// candidates and the results (ids, weights, the K-th and (K+1)-th scores) go
+// to LDS, and a quad's results are stored at the top of the next trip, right
+// after the wait for that trip's rows.  So the one wait per trip is for loads
+// issued a whole selection earlier, and no store or gather sits between a
+// load and its wait.
+//
+// The bias is read once as beta + 0, which turns -0 into +0.  Under round to
+// nearest a sum is -0 only when both operands are -0, so no biased score is
+// -0, and for finite scores the float order is the order of the keys (the two
+// zeros compare equal, as they share a key).  The sigmoid weight is evaluated
+// in fp32 (relative error a few ulp, within the 1e-6 of the weights); logits
+// below -80, where e^-z nears the fp32 range, take the fp64 form.
+//
+// (1) L = the (K+1)-th largest of the row's 16 lane maxima (with
+// multiplicity): every entry of the row's top K+1 is >= L.
+// (2) The candidates (score >= L) are compacted into the row's LDS list as
+// (score, expert, logit), and each is ranked by the number of candidates
+// before it in the selection order (score descending, expert ascending).  A
+// row with more than kRouteCap candidates (many scores tied at or above L)
+// sends its wave to (2'): K+1 rounds pop the row's largest (score, lowest
+// expert), which gives the same ids in the same order, and the same K-th and
+// (K+1)-th scores.
+constexpr int kRouteCap = 64;
 
 template <int NC, bool FULL>
 __global__ __launch_bounds__(256) void route_group_kernel(
@@ -201,22 +219,33 @@ __global__ __launch_bounds__(256) void route_group_kernel(
   const int g = lane & 15;     // lane within the row's 16
   const int grp = lane >> 4;   // row of the wave's quad
   const int wib = threadIdx.x >> 6;
-  __shared__ uint64_t cand[4][4][16 * NVL];
-  __shared__ uint32_t kk[4][4][2];
+  __shared__ float4 sbeta[16 * NC];  // [j][g]: the bias of lane g's four experts of j
+  __shared__ float cand_s[4][4][kRouteCap];     // candidate scores
+  __shared__ uint32_t cand_e[4][4][kRouteCap];  // their experts
+  __shared__ int32_t out_id[4][4][MOE_KMAX_INTERNAL];
+  __shared__ float out_s[4][4][MOE_KMAX_INTERNAL];
+  __shared__ float kk[4][4][2];                 // K-th and (K+1)-th score
+  for (int i = (int)threadIdx.x; i < 16 * NC; i += 256) {
+    const int e0 = 4 * (i & 15) + 64 * (i >> 4);
+    float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (beta && (FULL || e0 < E))
+      b = make_float4(beta[e0] + 0.0f, beta[e0 + 1] + 0.0f, beta[e0 + 2] + 0.0f,
+                      beta[e0 + 3] + 0.0f);
+    sbeta[i] = b;
+  }
+  __syncthreads();
   const int64_t nquads = (N + 3) / 4;
-  const int64_t nwaves = (int64_t)gridDim.x * 4;
-  int64_t quad = (int64_t)blockIdx.x * 4 + wib;
+  const int64_t quad = (int64_t)blockIdx.x * 4 + wib;  // one quad of rows per wave
   if (quad >= nquads) return;  // whole wave leaves together
 
-  float bv[NVL];
-#pragma unroll
-  for (int j = 0; j < NC; ++j)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int e = 4 * g + 64 * j + c;
-      bv[4 * j + c] = (beta && (FULL || e < E)) ? beta[e] + 0.0f : 0.0f;
-    }
-  auto load_row = [&](int64_t q, float4 (&v)[NC]) {
+  const uint64_t gmask = 0xFFFFull << (16 * grp);
+  float* cs = cand_s[wib][grp];
+  uint32_t* ce = cand_e[wib][grp];
+  int32_t* oid = out_id[wib][grp];
+  float* os = out_s[wib][grp];
+  float* kl = kk[wib][grp];
+
+  auto load_rows = [&](int64_t q, float4 (&v)[NC]) {
     const int64_t r = min(q * 4 + grp, N - 1);
     const float* zr = Z + r * (int64_t)E;
 #pragma unroll
@@ -226,41 +255,49 @@ __global__ __launch_bounds__(256) void route_group_kernel(
                               : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
-  const uint64_t gmask = 0xFFFFull << (16 * grp);
-  uint64_t* cl = cand[wib][grp];
-  uint32_t* kl = kk[wib][grp];
 
-  auto select = [&](int64_t q, const float4 (&cur)[NC]) {
+  // the results of quad q, from LDS to memory
+  auto flush = [&](int64_t q) {
     const int64_t row = q * 4 + grp;
-    const bool row_ok = row < N;
-    uint32_t key[NVL];
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      const float zc[4] = {cur[j].x, cur[j].y, cur[j].z, cur[j].w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int e = 4 * g + 64 * j + c;
-        key[4 * j + c] = (FULL || e < E) ? order_key_nonneg_zero(zc[c] + bv[4 * j + c]) : 0u;
+    if (row < N) {
+      if (g < K) {
+        if (ids) ids[row * K + g] = oid[g];
+        if (S) S[row * K + g] = os[g];
+      }
+      if (g == 0) {
+        if (alpha) alpha[row] = -kl[1];
+        if (margin) margin[row] = kl[0] - kl[1];
       }
     }
-    // (1) L = the (K+1)-th largest of the row's 16 lane maxima (with
-    // multiplicity): every entry of the row's top K+1 has key >= L.
-    uint32_t lm = key[0];
+  };
+
+  auto select = [&](const float4 (&cur)[NC]) {
+    float v[NVL];
 #pragma unroll
-    for (int i = 1; i < NVL; ++i) lm = max(lm, key[i]);
-    uint32_t L = 0u;
+    for (int j = 0; j < NC; ++j) {
+      const bool ok = FULL || 4 * g + 64 * j < E;
+      const float4 b = sbeta[16 * j + g];
+      v[4 * j + 0] = ok ? cur[j].x + b.x : -INFINITY;
+      v[4 * j + 1] = ok ? cur[j].y + b.y : -INFINITY;
+      v[4 * j + 2] = ok ? cur[j].z + b.z : -INFINITY;
+      v[4 * j + 3] = ok ? cur[j].w + b.w : -INFINITY;
+    }
+    // (1)
+    float lm = v[0];
+#pragma unroll
+    for (int i = 1; i < NVL; ++i) lm = fmaxf(lm, v[i]);
+    float L = -INFINITY;
 #pragma unroll
     for (int k = 0; k <= MOE_KMAX_INTERNAL; ++k) {
       if (k > K) break;  // uniform
-      L = row16_max_u32(lm);
+      L = row16_max_f32(lm);
       const int win = __ffsll((unsigned long long)(ballot(lm == L) & gmask)) - 1;
-      if (lane == win) lm = 0u;
+      if (lane == win) lm = -INFINITY;
     }
-    // (2) compact the candidates (key >= L) of the row into its LDS list as
-    // composites (key << 32) | (2^32 - 1 - expert), in lane order
+    // (2) candidates of the row, in lane order
     uint32_t cnt = 0;
 #pragma unroll
-    for (int i = 0; i < NVL; ++i) cnt += (key[i] >= L) ? 1u : 0u;
+    for (int i = 0; i < NVL; ++i) cnt += (v[i] >= L) ? 1u : 0u;
     uint32_t off = 0, total = 0;
 #pragma unroll
     for (int b = 0; b < 5; ++b) {  // cnt <= 24
@@ -269,53 +306,77 @@ __global__ __launch_bounds__(256) void route_group_kernel(
                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
       total += (uint32_t)__popcll(m) << b;
     }
+    if (ballot(total > (uint32_t)kRouteCap) == 0) {
 #pragma unroll
-    for (int j = 0; j < NC; ++j)
+      for (int j = 0; j < NC; ++j)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int i = 4 * j + c;
-        if (key[i] >= L) {
-          const uint32_t e = (uint32_t)(4 * g + 64 * j + c);
-          cl[off++] = ((uint64_t)key[i] << 32) | (uint64_t)(0xFFFFFFFFu - e);
+        for (int c = 0; c < 4; ++c) {
+          const int i = 4 * j + c;
+          if (v[i] >= L) {
+            cs[off] = v[i];
+            ce[off] = (uint32_t)(4 * g + 64 * j + c);
+            ++off;
+          }
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own list is written
+      for (uint32_t i = (uint32_t)g; i < total; i += 16) {
+        const float si = cs[i];
+        const uint32_t ei = ce[i];
+        uint32_t rank = 0;
+#pragma unroll 4
+        for (uint32_t j = 0; j < total; ++j) {
+          const float sj = cs[j];
+          const uint32_t ej = ce[j];
+          rank += (uint32_t)((sj > si) | ((sj == si) & (ej < ei)));
+        }
+        if (rank < (uint32_t)K) {
+          oid[rank] = (int32_t)ei;
+          os[rank] = sigmoid_weight(Z[(quad * 4 + grp) * (int64_t)E + ei]);
+        }
+        if (rank == (uint32_t)K - 1) kl[0] = si;
+        if (rank == (uint32_t)K) kl[1] = si;
+      }
+    } else {
+      // (2') pops: the lane's largest score and, among equal ones, its lowest
+      // expert (the slots run in expert order), then the row's
+      float vK = 0.f, vK1 = 0.f;
+#pragma unroll 1
+      for (int r = 0; r <= K; ++r) {
+        float lmx = v[0];
+#pragma unroll
+        for (int i = 1; i < NVL; ++i) lmx = fmaxf(lmx, v[i]);
+        int bi = NVL - 1;
+#pragma unroll
+        for (int i = NVL - 1; i >= 0; --i) bi = (v[i] == lmx) ? i : bi;
+        const uint32_t el = (uint32_t)(64 * (bi >> 2) + 4 * g + (bi & 3));
+        const float rmx = row16_max_f32(lmx);
+        const uint32_t we = row16_min_u32(lmx == rmx ? el : 0xFFFFFFFFu);
+        if (r == K - 1) vK = rmx;
+        if (r == K) vK1 = rmx;
+        if (el == we) {
+          const float z = Z[(quad * 4 + grp) * (int64_t)E + we];
+          if (r < K) {
+            oid[r] = (int32_t)we;
+            os[r] = sigmoid_weight(z);
+          }
+#pragma unroll
+          for (int i = 0; i < NVL; ++i) v[i] = (i == bi) ? -INFINITY : v[i];
         }
       }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own list is written
-    // (3) rank = number of larger composites
-    for (uint32_t i = (uint32_t)g; i < total; i += 16) {
-      const uint64_t ci = cl[i];
-      uint32_t rank = 0;
-#pragma unroll 4
-      for (uint32_t j = 0; j < total; ++j) rank += (cl[j] > ci) ? 1u : 0u;
-      if (row_ok && rank < (uint32_t)K) {
-        const uint32_t e = 0xFFFFFFFFu - (uint32_t)ci;
-        if (ids) ids[row * K + rank] = (int32_t)e;
-        if (S) S[row * K + rank] = sigmoid_weight(Z[row * (int64_t)E + e]);
+      if (g == 0) {
+        kl[0] = vK;
+        kl[1] = vK1;
       }
-      if (rank == (uint32_t)K - 1) kl[0] = (uint32_t)(ci >> 32);
-      if (rank == (uint32_t)K) kl[1] = (uint32_t)(ci >> 32);
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_wave_barrier();
-    if (g == 0 && row_ok) {
-      const float vK = f32_from_order_key(kl[0]);
-      const float vK1 = f32_from_order_key(kl[1]);
-      if (alpha) alpha[row] = -vK1;
-      if (margin) margin[row] = vK - vK1;
-    }
-    // the next quad's candidates overwrite this quad's lists
+    // the results are in LDS before the flush reads them
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_wave_barrier();
   };
 
-  float4 cur[NC], nxt[NC];
-  load_row(quad, cur);
-  for (; quad < nquads; quad += nwaves) {
-    const int64_t nq = quad + nwaves;
-    if (nq < nquads) load_row(nq, nxt);
-    select(quad, cur);
-#pragma unroll
-    for (int j = 0; j < NC; ++j) cur[j] = nxt[j];
-  }
+  float4 cur[NC];
+  load_rows(quad, cur);
+  select(cur);
+  flush(quad);
 }
 
 // Blocks of 256 threads of one variant that the device holds at once
@@ -360,10 +421,9 @@ hipError_t launch_route(const float* Z, const float* beta, int64_t N, int E, int
   const bool alpha_only = ids == nullptr && S == nullptr && margin == nullptr && alpha != nullptr;
   const dim3 block(256);
   if (E % 4 == 0 && (uintptr_t)Z % 16 == 0) {
-    // 16 lanes per row; the waves walk quads of rows with a grid stride
-    int64_t blocks = ((N + 3) / 4 + 3) / 4;
-    const int64_t cap = route_resident_blocks(nv, 2);
-    if (blocks > cap) blocks = cap;
+    // 16 lanes per row, one quad of rows per wave
+    const int64_t blocks = ((N + 3) / 4 + 3) / 4;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks);
     switch (nv) {
 #define MOE_ROUTE_GROUP_CASE(V)                                                           \

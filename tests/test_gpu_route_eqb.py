@@ -63,6 +63,33 @@ def test_route_parity(M, seed, N, E, K, ties, with_beta):
     _route_case(M, Z, beta, K)
 
 
+@pytest.mark.parametrize("E,K", [(64, 6), (68, 8), (100, 6), (128, 8), (384, 6)])
+def test_route_tied_candidates(M, E, K):
+    """Rows whose largest scores tie across many experts, so that the
+    candidate list of a row (scores at or above the bound from the lane
+    maxima) holds K, K+1, 63, 64, 65 or all E entries: beyond 64 a wave
+    selects by popping the row maximum instead, and the rows of that wave
+    that did not overflow must come out the same.  Also whole rows of one
+    value and rows of signed zeros."""
+    say("route tied candidates", E, K)
+    rng = np.random.default_rng(230 + E)
+    counts = [K, K + 1, 63, 64, 65, E]
+    N = 4 * len(counts) + 9
+    Z = rng.standard_normal((N, E)).astype(np.float32)
+    for t in range(N):
+        kind = t % 8
+        if kind < len(counts):
+            m = min(counts[kind], E)
+            Z[t, rng.choice(E, m, replace=False)] = 4.0
+        elif kind == 6:
+            Z[t] = 0.25
+        else:
+            Z[t] = np.where(rng.random(E) < 0.5, np.float32(-0.0), np.float32(0.0))
+    _route_case(M, Z, None, K)
+    beta = (np.round(make_bias(231 + E, E, 0.25) * 8) / 8).astype(np.float32)
+    _route_case(M, Z - beta, beta, K)
+
+
 def test_route_parity_full_size_skewed(M):
     """N=65536, E=384, K=6 at the launch size of the benchmark."""
     say("route full 65536x384")
