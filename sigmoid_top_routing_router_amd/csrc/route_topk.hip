@@ -379,12 +379,12 @@ __global__ __launch_bounds__(256) void route_group_kernel(
   flush(quad);
 }
 
-// Blocks of 256 threads of one variant that the device holds at once
-// (occupancy x compute units), queried once per variant and device.
-// kind 0: one wave per row, 1: its keys-only variant, 2: 16 lanes per row.
-// Host threads may race to fill an entry; each computes the same value.
+// Blocks of 256 threads of one variant of the one-wave kernel that the device
+// holds at once (occupancy x compute units), queried once per variant and
+// device.  kind 0: full selection, 1: the keys-only variant.  Host threads
+// may race to fill an entry; each computes the same value.
 static int64_t route_resident_blocks(int nv, int kind) {
-  static std::atomic<int64_t> cache[3][8][7] = {};
+  static std::atomic<int64_t> cache[2][8][7] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 8) return 2048;
   std::atomic<int64_t>& c = cache[kind][dev][nv];
@@ -394,9 +394,8 @@ static int64_t route_resident_blocks(int nv, int kind) {
   switch (nv) {
 #define MOE_ROUTE_FN(V)                                                        \
     case V:                                                                    \
-      fn = kind == 2 ? (const void*)route_group_kernel<V, false>               \
-           : kind == 1 ? (const void*)route_topk_kernel<V, true>               \
-                       : (const void*)route_topk_kernel<V, false>;             \
+      fn = kind == 1 ? (const void*)route_topk_kernel<V, true>                 \
+                     : (const void*)route_topk_kernel<V, false>;               \
       break;
     MOE_ROUTE_FN(1) MOE_ROUTE_FN(2) MOE_ROUTE_FN(3) MOE_ROUTE_FN(4) MOE_ROUTE_FN(5) MOE_ROUTE_FN(6)
 #undef MOE_ROUTE_FN
