@@ -436,8 +436,8 @@ def library_ceilings(torch):
     out = {}
     for m, n, k, what in [(8192, 8192, 8192, "square"),
                           (16384, 16384, 4096, "large"),
-                          (65536, 2560, 512, "down projection of 65,536 x 6 pairs as one dense GEMM "
-                                             "(a sixth of its rows)"),
+                          (65536, 2560, 512, "the down projection's shape (k 512, n 2560) as one "
+                                             "dense GEMM of 65,536 rows"),
                           (16384, 1024, 2560, "gate/up of one 16,384-token shared expert")]:
         A = torch.randn(m, k, device=dev, dtype=torch.bfloat16)
         B = torch.randn(k, n, device=dev, dtype=torch.bfloat16)
