@@ -4,14 +4,14 @@
 // section: router x W_r^T, SwiGLU gate/up and down projections; FP8 section
 // for the E4M3 variant), for tiles of few rows: with N <= 64 tokens every
 // expert holds at most 64 rows, and the layer is bound by reading each
-// touched expert's weights once from HBM.  The tile engine keeps one block
-// per CU with its weights going through a 160 KB LDS ring, which leaves too
-// few bytes in flight for that; here the weights go straight from HBM into
-// the MFMA operand registers:
+// touched expert's weights once from HBM.  The tile engine's 256 x 256 tile
+// keeps too few weight bytes in flight per CU for that when a tile has few
+// rows; here every wave streams its own weight rows:
 //  * a block of 4 waves covers 256 weight rows (gate/up: 128 gate rows and
 //    the 128 up rows of the same hidden columns, one 1 x 128 group of H);
-//    each wave streams 64 of them as four 16-row MFMA blocks, with the next
-//    k-set of loads in flight while the current one multiplies;
+//    each wave streams 64 of them as four 16-row MFMA blocks through a ring
+//    of k-sets in LDS (below), with the next k-sets loading while the
+//    current one multiplies;
 //  * the (few) activation rows are read from global memory (L2-resident) in
 //    the MFMA layout, 16 rows per pass; a tile with more than 16 rows runs
 //    one pass per 16 rows;
