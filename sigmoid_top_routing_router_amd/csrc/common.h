@@ -159,10 +159,13 @@ __device__ __forceinline__ float sigmoid_weight(float z) {
 }
 // Grid-stride clear of n words (a buffer that later kernels accumulate into),
 // ahead of a kernel's own work.
+// BLOCK is the launch's block size (a constant, so that no load of the
+// dispatch packet's block size stands in front of the kernel's own loads).
+template <int BLOCK>
 __device__ __forceinline__ void clear_words(uint32_t* __restrict__ p, int64_t n) {
   if (!p) return;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
+  const int64_t stride = (int64_t)gridDim.x * BLOCK;
+  for (int64_t i = (int64_t)blockIdx.x * BLOCK + threadIdx.x; i < n; i += stride) p[i] = 0u;
 }
 
 // ---------------------------------------------------------------- MFMA types

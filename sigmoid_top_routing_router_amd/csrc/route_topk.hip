@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     int K, int32_t* __restrict__ ids, float* __restrict__ S,
     float* __restrict__ alpha, float* __restrict__ margin, uint32_t* __restrict__ zero,
     int64_t zero_n) {
-  clear_words(zero, zero_n);
+  clear_words<256>(zero, zero_n);
   const int lane = lane_id();
   const int64_t nwaves = (int64_t)gridDim.x * 4;
   // per wave: candidate composites of the current row (at most 64 * NV)
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void route_group_kernel(
     const float* __restrict__ Z, const float* __restrict__ beta, int64_t N, int E, int K,
     int32_t* __restrict__ ids, float* __restrict__ S, float* __restrict__ alpha,
     float* __restrict__ margin, uint32_t* __restrict__ zero, int64_t zero_n) {
-  clear_words(zero, zero_n);
+  clear_words<256>(zero, zero_n);
   constexpr int NVL = 4 * NC;  // experts per lane
   const int lane = lane_id();
   const int g = lane & 15;     // lane within the row's 16

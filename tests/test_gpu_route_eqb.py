@@ -50,6 +50,8 @@ ROUTE_CASES = [
     (107, 257, 100, 3, 0.9, True),
     (108, 129, 383, 1, 0.2, False),
     (109, 64, 65, 4, 0.0, True),
+    (110, 301, 128, 1, 0.3, True),
+    (111, 299, 192, 7, 0.6, True),
 ]
 
 
