@@ -181,14 +181,14 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 // nothing.  FULL: E is 64 * NC, so no lane holds a slot past E (other slots
 // score -inf, below every finite score).
 //
-// Memory schedule: the waves walk the quads with a grid stride.  The loads of
-// the next quad are issued before the current one is selected, and the
-// selection itself touches only registers and LDS: the unbiased logits of the
-// candidates and the results (ids, weights, the K-th and (K+1)-th scores) go
-// to LDS, and a quad's results are stored at the top of the next trip, right
-// after the wait for that trip's rows.  So the one wait per trip is for loads
-// issued a whole selection earlier, and no store or gather sits between a
-// load and its wait.
+// Schedule: one quad of rows per wave and a block per four quads, with no
+// loop; four blocks per CU are resident (registers), so other waves' loads
+// overlap a wave's selection.  The results (ids, weights, the K-th and
+// (K+1)-th scores) are gathered in LDS and stored by the wave at its end; the
+// lanes that rank a winning candidate read its unbiased logit back from
+// memory (an L2 hit) for the weight.  (A grid-stride loop that loads the next
+// quad during the selection was no faster: the gather for the weights waits
+// for every load in flight, the prefetch included.)
 //
 // The bias is read once as beta + 0, which turns -0 into +0.  Under round to
 // nearest a sum is -0 only when both operands are -0, so no biased score is
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 // (1) L = the (K+1)-th largest of the row's 16 lane maxima (with
 // multiplicity): every entry of the row's top K+1 is >= L.
 // (2) The candidates (score >= L) are compacted into the row's LDS list as
-// (score, expert, logit), and each is ranked by the number of candidates
+// (score, expert) pairs, and each is ranked by the number of candidates
 // before it in the selection order (score descending, expert ascending).  A
 // row with more than kRouteCap candidates (many scores tied at or above L)
 // sends its wave to (2'): K+1 rounds pop the row's largest (score, lowest
