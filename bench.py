@@ -47,18 +47,32 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-GEMM_SRC = [os.path.join(ROOT, "sigmoid_top_routing_router_amd", "csrc", f)
-            for f in ("grouped_gemm.hip", "gemm_args.h")]
+_CSRC = os.path.join(ROOT, "sigmoid_top_routing_router_amd", "csrc")
+
+
+def roofline_kernel(n_tokens, fp8):
+    """The kernel the roofline object covers (the routed gate/up GEMM of the
+    path the layer takes): (name as rocprofv3 reports it, sources it is built
+    from).  Batches of at most 64 tokens take the weight-streaming kernel."""
+    if n_tokens <= 64:
+        return (f"skinny_kernel<0, {'true' if fp8 else 'false'}>",
+                [os.path.join(_CSRC, f) for f in ("skinny_gemm.hip", "gemm_args.h")])
+    return ("gemm_fp8_kernel<0>" if fp8 else "gemm_kernel<0, true>",
+            [os.path.join(_CSRC, f) for f in ("grouped_gemm.hip", "gemm_args.h")])
+
+
+def traffic_key(workload, fp8):
+    return workload + ("_fp8" if fp8 else "")
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the tile engine's sources (the kernel the traffic record covers)."""
+def kernel_source_hash(sources) -> str:
+    """Hash of a kernel's sources (a traffic record holds for them only)."""
     h = hashlib.sha256()
-    for path in GEMM_SRC:
+    for path in sources:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -81,24 +95,30 @@ def gateup_algorithmic(cfg, counts, fp8=False):
     return flops, bytes_
 
 
-def traffic_for(workload):
+def traffic_for(workload, n_tokens, fp8):
+    """Recorded HBM bytes per launch of the roofline kernel, or None when no
+    record exists or the kernel's sources changed since it was taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
-    ent = t.get(workload)
-    if not ent or ent.get("source_sha256_16") != kernel_source_hash():
+    ent = t.get(traffic_key(workload, fp8))
+    name, sources = roofline_kernel(n_tokens, fp8)
+    if not ent or ent.get("kernel_name") != name or \
+            ent.get("source_sha256_16") != kernel_source_hash(sources):
         return None
     return ent.get("bytes_per_launch")
 
 
-ROUTED_GATEUP = "gemm_kernel<0, true>"
 COPY_KERNEL = "copyBuffer"
 
 
-def _counter_means(csv_dir, counter):
-    """Mean per-dispatch value of `counter` (KiB) for the routed gate/up kernel
-    and the largest plain copy in one rocprofv3 --pmc output directory."""
+def _counter_means(csv_dir, counter, kernel):
+    """Mean per-dispatch value of `counter` (KiB) for `kernel` and the
+    largest plain copy in one rocprofv3 --pmc output directory.  Where the
+    same kernel also runs a smaller product (the E4M3 tile serves the shared
+    expert too), only the dispatches of the largest grid count: the routed
+    launch, sized for the worst-case tile table."""
     import csv
     import glob
     gu, cp = [], []
@@ -107,24 +127,27 @@ def _counter_means(csv_dir, counter):
             for r in csv.DictReader(f):
                 if r["Counter_Name"] != counter:
                     continue
-                if ROUTED_GATEUP in r["Kernel_Name"]:
-                    gu.append(float(r["Counter_Value"]))
+                if kernel in r["Kernel_Name"]:
+                    gu.append((int(r["Grid_Size"]), float(r["Counter_Value"])))
                 elif COPY_KERNEL in r["Kernel_Name"]:
                     cp.append(float(r["Counter_Value"]))
     if not gu or not cp:
-        raise SystemExit(f"{csv_dir}: no {counter} rows for the routed gate/up kernel or the copy")
-    return sum(gu) / len(gu), max(cp), len(gu)
+        raise SystemExit(f"{csv_dir}: no {counter} rows for {kernel} or the copy")
+    big = max(g for g, _ in gu)
+    vals = [v for g, v in gu if g == big]
+    return sum(vals) / len(vals), max(cp), len(vals)
 
 
-def record_traffic(workload, fetch_dir, write_dir, copy_mib):
+def record_traffic(workload, n_tokens, fp8, fetch_dir, write_dir, copy_mib):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
     WRITE_SIZE, each with --calibrate-copy-mib) into HBM bytes per launch of
-    the routed gate/up GEMM.  Each counter is scaled by the factor that makes
-    it read the known size of the calibration copy (copy_mib MiB read and
-    written)."""
+    the roofline kernel (the routed gate/up GEMM of that path).  Each counter
+    is scaled by the factor that makes it read the known size of the
+    calibration copy (copy_mib MiB read and written)."""
     known_kib = copy_mib * 1024.0
-    f_gu, f_cp, n_f = _counter_means(fetch_dir, "FETCH_SIZE")
-    w_gu, w_cp, n_w = _counter_means(write_dir, "WRITE_SIZE")
+    name, sources = roofline_kernel(n_tokens, fp8)
+    f_gu, f_cp, n_f = _counter_means(fetch_dir, "FETCH_SIZE", name)
+    w_gu, w_cp, n_w = _counter_means(write_dir, "WRITE_SIZE", name)
     f_scale, w_scale = known_kib / f_cp, known_kib / w_cp
     fetch_b = f_gu * f_scale * 1024.0
     write_b = w_gu * w_scale * 1024.0
@@ -132,20 +155,22 @@ def record_traffic(workload, fetch_dir, write_dir, copy_mib):
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-    t[workload] = {
-        "kernel": "routed gate/up GEMM (" + ROUTED_GATEUP + ")",
+    key = traffic_key(workload, fp8)
+    t[key] = {
+        "kernel": "routed gate/up GEMM (" + name + ")",
+        "kernel_name": name,
         "bytes_per_launch": fetch_b + write_b,
         "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
         "fetch_kib_raw_mean": f_gu, "write_kib_raw_mean": w_gu,
         "launches": [n_f, n_w],
         "copy_calibration": {"copy_mib": copy_mib, "fetch_kib": f_cp, "write_kib": w_cp,
                              "fetch_scale": f_scale, "write_scale": w_scale},
-        "source_sha256_16": kernel_source_hash(),
+        "source_sha256_16": kernel_source_hash(sources),
     }
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(t, f, indent=1)
-    print(json.dumps(t[workload]))
+    print(json.dumps(t[key]))
 
 
 def _blas_info():
@@ -498,10 +523,10 @@ def main():
                          "rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE) of "
                          "this script run with --calibrate-copy-mib")
     args = ap.parse_args()
-    if args.fp8 and (args.record_traffic or args.calibrate_copy_mib):
-        ap.error("--fp8 has no traffic record")
     if args.record_traffic:
-        record_traffic(args.workload, *args.record_traffic, args.calibrate_copy_mib or 1024)
+        from synth import CONFIGS
+        record_traffic(args.workload, CONFIGS[args.workload].N, args.fp8, *args.record_traffic,
+                       args.calibrate_copy_mib or 1024)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the layer has no multi-GPU path "
@@ -625,13 +650,11 @@ def main():
         roof = {"bound": "mfma", "achieved": flops / t_gu / 1e12, "peak": peak_mfma,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None if args.fp8 else traffic_for(args.workload)
-    if cfg.N <= 64:  # batches of at most 64 tokens take the weight-streaming kernel
-        roof["kernel"] = (f"skinny_kernel<0, {'true' if args.fp8 else 'false'}> "
-                          "(routed gate/up GEMM, weight-streaming)")
-    else:
-        roof["kernel"] = ("gemm_fp8_kernel<0> (routed gate/up GEMM, E4M3)" if args.fp8
-                          else "gemm_kernel<0, true> (routed gate/up GEMM)")
+    roof["traffic"] = traffic_for(args.workload, cfg.N, args.fp8)
+    kname, _ = roofline_kernel(cfg.N, args.fp8)
+    roof["kernel"] = kname + (" (routed gate/up GEMM, weight-streaming)" if cfg.N <= 64 else
+                              " (routed gate/up GEMM, E4M3)" if args.fp8 else
+                              " (routed gate/up GEMM)")
     roof["per_launch"] = {"flops": flops, "bytes": bytes_, "avg_ms": gateup_ms,
                           "tflops": flops / t_gu / 1e12, "gbs": bytes_ / t_gu / 1e9,
                           "mfma_frac": flops / t_gu / 1e12 / peak_mfma}
