@@ -687,7 +687,15 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
   const int wg = wave >> 2;
   const int wp = wave & 3;
   const int sub = lane >> 3;
-  const int chunk = (lane & 7) ^ ((4 * wave + (sub >> 1)) & 7);  // as in the bf16 tile
+  // LDS layout of an operand row (128 bytes, eight 16-byte chunks): chunk c
+  // of row r sits at slot g(c) ^ ((r >> 1) & 7), g(c) = c ^ 4 ((c >> 1) & 1),
+  // so the 32-byte fragment reads below (lane l: row l & 15, chunks 2q and
+  // 2q + 1 of q = l >> 4) put lanes of quads 0 and 1 (2 and 3) on different
+  // banks; with the bf16 tile's c ^ ((r >> 1) & 7) they shared them (0.7
+  // conflicts per LDS access).  g is its own inverse: LDS slot (l & 7) of a
+  // lane's row receives global chunk g((l & 7) ^ ((r >> 1) & 7)).
+  auto g_chunk = [](int c) { return c ^ (4 * ((c >> 1) & 1)); };
+  const int chunk = g_chunk((lane & 7) ^ ((4 * wave + (sub >> 1)) & 7));
   constexpr uint32_t kNoRow = 0xFFFFFFFFu - 64u * 1024u;  // past any 4 GiB buffer
   constexpr int NA_LD = XR ? 5 : 4;
   uint32_t a_voff[NA_LD], b_voff[4];
@@ -695,7 +703,7 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
   for (int i = 0; i < NA_LD; ++i) {
     // the extra load (XR) of wave w: rows 256 + 4w .. +3 from lanes 0-31
     const int r = (i < 4) ? 8 * (8 * i + wave) + sub : BM + 4 * wave + (sub & 3);
-    const int ch = (i < 4) ? chunk : ((lane & 7) ^ ((2 * wave + (sub >> 1)) & 7));
+    const int ch = (i < 4) ? chunk : g_chunk((lane & 7) ^ ((2 * wave + (sub >> 1)) & 7));
     if (r < rows) {
       int64_t arow = row0 + r;
       if (GROUPED && a.gather) arow = a.gather[arow] / a.gather_div;
@@ -833,11 +841,11 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
     constexpr int LIVE = decltype(live_tag)::value;
     constexpr int MB = 2 * LIVE;  // 16-row blocks
     constexpr bool XB = XR > 0 && LIVE > 0;  // the extra block
-    const int s0 = ((2 * quad) ^ ((lane >> 1) & 7)) * 16;
-    const int s1 = ((2 * quad + 1) ^ ((lane >> 1) & 7)) * 16;
-    // lane l reads 32 bytes of its row: chunks 2*(l>>4) and +1 (swizzled;
-    // fragments start on multiples of 16 rows, so (row >> 1) & 7 =
-    // (l >> 1) & 7)
+    const int s0 = ((2 * quad) ^ (4 * (quad & 1)) ^ ((lane >> 1) & 7)) * 16;
+    const int s1 = ((2 * quad + 1) ^ (4 * (quad & 1)) ^ ((lane >> 1) & 7)) * 16;
+    // lane l reads 32 bytes of its row: chunks 2*(l>>4) and +1 at their
+    // slots g(c) ^ ((row >> 1) & 7) (fragments start on multiples of 16
+    // rows, so (row >> 1) & 7 = (l >> 1) & 7)
     auto frag = [&](const char* rowp) {
       typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
       const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(rowp + s0);
