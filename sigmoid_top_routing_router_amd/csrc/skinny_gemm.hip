@@ -91,9 +91,11 @@ __global__ __launch_bounds__(256) void skinny_kernel(GemmArgs a, int n_chunks) {
   // one k-step of 128.  Each LDS-DMA load moves 8 whole rows of a set (lane i:
   // row i >> 3, 16-byte chunk i & 7 of the LDS row), so every access is one
   // whole 128-byte line; a 16-row block takes two loads.  The eight chunks of
-  // row r sit at LDS slot c ^ ((r >> 1) & 7) (the loads pick their global
+  // row r sit at LDS slot g(c) ^ ((r >> 1) & 7) (the loads pick their global
   // chunk accordingly), so the fragment reads of 16 rows with one chunk hit
-  // 16 different bank groups.  A set: 4 weight blocks, the block of 16
+  // 16 different bank groups; g(c) = c for bf16, and for E4M3, whose lanes of
+  // quads 0 and 1 (2 and 3) read chunks 2q and 2q + 1 of the same rows,
+  // g(c) = c ^ 4 ((c >> 1) & 1) keeps those quads on different banks too.  A set: 4 weight blocks, the block of 16
   // activation rows, and for E4M3 the activation scale of each lane's row
   // and the two weight-block scales (4-byte loads).  The loads do not go
   // through registers, so the compiler inserts no waits for them; the
@@ -103,9 +105,11 @@ __global__ __launch_bounds__(256) void skinny_kernel(GemmArgs a, int n_chunks) {
   const int nsets = (a.kdim + SET_K - 1) / SET_K;
   const bool half_last = !FP8 && (a.kdim % 64) != 0;  // last bf16 set holds one k-step
   // DMA lane roles: row 8*h + (lane >> 3) of a 16-row block (h = 0, 1), LDS
-  // chunk lane & 7, global chunk (lane & 7) ^ ((4*h + (lane >> 4)) & 7)
-  const uint32_t gchunk0 = (uint32_t)((lane & 7) ^ ((lane >> 4) & 7)) * 16u;
-  const uint32_t gchunk1 = (uint32_t)((lane & 7) ^ ((4 + (lane >> 4)) & 7)) * 16u;
+  // chunk lane & 7, global chunk g((lane & 7) ^ ((4*h + (lane >> 4)) & 7))
+  // (g is its own inverse)
+  auto g_chunk = [](int c) { return FP8 ? (c ^ (4 * ((c >> 1) & 1))) : c; };
+  const uint32_t gchunk0 = (uint32_t)g_chunk((lane & 7) ^ ((lane >> 4) & 7)) * 16u;
+  const uint32_t gchunk1 = (uint32_t)g_chunk((lane & 7) ^ ((4 + (lane >> 4)) & 7)) * 16u;
   const uint32_t set_bytes = SET_K * EB;
   const uint32_t b_bytes = (uint32_t)a.b_rows * (uint32_t)a.kdim * EB;
   const char* bexp0 = reinterpret_cast<const char*>(a.B0) + (int64_t)expert * a.b_expert_stride * EB;
@@ -196,7 +200,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(GemmArgs a, int n_chunks) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int c = FP8 ? 2 * q + j : 4 * j + q;
-        foff[j] = fr * 128 + ((c ^ ((fr >> 1) & 7)) * 16);
+        foff[j] = fr * 128 + ((g_chunk(c) ^ ((fr >> 1) & 7)) * 16);
       }
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
