@@ -264,3 +264,22 @@ def test_stage_timing_records_every_stage(M):
     M.stage_timing(False)
     assert calls == 2 and times["gate_up"] > 0
     assert all(v == 0 for k, v in times.items() if k != "gate_up"), times
+    # light mode also on the weight-streaming path (N <= 64) and with E4M3
+    # experts
+    small = scaled(CONFIGS["prefill"], 64)
+    Ls = _inputs(small)
+    Wq = M.quantize_experts(W)
+    for run in (lambda: M.forward(bf16_dev(Ls.x), weights_dev(Ls), small.K,
+                                  beta_in=dev(Ls.beta_in), recompute_bias=True),
+                lambda: M.forward_fp8(x, Wq, cfg.K, beta_in=dev(L.beta_in), recompute_bias=True)):
+        M.stage_timing(2)
+        run()
+        times, calls = M.stage_times()
+        M.stage_timing(False)
+        assert calls == 1 and times["gate_up"] > 0, times
+    # and full mode again after it times every stage
+    M.stage_timing(True)
+    M.forward(x, W, cfg.K, beta_in=dev(L.beta_in), recompute_bias=True)
+    times, calls = M.stage_times()
+    M.stage_timing(False)
+    assert calls == 1 and all(v > 0 for v in times.values()), times
