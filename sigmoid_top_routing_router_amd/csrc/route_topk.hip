@@ -182,11 +182,13 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 // score -inf, below every finite score).
 //
 // Schedule: one quad of rows per wave and a block per four quads, with no
-// loop; four blocks per CU are resident (registers), so other waves' loads
-// overlap a wave's selection.  The results (ids, weights, the K-th and
-// (K+1)-th scores) are gathered in LDS and stored by the wave at its end; the
-// lanes that rank a winning candidate read its unbiased logit back from
-// memory (an L2 hit) for the weight.  (A grid-stride loop that loads the next
+// loop; seven blocks per CU are resident (registers, at E = 384), so other
+// waves' loads overlap a wave's selection.  The results (ids, the picks'
+// unbiased logits, the K-th and (K+1)-th scores) are gathered in LDS and
+// stored by the wave at its end; the lanes that rank a winning candidate read
+// its unbiased logit back from memory (an L2 hit), and the weight is formed
+// from it only at the store, where little else is live (the sigmoid's fp64
+// branch needs many registers).  (A grid-stride loop that loads the next
 // quad during the selection was no faster: the gather for the weights waits
 // for every load in flight, the prefetch included.)
 //
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(256) void route_group_kernel(
   __shared__ float cand_s[4][4][kRouteCap];     // candidate scores
   __shared__ uint32_t cand_e[4][4][kRouteCap];  // their experts
   __shared__ int32_t out_id[4][4][MOE_KMAX_INTERNAL];
-  __shared__ float out_s[4][4][MOE_KMAX_INTERNAL];
+  __shared__ float out_s[4][4][MOE_KMAX_INTERNAL];  // unbiased logits of the picks
   __shared__ float kk[4][4][2];                 // K-th and (K+1)-th score
   for (int i = (int)threadIdx.x; i < 16 * NC; i += 256) {
     const int e0 = 4 * (i & 15) + 64 * (i >> 4);
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(256) void route_group_kernel(
     if (row < N) {
       if (g < K) {
         if (ids) ids[row * K + g] = oid[g];
-        if (S) S[row * K + g] = os[g];
+        if (S) S[row * K + g] = sigmoid_weight(os[g]);
       }
       if (g == 0) {
         if (alpha) alpha[row] = -kl[1];
@@ -331,37 +333,45 @@ __global__ __launch_bounds__(256) void route_group_kernel(
         }
         if (rank < (uint32_t)K) {
           oid[rank] = (int32_t)ei;
-          os[rank] = sigmoid_weight(Z[(quad * 4 + grp) * (int64_t)E + ei]);
+          os[rank] = Z[(quad * 4 + grp) * (int64_t)E + ei];
         }
         if (rank == (uint32_t)K - 1) kl[0] = si;
         if (rank == (uint32_t)K) kl[1] = si;
       }
     } else {
-      // (2') pops: the lane's largest score and, among equal ones, its lowest
-      // expert (the slots run in expert order), then the row's
-      float vK = 0.f, vK1 = 0.f;
+      // (2') pops in the order (score descending, expert ascending): pop r
+      // takes the row's best (score, expert) that comes after pop r - 1 in
+      // that order, so the scores are only read, never cleared.  A lane's
+      // experts 64*(i >> 2) + 4g + (i & 3) rise with its slot i, so "expert
+      // above ep" is "slot at least k_le", the number of the lane's experts
+      // up to ep, and the lane's lowest expert of equal scores is its first
+      // slot of them: no expert ids are held per slot.
+      float sp = INFINITY, vK = 0.f, vK1 = 0.f;
+      int k_le = 0;
 #pragma unroll 1
       for (int r = 0; r <= K; ++r) {
-        float lmx = v[0];
+        float bs = -INFINITY;
+        int bi = -1;
 #pragma unroll
-        for (int i = 1; i < NVL; ++i) lmx = fmaxf(lmx, v[i]);
-        int bi = NVL - 1;
-#pragma unroll
-        for (int i = NVL - 1; i >= 0; --i) bi = (v[i] == lmx) ? i : bi;
-        const uint32_t el = (uint32_t)(64 * (bi >> 2) + 4 * g + (bi & 3));
-        const float rmx = row16_max_f32(lmx);
-        const uint32_t we = row16_min_u32(lmx == rmx ? el : 0xFFFFFFFFu);
+        for (int i = 0; i < NVL; ++i) {
+          const float sv = v[i];
+          const bool after = r == 0 || sv < sp || (sv == sp && i >= k_le);
+          const bool better = after && sv > bs;
+          bs = better ? sv : bs;
+          bi = better ? i : bi;
+        }
+        const uint32_t be = bi >= 0 ? (uint32_t)(64 * (bi >> 2) + 4 * g + (bi & 3)) : 0xFFFFFFFFu;
+        const float rmx = row16_max_f32(bs);
+        const uint32_t we = row16_min_u32(bs == rmx ? be : 0xFFFFFFFFu);
         if (r == K - 1) vK = rmx;
         if (r == K) vK1 = rmx;
-        if (el == we) {
-          const float z = Z[(quad * 4 + grp) * (int64_t)E + we];
-          if (r < K) {
-            oid[r] = (int32_t)we;
-            os[r] = sigmoid_weight(z);
-          }
-#pragma unroll
-          for (int i = 0; i < NVL; ++i) v[i] = (i == bi) ? -INFINITY : v[i];
+        if (r < K && be == we) {
+          oid[r] = (int32_t)we;
+          os[r] = Z[(quad * 4 + grp) * (int64_t)E + we];
         }
+        sp = rmx;
+        const int wa = (int)(we >> 6), wg2 = (int)((we >> 2) & 15u), wc = (int)(we & 3u);
+        k_le = 4 * wa + (g < wg2 ? 4 : (g == wg2 ? wc + 1 : 0));
       }
       if (g == 0) {
         kl[0] = vK;
