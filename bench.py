@@ -289,7 +289,7 @@ def cpu_baseline(cfg, L, gpu, runs=3):
     return base, parity
 
 
-def run_extra(M, torch, name, steps, warmup):
+def run_extra(M, torch, name, steps, warmup, packed=True):
     """Another workload of the same layer shape in the same run: step time
     and tokens/s (`steps` timed steps between device synchronisations), and
     the stage times of `steps` further steps (HIP events between stages).
@@ -307,6 +307,9 @@ def run_extra(M, torch, name, steps, warmup):
 
     W = M.ExpertWeights(bf16(L.w_router), bf16(L.w_gate), bf16(L.w_up), bf16(L.w_down),
                         bf16(L.ws_gate), bf16(L.ws_up), bf16(L.ws_down))
+    if packed:
+        W = M.pack_gateup(W)  # untimed, as at weight-loading time
+        torch.cuda.synchronize()
     x = bf16(L.x)
     beta = torch.from_numpy(L.beta_in).cuda()
     off = None if L.logit_offset is None else torch.from_numpy(L.logit_offset).cuda()
@@ -504,6 +507,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the skewed and decode workloads measured after the headline")
+    ap.add_argument("--row-major", action="store_true",
+                    help="bf16 routed gate/up weights in the row-major layout instead of the "
+                         "packed one (moe_pack_gateup_weights)")
     ap.add_argument("--fp8", action="store_true",
                     help="E4M3 experts (moe_forward_fp8) quantised from the same bf16 weights")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -565,6 +571,12 @@ def main():
         W = M.quantize_experts(W)
         torch.cuda.synchronize()
         fwd, ws_fn = M.forward_fp8, M.forward_fp8_workspace_bytes
+    elif not args.row_major:
+        # the routed gate/up weights in the library's packed layout, as a
+        # deployment stores them (untimed; the results are bit-identical)
+        W = M.pack_gateup(W)
+        torch.cuda.synchronize()
+        log("gate/up weights packed")
     x = bf16(L.x)
     beta = torch.from_numpy(L.beta_in).cuda()
     off = None if L.logit_offset is None else torch.from_numpy(L.logit_offset).cuda()
@@ -650,7 +662,8 @@ def main():
         roof = {"bound": "mfma", "achieved": flops / t_gu / 1e12, "peak": peak_mfma,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = traffic_for(args.workload, cfg.N, args.fp8)
+    # the traffic records are taken with the default (packed) layout
+    roof["traffic"] = None if args.row_major else traffic_for(args.workload, cfg.N, args.fp8)
     kname, _ = roofline_kernel(cfg.N, args.fp8)
     roof["kernel"] = kname + (" (routed gate/up GEMM, weight-streaming)" if cfg.N <= 64 else
                               " (routed gate/up GEMM, E4M3)" if args.fp8 else
@@ -670,7 +683,9 @@ def main():
         "data": "synthetic (seeded normal inputs and random-init weights of the layer shape)",
         "config": {**cfg.describe(), "parallelism": "none (1 GPU)",
                    **({"experts": "e4m3, 128x128 block scales, 1x128 activation groups"}
-                      if args.fp8 else {})},
+                      if args.fp8 else
+                      {"gate_up_weights": "row-major" if args.row_major else
+                       "packed k-block-major (moe_pack_gateup_weights, untimed)"})},
         "layer_tflops": layer_flops / (ms_step * 1e-3) / 1e12,
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "loads": {"max_over_mean_before": float(counts_before.max() / counts_before.mean()),
@@ -681,8 +696,8 @@ def main():
             and not args.inference:
         del ws, y, x, W
         torch.cuda.empty_cache()
-        out["extras"] = {n: run_extra(M, torch, n, s, 3) for n, s in (("skewed", 10),
-                                                                      ("decode", 50))}
+        out["extras"] = {n: run_extra(M, torch, n, s, 3, not args.row_major)
+                         for n, s in (("skewed", 10), ("decode", 50))}
     if not args.no_cpu_baseline and not args.fp8:
         log("cpu baseline ...")
         out["cpu_baseline"], out["parity"] = cpu_baseline(cfg, L, gpu_out, args.cpu_runs)

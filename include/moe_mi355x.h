@@ -56,6 +56,7 @@ typedef enum {
 /* Flags of moe_problem_t.flags */
 #define MOE_RECOMPUTE_BIAS 0x1u  /* route with beta_in, one exact quantile update, re-route */
 #define MOE_KEY32 0x2u           /* quantile over fp32 keys instead of bf16 keys */
+#define MOE_PACKED_GATEUP 0x4u   /* w_gate, w_up packed by moe_pack_gateup_weights (bf16 only) */
 
 /*
  * moe_route - bias-corrected top-K selection and sigmoid mixture weights over
@@ -214,7 +215,7 @@ typedef struct {
   int32_t h;          /* routed expert hidden width */
   int32_t n_shared;   /* 0 or 1 always-on shared expert */
   int32_t h_shared;   /* shared expert hidden width */
-  uint32_t flags;     /* MOE_RECOMPUTE_BIAS | MOE_KEY32 */
+  uint32_t flags;     /* MOE_RECOMPUTE_BIAS | MOE_KEY32 | MOE_PACKED_GATEUP */
   const float* logit_offset; /* [E] fp32 or NULL: added to Z before the bias
                                 (an input-side knob, not part of the method) */
   const float* logits_in;    /* [N,E] fp32 or NULL: use these logits instead
@@ -287,6 +288,29 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_weights_t* w,
                          const uint16_t* x, const float* beta_in, uint16_t* y,
                          moe_aux_t* aux, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/*
+ * Packed gate/up weights, for moe_forward and moe_forward_noalloc with
+ * MOE_PACKED_GATEUP.  The routed experts' gate and up products of the
+ * SwiGLU in [K1D] (Routing section) read their weights 64 columns (128
+ * bytes) of every row at a time; this layout keeps the pieces read together
+ * next to each other.  It changes no value and no order of arithmetic: the
+ * layer's output with packed weights is bit-identical to the row-major one.
+ *
+ * moe_pack_gateup_weights - `count` bf16 matrices w [count,rows,cols]
+ *   (row-major; the layer's w_gate or w_up, [E,h,d]) -> out
+ *   [count, cols/64, rows, 64], i.e. out[c][k][r][j] = w[c][r][64k + j].
+ *   cols % 64 == 0 (64 <= cols <= 65536), 1 <= rows <= 65536,
+ *   0 <= count <= 65535; w and out are caller-owned device memory, 16-byte
+ *   aligned, not overlapping.  Enqueues one kernel on `stream`; out is fully
+ *   overwritten.  With MOE_PACKED_GATEUP set, moe_forward reads w_gate and
+ *   w_up in this layout (the shared expert and w_down stay row-major);
+ *   moe_forward_fp8 rejects the flag.
+ * Errors: INVALID_ARGUMENT (NULL, misaligned or overlapping buffers),
+ *   UNSUPPORTED_SHAPE, HIP.
+ */
+moe_status_t moe_pack_gateup_weights(const uint16_t* w, int64_t count, int32_t rows,
+                                     int32_t cols, uint16_t* out, void* stream);
 
 /*
  * FP8 (E4M3) experts, [K1D] FP8 section: expert weights stored as E4M3 in

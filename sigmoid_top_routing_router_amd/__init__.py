@@ -10,19 +10,19 @@ from __future__ import annotations
 
 import contextlib
 import ctypes as C
-from dataclasses import dataclass
+from dataclasses import dataclass, replace
 from typing import Optional
 
 from . import _lib
-from ._lib import (MOE_KEY32, MOE_RECOMPUTE_BIAS, MoeAux, MoeError, MoeFp8Weights, MoeProblem,
-                   MoeWeights)
+from ._lib import (MOE_KEY32, MOE_PACKED_GATEUP, MOE_RECOMPUTE_BIAS, MoeAux, MoeError,
+                   MoeFp8Weights, MoeProblem, MoeWeights)
 
 __all__ = ["route", "eqb_bias", "eqb_workspace_bytes", "EqbState", "eqb_bias_parts",
            "route_stats", "read_route_stats", "lei_backward", "forward",
            "forward_workspace_bytes", "fp8_quantize_blocks", "fp8_quantize_rows",
            "Fp8ExpertWeights", "quantize_experts", "forward_fp8", "forward_fp8_workspace_bytes",
            "ExpertWeights", "MoeError", "load_library", "stage_timing", "stage_times",
-           "forward_noalloc"]
+           "forward_noalloc", "pack_gateup", "pack_gateup_weights"]
 
 AUX_FIELDS = [f for f, _ in MoeAux._fields_]
 
@@ -247,6 +247,7 @@ class ExpertWeights:
     ws_gate: object = None  # [S, hs, d]
     ws_up: object = None    # [S, hs, d]
     ws_down: object = None  # [S, d, hs]
+    packed: bool = False    # w_gate, w_up as [E, d/64, h, 64] (pack_gateup)
 
 
 def _problem(N, d, E, K, h, n_shared, h_shared, flags, logit_offset, logits_in):
@@ -266,6 +267,31 @@ def forward_fp8_workspace_bytes(N, d, E, K, h, n_shared=1, h_shared=None,
     flags = (MOE_RECOMPUTE_BIAS if recompute_bias else 0) | (MOE_KEY32 if key_bits == 32 else 0)
     p = _problem(N, d, E, K, h, n_shared, h_shared or h, flags, None, None)
     return int(_lib.load().moe_forward_fp8_workspace_bytes(C.byref(p)))
+
+
+def pack_gateup_weights(w, stream=None):
+    """moe_pack_gateup_weights: bf16 [count, rows, cols] (cols % 64 == 0) ->
+    [count, cols/64, rows, 64], out[c, k, r, j] = w[c, r, 64k + j]."""
+    torch = _torch()
+    w = _dev(w, "w", _bf16())
+    if w.dim() != 3:
+        raise ValueError("w must be [count, rows, cols]")
+    cnt, R, Cc = w.shape
+    with _on(stream):
+        out = torch.empty((cnt, Cc // 64, R, 64), dtype=torch.bfloat16, device=w.device)
+        _lib.check(_lib.load().moe_pack_gateup_weights(_ptr(w), cnt, R, Cc, _ptr(out),
+                                                       _stream(stream)))
+    return out
+
+
+def pack_gateup(weights: ExpertWeights, stream=None) -> ExpertWeights:
+    """The same layer with its routed gate and up weights packed for the
+    tile engine (MOE_PACKED_GATEUP); forward() gives bit-identical results
+    with either form."""
+    if weights.packed:
+        return weights
+    return replace(weights, w_gate=pack_gateup_weights(weights.w_gate, stream),
+                   w_up=pack_gateup_weights(weights.w_up, stream), packed=True)
 
 
 def fp8_quantize_blocks(w, stream=None):
@@ -324,6 +350,8 @@ class Fp8ExpertWeights:
 def quantize_experts(weights: ExpertWeights, stream=None) -> Fp8ExpertWeights:
     """Quantise the expert weights of a bf16 layer with the library's block
     quantiser; the router is kept as it is."""
+    if weights.packed:
+        raise ValueError("quantize_experts takes row-major weights, not packed ones")
     q = {}
     for name in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
         t = getattr(weights, name)
@@ -351,14 +379,14 @@ def _aux_tensors(aux, N, E, K, device):
 
 
 def _run_forward(fp8, x, wstruct, N, d, E, K, h, n_shared, h_shared, beta_in, recompute_bias,
-                 key_bits, logit_offset, logits_in, aux, workspace, out, stream):
+                 key_bits, logit_offset, logits_in, aux, workspace, out, stream, extra_flags=0):
     torch = _torch()
     lib = _lib.load()
     beta_in = _dev(beta_in, "beta_in", torch.float32, (E,))
     logit_offset = _dev(logit_offset, "logit_offset", torch.float32, (E,))
     logits_in = _dev(logits_in, "logits_in", torch.float32, (N, E))
     flags = (MOE_RECOMPUTE_BIAS if recompute_bias else 0) | (MOE_KEY32 if key_bits == 32 else 0)
-    p = _problem(N, d, E, K, h, n_shared, h_shared, flags, logit_offset, logits_in)
+    p = _problem(N, d, E, K, h, n_shared, h_shared, flags | extra_flags, logit_offset, logits_in)
     ws_fn = lib.moe_forward_fp8_workspace_bytes if fp8 else lib.moe_forward_workspace_bytes
     fwd = lib.moe_forward_fp8 if fp8 else lib.moe_forward
     need = int(ws_fn(C.byref(p)))
@@ -381,8 +409,14 @@ def _bf16_weights(x, weights: ExpertWeights):
     x = _dev(x, "x", _bf16())
     N, d = x.shape
     wg = _dev(weights.w_gate, "w_gate", _bf16())
-    E, h, _ = wg.shape
-    _dev(weights.w_up, "w_up", _bf16(), (E, h, d))
+    if weights.packed:
+        if wg.dim() != 4 or wg.shape[1] * 64 != d or wg.shape[3] != 64:
+            raise ValueError("packed w_gate must be [E, d/64, h, 64]")
+        E, _, h, _ = wg.shape
+        _dev(weights.w_up, "w_up", _bf16(), (E, d // 64, h, 64))
+    else:
+        E, h, _ = wg.shape
+        _dev(weights.w_up, "w_up", _bf16(), (E, h, d))
     _dev(weights.w_down, "w_down", _bf16(), (E, d, h))
     if weights.w_router is not None:
         _dev(weights.w_router, "w_router", _bf16(), (E, d))
@@ -405,7 +439,8 @@ def forward(x, weights: ExpertWeights, K: int, beta_in=None, recompute_bias: boo
     (y, dict) when ``aux`` names optional outputs (see moe_aux_t)."""
     x, w, N, d, E, h, n_shared, h_shared = _bf16_weights(x, weights)
     return _run_forward(False, x, w, N, d, E, K, h, n_shared, h_shared, beta_in, recompute_bias,
-                        key_bits, logit_offset, logits_in, aux, workspace, out, stream)
+                        key_bits, logit_offset, logits_in, aux, workspace, out, stream,
+                        MOE_PACKED_GATEUP if weights.packed else 0)
 
 
 def forward_noalloc(x, weights: ExpertWeights, K: int, beta_in=None,
@@ -423,6 +458,7 @@ def forward_noalloc(x, weights: ExpertWeights, K: int, beta_in=None,
     logit_offset = _dev(logit_offset, "logit_offset", torch.float32, (E,))
     logits_in = _dev(logits_in, "logits_in", torch.float32, (N, E))
     flags = (MOE_RECOMPUTE_BIAS if recompute_bias else 0) | (MOE_KEY32 if key_bits == 32 else 0)
+    flags |= MOE_PACKED_GATEUP if weights.packed else 0
     p = _problem(N, d, E, K, h, n_shared, h_shared, flags, logit_offset, logits_in)
     with _on(stream):
         y = out if out is not None else torch.empty((N, d), dtype=torch.bfloat16, device=x.device)

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
 MOE_OK = 0
 MOE_RECOMPUTE_BIAS = 0x1
 MOE_KEY32 = 0x2
+MOE_PACKED_GATEUP = 0x4
 
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED_SHAPE",
                 3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
@@ -22,7 +23,8 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPOR
 EXPORTED = ["moe_route", "moe_eqb_workspace_bytes", "moe_eqb_bias", "moe_eqb_state_bytes",
             "moe_eqb_begin", "moe_eqb_accumulate", "moe_eqb_select", "moe_route_stats",
             "moe_lei_workspace_bytes", "moe_lei_backward",
-            "moe_forward_workspace_bytes", "moe_forward", "moe_fp8_quantize_blocks",
+            "moe_forward_workspace_bytes", "moe_forward", "moe_pack_gateup_weights",
+            "moe_fp8_quantize_blocks",
             "moe_fp8_quantize_rows", "moe_forward_fp8_workspace_bytes", "moe_forward_fp8",
             "moe_forward_noalloc",
             "moe_status_string",
@@ -114,6 +116,8 @@ def load(path: str = LIB_PATH):
     lib.moe_forward.argtypes = [C.POINTER(MoeProblem), C.POINTER(MoeWeights), vp, vp, vp,
                                 C.POINTER(MoeAux), vp, C.c_size_t, vp]
     lib.moe_forward.restype = C.c_int
+    lib.moe_pack_gateup_weights.argtypes = [vp, i64, i32, i32, vp, vp]
+    lib.moe_pack_gateup_weights.restype = C.c_int
     lib.moe_fp8_quantize_blocks.argtypes = [vp, i64, i32, i32, vp, vp, vp]
     lib.moe_fp8_quantize_blocks.restype = C.c_int
     lib.moe_fp8_quantize_rows.argtypes = [vp, i64, i32, vp, vp, vp]

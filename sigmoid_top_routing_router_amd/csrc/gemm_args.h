@@ -41,7 +41,25 @@ struct GemmArgs {
   // gate/up only: when set, H leaves as E4M3 codes (out, ldo bytes per row)
   // with one fp32 scale per 1 x 128 group of a row (out_scale [rows][ldo/128])
   float* out_scale;
+  // Layout of an expert's B matrix, in bytes: from one row to the next, and
+  // from one 128-byte k-block of a row to the next.  Row-major: (kdim times
+  // the element size, 128); k-block-major (bf16 gate/up weights packed by
+  // moe_pack_gateup_weights): (128, b_rows * 128), so that the 128-byte
+  // pieces one stage of the tile reads are one contiguous run.
+  uint32_t b_row_pitch;
+  uint32_t b_kblk_pitch;
 };
+
+// Row-major B (every builder's default).
+inline void b_row_major(GemmArgs& a, int elem_bytes) {
+  a.b_row_pitch = (uint32_t)a.kdim * (uint32_t)elem_bytes;
+  a.b_kblk_pitch = 128u;
+}
+// k-block-major B: [expert][kdim / 64][b_rows][64] bf16.
+inline void b_kblock_major(GemmArgs& a) {
+  a.b_row_pitch = 128u;
+  a.b_kblk_pitch = (uint32_t)a.b_rows * 128u;
+}
 
 // ---- builders (bf16 operands unless named fp8)
 inline GemmArgs router_args(const uint16_t* x, const uint16_t* w_router, const float* offset,
@@ -52,6 +70,7 @@ inline GemmArgs router_args(const uint16_t* x, const uint16_t* w_router, const f
   a.B0 = w_router; a.B1 = nullptr; a.b_expert_stride = 0; a.b_rows = E; a.kdim = d;
   a.n_tiles_n = (E + kTileN - 1) / kTileN; a.out = Z; a.ldo = E; a.offset = offset;
   a.a_bytes = (uint32_t)(N * d * 2);
+  b_row_major(a, 2);
   return a;
 }
 
@@ -65,6 +84,7 @@ inline GemmArgs gateup_args(const uint16_t* x, int64_t x_rows, const int32_t* so
   a.B0 = w_gate; a.B1 = w_up; a.b_expert_stride = (int64_t)h * d; a.b_rows = h; a.kdim = d;
   a.n_tiles_n = (h + kTileN / 2 - 1) / (kTileN / 2); a.out = H; a.ldo = h; a.offset = nullptr;
   a.a_bytes = (uint32_t)(x_rows * d * 2);
+  b_row_major(a, 2);
   return a;
 }
 
@@ -77,6 +97,7 @@ inline GemmArgs down_args(const uint16_t* H, int64_t h_rows, const int32_t* tile
   a.B0 = w_down; a.B1 = nullptr; a.b_expert_stride = (int64_t)d * h; a.b_rows = d; a.kdim = h;
   a.n_tiles_n = (d + kTileN - 1) / kTileN; a.out = Y; a.ldo = d; a.offset = nullptr;
   a.a_bytes = (uint32_t)(h_rows * h * 2);
+  b_row_major(a, 2);
   return a;
 }
 
@@ -95,6 +116,7 @@ inline GemmArgs gateup_fp8_args(const uint8_t* xq, const float* xs, int64_t x_ro
   a.a_bytes = (uint32_t)(x_rows * d);
   a.sa = xs; a.sb0 = sg; a.sb1 = su; a.sb_es = (int64_t)(h / 128) * (d / 128);
   a.out_scale = Hs;
+  b_row_major(a, 1);
   return a;
 }
 
@@ -110,6 +132,7 @@ inline GemmArgs down_fp8_args(const uint8_t* Hq, const float* Hs, int64_t h_rows
   a.a_bytes = (uint32_t)(h_rows * h);
   a.sa = Hs; a.sb0 = sd; a.sb1 = sd; a.sb_es = (int64_t)(d / 128) * (h / 128);
   a.out_scale = nullptr;
+  b_row_major(a, 1);
   return a;
 }
 

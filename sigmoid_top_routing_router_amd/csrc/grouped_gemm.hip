@@ -409,7 +409,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
       const int brow = (MODE == kGateUp) ? nt * (BN / 2) + (r & (BN / 2 - 1))
                        : NARROW ? (r < BN / 2 ? nt * (BN / 2) + r : a.b_rows)
                                 : nt * BN + r;
-      b_voff[i] = (brow < a.b_rows) ? (uint32_t)brow * (uint32_t)a.kdim * 2u + (uint32_t)chunk * 16u
+      b_voff[i] = (brow < a.b_rows) ? (uint32_t)brow * a.b_row_pitch + (uint32_t)chunk * 16u
                                     : kNoRow;
     }
   }
@@ -445,7 +445,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int64_t mt, int nt,
   // B load i of stage ks fills quarter i (B rows 64*i .. +63)
   auto dma_b = [&](int ks, int i) {
     dma16<BNT ? kCpolNT : 0>((MODE == kGateUp && i >= 2) ? rb1 : rb0, voff_at(b_voff[i], ks, tail_adj),
-          (uint32_t)ks * (BK * 2),
+          (uint32_t)ks * a.b_kblk_pitch,
           (lds_void_t*)(lds_raw + B_BASE + bq(ks, i) * QUARTER + wave * 1024));
   };
 
@@ -1171,9 +1171,10 @@ hipError_t launch_gateup(const uint16_t* x, int64_t x_rows, const int32_t* sorte
                          const int32_t* tiles, const int32_t* n_tiles, int64_t max_tiles,
                          int64_t rows_dense, const uint16_t* w_gate,
                          const uint16_t* w_up, int d, int h, uint16_t* H,
-                         hipStream_t stream) {
-  const GemmArgs a = gateup_args(x, x_rows, sorted_src, K, tiles, n_tiles, rows_dense, w_gate,
-                                 w_up, d, h, H);
+                         hipStream_t stream, bool kblock_major) {
+  GemmArgs a = gateup_args(x, x_rows, sorted_src, K, tiles, n_tiles, rows_dense, w_gate, w_up, d,
+                           h, H);
+  if (kblock_major) b_kblock_major(a);
   const int64_t mt = tiles ? max_tiles : (rows_dense + BM - 1) / BM;
   return launch_gemm(kGateUp, a, mt, stream);
 }

@@ -79,11 +79,13 @@ hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w_router,
 // silu(X W_g^T) * (X W_u^T) (bf16).  When `tiles` is NULL the rows are the
 // tokens 0..N-1 of one expert (shared expert), otherwise A rows are gathered
 // through sorted_src / K.  x has x_rows rows; x_rows * d * 2 < 4 GiB.
+// kblock_major: w_gate and w_up are [E][d/64][h][64] (moe_pack_gateup_weights)
+// instead of [E][h][d].
 hipError_t launch_gateup(const uint16_t* x, int64_t x_rows, const int32_t* sorted_src, int K,
                          const int32_t* tiles, const int32_t* n_tiles, int64_t max_tiles,
                          int64_t rows_dense, const uint16_t* w_gate,
                          const uint16_t* w_up, int d, int h, uint16_t* H,
-                         hipStream_t stream);
+                         hipStream_t stream, bool kblock_major = false);
 // Grouped down projection: Y rows = H rows W_d^T (bf16 out).  H has h_rows
 // rows; h_rows * h * 2 < 4 GiB.
 hipError_t launch_down(const uint16_t* H, int64_t h_rows, const int32_t* tiles, const int32_t* n_tiles,
@@ -172,6 +174,9 @@ hipError_t launch_gateup_small(const uint16_t* x, int64_t x_rows, const int32_t*
                                int K, const int32_t* tiles, const int32_t* n_tiles,
                                int64_t max_tiles, int64_t rows_dense, const uint16_t* w_gate,
                                const uint16_t* w_up, int d, int h, uint16_t* H,
+                               hipStream_t stream, bool kblock_major = false);
+// Packs [E][rows][cols] bf16 (cols % 64 == 0) into [E][cols/64][rows][64].
+hipError_t launch_pack_kblocks(const uint16_t* w, int64_t E, int rows, int cols, uint16_t* out,
                                hipStream_t stream);
 hipError_t launch_down_small(const uint16_t* H, int64_t h_rows, const int32_t* tiles,
                              const int32_t* n_tiles, int64_t max_tiles, int64_t rows_dense,

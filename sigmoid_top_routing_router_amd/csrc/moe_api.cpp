@@ -182,7 +182,7 @@ moe_status_t check_problem(const moe_problem_t* p) {
                 "N=%lld too large: x [N,d], the routed hidden rows [N*K,h] and the shared "
                 "hidden rows [N,h_shared] must each be below 4 GiB in bf16",
                 (long long)p->N);
-  if (p->flags & ~(MOE_RECOMPUTE_BIAS | MOE_KEY32))
+  if (p->flags & ~(MOE_RECOMPUTE_BIAS | MOE_KEY32 | MOE_PACKED_GATEUP))
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", p->flags);
   if (p->logits_in && p->logit_offset)
     return fail(MOE_ERR_INVALID_ARGUMENT, "logit_offset applies to computed logits only; logits_in is set");
@@ -199,6 +199,8 @@ moe_status_t check_problem_fp8(const moe_problem_t* p) {
     return fail(MOE_ERR_UNSUPPORTED_SHAPE,
                 "FP8 experts need d, h and h_shared to be multiples of 128 (d=%d h=%d hs=%d)",
                 p->d, p->h, p->h_shared);
+  if (p->flags & MOE_PACKED_GATEUP)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "MOE_PACKED_GATEUP applies to bf16 experts only");
   return MOE_OK;
 }
 
@@ -510,7 +512,8 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
                 "moe_forward: gate/up");
   else
     MOE_TRY_HIP(gateup(x, N, pw.sorted_src, K, pw.tiles, pw.n_tiles, l.max_tiles, 0, w->w_gate,
-                       w->w_up, d, h, l.H, st), "moe_forward: gate/up");
+                       w->w_up, d, h, l.H, st, (p->flags & MOE_PACKED_GATEUP) != 0),
+                "moe_forward: gate/up");
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
   if (ex.fp8)
     MOE_TRY_HIP(down8(l.Hq, l.Hqs, N * K, pw.tiles, pw.n_tiles, l.max_tiles, 0, q->w_down,
@@ -888,6 +891,28 @@ moe_status_t moe_fp8_quantize_blocks(const uint16_t* w, int64_t count, int32_t r
   if (!aligned(w, 2) || !aligned(scales, 4)) return fail(MOE_ERR_INVALID_ARGUMENT, "misaligned buffer");
   MOE_TRY_HIP(moe::launch_quant_blocks(w, count, rows, cols, codes, scales, (hipStream_t)stream),
               "moe_fp8_quantize_blocks");
+  return ok();
+}
+
+moe_status_t moe_pack_gateup_weights(const uint16_t* w, int64_t count, int32_t rows,
+                                     int32_t cols, uint16_t* out, void* stream) {
+  if (count < 0 || count > 65535 || rows < 1 || rows > 65536 || cols < 64 || cols > 65536 ||
+      cols % 64)
+    return fail(MOE_ERR_UNSUPPORTED_SHAPE,
+                "count=%lld rows=%d cols=%d: need 0 <= count <= 65535, 1 <= rows <= 65536 and "
+                "cols a multiple of 64 in [64, 65536]",
+                (long long)count, rows, cols);
+  if (count == 0) return ok();
+  if (!w || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "w and out are required");
+  if (!aligned(w, 16) || !aligned(out, 16))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "w and out must be 16-byte aligned");
+  const size_t bytes = (size_t)count * (size_t)rows * (size_t)cols * 2u;
+  const char* a0 = reinterpret_cast<const char*>(w);
+  const char* b0 = reinterpret_cast<const char*>(out);
+  if (a0 < b0 + bytes && b0 < a0 + bytes)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "out must not overlap w");
+  MOE_TRY_HIP(moe::launch_pack_kblocks(w, count, rows, cols, out, (hipStream_t)stream),
+              "moe_pack_gateup_weights");
   return ok();
 }
 

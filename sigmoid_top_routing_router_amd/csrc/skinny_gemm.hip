@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(GemmArgs a, int n_chunks) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int r = min(wcol[mb] + 8 * h + (lane >> 3), a.b_rows - 1);
-      w_voff[mb][h] = (uint32_t)r * (uint32_t)a.kdim * EB + (h ? gchunk1 : gchunk0);
+      w_voff[mb][h] = (uint32_t)r * a.b_row_pitch + (h ? gchunk1 : gchunk0);
     }
   // E4M3 scales: [A rows][kdim / 128] for the activations, the expert's
   // [b_rows / 128][kdim / 128] for the weights (unused resources cover 0 bytes)
@@ -161,11 +161,12 @@ __global__ __launch_bounds__(256) void skinny_kernel(GemmArgs a, int n_chunks) {
     auto issue = [&](int s) {
       char* slot = ring + (s % kRing) * kSlot;
       const uint32_t soff = (uint32_t)s * set_bytes;
+      const uint32_t soff_w = (uint32_t)s * a.b_kblk_pitch;  // a set is one 128-byte k-block
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         const __amdgpu_buffer_rsrc_t rw = (MODE == kGateUp && mb >= 2) ? rw1 : rw0;
-        dma16(rw, w_voff[mb][0], soff, (lds_void_t*)(slot + (2 * mb) * 1024));
-        dma16(rw, w_voff[mb][1], soff, (lds_void_t*)(slot + (2 * mb + 1) * 1024));
+        dma16(rw, w_voff[mb][0], soff_w, (lds_void_t*)(slot + (2 * mb) * 1024));
+        dma16(rw, w_voff[mb][1], soff_w, (lds_void_t*)(slot + (2 * mb + 1) * 1024));
       }
       dma16(ra, t_voff[0], soff, (lds_void_t*)(slot + 8 * 1024));
       dma16(ra, t_voff[1], soff, (lds_void_t*)(slot + 9 * 1024));
@@ -350,9 +351,10 @@ hipError_t launch_gateup_small(const uint16_t* x, int64_t x_rows, const int32_t*
                                int K, const int32_t* tiles, const int32_t* n_tiles,
                                int64_t max_tiles, int64_t rows_dense, const uint16_t* w_gate,
                                const uint16_t* w_up, int d, int h, uint16_t* H,
-                               hipStream_t stream) {
-  const GemmArgs a = gateup_args(x, x_rows, sorted_src, K, tiles, n_tiles, rows_dense, w_gate,
-                                 w_up, d, h, H);
+                               hipStream_t stream, bool kblock_major) {
+  GemmArgs a = gateup_args(x, x_rows, sorted_src, K, tiles, n_tiles, rows_dense, w_gate, w_up, d,
+                           h, H);
+  if (kblock_major) b_kblock_major(a);
   if (!tiles) return hipErrorInvalidValue;
   return launch_skinny_mode<kGateUp, false>(a, max_tiles, stream);
 }

@@ -286,3 +286,20 @@ def test_fp8_entry_points_reject_bad_arguments(lib):
     assert lib.moe_fp8_quantize_blocks(p16, 1, 0, 128, p16, p16, None) == 2
     assert lib.moe_fp8_quantize_blocks(p16, 1, 128, 128, p16, None, None) == 1
     assert lib.moe_fp8_quantize_blocks(None, 0, 128, 128, None, None, None) == 0
+
+
+def test_pack_gateup_arguments_and_flag(lib):
+    buf = C.create_string_buffer(8192)
+    p16 = (C.cast(buf, C.c_void_p).value + 15) // 16 * 16
+    f = lib.moe_pack_gateup_weights
+    assert f(p16, -1, 32, 64, p16 + 4096, None) == 2    # count below 0
+    assert f(p16, 1, 32, 100, p16 + 4096, None) == 2    # cols not a multiple of 64
+    assert f(p16, 1, 0, 64, p16 + 4096, None) == 2      # no rows
+    assert f(None, 1, 8, 64, p16 + 4096, None) == 1     # NULL input
+    assert f(p16 + 8, 1, 8, 64, p16 + 4096, None) == 1  # misaligned input
+    assert f(p16, 1, 8, 64, p16 + 512, None) == 1       # output overlaps the 1 KiB input
+    assert f(None, 0, 8, 64, None, None) == 0            # empty: nothing to enqueue
+    # MOE_PACKED_GATEUP: accepted with bf16 experts, rejected with E4M3 ones
+    assert lib.moe_forward_workspace_bytes(C.byref(_problem(flags=4))) > 0
+    assert lib.moe_forward_fp8_workspace_bytes(C.byref(_problem())) > 0
+    assert lib.moe_forward_fp8_workspace_bytes(C.byref(_problem(flags=4))) == 0
