@@ -508,7 +508,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the skewed and decode workloads measured after the headline")
     ap.add_argument("--row-major", action="store_true",
-                    help="bf16 routed gate/up weights in the row-major layout instead of the "
+                    help="routed gate/up weights in the row-major layout instead of the "
                          "packed one (moe_pack_gateup_weights)")
     ap.add_argument("--fp8", action="store_true",
                     help="E4M3 experts (moe_forward_fp8) quantised from the same bf16 weights")
@@ -571,7 +571,7 @@ def main():
         W = M.quantize_experts(W)
         torch.cuda.synchronize()
         fwd, ws_fn = M.forward_fp8, M.forward_fp8_workspace_bytes
-    elif not args.row_major:
+    if not args.row_major:
         # the routed gate/up weights in the library's packed layout, as a
         # deployment stores them (untimed; the results are bit-identical)
         W = M.pack_gateup(W)
@@ -683,9 +683,9 @@ def main():
         "data": "synthetic (seeded normal inputs and random-init weights of the layer shape)",
         "config": {**cfg.describe(), "parallelism": "none (1 GPU)",
                    **({"experts": "e4m3, 128x128 block scales, 1x128 activation groups"}
-                      if args.fp8 else
-                      {"gate_up_weights": "row-major" if args.row_major else
-                       "packed k-block-major (moe_pack_gateup_weights, untimed)"})},
+                      if args.fp8 else {}),
+                   "gate_up_weights": "row-major" if args.row_major else
+                   "packed k-block-major (moe_pack_gateup_weights, untimed)"},
         "layer_tflops": layer_flops / (ms_step * 1e-3) / 1e12,
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "loads": {"max_over_mean_before": float(counts_before.max() / counts_before.mean()),

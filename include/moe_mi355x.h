@@ -56,7 +56,7 @@ typedef enum {
 /* Flags of moe_problem_t.flags */
 #define MOE_RECOMPUTE_BIAS 0x1u  /* route with beta_in, one exact quantile update, re-route */
 #define MOE_KEY32 0x2u           /* quantile over fp32 keys instead of bf16 keys */
-#define MOE_PACKED_GATEUP 0x4u   /* w_gate, w_up packed by moe_pack_gateup_weights (bf16 only) */
+#define MOE_PACKED_GATEUP 0x4u   /* w_gate, w_up packed by moe_pack_gateup_weights */
 
 /*
  * moe_route - bias-corrected top-K selection and sigmoid mixture weights over
@@ -290,22 +290,25 @@ moe_status_t moe_forward(const moe_problem_t* p, const moe_weights_t* w,
                          void* stream);
 
 /*
- * Packed gate/up weights, for moe_forward and moe_forward_noalloc with
- * MOE_PACKED_GATEUP.  The routed experts' gate and up products of the
- * SwiGLU in [K1D] (Routing section) read their weights 64 columns (128
- * bytes) of every row at a time; this layout keeps the pieces read together
+ * Packed gate/up weights, for moe_forward, moe_forward_noalloc and
+ * moe_forward_fp8 with MOE_PACKED_GATEUP.  The routed experts' gate and up
+ * products of the SwiGLU in [K1D] (Routing section) read their weights 128
+ * bytes of every row at a time; this layout keeps the pieces read together
  * next to each other.  It changes no value and no order of arithmetic: the
  * layer's output with packed weights is bit-identical to the row-major one.
  *
- * moe_pack_gateup_weights - `count` bf16 matrices w [count,rows,cols]
- *   (row-major; the layer's w_gate or w_up, [E,h,d]) -> out
- *   [count, cols/64, rows, 64], i.e. out[c][k][r][j] = w[c][r][64k + j].
- *   cols % 64 == 0 (64 <= cols <= 65536), 1 <= rows <= 65536,
- *   0 <= count <= 65535; w and out are caller-owned device memory, 16-byte
- *   aligned, not overlapping.  Enqueues one kernel on `stream`; out is fully
- *   overwritten.  With MOE_PACKED_GATEUP set, moe_forward reads w_gate and
- *   w_up in this layout (the shared expert and w_down stay row-major);
- *   moe_forward_fp8 rejects the flag.
+ * moe_pack_gateup_weights - `count` matrices of 16-bit words w
+ *   [count,rows,cols] (row-major) -> out [count, cols/64, rows, 64], i.e.
+ *   out[c][k][r][j] = w[c][r][64k + j].  For bf16 experts w is the layer's
+ *   w_gate or w_up [E,h,d]; for E4M3 experts it is their codes [E,h,d]
+ *   viewed as [E,h,d/2] words, so that each row's 128-code k-blocks stay
+ *   whole: out is then the codes [E, d/128, h, 128] (the block scales are
+ *   not packed).  cols % 64 == 0 (64 <= cols <= 65536),
+ *   1 <= rows <= 65536, 0 <= count <= 65535; w and out are caller-owned
+ *   device memory, 16-byte aligned, not overlapping.  Enqueues one kernel
+ *   on `stream`; out is fully overwritten.  With MOE_PACKED_GATEUP set, the
+ *   forward calls read w_gate and w_up in this layout (the shared expert
+ *   and w_down stay row-major).
  * Errors: INVALID_ARGUMENT (NULL, misaligned or overlapping buffers),
  *   UNSUPPORTED_SHAPE, HIP.
  */

@@ -284,12 +284,22 @@ def pack_gateup_weights(w, stream=None):
     return out
 
 
-def pack_gateup(weights: ExpertWeights, stream=None) -> ExpertWeights:
-    """The same layer with its routed gate and up weights packed for the
-    tile engine (MOE_PACKED_GATEUP); forward() gives bit-identical results
-    with either form."""
+def pack_gateup(weights, stream=None):
+    """The same layer (ExpertWeights or Fp8ExpertWeights) with its routed
+    gate and up weights packed k-block-major (MOE_PACKED_GATEUP); forward()
+    and forward_fp8() give bit-identical results with either form.  E4M3
+    codes are packed as 16-bit words, so each row's 128-code k-blocks stay
+    whole: [E, h, d] -> [E, d/128, h, 128]."""
     if weights.packed:
         return weights
+    if isinstance(weights, Fp8ExpertWeights):
+        torch = _torch()
+
+        def pack_codes(c):
+            c = _dev(c, "codes", torch.uint8)
+            return pack_gateup_weights(c.view(torch.bfloat16), stream).view(torch.uint8)
+        return replace(weights, w_gate=pack_codes(weights.w_gate),
+                       w_up=pack_codes(weights.w_up), packed=True)
     return replace(weights, w_gate=pack_gateup_weights(weights.w_gate, stream),
                    w_up=pack_gateup_weights(weights.w_up, stream), packed=True)
 
@@ -345,6 +355,7 @@ class Fp8ExpertWeights:
     ss_up: object = None
     ws_down: object = None             # [S, d, hs]
     ss_down: object = None
+    packed: bool = False               # w_gate, w_up as [E, d/128, h, 128] (pack_gateup)
 
 
 def quantize_experts(weights: ExpertWeights, stream=None) -> Fp8ExpertWeights:
@@ -481,8 +492,14 @@ def forward_fp8(x, weights: Fp8ExpertWeights, K: int, beta_in=None,
     N, d = x.shape
     u8, f32 = torch.uint8, torch.float32
     wg = _dev(weights.w_gate, "w_gate", u8)
-    E, h, _ = wg.shape
-    _dev(weights.w_up, "w_up", u8, (E, h, d))
+    if weights.packed:
+        if wg.dim() != 4 or wg.shape[1] * 128 != d or wg.shape[3] != 128:
+            raise ValueError("packed w_gate codes must be [E, d/128, h, 128]")
+        E, _, h, _ = wg.shape
+        _dev(weights.w_up, "w_up", u8, (E, d // 128, h, 128))
+    else:
+        E, h, _ = wg.shape
+        _dev(weights.w_up, "w_up", u8, (E, h, d))
     _dev(weights.w_down, "w_down", u8, (E, d, h))
     for name, shp in (("s_gate", (E, h // 128, d // 128)), ("s_up", (E, h // 128, d // 128)),
                       ("s_down", (E, d // 128, h // 128))):
@@ -501,7 +518,8 @@ def forward_fp8(x, weights: Fp8ExpertWeights, K: int, beta_in=None,
             _dev(getattr(weights, name), name, f32, shp)
     w = MoeFp8Weights(*[_ptr(getattr(weights, f)) for f, _ in MoeFp8Weights._fields_])
     return _run_forward(True, x, w, N, d, E, K, h, n_shared, hs, beta_in, recompute_bias,
-                        key_bits, logit_offset, logits_in, aux, workspace, out, stream)
+                        key_bits, logit_offset, logits_in, aux, workspace, out, stream,
+                        MOE_PACKED_GATEUP if weights.packed else 0)
 
 
 def stage_timing(enable=True):

@@ -713,7 +713,7 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
     }
     if (i < 4) {
       const int brow = (MODE == kGateUp) ? nt * (BN / 2) + (r & (BN / 2 - 1)) : nt * BN + r;
-      b_voff[i] = (brow < a.b_rows) ? (uint32_t)brow * (uint32_t)a.kdim + (uint32_t)chunk * 16u
+      b_voff[i] = (brow < a.b_rows) ? (uint32_t)brow * a.b_row_pitch + (uint32_t)chunk * 16u
                                     : kNoRow;
     }
   }
@@ -755,7 +755,7 @@ __device__ __forceinline__ void gemm_tile_fp8(const GemmArgs& a, int64_t mt, int
           (lds_void_t*)(lds_raw + (ks % A_SLOTS) * A_TILE8 + (8 * i + wave) * 1024));
   };
   auto dma_b = [&](int ks, int i) {  // quarter i: B rows 64*i .. +63
-    dma16<BNT ? kCpolNT : 0>((MODE == kGateUp && i >= 2) ? rb1 : rb0, b_voff[i], (uint32_t)ks * 128u,
+    dma16<BNT ? kCpolNT : 0>((MODE == kGateUp && i >= 2) ? rb1 : rb0, b_voff[i], (uint32_t)ks * a.b_kblk_pitch,
           (lds_void_t*)(lds_raw + B_BASE8 + bq(ks, i) * QUARTER + wave * 1024));
   };
 
@@ -1238,9 +1238,10 @@ hipError_t launch_gateup_fp8(const uint8_t* xq, const float* xs, int64_t x_rows,
                              const int32_t* n_tiles, int64_t max_tiles, int64_t rows_dense,
                              const uint8_t* wg, const float* sg, const uint8_t* wu,
                              const float* su, int d, int h, uint8_t* Hq, float* Hs,
-                             hipStream_t stream) {
-  const GemmArgs a = gateup_fp8_args(xq, xs, x_rows, sorted_src, K, tiles, n_tiles, rows_dense,
-                                     wg, sg, wu, su, d, h, Hq, Hs);
+                             hipStream_t stream, bool kblock_major) {
+  GemmArgs a = gateup_fp8_args(xq, xs, x_rows, sorted_src, K, tiles, n_tiles, rows_dense, wg, sg,
+                               wu, su, d, h, Hq, Hs);
+  if (kblock_major) b_kblock_major(a);
   return launch_fp8(kGateUp, a, tiles ? max_tiles : (rows_dense + BM - 1) / BM, stream);
 }
 

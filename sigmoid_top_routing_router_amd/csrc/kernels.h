@@ -148,13 +148,15 @@ hipError_t launch_quant_blocks(const uint16_t* W, int64_t count, int R, int C, u
 // E4M3 GEMMs (d % 128 == 0, h % 128 == 0).  Weight scales are
 // [E][rows/128][cols/128]; activation scales [rows][cols/128].  The gate/up
 // GEMMs leave H as E4M3 codes [rows][h] with scales [rows][h/128] (quantised
-// in the epilogue from the bf16-rounded SiLU(g) * u).
+// in the epilogue from the fp32 SiLU(g) * u).  kblock_major: the gate and up
+// codes are [E][d/128][h][128] (moe_pack_gateup_weights on the codes viewed
+// as 16-bit words) instead of [E][h][d].
 hipError_t launch_gateup_fp8(const uint8_t* xq, const float* xs, int64_t x_rows,
                              const int32_t* sorted_src, int K, const int32_t* tiles,
                              const int32_t* n_tiles, int64_t max_tiles, int64_t rows_dense,
                              const uint8_t* wg, const float* sg, const uint8_t* wu,
                              const float* su, int d, int h, uint8_t* Hq, float* Hs,
-                             hipStream_t stream);
+                             hipStream_t stream, bool kblock_major = false);
 hipError_t launch_down_fp8(const uint8_t* Hq, const float* Hs, int64_t h_rows,
                            const int32_t* tiles, const int32_t* n_tiles, int64_t max_tiles,
                            int64_t rows_dense, const uint8_t* wd, const float* sd, int d, int h,
@@ -187,7 +189,7 @@ hipError_t launch_gateup_fp8_small(const uint8_t* xq, const float* xs, int64_t x
                                    const int32_t* n_tiles, int64_t max_tiles, int64_t rows_dense,
                                    const uint8_t* wg, const float* sg, const uint8_t* wu,
                                    const float* su, int d, int h, uint8_t* Hq, float* Hs,
-                                   hipStream_t stream);
+                                   hipStream_t stream, bool kblock_major = false);
 hipError_t launch_down_fp8_small(const uint8_t* Hq, const float* Hs, int64_t h_rows,
                                  const int32_t* tiles, const int32_t* n_tiles, int64_t max_tiles,
                                  int64_t rows_dense, const uint8_t* wd, const float* sd, int d,

@@ -199,8 +199,6 @@ moe_status_t check_problem_fp8(const moe_problem_t* p) {
     return fail(MOE_ERR_UNSUPPORTED_SHAPE,
                 "FP8 experts need d, h and h_shared to be multiples of 128 (d=%d h=%d hs=%d)",
                 p->d, p->h, p->h_shared);
-  if (p->flags & MOE_PACKED_GATEUP)
-    return fail(MOE_ERR_INVALID_ARGUMENT, "MOE_PACKED_GATEUP applies to bf16 experts only");
   return MOE_OK;
 }
 
@@ -506,13 +504,14 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
   auto gateup8 = small ? moe::launch_gateup_fp8_small : moe::launch_gateup_fp8;
   auto down = small ? moe::launch_down_small : moe::launch_down;
   auto down8 = small ? moe::launch_down_fp8_small : moe::launch_down_fp8;
+  const bool packed = (p->flags & MOE_PACKED_GATEUP) != 0;
   if (ex.fp8)
     MOE_TRY_HIP(gateup8(l.xq, l.xs, N, pw.sorted_src, K, pw.tiles, pw.n_tiles, l.max_tiles, 0,
-                        q->w_gate, q->s_gate, q->w_up, q->s_up, d, h, l.Hq, l.Hqs, st),
+                        q->w_gate, q->s_gate, q->w_up, q->s_up, d, h, l.Hq, l.Hqs, st, packed),
                 "moe_forward: gate/up");
   else
     MOE_TRY_HIP(gateup(x, N, pw.sorted_src, K, pw.tiles, pw.n_tiles, l.max_tiles, 0, w->w_gate,
-                       w->w_up, d, h, l.H, st, (p->flags & MOE_PACKED_GATEUP) != 0),
+                       w->w_up, d, h, l.H, st, packed),
                 "moe_forward: gate/up");
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
   if (ex.fp8)

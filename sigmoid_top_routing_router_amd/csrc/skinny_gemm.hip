@@ -373,9 +373,10 @@ hipError_t launch_gateup_fp8_small(const uint8_t* xq, const float* xs, int64_t x
                                    const int32_t* n_tiles, int64_t max_tiles, int64_t rows_dense,
                                    const uint8_t* wg, const float* sg, const uint8_t* wu,
                                    const float* su, int d, int h, uint8_t* Hq, float* Hs,
-                                   hipStream_t stream) {
-  const GemmArgs a = gateup_fp8_args(xq, xs, x_rows, sorted_src, K, tiles, n_tiles, rows_dense,
-                                     wg, sg, wu, su, d, h, Hq, Hs);
+                                   hipStream_t stream, bool kblock_major) {
+  GemmArgs a = gateup_fp8_args(xq, xs, x_rows, sorted_src, K, tiles, n_tiles, rows_dense, wg, sg,
+                               wu, su, d, h, Hq, Hs);
+  if (kblock_major) b_kblock_major(a);
   if (!tiles) return hipErrorInvalidValue;
   return launch_skinny_mode<kGateUp, true>(a, max_tiles, stream);
 }

@@ -299,7 +299,6 @@ def test_pack_gateup_arguments_and_flag(lib):
     assert f(p16 + 8, 1, 8, 64, p16 + 4096, None) == 1  # misaligned input
     assert f(p16, 1, 8, 64, p16 + 512, None) == 1       # output overlaps the 1 KiB input
     assert f(None, 0, 8, 64, None, None) == 0            # empty: nothing to enqueue
-    # MOE_PACKED_GATEUP: accepted with bf16 experts, rejected with E4M3 ones
+    # MOE_PACKED_GATEUP: accepted with bf16 and with E4M3 experts
     assert lib.moe_forward_workspace_bytes(C.byref(_problem(flags=4))) > 0
-    assert lib.moe_forward_fp8_workspace_bytes(C.byref(_problem())) > 0
-    assert lib.moe_forward_fp8_workspace_bytes(C.byref(_problem(flags=4))) == 0
+    assert lib.moe_forward_fp8_workspace_bytes(C.byref(_problem(flags=5))) > 0

@@ -4,7 +4,8 @@ The packed layout moves values, not arithmetic: the pack must equal the
 reshape it documents, and the layer with packed weights must give exactly
 the bits of the layer with row-major weights, on the tile engine (with
 288-row tiles), on the weight-streaming kernels of small batches, through
-the no-allocation entry point, and at the full prefill and skewed sizes.
+the no-allocation entry point, at the full prefill and skewed sizes, and
+with E4M3 experts (codes packed as 16-bit words).
 No oracle is needed for that: both sides are the same library on the same
 inputs (the row-major layer itself is held to the oracle elsewhere)."""
 from dataclasses import replace
@@ -100,8 +101,37 @@ def test_forward_packed_full_size(M, name):
     _same(a, b)
 
 
-def test_fp8_paths_refuse_packed_weights(M):
+def test_quantize_experts_refuses_packed_weights(M):
     L = make_inputs(CONFIGS["toy"])
     P = replace(weights_dev(L), packed=True)
     with pytest.raises(ValueError):
         M.quantize_experts(P)
+
+
+def _both_fp8(M, cfg):
+    import torch
+    L = make_inputs(cfg)
+    Q = M.quantize_experts(weights_dev(L))
+    P = M.pack_gateup(Q)
+    assert P.packed and P.w_gate.shape == (cfg.E, cfg.d // 128, cfg.h, 128)
+    x = bf16_dev(L.x)
+    beta = dev(L.beta_in)
+    off = None if L.logit_offset is None else dev(L.logit_offset)
+    out = []
+    for weights in (Q, P):
+        y, A = M.forward_fp8(x, weights, cfg.K, beta_in=beta, recompute_bias=cfg.recompute_bias,
+                             logit_offset=off, aux=("topk_ids", "counts"))
+        torch.cuda.synchronize()
+        out.append((y.view(torch.int16).cpu().numpy(), A["topk_ids"].cpu().numpy(),
+                    A["counts"].cpu().numpy()))
+    return out
+
+
+@pytest.mark.parametrize("name,N", [("prefill", 300), ("prefill", 17), ("prefill", None)])
+def test_forward_fp8_packed_is_bit_identical(M, name, N):
+    """E4M3 codes packed as 16-bit words (128-code k-blocks): the tile
+    engine, the weight-streaming kernel (17 tokens) and the full prefill."""
+    cfg = CONFIGS[name] if N is None else scaled(CONFIGS[name], N)
+    say("fp8 packed vs row-major", cfg.name, cfg.N)
+    a, b = _both_fp8(M, cfg)
+    _same(a, b)
