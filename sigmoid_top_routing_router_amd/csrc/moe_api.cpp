@@ -110,7 +110,8 @@ struct FwdLayout {
   float* Hqs;
   uint8_t* Hsq;
   float* Hss;
-  float* part;  // split-K partial sums of the dense products of a small batch
+  float* part;       // split-K partial sums of the dense products of a small batch
+  float* part_side;  // the same for the shared expert on the side stream
   size_t bytes;
   int64_t max_tiles;
 };
@@ -155,8 +156,11 @@ FwdLayout carve_forward(void* ws, const moe_problem_t& p, bool fp8 = false) {
     }
     l.sh = c.take<uint16_t>((size_t)N * p.d);
   }
-  if (N <= moe::kSmallBatch)
+  if (N <= moe::kSmallBatch) {
     l.part = c.take<float>(moe::dense_small_part_floats(N, p.d, p.E, p.n_shared ? p.h_shared : 0));
+    if (p.n_shared > 0)
+      l.part_side = c.take<float>(moe::dense_small_part_floats(N, p.d, 0, p.h_shared));
+  }
   l.bytes = c.off;
   return l;
 }
@@ -370,7 +374,7 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
   if (ex.fp8)
     MOE_TRY_HIP(moe::launch_quant_rows(x, N, d, l.xq, l.xs, st), "moe_forward: quantise x");
   SideJoin sj;
-  SideStream* side = (!small && shared && !ex.in_order) ? side_stream() : nullptr;
+  SideStream* side = (shared && !ex.in_order) ? side_stream() : nullptr;
   // the side stream starts from the caller's stream as it stands before the
   // router GEMM (the fork), but its work is enqueued after that GEMM, whose
   // blocks are then dispatched first
@@ -390,12 +394,12 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
                   "moe_forward: router GEMM");
       Z = zout;
     }
-    if (shared && ex.fp8)
+    if (shared_here && ex.fp8)
       MOE_TRY_HIP(moe::launch_shared_gateup_dense_small(l.xq, l.xs, N, d, q->ws_gate, q->ss_gate,
                                                         q->ws_up, q->ss_up, hs, true, l.Hsq,
                                                         l.Hss, l.part, st),
                   "moe_forward: shared gate/up");
-    else if (shared)
+    else if (shared_here)
       MOE_TRY_HIP(moe::launch_shared_gateup_dense_small(x, nullptr, N, d, w->ws_gate, nullptr,
                                                         w->ws_up, nullptr, hs, false, l.Hs,
                                                         nullptr, l.part, st),
@@ -438,7 +442,24 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
     MOE_TRY_HIP(hipStreamWaitEvent(s2, side->fork, 0), "moe_forward: fork");
     sj.st = st;
     sj.side = side;
-    if (ex.fp8) {
+    if (small) {
+      // the split-K kernels of a small batch, with partial sums of their own
+      if (ex.fp8)
+        MOE_TRY_HIP(moe::launch_shared_gateup_dense_small(l.xq, l.xs, N, d, q->ws_gate,
+                                                          q->ss_gate, q->ws_up, q->ss_up, hs,
+                                                          true, l.Hsq, l.Hss, l.part_side, s2),
+                    "moe_forward: shared gate/up");
+      else
+        MOE_TRY_HIP(moe::launch_shared_gateup_dense_small(x, nullptr, N, d, w->ws_gate, nullptr,
+                                                          w->ws_up, nullptr, hs, false, l.Hs,
+                                                          nullptr, l.part_side, s2),
+                    "moe_forward: shared gate/up");
+      MOE_TRY_HIP(moe::launch_shared_down_dense_small(
+                      ex.fp8 ? (const void*)l.Hsq : (const void*)l.Hs, ex.fp8 ? l.Hss : nullptr,
+                      N, d, ex.fp8 ? (const void*)q->ws_down : (const void*)w->ws_down,
+                      ex.fp8 ? q->ss_down : nullptr, hs, ex.fp8, l.sh, l.part_side, s2),
+                  "moe_forward: shared down");
+    } else if (ex.fp8) {
       MOE_TRY_HIP(moe::launch_gateup_fp8(l.xq, l.xs, N, nullptr, 1, nullptr, nullptr, 0, N,
                                          q->ws_gate, q->ss_gate, q->ws_up, q->ss_up, d, hs,
                                          l.Hsq, l.Hss, s2),
@@ -522,7 +543,7 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
                 "moe_forward: down");
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
   // the shared expert's down projection
-  if (shared && small)
+  if (shared_here && small)
     MOE_TRY_HIP(moe::launch_shared_down_dense_small(
                     ex.fp8 ? (const void*)l.Hsq : (const void*)l.Hs, ex.fp8 ? l.Hss : nullptr, N,
                     d, ex.fp8 ? (const void*)q->ws_down : (const void*)w->ws_down,
