@@ -662,8 +662,10 @@ def main():
         roof = {"bound": "mfma", "achieved": flops / t_gu / 1e12, "peak": peak_mfma,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    # the traffic records are taken with the default (packed) layout
-    roof["traffic"] = None if args.row_major else traffic_for(args.workload, cfg.N, args.fp8)
+    # the traffic records are taken with the default (packed) layout and the
+    # quantile update inside the step (other loads move other bytes)
+    roof["traffic"] = None if (args.row_major or args.inference) else \
+        traffic_for(args.workload, cfg.N, args.fp8)
     kname, _ = roofline_kernel(cfg.N, args.fp8)
     roof["kernel"] = kname + (" (routed gate/up GEMM, weight-streaming)" if cfg.N <= 64 else
                               " (routed gate/up GEMM, E4M3)" if args.fp8 else
