@@ -52,7 +52,7 @@ hipError_t launch_eqb_scan(const EqbWork& w, int E, int K, int key_bits, int pas
 // Stable counting sort of the (t,k) pairs by expert, plus the m-tile table of
 // the grouped GEMMs (tiles of `bm` rows per expert).
 struct PermWork {
-  uint32_t* chunk_counts;  // [n_chunks][E]
+  uint32_t* block_counts;  // [perm_count_rows(pairs)][E]
   int32_t* counts;         // [E]
   int32_t* offsets;        // [E+1]
   int32_t* sorted_src;     // [N*K]
@@ -60,8 +60,7 @@ struct PermWork {
   int32_t* tiles;          // [max_tiles][4]: expert, first row, rows, pad
   int32_t* n_tiles;        // [1]
 };
-int perm_chunk_pairs();
-int64_t perm_num_chunks(int64_t pairs);
+int64_t perm_count_rows(int64_t pairs);
 int64_t perm_max_tiles(int64_t pairs, int E, int bm);
 // Tiles hold bm rows; the last tile of a segment up to bm + xr rows.
 hipError_t launch_permute(const int32_t* ids, int64_t N, int E, int K, int bm, int xr,

@@ -92,7 +92,7 @@ struct FwdLayout {
   float* beta_new;
   int32_t* counts_before;
   EqbLayout eqb;
-  uint32_t* chunk_counts;
+  uint32_t* block_counts;
   int32_t* counts;
   int32_t* offsets;
   int32_t* sorted_src;
@@ -130,7 +130,7 @@ FwdLayout carve_forward(void* ws, const moe_problem_t& p, bool fp8 = false) {
   l.beta_new = c.take<float>((size_t)p.E);
   l.counts_before = c.take<int32_t>((size_t)p.E);
   l.eqb = carve_eqb(c, N, p.E, key_bits);
-  l.chunk_counts = c.take<uint32_t>((size_t)moe::perm_num_chunks(pairs) * p.E);
+  l.block_counts = c.take<uint32_t>((size_t)moe::perm_count_rows(pairs) * p.E);
   l.counts = c.take<int32_t>((size_t)p.E);
   l.offsets = c.take<int32_t>((size_t)p.E + 1);
   l.sorted_src = c.take<int32_t>((size_t)pairs);
@@ -509,7 +509,7 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
 
   // stable grouping by expert and the m-tile table
   moe::PermWork pw;
-  pw.chunk_counts = l.chunk_counts;
+  pw.block_counts = l.block_counts;
   pw.counts = A.counts ? A.counts : l.counts;
   pw.offsets = A.offsets ? A.offsets : l.offsets;
   pw.sorted_src = A.sorted_src ? A.sorted_src : l.sorted_src;

@@ -9,32 +9,50 @@
 // is also the order of t).
 //
 // Kernels (all integer work, bit-exact and deterministic); batches of at most
-// 16384 pairs use perm_small_kernel, one block doing all four steps:
-//  1. perm_count_kernel: one wave per chunk of kChunk consecutive pairs
-//     counts the experts of its chunk in LDS -> chunk_counts[e][chunk].
-//  2. perm_scan_kernel: one block per expert turns its row of chunk counts
-//     into exclusive chunk bases and the expert total.
-//  3. perm_tiles_kernel: one block; exclusive sums of the counts (offsets)
-//     by a block-wide scan, and the table of m-tiles (expert, first row, rows)
-//     that drives the grouped GEMMs from device memory.  A segment is cut
-//     into tiles of bm rows, except that its last tile takes up to bm + xr
-//     rows: a remainder of at most xr rows rides with the tile before it
-//     instead of streaming the expert's weights once more.
-//  4. perm_scatter_kernel: one wave per chunk walks its pairs in order, 64 at
-//     a time; lanes holding the same expert are found with nine ballots over
-//     the bits of the expert id, so the rank among them is a popcount and the
-//     lowest such lane advances the expert's running position in LDS.
+// 16384 pairs use perm_small_kernel, one block doing all four steps.  Larger
+// batches take two launches.  The pairs are cut into blocks of four chunks,
+// one chunk of cw consecutive pairs per wave (cw grows with the batch so that
+// there are at most kPermMaxBlocks blocks):
+//  1. perm_count_kernel: block b counts the experts of its pairs in LDS ->
+//     block_counts[b][e].
+//  2. perm_scatter_kernel: every block reads the whole count table (at most
+//     kPermMaxBlocks x E words), which gives it each expert's total and the
+//     pairs of that expert in the blocks before it; a block-wide scan in
+//     expert order turns the totals into the segment offsets, and block 0
+//     writes counts, offsets and the table of m-tiles (expert, first row,
+//     rows) that drives the grouped GEMMs from device memory.  A segment is
+//     cut into tiles of bm rows, except that its last tile takes up to
+//     bm + xr rows: a remainder of at most xr rows rides with the tile before
+//     it instead of streaming the expert's weights once more.  Each wave then
+//     counts its own chunk again, which places the four chunks inside the
+//     block, and walks its pairs in order, 64 at a time; lanes holding the
+//     same expert are found with nine ballots over the bits of the expert
+//     id, so the rank among them is a popcount and the lowest such lane
+//     advances the expert's running position in LDS.
+// The scan and the tile table ride in the scatter launch instead of two
+// launches of their own: each launch in this dependent chain waits for free
+// CUs while the shared expert's GEMM blocks hold them.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-constexpr int kChunk = 512;         // pairs per chunk (one wave)
-constexpr int kPermWaves = 4;       // waves per block in the chunk kernels
+constexpr int kChunkMin = 512;      // pairs per chunk (one wave), at least
+constexpr int kPermWaves = 4;       // waves (chunks) per block
+constexpr int kPermMaxBlocks = 64;  // blocks of the two chunk kernels, at most
 constexpr int kMaxE = 384;
 
-int perm_chunk_pairs() { return kChunk; }
-int64_t perm_num_chunks(int64_t pairs) { return (pairs + kChunk - 1) / kChunk; }
+// Pairs per chunk: 512, or more so that the batch needs at most
+// kPermMaxBlocks blocks; a multiple of 64.
+static int64_t perm_chunk(int64_t pairs) {
+  const int64_t per = (pairs + kPermWaves * kPermMaxBlocks - 1) / (kPermWaves * kPermMaxBlocks);
+  const int64_t cw = (per + 63) / 64 * 64;
+  return cw < kChunkMin ? kChunkMin : cw;
+}
+int64_t perm_count_rows(int64_t pairs) {
+  const int64_t bp = perm_chunk(pairs) * kPermWaves;
+  return (pairs + bp - 1) / bp;
+}
 int64_t perm_max_tiles(int64_t pairs, int E, int bm) { return pairs / bm + E; }
 
 // Number of m-tiles of a segment of c rows: bm rows each, the last one up to
@@ -60,113 +78,117 @@ __device__ __forceinline__ void emit_tiles(int32_t* tiles, uint32_t t0, int e, u
 }
 
 __global__ __launch_bounds__(256) void perm_count_kernel(
-    const int32_t* __restrict__ ids, int64_t pairs, int E, int64_t n_chunks,
-    uint32_t* __restrict__ chunk_counts) {
-  __shared__ uint32_t cnt[kPermWaves][kMaxE];
-  const int w = threadIdx.x >> 6, lane = lane_id();
-  const int64_t chunk = (int64_t)blockIdx.x * kPermWaves + w;
-  for (int e = lane; e < E; e += kWave) cnt[w][e] = 0u;
+    const int32_t* __restrict__ ids, int64_t pairs, int E, int64_t cw,
+    uint32_t* __restrict__ block_counts) {
+  __shared__ uint32_t cnt[kMaxE];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0u;
   __syncthreads();
-  if (chunk < n_chunks) {
-    const int64_t i0 = chunk * kChunk;
-    for (int j = lane; j < kChunk; j += kWave) {
-      const int64_t i = i0 + j;
-      if (i < pairs) atomicAdd(&cnt[w][ids[i]], 1u);
-    }
-  }
+  const int64_t i0 = (int64_t)blockIdx.x * kPermWaves * cw;
+  const int64_t i1 = min(pairs, i0 + kPermWaves * cw);
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += blockDim.x) atomicAdd(&cnt[ids[i]], 1u);
   __syncthreads();
-  if (chunk < n_chunks)
-    for (int e = lane; e < E; e += kWave) chunk_counts[(size_t)e * n_chunks + chunk] = cnt[w][e];
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    block_counts[(size_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// One block (256 threads) per expert: exclusive scan over the chunks.
-__global__ __launch_bounds__(256) void perm_scan_kernel(uint32_t* __restrict__ chunk_counts,
-                                                        int64_t n_chunks,
-                                                        int32_t* __restrict__ counts) {
-  __shared__ uint32_t wsum[4];
-  const int e = blockIdx.x;
-  const int w = threadIdx.x >> 6, lane = lane_id();
-  uint32_t* row = chunk_counts + (size_t)e * n_chunks;
-  uint32_t carry = 0u;
-  for (int64_t c0 = 0; c0 < n_chunks; c0 += 256) {
-    const int64_t c = c0 + threadIdx.x;
-    const uint32_t v = (c < n_chunks) ? row[c] : 0u;
-    const uint32_t incl = wave_inclusive_sum_u32(v);
-    if (lane == kWave - 1) wsum[w] = incl;
-    __syncthreads();
-    uint32_t before = carry;
-    for (int i = 0; i < w; ++i) before += wsum[i];
-    if (c < n_chunks) row[c] = before + incl - v;
-    const uint32_t block_total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
-    carry += block_total;
-  }
-  if (threadIdx.x == 0) counts[e] = (int32_t)carry;
-}
-
-// One block of 256 threads: offsets (exclusive sums of counts) and the m-tile
-// table.  Thread i owns experts 2i and 2i+1 (E <= 512); a block-wide scan in
-// thread order gives the sums in expert order.
-__global__ __launch_bounds__(256) void perm_tiles_kernel(const int32_t* __restrict__ counts,
-                                                         int E, int bm, int xr,
-                                                         int32_t* __restrict__ offsets,
-                                                         int32_t* __restrict__ tiles,
-                                                         int32_t* __restrict__ n_tiles) {
+__global__ __launch_bounds__(256) void perm_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t pairs, int E, int64_t cw, int64_t n_blocks,
+    const uint32_t* __restrict__ block_counts, int bm, int xr, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
+    int32_t* __restrict__ sorted_src, int32_t* __restrict__ src_pos) {
+  __shared__ uint32_t pos[kPermWaves][kMaxE];  // chunk counts, then chunk bases
+  __shared__ uint32_t base_s[kMaxE];           // segment start + pairs of earlier blocks
   __shared__ uint32_t wsum_c[4], wsum_t[4];
   const int tid = threadIdx.x, w = tid >> 6, lane = lane_id();
+  const int64_t b = blockIdx.x;
+  const int64_t i0 = (b * kPermWaves + w) * cw;
+  const int64_t i1 = min(pairs, i0 + cw);
+  for (int e = lane; e < E; e += kWave) pos[w][e] = 0u;
+  __builtin_amdgcn_wave_barrier();
+  for (int64_t i = i0 + lane; i < i1; i += kWave) atomicAdd(&pos[w][ids[i]], 1u);
+
+  // Totals and earlier-block sums of experts 2 tid and 2 tid + 1 (E <= 512),
+  // so that the block-wide scan below runs in expert order.
   const int e0 = 2 * tid, e1 = 2 * tid + 1;
-  const uint32_t c0 = e0 < E ? (uint32_t)counts[e0] : 0u;
-  const uint32_t c1 = e1 < E ? (uint32_t)counts[e1] : 0u;
-  const uint32_t t0 = seg_tiles(c0, bm, xr), t1 = seg_tiles(c1, bm, xr);
-  const uint32_t ic = wave_inclusive_sum_u32(c0 + c1);
+  uint32_t tot0 = 0u, tot1 = 0u, pre0 = 0u, pre1 = 0u;
+  if (e0 < E) {
+    const bool two = e1 < E;
+    int64_t r = 0;
+    for (; r + 8 <= n_blocks; r += 8) {
+      uint32_t v0[8], v1[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t* row = block_counts + (size_t)(r + j) * E;
+        v0[j] = row[e0];
+        v1[j] = two ? row[e1] : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        tot0 += v0[j];
+        tot1 += v1[j];
+        if (r + j < b) { pre0 += v0[j]; pre1 += v1[j]; }
+      }
+    }
+    for (; r < n_blocks; ++r) {
+      const uint32_t* row = block_counts + (size_t)r * E;
+      const uint32_t v0 = row[e0], v1 = two ? row[e1] : 0u;
+      tot0 += v0;
+      tot1 += v1;
+      if (r < b) { pre0 += v0; pre1 += v1; }
+    }
+  }
+  const uint32_t t0 = seg_tiles(tot0, bm, xr), t1 = seg_tiles(tot1, bm, xr);
+  const uint32_t ic = wave_inclusive_sum_u32(tot0 + tot1);
   const uint32_t it = wave_inclusive_sum_u32(t0 + t1);
   if (lane == kWave - 1) { wsum_c[w] = ic; wsum_t[w] = it; }
   __syncthreads();
   uint32_t bc = 0, bt = 0;
   for (int i = 0; i < w; ++i) { bc += wsum_c[i]; bt += wsum_t[i]; }
-  const uint32_t off0 = bc + ic - (c0 + c1), toff0 = bt + it - (t0 + t1);
-  if (tid == 255) {
-    offsets[E] = (int32_t)(bc + ic);
-    *n_tiles = (int32_t)(bt + it);
+  const uint32_t off0 = bc + ic - (tot0 + tot1), toff0 = bt + it - (t0 + t1);
+  if (b == 0) {
+    if (tid == 255) {
+      offsets[E] = (int32_t)(bc + ic);
+      *n_tiles = (int32_t)(bt + it);
+    }
+    if (e0 < E) {
+      counts[e0] = (int32_t)tot0;
+      offsets[e0] = (int32_t)off0;
+      emit_tiles(tiles, toff0, e0, off0, tot0, t0, bm);
+    }
+    if (e1 < E) {
+      counts[e1] = (int32_t)tot1;
+      offsets[e1] = (int32_t)(off0 + tot0);
+      emit_tiles(tiles, toff0 + t0, e1, off0 + tot0, tot1, t1, bm);
+    }
   }
-  if (e0 < E) {
-    offsets[e0] = (int32_t)off0;
-    emit_tiles(tiles, toff0, e0, off0, c0, t0, bm);
+  if (e0 < E) base_s[e0] = off0 + pre0;
+  if (e1 < E) base_s[e1] = off0 + tot0 + pre1;
+  __syncthreads();
+  // the four chunks of the block in order inside each expert's run
+  for (int e = tid; e < E; e += blockDim.x) {
+    uint32_t run = base_s[e];
+#pragma unroll
+    for (int q = 0; q < kPermWaves; ++q) {
+      const uint32_t c = pos[q][e];
+      pos[q][e] = run;
+      run += c;
+    }
   }
-  if (e1 < E) {
-    offsets[e1] = (int32_t)(off0 + c0);
-    emit_tiles(tiles, toff0 + t0, e1, off0 + c0, c1, t1, bm);
-  }
-}
-
-__global__ __launch_bounds__(256) void perm_scatter_kernel(
-    const int32_t* __restrict__ ids, int64_t pairs, int E, int64_t n_chunks,
-    const uint32_t* __restrict__ chunk_base, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_src, int32_t* __restrict__ src_pos) {
-  __shared__ uint32_t pos[kPermWaves][kMaxE];
-  const int w = threadIdx.x >> 6, lane = lane_id();
-  const int64_t chunk = (int64_t)blockIdx.x * kPermWaves + w;
-  if (chunk >= n_chunks) return;  // per-wave exit: no block barrier below
-  for (int e = lane; e < E; e += kWave)
-    pos[w][e] = (uint32_t)offsets[e] + chunk_base[(size_t)e * n_chunks + chunk];
-  __builtin_amdgcn_wave_barrier();
-  const int64_t i0 = chunk * kChunk;
-  for (int j = 0; j < kChunk; j += kWave) {
-    const int64_t i = i0 + j + lane;
-    const bool ok = i < pairs;
+  __syncthreads();
+  for (int64_t j = i0; j < i1; j += kWave) {
+    const int64_t i = j + lane;
+    const bool ok = i < i1;
     const uint32_t e = ok ? (uint32_t)ids[i] : 0u;
     uint64_t mask = ballot(ok);
-    if (mask == 0ull) break;
 #pragma unroll
-    for (int b = 0; b < 9; ++b) {
-      const bool bit = (e >> b) & 1u;
+    for (int bit_i = 0; bit_i < 9; ++bit_i) {
+      const bool bit = (e >> bit_i) & 1u;
       const uint64_t bb = ballot(bit);
       mask &= bit ? bb : ~bb;
     }
     const uint64_t lower = mask & lanemask_lt();
-    uint32_t dst = 0;
     if (ok) {
-      dst = pos[w][e] + (uint32_t)__popcll(lower);
+      const uint32_t dst = pos[w][e] + (uint32_t)__popcll(lower);
       sorted_src[dst] = (int32_t)i;
       src_pos[i] = (int32_t)dst;
     }
@@ -287,17 +309,14 @@ hipError_t launch_permute(const int32_t* ids, int64_t N, int E, int K, int bm, i
                        w.counts, w.offsets, w.sorted_src, w.src_pos, w.tiles, w.n_tiles);
     return hipGetLastError();
   }
-  const int64_t n_chunks = perm_num_chunks(pairs);
-  const dim3 block(256);
-  const dim3 cgrid((unsigned)((n_chunks + kPermWaves - 1) / kPermWaves));
-  hipLaunchKernelGGL(perm_count_kernel, cgrid, block, 0, stream, ids, pairs, E, n_chunks,
-                     w.chunk_counts);
-  hipLaunchKernelGGL(perm_scan_kernel, dim3((unsigned)E), block, 0, stream, w.chunk_counts,
-                     n_chunks, w.counts);
-  hipLaunchKernelGGL(perm_tiles_kernel, dim3(1), block, 0, stream, w.counts, E, bm, xr, w.offsets,
-                     w.tiles, w.n_tiles);
-  hipLaunchKernelGGL(perm_scatter_kernel, cgrid, block, 0, stream, ids, pairs, E, n_chunks,
-                     w.chunk_counts, w.offsets, w.sorted_src, w.src_pos);
+  const int64_t cw = perm_chunk(pairs);
+  const int64_t n_blocks = perm_count_rows(pairs);
+  const dim3 grid((unsigned)n_blocks), block(256);
+  hipLaunchKernelGGL(perm_count_kernel, grid, block, 0, stream, ids, pairs, E, cw,
+                     w.block_counts);
+  hipLaunchKernelGGL(perm_scatter_kernel, grid, block, 0, stream, ids, pairs, E, cw, n_blocks,
+                     w.block_counts, bm, xr, w.counts, w.offsets, w.tiles, w.n_tiles,
+                     w.sorted_src, w.src_pos);
   return hipGetLastError();
 }
 
