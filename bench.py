@@ -21,6 +21,7 @@ workloads measured in the same run after the headline.
 from __future__ import annotations
 
 import argparse
+import functools
 import hashlib
 import json
 import os
@@ -289,7 +290,7 @@ def cpu_baseline(cfg, L, gpu, runs=3):
     return base, parity
 
 
-def run_extra(M, torch, name, steps, warmup, packed=True):
+def run_extra(M, torch, name, steps, warmup, packed=True, route_fused=False):
     """Another workload of the same layer shape in the same run: step time
     and tokens/s (`steps` timed steps between device synchronisations), and
     the stage times of `steps` further steps (HIP events between stages).
@@ -321,10 +322,11 @@ def run_extra(M, torch, name, steps, warmup, packed=True):
 
     def step():
         M.forward(x, W, cfg.K, beta_in=beta, recompute_bias=cfg.recompute_bias,
-                  logit_offset=off, workspace=ws, out=y)
+                  logit_offset=off, workspace=ws, out=y, route_fused=route_fused)
 
     _, aux = M.forward(x, W, cfg.K, beta_in=beta, recompute_bias=cfg.recompute_bias,
-                       logit_offset=off, workspace=ws, out=y, aux=("counts",))
+                       logit_offset=off, workspace=ws, out=y, aux=("counts",),
+                       route_fused=route_fused)
     counts = aux["counts"].cpu().numpy()
     for _ in range(warmup):
         step()
@@ -518,6 +520,9 @@ def main():
     ap.add_argument("--inference", action="store_true",
                     help="route with the given bias only (no quantile update in the step), "
                          "the layer as inference runs it")
+    ap.add_argument("--route-fused", action="store_true",
+                    help="select the experts inside the router GEMM's epilogue "
+                         "(MOE_ROUTE_FUSED) instead of in a pass of their own")
     ap.add_argument("--parts", action="store_true",
                     help="instead of the layer: time moe_route and moe_eqb_bias alone on the "
                          "workload's logits (warm and cold, median/p10/p90 of --steps samples)")
@@ -566,11 +571,15 @@ def main():
     W = M.ExpertWeights(bf16(L.w_router), bf16(L.w_gate), bf16(L.w_up), bf16(L.w_down),
                         bf16(L.ws_gate), bf16(L.ws_up), bf16(L.ws_down))
     fwd, ws_fn = M.forward, M.forward_workspace_bytes
+    if args.route_fused:
+        fwd = functools.partial(fwd, route_fused=True)
     if args.fp8:
         # E4M3 experts quantised from the bf16 weights by the library (untimed)
         W = M.quantize_experts(W)
         torch.cuda.synchronize()
         fwd, ws_fn = M.forward_fp8, M.forward_fp8_workspace_bytes
+        if args.route_fused:
+            fwd = functools.partial(fwd, route_fused=True)
     if not args.row_major:
         # the routed gate/up weights in the library's packed layout, as a
         # deployment stores them (untimed; the results are bit-identical)
@@ -687,7 +696,9 @@ def main():
                    **({"experts": "e4m3, 128x128 block scales, 1x128 activation groups"}
                       if args.fp8 else {}),
                    "gate_up_weights": "row-major" if args.row_major else
-                   "packed k-block-major (moe_pack_gateup_weights, untimed)"},
+                   "packed k-block-major (moe_pack_gateup_weights, untimed)",
+                   "selection": "fused into the router GEMM (merge kernel after it)"
+                   if args.route_fused else "separate pass over the logits"},
         "layer_tflops": layer_flops / (ms_step * 1e-3) / 1e12,
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "loads": {"max_over_mean_before": float(counts_before.max() / counts_before.mean()),
@@ -698,7 +709,8 @@ def main():
             and not args.inference:
         del ws, y, x, W
         torch.cuda.empty_cache()
-        out["extras"] = {n: run_extra(M, torch, n, s, 3, not args.row_major)
+        out["extras"] = {n: run_extra(M, torch, n, s, 3, not args.row_major,
+                                         args.route_fused)
                          for n, s in (("skewed", 10), ("decode", 50))}
     if not args.no_cpu_baseline and not args.fp8:
         log("cpu baseline ...")

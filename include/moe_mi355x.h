@@ -57,6 +57,13 @@ typedef enum {
 #define MOE_RECOMPUTE_BIAS 0x1u  /* route with beta_in, one exact quantile update, re-route */
 #define MOE_KEY32 0x2u           /* quantile over fp32 keys instead of bf16 keys */
 #define MOE_PACKED_GATEUP 0x4u   /* w_gate, w_up packed by moe_pack_gateup_weights */
+/* Select the experts inside the router GEMM's epilogue ([KPT] §6.1 routing
+ * equations, §7.1 token bias): every column tile of the router product also
+ * writes each row's K + 1 first (biased score, expert) entries, and a merge
+ * ranks them.  The outputs are the same as without the flag (a separate pass
+ * over the stored logits, the default, which measured faster); batches of at
+ * most 64 tokens and calls with logits_in ignore the flag. */
+#define MOE_ROUTE_FUSED 0x8u
 
 /*
  * moe_route - bias-corrected top-K selection and sigmoid mixture weights over
@@ -215,7 +222,7 @@ typedef struct {
   int32_t h;          /* routed expert hidden width */
   int32_t n_shared;   /* 0 or 1 always-on shared expert */
   int32_t h_shared;   /* shared expert hidden width */
-  uint32_t flags;     /* MOE_RECOMPUTE_BIAS | MOE_KEY32 | MOE_PACKED_GATEUP */
+  uint32_t flags;     /* MOE_RECOMPUTE_BIAS | MOE_KEY32 | MOE_PACKED_GATEUP | MOE_ROUTE_FUSED */
   const float* logit_offset; /* [E] fp32 or NULL: added to Z before the bias
                                 (an input-side knob, not part of the method) */
   const float* logits_in;    /* [N,E] fp32 or NULL: use these logits instead

@@ -14,7 +14,8 @@ from dataclasses import dataclass, replace
 from typing import Optional
 
 from . import _lib
-from ._lib import (MOE_KEY32, MOE_PACKED_GATEUP, MOE_RECOMPUTE_BIAS, MoeAux, MoeError,
+from ._lib import (MOE_KEY32, MOE_PACKED_GATEUP, MOE_RECOMPUTE_BIAS, MOE_ROUTE_FUSED, MoeAux,
+                   MoeError,
                    MoeFp8Weights, MoeProblem, MoeWeights)
 
 __all__ = ["route", "eqb_bias", "eqb_workspace_bytes", "EqbState", "eqb_bias_parts",
@@ -445,18 +446,22 @@ def _bf16_weights(x, weights: ExpertWeights):
 
 def forward(x, weights: ExpertWeights, K: int, beta_in=None, recompute_bias: bool = False,
             key_bits: int = 16, logit_offset=None, logits_in=None, aux=(),
-            workspace=None, out=None, stream=None):
+            workspace=None, out=None, stream=None, route_fused: bool = False):
     """MoE layer forward.  x: [N, d] bf16.  Returns y [N, d] bf16, or
-    (y, dict) when ``aux`` names optional outputs (see moe_aux_t)."""
+    (y, dict) when ``aux`` names optional outputs (see moe_aux_t).
+    ``route_fused`` selects the experts inside the router GEMM's epilogue
+    (MOE_ROUTE_FUSED; same outputs as the default separate pass)."""
     x, w, N, d, E, h, n_shared, h_shared = _bf16_weights(x, weights)
+    flags = (MOE_PACKED_GATEUP if weights.packed else 0) | \
+        (MOE_ROUTE_FUSED if route_fused else 0)
     return _run_forward(False, x, w, N, d, E, K, h, n_shared, h_shared, beta_in, recompute_bias,
-                        key_bits, logit_offset, logits_in, aux, workspace, out, stream,
-                        MOE_PACKED_GATEUP if weights.packed else 0)
+                        key_bits, logit_offset, logits_in, aux, workspace, out, stream, flags)
 
 
 def forward_noalloc(x, weights: ExpertWeights, K: int, beta_in=None,
                     recompute_bias: bool = False, key_bits: int = 16, logit_offset=None,
-                    logits_in=None, aux=(), out=None, stream=None):
+                    logits_in=None, aux=(), out=None, stream=None,
+                    route_fused: bool = False):
     """moe_forward_noalloc: the layer forward with the library's fixed
     per-GPU scratch array as its workspace (for callers that cannot allocate
     device memory; problems needing more than 64 MiB of workspace are
@@ -470,6 +475,7 @@ def forward_noalloc(x, weights: ExpertWeights, K: int, beta_in=None,
     logits_in = _dev(logits_in, "logits_in", torch.float32, (N, E))
     flags = (MOE_RECOMPUTE_BIAS if recompute_bias else 0) | (MOE_KEY32 if key_bits == 32 else 0)
     flags |= MOE_PACKED_GATEUP if weights.packed else 0
+    flags |= MOE_ROUTE_FUSED if route_fused else 0
     p = _problem(N, d, E, K, h, n_shared, h_shared, flags, logit_offset, logits_in)
     with _on(stream):
         y = out if out is not None else torch.empty((N, d), dtype=torch.bfloat16, device=x.device)
@@ -484,7 +490,8 @@ def forward_noalloc(x, weights: ExpertWeights, K: int, beta_in=None,
 
 def forward_fp8(x, weights: Fp8ExpertWeights, K: int, beta_in=None,
                 recompute_bias: bool = False, key_bits: int = 16, logit_offset=None,
-                logits_in=None, aux=(), workspace=None, out=None, stream=None):
+                logits_in=None, aux=(), workspace=None, out=None, stream=None,
+                route_fused: bool = False):
     """MoE layer forward with E4M3 experts (moe_forward_fp8).  x: [N, d] bf16;
     weights from ``quantize_experts`` or given codes and scales."""
     torch = _torch()
@@ -517,9 +524,10 @@ def forward_fp8(x, weights: Fp8ExpertWeights, K: int, beta_in=None,
                           ("ss_down", (n_shared, d // 128, hs // 128))):
             _dev(getattr(weights, name), name, f32, shp)
     w = MoeFp8Weights(*[_ptr(getattr(weights, f)) for f, _ in MoeFp8Weights._fields_])
+    flags = (MOE_PACKED_GATEUP if weights.packed else 0) | \
+        (MOE_ROUTE_FUSED if route_fused else 0)
     return _run_forward(True, x, w, N, d, E, K, h, n_shared, hs, beta_in, recompute_bias,
-                        key_bits, logit_offset, logits_in, aux, workspace, out, stream,
-                        MOE_PACKED_GATEUP if weights.packed else 0)
+                        key_bits, logit_offset, logits_in, aux, workspace, out, stream, flags)
 
 
 def stage_timing(enable=True):

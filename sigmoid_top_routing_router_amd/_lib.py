@@ -16,6 +16,7 @@ MOE_OK = 0
 MOE_RECOMPUTE_BIAS = 0x1
 MOE_KEY32 = 0x2
 MOE_PACKED_GATEUP = 0x4
+MOE_ROUTE_FUSED = 0x8
 
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED_SHAPE",
                 3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}

@@ -48,6 +48,15 @@ struct GemmArgs {
   // pieces one stage of the tile reads are one contiguous run.
   uint32_t b_row_pitch;
   uint32_t b_kblk_pitch;
+  // Router only, the selection fused into the epilogue (off while cand_s is
+  // NULL): every tile also writes, for each of its rows, the sel_k entries
+  // of its columns that come first in the selection order (biased score
+  // logit + sel_beta descending, then expert ascending) to
+  // cand_s / cand_e [row][n_tiles_n][sel_k]; sel_beta NULL is a zero bias.
+  const float* sel_beta;
+  float* cand_s;
+  uint32_t* cand_e;
+  int sel_k;
 };
 
 // Row-major B (every builder's default).

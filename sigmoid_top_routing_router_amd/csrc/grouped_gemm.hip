@@ -196,6 +196,164 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& a, int nt, int64_
   }
 }
 
+// ---- selection fused into the router tile ("Kolibri Pre-Training from
+// Scratch" §6.1, routing equations: the bias enters the selection only; §7.1:
+// the token bias needs the (K+1)-th largest biased score).  Once the tile's
+// logits are stored, the block reads them back (its own stores, visible
+// after the barrier; L2 hits) 16 lanes per row, 32 rows per round, the next
+// round's rows in flight while one is selected.  Each row's biased scores
+// b = z + (beta + 0) (-0 becomes +0) over the tile's columns give its
+// KC = K + 1 first entries in the order (score descending, expert
+// ascending), as the routing kernel does over a whole row: L = the KC-th
+// largest of the 16 lane maxima bounds the KC-th largest score from below,
+// the candidates (score >= L, usually a few) are ranked exactly in a
+// per-row LDS list, and a row with more than kSelCap candidates (many tied
+// scores) pops its KC entries one by one.  Columns past E score -inf.  The
+// KC first entries of a whole row are among the union of its tiles' lists,
+// so a small merge finishes the selection.
+constexpr int kSelCap = 64;
+
+template <bool NARROW>
+__device__ __forceinline__ void router_tile_select(const GemmArgs& a, int nt, int64_t row0,
+                                                   int rows, int lane, int tid, char* lds_raw) {
+  constexpr int TC = NARROW ? BN / 2 : BN;  // columns of the tile
+  constexpr int NC = TC / 64;               // 4-column pieces per lane and row
+  constexpr int NVL = 4 * NC;               // scores per lane and row
+  static_assert(32 * kSelCap * 8 <= LDS_BYTES, "selection LDS");
+  const float* Z = reinterpret_cast<const float*>(a.out);
+  const int E = a.b_rows;
+  const int KC = a.sel_k;
+  const int col_base = nt * TC;
+  const int ntn = a.n_tiles_n;
+  const int rsel = tid >> 4;  // row of this thread in a round of 32
+  const int g = tid & 15;     // lane within the row's 16
+  const uint64_t gmask = 0xFFFFull << (16 * ((tid >> 4) & 3));
+  float* cs = reinterpret_cast<float*>(lds_raw) + rsel * kSelCap;
+  uint32_t* ce = reinterpret_cast<uint32_t*>(lds_raw) + 32 * kSelCap + rsel * kSelCap;
+  // bias of this lane's columns; -inf marks columns past E
+  float bv[NVL];
+#pragma unroll
+  for (int i = 0; i < NVL; ++i) {
+    const int e = col_base + 64 * (i >> 2) + 4 * g + (i & 3);
+    bv[i] = e < E ? (a.sel_beta ? a.sel_beta[e] + 0.0f : 0.0f) : -INFINITY;
+  }
+  const bool vec = (E & 3) == 0;
+  auto load_row = [&](int r0, float (&v)[NVL]) {
+    const int rl = min(r0 + rsel, rows - 1);
+    const float* zr = Z + (row0 + rl) * (int64_t)E + col_base;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int c = 4 * g + 64 * j;
+      if (vec) {
+        const float4 t = col_base + c < E ? *reinterpret_cast<const float4*>(zr + c)
+                                          : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[4 * j + k] = col_base + c + k < E ? zr[c + k] : 0.0f;
+      }
+    }
+  };
+  __syncthreads();  // the tile's logits are stored; the fragment reads are done
+  float cur[NVL], nxt[NVL];
+  load_row(0, cur);
+#pragma unroll 1
+  for (int r0 = 0; r0 < rows; r0 += 32) {
+    if (r0 + 32 < rows) load_row(r0 + 32, nxt);
+    const int rl = r0 + rsel;
+    const bool live = rl < rows;
+    float v[NVL];
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) v[i] = bv[i] == -INFINITY ? -INFINITY : cur[i] + bv[i];
+    float* os = a.cand_s + ((row0 + rl) * ntn + nt) * KC;
+    uint32_t* oe = a.cand_e + ((row0 + rl) * ntn + nt) * KC;
+    // (1) lower bound L of the KC-th largest score
+    float lm = v[0];
+#pragma unroll
+    for (int i = 1; i < NVL; ++i) lm = fmaxf(lm, v[i]);
+    float L = -INFINITY;
+#pragma unroll
+    for (int k = 0; k <= MOE_KMAX_INTERNAL; ++k) {
+      if (k >= KC) break;  // uniform
+      L = row16_max_f32(lm);
+      const int win = __ffsll((unsigned long long)(ballot(lm == L) & gmask)) - 1;
+      if (lane == win) lm = -INFINITY;
+    }
+    // (2) the candidates, compacted in lane order
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) cnt += (v[i] >= L) ? 1u : 0u;
+    uint32_t off = 0, total = 0;
+#pragma unroll
+    for (int bit = 0; bit < 5; ++bit) {  // cnt <= 16
+      const uint64_t mk = ballot(((cnt >> bit) & 1u) != 0u) & gmask;
+      off += (uint32_t)__builtin_amdgcn_mbcnt_hi(
+                 (uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u)) << bit;
+      total += (uint32_t)__popcll(mk) << bit;
+    }
+    if (ballot(total > (uint32_t)kSelCap) == 0) {
+#pragma unroll
+      for (int i = 0; i < NVL; ++i) {
+        if (v[i] >= L) {
+          cs[off] = v[i];
+          ce[off] = (uint32_t)(col_base + 64 * (i >> 2) + 4 * g + (i & 3));
+          ++off;
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the row's list is written
+      for (uint32_t i = (uint32_t)g; i < total; i += 16) {
+        const float si = cs[i];
+        const uint32_t ei = ce[i];
+        uint32_t rank = 0;
+        for (uint32_t j = 0; j < total; ++j) {
+          const float sj = cs[j];
+          const uint32_t ej = ce[j];
+          rank += (uint32_t)((sj > si) | ((sj == si) & (ej < ei)));
+        }
+        if (live && rank < (uint32_t)KC) {
+          os[rank] = si;
+          oe[rank] = ei;
+        }
+      }
+    } else {
+      // (2') KC pops: pop r takes the row's first (score, expert) after pop
+      // r - 1.  A lane's experts rise with its slot i, so "expert after the
+      // last pop's" is "slot >= k_le" among scores equal to the last pop's.
+      float sp = INFINITY;
+      int k_le = 0;
+#pragma unroll 1
+      for (int r = 0; r < KC; ++r) {
+        float bs = -INFINITY;
+        int bi = -1;
+#pragma unroll
+        for (int i = 0; i < NVL; ++i) {
+          const float sv = v[i];
+          const bool after = r == 0 || sv < sp || (sv == sp && i >= k_le);
+          const bool better = after && (sv > bs || (bi < 0 && sv == bs));
+          bs = better ? sv : bs;
+          bi = better ? i : bi;
+        }
+        const uint32_t be =
+            bi >= 0 ? (uint32_t)(64 * (bi >> 2) + 4 * g + (bi & 3)) : 0xFFFFFFFFu;
+        const float rmx = row16_max_f32(bs);
+        const uint32_t we = row16_min_u32(bs == rmx ? be : 0xFFFFFFFFu);
+        if (live && g == 0) {
+          os[r] = rmx;
+          oe[r] = we == 0xFFFFFFFFu ? we : (uint32_t)col_base + we;
+        }
+        sp = rmx;
+        const int wa = (int)(we >> 6), wl = (int)((we >> 2) & 15u), wc = (int)(we & 3u);
+        k_le = we == 0xFFFFFFFFu ? NVL : 4 * wa + (g < wl ? 4 : (g == wl ? wc + 1 : 0));
+      }
+    }
+    // the row lists are read before the next round writes them
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) cur[i] = nxt[i];
+  }
+}
+
 // Epilogue of one tile: accumulators acc[m][f] of wave (wg, wp) -> the output
 // (router: fp32 logits + offset; gate/up: SiLU(g) * u in bf16; down: bf16).
 template <int MODE, int XR, bool NARROW = false>
@@ -211,12 +369,11 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, floatx16_t (&ac
   const int orow_l = lane & 31;
   const int ocol_l = 4 * (lane >> 5);
   if (MODE == kRouter) {
-    if (!any) return;
     float* Zo = reinterpret_cast<float*>(a.out);
     const bool vec = (a.ldo % 4) == 0;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      if (m >= live_m) break;
+      if (!any || m >= live_m) break;
       // narrow tiles: wave (wg, wp) holds rows wg*128 + (wp>>1)*64 .. +64
       const int rr = wg * 128 + (NARROW ? (wp >> 1) * 64 : 0) + m * 32 + orow_l;
       if (rr >= rows) continue;
@@ -242,6 +399,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, floatx16_t (&ac
         }
       }
     }
+    // uniform: every wave takes part in the selection's barrier
+    if (a.cand_s) router_tile_select<NARROW>(a, nt, row0, rows, lane, tid, lds_raw);
     return;
   }
   // bf16 outputs (H or Y) go through LDS: every wave converts its
@@ -1156,10 +1315,19 @@ static hipError_t launch_gemm(int mode, const GemmArgs& a, int64_t max_m_tiles,
 // 0.551 -> 0.541 ms on one box, 0.535 -> 0.532 ms on another).  Wider
 // routers keep the 256-wide tiles: narrow ones re-read the A rows once more
 // per 128 columns and measured no faster at E = 384.
+static void apply_sel(GemmArgs& a, const RouterSel* sel) {
+  if (!sel) return;
+  a.sel_beta = sel->beta;
+  a.cand_s = sel->cand_s;
+  a.cand_e = sel->cand_e;
+  a.sel_k = sel->K + 1;
+}
+
 hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w_router,
                               const float* offset, int64_t N, int d, int E, float* Z,
-                              hipStream_t stream) {
+                              hipStream_t stream, const RouterSel* sel) {
   GemmArgs a = router_args(x, w_router, offset, N, d, E, Z);
+  apply_sel(a, sel);
   if (E <= BN / 2) {
     a.n_tiles_n = 1;
     return launch_gemm(kRouterNarrow, a, (N + BM - 1) / BM, stream);
@@ -1196,8 +1364,9 @@ hipError_t launch_router_shared_gateup(const uint16_t* x, int64_t N, int d,
                                        const uint16_t* w_router, const float* offset, int E,
                                        float* Z, const uint16_t* ws_gate,
                                        const uint16_t* ws_up, int hs, uint16_t* Hs,
-                                       hipStream_t stream) {
-  const GemmArgs r = router_args(x, w_router, offset, N, d, E, Z);
+                                       hipStream_t stream, const RouterSel* sel) {
+  GemmArgs r = router_args(x, w_router, offset, N, d, E, Z);
+  apply_sel(r, sel);
   const GemmArgs g = gateup_args(x, N, nullptr, 1, nullptr, nullptr, N, ws_gate, ws_up, d, hs, Hs);
   const int64_t work = ((N + BM - 1) / BM) * (r.n_tiles_n + g.n_tiles_n);
   if (work <= 0) return hipSuccess;
@@ -1258,8 +1427,10 @@ hipError_t launch_router_shared_gateup_fp8(const uint16_t* x, const uint8_t* xq,
                                            const float* offset, int E, float* Z,
                                            const uint8_t* wsg, const float* ssg,
                                            const uint8_t* wsu, const float* ssu, int hs,
-                                           uint8_t* Hsq, float* Hss, hipStream_t stream) {
-  const GemmArgs r = router_args(x, w_router, offset, N, d, E, Z);
+                                           uint8_t* Hsq, float* Hss, hipStream_t stream,
+                                           const RouterSel* sel) {
+  GemmArgs r = router_args(x, w_router, offset, N, d, E, Z);
+  apply_sel(r, sel);
   const GemmArgs g = gateup_fp8_args(xq, xs, N, nullptr, 1, nullptr, nullptr, N, wsg, ssg, wsu,
                                      ssu, d, hs, Hsq, Hss);
   const int64_t work = ((N + BM - 1) / BM) * (r.n_tiles_n + g.n_tiles_n);

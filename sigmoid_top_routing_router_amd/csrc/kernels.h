@@ -19,6 +19,25 @@ hipError_t launch_route(const float* Z, const float* beta, int64_t N, int E, int
                         int32_t* ids, float* S, float* alpha, float* margin,
                         hipStream_t stream, uint32_t* zero = nullptr, size_t zero_n = 0);
 
+// Selection fused into the router GEMM (RouterSel given to the router
+// launchers below): every column tile of the router product writes, for
+// each row, its K + 1 first entries in the selection order (biased score
+// descending, expert ascending) to cand_s / cand_e [N][router_col_tiles(E)]
+// [K + 1]; the first K + 1 entries of a row lie among them.
+struct RouterSel {
+  const float* beta;  // selection bias [E] or NULL (zero)
+  float* cand_s;      // biased scores
+  uint32_t* cand_e;   // their experts
+  int K;
+};
+int router_col_tiles(int E);
+// The merge of those lists: the same ids, S, alpha and margin as
+// launch_route over Z with the same bias (any of the four may be NULL).
+hipError_t launch_route_merge(const float* cand_s, const uint32_t* cand_e, int n_col_tiles,
+                              const float* Z, int64_t N, int E, int K, int32_t* ids, float* S,
+                              float* alpha, float* margin, hipStream_t stream,
+                              uint32_t* zero = nullptr, size_t zero_n = 0);
+
 // ---------------------------------------------------------------- EQB
 // Workspace carved by the caller (all 256-byte aligned):
 //   hist  [passes][E][256] uint32 (passes = key_bits / 8)
@@ -73,7 +92,7 @@ hipError_t launch_count(const int32_t* ids, int64_t pairs, int E, int32_t* count
 // Router logits Z[N,E] = x[N,d] W_r[E,d]^T (+ offset[E]) in fp32; N*d*2 < 4 GiB.
 hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* w_router,
                               const float* offset, int64_t N, int d, int E, float* Z,
-                              hipStream_t stream);
+                              hipStream_t stream, const RouterSel* sel = nullptr);
 // Grouped SwiGLU gate/up: for every m-tile of the table, H rows =
 // silu(X W_g^T) * (X W_u^T) (bf16).  When `tiles` is NULL the rows are the
 // tokens 0..N-1 of one expert (shared expert), otherwise A rows are gathered
@@ -98,7 +117,7 @@ hipError_t launch_router_shared_gateup(const uint16_t* x, int64_t N, int d,
                                        const uint16_t* w_router, const float* offset, int E,
                                        float* Z, const uint16_t* ws_gate,
                                        const uint16_t* ws_up, int hs, uint16_t* Hs,
-                                       hipStream_t stream);
+                                       hipStream_t stream, const RouterSel* sel = nullptr);
 
 
 // ---------------------------------------------------------------- combine
@@ -165,7 +184,8 @@ hipError_t launch_router_shared_gateup_fp8(const uint16_t* x, const uint8_t* xq,
                                            const float* offset, int E, float* Z,
                                            const uint8_t* wsg, const float* ssg,
                                            const uint8_t* wsu, const float* ssu, int hs,
-                                           uint8_t* Hsq, float* Hss, hipStream_t stream);
+                                           uint8_t* Hsq, float* Hss, hipStream_t stream,
+                                           const RouterSel* sel = nullptr);
 
 // Weight-streaming variants of the routed (grouped) products for batches of
 // at most 64 tokens (every tile then holds at most 64 rows); same arguments

@@ -186,7 +186,7 @@ moe_status_t check_problem(const moe_problem_t* p) {
                 "N=%lld too large: x [N,d], the routed hidden rows [N*K,h] and the shared "
                 "hidden rows [N,h_shared] must each be below 4 GiB in bf16",
                 (long long)p->N);
-  if (p->flags & ~(MOE_RECOMPUTE_BIAS | MOE_KEY32 | MOE_PACKED_GATEUP))
+  if (p->flags & ~(MOE_RECOMPUTE_BIAS | MOE_KEY32 | MOE_PACKED_GATEUP | MOE_ROUTE_FUSED))
     return fail(MOE_ERR_INVALID_ARGUMENT, "unknown flag bits 0x%x", p->flags);
   if (p->logits_in && p->logit_offset)
     return fail(MOE_ERR_INVALID_ARGUMENT, "logit_offset applies to computed logits only; logits_in is set");
@@ -379,6 +379,21 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
   // router GEMM (the fork), but its work is enqueued after that GEMM, whose
   // blocks are then dispatched first
   if (side) MOE_TRY_HIP(hipEventRecord(side->fork, st), "moe_forward: fork");
+  // Selection inside the router GEMM's epilogue (MOE_ROUTE_FUSED): the
+  // tiles' candidate lists ([N][tiles][K+1] scores, then experts) live in the
+  // expert-output buffer Y, which nothing reads or writes before the down
+  // projection.
+  moe::RouterSel rsel{};
+  const moe::RouterSel* sel = nullptr;
+  const int sel_tiles = moe::router_col_tiles(E);
+  if (!small && !p->logits_in && (p->flags & MOE_ROUTE_FUSED)) {
+    const size_t n = (size_t)N * sel_tiles * (K + 1);
+    if (2 * n * sizeof(float) > (size_t)N * K * d * sizeof(uint16_t))
+      return fail(MOE_ERR_UNSUPPORTED_SHAPE, "router selection lists do not fit");
+    rsel = moe::RouterSel{beta_in, reinterpret_cast<float*>(l.Y),
+                          reinterpret_cast<uint32_t*>(l.Y) + n, K};
+    sel = &rsel;
+  }
   // the shared expert's products on the caller's stream (no side stream)
   const bool shared_here = shared && !side;
   if (small) {
@@ -424,14 +439,16 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
       MOE_TRY_HIP(moe::launch_router_shared_gateup_fp8(x, l.xq, l.xs, N, d, ex.w_router,
                                                        p->logit_offset, E, zout, q->ws_gate,
                                                        q->ss_gate, q->ws_up, q->ss_up, hs,
-                                                       l.Hsq, l.Hss, st),
+                                                       l.Hsq, l.Hss, st, sel),
                   "moe_forward: router GEMM + shared gate/up");
     else if (shared_here)
       MOE_TRY_HIP(moe::launch_router_shared_gateup(x, N, d, ex.w_router, p->logit_offset, E,
-                                                   zout, w->ws_gate, w->ws_up, hs, l.Hs, st),
+                                                   zout, w->ws_gate, w->ws_up, hs, l.Hs, st,
+                                                   sel),
                   "moe_forward: router GEMM + shared gate/up");
     else
-      MOE_TRY_HIP(moe::launch_router_gemm(x, ex.w_router, p->logit_offset, N, d, E, zout, st),
+      MOE_TRY_HIP(moe::launch_router_gemm(x, ex.w_router, p->logit_offset, N, d, E, zout, st,
+                                          sel),
                   "moe_forward: router GEMM");
     Z = zout;
   }
@@ -486,9 +503,15 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
   if (recompute) {
     // first pass: alpha only, unless the loads before the update are wanted;
     // it also clears the first histogram of the quantile update
-    MOE_TRY_HIP(moe::launch_route(Z, beta_in, N, E, K, A.counts_before ? l.ids0 : nullptr,
-                                  nullptr, alpha, nullptr, st, l.eqb.hist, (size_t)E * 256),
-                "moe_forward: first routing");
+    if (sel)
+      MOE_TRY_HIP(moe::launch_route_merge(sel->cand_s, sel->cand_e, sel_tiles, Z, N, E, K,
+                                          A.counts_before ? l.ids0 : nullptr, nullptr, alpha,
+                                          nullptr, st, l.eqb.hist, (size_t)E * 256),
+                  "moe_forward: first routing");
+    else
+      MOE_TRY_HIP(moe::launch_route(Z, beta_in, N, E, K, A.counts_before ? l.ids0 : nullptr,
+                                    nullptr, alpha, nullptr, st, l.eqb.hist, (size_t)E * 256),
+                  "moe_forward: first routing");
     if (A.counts_before)
       MOE_TRY_HIP(moe::launch_count(l.ids0, N * K, E, A.counts_before, st), "moe_forward: loads");
     float* beta_new = A.beta_out ? A.beta_out : l.beta_new;
@@ -498,6 +521,12 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
                 "moe_forward: quantile update");
     MOE_TRY_HIP(moe::launch_route(Z, beta_new, N, E, K, ids, S, nullptr, margin, st),
                 "moe_forward: routing");
+  } else if (sel) {
+    MOE_TRY_HIP(moe::launch_route_merge(sel->cand_s, sel->cand_e, sel_tiles, Z, N, E, K, ids, S,
+                                        alpha, margin, st),
+                "moe_forward: routing");
+    if (A.counts_before)
+      MOE_TRY_HIP(moe::launch_count(ids, N * K, E, A.counts_before, st), "moe_forward: loads");
   } else {
     MOE_TRY_HIP(moe::launch_route(Z, beta_in, N, E, K, ids, S, alpha, margin, st),
                 "moe_forward: routing");

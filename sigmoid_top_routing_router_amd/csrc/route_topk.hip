@@ -389,6 +389,76 @@ __global__ __launch_bounds__(256) void route_group_kernel(
   flush(quad);
 }
 
+// ---------------------------------------------------------------- merge
+// The end of the selection fused into the router GEMM: each of the row's
+// T column tiles left its KC = K + 1 first (biased score, expert) entries,
+// and the row's own first KC entries are the first KC of that union (an
+// entry among a row's KC first is among its tile's KC first).  16 lanes per
+// row rank the T * KC <= 32 entries exactly in the order (score descending,
+// expert ascending); the outputs are those of route_group_kernel: ids and
+// weights sigma(z) of the K picks (z, the unbiased logit, read back from
+// Z), alpha = -(K+1)-th score, margin = K-th minus (K+1)-th score.
+__global__ __launch_bounds__(256) void route_merge_kernel(
+    const float* __restrict__ cand_s, const uint32_t* __restrict__ cand_e, int C,
+    const float* __restrict__ Z, int64_t N, int E, int K, int32_t* __restrict__ ids,
+    float* __restrict__ S, float* __restrict__ alpha, float* __restrict__ margin,
+    uint32_t* __restrict__ zero, int64_t zero_n) {
+  clear_words<256>(zero, zero_n);
+  __shared__ float ls[16][32];
+  __shared__ uint32_t le[16][32];
+  __shared__ float kk[16][2];
+  const int g = threadIdx.x & 15;
+  const int rl = threadIdx.x >> 4;
+  const int64_t row = (int64_t)blockIdx.x * 16 + rl;
+  const bool ok = row < N;
+  if (ok) {
+    for (int c = g; c < C; c += 16) {
+      ls[rl][c] = cand_s[row * C + c];
+      le[rl][c] = cand_e[row * C + c];
+    }
+  }
+  __syncthreads();
+  if (ok) {
+    for (int i = g; i < C; i += 16) {
+      const float si = ls[rl][i];
+      const uint32_t ei = le[rl][i];
+      uint32_t rank = 0;
+      for (int j = 0; j < C; ++j) {
+        const float sj = ls[rl][j];
+        const uint32_t ej = le[rl][j];
+        rank += (uint32_t)((sj > si) | ((sj == si) & (ej < ei)));
+      }
+      if (rank < (uint32_t)K) {
+        if (ids) ids[row * K + rank] = (int32_t)ei;
+        if (S && ei < (uint32_t)E) S[row * K + rank] = sigmoid_weight(Z[row * (int64_t)E + ei]);
+      }
+      if (rank == (uint32_t)K - 1) kk[rl][0] = si;
+      if (rank == (uint32_t)K) kk[rl][1] = si;
+    }
+  }
+  __syncthreads();
+  if (ok && g == 0) {
+    if (alpha) alpha[row] = -kk[rl][1];
+    if (margin) margin[row] = kk[rl][0] - kk[rl][1];
+  }
+}
+
+int router_col_tiles(int E) { return (E + 255) / 256; }
+
+hipError_t launch_route_merge(const float* cand_s, const uint32_t* cand_e, int n_col_tiles,
+                              const float* Z, int64_t N, int E, int K, int32_t* ids, float* S,
+                              float* alpha, float* margin, hipStream_t stream, uint32_t* zero,
+                              size_t zero_n) {
+  const int C = n_col_tiles * (K + 1);
+  if (C > 32 || K > MOE_KMAX_INTERNAL || N < 1) return hipErrorInvalidValue;
+  const int64_t blocks = (N + 15) / 16;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(route_merge_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, cand_s,
+                     cand_e, C, Z, N, E, K, ids, S, alpha, margin, zero,
+                     zero ? (int64_t)zero_n : (int64_t)0);
+  return hipGetLastError();
+}
+
 // Blocks of 256 threads of one variant of the one-wave kernel that the device
 // holds at once (occupancy x compute units), queried once per variant and
 // device.  kind 0: full selection, 1: the keys-only variant.  Host threads

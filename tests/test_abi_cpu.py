@@ -84,7 +84,7 @@ def test_forward_workspace_sizes(lib):
     assert b >= pairs * (512 + 2560) * 2 + 16384 * 384 * 4
     assert b < 2 * (pairs * (512 + 2560) * 2 + 16384 * 384 * 4 + 16384 * (512 + 2560) * 2)
     for bad in (dict(K=0), dict(K=9), dict(E=6), dict(E=385), dict(d=100), dict(h=48),
-                dict(n_shared=2), dict(N=0), dict(flags=8)):
+                dict(n_shared=2), dict(N=0), dict(flags=16)):
         assert lib.moe_forward_workspace_bytes(C.byref(_problem(**bad))) == 0, bad
 
 
