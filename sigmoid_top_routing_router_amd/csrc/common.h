@@ -157,6 +157,23 @@ __device__ __forceinline__ float sigmoid_weight(float z) {
   if (z < -80.0f) return (float)(1.0 / (1.0 + exp(-(double)z)));
   return 1.0f / (1.0f + expf(-z));
 }
+// Mean of the raw expert biases -q[e], e < E, in fp64 with the terms added
+// in expert order ("Kolibri Pre-Training from Scratch" §7.1: the biases are
+// centred after the quantile step).  q is in LDS; one thread calls this.
+// The reads of 16 terms go ahead of their adds.
+__device__ __forceinline__ double raw_bias_mean(const float* q, int E) {
+  double acc = 0.0;
+  int i = 0;
+  for (; i + 16 <= E; i += 16) {
+    float b[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) b[j] = q[i + j];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc += (double)(-b[j]);
+  }
+  for (; i < E; ++i) acc += (double)(-q[i]);
+  return acc / (double)E;
+}
 // Grid-stride clear of n words (a buffer that later kernels accumulate into),
 // ahead of a kernel's own work.
 // BLOCK is the launch's block size (a constant, so that no load of the

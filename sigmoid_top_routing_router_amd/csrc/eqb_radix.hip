@@ -314,20 +314,7 @@ __global__ __launch_bounds__(256) void eqb_centre_kernel(const float* __restrict
   __shared__ float q_s[kEqbMaxE];
   for (int i = threadIdx.x; i < E; i += blockDim.x) q_s[i] = qraw[i];
   __syncthreads();
-  if (threadIdx.x == 0) {
-    // the sum in expert order; the LDS reads of 16 terms go ahead of their adds
-    double acc = 0.0;
-    int i = 0;
-    for (; i + 16 <= E; i += 16) {
-      float b[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) b[j] = q_s[i + j];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc += (double)(-b[j]);
-    }
-    for (; i < E; ++i) acc += (double)(-q_s[i]);
-    mean_s = acc / (double)E;
-  }
+  if (threadIdx.x == 0) mean_s = raw_bias_mean(q_s, E);
   __syncthreads();
   const double mean = mean_s;
   for (int i = threadIdx.x; i < E; i += blockDim.x)
@@ -406,6 +393,11 @@ hipError_t launch_eqb_hist(const float* Z, const float* alpha, int64_t N, int E,
   EqbPassArgs pa{};
   pa.prefix = prefix;
   return launch_hist<false>(Z, alpha, N, E, key_bits, pass, pa, hist_pass, stream);
+}
+
+hipError_t launch_eqb_centre(const float* qraw, int E, float* beta_out, hipStream_t stream) {
+  hipLaunchKernelGGL(eqb_centre_kernel, dim3(1), dim3(256), 0, stream, qraw, E, beta_out);
+  return hipGetLastError();
 }
 
 hipError_t launch_eqb_scan(const EqbWork& w, int E, int K, int key_bits, int pass,

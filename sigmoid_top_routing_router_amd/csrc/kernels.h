@@ -18,6 +18,14 @@ namespace moe {
 hipError_t launch_route(const float* Z, const float* beta, int64_t N, int E, int K,
                         int32_t* ids, float* S, float* alpha, float* margin,
                         hipStream_t stream, uint32_t* zero = nullptr, size_t zero_n = 0);
+// The same with the bias centred on the fly from raw quantiles qraw (the
+// last step of an exact quantile update): beta_e = fp32(fp64(-qraw_e) - mean)
+// is used for the selection and stored to beta_out (required); beta is
+// ignored.
+hipError_t launch_route_centred(const float* Z, const float* beta, const float* qraw,
+                                float* beta_out, int64_t N, int E, int K, int32_t* ids,
+                                float* S, float* alpha, float* margin, hipStream_t stream,
+                                uint32_t* zero = nullptr, size_t zero_n = 0);
 
 // Selection fused into the router GEMM (RouterSel given to the router
 // launchers below): every column tile of the router product writes, for
@@ -49,6 +57,8 @@ struct EqbWork {
   float* qraw;
 };
 size_t eqb_hist_bytes(int E, int key_bits);
+// One-block centring of raw quantiles: beta_out = fp32(fp64(-qraw) - mean).
+hipError_t launch_eqb_centre(const float* qraw, int E, float* beta_out, hipStream_t stream);
 size_t eqb_state_bytes(int E);
 // hist0_zeroed: the first pass's histogram (hist[0 .. E*256)) is already
 // zero (cleared by the routing launch that gave alpha); else a fill clears it.

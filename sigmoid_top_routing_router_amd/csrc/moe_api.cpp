@@ -516,10 +516,12 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
       MOE_TRY_HIP(moe::launch_count(l.ids0, N * K, E, A.counts_before, st), "moe_forward: loads");
     float* beta_new = A.beta_out ? A.beta_out : l.beta_new;
     moe::EqbWork ew{l.eqb.hist, l.eqb.state, l.eqb.qraw};
-    MOE_TRY_HIP(moe::launch_eqb(Z, alpha, N, E, K, key_bits, beta_new, A.quantile_out, ew, st,
+    // the centring of the raw quantiles happens inside the final routing pass
+    MOE_TRY_HIP(moe::launch_eqb(Z, alpha, N, E, K, key_bits, nullptr, A.quantile_out, ew, st,
                                 true),
                 "moe_forward: quantile update");
-    MOE_TRY_HIP(moe::launch_route(Z, beta_new, N, E, K, ids, S, nullptr, margin, st),
+    MOE_TRY_HIP(moe::launch_route_centred(Z, nullptr, l.eqb.qraw, beta_new, N, E, K, ids, S,
+                                          nullptr, margin, st),
                 "moe_forward: routing");
   } else if (sel) {
     MOE_TRY_HIP(moe::launch_route_merge(sel->cand_s, sel->cand_e, sel_tiles, Z, N, E, K, ids, S,

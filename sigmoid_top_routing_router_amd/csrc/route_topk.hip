@@ -209,12 +209,22 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 // expert), which gives the same ids in the same order, and the same K-th and
 // (K+1)-th scores.
 constexpr int kRouteCap = 64;
+__host__ __device__ constexpr int qraw_cap(int nc) { return 64 * nc; }
 
-template <int NC, bool FULL>
+//
+// Centring on the fly (CENTRE, after an exact quantile update): the bias is
+// beta_e = fp32(fp64(-qraw_e) - mean), the mean over all experts in fp64 in
+// expert order, exactly as eqb_centre_kernel forms it; every block computes
+// it (one thread, from the raw quantiles in LDS) before it loads its rows,
+// and block 0 stores the biases to beta_out.  (Loading the rows first
+// holds them in registers through the sum: 104 instead of 74 VGPRs.)  This saves the one-block
+// centring launch, which inside the layer waits for a free compute unit.
+template <int NC, bool FULL, bool CENTRE>
 __global__ __launch_bounds__(256) void route_group_kernel(
     const float* __restrict__ Z, const float* __restrict__ beta, int64_t N, int E, int K,
     int32_t* __restrict__ ids, float* __restrict__ S, float* __restrict__ alpha,
-    float* __restrict__ margin, uint32_t* __restrict__ zero, int64_t zero_n) {
+    float* __restrict__ margin, uint32_t* __restrict__ zero, int64_t zero_n,
+    const float* __restrict__ qraw, float* __restrict__ beta_out) {
   clear_words<256>(zero, zero_n);
   constexpr int NVL = 4 * NC;  // experts per lane
   const int lane = lane_id();
@@ -227,13 +237,36 @@ __global__ __launch_bounds__(256) void route_group_kernel(
   __shared__ int32_t out_id[4][4][MOE_KMAX_INTERNAL];
   __shared__ float out_s[4][4][MOE_KMAX_INTERNAL];  // unbiased logits of the picks
   __shared__ float kk[4][4][2];                 // K-th and (K+1)-th score
-  for (int i = (int)threadIdx.x; i < 16 * NC; i += 256) {
-    const int e0 = 4 * (i & 15) + 64 * (i >> 4);
-    float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (beta && (FULL || e0 < E))
-      b = make_float4(beta[e0] + 0.0f, beta[e0 + 1] + 0.0f, beta[e0 + 2] + 0.0f,
-                      beta[e0 + 3] + 0.0f);
-    sbeta[i] = b;
+  if constexpr (CENTRE) {
+    __shared__ float q_s[qraw_cap(NC)];  // raw quantiles
+    __shared__ double mean_s;
+    for (int i = (int)threadIdx.x; i < E; i += 256) q_s[i] = qraw[i];
+    __syncthreads();
+    if (threadIdx.x == 0) mean_s = raw_bias_mean(q_s, E);
+    __syncthreads();
+    const double mean = mean_s;
+    for (int i = (int)threadIdx.x; i < 16 * NC; i += 256) {
+      const int e0 = 4 * (i & 15) + 64 * (i >> 4);
+      float b[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (FULL || e0 + c < E) {
+          const float bc = (float)((double)(-q_s[e0 + c]) - mean);
+          if (blockIdx.x == 0 && beta_out) beta_out[e0 + c] = bc;
+          b[c] = bc + 0.0f;
+        }
+      }
+      sbeta[i] = make_float4(b[0], b[1], b[2], b[3]);
+    }
+  } else {
+    for (int i = (int)threadIdx.x; i < 16 * NC; i += 256) {
+      const int e0 = 4 * (i & 15) + 64 * (i >> 4);
+      float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (beta && (FULL || e0 < E))
+        b = make_float4(beta[e0] + 0.0f, beta[e0 + 1] + 0.0f, beta[e0 + 2] + 0.0f,
+                        beta[e0 + 3] + 0.0f);
+      sbeta[i] = b;
+    }
   }
   __syncthreads();
   const int64_t nquads = (N + 3) / 4;
@@ -494,6 +527,14 @@ static int64_t route_resident_blocks(int nv, int kind) {
 hipError_t launch_route(const float* Z, const float* beta, int64_t N, int E, int K,
                         int32_t* ids, float* S, float* alpha, float* margin,
                         hipStream_t stream, uint32_t* zero, size_t zero_n) {
+  return launch_route_centred(Z, beta, nullptr, nullptr, N, E, K, ids, S, alpha, margin, stream,
+                              zero, zero_n);
+}
+
+hipError_t launch_route_centred(const float* Z, const float* beta, const float* qraw,
+                                float* beta_out, int64_t N, int E, int K, int32_t* ids,
+                                float* S, float* alpha, float* margin, hipStream_t stream,
+                                uint32_t* zero, size_t zero_n) {
   const int64_t zn = zero ? (int64_t)zero_n : 0;
   const int nv = (E + kWave - 1) / kWave;
   // alpha alone: keys-only variant
@@ -505,21 +546,32 @@ hipError_t launch_route(const float* Z, const float* beta, int64_t N, int E, int
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     const dim3 grid((unsigned)blocks);
     switch (nv) {
+#define MOE_ROUTE_GROUP_LAUNCH(V, F, C)                                                   \
+  hipLaunchKernelGGL((route_group_kernel<V, F, C>), grid, block, 0, stream, Z, beta, N, E, K, \
+                     ids, S, alpha, margin, zero, zn, qraw, beta_out)
 #define MOE_ROUTE_GROUP_CASE(V)                                                           \
       case V:                                                                             \
-        if (E == 64 * V)                                                                  \
-          hipLaunchKernelGGL((route_group_kernel<V, true>), grid, block, 0, stream, Z, beta, N, \
-                             E, K, ids, S, alpha, margin, zero, zn);                      \
-        else                                                                              \
-          hipLaunchKernelGGL((route_group_kernel<V, false>), grid, block, 0, stream, Z, beta, \
-                             N, E, K, ids, S, alpha, margin, zero, zn);                   \
+        if (E == 64 * V) {                                                                \
+          if (qraw) MOE_ROUTE_GROUP_LAUNCH(V, true, true);                                \
+          else MOE_ROUTE_GROUP_LAUNCH(V, true, false);                                    \
+        } else {                                                                          \
+          if (qraw) MOE_ROUTE_GROUP_LAUNCH(V, false, true);                               \
+          else MOE_ROUTE_GROUP_LAUNCH(V, false, false);                                   \
+        }                                                                                 \
         break;
       MOE_ROUTE_GROUP_CASE(1) MOE_ROUTE_GROUP_CASE(2) MOE_ROUTE_GROUP_CASE(3)
       MOE_ROUTE_GROUP_CASE(4) MOE_ROUTE_GROUP_CASE(5) MOE_ROUTE_GROUP_CASE(6)
 #undef MOE_ROUTE_GROUP_CASE
+#undef MOE_ROUTE_GROUP_LAUNCH
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+  }
+  if (qraw) {
+    // the one-wave kernel takes a finished bias: centre in a launch of its own
+    const hipError_t err = launch_eqb_centre(qraw, E, beta_out, stream);
+    if (err != hipSuccess) return err;
+    beta = beta_out;
   }
   // The waves walk the rows with a grid stride; the grid is capped at what is
   // resident at once, so that no wave waits for a second round.
