@@ -174,6 +174,73 @@ __device__ __forceinline__ double raw_bias_mean(const float* q, int E) {
   for (; i < E; ++i) acc += (double)(-q[i]);
   return acc / (double)E;
 }
+// Highest and lowest set-bit positions (as powers of two) of a nonzero
+// finite float.
+__device__ __forceinline__ void f32_bit_span(float f, int& top, int& low) {
+  const uint32_t b = __float_as_uint(f);
+  const int ef = (int)((b >> 23) & 0xFFu);
+  const uint32_t m = b & 0x7FFFFFu;
+  if (ef == 0) {  // subnormal: m * 2^-149
+    top = 31 - __clz((int)m) - 149;
+    low = __ffs((int)m) - 1 - 149;
+  } else {
+    const uint32_t sig = m | 0x800000u;
+    top = ef - 127;
+    low = ef - 150 + (__ffs((int)sig) - 1);
+  }
+}
+// The same mean, formed by the whole block (BLOCK threads, all of them
+// calling).  When every partial sum of the E terms is exact in fp64 (all the
+// terms' set bits, and those of any sum of at most 2^9 of them, fit in 53
+// bits: top + 10 - low <= 53), the sum does not depend on the order of the
+// additions, so a tree over the block gives the bits of the sequential sum;
+// otherwise one thread adds them in expert order.  Every partial starts
+// from +0, so a zero total is +0 as in the sequential sum.
+template <int BLOCK>
+__device__ __forceinline__ double block_raw_bias_mean(const float* q, int E) {
+  constexpr int W = BLOCK / 64;
+  __shared__ double part_s[W];
+  __shared__ int top_s[W], low_s[W];
+  __shared__ double mean_s;
+  double part = 0.0;
+  int top = -100000, low = 100000;
+  for (int i = (int)threadIdx.x; i < E; i += BLOCK) {
+    const float v = -q[i];
+    part += (double)v;
+    if (v != 0.0f) {
+      int t, l;
+      f32_bit_span(v, t, l);
+      top = max(top, t);
+      low = min(low, l);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    part += __shfl_xor(part, o);
+    top = max(top, __shfl_xor(top, o));
+    low = min(low, __shfl_xor(low, o));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    part_s[threadIdx.x >> 6] = part;
+    top_s[threadIdx.x >> 6] = top;
+    low_s[threadIdx.x >> 6] = low;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double sum = 0.0;
+    int t = -100000, l = 100000;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      sum += part_s[w];
+      t = max(t, top_s[w]);
+      l = min(l, low_s[w]);
+    }
+    const bool exact = t < -99999 || t + 10 - l <= 53;
+    mean_s = exact ? sum / (double)E : raw_bias_mean(q, E);
+  }
+  __syncthreads();
+  return mean_s;
+}
 // Grid-stride clear of n words (a buffer that later kernels accumulate into),
 // ahead of a kernel's own work.
 // BLOCK is the launch's block size (a constant, so that no load of the

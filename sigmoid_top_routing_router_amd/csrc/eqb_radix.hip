@@ -31,8 +31,10 @@
 //    alpha, or by a fill).
 //  * eqb_last_kernel: one wave per expert selects the last byte of its key
 //    from the last histogram and decodes the quantile.
-//  * eqb_centre_kernel (one block): one thread sums the raw biases in expert
-//    order in fp64, every thread then writes fp32(fp64(beta_raw) - mean).
+//  * eqb_centre_kernel (one block): the mean of the raw biases in fp64 as
+//    their sum in expert order (block_raw_bias_mean: a tree over the block
+//    where every partial sum is exact, else one thread in order), then every
+//    thread writes fp32(fp64(beta_raw) - mean).
 // Five launches for 16-bit keys with alpha given: the fill, two histogram
 // passes, the last selection and the centring.
 //
@@ -304,19 +306,16 @@ __global__ __launch_bounds__(256) void eqb_scan_kernel(
   }
 }
 
-// Centring of the raw biases -Q_e: one thread sums them in expert order in
-// fp64, every thread writes fp32(fp64(-Q_e) - mean).  A kernel of its own
+// Centring of the raw biases -Q_e: their fp64 sum in expert order (formed by
+// block_raw_bias_mean), every thread writes fp32(fp64(-Q_e) - mean).  A kernel of its own
 // (one block) after the last scan, so the quantiles of all scan blocks are
 // visible without device-wide fences.
 __global__ __launch_bounds__(256) void eqb_centre_kernel(const float* __restrict__ qraw, int E,
                                                          float* __restrict__ beta_out) {
-  __shared__ double mean_s;
   __shared__ float q_s[kEqbMaxE];
   for (int i = threadIdx.x; i < E; i += blockDim.x) q_s[i] = qraw[i];
   __syncthreads();
-  if (threadIdx.x == 0) mean_s = raw_bias_mean(q_s, E);
-  __syncthreads();
-  const double mean = mean_s;
+  const double mean = block_raw_bias_mean<256>(q_s, E);
   for (int i = threadIdx.x; i < E; i += blockDim.x)
     beta_out[i] = (float)((double)(-q_s[i]) - mean);
 }

@@ -237,7 +237,7 @@ __device__ __forceinline__ void router_tile_select(const GemmArgs& a, int nt, in
     const int e = col_base + 64 * (i >> 2) + 4 * g + (i & 3);
     bv[i] = e < E ? (a.sel_beta ? a.sel_beta[e] + 0.0f : 0.0f) : -INFINITY;
   }
-  const bool vec = (E & 3) == 0;
+  const bool vec = (E & 3) == 0 && ((uintptr_t)Z & 15) == 0;
   auto load_row = [&](int r0, float (&v)[NVL]) {
     const int rl = min(r0 + rsel, rows - 1);
     const float* zr = Z + (row0 + rl) * (int64_t)E + col_base;

@@ -214,11 +214,11 @@ __host__ __device__ constexpr int qraw_cap(int nc) { return 64 * nc; }
 //
 // Centring on the fly (CENTRE, after an exact quantile update): the bias is
 // beta_e = fp32(fp64(-qraw_e) - mean), the mean over all experts in fp64 in
-// expert order, exactly as eqb_centre_kernel forms it; every block computes
-// it (one thread, from the raw quantiles in LDS) before it loads its rows,
-// and block 0 stores the biases to beta_out.  (Loading the rows first
-// holds them in registers through the sum: 104 instead of 74 VGPRs.)  This saves the one-block
-// centring launch, which inside the layer waits for a free compute unit.
+// expert order, formed as eqb_centre_kernel forms it (block_raw_bias_mean,
+// from the raw quantiles in LDS); every block computes it before it loads
+// its rows, and block 0 stores the biases to beta_out.  This saves the
+// one-block centring launch, which inside the layer waits for a free
+// compute unit.
 template <int NC, bool FULL, bool CENTRE>
 __global__ __launch_bounds__(256) void route_group_kernel(
     const float* __restrict__ Z, const float* __restrict__ beta, int64_t N, int E, int K,
@@ -239,12 +239,9 @@ __global__ __launch_bounds__(256) void route_group_kernel(
   __shared__ float kk[4][4][2];                 // K-th and (K+1)-th score
   if constexpr (CENTRE) {
     __shared__ float q_s[qraw_cap(NC)];  // raw quantiles
-    __shared__ double mean_s;
     for (int i = (int)threadIdx.x; i < E; i += 256) q_s[i] = qraw[i];
     __syncthreads();
-    if (threadIdx.x == 0) mean_s = raw_bias_mean(q_s, E);
-    __syncthreads();
-    const double mean = mean_s;
+    const double mean = block_raw_bias_mean<256>(q_s, E);
     for (int i = (int)threadIdx.x; i < 16 * NC; i += 256) {
       const int e0 = 4 * (i & 15) + 64 * (i >> 4);
       float b[4] = {0.f, 0.f, 0.f, 0.f};

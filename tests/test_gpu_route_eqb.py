@@ -203,6 +203,50 @@ def test_eqb_signed_zeros_and_subnormals(M, key_bits):
     assert np.any(q == 0.0)
 
 
+def _wide_span_logits(seed, N, E, K):
+    """Every row's K largest logits are columns 0..K-1 (1 + |n|), its
+    (K+1)-th is column K at exactly 0 (so alpha = -0 and v = Z), and the
+    other columns are -s_e |n| with s_e log-uniform over 1e-30 .. 1: the
+    quantiles then span about a hundred binades, more than a sum of E
+    of them can hold exactly in fp64."""
+    rng = np.random.default_rng(seed)
+    Z = np.empty((N, E), np.float32)
+    Z[:, :K] = 1.0 + np.abs(rng.standard_normal((N, K)))
+    Z[:, K] = 0.0
+    s = 10.0 ** rng.uniform(-30, 0, E - K - 1)
+    Z[:, K + 1:] = -(s[None, :] * np.abs(rng.standard_normal((N, E - K - 1))))
+    return Z.astype(np.float32)
+
+
+@pytest.mark.parametrize("key_bits", [16, 32])
+def test_eqb_centring_wide_exponent_span(M, key_bits):
+    """Quantiles whose sum is not exact in fp64 in every order: the
+    centring must then add them in expert order (the block-parallel sum is
+    taken only when every partial sum is exact), bit for bit with the
+    oracle; moe_eqb_bias (the one-block centring) and moe_forward (the final
+    routing pass centres the biases itself) both."""
+    N, E, K = 2048, 384, 6
+    Z = _wide_span_logits(231, N, E, K)
+    say("eqb wide exponent span", key_bits)
+    _, alpha, _ = O.route(Z, None, K)
+    assert np.all(alpha == 0.0)
+    rb, rq, _ = O.eqb_expert_bias(Z, alpha, K, key_bits)
+    nz = np.abs(rq[rq != 0].astype(np.float64))
+    assert np.log2(nz.max()) - np.log2(nz.min()) > 60
+    bo, q = M.eqb_bias(dev(Z), K, key_bits=key_bits)
+    assert bits_equal(host(q), rq)
+    assert bits_equal(host(bo), rb)
+    # the layer with these logits given: its beta_out comes from the routing pass
+    from synth import CONFIGS, make_inputs, scaled
+    from tests.gpu_util import bf16_dev, weights_dev
+    cfg = scaled(CONFIGS["prefill"], N)
+    L = make_inputs(cfg)
+    _, A = M.forward(bf16_dev(L.x), weights_dev(L), K, recompute_bias=True, key_bits=key_bits,
+                     logits_in=dev(Z), aux=("beta_out", "quantile_out"))
+    assert bits_equal(host(A["quantile_out"]), rq)
+    assert bits_equal(host(A["beta_out"]), rb)
+
+
 def test_route_signed_zeros(M):
     """Logits and biases with both zeros: -0 + -0 is the only -0 sum, and it
     ties with +0 (ids by expert order, alpha and margin bit-exact)."""
