@@ -128,6 +128,7 @@ SMALL = [
     ("decode", 64),
     ("prefill", 65),   # first size on the tile engine and the side stream
     ("skewed", 1000),
+    ("prefill", 3000),  # 18,000 pairs: the count table (9 rows), filled by the final routing pass
 ]
 
 
