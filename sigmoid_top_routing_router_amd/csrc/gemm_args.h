@@ -57,6 +57,15 @@ struct GemmArgs {
   float* cand_s;
   uint32_t* cand_e;
   int sel_k;
+  // Weight-streaming kernel only: an m-tile whose expert is -1 is the shared
+  // expert's (rows shared_row0 .. of H and Y; for gate/up its A rows are the
+  // tokens row - shared_row0, not gathered), with row-major weights Bs0 /
+  // Bs1 (E4M3: block scales sbs0 / sbs1).
+  const uint16_t* Bs0;
+  const uint16_t* Bs1;
+  const float* sbs0;
+  const float* sbs1;
+  int64_t shared_row0;
 };
 
 // Row-major B (every builder's default).

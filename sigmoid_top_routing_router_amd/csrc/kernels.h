@@ -92,8 +92,11 @@ struct PermWork {
 int64_t perm_count_rows(int64_t pairs);
 int64_t perm_max_tiles(int64_t pairs, int E, int bm);
 // Tiles hold bm rows; the last tile of a segment up to bm + xr rows.
+// shared_rows > 0 (one-block path only): ceil(shared_rows / 16) more m-tiles
+// of at most 16 rows, expert -1, over rows N*K .. N*K + shared_rows - 1
+// (the shared expert folded into the weight-streaming products).
 hipError_t launch_permute(const int32_t* ids, int64_t N, int E, int K, int bm, int xr,
-                          const PermWork& w, hipStream_t stream);
+                          const PermWork& w, hipStream_t stream, int shared_rows = 0);
 // Expert loads only (no permutation): counts[E] must be a device buffer.
 hipError_t launch_count(const int32_t* ids, int64_t pairs, int E, int32_t* counts,
                         hipStream_t stream);
@@ -197,6 +200,20 @@ hipError_t launch_router_shared_gateup_fp8(const uint16_t* x, const uint8_t* xq,
                                            uint8_t* Hsq, float* Hss, hipStream_t stream,
                                            const RouterSel* sel = nullptr);
 
+// The shared expert as more m-tiles of the weight-streaming products
+// (batches of at most 64 tokens with h_shared == h): the tile table's
+// entries with expert -1 cover rows row0 .. row0 + N - 1 of H and Y (tokens
+// 0 .. N - 1 of x, in order) with these row-major weights (E4M3: and
+// scales).
+struct SharedFold {
+  const void* gate;
+  const void* up;
+  const void* down;
+  const float* s_gate;
+  const float* s_up;
+  const float* s_down;
+  int64_t row0;
+};
 // Weight-streaming variants of the routed (grouped) products for batches of
 // at most 64 tokens (every tile then holds at most 64 rows); same arguments
 // and results as the launchers above, `tiles` required.
@@ -205,24 +222,27 @@ hipError_t launch_gateup_small(const uint16_t* x, int64_t x_rows, const int32_t*
                                int K, const int32_t* tiles, const int32_t* n_tiles,
                                int64_t max_tiles, int64_t rows_dense, const uint16_t* w_gate,
                                const uint16_t* w_up, int d, int h, uint16_t* H,
-                               hipStream_t stream, bool kblock_major = false);
+                               hipStream_t stream, bool kblock_major = false,
+                               const SharedFold* sf = nullptr);
 // Packs [E][rows][cols] bf16 (cols % 64 == 0) into [E][cols/64][rows][64].
 hipError_t launch_pack_kblocks(const uint16_t* w, int64_t E, int rows, int cols, uint16_t* out,
                                hipStream_t stream);
 hipError_t launch_down_small(const uint16_t* H, int64_t h_rows, const int32_t* tiles,
                              const int32_t* n_tiles, int64_t max_tiles, int64_t rows_dense,
                              const uint16_t* w_down, int d, int h, uint16_t* Y,
-                             hipStream_t stream);
+                             hipStream_t stream, const SharedFold* sf = nullptr);
 hipError_t launch_gateup_fp8_small(const uint8_t* xq, const float* xs, int64_t x_rows,
                                    const int32_t* sorted_src, int K, const int32_t* tiles,
                                    const int32_t* n_tiles, int64_t max_tiles, int64_t rows_dense,
                                    const uint8_t* wg, const float* sg, const uint8_t* wu,
                                    const float* su, int d, int h, uint8_t* Hq, float* Hs,
-                                   hipStream_t stream, bool kblock_major = false);
+                                   hipStream_t stream, bool kblock_major = false,
+                                   const SharedFold* sf = nullptr);
 hipError_t launch_down_fp8_small(const uint8_t* Hq, const float* Hs, int64_t h_rows,
                                  const int32_t* tiles, const int32_t* n_tiles, int64_t max_tiles,
                                  int64_t rows_dense, const uint8_t* wd, const float* sd, int d,
-                                 int h, uint16_t* Y, hipStream_t stream);
+                                 int h, uint16_t* Y, hipStream_t stream,
+                                 const SharedFold* sf = nullptr);
 
 // Dense products of a batch of at most 64 tokens (router, shared expert),
 // split over 64-row weight blocks and 256-wide k chunks; `part` holds

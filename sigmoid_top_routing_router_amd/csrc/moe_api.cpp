@@ -116,11 +116,21 @@ struct FwdLayout {
   int64_t max_tiles;
 };
 
+// A batch of at most 64 tokens whose shared expert has the routed experts'
+// hidden width runs that expert as up to four more m-tiles (16 rows each)
+// of the weight-streaming products (no side stream, no launches of its own).
+static bool shared_folded(const moe_problem_t& p) {
+  return p.N <= moe::kSmallBatch && p.n_shared == 1 && p.h_shared == p.h;
+}
+
 FwdLayout carve_forward(void* ws, const moe_problem_t& p, bool fp8 = false) {
   Carver c(ws);
   FwdLayout l{};
   const int64_t N = p.N, pairs = p.N * (int64_t)p.K;
   const int key_bits = (p.flags & MOE_KEY32) ? 32 : 16;
+  // the shared expert folded into the weight-streaming products: N more
+  // rows of H and Y, at most four more m-tiles of 16 rows
+  const int64_t hy_rows = pairs + (shared_folded(p) ? N : 0);
   l.Z = c.take<float>((size_t)N * p.E);
   l.ids0 = c.take<int32_t>((size_t)pairs);
   l.alpha = c.take<float>((size_t)N);
@@ -135,18 +145,18 @@ FwdLayout carve_forward(void* ws, const moe_problem_t& p, bool fp8 = false) {
   l.offsets = c.take<int32_t>((size_t)p.E + 1);
   l.sorted_src = c.take<int32_t>((size_t)pairs);
   l.src_pos = c.take<int32_t>((size_t)pairs);
-  l.max_tiles = moe::perm_max_tiles(pairs, p.E, moe::gemm_bm());
+  l.max_tiles = moe::perm_max_tiles(pairs, p.E, moe::gemm_bm()) + (shared_folded(p) ? 4 : 0);
   l.tiles = c.take<int32_t>((size_t)l.max_tiles * 4);
   l.n_tiles = c.take<int32_t>(4);
   if (fp8) {
     l.xq = c.take<uint8_t>((size_t)N * p.d);
     l.xs = c.take<float>((size_t)N * (p.d / 128));
-    l.Hq = c.take<uint8_t>((size_t)pairs * p.h);
-    l.Hqs = c.take<float>((size_t)pairs * (p.h / 128));
+    l.Hq = c.take<uint8_t>((size_t)hy_rows * p.h);
+    l.Hqs = c.take<float>((size_t)hy_rows * (p.h / 128));
   } else {
-    l.H = c.take<uint16_t>((size_t)pairs * p.h);
+    l.H = c.take<uint16_t>((size_t)hy_rows * p.h);
   }
-  l.Y = c.take<uint16_t>((size_t)pairs * p.d);
+  l.Y = c.take<uint16_t>((size_t)hy_rows * p.d);
   if (p.n_shared > 0) {
     if (fp8) {
       l.Hsq = c.take<uint8_t>((size_t)N * p.h_shared);
@@ -374,7 +384,8 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
   if (ex.fp8)
     MOE_TRY_HIP(moe::launch_quant_rows(x, N, d, l.xq, l.xs, st), "moe_forward: quantise x");
   SideJoin sj;
-  SideStream* side = (shared && !ex.in_order) ? side_stream() : nullptr;
+  const bool folded = shared_folded(*p);
+  SideStream* side = (shared && !folded && !ex.in_order) ? side_stream() : nullptr;
   // the side stream starts from the caller's stream as it stands before the
   // router GEMM (the fork), but its work is enqueued after that GEMM, whose
   // blocks are then dispatched first
@@ -395,7 +406,7 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
     sel = &rsel;
   }
   // the shared expert's products on the caller's stream (no side stream)
-  const bool shared_here = shared && !side;
+  const bool shared_here = shared && !folded && !side;
   if (small) {
     if (p->logits_in) {
       Z = p->logits_in;
@@ -547,30 +558,61 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
   pw.src_pos = A.src_pos ? A.src_pos : l.src_pos;
   pw.tiles = l.tiles;
   pw.n_tiles = l.n_tiles;
-  MOE_TRY_HIP(moe::launch_permute(ids, N, E, K, moe::gemm_bm(), moe::gemm_xrows(), pw, st),
+  MOE_TRY_HIP(moe::launch_permute(ids, N, E, K, moe::gemm_bm(), moe::gemm_xrows(), pw, st,
+                                  folded ? (int)N : 0),
               "moe_forward: grouping");
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
 
   // routed experts (the gather is fused into the gate/up A loads)
-  auto gateup = small ? moe::launch_gateup_small : moe::launch_gateup;
-  auto gateup8 = small ? moe::launch_gateup_fp8_small : moe::launch_gateup_fp8;
-  auto down = small ? moe::launch_down_small : moe::launch_down;
-  auto down8 = small ? moe::launch_down_fp8_small : moe::launch_down_fp8;
   const bool packed = (p->flags & MOE_PACKED_GATEUP) != 0;
-  if (ex.fp8)
-    MOE_TRY_HIP(gateup8(l.xq, l.xs, N, pw.sorted_src, K, pw.tiles, pw.n_tiles, l.max_tiles, 0,
-                        q->w_gate, q->s_gate, q->w_up, q->s_up, d, h, l.Hq, l.Hqs, st, packed),
+  const int64_t hy_rows = N * K + (folded ? N : 0);
+  moe::SharedFold fold{};
+  if (folded) {
+    fold.gate = ex.fp8 ? (const void*)q->ws_gate : (const void*)w->ws_gate;
+    fold.up = ex.fp8 ? (const void*)q->ws_up : (const void*)w->ws_up;
+    fold.down = ex.fp8 ? (const void*)q->ws_down : (const void*)w->ws_down;
+    fold.s_gate = ex.fp8 ? q->ss_gate : nullptr;
+    fold.s_up = ex.fp8 ? q->ss_up : nullptr;
+    fold.s_down = ex.fp8 ? q->ss_down : nullptr;
+    fold.row0 = N * K;
+  }
+  const moe::SharedFold* sf = folded ? &fold : nullptr;
+  if (ex.fp8 && small)
+    MOE_TRY_HIP(moe::launch_gateup_fp8_small(l.xq, l.xs, N, pw.sorted_src, K, pw.tiles,
+                                             pw.n_tiles, l.max_tiles, 0, q->w_gate, q->s_gate,
+                                             q->w_up, q->s_up, d, h, l.Hq, l.Hqs, st, packed, sf),
+                "moe_forward: gate/up");
+  else if (ex.fp8)
+    MOE_TRY_HIP(moe::launch_gateup_fp8(l.xq, l.xs, N, pw.sorted_src, K, pw.tiles, pw.n_tiles,
+                                       l.max_tiles, 0, q->w_gate, q->s_gate, q->w_up, q->s_up, d,
+                                       h, l.Hq, l.Hqs, st, packed),
+                "moe_forward: gate/up");
+  else if (small)
+    MOE_TRY_HIP(moe::launch_gateup_small(x, N, pw.sorted_src, K, pw.tiles, pw.n_tiles,
+                                         l.max_tiles, 0, w->w_gate, w->w_up, d, h, l.H, st,
+                                         packed, sf),
                 "moe_forward: gate/up");
   else
-    MOE_TRY_HIP(gateup(x, N, pw.sorted_src, K, pw.tiles, pw.n_tiles, l.max_tiles, 0, w->w_gate,
-                       w->w_up, d, h, l.H, st, packed),
+    MOE_TRY_HIP(moe::launch_gateup(x, N, pw.sorted_src, K, pw.tiles, pw.n_tiles, l.max_tiles, 0,
+                                   w->w_gate, w->w_up, d, h, l.H, st, packed),
                 "moe_forward: gate/up");
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
-  if (ex.fp8)
-    MOE_TRY_HIP(down8(l.Hq, l.Hqs, N * K, pw.tiles, pw.n_tiles, l.max_tiles, 0, q->w_down,
-                      q->s_down, d, h, l.Y, st), "moe_forward: down");
+  if (ex.fp8 && small)
+    MOE_TRY_HIP(moe::launch_down_fp8_small(l.Hq, l.Hqs, hy_rows, pw.tiles, pw.n_tiles,
+                                           l.max_tiles, 0, q->w_down, q->s_down, d, h, l.Y, st,
+                                           sf),
+                "moe_forward: down");
+  else if (ex.fp8)
+    MOE_TRY_HIP(moe::launch_down_fp8(l.Hq, l.Hqs, N * K, pw.tiles, pw.n_tiles, l.max_tiles, 0,
+                                     q->w_down, q->s_down, d, h, l.Y, st),
+                "moe_forward: down");
+  else if (small)
+    MOE_TRY_HIP(moe::launch_down_small(l.H, hy_rows, pw.tiles, pw.n_tiles, l.max_tiles, 0,
+                                       w->w_down, d, h, l.Y, st, sf),
+                "moe_forward: down");
   else
-    MOE_TRY_HIP(down(l.H, N * K, pw.tiles, pw.n_tiles, l.max_tiles, 0, w->w_down, d, h, l.Y, st),
+    MOE_TRY_HIP(moe::launch_down(l.H, N * K, pw.tiles, pw.n_tiles, l.max_tiles, 0, w->w_down, d,
+                                 h, l.Y, st),
                 "moe_forward: down");
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
   // the shared expert's down projection
@@ -589,7 +631,9 @@ static moe_status_t forward_impl(const moe_problem_t* p, const Experts& ex, cons
   MOE_TRY_HIP(sj.join(), "moe_forward: join");
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
   // weighted combine
-  MOE_TRY_HIP(moe::launch_combine(shared ? l.sh : nullptr, l.Y, S, pw.src_pos, N, K, d, y, st),
+  // the folded shared expert's output: rows N*K .. of Y, in token order
+  const uint16_t* sh_out = folded ? l.Y + (size_t)N * K * d : (shared ? l.sh : nullptr);
+  MOE_TRY_HIP(moe::launch_combine(sh_out, l.Y, S, pw.src_pos, N, K, d, y, st),
               "moe_forward: combine");
   MOE_TRY_HIP(tm.mark(), "moe_forward: stage timer");
   return ok();

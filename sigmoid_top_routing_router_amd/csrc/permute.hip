@@ -229,7 +229,7 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(
     const int32_t* __restrict__ ids, int64_t pairs, int E, int bm, int xr,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_src, int32_t* __restrict__ src_pos,
-    int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+    int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles, int shared_rows) {
   __shared__ uint32_t wcnt[kSmallWaves][kMaxE];  // counts, then bases per wave
   __shared__ uint32_t tot[kMaxE];
   __shared__ uint32_t wsum_c[kSmallWaves], wsum_t[kSmallWaves];
@@ -266,7 +266,14 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(
   uint32_t toff = bt + it - t;
   if (tid == blockDim.x - 1) {
     offsets[E] = (int32_t)(bc + ic);
-    *n_tiles = (int32_t)(bt + it);
+    // the shared expert's tiles after the routed ones, 16 rows each: the
+    // weight-streaming kernel streams a tile's weights once per 16 rows, so
+    // a 64-row tile would take one block four times as long as the others
+    uint32_t nt = bt + it;
+    for (int r = 0; r < shared_rows; r += 16)
+      reinterpret_cast<int4*>(tiles)[nt++] =
+          make_int4(-1, (int32_t)(pairs + r), min(16, shared_rows - r), r);
+    *n_tiles = (int32_t)nt;
   }
   if (tid < E) {
     counts[tid] = (int32_t)c;
@@ -302,13 +309,15 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(
 }
 
 hipError_t launch_permute(const int32_t* ids, int64_t N, int E, int K, int bm, int xr,
-                          const PermWork& w, hipStream_t stream) {
+                          const PermWork& w, hipStream_t stream, int shared_rows) {
   const int64_t pairs = N * (int64_t)K;
   if (pairs <= kSmallPairs) {
     hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(1024), 0, stream, ids, pairs, E, bm, xr,
-                       w.counts, w.offsets, w.sorted_src, w.src_pos, w.tiles, w.n_tiles);
+                       w.counts, w.offsets, w.sorted_src, w.src_pos, w.tiles, w.n_tiles,
+                       shared_rows);
     return hipGetLastError();
   }
+  if (shared_rows > 0) return hipErrorInvalidValue;
   const int64_t cw = perm_chunk(pairs);
   const int64_t n_blocks = perm_count_rows(pairs);
   const dim3 grid((unsigned)n_blocks), block(256);

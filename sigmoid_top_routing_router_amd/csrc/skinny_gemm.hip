@@ -112,9 +112,17 @@ __global__ __launch_bounds__(256) void skinny_kernel(GemmArgs a, int n_chunks) {
   const uint32_t gchunk1 = (uint32_t)g_chunk((lane & 7) ^ ((4 + (lane >> 4)) & 7)) * 16u;
   const uint32_t set_bytes = SET_K * EB;
   const uint32_t b_bytes = (uint32_t)a.b_rows * (uint32_t)a.kdim * EB;
-  const char* bexp0 = reinterpret_cast<const char*>(a.B0) + (int64_t)expert * a.b_expert_stride * EB;
-  const char* bexp1 = reinterpret_cast<const char*>(MODE == kGateUp ? a.B1 : a.B0) +
-                      (int64_t)expert * a.b_expert_stride * EB;
+  // the shared expert's tile (expert -1): its own row-major weights
+  const bool shared = expert < 0;
+  const uint32_t row_pitch = shared ? (uint32_t)a.kdim * EB : a.b_row_pitch;
+  const uint32_t kblk_pitch = shared ? 128u : a.b_kblk_pitch;
+  const char* bexp0 =
+      shared ? reinterpret_cast<const char*>(a.Bs0)
+             : reinterpret_cast<const char*>(a.B0) + (int64_t)expert * a.b_expert_stride * EB;
+  const char* bexp1 =
+      shared ? reinterpret_cast<const char*>(MODE == kGateUp ? a.Bs1 : a.Bs0)
+             : reinterpret_cast<const char*>(MODE == kGateUp ? a.B1 : a.B0) +
+                   (int64_t)expert * a.b_expert_stride * EB;
   const __amdgpu_buffer_rsrc_t rw0 = make_rsrc(bexp0, b_bytes);
   const __amdgpu_buffer_rsrc_t rw1 = make_rsrc(bexp1, b_bytes);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, a.a_bytes);
@@ -124,16 +132,18 @@ __global__ __launch_bounds__(256) void skinny_kernel(GemmArgs a, int n_chunks) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int r = min(wcol[mb] + 8 * h + (lane >> 3), a.b_rows - 1);
-      w_voff[mb][h] = (uint32_t)r * a.b_row_pitch + (h ? gchunk1 : gchunk0);
+      w_voff[mb][h] = (uint32_t)r * row_pitch + (h ? gchunk1 : gchunk0);
     }
   // E4M3 scales: [A rows][kdim / 128] for the activations, the expert's
   // [b_rows / 128][kdim / 128] for the weights (unused resources cover 0 bytes)
   const __amdgpu_buffer_rsrc_t rsa = make_rsrc(FP8 ? (const void*)a.sa : a.A, FP8 ? a.a_bytes / 32 : 0u);
-  const __amdgpu_buffer_rsrc_t rsb0 = make_rsrc(
-      FP8 ? (const void*)(a.sb0 + (int64_t)expert * a.sb_es) : a.A, FP8 ? (uint32_t)a.sb_es * 4u : 0u);
-  const __amdgpu_buffer_rsrc_t rsb1 = make_rsrc(
-      FP8 ? (const void*)((MODE == kGateUp ? a.sb1 : a.sb0) + (int64_t)expert * a.sb_es) : a.A,
-      FP8 ? (uint32_t)a.sb_es * 4u : 0u);
+  const float* sbase0 = shared ? a.sbs0 : a.sb0 + (int64_t)expert * a.sb_es;
+  const float* sbase1 = shared ? (MODE == kGateUp ? a.sbs1 : a.sbs0)
+                               : (MODE == kGateUp ? a.sb1 : a.sb0) + (int64_t)expert * a.sb_es;
+  const __amdgpu_buffer_rsrc_t rsb0 = make_rsrc(FP8 ? (const void*)sbase0 : a.A,
+                                                FP8 ? (uint32_t)a.sb_es * 4u : 0u);
+  const __amdgpu_buffer_rsrc_t rsb1 = make_rsrc(FP8 ? (const void*)sbase1 : a.A,
+                                                FP8 ? (uint32_t)a.sb_es * 4u : 0u);
   const int nblk = (a.b_rows + 127) / 128;
   const int sblk = (MODE == kGateUp) ? nc : min(c0 / 128, nblk - 1);
   const uint32_t sb_voff0 = (uint32_t)(sblk * nkb) * 4u, sb_voff1 = sb_voff0;
@@ -149,7 +159,8 @@ __global__ __launch_bounds__(256) void skinny_kernel(GemmArgs a, int n_chunks) {
     // A row of tile row tt (rows past the tile read the first row)
     auto a_row = [&](int tt) -> int64_t {
       const int64_t r = row0 + (tt < rows ? tt : 0);
-      return a.gather ? (int64_t)(a.gather[r] / a.gather_div) : r;
+      if (!a.gather) return r;
+      return shared ? r - a.shared_row0 : (int64_t)(a.gather[r] / a.gather_div);
     };
     uint32_t t_voff[2];
 #pragma unroll
@@ -161,7 +172,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(GemmArgs a, int n_chunks) {
     auto issue = [&](int s) {
       char* slot = ring + (s % kRing) * kSlot;
       const uint32_t soff = (uint32_t)s * set_bytes;
-      const uint32_t soff_w = (uint32_t)s * a.b_kblk_pitch;  // a set is one 128-byte k-block
+      const uint32_t soff_w = (uint32_t)s * kblk_pitch;  // a set is one 128-byte k-block
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         const __amdgpu_buffer_rsrc_t rw = (MODE == kGateUp && mb >= 2) ? rw1 : rw0;
@@ -347,14 +358,24 @@ hipError_t launch_skinny_mode(const GemmArgs& a, int64_t m_tiles, hipStream_t st
 
 }  // namespace
 
+static void apply_fold(GemmArgs& a, const SharedFold* sf, int mode) {
+  if (!sf) return;
+  a.Bs0 = static_cast<const uint16_t*>(mode == kGateUp ? sf->gate : sf->down);
+  a.Bs1 = static_cast<const uint16_t*>(sf->up);
+  a.sbs0 = mode == kGateUp ? sf->s_gate : sf->s_down;
+  a.sbs1 = sf->s_up;
+  a.shared_row0 = sf->row0;
+}
+
 hipError_t launch_gateup_small(const uint16_t* x, int64_t x_rows, const int32_t* sorted_src,
                                int K, const int32_t* tiles, const int32_t* n_tiles,
                                int64_t max_tiles, int64_t rows_dense, const uint16_t* w_gate,
                                const uint16_t* w_up, int d, int h, uint16_t* H,
-                               hipStream_t stream, bool kblock_major) {
+                               hipStream_t stream, bool kblock_major, const SharedFold* sf) {
   GemmArgs a = gateup_args(x, x_rows, sorted_src, K, tiles, n_tiles, rows_dense, w_gate, w_up, d,
                            h, H);
   if (kblock_major) b_kblock_major(a);
+  apply_fold(a, sf, kGateUp);
   if (!tiles) return hipErrorInvalidValue;
   return launch_skinny_mode<kGateUp, false>(a, max_tiles, stream);
 }
@@ -362,8 +383,9 @@ hipError_t launch_gateup_small(const uint16_t* x, int64_t x_rows, const int32_t*
 hipError_t launch_down_small(const uint16_t* H, int64_t h_rows, const int32_t* tiles,
                              const int32_t* n_tiles, int64_t max_tiles, int64_t rows_dense,
                              const uint16_t* w_down, int d, int h, uint16_t* Y,
-                             hipStream_t stream) {
-  const GemmArgs a = down_args(H, h_rows, tiles, n_tiles, rows_dense, w_down, d, h, Y);
+                             hipStream_t stream, const SharedFold* sf) {
+  GemmArgs a = down_args(H, h_rows, tiles, n_tiles, rows_dense, w_down, d, h, Y);
+  apply_fold(a, sf, kDown);
   if (!tiles) return hipErrorInvalidValue;
   return launch_skinny_mode<kDown, false>(a, max_tiles, stream);
 }
@@ -373,10 +395,11 @@ hipError_t launch_gateup_fp8_small(const uint8_t* xq, const float* xs, int64_t x
                                    const int32_t* n_tiles, int64_t max_tiles, int64_t rows_dense,
                                    const uint8_t* wg, const float* sg, const uint8_t* wu,
                                    const float* su, int d, int h, uint8_t* Hq, float* Hs,
-                                   hipStream_t stream, bool kblock_major) {
+                                   hipStream_t stream, bool kblock_major, const SharedFold* sf) {
   GemmArgs a = gateup_fp8_args(xq, xs, x_rows, sorted_src, K, tiles, n_tiles, rows_dense, wg, sg,
                                wu, su, d, h, Hq, Hs);
   if (kblock_major) b_kblock_major(a);
+  apply_fold(a, sf, kGateUp);
   if (!tiles) return hipErrorInvalidValue;
   return launch_skinny_mode<kGateUp, true>(a, max_tiles, stream);
 }
@@ -384,8 +407,9 @@ hipError_t launch_gateup_fp8_small(const uint8_t* xq, const float* xs, int64_t x
 hipError_t launch_down_fp8_small(const uint8_t* Hq, const float* Hs, int64_t h_rows,
                                  const int32_t* tiles, const int32_t* n_tiles, int64_t max_tiles,
                                  int64_t rows_dense, const uint8_t* wd, const float* sd, int d,
-                                 int h, uint16_t* Y, hipStream_t stream) {
-  const GemmArgs a = down_fp8_args(Hq, Hs, h_rows, tiles, n_tiles, rows_dense, wd, sd, d, h, Y);
+                                 int h, uint16_t* Y, hipStream_t stream, const SharedFold* sf) {
+  GemmArgs a = down_fp8_args(Hq, Hs, h_rows, tiles, n_tiles, rows_dense, wd, sd, d, h, Y);
+  apply_fold(a, sf, kDown);
   if (!tiles) return hipErrorInvalidValue;
   return launch_skinny_mode<kDown, true>(a, max_tiles, stream);
 }
