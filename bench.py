@@ -84,15 +84,22 @@ def gateup_algorithmic(cfg, counts, fp8=False):
     row times both d x h projections; each active expert's gate and up
     weights once, x once, H written once (bf16; with FP8 experts: E4M3 codes
     plus one fp32 scale per 128 x 128 weight block and per 1 x 128 group of
-    x and of H)."""
+    x and of H).  Batches of at most 64 tokens whose shared expert has the
+    routed width run that expert inside the same launch (its tiles follow
+    the routed ones): its gate and up weights and its N rows of H count
+    too."""
     pairs = cfg.N * cfg.K
-    flops = 2.0 * pairs * (2 * cfg.h) * cfg.d
-    active = int((counts > 0).sum())
+    experts = int((counts > 0).sum())
+    rows = pairs
+    if cfg.N <= 64 and cfg.n_shared == 1 and cfg.h_shared == cfg.h:
+        experts += 1
+        rows += cfg.N
+    flops = 2.0 * rows * (2 * cfg.h) * cfg.d
     if fp8:
-        bytes_ = (active * 2 * (cfg.h * cfg.d + (cfg.h // 128) * (cfg.d // 128) * 4)
-                  + cfg.N * cfg.d * (1 + 4 / 128) + pairs * cfg.h * (1 + 4 / 128))
+        bytes_ = (experts * 2 * (cfg.h * cfg.d + (cfg.h // 128) * (cfg.d // 128) * 4)
+                  + cfg.N * cfg.d * (1 + 4 / 128) + rows * cfg.h * (1 + 4 / 128))
     else:
-        bytes_ = active * 2 * cfg.h * cfg.d * 2 + cfg.N * cfg.d * 2 + pairs * cfg.h * 2
+        bytes_ = experts * 2 * cfg.h * cfg.d * 2 + cfg.N * cfg.d * 2 + rows * cfg.h * 2
     return flops, bytes_
 
 

@@ -202,6 +202,17 @@ def test_forward_router_column_tails(M, E):
     run_case(M, cfg)
 
 
+@pytest.mark.parametrize("N,hs", [(50, None), (37, 1024)])
+def test_forward_decode_shared_expert_paths(M, N, hs):
+    """At most 64 tokens: with h_shared == h the shared expert runs as 16-row
+    tiles (the last one ragged) inside the weight-streaming products; with a
+    wider shared expert it keeps its own split-K products on the side
+    stream.  Every token against the oracle."""
+    base = scaled(CONFIGS["decode"], N)
+    cfg = replace(base, h_shared=hs or base.h, name=f"decode_shared_{N}_{hs}")
+    run_case(M, cfg, free_running=True)
+
+
 def test_forward_without_shared_expert(M):
     cfg = replace(scaled(CONFIGS["prefill"], 200), n_shared=0, name="noshared")
     run_case(M, cfg)
